@@ -1,0 +1,297 @@
+/*
+ * kvx_oracle.c -- CPU oracle for the paged-KV data-movement path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this library.  It shares no code, no
+ * header and no constant with the HIP library; it is a plain, slow,
+ * obviously-correct row-by-row memcpy loop over the slot tables.
+ *
+ * Sources (the pages' titles and the sections used):
+ *   [budget]  "穷人版 PD 分离：在消费级显卡上把 TTS 推理拆成两半" (kilerd.me,
+ *             pd-on-a-budget): sections "B300：让 P 直接写 D 的显存" and
+ *             "5090：一个看得见所有卡的代理", plus its failure-handling section.
+ *   [mini]    "mini-infer系统实战-18-PD 解耦：把 Prefill 和 Decode 拆进两个进程之后
+ *             发生了什么" (smarter.xin): section "KV 序列化格式选择".
+ *   [survey]  "PD分离调研：从推理阶段拆分到Mooncake的KVCache中心架构"
+ *             (gentlecold.top): sections 7.4 (registering the per-layer KV
+ *             cache addresses) and 7.6 (P writes KV blocks into D).
+ *
+ * What it computes (every function is a bitwise copy; no arithmetic touches
+ * the KV values, so fp16 / bf16 / NaN payloads pass through unchanged):
+ *
+ *   Token-paged pool ([budget], 5090 section).  The pool is paged per token,
+ *   so one request's KV is spread over the pool in thousands of pieces of a
+ *   few KB, and a freshly started pool yields one contiguous block per
+ *   (layer, K/V).  A pool is therefore read as Q planes (Q = layers x {K,V}),
+ *   each an array of slots of R bytes (R = kv_heads * head_dim * element
+ *   size); slot s of plane q sits at planes[q] + s*stride.
+ *
+ *   Paged blocks ([survey] 7.4).  Each per-layer cache tensor is cut into
+ *   num_blocks equal blocks.  With B tokens per page, token t of request r
+ *   lives in page ids[pg_off[r] + t/B], row t%B of it: slot page*B + t%B.
+ *
+ *   Gather / scatter ([budget], 5090 section).  P first collects the rows to
+ *   be sent into one contiguous staging area, one transfer moves it, and D
+ *   writes the rows back into its own pages.  The staging layout is the
+ *   per-layer (k, v) list of [seq, kv_heads, head_dim] tensors of [mini],
+ *   laid end to end: request r starts at token offset tok_off[r] and holds,
+ *   plane by plane, its n_r rows.  Byte offset of (r, q, t):
+ *       (tok_off[r] * Q + q * n_r + t) * R.
+ *
+ *   Gather-scatter ([budget], B300 section; [survey] 7.6).  Each scattered
+ *   source row is written straight into its destination page, with no
+ *   staging in between.
+ *
+ *   Extract / rebuild permute ([mini]).  Extract keeps batch 0 and the first
+ *   seq_len positions of a [1, H, S, D] layer cache and swaps the head and
+ *   sequence axes, giving [seq, H, D]; rebuild swaps them back into
+ *   [1, H, seq, D].  The Q per-plane [seq, H, D] results are stacked as one
+ *   [Q][seq][H][D] buffer.
+ *
+ *   Out-of-range page ids (page < 0 or page >= num_pages) are never
+ *   dereferenced: the row is skipped, counted, and its destination bytes keep
+ *   their prior contents ([budget], failure-handling section: the failure to
+ *   rule out is a late write landing in pages already handed to someone
+ *   else).
+ *
+ * Every function returns the number of skipped rows (>= 0).  Work may be
+ * split over nthreads POSIX threads by (request, plane) pairs; the result does
+ * not depend on nthreads because no two pairs write the same byte under the
+ * precondition that destination rows are distinct.
+ */
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- tables -- */
+
+/* Slot of token t of request r in a pool with page_size tokens per page, or -1
+ * when the page id is out of range. */
+static int64_t slot_of(const int64_t* pg_off, const int32_t* ids, int32_t page_size,
+                       int64_t num_pages, int64_t r, int64_t t)
+{
+    int64_t page = (int64_t)ids[pg_off[r] + t / page_size];
+    if (page < 0 || page >= num_pages) return -1;
+    return page * page_size + t % page_size;
+}
+
+/* A pool side of a move: Q plane base pointers, slot stride, paging. */
+typedef struct {
+    uint8_t* const* planes;
+    int64_t stride;
+    int32_t page_size;
+    int64_t num_pages;
+    const int64_t* pg_off;
+    const int32_t* ids;
+} pool_side;
+
+enum { OP_GATHER = 0, OP_SCATTER = 1, OP_GATHER_SCATTER = 2 };
+
+typedef struct {
+    int op;
+    int32_t Q;
+    int64_t R;
+    int32_t num_reqs;
+    const int64_t* tok_off;
+    pool_side src, dst;
+    uint8_t* staging;       /* gather: destination; scatter: source */
+    int64_t first_pair, last_pair;   /* (r, q) pairs [first, last) */
+    int64_t skipped;
+} row_job;
+
+static void* run_rows(void* arg)
+{
+    row_job* j = (row_job*)arg;
+    int64_t skipped = 0;
+    for (int64_t pair = j->first_pair; pair < j->last_pair; ++pair) {
+        int64_t r = pair / j->Q;
+        int64_t q = pair % j->Q;
+        int64_t n = j->tok_off[r + 1] - j->tok_off[r];
+        for (int64_t t = 0; t < n; ++t) {
+            uint8_t* staged = j->staging
+                ? j->staging + (j->tok_off[r] * j->Q + q * n + t) * j->R : NULL;
+            if (j->op == OP_GATHER) {
+                int64_t s = slot_of(j->src.pg_off, j->src.ids, j->src.page_size,
+                                    j->src.num_pages, r, t);
+                if (s < 0) { ++skipped; continue; }
+                memcpy(staged, j->src.planes[q] + s * j->src.stride, (size_t)j->R);
+            } else if (j->op == OP_SCATTER) {
+                int64_t d = slot_of(j->dst.pg_off, j->dst.ids, j->dst.page_size,
+                                    j->dst.num_pages, r, t);
+                if (d < 0) { ++skipped; continue; }
+                memcpy(j->dst.planes[q] + d * j->dst.stride, staged, (size_t)j->R);
+            } else {
+                int64_t s = slot_of(j->src.pg_off, j->src.ids, j->src.page_size,
+                                    j->src.num_pages, r, t);
+                int64_t d = slot_of(j->dst.pg_off, j->dst.ids, j->dst.page_size,
+                                    j->dst.num_pages, r, t);
+                if (s < 0 || d < 0) { ++skipped; continue; }
+                memcpy(j->dst.planes[q] + d * j->dst.stride,
+                       j->src.planes[q] + s * j->src.stride, (size_t)j->R);
+            }
+        }
+    }
+    j->skipped = skipped;
+    return NULL;
+}
+
+/* Split the (request, plane) pairs over nthreads threads and run them. */
+static int64_t run_split(row_job proto, int nthreads)
+{
+    int64_t pairs = (int64_t)proto.num_reqs * proto.Q;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (pairs < nthreads) nthreads = pairs > 0 ? (int)pairs : 1;
+    row_job jobs[256];
+    pthread_t tids[256];
+    int started[256];
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = proto;
+        jobs[i].first_pair = pairs * i / nthreads;
+        jobs[i].last_pair = pairs * (i + 1) / nthreads;
+        jobs[i].skipped = 0;
+        started[i] = 0;
+    }
+    for (int i = 1; i < nthreads; ++i)
+        started[i] = pthread_create(&tids[i], NULL, run_rows, &jobs[i]) == 0;
+    run_rows(&jobs[0]);
+    for (int i = 1; i < nthreads; ++i) {
+        if (started[i]) pthread_join(tids[i], NULL);
+        else run_rows(&jobs[i]);
+    }
+    int64_t total = 0;
+    for (int i = 0; i < nthreads; ++i) total += jobs[i].skipped;
+    return total;
+}
+
+/* Gather: staging(r, q, t) <- src plane q, slot of token t of request r. */
+int64_t oracle_gather(int32_t Q, int64_t R,
+                      uint8_t* const* src_planes, int64_t src_stride,
+                      int32_t src_page_size, int64_t src_num_pages,
+                      int32_t num_reqs, const int64_t* tok_off,
+                      const int64_t* src_pg_off, const int32_t* src_ids,
+                      uint8_t* staging, int nthreads)
+{
+    row_job j;
+    memset(&j, 0, sizeof j);
+    j.op = OP_GATHER; j.Q = Q; j.R = R; j.num_reqs = num_reqs; j.tok_off = tok_off;
+    j.src.planes = src_planes; j.src.stride = src_stride; j.src.page_size = src_page_size;
+    j.src.num_pages = src_num_pages; j.src.pg_off = src_pg_off; j.src.ids = src_ids;
+    j.staging = staging;
+    return run_split(j, nthreads);
+}
+
+/* Scatter: dst plane q, slot of token t of request r <- staging(r, q, t). */
+int64_t oracle_scatter(int32_t Q, int64_t R, const uint8_t* staging,
+                       int32_t num_reqs, const int64_t* tok_off,
+                       const int64_t* dst_pg_off, const int32_t* dst_ids,
+                       uint8_t* const* dst_planes, int64_t dst_stride,
+                       int32_t dst_page_size, int64_t dst_num_pages, int nthreads)
+{
+    row_job j;
+    memset(&j, 0, sizeof j);
+    j.op = OP_SCATTER; j.Q = Q; j.R = R; j.num_reqs = num_reqs; j.tok_off = tok_off;
+    j.dst.planes = dst_planes; j.dst.stride = dst_stride; j.dst.page_size = dst_page_size;
+    j.dst.num_pages = dst_num_pages; j.dst.pg_off = dst_pg_off; j.dst.ids = dst_ids;
+    j.staging = (uint8_t*)staging;
+    return run_split(j, nthreads);
+}
+
+/* Gather-scatter: dst plane q at the dst slot of (r, t) <- src plane q at the
+ * src slot of (r, t).  Both sides share the token CSR tok_off; each has its
+ * own page table and page size. */
+int64_t oracle_gather_scatter(int32_t Q, int64_t R,
+                              uint8_t* const* src_planes, int64_t src_stride,
+                              int32_t src_page_size, int64_t src_num_pages,
+                              const int64_t* src_pg_off, const int32_t* src_ids,
+                              int32_t num_reqs, const int64_t* tok_off,
+                              uint8_t* const* dst_planes, int64_t dst_stride,
+                              int32_t dst_page_size, int64_t dst_num_pages,
+                              const int64_t* dst_pg_off, const int32_t* dst_ids,
+                              int nthreads)
+{
+    row_job j;
+    memset(&j, 0, sizeof j);
+    j.op = OP_GATHER_SCATTER; j.Q = Q; j.R = R; j.num_reqs = num_reqs; j.tok_off = tok_off;
+    j.src.planes = src_planes; j.src.stride = src_stride; j.src.page_size = src_page_size;
+    j.src.num_pages = src_num_pages; j.src.pg_off = src_pg_off; j.src.ids = src_ids;
+    j.dst.planes = dst_planes; j.dst.stride = dst_stride; j.dst.page_size = dst_page_size;
+    j.dst.num_pages = dst_num_pages; j.dst.pg_off = dst_pg_off; j.dst.ids = dst_ids;
+    return run_split(j, nthreads);
+}
+
+/* ------------------------------------------------------------- permutes -- */
+
+typedef struct {
+    int rebuild;
+    int32_t H;
+    int64_t Db;              /* head_dim * element size */
+    int64_t s_cap, seq;
+    uint8_t* const* hf;      /* [Q] planes, each [1][H][s_cap][D] */
+    uint8_t* flat;           /* [Q][seq][H][D] */
+    int32_t q0, q1;
+} perm_job;
+
+static void* run_perm(void* arg)
+{
+    perm_job* j = (perm_job*)arg;
+    for (int32_t q = j->q0; q < j->q1; ++q)
+        for (int64_t s = 0; s < j->seq; ++s)
+            for (int32_t h = 0; h < j->H; ++h) {
+                uint8_t* hf_row = j->hf[q] + ((int64_t)h * j->s_cap + s) * j->Db;
+                uint8_t* flat_row = j->flat + (((int64_t)q * j->seq + s) * j->H + h) * j->Db;
+                if (j->rebuild) memcpy(hf_row, flat_row, (size_t)j->Db);
+                else memcpy(flat_row, hf_row, (size_t)j->Db);
+            }
+    return NULL;
+}
+
+static void run_perm_split(perm_job proto, int32_t Q, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (Q < nthreads) nthreads = Q > 0 ? Q : 1;
+    perm_job jobs[256];
+    pthread_t tids[256];
+    int started[256];
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = proto;
+        jobs[i].q0 = (int32_t)((int64_t)Q * i / nthreads);
+        jobs[i].q1 = (int32_t)((int64_t)Q * (i + 1) / nthreads);
+        started[i] = 0;
+    }
+    for (int i = 1; i < nthreads; ++i)
+        started[i] = pthread_create(&tids[i], NULL, run_perm, &jobs[i]) == 0;
+    run_perm(&jobs[0]);
+    for (int i = 1; i < nthreads; ++i) {
+        if (started[i]) pthread_join(tids[i], NULL);
+        else run_perm(&jobs[i]);
+    }
+}
+
+/* Extract: out[q][s][h][:] <- hf[q][0][h][s][:] for s < seq. */
+int64_t oracle_extract_permute(int32_t Q, int32_t H, int64_t Db,
+                               uint8_t* const* hf_planes, int64_t s_cap, int64_t seq,
+                               uint8_t* out, int nthreads)
+{
+    perm_job j;
+    memset(&j, 0, sizeof j);
+    j.rebuild = 0; j.H = H; j.Db = Db; j.s_cap = s_cap; j.seq = seq;
+    j.hf = hf_planes; j.flat = out;
+    run_perm_split(j, Q, nthreads);
+    return 0;
+}
+
+/* Rebuild: hf[q][0][h][s][:] <- in[q][s][h][:] for s < seq; s >= seq untouched. */
+int64_t oracle_rebuild_permute(int32_t Q, int32_t H, int64_t Db,
+                               const uint8_t* in, int64_t seq,
+                               uint8_t* const* hf_planes, int64_t s_cap, int nthreads)
+{
+    perm_job j;
+    memset(&j, 0, sizeof j);
+    j.rebuild = 1; j.H = H; j.Db = Db; j.s_cap = s_cap; j.seq = seq;
+    j.hf = hf_planes; j.flat = (uint8_t*)in;
+    run_perm_split(j, Q, nthreads);
+    return 0;
+}

@@ -1,0 +1,74 @@
+"""Plant a mistake in the oracle (on the CPU) and check that the pins catch it.
+
+Each mutant is a textual edit of a copy of oracle/kvx_oracle.c, compiled into a
+temporary directory and driven by the pin checks in a child process (so a
+mutant that reads or writes out of bounds and crashes counts as caught).  The
+real oracle source is never modified.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "kvx_oracle.c")
+
+MUTANTS = {
+    "row_in_page_uses_div": ("page * page_size + t % page_size", "page * page_size + t / page_size"),
+    "page_index_uses_mod": ("ids[pg_off[r] + t / page_size]", "ids[pg_off[r] + t % page_size]"),
+    "staging_drops_Q_factor": ("(j->tok_off[r] * j->Q + q * n + t)", "(j->tok_off[r] + q * n + t)"),
+    "staging_token_major": ("(j->tok_off[r] * j->Q + q * n + t)",
+                            "(j->tok_off[r] * j->Q + t * j->Q + q)"),
+    "bound_off_by_one": ("page >= num_pages", "page > num_pages"),
+    "last_token_dropped": ("for (int64_t t = 0; t < n; ++t)", "for (int64_t t = 0; t + 1 < n; ++t)"),
+    "gather_reads_plane0": ("memcpy(staged, j->src.planes[q]", "memcpy(staged, j->src.planes[0]"),
+    "gs_dst_uses_src_stride": ("memcpy(j->dst.planes[q] + d * j->dst.stride,\n"
+                               "                       j->src.planes[q]",
+                               "memcpy(j->dst.planes[q] + d * j->src.stride,\n"
+                               "                       j->src.planes[q]"),
+    "gs_ignores_dst_oor": ("if (s < 0 || d < 0)", "if (s < 0)"),
+    "hf_index_transposed": ("((int64_t)h * j->s_cap + s)", "((int64_t)s * j->H + h)"),
+    "flat_index_transposed": ("(((int64_t)q * j->seq + s) * j->H + h)",
+                              "(((int64_t)q * j->H + h) * j->seq + s)"),
+    "permute_direction_swapped": ("if (j->rebuild) memcpy(hf_row, flat_row, (size_t)j->Db);",
+                                  "if (!j->rebuild) memcpy(hf_row, flat_row, (size_t)j->Db);"),
+    "permute_runs_to_s_cap": ("for (int64_t s = 0; s < j->seq; ++s)",
+                              "for (int64_t s = 0; s < j->s_cap; ++s)"),
+    "skip_not_counted": ("if (s < 0) { ++skipped; continue; }", "if (s < 0) { continue; }"),
+}
+
+DRIVER = r"""
+import sys
+sys.path.insert(0, {root!r})
+import oracle
+oracle._lib = oracle.bind({lib!r})
+from tests import oracle_pins
+for check in oracle_pins.ALL_CHECKS:
+    try:
+        check()
+    except AssertionError:
+        print("CAUGHT", check.__name__, flush=True)
+        sys.exit(0)
+print("MISSED", flush=True)
+sys.exit(3)
+"""
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) >= 1, f"mutation site for {name} not found"
+    with tempfile.TemporaryDirectory() as tmp:
+        src = os.path.join(tmp, "mutant.c")
+        lib = os.path.join(tmp, "libmutant.so")
+        open(src, "w").write(text.replace(old, new))
+        subprocess.run(["gcc", "-O1", "-fPIC", "-shared", "-pthread", src, "-o", lib], check=True)
+        p = subprocess.run([sys.executable, "-c", DRIVER.format(root=ROOT, lib=lib)], cwd=ROOT,
+                           capture_output=True, text=True, timeout=300)
+    out = p.stdout + p.stderr
+    # caught by a pin (exit 0 after CAUGHT) or crashed on its own bad access
+    assert "MISSED" not in out, f"mutant {name} passed every pin:\n{out[-2000:]}"
+    assert p.returncode == 0 or p.returncode < 0 or "CAUGHT" in out or "Error" in out, out[-2000:]
