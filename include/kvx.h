@@ -1,0 +1,203 @@
+/*
+ * kvx.h -- C ABI of libkvx.so: paged KV-cache gather, scatter, pool-to-pool
+ * gather-scatter and the HF [1, H, S, D] <-> [S, H, D] permutes, on one
+ * MI355X (gfx950) GPU.
+ *
+ * Sources (the pages' titles and the sections each call follows):
+ *   [budget]  "穷人版 PD 分离：在消费级显卡上把 TTS 推理拆成两半" (kilerd.me,
+ *             pd-on-a-budget): "B300：让 P 直接写 D 的显存" (a kernel writes the
+ *             scattered source rows straight into D's pages) and
+ *             "5090：一个看得见所有卡的代理" (a token-paged pool leaves one
+ *             request's KV in thousands of few-KB pieces; P gathers them into
+ *             contiguous staging, D scatters them back into its pages).
+ *   [mini]    "mini-infer系统实战-18-PD 解耦：把 Prefill 和 Decode 拆进两个进程之后
+ *             发生了什么" (smarter.xin): "KV 序列化格式选择" (per-layer (k, v)
+ *             tensors [seq, kv_heads, head_dim] extracted from and rebuilt
+ *             into the HF [batch, heads, seq, dim] cache).
+ *   [survey]  "PD分离调研：从推理阶段拆分到Mooncake的KVCache中心架构"
+ *             (gentlecold.top): 6.1 (a batch of non-contiguous src/dst
+ *             transfers submitted at once), 7.4 (per-layer cache base
+ *             addresses and block length = tensor bytes / num_blocks), 7.6
+ *             (P builds src/dst/length lists from block ids and writes D's
+ *             KV blocks directly).
+ *   [distserve] "DistServe 完全拆解：拆开 Prefill 与 Decode，按 Goodput 调度大模型
+ *             推理" (pinghaoyang.com.cn): "KV Cache 跨实例传输：省下重算，付出通信"
+ *             (bytes per request = 2 x prompt length x layers x KV heads x
+ *             head dim x element bytes).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Row.    One token of one plane: kv_heads * head_dim elements, R bytes.
+ * Plane.  q = layer * num_kv + kv (kv = 0 for K, 1 for V); Q = num_layers *
+ *         num_kv planes.  Each plane of a pool is an array of slots of R
+ *         bytes: slot s of plane q starts at planes[q] + s * slot_stride
+ *         (slot_stride = R for a layer-major [slots, H, D] tensor per plane,
+ *         Q * R for a token-major pool).
+ * Pages.  A pool holds num_pages pages of page_size consecutive slots.
+ *         Token t of request r lives in page ids[pg_off[r] + t / page_size],
+ *         at slot page * page_size + t % page_size.  page_size = 1 is the
+ *         token-paged pool of [budget]; 16 is a vLLM-style block ([survey] 7.4).
+ * Staging. Request r's rows start at byte tok_off[r] * Q * R; inside it the
+ *         layout is [q][t][h][d]: the per-layer (k, v) [seq, H, D] tensors of
+ *         [mini], concatenated plane by plane, then request by request.
+ * Copy.   Every call is a bitwise copy of whole rows: dtype only fixes the
+ *         element size; NaN payloads, -0 and subnormals are preserved.
+ *
+ * Asynchrony and ownership.  Every call validates its arguments on the host,
+ * enqueues its kernel(s) on `stream` and returns without synchronising.  The
+ * library allocates nothing, keeps no state between calls (apart from a
+ * cached compute-unit count per device) and needs no memory registration: on
+ * one GPU every device pointer is usable as is.  The caller owns every buffer
+ * (pools, staging, tables, counter).  Host arrays (plane pointer lists, the
+ * structs themselves) are read only during the call.  Device inputs must stay
+ * alive and unmodified, and destination rows must not be read or reused,
+ * until the stream has passed the call: completion of the stream (an event
+ * or a synchronisation) is the only proof that every write has landed.
+ *
+ * Errors.  Argument errors return a nonzero kvx_status and enqueue nothing.
+ * KVX_E_HIP means the launch itself was refused by the HIP runtime; faults
+ * inside a kernel surface at the caller's next synchronisation, as for any
+ * HIP kernel.  There is no fallback to a slower path: an unsupported case is
+ * an error status.
+ *
+ * Out-of-range ids.  A page id < 0 or >= num_pages, a page-table index
+ * outside [0, num_ids), or a token range that contradicts total_tokens is
+ * never dereferenced: that row is skipped, its destination bytes keep their
+ * prior contents, and (when `skipped` is not NULL) the row is added to
+ * *skipped with a device atomic.  No write can land outside the destination
+ * pool or staging ([budget], failure-handling section: a late write landing
+ * in pages that were already given to another request is the failure to rule
+ * out).
+ *
+ * Preconditions the library does not check (they would need the device
+ * tables on the host): within one call the destination rows are pairwise
+ * distinct, and source and destination bytes do not overlap.  Under them the
+ * result is unique and equals the row-by-row definition above.
+ */
+#ifndef KVX_H
+#define KVX_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVX_ABI_VERSION 1
+
+typedef enum kvx_status {
+    KVX_OK = 0,
+    KVX_E_NULL = 1,         /* a required pointer (struct, plane, table, buffer) is NULL */
+    KVX_E_SHAPE = 2,        /* counts or sizes are negative, inconsistent or too small */
+    KVX_E_ALIGN = 3,        /* a plane base, stride, buffer or row size is not a multiple of 16 B */
+    KVX_E_DTYPE = 4,        /* unknown kvx_dtype code */
+    KVX_E_RANGE = 5,        /* a size beyond what one call supports (see each limit below) */
+    KVX_E_UNSUPPORTED = 6,  /* a valid request this build does not implement */
+    KVX_E_HIP = 7           /* the HIP runtime refused a launch or a device query */
+} kvx_status;
+
+typedef enum kvx_dtype {
+    KVX_F16 = 1,            /* 2-byte elements */
+    KVX_BF16 = 2,           /* 2-byte elements */
+    KVX_FP8 = 3,            /* 1-byte elements */
+    KVX_F32 = 4             /* 4-byte elements */
+} kvx_dtype;
+
+/* Row shape of a KV cache ([distserve] byte formula; [mini] tensor shapes).
+ * R = kv_heads * head_dim * element size must be a multiple of 16 bytes and
+ * at most 65536; Q = num_layers * num_kv. */
+typedef struct kvx_layout {
+    int32_t num_layers;     /* >= 1 */
+    int32_t num_kv;         /* 2 for separate K and V planes, 1 for one latent plane per layer */
+    int32_t kv_heads;       /* >= 1 */
+    int32_t head_dim;       /* >= 1 */
+    int32_t dtype;          /* a kvx_dtype */
+} kvx_layout;
+
+/* A paged pool ([survey] 7.4: per-layer cache base addresses, each cut into
+ * num_blocks equal blocks).  planes is a HOST array of Q DEVICE pointers,
+ * each 16-byte aligned and addressing at least
+ * (num_pages * page_size - 1) * slot_stride + R bytes. */
+typedef struct kvx_pool {
+    void* const* planes;
+    int64_t num_pages;      /* >= 0 */
+    int32_t page_size;      /* tokens per page, >= 1 */
+    int64_t slot_stride;    /* bytes between consecutive slots of a plane, >= R, multiple of 16 */
+} kvx_pool;
+
+/* A batch of requests: request r owns tokens [tok_off[r], tok_off[r+1]) of the
+ * batch.  tok_off is a DEVICE array of num_reqs + 1 int64 values with
+ * tok_off[0] = 0, non-decreasing, tok_off[num_reqs] = total_tokens (a host
+ * copy of the last entry, used for sizing the launch).  Empty requests are
+ * allowed. */
+typedef struct kvx_reqs {
+    int32_t num_reqs;       /* >= 0 */
+    int64_t total_tokens;   /* >= 0 */
+    const int64_t* tok_off; /* DEVICE [num_reqs + 1] */
+} kvx_reqs;
+
+/* Where a batch's tokens live in one pool ([survey] 7.5/7.6: per-request
+ * block id lists).  Request r's page ids are page_ids[pg_off[r] ..
+ * pg_off[r+1]); it needs at least ceil(n_r / page_size) of them. */
+typedef struct kvx_table {
+    const int64_t* pg_off;   /* DEVICE [num_reqs + 1] */
+    const int32_t* page_ids; /* DEVICE [num_ids] */
+    int64_t num_ids;         /* host: length of page_ids (reads never go past it) */
+} kvx_table;
+
+/* Gather ([budget] 5090 section; [survey] 6.1): copy every row of every
+ * request, all Q planes, from pool `src` into contiguous staging laid out as
+ * described above.  staging_bytes must be >= total_tokens * Q * R.  Staging
+ * rows of skipped tokens keep their prior contents.  One launch for the whole
+ * batch (two or more only when Q > 128). */
+kvx_status kvx_gather(const kvx_layout* layout, const kvx_pool* src, const kvx_table* src_table,
+                      const kvx_reqs* reqs, void* staging, int64_t staging_bytes,
+                      unsigned long long* skipped, hipStream_t stream);
+
+/* Scatter ([budget] 5090 section): the inverse of kvx_gather -- copy staging
+ * rows into pool `dst` at the slots of dst_table.  Every destination byte
+ * outside the written rows (other slots, the unused rows of a partly filled
+ * last page) is left untouched. */
+kvx_status kvx_scatter(const kvx_layout* layout, const void* staging, int64_t staging_bytes,
+                       const kvx_reqs* reqs, const kvx_pool* dst, const kvx_table* dst_table,
+                       unsigned long long* skipped, hipStream_t stream);
+
+/* Gather-scatter ([budget] B300 section; [survey] 7.6): copy each row of pool
+ * `src` at its src_table slot directly to pool `dst` at its dst_table slot,
+ * with no staging.  Both tables index the same request batch; the two pools
+ * may differ in page size and slot stride, not in layout. */
+kvx_status kvx_gather_scatter(const kvx_layout* layout,
+                              const kvx_pool* src, const kvx_table* src_table,
+                              const kvx_reqs* reqs,
+                              const kvx_pool* dst, const kvx_table* dst_table,
+                              unsigned long long* skipped, hipStream_t stream);
+
+/* Extract permute ([mini]): for each plane q, hf_planes[q] is a DEVICE
+ * [1][H][s_cap][D] tensor (batch 1, contiguous); write
+ * out[q][s][h][:] = hf_planes[q][0][h][s][:] for s < seq_len.  out is a
+ * contiguous DEVICE [Q][seq_len][H][D] buffer of out_bytes >= Q * seq_len * R
+ * bytes.  Requires seq_len <= s_cap and head_dim * element size a multiple of
+ * 16 bytes.  hf_planes is a HOST array of Q DEVICE pointers. */
+kvx_status kvx_extract_permute(const kvx_layout* layout, const void* const* hf_planes,
+                               int64_t s_cap, int64_t seq_len,
+                               void* out, int64_t out_bytes, hipStream_t stream);
+
+/* Rebuild permute ([mini]): the inverse of extract --
+ * hf_planes[q][0][h][s][:] = in[q][s][h][:] for s < seq_len; positions
+ * s >= seq_len keep their prior contents. */
+kvx_status kvx_rebuild_permute(const kvx_layout* layout, const void* in, int64_t in_bytes,
+                               int64_t seq_len, void* const* hf_planes, int64_t s_cap,
+                               hipStream_t stream);
+
+/* Static string naming a status code (never NULL). */
+const char* kvx_status_str(kvx_status status);
+
+/* KVX_ABI_VERSION of the built library. */
+int32_t kvx_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVX_H */

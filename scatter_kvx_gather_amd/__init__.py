@@ -1,0 +1,256 @@
+"""kvx: paged KV-cache gather / scatter / gather-scatter and the HF
+[1, H, S, D] <-> [S, H, D] permutes on one MI355X (gfx950).
+
+A thin ctypes binding over ``libkvx.so`` (C ABI and contract: include/kvx.h).
+It only marshals arguments -- torch tensors become device pointers and sizes,
+streams become ``hipStream_t`` handles -- and every byte is moved by the HIP
+kernels in the library.  PyTorch is used for device memory and streams only.
+
+There is no CPU fallback: if the library is missing or a call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Union
+
+import torch
+
+__all__ = ["KvxError", "Layout", "Pool", "Requests", "Table", "gather", "scatter",
+           "gather_scatter", "extract_permute", "rebuild_permute", "library_path",
+           "DTYPE_CODES", "load_library"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkvx.so")
+_lib = None
+
+DTYPE_CODES = {"f16": 1, "bf16": 2, "fp8": 3, "f32": 4}
+_ELEM = {"f16": 2, "bf16": 2, "fp8": 1, "f32": 4}
+
+
+class KvxError(RuntimeError):
+    """A kvx call returned a nonzero status (nothing was enqueued)."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_status_str(status)} (status {status})")
+
+
+class _CLayout(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_kv", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class _CPool(ctypes.Structure):
+    _fields_ = [("planes", ctypes.POINTER(ctypes.c_void_p)), ("num_pages", ctypes.c_int64),
+                ("page_size", ctypes.c_int32), ("slot_stride", ctypes.c_int64)]
+
+
+class _CReqs(ctypes.Structure):
+    _fields_ = [("num_reqs", ctypes.c_int32), ("total_tokens", ctypes.c_int64),
+                ("tok_off", ctypes.c_void_p)]
+
+
+class _CTable(ctypes.Structure):
+    _fields_ = [("pg_off", ctypes.c_void_p), ("page_ids", ctypes.c_void_p),
+                ("num_ids", ctypes.c_int64)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Open libkvx.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, p64, vp = ctypes.POINTER, ctypes.c_int64, ctypes.c_void_p
+    lib.kvx_gather.argtypes = [P(_CLayout), P(_CPool), P(_CTable), P(_CReqs), vp, p64, vp, vp]
+    lib.kvx_scatter.argtypes = [P(_CLayout), vp, p64, P(_CReqs), P(_CPool), P(_CTable), vp, vp]
+    lib.kvx_gather_scatter.argtypes = [P(_CLayout), P(_CPool), P(_CTable), P(_CReqs),
+                                       P(_CPool), P(_CTable), vp, vp]
+    lib.kvx_extract_permute.argtypes = [P(_CLayout), P(vp), p64, p64, vp, p64, vp]
+    lib.kvx_rebuild_permute.argtypes = [P(_CLayout), vp, p64, p64, P(vp), p64, vp]
+    for f in (lib.kvx_gather, lib.kvx_scatter, lib.kvx_gather_scatter,
+              lib.kvx_extract_permute, lib.kvx_rebuild_permute):
+        f.restype = ctypes.c_int
+    lib.kvx_status_str.argtypes = [ctypes.c_int]
+    lib.kvx_status_str.restype = ctypes.c_char_p
+    lib.kvx_abi_version.argtypes = []
+    lib.kvx_abi_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def _status_str(status: int) -> str:
+    try:
+        return load_library().kvx_status_str(status).decode()
+    except Exception:  # noqa: BLE001 -- only used to format an error message
+        return "unknown"
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise KvxError(status, what)
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    raise TypeError(f"expected a tensor or a device pointer, got {type(x)}")
+
+
+def _nbytes(x) -> int:
+    return x.numel() * x.element_size() if isinstance(x, torch.Tensor) else 0
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+class Layout:
+    """Row shape: Q = num_layers * num_kv planes of kv_heads x head_dim elements."""
+
+    def __init__(self, num_layers: int, num_kv: int, kv_heads: int, head_dim: int,
+                 dtype: str = "bf16"):
+        if dtype not in DTYPE_CODES:
+            raise ValueError(f"dtype must be one of {sorted(DTYPE_CODES)}")
+        self.num_layers, self.num_kv, self.kv_heads, self.head_dim = (
+            num_layers, num_kv, kv_heads, head_dim)
+        self.dtype = dtype
+        self._c = _CLayout(num_layers, num_kv, kv_heads, head_dim, DTYPE_CODES[dtype])
+
+    @property
+    def planes(self) -> int:
+        return self.num_layers * self.num_kv
+
+    @property
+    def row_bytes(self) -> int:
+        return self.kv_heads * self.head_dim * _ELEM[self.dtype]
+
+
+def _plane_array(planes) -> ctypes.Array:
+    if isinstance(planes, torch.Tensor):
+        ptrs = [planes[q].data_ptr() for q in range(planes.shape[0])]
+    else:
+        ptrs = [_ptr(p) for p in planes]
+    arr = (ctypes.c_void_p * max(len(ptrs), 1))()
+    for i, p in enumerate(ptrs):
+        arr[i] = p
+    return arr
+
+
+class Pool:
+    """A paged pool: Q plane base pointers, num_pages pages of page_size slots.
+
+    ``planes`` is a device tensor whose first dimension indexes planes (each
+    ``planes[q]`` starting at slot 0), or a sequence of tensors / device
+    pointers, one per plane.  ``slot_stride`` defaults to the row size.
+    The pool keeps references to its tensors; the caller keeps them unchanged
+    until the stream has passed every call that uses them.
+    """
+
+    def __init__(self, planes: Union[torch.Tensor, Sequence], num_pages: int,
+                 page_size: int = 1, slot_stride: Optional[int] = None,
+                 row_bytes: Optional[int] = None):
+        self._keep = planes
+        self._arr = _plane_array(planes)
+        self.num_planes = planes.shape[0] if isinstance(planes, torch.Tensor) else len(planes)
+        if slot_stride is None:
+            if row_bytes is None:
+                if not isinstance(planes, torch.Tensor):
+                    raise ValueError("slot_stride or row_bytes is needed for pointer lists")
+                row_bytes = planes[0].numel() * planes.element_size() // (num_pages * page_size)
+            slot_stride = row_bytes
+        self.num_pages, self.page_size, self.slot_stride = num_pages, page_size, slot_stride
+        self._c = _CPool(ctypes.cast(self._arr, ctypes.POINTER(ctypes.c_void_p)), num_pages,
+                         page_size, slot_stride)
+
+
+class Requests:
+    """A batch: device int64 ``tok_off`` [num_reqs + 1] and its last entry."""
+
+    def __init__(self, tok_off: torch.Tensor, total_tokens: int):
+        if tok_off.dtype != torch.int64 or tok_off.dim() != 1:
+            raise ValueError("tok_off must be a 1-D int64 tensor")
+        self.tok_off = tok_off
+        self.num_reqs = tok_off.numel() - 1
+        self.total_tokens = int(total_tokens)
+        self._c = _CReqs(self.num_reqs, self.total_tokens, _ptr(tok_off))
+
+
+class Table:
+    """Per-request page ids in one pool: device int64 ``pg_off`` and int32 ids."""
+
+    def __init__(self, pg_off: torch.Tensor, page_ids: torch.Tensor):
+        if pg_off.dtype != torch.int64 or page_ids.dtype != torch.int32:
+            raise ValueError("pg_off must be int64 and page_ids int32")
+        self.pg_off, self.page_ids = pg_off, page_ids
+        self._c = _CTable(_ptr(pg_off), _ptr(page_ids) if page_ids.numel() else 0,
+                          page_ids.numel())
+
+
+def gather(layout: Layout, src: Pool, src_table: Table, reqs: Requests, staging: torch.Tensor,
+           skipped: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Pool -> contiguous staging [request][plane][token][H][D] (kvx_gather)."""
+    lib = load_library()
+    _check(lib.kvx_gather(ctypes.byref(layout._c), ctypes.byref(src._c),
+                          ctypes.byref(src_table._c), ctypes.byref(reqs._c), _ptr(staging),
+                          _nbytes(staging), _ptr(skipped), _stream(stream)), "kvx_gather")
+
+
+def scatter(layout: Layout, staging: torch.Tensor, reqs: Requests, dst: Pool, dst_table: Table,
+            skipped: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Contiguous staging -> pool (kvx_scatter)."""
+    lib = load_library()
+    _check(lib.kvx_scatter(ctypes.byref(layout._c), _ptr(staging), _nbytes(staging),
+                           ctypes.byref(reqs._c), ctypes.byref(dst._c),
+                           ctypes.byref(dst_table._c), _ptr(skipped), _stream(stream)),
+           "kvx_scatter")
+
+
+def gather_scatter(layout: Layout, src: Pool, src_table: Table, reqs: Requests, dst: Pool,
+                   dst_table: Table, skipped: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+    """Pool -> pool, row by row, no staging (kvx_gather_scatter)."""
+    lib = load_library()
+    _check(lib.kvx_gather_scatter(ctypes.byref(layout._c), ctypes.byref(src._c),
+                                  ctypes.byref(src_table._c), ctypes.byref(reqs._c),
+                                  ctypes.byref(dst._c), ctypes.byref(dst_table._c),
+                                  _ptr(skipped), _stream(stream)), "kvx_gather_scatter")
+
+
+def extract_permute(layout: Layout, hf_planes: Union[torch.Tensor, Sequence], s_cap: int,
+                    seq_len: int, out: torch.Tensor, stream=None) -> None:
+    """[1, H, s_cap, D] per plane -> out [Q][seq_len][H][D] (kvx_extract_permute)."""
+    lib = load_library()
+    arr = _plane_array(hf_planes)
+    _check(lib.kvx_extract_permute(ctypes.byref(layout._c),
+                                   ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), s_cap,
+                                   seq_len, _ptr(out), _nbytes(out), _stream(stream)),
+           "kvx_extract_permute")
+
+
+def rebuild_permute(layout: Layout, flat: torch.Tensor, seq_len: int,
+                    hf_planes: Union[torch.Tensor, Sequence], s_cap: int, stream=None) -> None:
+    """flat [Q][seq_len][H][D] -> [1, H, s_cap, D] per plane (kvx_rebuild_permute)."""
+    lib = load_library()
+    arr = _plane_array(hf_planes)
+    _check(lib.kvx_rebuild_permute(ctypes.byref(layout._c), _ptr(flat), _nbytes(flat), seq_len,
+                                   ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), s_cap,
+                                   _stream(stream)), "kvx_rebuild_permute")

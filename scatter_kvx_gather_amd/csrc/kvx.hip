@@ -1,0 +1,430 @@
+// kvx.hip -- host side of libkvx.so: argument validation, variant dispatch and
+// one launch per call on the caller's stream.  The C ABI and its contract are
+// declared and documented in include/kvx.h.
+#include "kvx.h"
+#include "kvx_kernels.hpp"
+
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <type_traits>
+
+using namespace kvx;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxRowBytes = 65536;
+
+std::atomic<int> g_cus[kMaxDevices];
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char* e = std::getenv("KVX_LOG");
+        return e != nullptr && e[0] == '1';
+    }();
+    return on;
+}
+
+// Workgroups per compute unit for the persistent grid (KVX_BLOCKS_PER_CU
+// overrides; 0 = one wave per chunk, no grid-stride reuse).
+int blocks_per_cu() {
+    static const int n = [] {
+        const char* e = std::getenv("KVX_BLOCKS_PER_CU");
+        if (e == nullptr) return 8;
+        int v = std::atoi(e);
+        return v < 0 ? 8 : v;
+    }();
+    return n;
+}
+
+kvx_status device_cus(int* cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KVX_E_HIP;
+    if (dev >= 0 && dev < kMaxDevices) {
+        int n = g_cus[dev].load(std::memory_order_relaxed);
+        if (n > 0) { *cus = n; return KVX_OK; }
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        return KVX_E_HIP;
+    if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(n, std::memory_order_relaxed);
+    *cus = n;
+    return KVX_OK;
+}
+
+int elem_bytes(int32_t dtype) {
+    switch (dtype) {
+        case KVX_F16: case KVX_BF16: return 2;
+        case KVX_FP8: return 1;
+        case KVX_F32: return 4;
+        default: return 0;
+    }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// a * b into *out, false on int64 overflow (a, b >= 0).
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a < 0 || b < 0) return false;
+    return !__builtin_mul_overflow(a, b, out);
+}
+
+struct Geom {
+    int32_t Q;
+    int64_t R;       // row bytes
+    int64_t Db;      // head_dim * element size
+    int32_t H;
+};
+
+kvx_status check_layout(const kvx_layout* l, Geom* g) {
+    if (l == nullptr) return KVX_E_NULL;
+    const int eb = elem_bytes(l->dtype);
+    if (eb == 0) return KVX_E_DTYPE;
+    if (l->num_layers < 1 || l->num_kv < 1 || l->num_kv > 2 || l->kv_heads < 1 ||
+        l->head_dim < 1)
+        return KVX_E_SHAPE;
+    int64_t Q = static_cast<int64_t>(l->num_layers) * l->num_kv;
+    int64_t Db = static_cast<int64_t>(l->head_dim) * eb;
+    int64_t R = Db * l->kv_heads;
+    if (Q > (1 << 20)) return KVX_E_RANGE;
+    if (R > kMaxRowBytes) return KVX_E_RANGE;
+    if (R % 16 != 0) return KVX_E_ALIGN;
+    g->Q = static_cast<int32_t>(Q);
+    g->R = R;
+    g->Db = Db;
+    g->H = l->kv_heads;
+    return KVX_OK;
+}
+
+kvx_status check_pool(const kvx_pool* p, const Geom& g) {
+    if (p == nullptr || p->planes == nullptr) return KVX_E_NULL;
+    if (p->num_pages < 0 || p->page_size < 1 || p->slot_stride < g.R) return KVX_E_SHAPE;
+    if (p->slot_stride % 16 != 0) return KVX_E_ALIGN;
+    int64_t slots = 0, bytes = 0;
+    if (!mul_ok(p->num_pages, p->page_size, &slots) || !mul_ok(slots, p->slot_stride, &bytes))
+        return KVX_E_RANGE;
+    for (int32_t q = 0; q < g.Q; ++q) {
+        if (p->planes[q] == nullptr) return KVX_E_NULL;
+        if (!aligned16(p->planes[q])) return KVX_E_ALIGN;
+    }
+    return KVX_OK;
+}
+
+kvx_status check_reqs(const kvx_reqs* r) {
+    if (r == nullptr) return KVX_E_NULL;
+    if (r->num_reqs < 0 || r->total_tokens < 0) return KVX_E_SHAPE;
+    if (r->num_reqs == 0 && r->total_tokens != 0) return KVX_E_SHAPE;
+    if (r->num_reqs > 0 && r->tok_off == nullptr) return KVX_E_NULL;
+    if (r->total_tokens >= (int64_t(1) << 31)) return KVX_E_RANGE;
+    return KVX_OK;
+}
+
+kvx_status check_table(const kvx_table* t, const kvx_reqs* r) {
+    if (t == nullptr) return KVX_E_NULL;
+    if (t->num_ids < 0) return KVX_E_SHAPE;
+    if (r->num_reqs > 0 && t->pg_off == nullptr) return KVX_E_NULL;
+    if (t->num_ids > 0 && t->page_ids == nullptr) return KVX_E_NULL;
+    return KVX_OK;
+}
+
+void fill_pool_ref(PoolRef* ref, const kvx_pool* p, const kvx_table* t, int32_t q0, int32_t nq) {
+    std::memset(ref, 0, sizeof(*ref));
+    for (int32_t i = 0; i < nq; ++i) ref->plane[i] = static_cast<char*>(p->planes[q0 + i]);
+    ref->stride = p->slot_stride;
+    ref->num_pages = p->num_pages;
+    ref->pg_off = t->pg_off;
+    ref->ids = t->page_ids;
+    ref->num_ids = t->num_ids;
+    ref->page_size = p->page_size;
+    int shift = -1;
+    if ((p->page_size & (p->page_size - 1)) == 0) {
+        shift = 0;
+        while ((1 << shift) < p->page_size) ++shift;
+    }
+    ref->page_shift = shift;
+}
+
+// Chunk shape for a unit size: (VPL, U) for the wide copy, VPL = 0 for flat.
+struct Shape {
+    int vpl;
+    uint32_t U;
+};
+
+Shape shape_for(int64_t unit_bytes) {
+    if (unit_bytes % 1024 == 0) {
+        int64_t vpl = unit_bytes / 1024;
+        if (vpl == 1 || vpl == 2 || vpl == 4 || vpl == 8 || vpl == 16)
+            return {static_cast<int>(vpl), static_cast<uint32_t>(16 / vpl)};
+    }
+    int64_t u = kChunkBytes / unit_bytes;
+    if (u < 1) u = 1;
+    if (u > kWave) u = kWave;
+    return {0, static_cast<uint32_t>(u)};
+}
+
+// Fill the shape-dependent fields of Common; false if the chunk count overflows.
+bool set_chunks(Common* c, const Shape& sh, uint32_t units_per_plane, int32_t nq) {
+    c->U = sh.U;
+    c->units_per_plane = units_per_plane;
+    c->chunks_per_plane = (units_per_plane + sh.U - 1) / sh.U;
+    uint64_t n = static_cast<uint64_t>(c->chunks_per_plane) * static_cast<uint64_t>(nq);
+    if (n >= (uint64_t(1) << 31)) return false;
+    c->nchunks = static_cast<uint32_t>(n);
+    c->V = static_cast<uint32_t>(c->R / 16);
+    c->v_magic = c->V == 1 ? 0u
+                           : static_cast<uint32_t>(((uint64_t(1) << 32) + c->V - 1) / c->V);
+    return true;
+}
+
+uint32_t grid_for(uint32_t nchunks, int cus) {
+    uint64_t need = (static_cast<uint64_t>(nchunks) + kWavesPerBlock - 1) / kWavesPerBlock;
+    uint64_t g = need;
+    int bpc = blocks_per_cu();
+    if (bpc > 0) {
+        uint64_t cap = static_cast<uint64_t>(cus) * bpc;
+        if (g > cap) g = cap;
+    }
+    if (g >= kXcds) g = (g + kXcds - 1) / kXcds * kXcds;   // XCD renumbering needs G % 8 == 0
+    if (g < 1) g = 1;
+    return static_cast<uint32_t>(g);
+}
+
+template <class Args>
+kvx_status launch(const void* fn, uint32_t grid, Args& a, hipStream_t stream) {
+    void* params[] = {&a};
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kBlock), params, 0, stream);
+    return e == hipSuccess ? KVX_OK : KVX_E_HIP;
+}
+
+template <class Src, class Dst>
+const void* paged_kernel(int vpl) {
+    switch (vpl) {
+        case 1: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, 16>);
+        case 2: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 2, 8>);
+        case 4: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 4, 4>);
+        case 8: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 8, 2>);
+        case 16: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 16, 1>);
+        default: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 0, 0>);
+    }
+}
+
+template <bool REBUILD>
+const void* permute_kernel(int vpl) {
+    switch (vpl) {
+        case 1: return reinterpret_cast<const void*>(&k_permute<REBUILD, 1, 16>);
+        case 2: return reinterpret_cast<const void*>(&k_permute<REBUILD, 2, 8>);
+        case 4: return reinterpret_cast<const void*>(&k_permute<REBUILD, 4, 4>);
+        case 8: return reinterpret_cast<const void*>(&k_permute<REBUILD, 8, 2>);
+        case 16: return reinterpret_cast<const void*>(&k_permute<REBUILD, 16, 1>);
+        default: return reinterpret_cast<const void*>(&k_permute<REBUILD, 0, 0>);
+    }
+}
+
+const char* op_name(int op) {
+    static const char* names[] = {"gather", "scatter", "gather_scatter"};
+    return names[op];
+}
+
+// Shared body of the three paged calls.  Exactly one of (src pool, staging
+// source) and one of (dst pool, staging destination) is set.
+template <class Src, class Dst>
+kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
+                     const kvx_pool* src, const kvx_table* st, void* src_stage,
+                     const kvx_pool* dst, const kvx_table* dt, void* dst_stage,
+                     unsigned long long* skipped, hipStream_t stream) {
+    if (reqs->total_tokens == 0) return KVX_OK;           // nothing to move
+    int cus = 0;
+    kvx_status s = device_cus(&cus);
+    if (s != KVX_OK) return s;
+    const Shape sh = shape_for(g.R);
+    for (int32_t q0 = 0; q0 < g.Q; q0 += kTab) {
+        const int32_t nq = g.Q - q0 < kTab ? g.Q - q0 : kTab;
+        PagedArgs<Src, Dst> a;
+        std::memset(&a, 0, sizeof(a));
+        a.c.tok_off = reqs->tok_off;
+        a.c.skipped = skipped;
+        a.c.T = reqs->total_tokens;
+        a.c.num_reqs = reqs->num_reqs;
+        a.c.q0 = q0;
+        a.c.Q = g.Q;
+        a.c.R = static_cast<int32_t>(g.R);
+        if (!set_chunks(&a.c, sh, static_cast<uint32_t>(reqs->total_tokens), nq))
+            return KVX_E_RANGE;
+        if constexpr (std::is_same<Src, PoolRef>::value) fill_pool_ref(&a.src, src, st, q0, nq);
+        else a.src.base = static_cast<char*>(src_stage);
+        if constexpr (std::is_same<Dst, PoolRef>::value) fill_pool_ref(&a.dst, dst, dt, q0, nq);
+        else a.dst.base = static_cast<char*>(dst_stage);
+        const uint32_t grid = grid_for(a.c.nchunks, cus);
+        if (log_enabled())
+            std::fprintf(stderr,
+                         "kvx: %s Q=%d planes[%d,%d) R=%lld T=%lld reqs=%d copy=%s U=%u "
+                         "chunks=%u grid=%u\n",
+                         op_name(op), g.Q, q0, q0 + nq, static_cast<long long>(g.R),
+                         static_cast<long long>(reqs->total_tokens), reqs->num_reqs,
+                         sh.vpl ? "wide" : "flat", sh.U, a.c.nchunks, grid);
+        s = launch(paged_kernel<Src, Dst>(sh.vpl), grid, a, stream);
+        if (s != KVX_OK) return s;
+    }
+    return KVX_OK;
+}
+
+template <bool REBUILD>
+kvx_status run_permute(const Geom& g, void* const* hf, int64_t s_cap, int64_t seq, void* flat,
+                       hipStream_t stream) {
+    if (seq == 0) return KVX_OK;
+    int cus = 0;
+    kvx_status s = device_cus(&cus);
+    if (s != KVX_OK) return s;
+    const Shape sh = shape_for(g.Db);
+    for (int32_t q0 = 0; q0 < g.Q; q0 += kTab) {
+        const int32_t nq = g.Q - q0 < kTab ? g.Q - q0 : kTab;
+        PermuteArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.c.T = seq;
+        a.c.q0 = q0;
+        a.c.Q = g.Q;
+        a.c.R = static_cast<int32_t>(g.Db);
+        if (!set_chunks(&a.c, sh, static_cast<uint32_t>(seq * g.H), nq)) return KVX_E_RANGE;
+        for (int32_t i = 0; i < nq; ++i) a.hf[i] = static_cast<char*>(hf[q0 + i]);
+        a.flat = static_cast<char*>(flat);
+        a.s_cap = s_cap;
+        a.H = g.H;
+        const uint32_t grid = grid_for(a.c.nchunks, cus);
+        if (log_enabled())
+            std::fprintf(stderr,
+                         "kvx: %s Q=%d planes[%d,%d) H=%d Db=%lld seq=%lld s_cap=%lld copy=%s "
+                         "U=%u chunks=%u grid=%u\n",
+                         REBUILD ? "rebuild" : "extract", g.Q, q0, q0 + nq, g.H,
+                         static_cast<long long>(g.Db), static_cast<long long>(seq),
+                         static_cast<long long>(s_cap), sh.vpl ? "wide" : "flat", sh.U,
+                         a.c.nchunks, grid);
+        s = launch(permute_kernel<REBUILD>(sh.vpl), grid, a, stream);
+        if (s != KVX_OK) return s;
+    }
+    return KVX_OK;
+}
+
+kvx_status check_staging(const void* p, int64_t bytes, const Geom& g, const kvx_reqs* r) {
+    int64_t need = 0;
+    if (!mul_ok(r->total_tokens, static_cast<int64_t>(g.Q) * g.R, &need)) return KVX_E_RANGE;
+    if (need > 0 && p == nullptr) return KVX_E_NULL;
+    if (!aligned16(p)) return KVX_E_ALIGN;
+    if (bytes < need) return KVX_E_SHAPE;
+    return KVX_OK;
+}
+
+kvx_status check_hf(const Geom& g, const void* const* hf, int64_t s_cap, int64_t seq) {
+    if (hf == nullptr) return KVX_E_NULL;
+    if (s_cap < 0 || seq < 0 || seq > s_cap) return KVX_E_SHAPE;
+    if (g.Db % 16 != 0) return KVX_E_ALIGN;
+    if (seq * static_cast<int64_t>(g.H) >= (int64_t(1) << 31)) return KVX_E_RANGE;
+    int64_t plane_bytes = 0;
+    if (!mul_ok(s_cap * g.H, g.Db, &plane_bytes)) return KVX_E_RANGE;
+    for (int32_t q = 0; q < g.Q; ++q) {
+        if (hf[q] == nullptr) return KVX_E_NULL;
+        if (!aligned16(hf[q])) return KVX_E_ALIGN;
+    }
+    return KVX_OK;
+}
+
+#define KVX_TRY(expr)                         \
+    do {                                      \
+        kvx_status _s = (expr);               \
+        if (_s != KVX_OK) return _s;          \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+kvx_status kvx_gather(const kvx_layout* layout, const kvx_pool* src, const kvx_table* src_table,
+                      const kvx_reqs* reqs, void* staging, int64_t staging_bytes,
+                      unsigned long long* skipped, hipStream_t stream) {
+    Geom g;
+    KVX_TRY(check_layout(layout, &g));
+    KVX_TRY(check_reqs(reqs));
+    KVX_TRY(check_pool(src, g));
+    KVX_TRY(check_table(src_table, reqs));
+    KVX_TRY(check_staging(staging, staging_bytes, g, reqs));
+    return run_paged<PoolRef, StageRef>(0, g, reqs, src, src_table, nullptr, nullptr, nullptr,
+                                        staging, skipped, stream);
+}
+
+kvx_status kvx_scatter(const kvx_layout* layout, const void* staging, int64_t staging_bytes,
+                       const kvx_reqs* reqs, const kvx_pool* dst, const kvx_table* dst_table,
+                       unsigned long long* skipped, hipStream_t stream) {
+    Geom g;
+    KVX_TRY(check_layout(layout, &g));
+    KVX_TRY(check_reqs(reqs));
+    KVX_TRY(check_pool(dst, g));
+    KVX_TRY(check_table(dst_table, reqs));
+    KVX_TRY(check_staging(staging, staging_bytes, g, reqs));
+    return run_paged<StageRef, PoolRef>(1, g, reqs, nullptr, nullptr, const_cast<void*>(staging),
+                                        dst, dst_table, nullptr, skipped, stream);
+}
+
+kvx_status kvx_gather_scatter(const kvx_layout* layout,
+                              const kvx_pool* src, const kvx_table* src_table,
+                              const kvx_reqs* reqs,
+                              const kvx_pool* dst, const kvx_table* dst_table,
+                              unsigned long long* skipped, hipStream_t stream) {
+    Geom g;
+    KVX_TRY(check_layout(layout, &g));
+    KVX_TRY(check_reqs(reqs));
+    KVX_TRY(check_pool(src, g));
+    KVX_TRY(check_table(src_table, reqs));
+    KVX_TRY(check_pool(dst, g));
+    KVX_TRY(check_table(dst_table, reqs));
+    return run_paged<PoolRef, PoolRef>(2, g, reqs, src, src_table, nullptr, dst, dst_table,
+                                       nullptr, skipped, stream);
+}
+
+kvx_status kvx_extract_permute(const kvx_layout* layout, const void* const* hf_planes,
+                               int64_t s_cap, int64_t seq_len, void* out, int64_t out_bytes,
+                               hipStream_t stream) {
+    Geom g;
+    KVX_TRY(check_layout(layout, &g));
+    KVX_TRY(check_hf(g, hf_planes, s_cap, seq_len));
+    int64_t need = 0;
+    if (!mul_ok(seq_len, static_cast<int64_t>(g.Q) * g.R, &need)) return KVX_E_RANGE;
+    if (need > 0 && out == nullptr) return KVX_E_NULL;
+    if (!aligned16(out)) return KVX_E_ALIGN;
+    if (out_bytes < need) return KVX_E_SHAPE;
+    return run_permute<false>(g, const_cast<void* const*>(hf_planes), s_cap, seq_len, out,
+                              stream);
+}
+
+kvx_status kvx_rebuild_permute(const kvx_layout* layout, const void* in, int64_t in_bytes,
+                               int64_t seq_len, void* const* hf_planes, int64_t s_cap,
+                               hipStream_t stream) {
+    Geom g;
+    KVX_TRY(check_layout(layout, &g));
+    KVX_TRY(check_hf(g, hf_planes, s_cap, seq_len));
+    int64_t need = 0;
+    if (!mul_ok(seq_len, static_cast<int64_t>(g.Q) * g.R, &need)) return KVX_E_RANGE;
+    if (need > 0 && in == nullptr) return KVX_E_NULL;
+    if (!aligned16(in)) return KVX_E_ALIGN;
+    if (in_bytes < need) return KVX_E_SHAPE;
+    return run_permute<true>(g, hf_planes, s_cap, seq_len, const_cast<void*>(in), stream);
+}
+
+const char* kvx_status_str(kvx_status status) {
+    switch (status) {
+        case KVX_OK: return "KVX_OK";
+        case KVX_E_NULL: return "KVX_E_NULL: a required pointer is NULL";
+        case KVX_E_SHAPE: return "KVX_E_SHAPE: counts or sizes are negative, inconsistent or too small";
+        case KVX_E_ALIGN: return "KVX_E_ALIGN: a base, stride, buffer or row size is not a multiple of 16 bytes";
+        case KVX_E_DTYPE: return "KVX_E_DTYPE: unknown dtype code";
+        case KVX_E_RANGE: return "KVX_E_RANGE: a size exceeds what one call supports";
+        case KVX_E_UNSUPPORTED: return "KVX_E_UNSUPPORTED: not implemented by this build";
+        case KVX_E_HIP: return "KVX_E_HIP: the HIP runtime refused a launch or a device query";
+        default: return "unknown kvx_status";
+    }
+}
+
+int32_t kvx_abi_version(void) { return KVX_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,368 @@
+// kvx_kernels.hpp -- HIP kernels (gfx950 / CDNA4) behind libkvx.so.
+//
+// All five calls are one row-moving kernel with a different address
+// resolver.  The work of a call is split into chunks of U units (a unit is
+// one row of R bytes, or one head row of head_dim elements for the permutes),
+// each chunk sized to about 16 KiB.  A wave takes one chunk at a time:
+//
+//   1. resolve: lane u < U computes unit u's source and destination byte
+//      addresses from the tables (token -> request by a search over tok_off,
+//      page id lookup, bounds checks) and a status: copy, skip (out of range),
+//      or none (past the end);
+//   2. copy: every 16-byte vector of the chunk's rows is loaded with a
+//      nontemporal dwordx4 load (all loads of the chunk are issued before the
+//      first store), then stored with a nontemporal dwordx4 store.
+//
+// Rows of 1, 2, 4, 8 or 16 KiB use the "wide" copy: the row addresses are
+// broadcast into scalar registers (readlane) and each lane moves 16 bytes at
+// lane*16 + v*1024 of every row, so all 64 lanes of an instruction cover one
+// contiguous 1 KiB of one row.  Other row sizes use the "flat" copy: the
+// chunk's U*V vectors (V = R/16) are numbered and dealt round-robin to lanes,
+// and each lane fetches its row's addresses from the resolving lane with a
+// cross-lane permute.
+//
+// The grid is persistent (a few workgroups per compute unit, grid-stride over
+// chunks) and workgroup ids are renumbered so that consecutive chunks (the
+// same plane, adjacent tokens) run on the same XCD: gfx950 deals workgroups
+// to its 8 XCDs round-robin, and each XCD has its own L2 and translation
+// caches.
+//
+// There is no arithmetic on the KV values anywhere: the kernels are pure data
+// movement and are bound by HBM bandwidth.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvx {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = kWave * kWavesPerBlock;
+constexpr int kTab = 128;          // plane pointers carried per side per launch
+constexpr int kChunkBytes = 16384; // target bytes a wave moves per chunk
+constexpr int kXcds = 8;           // XCDs on gfx950
+constexpr int kFlatNV = 16;        // vectors per lane per pass of the flat copy
+
+enum Code : int { kNone = 0, kCopy = 1, kSkip = 2 };
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------- arguments --
+
+// Launch-wide scalars shared by every op.
+struct Common {
+    const int64_t* tok_off;     // paged ops: DEVICE [num_reqs + 1]
+    unsigned long long* skipped;
+    int64_t T;                  // paged: total tokens; permute: seq_len
+    int32_t num_reqs;
+    int32_t q0;                 // first plane of this launch
+    int32_t Q;                  // planes of the layout
+    int32_t R;                  // unit bytes
+    uint32_t U;                 // units per chunk
+    uint32_t units_per_plane;   // paged: T; permute: seq_len * H
+    uint32_t chunks_per_plane;
+    uint32_t nchunks;
+    uint32_t V;                 // 16-byte vectors per unit
+    uint32_t v_magic;           // ceil(2^32 / V)
+};
+
+// One side of a paged move that is a pool.
+struct PoolRef {
+    char* plane[kTab];          // bases of planes q0 .. q0 + nq - 1
+    int64_t stride;
+    int64_t num_pages;
+    const int64_t* pg_off;
+    const int32_t* ids;
+    int64_t num_ids;
+    int32_t page_size;
+    int32_t page_shift;         // log2(page_size) when a power of two, else -1
+};
+
+// One side of a paged move that is the contiguous staging buffer.
+struct StageRef {
+    char* base;
+};
+
+template <class Src, class Dst>
+struct PagedArgs {
+    Common c;
+    Src src;
+    Dst dst;
+};
+
+struct PermuteArgs {
+    Common c;
+    char* hf[kTab];             // [1][H][s_cap][D] planes q0 .. q0 + nq - 1
+    char* flat;                 // [Q][seq][H][D]
+    int64_t s_cap;
+    int32_t H;
+};
+
+// ---------------------------------------------------------------- helpers --
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t x, int lane) {
+    uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(x), lane);
+    uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(x >> 32), lane);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint32_t bperm32(uint32_t x, uint32_t lane) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_ds_bpermute(static_cast<int>(lane << 2), static_cast<int>(x)));
+}
+
+__device__ __forceinline__ uint64_t bperm64(uint64_t x, uint32_t lane) {
+    uint32_t lo = bperm32(static_cast<uint32_t>(x), lane);
+    uint32_t hi = bperm32(static_cast<uint32_t>(x >> 32), lane);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Global-address-space views, so loads and stores are emitted as global_*
+// (with an SGPR base where the address is wave-uniform) rather than flat_*.
+typedef __attribute__((address_space(1))) char gchar;
+typedef __attribute__((address_space(1))) v4u gv4u;
+
+__device__ __forceinline__ v4u load_nt(uint64_t base, uint32_t off) {
+    const gchar* p = reinterpret_cast<const gchar*>(base) + off;
+    return __builtin_nontemporal_load(reinterpret_cast<const gv4u*>(p));
+}
+
+__device__ __forceinline__ void store_nt(uint64_t base, uint32_t off, v4u x) {
+    gchar* p = reinterpret_cast<gchar*>(base) + off;
+    __builtin_nontemporal_store(x, reinterpret_cast<gv4u*>(p));
+}
+
+// ------------------------------------------------------- paged resolvers --
+
+// Chunk-level context of a paged op (wave-uniform).
+struct PagedChunk {
+    int64_t tok0;   // first batch token of the chunk
+    int32_t ql;     // plane within this launch
+    int32_t r0;     // request holding tok0
+};
+
+// Largest r < num_reqs with tok_off[r] <= tok (tok < T): request of a token.
+__device__ __forceinline__ int32_t request_of(const int64_t* __restrict__ tok_off,
+                                              int32_t num_reqs, int64_t tok) {
+    int32_t lo = 0, hi = num_reqs - 1;
+    while (lo < hi) {
+        int32_t mid = (lo + hi + 1) >> 1;
+        if (tok_off[mid] <= tok) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ PagedChunk paged_chunk(const Common& c, uint32_t chunk) {
+    PagedChunk k;
+    uint32_t ql = chunk / c.chunks_per_plane;
+    uint32_t j = chunk - ql * c.chunks_per_plane;
+    k.ql = static_cast<int32_t>(ql);
+    k.tok0 = static_cast<int64_t>(j) * c.U;
+    k.r0 = request_of(c.tok_off, c.num_reqs, k.tok0);
+    return k;
+}
+
+// Address of token t of request r in plane ql of a pool; false when any index
+// is out of range (the row is then skipped, never dereferenced).
+__device__ __forceinline__ bool pool_addr(const PoolRef& p, int32_t ql, int32_t r, int64_t t,
+                                          uint64_t& addr) {
+    int64_t pidx, row;
+    if (p.page_shift >= 0) {
+        pidx = t >> p.page_shift;
+        row = t & ((int64_t(1) << p.page_shift) - 1);
+    } else {
+        pidx = t / p.page_size;
+        row = t - pidx * p.page_size;
+    }
+    int64_t idx = p.pg_off[r] + pidx;
+    if (idx < 0 || idx >= p.num_ids) return false;
+    int64_t page = p.ids[idx];
+    if (page < 0 || page >= p.num_pages) return false;
+    addr = reinterpret_cast<uint64_t>(p.plane[ql]) +
+           static_cast<uint64_t>(page * p.page_size + row) * static_cast<uint64_t>(p.stride);
+    return true;
+}
+
+__device__ __forceinline__ uint64_t stage_addr(const StageRef& s, const Common& c, int32_t ql,
+                                               int64_t off_r, int64_t n_r, int64_t t) {
+    int64_t q = c.q0 + ql;
+    int64_t row = off_r * c.Q + q * n_r + t;
+    return reinterpret_cast<uint64_t>(s.base) + static_cast<uint64_t>(row) * c.R;
+}
+
+template <class Side>
+struct SideAddr;
+
+template <>
+struct SideAddr<PoolRef> {
+    __device__ static bool get(const PoolRef& p, const Common&, int32_t ql, int32_t r,
+                               int64_t, int64_t, int64_t t, uint64_t& a) {
+        return pool_addr(p, ql, r, t, a);
+    }
+};
+
+template <>
+struct SideAddr<StageRef> {
+    __device__ static bool get(const StageRef& s, const Common& c, int32_t ql, int32_t,
+                               int64_t off_r, int64_t n_r, int64_t t, uint64_t& a) {
+        a = stage_addr(s, c, ql, off_r, n_r, t);
+        return true;
+    }
+};
+
+// Resolve unit u (one lane) of a paged chunk.
+template <class Src, class Dst>
+__device__ __forceinline__ int resolve(const PagedArgs<Src, Dst>& a, const PagedChunk& k,
+                                       uint32_t u, uint64_t& s, uint64_t& d) {
+    const Common& c = a.c;
+    int64_t tok = k.tok0 + u;
+    if (u >= c.U || tok >= c.T) return kNone;
+    int32_t r = k.r0;
+    while (r + 1 < c.num_reqs && c.tok_off[r + 1] <= tok) ++r;
+    int64_t off_r = c.tok_off[r];
+    int64_t end_r = c.tok_off[r + 1];
+    // a token range that contradicts total_tokens is never dereferenced
+    if (off_r < 0 || tok < off_r || tok >= end_r || end_r > c.T) return kSkip;
+    int64_t t = tok - off_r;
+    int64_t n_r = end_r - off_r;
+    bool ok = SideAddr<Src>::get(a.src, c, k.ql, r, off_r, n_r, t, s);
+    ok = SideAddr<Dst>::get(a.dst, c, k.ql, r, off_r, n_r, t, d) && ok;
+    return ok ? kCopy : kSkip;
+}
+
+// ----------------------------------------------------- permute resolver --
+
+struct PermChunk {
+    uint32_t p0;    // first unit (s * H + h) of the chunk within its plane
+    int32_t ql;
+};
+
+__device__ __forceinline__ PermChunk perm_chunk(const Common& c, uint32_t chunk) {
+    PermChunk k;
+    uint32_t ql = chunk / c.chunks_per_plane;
+    k.ql = static_cast<int32_t>(ql);
+    k.p0 = (chunk - ql * c.chunks_per_plane) * c.U;
+    return k;
+}
+
+// Unit p = s * H + h of plane q: the HF row hf[q][0][h][s][:] and the flat
+// row flat[q][s][h][:].  REBUILD swaps source and destination.
+template <bool REBUILD>
+__device__ __forceinline__ int resolve_perm(const PermuteArgs& a, const PermChunk& k,
+                                            uint32_t u, uint64_t& s, uint64_t& d) {
+    const Common& c = a.c;
+    uint32_t p = k.p0 + u;
+    if (u >= c.U || p >= c.units_per_plane) return kNone;
+    uint32_t sq = p / static_cast<uint32_t>(a.H);
+    uint32_t h = p - sq * static_cast<uint32_t>(a.H);
+    uint64_t hf = reinterpret_cast<uint64_t>(a.hf[k.ql]) +
+                  (static_cast<uint64_t>(h) * a.s_cap + sq) * static_cast<uint64_t>(c.R);
+    uint64_t fl = reinterpret_cast<uint64_t>(a.flat) +
+                  (static_cast<uint64_t>(c.q0 + k.ql) * c.units_per_plane + p) *
+                      static_cast<uint64_t>(c.R);
+    s = REBUILD ? fl : hf;
+    d = REBUILD ? hf : fl;
+    return kCopy;
+}
+
+// ------------------------------------------------------------ copy phase --
+
+// Rows of VPL KiB, U rows per chunk; row addresses broadcast to SGPRs.
+template <int VPL, int U>
+__device__ __forceinline__ void copy_wide(uint64_t s_l, uint64_t d_l, int code_l, int lane) {
+    v4u x[U][VPL];
+    const uint32_t off = static_cast<uint32_t>(lane) * 16u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (__builtin_amdgcn_readlane(code_l, u) == kCopy) {
+            const uint64_t s = readlane64(s_l, u);
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) x[u][v] = load_nt(s, off + v * 1024);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (__builtin_amdgcn_readlane(code_l, u) == kCopy) {
+            const uint64_t d = readlane64(d_l, u);
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) store_nt(d, off + v * 1024, x[u][v]);
+        }
+    }
+}
+
+// Any row size: U*V vectors dealt round-robin to lanes, kFlatNV per pass.
+__device__ __forceinline__ void copy_flat(const Common& c, uint64_t s_l, uint64_t d_l,
+                                          int code_l, int lane) {
+    const uint32_t total = c.U * c.V;
+    for (uint32_t base = 0; base < total; base += kWave * kFlatNV) {
+        v4u x[kFlatNV];
+        uint64_t dst[kFlatNV];
+        bool act[kFlatNV];
+#pragma unroll
+        for (int j = 0; j < kFlatNV; ++j) {
+            uint32_t i = base + j * kWave + lane;
+            // i / V: exact for i * V < 2^32; V = 1 has no 32-bit magic
+            uint32_t u = c.V == 1 ? i : __umulhi(i, c.v_magic);
+            uint32_t vec = i - u * c.V;
+            uint64_t s = bperm64(s_l, u);
+            uint64_t d = bperm64(d_l, u);
+            int code = static_cast<int>(bperm32(static_cast<uint32_t>(code_l), u));
+            act[j] = (i < total) && code == kCopy;
+            dst[j] = d + static_cast<uint64_t>(vec) * 16u;
+            if (act[j]) x[j] = load_nt(s, vec * 16u);
+        }
+#pragma unroll
+        for (int j = 0; j < kFlatNV; ++j)
+            if (act[j]) store_nt(dst[j], 0, x[j]);
+    }
+}
+
+// --------------------------------------------------------------- kernels --
+
+// Wave number with XCD-aware workgroup renumbering: with G % 8 == 0, logical
+// block (b % 8) * (G / 8) + b / 8 puts logical blocks [x*G/8, (x+1)*G/8) on
+// XCD x, so the chunks a grid-stride round hands to one XCD are contiguous.
+__device__ __forceinline__ uint32_t wave_id() {
+    const uint32_t G = gridDim.x;
+    const uint32_t b = blockIdx.x;
+    const uint32_t lb = (G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
+    return __builtin_amdgcn_readfirstlane(lb * kWavesPerBlock + (threadIdx.x >> 6));
+}
+
+__device__ __forceinline__ void count_skips(unsigned long long* counter, unsigned long long n,
+                                            int lane) {
+    if (counter != nullptr && n != 0 && lane == 0) atomicAdd(counter, n);
+}
+
+// VPL > 0: wide copy with U rows per chunk; VPL == 0: flat copy.
+template <class Src, class Dst, int VPL, int U>
+__global__ __launch_bounds__(kBlock) void k_paged(PagedArgs<Src, Dst> a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t nwaves = gridDim.x * kWavesPerBlock;
+    unsigned long long nskip = 0;
+    for (uint32_t chunk = wave_id(); chunk < a.c.nchunks; chunk += nwaves) {
+        const PagedChunk k = paged_chunk(a.c, chunk);
+        uint64_t s = 0, d = 0;
+        const int code = resolve(a, k, static_cast<uint32_t>(lane), s, d);
+        nskip += __popcll(__ballot(code == kSkip));
+        if constexpr (VPL > 0) copy_wide<VPL, U>(s, d, code, lane);
+        else copy_flat(a.c, s, d, code, lane);
+    }
+    count_skips(a.c.skipped, nskip, lane);
+}
+
+template <bool REBUILD, int VPL, int U>
+__global__ __launch_bounds__(kBlock) void k_permute(PermuteArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t nwaves = gridDim.x * kWavesPerBlock;
+    for (uint32_t chunk = wave_id(); chunk < a.c.nchunks; chunk += nwaves) {
+        const PermChunk k = perm_chunk(a.c, chunk);
+        uint64_t s = 0, d = 0;
+        const int code = resolve_perm<REBUILD>(a, k, static_cast<uint32_t>(lane), s, d);
+        if constexpr (VPL > 0) copy_wide<VPL, U>(s, d, code, lane);
+        else copy_flat(a.c, s, d, code, lane);
+    }
+}
+
+}  // namespace kvx

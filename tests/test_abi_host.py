@@ -1,0 +1,166 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every function
+include/kvx.h declares, and rejects bad arguments with the documented status
+before anything reaches the GPU (validation never touches a device pointer)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import scatter_kvx_gather_amd as kvx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvx.h")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_RANGE = 0, 1, 2, 3, 4, 5
+
+# Fake, 16-byte aligned "device" addresses: validation only looks at their
+# values, never dereferences them, and every call below fails validation.
+A = 0x7F0000000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvx_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert names == sorted(["kvx_gather", "kvx_scatter", "kvx_gather_scatter",
+                            "kvx_extract_permute", "kvx_rebuild_permute", "kvx_status_str",
+                            "kvx_abi_version"])
+    lib = ctypes.CDLL(kvx.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", kvx.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (kvx_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_abi_version_and_strings():
+    lib = kvx.load_library()
+    assert lib.kvx_abi_version() == 1
+    for s in range(8):
+        assert lib.kvx_status_str(s).startswith(b"KVX_")
+    assert lib.kvx_status_str(99) == b"unknown kvx_status"
+
+
+def _layout(L=2, kv=2, H=8, D=128, dtype=2):
+    return kvx._CLayout(L, kv, H, D, dtype)
+
+
+def _pool(Q, num_pages=16, page_size=1, stride=2048, base=A):
+    arr = (ctypes.c_void_p * Q)(*[base + q * (1 << 20) for q in range(Q)])
+    return kvx._CPool(ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), num_pages, page_size,
+                      stride), arr
+
+
+def _reqs(n=1, T=4):
+    return kvx._CReqs(n, T, A + 0x100000)
+
+
+def _table(n_ids=4):
+    return kvx._CTable(A + 0x200000, A + 0x300000, n_ids)
+
+
+def gather(layout, pool, table, reqs, staging=A + 0x400000, nbytes=1 << 30):
+    lib = kvx.load_library()
+    return lib.kvx_gather(ctypes.byref(layout) if layout is not None else None,
+                          ctypes.byref(pool) if pool is not None else None,
+                          ctypes.byref(table) if table is not None else None,
+                          ctypes.byref(reqs) if reqs is not None else None,
+                          staging, nbytes, None, None)
+
+
+def test_gather_validation():
+    lay = _layout()
+    pool, keep = _pool(4)
+    tab, reqs = _table(), _reqs()
+    assert gather(None, pool, tab, reqs) == E_NULL
+    assert gather(_layout(dtype=9), pool, tab, reqs) == E_DTYPE
+    assert gather(_layout(H=1, D=4), pool, tab, reqs) == E_ALIGN            # R = 8 bytes
+    assert gather(_layout(kv=3), pool, tab, reqs) == E_SHAPE
+    assert gather(_layout(L=0), pool, tab, reqs) == E_SHAPE
+    assert gather(_layout(H=512, D=128), pool, tab, reqs) == E_RANGE        # R = 128 KiB
+    assert gather(lay, None, tab, reqs) == E_NULL
+    assert gather(lay, pool, None, reqs) == E_NULL
+    assert gather(lay, pool, tab, None) == E_NULL
+    bad, k2 = _pool(4, base=A + 8)
+    assert gather(lay, bad, tab, reqs) == E_ALIGN
+    small, k3 = _pool(4, stride=1024)                                         # stride < R
+    assert gather(lay, small, tab, reqs) == E_SHAPE
+    odd, k4 = _pool(4, stride=2056)
+    assert gather(lay, odd, tab, reqs) == E_ALIGN
+    assert gather(lay, pool, tab, _reqs(1, -1)) == E_SHAPE
+    assert gather(lay, pool, tab, _reqs(0, 5)) == E_SHAPE
+    assert gather(lay, pool, tab, reqs, staging=A + 0x400008) == E_ALIGN
+    assert gather(lay, pool, tab, reqs, nbytes=4 * 4 * 2048 - 16) == E_SHAPE
+    assert gather(lay, pool, tab, reqs, staging=None) == E_NULL
+    zero_pages, k5 = _pool(4, num_pages=-1)
+    assert gather(lay, zero_pages, tab, reqs) == E_SHAPE
+    huge, k6 = _pool(4, num_pages=1 << 62, page_size=16)
+    assert gather(lay, huge, tab, reqs) == E_RANGE
+    # a NULL plane pointer
+    arr = (ctypes.c_void_p * 4)(A, None, A, A)
+    p = kvx._CPool(ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), 16, 1, 2048)
+    assert gather(lay, p, tab, reqs) == E_NULL
+
+
+def test_empty_batch_enqueues_nothing():
+    # zero tokens: valid, nothing to move, returns before any device query
+    lay = _layout()
+    pool, keep = _pool(4)
+    assert gather(lay, pool, _table(0), _reqs(0, 0), staging=None, nbytes=0) == OK
+
+
+def test_permute_validation():
+    lib = kvx.load_library()
+    lay = _layout(L=2, kv=2, H=4, D=128, dtype=1)
+    arr = (ctypes.c_void_p * 4)(*[A + q * (1 << 24) for q in range(4)])
+    hf = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    need = 4 * 100 * 4 * 256
+    ex = lambda s_cap, seq, out=A + 0x1000000, nb=need: lib.kvx_extract_permute(  # noqa: E731
+        ctypes.byref(lay), hf, s_cap, seq, out, nb, None)
+    assert ex(50, 100) == E_SHAPE                  # seq > s_cap
+    assert ex(100, -1) == E_SHAPE
+    assert ex(100, 100, nb=need - 16) == E_SHAPE
+    assert ex(100, 100, out=A + 4) == E_ALIGN
+    assert ex(100, 100, out=None) == E_NULL
+    assert lib.kvx_extract_permute(ctypes.byref(lay), None, 100, 100, A, need, None) == E_NULL
+    lay_odd = _layout(L=1, kv=2, H=2, D=4, dtype=2)    # head row of 8 bytes
+    assert lib.kvx_extract_permute(ctypes.byref(lay_odd), hf, 10, 10, A, 1 << 20, None) == E_ALIGN
+    assert lib.kvx_extract_permute(ctypes.byref(lay), hf, 100, 0, None, 0, None) == OK
+    rb = lambda seq, inp=A + 0x1000000, nb=need: lib.kvx_rebuild_permute(  # noqa: E731
+        ctypes.byref(lay), inp, nb, seq, hf, 100, None)
+    assert rb(101) == E_SHAPE
+    assert rb(100, nb=need - 1) == E_SHAPE
+    assert rb(100, inp=None) == E_NULL
+
+
+def test_python_binding_raises():
+    with pytest.raises(ValueError):
+        kvx.Layout(1, 2, 1, 8, dtype="int4")
+    err = kvx.KvxError(3, "kvx_gather")
+    assert "KVX_E_ALIGN" in str(err) and err.status == 3
+
+
+def test_flat_copy_row_division_is_exact():
+    """The flat copy finds a vector's row as umulhi(i, ceil(2^32 / V)) (V > 1)
+    or i itself (V = 1); check it equals i // V for every vector index of a
+    chunk, for every row size the library accepts (16 B .. 64 KiB)."""
+    import numpy as np
+    for V in range(1, 4097):
+        R = 16 * V
+        if R % 1024 == 0 and R // 1024 in (1, 2, 4, 8, 16):
+            continue                                   # wide copy, no division
+        U = min(64, max(1, 16384 // R))
+        i = np.arange(U * V, dtype=np.uint64)
+        if V == 1:
+            u = i
+        else:
+            magic = np.uint64(((1 << 32) + V - 1) // V)
+            u = (i * magic) >> np.uint64(32)
+        assert np.array_equal(u, i // np.uint64(V)), V

@@ -1,0 +1,207 @@
+"""GPU parity at small sizes: every kvx call through the C ABI against the CPU
+oracle, byte for byte over the whole destination (pool, staging plus guard
+bytes, or HF tensors), on seeded random inputs that span several chunks and a
+ragged tail, across row sizes that take both copy variants."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scatter_kvx_gather_amd as kvx
+import workloads as wl
+from tests.gpu_util import (DEV, assert_bytes_equal, d, layout_of, oracle_gather,
+                            oracle_gather_scatter, oracle_scatter, requests, say, table)
+
+pytestmark = pytest.mark.gpu
+
+# (geometry, max tokens per request): row sizes 16 B .. 32 KiB, wide (multiples
+# of 1 KiB in {1, 2, 4, 8, 16} KiB) and flat (everything else), four dtypes
+GEOMS = [
+    (wl.Geometry(1, 2, 1, 8, "bf16"), 300),      # R = 16
+    (wl.Geometry(2, 1, 3, 8, "f16"), 200),       # R = 48
+    (wl.Geometry(1, 2, 3, 16, "bf16"), 200),     # R = 96
+    (wl.Geometry(2, 2, 1, 128, "f16"), 150),     # R = 256
+    (wl.Geometry(1, 2, 2, 128, "f16"), 150),     # R = 512
+    (wl.Geometry(2, 2, 3, 128, "bf16"), 100),    # R = 768
+    (wl.Geometry(2, 2, 4, 128, "bf16"), 100),    # R = 1 KiB  (wide)
+    (wl.Geometry(3, 1, 1, 576, "bf16"), 100),    # R = 1152   (MLA-sized row)
+    (wl.Geometry(2, 2, 8, 128, "bf16"), 70),     # R = 2 KiB  (wide)
+    (wl.Geometry(1, 2, 12, 128, "bf16"), 60),    # R = 3 KiB
+    (wl.Geometry(1, 2, 16, 128, "bf16"), 50),    # R = 4 KiB  (wide)
+    (wl.Geometry(1, 2, 32, 128, "bf16"), 20),    # R = 8 KiB  (wide)
+    (wl.Geometry(1, 1, 64, 128, "bf16"), 12),    # R = 16 KiB (wide)
+    (wl.Geometry(1, 1, 128, 128, "bf16"), 8),    # R = 32 KiB (flat, several passes)
+    (wl.Geometry(1, 2, 2, 8, "fp8"), 300),       # R = 16, 1-byte elements
+    (wl.Geometry(2, 2, 2, 128, "f32"), 80),      # R = 1 KiB, 4-byte elements
+]
+
+
+def run_paged_case(case, seed, guard=256):
+    g = case.geom
+    Q, R = g.planes, g.row_bytes
+    rng = np.random.default_rng(seed)
+    src_h = rng.integers(0, 256, (Q, case.src.num_slots, R), dtype=np.uint8)
+    dst_h = rng.integers(0, 256, (Q, case.dst.num_slots, R), dtype=np.uint8)
+    n = case.total_tokens * Q * R
+    stage_prefill = rng.integers(0, 256, n + guard, dtype=np.uint8)
+    stage_in = rng.integers(0, 256, n, dtype=np.uint8)
+    lay = layout_of(g)
+    reqs = requests(case)
+    st, dt = table(case.src), table(case.dst)
+    src_d = d(src_h)
+    src = kvx.Pool(src_d, case.src.num_pages, case.src.page_size)
+    skipped = torch.zeros(3, dtype=torch.int64, device=DEV)
+
+    say(case.name, f"Q={Q} R={R} T={case.total_tokens} pages {case.src.page_size}/"
+        f"{case.dst.page_size}: gather")
+    staging = d(stage_prefill)
+    kvx.gather(lay, src, st, reqs, staging, skipped=skipped[0:1])
+    say(case.name, "scatter")
+    dst_d1 = d(dst_h)
+    kvx.scatter(lay, d(stage_in), reqs, kvx.Pool(dst_d1, case.dst.num_pages, case.dst.page_size),
+                dt, skipped=skipped[1:2])
+    say(case.name, "gather_scatter")
+    dst_d2 = d(dst_h)
+    kvx.gather_scatter(lay, src, st, reqs,
+                       kvx.Pool(dst_d2, case.dst.num_pages, case.dst.page_size), dt,
+                       skipped=skipped[2:3])
+    torch.cuda.synchronize()
+
+    exp_stage = stage_prefill.copy()
+    s0 = oracle_gather(case, src_h, exp_stage)
+    exp_dst1 = dst_h.copy()
+    s1 = oracle_scatter(case, stage_in, exp_dst1)
+    exp_dst2 = dst_h.copy()
+    s2 = oracle_gather_scatter(case, src_h, exp_dst2)
+    assert_bytes_equal(staging.cpu().numpy(), exp_stage, f"{case.name} gather")
+    assert_bytes_equal(dst_d1.cpu().numpy(), exp_dst1, f"{case.name} scatter")
+    assert_bytes_equal(dst_d2.cpu().numpy(), exp_dst2, f"{case.name} gather_scatter")
+    assert skipped.cpu().tolist() == [s0, s1, s2], case.name
+
+
+@pytest.mark.parametrize("gi", range(len(GEOMS)))
+@pytest.mark.parametrize("pages", [(1, 1), (16, 16), (1, 16), (3, 2)])
+def test_paged_ops(gi, pages):
+    g, max_len = GEOMS[gi]
+    seed = 1000 * gi + 10 * pages[0] + pages[1]
+    case = wl.random_case(seed, geom=g, max_reqs=5, max_len=max_len, src_page=pages[0],
+                          dst_page=pages[1])
+    run_paged_case(case, seed)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_paged_out_of_range_ids(seed):
+    g, max_len = GEOMS[seed % len(GEOMS)]
+    case = wl.random_case(5000 + seed, geom=g, max_reqs=6, max_len=max_len, oor_frac=0.15)
+    run_paged_case(case, seed)
+
+
+def test_many_requests_and_empty_ones():
+    # 300 requests, a third of them empty: the token -> request search and the
+    # chunks that straddle request boundaries
+    rng = np.random.default_rng(3)
+    lens = rng.integers(0, 9, 300)
+    lens[::3] = 0
+    g = wl.Geometry(1, 2, 8, 128, "bf16")
+    S = int(lens.sum()) + 50
+    perm_s, perm_d = rng.permutation(S), rng.permutation(S)
+    lists_s, lists_d, pos = [], [], 0
+    for n in lens:
+        lists_s.append(perm_s[pos:pos + n])
+        lists_d.append(perm_d[pos:pos + n])
+        pos += int(n)
+    case = wl.PagedCase("many_reqs", g, wl.csr_from_lengths(lens),
+                        wl.side_from_slot_lists(lists_s, S), wl.side_from_slot_lists(lists_d, S),
+                        0, 0, 0)
+    run_paged_case(case, 3)
+
+
+def test_more_than_128_planes():
+    # Q = 160 planes: the host splits the launch into plane ranges of 128
+    case = wl.random_case(77, geom=wl.Geometry(80, 2, 1, 8, "bf16"), max_reqs=3, max_len=40,
+                          src_page=2, dst_page=1)
+    run_paged_case(case, 77)
+
+
+def test_token_major_pools_and_mixed_strides():
+    """Source pool token-major (plane q of slot s at (s*Q + q)*R), destination
+    pool with slots padded to 3R: strides differ from R and from each other."""
+    g = wl.Geometry(2, 2, 8, 128, "bf16")
+    Q, R = g.planes, g.row_bytes
+    case = wl.random_case(88, geom=g, max_reqs=4, max_len=60, src_page=16, dst_page=1)
+    rng = np.random.default_rng(88)
+    src_tm = rng.integers(0, 256, case.src.num_slots * Q * R, dtype=np.uint8)
+    dst_pad = rng.integers(0, 256, (Q, case.dst.num_slots, 3 * R), dtype=np.uint8)
+    src_d, dst_d = d(src_tm), d(dst_pad)
+    lay, reqs = layout_of(g), requests(case)
+    src = kvx.Pool([src_d.data_ptr() + q * R for q in range(Q)], case.src.num_pages,
+                   case.src.page_size, slot_stride=Q * R)
+    src._keep = src_d
+    dst = kvx.Pool([dst_d[q].data_ptr() for q in range(Q)], case.dst.num_pages,
+                   case.dst.page_size, slot_stride=3 * R)
+    dst._keep = dst_d
+    say("token_major gather_scatter")
+    kvx.gather_scatter(lay, src, table(case.src), reqs, dst, table(case.dst))
+    torch.cuda.synchronize()
+    exp = dst_pad.copy()
+    oracle.gather_scatter([src_tm[q * R:] for q in range(Q)], Q * R, case.src.page_size,
+                          case.src.num_pages, case.src.pg_off, case.src.ids, R, case.tok_off,
+                          [exp[q].reshape(-1) for q in range(Q)], 3 * R, case.dst.page_size,
+                          case.dst.num_pages, case.dst.pg_off, case.dst.ids)
+    assert_bytes_equal(dst_d.cpu().numpy(), exp, "token-major gather_scatter")
+
+
+# ------------------------------------------------------------------ permutes --
+
+PERMS = [
+    # (Q, H, D, dtype, s_cap, seq)
+    (4, 4, 128, "f16", 300, 300),     # head rows of 256 B (config-4 shape)
+    (3, 4, 128, "f16", 300, 173),     # s_cap > seq: rebuild leaves s >= seq alone
+    (2, 1, 128, "bf16", 100, 100),    # H = 1: a plain copy
+    (2, 8, 64, "bf16", 64, 1),        # seq = 1
+    (2, 3, 24, "bf16", 77, 50),       # head rows of 48 B
+    (2, 2, 8, "f16", 500, 499),       # head rows of 16 B
+    (2, 4, 512, "bf16", 40, 33),      # head rows of 1 KiB (wide copy)
+    (2, 2, 1024, "bf16", 20, 20),     # head rows of 2 KiB (wide copy)
+    (2, 100, 128, "f16", 10, 7),      # many heads
+    (160, 2, 8, "bf16", 9, 9),        # Q > 128: plane ranges
+    (2, 4, 128, "f16", 16, 0),        # seq = 0: nothing moves
+]
+
+
+@pytest.mark.parametrize("case", PERMS, ids=lambda c: "Q{}_H{}_D{}_{}_cap{}_seq{}".format(*c))
+def test_permutes(case):
+    Q, H, D, dtype, s_cap, seq = case
+    eb = wl.ELEM_BYTES[dtype]
+    Db = D * eb
+    lay = kvx.Layout(Q, 1, H, D, dtype)
+    rng = np.random.default_rng(Q * 1000 + H * 10 + seq)
+    hf_h = rng.integers(0, 256, (Q, H * s_cap * Db), dtype=np.uint8)
+    out_guard = 64
+    out_pre = rng.integers(0, 256, Q * seq * H * Db + out_guard, dtype=np.uint8)
+    tgt_h = rng.integers(0, 256, (Q, H * s_cap * Db), dtype=np.uint8)
+    flat_in = rng.integers(0, 256, Q * seq * H * Db, dtype=np.uint8)
+    hf_d, out_d, tgt_d, flat_d = d(hf_h), d(out_pre), d(tgt_h), d(flat_in)
+    say(f"extract Q={Q} H={H} Db={Db} s_cap={s_cap} seq={seq}")
+    kvx.extract_permute(lay, hf_d, s_cap, seq, out_d)
+    say("rebuild")
+    kvx.rebuild_permute(lay, flat_d, seq, tgt_d, s_cap)
+    torch.cuda.synchronize()
+    exp_out = out_pre.copy()
+    oracle.extract_permute([hf_h[q] for q in range(Q)], H, Db, s_cap, seq, exp_out)
+    exp_tgt = tgt_h.copy()
+    oracle.rebuild_permute(flat_in, H, Db, seq, [exp_tgt[q] for q in range(Q)], s_cap)
+    assert_bytes_equal(out_d.cpu().numpy(), exp_out, "extract")
+    assert_bytes_equal(tgt_d.cpu().numpy(), exp_tgt, "rebuild")
+
+
+def test_device_fill_matches_host_hash():
+    """The generators' device fill writes SplitMix64 words, as the host does."""
+    from workloads import device as wdev
+    t = torch.empty(3 * 1000 * 48, dtype=torch.uint8, device=DEV)
+    say("fill_hash")
+    wdev.fill_hash(t, 1234567, ctr0=0)
+    torch.cuda.synchronize()
+    assert_bytes_equal(t.cpu().numpy(), wl.hash_fill_host(1234567, t.numel()), "fill_hash")
+    w = t[:40].cpu().numpy().view("<u8")
+    assert int(w[0]) == 6457827717110365317

@@ -1,0 +1,50 @@
+"""Device-side generators: fill torch device buffers with the hash words of
+workloads.splitmix64, and a plain copy kernel for counter calibration."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkvx_workloads.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it first")
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.wl_fill_hash.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
+                                     ctypes.c_uint64, ctypes.c_void_p]
+        lib.wl_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                ctypes.c_void_p]
+        lib.wl_fill_hash.restype = lib.wl_copy.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _stream(stream):
+    return (stream or torch.cuda.current_stream()).cuda_stream
+
+
+def fill_hash(t: torch.Tensor, seed: int, ctr0: int = 0, stream=None) -> None:
+    """Word i of contiguous device tensor ``t`` <- splitmix64 output ctr0 + i."""
+    if not t.is_contiguous() or not t.is_cuda:
+        raise ValueError("fill_hash needs a contiguous device tensor")
+    rc = _load().wl_fill_hash(t.data_ptr(), t.numel() * t.element_size(), seed, ctr0,
+                              _stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"wl_fill_hash failed ({rc})")
+
+
+def copy_bytes(dst: torch.Tensor, src: torch.Tensor, nbytes: int, stream=None) -> None:
+    """Plain copy of ``nbytes`` from src to dst (both contiguous device tensors)."""
+    if nbytes > dst.numel() * dst.element_size() or nbytes > src.numel() * src.element_size():
+        raise ValueError("copy larger than a buffer")
+    rc = _load().wl_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"wl_copy failed ({rc})")
