@@ -1,0 +1,428 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV data-movement path on one MI355X.
+
+Workload: one 2048-token request at 144 KiB per token (36 layers x {K,V} x 8
+KV heads x 128, bf16; 288 MiB), in token-paged pools of 32768 slots (4.5 GiB
+each), two pools in the one GPU's HBM, slots a seeded random subset of each
+pool.  A step is one pass of the whole path over one such request:
+
+  gather_scatter  pool A -> pool B directly ("P writes D's pages")
+  gather          pool A -> contiguous staging [plane][token][H][D]
+  rebuild         staging -> HF cache tensors [1, H, seq, D] per plane
+  extract         HF cache tensors -> a second staging buffer
+  scatter         second staging -> pool B
+
+Each op moves 288 MiB in and 288 MiB out (603,979,776 bytes read + written).
+Steps rotate over 16 disjoint requests of the pools, so no launch finds its
+rows in the 256 MiB Infinity Cache from an earlier launch.  Inputs are
+resident in HBM before the timed region.
+
+Printed (one JSON line on stdout): step throughput in GB/s (read + write,
+decimal), its fraction of the 8 TB/s HBM peak, ms per 288 MiB request for the
+gather-scatter, per-op times from HIP events recorded on the launch stream, a
+contiguous-copy ceiling of equal bytes, the roofline of the dominant kernel,
+and the CPU oracle timed on the host on a bounded sample of the same steps.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+  python bench.py --pmc-pass            (short run for rocprofv3 --pmc)
+  python bench.py --summarize-pmc DIR   (traffic summary from two pmc runs)
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged KV gather GB/s (read+write) & % HBM peak; ms per 288 MiB request"
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, 8 TB/s
+NREQ = 16                         # disjoint 2048-token requests per pool
+OPS = ["gather_scatter", "gather", "rebuild", "extract", "scatter"]
+KERNEL_SOURCES = ["scatter_kvx_gather_amd/csrc/kvx_kernels.hpp",
+                  "scatter_kvx_gather_amd/csrc/kvx.hip"]
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "kv144k_2048tok_page1_hbm_traffic.md")
+COPY_CALIB_BYTES = 4 * 32768 * 2048     # four 64 MiB planes
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic():
+    """Per-launch HBM bytes of the dominant kernel from the committed counter
+    summary, or None when it is missing or the kernel changed since."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None, None
+    vals = {}
+    with open(PMC_SUMMARY) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != kernel_source_sha256():
+        return None, vals.get("kernel")
+    try:
+        return int(vals["traffic_bytes_per_launch"]), vals.get("kernel")
+    except (KeyError, ValueError):
+        return None, vals.get("kernel")
+
+
+# ------------------------------------------------------------------ setup --
+
+class Workload:
+    def __init__(self, torch, kvx, wl, wdev, dev, stream):
+        self.torch = torch
+        g = wl.KV144K
+        self.geom = g
+        self.Q, self.R, self.S = g.planes, g.row_bytes, 32768
+        self.T = 2048
+        self.cases = [wl.config2(k) for k in range(NREQ)]
+        c0 = self.cases[0]
+        Q, R, S, T = self.Q, self.R, self.S, self.T
+        with torch.cuda.stream(stream):
+            self.A = torch.empty((Q, S, R), dtype=torch.uint8, device=dev)
+            self.B = torch.empty((Q, S, R), dtype=torch.uint8, device=dev)
+            wdev.fill_hash(self.A, c0.value_seed, stream=stream)
+            wdev.fill_hash(self.B, c0.sentinel_seed, stream=stream)
+            self.S1 = torch.zeros(T * Q * R, dtype=torch.uint8, device=dev)
+            self.S2 = torch.zeros(T * Q * R, dtype=torch.uint8, device=dev)
+            self.HF = torch.zeros((Q, g.kv_heads * T * g.head_bytes), dtype=torch.uint8,
+                                  device=dev)
+
+            def d(a):
+                return torch.from_numpy(a).to(dev)
+            self.reqs = kvx.Requests(d(c0.tok_off), T)
+            self.src_tabs = [kvx.Table(d(c.src.pg_off), d(c.src.ids)) for c in self.cases]
+            self.dst_tabs = [kvx.Table(d(c.dst.pg_off), d(c.dst.ids)) for c in self.cases]
+        self.lay = kvx.Layout(g.num_layers, g.num_kv, g.kv_heads, g.head_dim, g.dtype)
+        self.PA = kvx.Pool(self.A, S)
+        self.PB = kvx.Pool(self.B, S)
+        self.op_bytes = 2 * T * Q * R               # read + write per op
+        self.kvx = kvx
+
+    def step(self, i, stream, ev=None):
+        kvx, lay = self.kvx, self.lay
+        k1, k2 = (2 * i) % NREQ, (2 * i + 1) % NREQ
+        T = self.T
+
+        def mark(j):
+            if ev is not None:
+                ev[j].record(stream)
+        mark(0)
+        kvx.gather_scatter(lay, self.PA, self.src_tabs[k1], self.reqs, self.PB,
+                           self.dst_tabs[k1], stream=stream)
+        mark(1)
+        kvx.gather(lay, self.PA, self.src_tabs[k2], self.reqs, self.S1, stream=stream)
+        mark(2)
+        kvx.rebuild_permute(lay, self.S1, T, self.HF, T, stream=stream)
+        mark(3)
+        kvx.extract_permute(lay, self.HF, T, T, self.S2, stream=stream)
+        mark(4)
+        kvx.scatter(lay, self.S2, self.reqs, self.PB, self.dst_tabs[k2], stream=stream)
+        mark(5)
+
+
+# -------------------------------------------------------------- cpu side --
+
+def cpu_baseline(wk, budget_s):
+    """Time the oracle on host copies of the same pools and requests."""
+    import numpy as np
+
+    import oracle
+    torch = wk.torch
+    Q, R, S, T = wk.Q, wk.R, wk.S, wk.T
+    g = wk.geom
+    log("cpu baseline: reading pools back to host")
+    A_h = wk.A.cpu().numpy()
+    B_h = wk.B.cpu().numpy()
+    S1 = np.zeros(T * Q * R, np.uint8)
+    S2 = np.zeros(T * Q * R, np.uint8)
+    HF = np.zeros((Q, g.kv_heads * T * g.head_bytes), np.uint8)
+    A_planes = [A_h[q].reshape(-1) for q in range(Q)]
+    B_planes = [B_h[q].reshape(-1) for q in range(Q)]
+    HF_planes = [HF[q] for q in range(Q)]
+    c0 = wk.cases[0]
+
+    def step(i, nt):
+        a, b = wk.cases[(2 * i) % NREQ], wk.cases[(2 * i + 1) % NREQ]
+        oracle.gather_scatter(A_planes, R, 1, S, a.src.pg_off, a.src.ids, R, c0.tok_off,
+                              B_planes, R, 1, S, a.dst.pg_off, a.dst.ids, nt)
+        oracle.gather(A_planes, R, 1, S, R, c0.tok_off, b.src.pg_off, b.src.ids, S1, nt)
+        oracle.rebuild_permute(S1, g.kv_heads, g.head_bytes, T, HF_planes, T, nt)
+        oracle.extract_permute(HF_planes, g.kv_heads, g.head_bytes, T, T, S2, nt)
+        oracle.scatter(S2, R, c0.tok_off, b.dst.pg_off, b.dst.ids, B_planes, R, 1, S, nt)
+
+    out = {}
+    ncores = min(16, os.cpu_count() or 1)
+    for nt in sorted({1, ncores}):
+        step(0, nt)                                # pre-fault staging and HF pages
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            step(steps + 1, nt)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or steps >= 200:
+                break
+        out[nt] = (steps, el)
+        log(f"cpu baseline: {nt} thread(s): {steps} steps in {el:.2f} s")
+    del A_h, B_h
+    return out, ncores
+
+
+# ----------------------------------------------------------------- pmc --
+
+def summarize_pmc(fetch_dir, write_dir, out_path):
+    """Traffic per launch of the dominant kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter reads
+    for the plain copy kernel of COPY_CALIB_BYTES run in the same process."""
+    def rows(d):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        out = []
+        for fn in files:
+            with open(fn) as f:
+                out.extend(csv.DictReader(f))
+        return out
+
+    def per_kernel(d, counter):
+        acc = {}
+        for r in rows(d):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r["Kernel_Name"]
+            acc.setdefault(name, []).append(float(r["Counter_Value"]))
+        return acc
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+
+    def pick(acc, key):
+        ks = [k for k in acc if key in k]
+        if not ks:
+            raise SystemExit(f"kernel matching {key!r} not found: {sorted(acc)[:8]}")
+        vals = acc[ks[0]]
+        return ks[0], sorted(vals)[len(vals) // 2]
+    dom = "k_paged<kvx::PoolRef, kvx::PoolRef"
+    kname, f_kib = pick(fetch, dom)
+    _, w_kib = pick(write, dom)
+    _, fc_kib = pick(fetch, "k_copy16")
+    _, wc_kib = pick(write, "k_copy16")
+    f_scale = (COPY_CALIB_BYTES / 1024.0) / fc_kib
+    w_scale = (COPY_CALIB_BYTES / 1024.0) / wc_kib
+    fetch_b = f_kib * f_scale * 1024
+    write_b = w_kib * w_scale * 1024
+    algo = 2 * 2048 * 72 * 2048
+    with open(out_path, "w") as f:
+        f.write("# HBM traffic of the gather-scatter kernel, 288 MiB request (kv144k, page 1)\n\n")
+        f.write("Two `rocprofv3 --pmc` runs of `python bench.py --pmc-pass` (one counter each);\n")
+        f.write("median per dispatch, scaled by the plain copy kernel `k_copy16` of\n")
+        f.write(f"{COPY_CALIB_BYTES} bytes run in the same process.\n\n")
+        f.write("Commands (from the repository root, on the GPU box):\n\n")
+        f.write("    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch --output-format csv "
+                "-- python3 bench.py --pmc-pass\n")
+        f.write("    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write --output-format csv "
+                "-- python3 bench.py --pmc-pass\n")
+        f.write("    python3 bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write "
+                "--pmc-out profiles/kv144k_2048tok_page1_hbm_traffic.md\n\n")
+        f.write(f"- kernel: `{kname}`\n")
+        f.write(f"- fetch_kib_per_dispatch: {f_kib:.1f}\n")
+        f.write(f"- write_kib_per_dispatch: {w_kib:.1f}\n")
+        f.write(f"- copy_fetch_kib: {fc_kib:.1f}\n")
+        f.write(f"- copy_write_kib: {wc_kib:.1f}\n")
+        f.write(f"- copy_bytes: {COPY_CALIB_BYTES}\n")
+        f.write(f"- fetch_scale: {f_scale:.4f}\n")
+        f.write(f"- write_scale: {w_scale:.4f}\n")
+        f.write(f"- fetch_bytes_per_launch: {int(fetch_b)}\n")
+        f.write(f"- write_bytes_per_launch: {int(write_b)}\n")
+        f.write(f"- traffic_bytes_per_launch: {int(fetch_b + write_b)}\n")
+        f.write(f"- algorithmic_bytes_per_launch: {algo}\n")
+        f.write(f"- traffic_over_algorithmic: {(fetch_b + write_b) / algo:.4f}\n")
+        f.write(f"- kernel_source_sha256: {kernel_source_sha256()}\n")
+    print(open(out_path).read())
+
+
+# ----------------------------------------------------------------- main --
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="time budget per oracle thread count")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="a short run for counter collection (no JSON line)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--pmc-out", default=PMC_SUMMARY, help="where --summarize-pmc writes")
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_out)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the path on one GPU only: both pools live in that GPU's "
+              "HBM and nothing here spans GPUs; run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import scatter_kvx_gather_amd as kvx
+    import workloads as wl
+    from workloads import device as wdev
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        return 2
+    kvx.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    log("setup: 2 pools of 4.5 GiB, 16 request tables")
+    wk = Workload(torch, kvx, wl, wdev, dev, stream)
+    torch.cuda.synchronize()
+
+    if args.pmc_pass:
+        for i in range(3):
+            wk.step(i, stream)
+        for k in range(3):
+            wdev.copy_bytes(wk.B[k * 4:(k + 1) * 4].reshape(-1), wk.A[k * 4:(k + 1) * 4]
+                            .reshape(-1), COPY_CALIB_BYTES, stream=stream)
+        torch.cuda.synchronize()
+        log("pmc pass done")
+        return 0
+
+    K, W = args.steps, args.warmup
+    for i in range(W):
+        wk.step(i, stream)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()                       # barrier: one rank
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(K):
+        wk.step(W + i, stream, events[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / K
+    op_ms = {op: sum(e[j].elapsed_time(e[j + 1]) for e in events) / K
+             for j, op in enumerate(OPS)}
+    step_bytes = wk.op_bytes * len(OPS)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"timed {K} steps: {ms_step:.4f} ms/step (wall {wall * 1e3 / K:.4f} ms/step)")
+    for op in OPS:
+        log(f"  {op:15s} {op_ms[op] * 1e3:8.1f} us  {wk.op_bytes / op_ms[op] / 1e6:8.1f} GB/s")
+
+    # contiguous copy ceiling: the same bytes as one op, over rotating chunks
+    ncopy = 16
+    chunk = wk.A.shape[1] * wk.R * 4              # 4 planes = 256 MiB contiguous
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ce[0].record(stream)
+    for k in range(ncopy):
+        p = (k * 4) % wk.Q
+        wdev.copy_bytes(wk.B[p:p + 4].reshape(-1), wk.A[p:p + 4].reshape(-1), chunk,
+                        stream=stream)
+    ce[1].record(stream)
+    torch.cuda.synchronize()
+    copy_ms = ce[0].elapsed_time(ce[1]) / ncopy
+    copy_gbps = 2 * chunk / (copy_ms * 1e-3) / 1e9
+
+    # the same gather kernel over contiguous rows (2048 consecutive slots of
+    # each plane, rotating over the 16 disjoint ranges, into staging): the
+    # access-pattern ceiling of the row mover itself
+    idents = [kvx.Table(torch.tensor([0, wk.T], dtype=torch.int64, device=dev),
+                        torch.arange(k * wk.T, (k + 1) * wk.T, dtype=torch.int32, device=dev))
+              for k in range(NREQ)]
+    torch.cuda.synchronize()
+    ce[0].record(stream)
+    for k in range(ncopy):
+        kvx.gather(wk.lay, wk.PA, idents[k % NREQ], wk.reqs, wk.S1, stream=stream)
+    ce[1].record(stream)
+    torch.cuda.synchronize()
+    ident_ms = ce[0].elapsed_time(ce[1]) / ncopy
+
+    dom = max(OPS, key=lambda o: op_ms[o])
+    kernel_of = {"gather_scatter": "k_paged<PoolRef, PoolRef, 2, 8>",
+                 "gather": "k_paged<PoolRef, StageRef, 2, 8>",
+                 "scatter": "k_paged<StageRef, PoolRef, 2, 8>",
+                 "rebuild": "k_permute<true, 0, 0>", "extract": "k_permute<false, 0, 0>"}
+    achieved = wk.op_bytes / (op_ms[dom] * 1e-3) / 1e9
+    traffic, traffic_kernel = read_traffic()
+    if traffic is not None and traffic_kernel and "PoolRef, kvx::PoolRef" not in traffic_kernel:
+        traffic = None
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic if dom == "gather_scatter" else None,
+                "kernel": kernel_of[dom], "op": dom,
+                "algorithmic_bytes_per_launch": wk.op_bytes}
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {
+            "workload": "kv144k_2048tok_page1: 1 request x 2048 tokens x 36 layers x {K,V} x "
+                        "8 kv_heads x 128 (144 KiB/token, 288 MiB), bf16 payload copied "
+                        "bitwise; token-paged pools of 32768 slots (4.5 GiB each), 16 "
+                        "disjoint requests rotated",
+            "step": "gather_scatter + gather + rebuild_permute + extract_permute + scatter",
+            "bytes_per_step": step_bytes,
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "ms_per_288MiB_request": round(op_ms["gather_scatter"], 5),
+        "ops": {op: {"ms": round(op_ms[op], 5),
+                     "GBps": round(wk.op_bytes / (op_ms[op] * 1e-3) / 1e9, 1)} for op in OPS},
+        "copy_ceiling": {"plain_copy_GBps": round(copy_gbps, 1),
+                         "plain_copy_bytes": 2 * chunk,
+                         "gather_contiguous_rows_GBps":
+                             round(wk.op_bytes / (ident_ms * 1e-3) / 1e9, 1)},
+        "wall_ms_per_step": round(wall * 1e3 / K, 5),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res, ncores = cpu_baseline(wk, args.cpu_seconds)
+        steps_n, el_n = res[ncores]
+        steps_1, el_1 = res[1]
+        result["cpu_baseline"] = {
+            "value": round(steps_n * step_bytes / el_n / 1e9, 2), "unit": "GB/s",
+            "cores": ncores, "kind": "oracle",
+            "sample": f"{steps_n} full steps (the same 5 ops on rotating 2048-token "
+                      f"requests of host copies of the same 4.5 GiB pools) in {el_n:.1f} s "
+                      f"with {ncores} threads",
+            "one_thread_GBps": round(steps_1 * step_bytes / el_1 / 1e9, 2),
+            "ms_per_step": round(el_n / steps_n * 1e3, 2),
+        }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

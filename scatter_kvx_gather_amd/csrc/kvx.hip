@@ -27,14 +27,17 @@ bool log_enabled() {
     return on;
 }
 
-// Workgroups per compute unit for the persistent grid (KVX_BLOCKS_PER_CU
-// overrides; 0 = one wave per chunk, no grid-stride reuse).
+// Cap on workgroups per compute unit; beyond it the waves grid-stride over
+// the chunks.  0 (the default) means no cap: one wave per chunk.  Measured on
+// the 2048-token, 144 KiB/token request: no cap and caps of 2-6 are within
+// 1-3% of each other; 8 or more (more waves than fit at once) is 5-25%
+// slower.  KVX_BLOCKS_PER_CU overrides it.
 int blocks_per_cu() {
     static const int n = [] {
         const char* e = std::getenv("KVX_BLOCKS_PER_CU");
-        if (e == nullptr) return 8;
+        if (e == nullptr) return 0;
         int v = std::atoi(e);
-        return v < 0 ? 8 : v;
+        return v < 0 ? 0 : v;
     }();
     return n;
 }
@@ -153,11 +156,22 @@ struct Shape {
     uint32_t U;
 };
 
+// Rows per chunk of the wide copy for a row of vpl KiB.
+template <int VPL>
+constexpr int wide_rows() {
+    return KVX_CHUNK_KIB / VPL > 0 ? KVX_CHUNK_KIB / VPL : 1;
+}
+
 Shape shape_for(int64_t unit_bytes) {
     if (unit_bytes % 1024 == 0) {
-        int64_t vpl = unit_bytes / 1024;
-        if (vpl == 1 || vpl == 2 || vpl == 4 || vpl == 8 || vpl == 16)
-            return {static_cast<int>(vpl), static_cast<uint32_t>(16 / vpl)};
+        switch (unit_bytes / 1024) {
+            case 1: return {1, static_cast<uint32_t>(wide_rows<1>())};
+            case 2: return {2, static_cast<uint32_t>(wide_rows<2>())};
+            case 4: return {4, static_cast<uint32_t>(wide_rows<4>())};
+            case 8: return {8, static_cast<uint32_t>(wide_rows<8>())};
+            case 16: return {16, static_cast<uint32_t>(wide_rows<16>())};
+            default: break;
+        }
     }
     int64_t u = kChunkBytes / unit_bytes;
     if (u < 1) u = 1;
@@ -202,24 +216,26 @@ kvx_status launch(const void* fn, uint32_t grid, Args& a, hipStream_t stream) {
 template <class Src, class Dst>
 const void* paged_kernel(int vpl) {
     switch (vpl) {
-        case 1: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, 16>);
-        case 2: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 2, 8>);
-        case 4: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 4, 4>);
-        case 8: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 8, 2>);
-        case 16: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 16, 1>);
+        case 1: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, wide_rows<1>()>);
+        case 2: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 2, wide_rows<2>()>);
+        case 4: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 4, wide_rows<4>()>);
+        case 8: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 8, wide_rows<8>()>);
+        case 16: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 16, wide_rows<16>()>);
         default: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 0, 0>);
     }
 }
 
+// Token-row permute kernel for rows of vpl KiB; nullptr for the head-row
+// (flat) kernel.
 template <bool REBUILD>
-const void* permute_kernel(int vpl) {
+const void* permute_rows_kernel(int vpl) {
     switch (vpl) {
-        case 1: return reinterpret_cast<const void*>(&k_permute<REBUILD, 1, 16>);
-        case 2: return reinterpret_cast<const void*>(&k_permute<REBUILD, 2, 8>);
-        case 4: return reinterpret_cast<const void*>(&k_permute<REBUILD, 4, 4>);
-        case 8: return reinterpret_cast<const void*>(&k_permute<REBUILD, 8, 2>);
-        case 16: return reinterpret_cast<const void*>(&k_permute<REBUILD, 16, 1>);
-        default: return reinterpret_cast<const void*>(&k_permute<REBUILD, 0, 0>);
+        case 1: return reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 1, wide_rows<1>()>);
+        case 2: return reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 2, wide_rows<2>()>);
+        case 4: return reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 4, wide_rows<4>()>);
+        case 8: return reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 8, wide_rows<8>()>);
+        case 16: return reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 16, wide_rows<16>()>);
+        default: return nullptr;
     }
 }
 
@@ -278,7 +294,12 @@ kvx_status run_permute(const Geom& g, void* const* hf, int64_t s_cap, int64_t se
     int cus = 0;
     kvx_status s = device_cus(&cus);
     if (s != KVX_OK) return s;
-    const Shape sh = shape_for(g.Db);
+    // Whole token rows (H * Db bytes) when they are 1..16 KiB powers of two;
+    // otherwise head rows of Db bytes with the flat copy.
+    const Shape tok = shape_for(g.R);
+    const bool rows = tok.vpl > 0;
+    const Shape sh = rows ? tok : shape_for(g.Db);
+    const uint32_t units = static_cast<uint32_t>(rows ? seq : seq * g.H);
     for (int32_t q0 = 0; q0 < g.Q; q0 += kTab) {
         const int32_t nq = g.Q - q0 < kTab ? g.Q - q0 : kTab;
         PermuteArgs a;
@@ -287,7 +308,7 @@ kvx_status run_permute(const Geom& g, void* const* hf, int64_t s_cap, int64_t se
         a.c.q0 = q0;
         a.c.Q = g.Q;
         a.c.R = static_cast<int32_t>(g.Db);
-        if (!set_chunks(&a.c, sh, static_cast<uint32_t>(seq * g.H), nq)) return KVX_E_RANGE;
+        if (!set_chunks(&a.c, sh, units, nq)) return KVX_E_RANGE;
         for (int32_t i = 0; i < nq; ++i) a.hf[i] = static_cast<char*>(hf[q0 + i]);
         a.flat = static_cast<char*>(flat);
         a.s_cap = s_cap;
@@ -295,13 +316,15 @@ kvx_status run_permute(const Geom& g, void* const* hf, int64_t s_cap, int64_t se
         const uint32_t grid = grid_for(a.c.nchunks, cus);
         if (log_enabled())
             std::fprintf(stderr,
-                         "kvx: %s Q=%d planes[%d,%d) H=%d Db=%lld seq=%lld s_cap=%lld copy=%s "
+                         "kvx: %s Q=%d planes[%d,%d) H=%d Db=%lld seq=%lld s_cap=%lld unit=%s "
                          "U=%u chunks=%u grid=%u\n",
                          REBUILD ? "rebuild" : "extract", g.Q, q0, q0 + nq, g.H,
                          static_cast<long long>(g.Db), static_cast<long long>(seq),
-                         static_cast<long long>(s_cap), sh.vpl ? "wide" : "flat", sh.U,
+                         static_cast<long long>(s_cap), rows ? "token-row" : "head-row", sh.U,
                          a.c.nchunks, grid);
-        s = launch(permute_kernel<REBUILD>(sh.vpl), grid, a, stream);
+        const void* fn = rows ? permute_rows_kernel<REBUILD>(sh.vpl)
+                              : reinterpret_cast<const void*>(&k_permute<REBUILD>);
+        s = launch(fn, grid, a, stream);
         if (s != KVX_OK) return s;
     }
     return KVX_OK;

@@ -21,11 +21,11 @@
 // and each lane fetches its row's addresses from the resolving lane with a
 // cross-lane permute.
 //
-// The grid is persistent (a few workgroups per compute unit, grid-stride over
-// chunks) and workgroup ids are renumbered so that consecutive chunks (the
-// same plane, adjacent tokens) run on the same XCD: gfx950 deals workgroups
-// to its 8 XCDs round-robin, and each XCD has its own L2 and translation
-// caches.
+// Waves grid-stride over the chunks (by default the grid has one wave per
+// chunk; the host can cap it at a few workgroups per compute unit), and
+// workgroup ids are renumbered so that consecutive chunks (the same plane,
+// adjacent tokens) run on the same XCD: gfx950 deals workgroups to its 8 XCDs
+// round-robin, and each XCD has its own L2 and translation caches.
 //
 // There is no arithmetic on the KV values anywhere: the kernels are pure data
 // movement and are bound by HBM bandwidth.
@@ -34,13 +34,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kvx {
+
+// Tuning knobs (compile-time; the defaults are the measured best).
+#ifndef KVX_CHUNK_KIB
+#define KVX_CHUNK_KIB 16           // bytes a wave moves per chunk, in KiB
+#endif
+#ifndef KVX_LOAD_NT
+#define KVX_LOAD_NT 1              // nontemporal loads
+#endif
+#ifndef KVX_XCD_REMAP
+#define KVX_XCD_REMAP 1            // XCD-aware workgroup renumbering
+#endif
 
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kWave * kWavesPerBlock;
 constexpr int kTab = 128;          // plane pointers carried per side per launch
-constexpr int kChunkBytes = 16384; // target bytes a wave moves per chunk
+constexpr int kChunkBytes = KVX_CHUNK_KIB * 1024;
 constexpr int kXcds = 8;           // XCDs on gfx950
 constexpr int kFlatNV = 16;        // vectors per lane per pass of the flat copy
 
@@ -125,12 +138,23 @@ typedef __attribute__((address_space(1))) v4u gv4u;
 
 __device__ __forceinline__ v4u load_nt(uint64_t base, uint32_t off) {
     const gchar* p = reinterpret_cast<const gchar*>(base) + off;
+#if KVX_LOAD_NT
     return __builtin_nontemporal_load(reinterpret_cast<const gv4u*>(p));
+#else
+    return *reinterpret_cast<const gv4u*>(p);
+#endif
 }
 
-__device__ __forceinline__ void store_nt(uint64_t base, uint32_t off, v4u x) {
+// NT: nontemporal store.  Stores to scattered pool rows use it; stores to a
+// contiguous destination (staging, permute outputs) are ordinary, which lets
+// L2 hand whole runs of lines to memory (measured ~6.4 TB/s for contiguous
+// ordinary stores vs ~5.6 TB/s nontemporal; scattered 2 KiB rows ~4.9 TB/s
+// with any cache policy).
+template <bool NT>
+__device__ __forceinline__ void store_v(uint64_t base, uint32_t off, v4u x) {
     gchar* p = reinterpret_cast<gchar*>(base) + off;
-    __builtin_nontemporal_store(x, reinterpret_cast<gv4u*>(p));
+    if constexpr (NT) __builtin_nontemporal_store(x, reinterpret_cast<gv4u*>(p));
+    else *reinterpret_cast<gv4u*>(p) = x;
 }
 
 // ------------------------------------------------------- paged resolvers --
@@ -269,7 +293,7 @@ __device__ __forceinline__ int resolve_perm(const PermuteArgs& a, const PermChun
 // ------------------------------------------------------------ copy phase --
 
 // Rows of VPL KiB, U rows per chunk; row addresses broadcast to SGPRs.
-template <int VPL, int U>
+template <int VPL, int U, bool NTS>
 __device__ __forceinline__ void copy_wide(uint64_t s_l, uint64_t d_l, int code_l, int lane) {
     v4u x[U][VPL];
     const uint32_t off = static_cast<uint32_t>(lane) * 16u;
@@ -286,35 +310,44 @@ __device__ __forceinline__ void copy_wide(uint64_t s_l, uint64_t d_l, int code_l
         if (__builtin_amdgcn_readlane(code_l, u) == kCopy) {
             const uint64_t d = readlane64(d_l, u);
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) store_nt(d, off + v * 1024, x[u][v]);
+            for (int v = 0; v < VPL; ++v) store_v<NTS>(d, off + v * 1024, x[u][v]);
         }
     }
 }
 
 // Any row size: U*V vectors dealt round-robin to lanes, kFlatNV per pass.
+// Each lane fetches its row's addresses from the resolving lane; the
+// destination address is fetched again at store time rather than held.
+// Every cross-lane fetch runs with all lanes active: a permute reads nothing
+// from a lane that is switched off by a branch.
+template <bool NTS>
 __device__ __forceinline__ void copy_flat(const Common& c, uint64_t s_l, uint64_t d_l,
                                           int code_l, int lane) {
     const uint32_t total = c.U * c.V;
     for (uint32_t base = 0; base < total; base += kWave * kFlatNV) {
         v4u x[kFlatNV];
-        uint64_t dst[kFlatNV];
-        bool act[kFlatNV];
+        uint32_t act = 0;                            // bit j: vector j is copied
 #pragma unroll
         for (int j = 0; j < kFlatNV; ++j) {
             uint32_t i = base + j * kWave + lane;
             // i / V: exact for i * V < 2^32; V = 1 has no 32-bit magic
             uint32_t u = c.V == 1 ? i : __umulhi(i, c.v_magic);
             uint32_t vec = i - u * c.V;
-            uint64_t s = bperm64(s_l, u);
-            uint64_t d = bperm64(d_l, u);
             int code = static_cast<int>(bperm32(static_cast<uint32_t>(code_l), u));
-            act[j] = (i < total) && code == kCopy;
-            dst[j] = d + static_cast<uint64_t>(vec) * 16u;
-            if (act[j]) x[j] = load_nt(s, vec * 16u);
+            uint64_t s = bperm64(s_l, u);
+            if (i < total && code == kCopy) {
+                act |= 1u << j;
+                x[j] = load_nt(s, vec * 16u);
+            }
         }
 #pragma unroll
-        for (int j = 0; j < kFlatNV; ++j)
-            if (act[j]) store_nt(dst[j], 0, x[j]);
+        for (int j = 0; j < kFlatNV; ++j) {
+            uint32_t i = base + j * kWave + lane;
+            uint32_t u = c.V == 1 ? i : __umulhi(i, c.v_magic);
+            uint32_t vec = i - u * c.V;
+            uint64_t d = bperm64(d_l, u);
+            if (act & (1u << j)) store_v<NTS>(d, vec * 16u, x[j]);
+        }
     }
 }
 
@@ -326,7 +359,8 @@ __device__ __forceinline__ void copy_flat(const Common& c, uint64_t s_l, uint64_
 __device__ __forceinline__ uint32_t wave_id() {
     const uint32_t G = gridDim.x;
     const uint32_t b = blockIdx.x;
-    const uint32_t lb = (G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
+    const uint32_t lb =
+        (KVX_XCD_REMAP && G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
     return __builtin_amdgcn_readfirstlane(lb * kWavesPerBlock + (threadIdx.x >> 6));
 }
 
@@ -346,13 +380,15 @@ __global__ __launch_bounds__(kBlock) void k_paged(PagedArgs<Src, Dst> a) {
         uint64_t s = 0, d = 0;
         const int code = resolve(a, k, static_cast<uint32_t>(lane), s, d);
         nskip += __popcll(__ballot(code == kSkip));
-        if constexpr (VPL > 0) copy_wide<VPL, U>(s, d, code, lane);
-        else copy_flat(a.c, s, d, code, lane);
+        constexpr bool nts = std::is_same<Dst, PoolRef>::value;
+        if constexpr (VPL > 0) copy_wide<VPL, U, nts>(s, d, code, lane);
+        else copy_flat<nts>(a.c, s, d, code, lane);
     }
     count_skips(a.c.skipped, nskip, lane);
 }
 
-template <bool REBUILD, int VPL, int U>
+// Permute with head rows as units (any head row size, flat copy).
+template <bool REBUILD>
 __global__ __launch_bounds__(kBlock) void k_permute(PermuteArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t nwaves = gridDim.x * kWavesPerBlock;
@@ -360,8 +396,64 @@ __global__ __launch_bounds__(kBlock) void k_permute(PermuteArgs a) {
         const PermChunk k = perm_chunk(a.c, chunk);
         uint64_t s = 0, d = 0;
         const int code = resolve_perm<REBUILD>(a, k, static_cast<uint32_t>(lane), s, d);
-        if constexpr (VPL > 0) copy_wide<VPL, U>(s, d, code, lane);
-        else copy_flat(a.c, s, d, code, lane);
+        copy_flat<false>(a.c, s, d, code, lane);
+    }
+}
+
+// Permute with token rows as units: token s of plane q is H*Db = VPL KiB,
+// contiguous in the flat layout and H head rows of Db bytes in the HF layout.
+// Lane l always moves the 16-byte vectors l + 64*j (j < VPL) of a token row;
+// their head h_j and offset within the head row are fixed for the whole
+// kernel, so every address is a per-lane constant plus s * Db (HF) or
+// s * H * Db (flat): no cross-lane exchange is needed.  U tokens per chunk.
+template <bool REBUILD, int VPL, int U>
+__global__ __launch_bounds__(kBlock) void k_permute_rows(PermuteArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t nwaves = gridDim.x * kWavesPerBlock;
+    const uint64_t Db = static_cast<uint64_t>(a.c.R);
+    const uint64_t row = Db * static_cast<uint64_t>(a.H);         // token row bytes
+    const uint32_t vd = a.c.V;                                      // vectors per head row
+    uint64_t hf_off[VPL];                                           // per-lane HF offsets
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+        const uint32_t idx = static_cast<uint32_t>(lane + kWave * j);
+        const uint32_t h = idx / vd;
+        hf_off[j] = static_cast<uint64_t>(h) * a.s_cap * Db + (idx - h * vd) * 16u;
+    }
+    const uint32_t seq = a.c.units_per_plane;
+    for (uint32_t chunk = wave_id(); chunk < a.c.nchunks; chunk += nwaves) {
+        const uint32_t ql = chunk / a.c.chunks_per_plane;
+        const uint32_t s0 = (chunk - ql * a.c.chunks_per_plane) * U;
+        const uint64_t hf = reinterpret_cast<uint64_t>(a.hf[ql]);
+        const uint64_t fl = reinterpret_cast<uint64_t>(a.flat) +
+                            (static_cast<uint64_t>(a.c.q0 + ql) * seq + s0) * row;
+        v4u x[U][VPL];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (s0 + u < seq) {
+#pragma unroll
+                for (int j = 0; j < VPL; ++j) {
+                    const uint32_t foff = static_cast<uint32_t>(lane + kWave * j) * 16u;
+                    if constexpr (REBUILD)
+                        x[u][j] = load_nt(fl + u * row, foff);
+                    else
+                        x[u][j] = load_nt(hf + hf_off[j] + (s0 + u) * Db, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (s0 + u < seq) {
+#pragma unroll
+                for (int j = 0; j < VPL; ++j) {
+                    const uint32_t foff = static_cast<uint32_t>(lane + kWave * j) * 16u;
+                    if constexpr (REBUILD)
+                        store_v<false>(hf + hf_off[j] + (s0 + u) * Db, 0, x[u][j]);
+                    else
+                        store_v<false>(fl + u * row, foff, x[u][j]);
+                }
+            }
+        }
     }
 }
 

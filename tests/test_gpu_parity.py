@@ -166,6 +166,11 @@ PERMS = [
     (2, 100, 128, "f16", 10, 7),      # many heads
     (160, 2, 8, "bf16", 9, 9),        # Q > 128: plane ranges
     (2, 4, 128, "f16", 16, 0),        # seq = 0: nothing moves
+    (2, 8, 128, "bf16", 100, 77),     # token rows of 2 KiB, ragged last chunk
+    (2, 16, 128, "bf16", 50, 45),     # token rows of 4 KiB
+    (1, 32, 128, "bf16", 9, 5),       # token rows of 8 KiB
+    (2, 64, 128, "bf16", 9, 9),       # token rows of 16 KiB (one token per chunk)
+    (3, 12, 128, "bf16", 40, 40),     # token rows of 3 KiB: head-row kernel
 ]
 
 
