@@ -257,6 +257,161 @@ def summarize_pmc(fetch_dir, write_dir, out_path):
     print(open(out_path).read())
 
 
+# ------------------------------------------------------ all workloads --
+
+def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
+    """Time every op on every workload at full size (one JSON line each)."""
+    def d(a):
+        return torch.from_numpy(a).to(dev)
+
+    def lay_of(g):
+        return kvx.Layout(g.num_layers, g.num_kv, g.kv_heads, g.head_dim, g.dtype)
+
+    def timed(fn, n):
+        """GPU time per launch: n launches captured in one graph, replayed, so
+        host-side call overhead does not hide short kernels."""
+        fn(0)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(n):
+                fn(i + 1)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        del graph
+        return e0.elapsed_time(e1) / n
+
+    def emit(cfg, op, ms, nbytes, note=""):
+        print(json.dumps({"workload": cfg, "op": op, "ms": round(ms, 5),
+                          "bytes_rw": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                          "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 /
+                                                HBM_PEAK_GBPS, 2), "note": note}), flush=True)
+
+    def pool_of(case, side, seed):
+        g = case.geom
+        t = torch.empty((g.planes, side.num_slots, g.row_bytes), dtype=torch.uint8, device=dev)
+        wdev.fill_hash(t, seed, stream=stream)
+        return t
+
+    with torch.cuda.stream(stream):
+        # 1: 128 tokens x 28 KiB, page 1, 1024-slot pools (fits in cache)
+        c = wl.config1()
+        g = c.geom
+        A, B = pool_of(c, c.src, 1), pool_of(c, c.dst, 2)
+        st = torch.empty(c.total_tokens * g.token_bytes, dtype=torch.uint8, device=dev)
+        reqs = kvx.Requests(d(c.tok_off), c.total_tokens)
+        ts, td = kvx.Table(d(c.src.pg_off), d(c.src.ids)), kvx.Table(d(c.dst.pg_off), d(c.dst.ids))
+        lay = lay_of(g)
+        nb = 2 * c.payload_bytes()
+        emit(c.name, "gather", timed(lambda i: kvx.gather(lay, kvx.Pool(A, 1024), ts, reqs, st,
+                                                         stream=stream), reps * 10), nb,
+             "3.5 MiB request: launch-latency bound, cache resident")
+        emit(c.name, "scatter", timed(lambda i: kvx.scatter(lay, st, reqs, kvx.Pool(B, 1024), td,
+                                                           stream=stream), reps * 10), nb,
+             "launch-latency bound")
+        del A, B, st
+        torch.cuda.empty_cache()
+
+        # 2: the bench request, each op alone, rotating 16 disjoint requests
+        cs = [wl.config2(k) for k in range(NREQ)]
+        g = cs[0].geom
+        A, B = pool_of(cs[0], cs[0].src, 1), pool_of(cs[0], cs[0].dst, 2)
+        st = torch.empty(2048 * g.token_bytes, dtype=torch.uint8, device=dev)
+        reqs = kvx.Requests(d(cs[0].tok_off), 2048)
+        tabs = [(kvx.Table(d(c.src.pg_off), d(c.src.ids)), kvx.Table(d(c.dst.pg_off),
+                                                                      d(c.dst.ids)))
+                for c in cs]
+        lay = lay_of(g)
+        PA, PB = kvx.Pool(A, 32768), kvx.Pool(B, 32768)
+        nb = 2 * cs[0].payload_bytes()
+        emit(cs[0].name, "gather_scatter", timed(lambda i: kvx.gather_scatter(
+            lay, PA, tabs[i % NREQ][0], reqs, PB, tabs[i % NREQ][1], stream=stream), reps * 4), nb)
+        emit(cs[0].name, "gather", timed(lambda i: kvx.gather(
+            lay, PA, tabs[i % NREQ][0], reqs, st, stream=stream), reps * 4), nb)
+        emit(cs[0].name, "scatter", timed(lambda i: kvx.scatter(
+            lay, st, reqs, PB, tabs[i % NREQ][1], stream=stream), reps * 4), nb)
+        del A, B, st, PA, PB
+        torch.cuda.empty_cache()
+
+        # 3: 32 fragmented requests, one batched gather
+        c = wl.config3()
+        g = c.geom
+        A = pool_of(c, c.src, 1)
+        st = torch.empty(c.total_tokens * g.token_bytes, dtype=torch.uint8, device=dev)
+        reqs = kvx.Requests(d(c.tok_off), c.total_tokens)
+        ts = kvx.Table(d(c.src.pg_off), d(c.src.ids))
+        emit(c.name, "gather", timed(lambda i: kvx.gather(lay_of(g), kvx.Pool(A, c.src.num_slots),
+                                                         ts, reqs, st, stream=stream), reps),
+             2 * c.payload_bytes(), f"{c.num_reqs} requests, {c.total_tokens} tokens")
+        del A, st
+        torch.cuda.empty_cache()
+
+        # 4: HF permutes, seq 1024 and 8192 (two buffer sets alternate)
+        for seq in (1024, 8192):
+            c = wl.config4(seq)
+            g = c.geom
+            lay = lay_of(g)
+            hf = [torch.empty((g.planes, g.kv_heads * seq * g.head_bytes), dtype=torch.uint8,
+                              device=dev) for _ in range(2)]
+            fl = [torch.empty(g.planes * seq * g.row_bytes, dtype=torch.uint8, device=dev)
+                  for _ in range(2)]
+            for t in hf + fl:
+                wdev.fill_hash(t, 3, stream=stream)
+            nb = 2 * c.payload_bytes()
+            emit(c.name, "extract", timed(lambda i: kvx.extract_permute(
+                lay, hf[i % 2], seq, seq, fl[i % 2], stream=stream), reps * 4), nb)
+            emit(c.name, "rebuild", timed(lambda i: kvx.rebuild_permute(
+                lay, fl[i % 2], seq, hf[i % 2], seq, stream=stream), reps * 4), nb)
+            del hf, fl
+            torch.cuda.empty_cache()
+
+        # 5: 64 requests, page-16 block pools of 36 GiB, one gather-scatter
+        c = wl.config5()
+        g = c.geom
+        A, B = pool_of(c, c.src, 1), pool_of(c, c.dst, 2)
+        reqs = kvx.Requests(d(c.tok_off), c.total_tokens)
+        ts, td = kvx.Table(d(c.src.pg_off), d(c.src.ids)), kvx.Table(d(c.dst.pg_off), d(c.dst.ids))
+        emit(c.name, "gather_scatter", timed(lambda i: kvx.gather_scatter(
+            lay_of(g), kvx.Pool(A, c.src.num_pages, 16), ts, reqs, kvx.Pool(B, c.dst.num_pages, 16),
+            td, stream=stream), reps), 2 * c.payload_bytes(),
+             f"{c.num_reqs} requests, {c.total_tokens} tokens, page 16")
+        del A, B
+        torch.cuda.empty_cache()
+
+
+def summarize_trace(trace_dir, out_path, title, command):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run."""
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            rows.extend(csv.DictReader(f))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    with open(out_path, "w") as f:
+        f.write(f"# {title}\n\n")
+        f.write("Kernel durations from `rocprofv3 --kernel-trace --stats` (microseconds).\n\n")
+        f.write("Command (from the repository root, on the GPU box):\n\n")
+        f.write(f"    {command}\n\n")
+        f.write("| kernel | calls | avg us | min us | max us | share % |\n")
+        f.write("|---|---:|---:|---:|---:|---:|\n")
+        for r in rows:
+            name = r["Name"].replace("|", "/")
+            if len(name) > 110:
+                name = name[:107] + "..."
+            f.write(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                    f"{float(r['Percentage']):.2f} |\n")
+    print(open(out_path).read())
+
+
 # ----------------------------------------------------------------- main --
 
 def main():
@@ -269,10 +424,17 @@ def main():
                     help="time budget per oracle thread count")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="a short run for counter collection (no JSON line)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="time every op on all five workloads (JSON line per op)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "OUT", "TITLE", "CMD"),
+                    help="markdown summary of a rocprofv3 --kernel-trace --stats run")
     ap.add_argument("--pmc-out", default=PMC_SUMMARY, help="where --summarize-pmc writes")
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return 0
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_out)
         return 0
@@ -293,6 +455,9 @@ def main():
     kvx.load_library()
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)
+    if args.all_configs:
+        all_configs(torch, kvx, wl, wdev, dev, stream, reps=5)
+        return 0
     log("setup: 2 pools of 4.5 GiB, 16 request tables")
     wk = Workload(torch, kvx, wl, wdev, dev, stream)
     torch.cuda.synchronize()

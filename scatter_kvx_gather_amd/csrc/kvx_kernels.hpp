@@ -163,8 +163,16 @@ __device__ __forceinline__ void store_v(uint64_t base, uint32_t off, v4u x) {
 struct PagedChunk {
     int64_t tok0;   // first batch token of the chunk
     int32_t ql;     // plane within this launch
-    int32_t r0;     // request holding tok0
 };
+
+__device__ __forceinline__ PagedChunk paged_chunk(const Common& c, uint32_t chunk) {
+    PagedChunk k;
+    uint32_t ql = chunk / c.chunks_per_plane;
+    uint32_t j = chunk - ql * c.chunks_per_plane;
+    k.ql = static_cast<int32_t>(ql);
+    k.tok0 = static_cast<int64_t>(j) * c.U;
+    return k;
+}
 
 // Largest r < num_reqs with tok_off[r] <= tok (tok < T): request of a token.
 __device__ __forceinline__ int32_t request_of(const int64_t* __restrict__ tok_off,
@@ -177,20 +185,79 @@ __device__ __forceinline__ int32_t request_of(const int64_t* __restrict__ tok_of
     return lo;
 }
 
-__device__ __forceinline__ PagedChunk paged_chunk(const Common& c, uint32_t chunk) {
-    PagedChunk k;
-    uint32_t ql = chunk / c.chunks_per_plane;
-    uint32_t j = chunk - ql * c.chunks_per_plane;
-    k.ql = static_cast<int32_t>(ql);
-    k.tok0 = static_cast<int64_t>(j) * c.U;
-    k.r0 = request_of(c.tok_off, c.num_reqs, k.tok0);
-    return k;
+// The request a lane's token belongs to, with its token range and the start
+// of its page list in each pool-side table.
+struct ReqOf {
+    int64_t off, end;       // tok_off[r], tok_off[r + 1]
+    int64_t pg_src, pg_dst; // pg_off[r] of the source / destination table
+    int32_t r;
+};
+
+template <class Side>
+__device__ __forceinline__ const int64_t* pg_off_of(const Side&) { return nullptr; }
+template <>
+__device__ __forceinline__ const int64_t* pg_off_of<PoolRef>(const PoolRef& p) {
+    return p.pg_off;
 }
 
-// Address of token t of request r in plane ql of a pool; false when any index
-// is out of range (the row is then skipped, never dereferenced).
-__device__ __forceinline__ bool pool_addr(const PoolRef& p, int32_t ql, int32_t r, int64_t t,
-                                          uint64_t& addr) {
+// Request lookup for lane token `tok` of a chunk starting at tok0.  Must be
+// called with every lane active (it uses cross-lane reads).
+//
+// Batches of at most 64 requests: lane j loads tok_off[j] and the pg_off[j]
+// entries in one round trip (lane num_reqs holds T); a ballot counts the
+// request starts <= tok0, giving the chunk's first request, and each lane
+// steps forward past the request ends below its token by reading the next
+// start from the lane that holds it.  No dependent loads.
+// Larger batches: a binary search for the chunk's first request, then a
+// per-lane walk, both over memory.
+template <class Src, class Dst>
+__device__ __forceinline__ ReqOf request_lookup(const PagedArgs<Src, Dst>& a, int64_t tok0,
+                                                int64_t tok, bool active, int lane) {
+    const Common& c = a.c;
+    const int32_t nr = c.num_reqs;
+    const int64_t* ps = pg_off_of(a.src);
+    const int64_t* pd = pg_off_of(a.dst);
+    ReqOf q;
+    if (nr <= kWave) {
+        const int64_t tv = lane < nr ? c.tok_off[lane] : (lane == nr ? c.T : INT64_MAX);
+        const int64_t sv = (ps != nullptr && lane < nr) ? ps[lane] : 0;
+        const int64_t dv = (pd != nullptr && lane < nr) ? pd[lane] : 0;
+        int32_t r = static_cast<int32_t>(__popcll(__ballot(tv <= tok0))) - 1;
+        if (r < 0) r = 0;
+        for (;;) {
+            const int64_t nxt_l = static_cast<int64_t>(bperm64(static_cast<uint64_t>(tv),
+                                                               static_cast<uint32_t>(r + 1)));
+            const int64_t nxt = r + 1 < kWave ? nxt_l : c.T;
+            const bool adv = active && r + 1 < nr && nxt <= tok;
+            if (__ballot(adv) == 0) break;
+            r += adv ? 1 : 0;
+        }
+        const uint32_t rl = static_cast<uint32_t>(r);
+        q.off = static_cast<int64_t>(bperm64(static_cast<uint64_t>(tv), rl));
+        const int64_t end_l = static_cast<int64_t>(bperm64(static_cast<uint64_t>(tv), rl + 1));
+        q.end = r + 1 < kWave ? end_l : c.T;
+        q.pg_src = static_cast<int64_t>(bperm64(static_cast<uint64_t>(sv), rl));
+        q.pg_dst = static_cast<int64_t>(bperm64(static_cast<uint64_t>(dv), rl));
+        q.r = r;
+    } else {
+        int32_t r = request_of(c.tok_off, nr, tok0);
+        if (active) {
+            while (r + 1 < nr && c.tok_off[r + 1] <= tok) ++r;
+        }
+        q.off = c.tok_off[r];
+        q.end = c.tok_off[r + 1];
+        q.pg_src = ps != nullptr ? ps[r] : 0;
+        q.pg_dst = pd != nullptr ? pd[r] : 0;
+        q.r = r;
+    }
+    return q;
+}
+
+// Address of token t of a request whose page list starts at pg_off_r, in
+// plane ql of a pool; false when any index is out of range (the row is then
+// skipped, never dereferenced).
+__device__ __forceinline__ bool pool_addr(const PoolRef& p, int32_t ql, int64_t pg_off_r,
+                                          int64_t t, uint64_t& addr) {
     int64_t pidx, row;
     if (p.page_shift >= 0) {
         pidx = t >> p.page_shift;
@@ -199,7 +266,7 @@ __device__ __forceinline__ bool pool_addr(const PoolRef& p, int32_t ql, int32_t 
         pidx = t / p.page_size;
         row = t - pidx * p.page_size;
     }
-    int64_t idx = p.pg_off[r] + pidx;
+    int64_t idx = pg_off_r + pidx;
     if (idx < 0 || idx >= p.num_ids) return false;
     int64_t page = p.ids[idx];
     if (page < 0 || page >= p.num_pages) return false;
@@ -220,38 +287,36 @@ struct SideAddr;
 
 template <>
 struct SideAddr<PoolRef> {
-    __device__ static bool get(const PoolRef& p, const Common&, int32_t ql, int32_t r,
+    __device__ static bool get(const PoolRef& p, const Common&, int32_t ql, int64_t pg_off_r,
                                int64_t, int64_t, int64_t t, uint64_t& a) {
-        return pool_addr(p, ql, r, t, a);
+        return pool_addr(p, ql, pg_off_r, t, a);
     }
 };
 
 template <>
 struct SideAddr<StageRef> {
-    __device__ static bool get(const StageRef& s, const Common& c, int32_t ql, int32_t,
+    __device__ static bool get(const StageRef& s, const Common& c, int32_t ql, int64_t,
                                int64_t off_r, int64_t n_r, int64_t t, uint64_t& a) {
         a = stage_addr(s, c, ql, off_r, n_r, t);
         return true;
     }
 };
 
-// Resolve unit u (one lane) of a paged chunk.
+// Resolve unit u (one lane) of a paged chunk.  Called with every lane active.
 template <class Src, class Dst>
 __device__ __forceinline__ int resolve(const PagedArgs<Src, Dst>& a, const PagedChunk& k,
                                        uint32_t u, uint64_t& s, uint64_t& d) {
     const Common& c = a.c;
-    int64_t tok = k.tok0 + u;
-    if (u >= c.U || tok >= c.T) return kNone;
-    int32_t r = k.r0;
-    while (r + 1 < c.num_reqs && c.tok_off[r + 1] <= tok) ++r;
-    int64_t off_r = c.tok_off[r];
-    int64_t end_r = c.tok_off[r + 1];
+    const int64_t tok = k.tok0 + u;
+    const bool active = u < c.U && tok < c.T;
+    const ReqOf q = request_lookup(a, k.tok0, tok, active, static_cast<int>(u));
+    if (!active) return kNone;
     // a token range that contradicts total_tokens is never dereferenced
-    if (off_r < 0 || tok < off_r || tok >= end_r || end_r > c.T) return kSkip;
-    int64_t t = tok - off_r;
-    int64_t n_r = end_r - off_r;
-    bool ok = SideAddr<Src>::get(a.src, c, k.ql, r, off_r, n_r, t, s);
-    ok = SideAddr<Dst>::get(a.dst, c, k.ql, r, off_r, n_r, t, d) && ok;
+    if (q.off < 0 || tok < q.off || tok >= q.end || q.end > c.T) return kSkip;
+    const int64_t t = tok - q.off;
+    const int64_t n_r = q.end - q.off;
+    bool ok = SideAddr<Src>::get(a.src, c, k.ql, q.pg_src, q.off, n_r, t, s);
+    ok = SideAddr<Dst>::get(a.dst, c, k.ql, q.pg_dst, q.off, n_r, t, d) && ok;
     return ok ? kCopy : kSkip;
 }
 

@@ -116,6 +116,28 @@ def test_many_requests_and_empty_ones():
     run_paged_case(case, 3)
 
 
+@pytest.mark.parametrize("nreq", [1, 2, 63, 64, 65, 130])
+@pytest.mark.parametrize("R", [2048, 512])
+def test_request_lookup_limits(nreq, R):
+    """Batches around the 64-request limit of the wave-parallel request lookup,
+    with tiny and empty requests so one chunk crosses many request ends."""
+    rng = np.random.default_rng(nreq * 7 + R)
+    lens = rng.integers(0, 6, nreq)
+    lens[rng.integers(nreq)] = 0
+    lens[-1] = max(int(lens[-1]), 1)
+    g = wl.Geometry(1, 2, R // 256, 128, "bf16")
+    S = int(lens.sum()) + 40
+    perm_s, perm_d = rng.permutation(S), rng.permutation(S)
+    ls, ld, pos = [], [], 0
+    for n in lens:
+        ls.append(perm_s[pos:pos + n])
+        ld.append(perm_d[pos:pos + n])
+        pos += int(n)
+    case = wl.PagedCase(f"lookup_{nreq}", g, wl.csr_from_lengths(lens),
+                        wl.side_from_slot_lists(ls, S), wl.side_from_slot_lists(ld, S), 0, 0, 0)
+    run_paged_case(case, nreq)
+
+
 def test_more_than_128_planes():
     # Q = 160 planes: the host splits the launch into plane ranges of 128
     case = wl.random_case(77, geom=wl.Geometry(80, 2, 1, 8, "bf16"), max_reqs=3, max_len=40,
