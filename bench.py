@@ -525,10 +525,10 @@ def main():
     ident_ms = ce[0].elapsed_time(ce[1]) / ncopy
 
     dom = max(OPS, key=lambda o: op_ms[o])
-    kernel_of = {"gather_scatter": "k_paged<PoolRef, PoolRef, 2, 8>",
-                 "gather": "k_paged<PoolRef, StageRef, 2, 8>",
-                 "scatter": "k_paged<StageRef, PoolRef, 2, 8>",
-                 "rebuild": "k_permute<true, 0, 0>", "extract": "k_permute<false, 0, 0>"}
+    kernel_of = {"gather_scatter": "k_paged<PoolRef, PoolRef, 2, 4>",
+                 "gather": "k_paged<PoolRef, StageRef, 2, 4>",
+                 "scatter": "k_paged<StageRef, PoolRef, 2, 4>",
+                 "rebuild": "k_permute_rows<true, 2, 4>", "extract": "k_permute_rows<false, 2, 4>"}
     achieved = wk.op_bytes / (op_ms[dom] * 1e-3) / 1e9
     traffic, traffic_kernel = read_traffic()
     if traffic is not None and traffic_kernel and "PoolRef, kvx::PoolRef" not in traffic_kernel:

@@ -3,7 +3,7 @@
 // All five calls are one row-moving kernel with a different address
 // resolver.  The work of a call is split into chunks of U units (a unit is
 // one row of R bytes, or one head row of head_dim elements for the permutes),
-// each chunk sized to about 16 KiB.  A wave takes one chunk at a time:
+// each chunk sized to about 8 KiB.  A wave takes one chunk at a time:
 //
 //   1. resolve: lane u < U computes unit u's source and destination byte
 //      addresses from the tables (token -> request by a search over tok_off,
@@ -38,9 +38,12 @@
 
 namespace kvx {
 
-// Tuning knobs (compile-time; the defaults are the measured best).
+// Tuning knobs (compile-time; the defaults are the measured best).  Chunk
+// size, averaged over repeated runs of all five workloads: 4, 8 and 12 KiB
+// are within noise of each other and 6% ahead of 16 KiB on the five-op step
+// of the 2048-token request; 8 KiB has the best mean.
 #ifndef KVX_CHUNK_KIB
-#define KVX_CHUNK_KIB 16           // bytes a wave moves per chunk, in KiB
+#define KVX_CHUNK_KIB 8            // bytes a wave moves per chunk, in KiB
 #endif
 #ifndef KVX_LOAD_NT
 #define KVX_LOAD_NT 1              // nontemporal loads

@@ -9,9 +9,10 @@ Independent references used here:
 * element-by-element Python loops over [Q][slots][H][D] arrays;
 * ``numpy.take`` (page size 1: gather is a row take per plane);
 * page tables expanded into explicit slot lists built from whole pages;
-* the permute expressions printed on the mini-infer PD page (section
-  "KV 序列化格式选择"): ``x[0, :, :seq, :].permute(1, 0, 2)`` and
-  ``k.permute(1, 0, 2).unsqueeze(0)``, evaluated by torch on the CPU;
+* the permute the mini-infer PD page describes (section "KV 序列化格式选择"):
+  batch 0 and the first seq positions, head and sequence axes swapped, and
+  its inverse with a leading unit axis -- evaluated with torch's axis moves
+  on the CPU;
 * round trips, untouched-byte invariants and the page-printed byte counts.
 """
 from __future__ import annotations
@@ -447,9 +448,10 @@ def _torch():
 
 
 def check_permute_torch():
-    """Extract equals x[0, :, :seq, :].permute(1, 0, 2) per plane; rebuild
-    equals k.permute(1, 0, 2).unsqueeze(0) written into positions < seq, with
-    positions >= seq untouched (mini-infer PD page, "KV 序列化格式选择")."""
+    """Extract equals torch's swap of the head and sequence axes of batch 0,
+    cut to the first seq positions, per plane; rebuild equals the swap back
+    with a leading unit axis, written into positions < seq, with positions
+    >= seq untouched (mini-infer PD page, "KV 序列化格式选择")."""
     torch = _torch()
     rng = np.random.default_rng(20)
     for Q, H, S_cap, seq, D in [(3, 2, 9, 9, 8), (2, 3, 12, 7, 16), (4, 1, 5, 5, 8),
@@ -460,7 +462,7 @@ def check_permute_torch():
                                S_cap, seq, out.view(np.uint8))
         for q in range(Q):
             x = torch.from_numpy(hf[q].astype(np.int32))
-            ref = x[0, :, :seq, :].permute(1, 0, 2).contiguous().numpy().astype(np.uint16)
+            ref = torch.movedim(x.squeeze(0), 1, 0)[:seq].contiguous().numpy().astype(np.uint16)
             assert np.array_equal(out.reshape(Q, seq, H, D)[q], ref)
         flat = rng.integers(0, 1 << 16, size=(Q, seq, H, D), dtype=np.uint16)
         tgt = rng.integers(0, 1 << 16, size=(Q, 1, H, S_cap, D), dtype=np.uint16)
@@ -469,7 +471,7 @@ def check_permute_torch():
                                [tgt[q].reshape(-1).view(np.uint8) for q in range(Q)], S_cap)
         for q in range(Q):
             k = torch.from_numpy(flat[q].astype(np.int32))
-            ref = k.permute(1, 0, 2).unsqueeze(0).numpy().astype(np.uint16)
+            ref = k.transpose(0, 1)[None].contiguous().numpy().astype(np.uint16)
             assert np.array_equal(tgt[q][:, :, :seq], ref)
             assert np.array_equal(tgt[q][:, :, seq:], before[q][:, :, seq:])
         # round trips
