@@ -41,10 +41,14 @@ def bind(path: str):
                                    ctypes.c_int]
     lib.oracle_gather_scatter.argtypes = [_i32, _i64, pp, _i64, _i32, _i64, _p, _p, _i32, _p,
                                           pp, _i64, _i32, _i64, _p, _p, ctypes.c_int]
+    lib.oracle_gather_scatter_heads.argtypes = [
+        _i32, _i32, _i64, pp, _i64, _i32, _i64, _p, _p, _i32, _i32, _i32, _i32, _p,
+        pp, _i64, _i32, _i64, _p, _p, _i32, _i32, _i32, ctypes.c_int]
     lib.oracle_extract_permute.argtypes = [_i32, _i32, _i64, pp, _i64, _i64, _p, ctypes.c_int]
     lib.oracle_rebuild_permute.argtypes = [_i32, _i32, _i64, _p, _i64, pp, _i64, ctypes.c_int]
     for f in (lib.oracle_gather, lib.oracle_scatter, lib.oracle_gather_scatter,
-              lib.oracle_extract_permute, lib.oracle_rebuild_permute):
+              lib.oracle_gather_scatter_heads, lib.oracle_extract_permute,
+              lib.oracle_rebuild_permute):
         f.restype = _i64
     return lib
 
@@ -152,6 +156,34 @@ def gather_scatter(src_planes: Sequence[np.ndarray], src_stride: int, src_page_s
         src_num_pages, _ptr(src_pg_off), _ptr(src_ids), reqs, _ptr(tok_off),
         _ptr_array(dst_planes), dst_stride, dst_page_size, dst_num_pages, _ptr(dst_pg_off),
         _ptr(dst_ids), nthreads))
+
+
+def gather_scatter_heads(src_planes: Sequence[np.ndarray], src_stride: int, src_page_size: int,
+                         src_num_pages: int, src_pg_off, src_ids, src_heads, head_bytes: int,
+                         nh: int, tok_off, dst_planes: Sequence[np.ndarray], dst_stride: int,
+                         dst_page_size: int, dst_num_pages: int, dst_pg_off, dst_ids, dst_heads,
+                         nthreads: int = 1) -> int:
+    """Pool -> pool, nh heads of every token row.  ``src_heads`` / ``dst_heads``
+    are (kv_heads, head0, hnd) per side: heads per token row in that pool, the
+    first head of the slice, and 1 for head-major (HND) blocks.  ``*_stride`` is
+    the bytes of one token row.  Returns the number of skipped token rows."""
+    tok_off = _csr(tok_off, np.int64)
+    src_pg_off, dst_pg_off = _csr(src_pg_off, np.int64), _csr(dst_pg_off, np.int64)
+    src_ids, dst_ids = _csr(src_ids, np.int32), _csr(dst_ids, np.int32)
+    reqs = len(tok_off) - 1
+    _check_table("src", reqs, tok_off, src_pg_off, src_ids, src_page_size)
+    _check_table("dst", reqs, tok_off, dst_pg_off, dst_ids, dst_page_size)
+    for name, (H, h0, hnd), stride in (("src", src_heads, src_stride),
+                                        ("dst", dst_heads, dst_stride)):
+        if h0 < 0 or h0 + nh > H or stride < H * head_bytes:
+            raise ValueError(f"{name}: head slice outside the row")
+    _check_planes("src", src_planes, src_stride, src_page_size, src_num_pages, src_stride)
+    _check_planes("dst", dst_planes, dst_stride, dst_page_size, dst_num_pages, dst_stride)
+    return int(_load().oracle_gather_scatter_heads(
+        len(src_planes), nh, head_bytes, _ptr_array(src_planes), src_stride, src_page_size,
+        src_num_pages, _ptr(src_pg_off), _ptr(src_ids), *src_heads, reqs, _ptr(tok_off),
+        _ptr_array(dst_planes), dst_stride, dst_page_size, dst_num_pages, _ptr(dst_pg_off),
+        _ptr(dst_ids), *dst_heads, nthreads))
 
 
 def extract_permute(hf_planes: Sequence[np.ndarray], kv_heads: int, head_bytes: int,

@@ -14,7 +14,8 @@
  *             发生了什么" (smarter.xin): section "KV 序列化格式选择".
  *   [survey]  "PD分离调研：从推理阶段拆分到Mooncake的KVCache中心架构"
  *             (gentlecold.top): sections 7.4 (registering the per-layer KV
- *             cache addresses) and 7.6 (P writes KV blocks into D).
+ *             cache addresses), 7.6 (P writes KV blocks into D) and 7.7
+ *             (the transfer plan for P and D with different TP sizes).
  *
  * What it computes (every function is a bitwise copy; no arithmetic touches
  * the KV values, so fp16 / bf16 / NaN payloads pass through unchanged):
@@ -219,6 +220,127 @@ int64_t oracle_gather_scatter(int32_t Q, int64_t R,
     j.dst.planes = dst_planes; j.dst.stride = dst_stride; j.dst.page_size = dst_page_size;
     j.dst.num_pages = dst_num_pages; j.dst.pg_off = dst_pg_off; j.dst.ids = dst_ids;
     return run_split(j, nthreads);
+}
+
+/* ---------------------------------------------------- head-sliced copies -- */
+
+/* Head-sliced gather-scatter ([survey] 7.7).  When P and D run with different
+ * tensor-parallel sizes, a rank holds kv_heads / tp heads of every row, and a
+ * P rank and a D rank move only the heads they share: a contiguous head range
+ * that starts at one head in the source rows and at another in the
+ * destination rows.  The same section notes that non-MLA models then keep
+ * each block head-major (HND), which makes one head of one block contiguous.
+ *
+ * A pool side: H heads per token row, the slice starts at head h0, and a page
+ * of B tokens is laid out token-major (NHD: [B][H][D]) or head-major (HND:
+ * [H][B][D]); stride is the bytes of one token row (H * Db when dense), so a
+ * page spans B * stride bytes.  Byte offset of head h of token t in a page:
+ *     NHD: (page * B + t % B) * stride + h * Db
+ *     HND: page * B * stride + (h * B + t % B) * Db
+ * For every request r, plane q, token t < n_r and j < nh, the Db bytes of
+ * source head h0_src + j go to destination head h0_dst + j.  A token whose
+ * page id is out of range on either side is skipped (all nh heads) and
+ * counted once. */
+typedef struct {
+    uint8_t* const* planes;
+    int64_t stride;
+    int32_t page_size;
+    int64_t num_pages;
+    const int64_t* pg_off;
+    const int32_t* ids;
+    int32_t H, h0, hnd;
+} head_side;
+
+typedef struct {
+    int32_t Q, nh;
+    int64_t Db;
+    int32_t num_reqs;
+    const int64_t* tok_off;
+    head_side src, dst;
+    int64_t first_pair, last_pair;
+    int64_t skipped;
+} head_job;
+
+/* Byte offset of head h of token t of request r within its plane, or -1 when
+ * the page id is out of range. */
+static int64_t head_offset(const head_side* s, int64_t Db, int64_t r, int64_t t, int64_t h)
+{
+    int64_t page = (int64_t)s->ids[s->pg_off[r] + t / s->page_size];
+    if (page < 0 || page >= s->num_pages) return -1;
+    int64_t row = t % s->page_size;
+    if (s->hnd) return page * s->page_size * s->stride + (h * s->page_size + row) * Db;
+    return (page * s->page_size + row) * s->stride + h * Db;
+}
+
+static void* run_heads(void* arg)
+{
+    head_job* j = (head_job*)arg;
+    int64_t skipped = 0;
+    for (int64_t pair = j->first_pair; pair < j->last_pair; ++pair) {
+        int64_t r = pair / j->Q;
+        int64_t q = pair % j->Q;
+        int64_t n = j->tok_off[r + 1] - j->tok_off[r];
+        for (int64_t t = 0; t < n; ++t) {
+            if (head_offset(&j->src, j->Db, r, t, j->src.h0) < 0 ||
+                head_offset(&j->dst, j->Db, r, t, j->dst.h0) < 0) {
+                ++skipped;
+                continue;
+            }
+            for (int32_t k = 0; k < j->nh; ++k) {
+                int64_t so = head_offset(&j->src, j->Db, r, t, j->src.h0 + k);
+                int64_t d = head_offset(&j->dst, j->Db, r, t, j->dst.h0 + k);
+                memcpy(j->dst.planes[q] + d, j->src.planes[q] + so, (size_t)j->Db);
+            }
+        }
+    }
+    j->skipped = skipped;
+    return NULL;
+}
+
+int64_t oracle_gather_scatter_heads(int32_t Q, int32_t nh, int64_t Db,
+                                    uint8_t* const* src_planes, int64_t src_stride,
+                                    int32_t src_page_size, int64_t src_num_pages,
+                                    const int64_t* src_pg_off, const int32_t* src_ids,
+                                    int32_t src_H, int32_t src_h0, int32_t src_hnd,
+                                    int32_t num_reqs, const int64_t* tok_off,
+                                    uint8_t* const* dst_planes, int64_t dst_stride,
+                                    int32_t dst_page_size, int64_t dst_num_pages,
+                                    const int64_t* dst_pg_off, const int32_t* dst_ids,
+                                    int32_t dst_H, int32_t dst_h0, int32_t dst_hnd,
+                                    int nthreads)
+{
+    head_job proto;
+    memset(&proto, 0, sizeof proto);
+    proto.Q = Q; proto.nh = nh; proto.Db = Db; proto.num_reqs = num_reqs; proto.tok_off = tok_off;
+    head_side s = {src_planes, src_stride, src_page_size, src_num_pages, src_pg_off, src_ids,
+                   src_H, src_h0, src_hnd};
+    head_side d = {dst_planes, dst_stride, dst_page_size, dst_num_pages, dst_pg_off, dst_ids,
+                   dst_H, dst_h0, dst_hnd};
+    proto.src = s;
+    proto.dst = d;
+    int64_t pairs = (int64_t)num_reqs * Q;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (pairs < nthreads) nthreads = pairs > 0 ? (int)pairs : 1;
+    head_job jobs[256];
+    pthread_t tids[256];
+    int started[256];
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = proto;
+        jobs[i].first_pair = pairs * i / nthreads;
+        jobs[i].last_pair = pairs * (i + 1) / nthreads;
+        started[i] = 0;
+    }
+    for (int i = 1; i < nthreads; ++i)
+        started[i] = pthread_create(&tids[i], NULL, run_heads, &jobs[i]) == 0;
+    run_heads(&jobs[0]);
+    for (int i = 1; i < nthreads; ++i) {
+        if (started[i]) pthread_join(tids[i], NULL);
+        else run_heads(&jobs[i]);
+    }
+    int64_t total = 0;
+    for (int i = 0; i < nthreads; ++i) total += jobs[i].skipped;
+    return total;
 }
 
 /* ------------------------------------------------------------- permutes -- */

@@ -442,6 +442,132 @@ def check_oor_boundaries():
     assert np.array_equal(out2[:, P * B:], pool[:, P * B:])
 
 
+# -------------------------------------------------- head-sliced copies --
+
+def head_view(pool_bytes, Q, P, B, H, D, hnd):
+    """uint16 view [Q, pages, B, H, D] (NHD) or [Q, pages, H, B, D] (HND)."""
+    w = pool_bytes.view(np.uint16)
+    return w.reshape(Q, P, H, B, D) if hnd else w.reshape(Q, P, B, H, D)
+
+
+def o_heads(case, src_b, dst_b, sH, sh0, shnd, dH, dh0, dhnd, nh, D, nthreads=1):
+    Q = case.geom.planes
+    Db = D * 2
+    return oracle.gather_scatter_heads(
+        [src_b[q] for q in range(Q)], sH * Db, case.src.page_size, case.src.num_pages,
+        case.src.pg_off, case.src.ids, (sH, sh0, shnd), Db, nh, case.tok_off,
+        [dst_b[q] for q in range(Q)], dH * Db, case.dst.page_size, case.dst.num_pages,
+        case.dst.pg_off, case.dst.ids, (dH, dh0, dhnd), nthreads)
+
+
+def heads_case(seed, oor=0.0):
+    rng = np.random.default_rng(seed)
+    D = int(rng.choice([8, 16]))
+    sH, dH = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+    nh = int(rng.integers(1, min(sH, dH) + 1))
+    sh0, dh0 = int(rng.integers(0, sH - nh + 1)), int(rng.integers(0, dH - nh + 1))
+    shnd, dhnd = int(rng.integers(0, 2)), int(rng.integers(0, 2))
+    case = wl.random_case(seed, geom=wl.Geometry(int(rng.integers(1, 3)), 2, nh, D), max_reqs=3,
+                          max_len=12, src_page=int(rng.choice([1, 2, 4])),
+                          dst_page=int(rng.choice([1, 3, 4])), oor_frac=oor, slack_pages=2)
+    return case, D, (sH, sh0, shnd), (dH, dh0, dhnd), nh
+
+
+def check_heads_bruteforce():
+    """Element by element over NHD / HND views of both pools."""
+    for seed in range(24):
+        case, D, (sH, sh0, shnd), (dH, dh0, dhnd), nh = heads_case(900 + seed,
+                                                                   oor=0.2 if seed % 3 else 0)
+        rng = np.random.default_rng(seed)
+        Q = case.geom.planes
+        Ps, Pd, Bs, Bd = case.src.num_pages, case.dst.num_pages, case.src.page_size, \
+            case.dst.page_size
+        src_b = rng.integers(0, 256, (Q, Ps * Bs * sH * D * 2), dtype=np.uint8)
+        dst_b = rng.integers(0, 256, (Q, Pd * Bd * dH * D * 2), dtype=np.uint8)
+        got = dst_b.copy()
+        skipped = o_heads(case, src_b, got, sH, sh0, shnd, dH, dh0, dhnd, nh, D)
+        sv = head_view(src_b, Q, Ps, Bs, sH, D, shnd)
+        exp = dst_b.copy()
+        dv = head_view(exp, Q, Pd, Bd, dH, D, dhnd)
+        bf_skip = 0
+        for r in range(case.num_reqs):
+            for t in range(int(case.lengths[r])):
+                ps = int(case.src.ids[case.src.pg_off[r] + t // Bs])
+                pd = int(case.dst.ids[case.dst.pg_off[r] + t // Bd])
+                for q in range(Q):
+                    if not (0 <= ps < Ps and 0 <= pd < Pd):
+                        bf_skip += 1
+                        continue
+                    for j in range(nh):
+                        for e in range(D):
+                            v = (sv[q, ps, sh0 + j, t % Bs, e] if shnd
+                                 else sv[q, ps, t % Bs, sh0 + j, e])
+                            if dhnd:
+                                dv[q, pd, dh0 + j, t % Bd, e] = v
+                            else:
+                                dv[q, pd, t % Bd, dh0 + j, e] = v
+        assert skipped == bf_skip, seed
+        assert np.array_equal(got, exp), seed
+
+
+def check_heads_full_row_is_row_copy():
+    """Slice = whole row, NHD on both sides: the pinned row gather-scatter."""
+    rng = np.random.default_rng(24)
+    for seed in range(4):
+        case = wl.random_case(950 + seed, geom=wl.Geometry(2, 2, 3, 8), max_reqs=3, max_len=20)
+        g = case.geom
+        src, dst = pools_for(case, rng)
+        a, b = dst.copy(), dst.copy()
+        o_gather_scatter(src, case, a)
+        Q = g.planes
+        sb = src.reshape(Q, -1).view(np.uint8)
+        bb = b.reshape(Q, -1).view(np.uint8)
+        o_heads(case, sb, bb, 3, 0, 0, 3, 0, 0, 3, 8)
+        assert np.array_equal(a, b)
+
+
+def check_heads_layout_conversion():
+    """NHD -> HND with the whole row equals numpy's per-page transpose of the
+    row-copied result."""
+    rng = np.random.default_rng(25)
+    case = wl.random_case(960, geom=wl.Geometry(1, 2, 4, 8), max_reqs=3, max_len=30,
+                          src_page=4, dst_page=4)
+    g = case.geom
+    Q, H, D, B = g.planes, 4, 8, 4
+    src, dst = pools_for(case, rng)
+    ref = dst.copy()
+    o_gather_scatter(src, case, ref)                     # NHD result
+    P = case.dst.num_pages
+    dst_hnd = np.ascontiguousarray(dst.reshape(Q, P, B, H, D).transpose(0, 1, 3, 2, 4))
+    got = dst_hnd.reshape(Q, -1).view(np.uint8).copy()
+    o_heads(case, src.reshape(Q, -1).view(np.uint8), got, H, 0, 0, H, 0, 1, H, D)
+    back = got.view(np.uint16).reshape(Q, P, H, B, D).transpose(0, 1, 3, 2, 4)
+    assert np.array_equal(np.ascontiguousarray(back).reshape(ref.shape), ref)
+
+
+def check_heads_tp_merge_and_split():
+    """Two P shards of H/2 heads into one D pool of H heads (two calls) equal
+    one row copy from the unsharded pool; one P pool split into two D shards
+    equals the row copy cut in halves."""
+    rng = np.random.default_rng(26)
+    case = wl.random_case(970, geom=wl.Geometry(2, 2, 4, 8), max_reqs=3, max_len=25,
+                          src_page=2, dst_page=4)
+    Q, H, D = case.geom.planes, 4, 8
+    full_src, dst = pools_for(case, rng)
+    ref = dst.copy()
+    o_gather_scatter(full_src, case, ref)
+    shards = [np.ascontiguousarray(full_src[..., 2 * k:2 * k + 2, :]) for k in range(2)]
+    merged = dst.copy().reshape(Q, -1).view(np.uint8)
+    for k, sh in enumerate(shards):
+        o_heads(case, sh.reshape(Q, -1).view(np.uint8), merged, 2, 0, 0, 4, 2 * k, 0, 2, D)
+    assert np.array_equal(merged.view(np.uint16).reshape(ref.shape), ref)
+    for k in range(2):
+        part = np.ascontiguousarray(dst[..., 2 * k:2 * k + 2, :])
+        pb = part.reshape(Q, -1).view(np.uint8)
+        o_heads(case, full_src.reshape(Q, -1).view(np.uint8), pb, 4, 2 * k, 0, 2, 0, 0, 2, D)
+        assert np.array_equal(pb.view(np.uint16).reshape(part.shape), ref[..., 2 * k:2 * k + 2, :])
+
+
 def _torch():
     import torch
     return torch
@@ -557,4 +683,8 @@ ALL_CHECKS = [
     check_numpy_transpose,
     check_closed_form_sizes,
     check_oor_boundaries,
+    check_heads_bruteforce,
+    check_heads_full_row_is_row_copy,
+    check_heads_layout_conversion,
+    check_heads_tp_merge_and_split,
 ]

@@ -37,6 +37,11 @@ MUTANTS = {
     "permute_runs_to_s_cap": ("for (int64_t s = 0; s < j->seq; ++s)",
                               "for (int64_t s = 0; s < j->s_cap; ++s)"),
     "skip_not_counted": ("if (s < 0) { ++skipped; continue; }", "if (s < 0) { continue; }"),
+    "hnd_index_swapped": ("(h * s->page_size + row) * Db", "(row * s->H + h) * Db"),
+    "nhd_head_offset_dropped": ("(page * s->page_size + row) * s->stride + h * Db",
+                                "(page * s->page_size + row) * s->stride"),
+    "dst_slice_uses_src_h0": ("head_offset(&j->dst, j->Db, r, t, j->dst.h0 + k)",
+                              "head_offset(&j->dst, j->Db, r, t, j->src.h0 + k)"),
 }
 
 DRIVER = r"""
