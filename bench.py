@@ -371,6 +371,28 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
             del hf, fl
             torch.cuda.empty_cache()
 
+        # head-sliced: P at TP=1 (8 heads, HND page 16) -> two D ranks at TP=2
+        c = wl.hetero_tp_case()
+        D, B = c.geom.head_dim, c.src.page_size
+        Db = c.geom.head_bytes
+        A = torch.empty((c.geom.planes, c.src.num_pages * B * 8 * Db), dtype=torch.uint8,
+                        device=dev)
+        Ds = [torch.empty((c.geom.planes, c.dst.num_pages * B * 4 * Db), dtype=torch.uint8,
+                          device=dev) for _ in range(2)]
+        for t in [A] + Ds:
+            wdev.fill_hash(t, 5, stream=stream)
+        reqs = kvx.Requests(d(c.tok_off), c.total_tokens)
+        ts, td = kvx.Table(d(c.src.pg_off), d(c.src.ids)), kvx.Table(d(c.dst.pg_off), d(c.dst.ids))
+        lay = lay_of(c.geom)
+        PA = kvx.Pool(A, c.src.num_pages, B, slot_stride=8 * Db)
+        PD = [kvx.Pool(t, c.dst.num_pages, B, slot_stride=4 * Db) for t in Ds]
+        emit(c.name, "gather_scatter_heads", timed(lambda i: kvx.gather_scatter_heads(
+            lay, PA, ts, kvx.Heads(8, 4 * (i % 2), "hnd"), reqs, PD[i % 2], td,
+            kvx.Heads(4, 0, "hnd"), stream=stream), reps * 2), 2 * c.payload_bytes(),
+             f"{c.num_reqs} requests, {c.total_tokens} tokens, 4 of 8 heads per launch")
+        del A, Ds, PA, PD
+        torch.cuda.empty_cache()
+
         # 5: 64 requests, page-16 block pools of 36 GiB, one gather-scatter
         c = wl.config5()
         g = c.geom

@@ -19,7 +19,8 @@
  *             transfers submitted at once), 7.4 (per-layer cache base
  *             addresses and block length = tensor bytes / num_blocks), 7.6
  *             (P builds src/dst/length lists from block ids and writes D's
- *             KV blocks directly).
+ *             KV blocks directly), 7.7 (P and D with different tensor-parallel
+ *             sizes move the head ranges they share; head-major blocks).
  *   [distserve] "DistServe 完全拆解：拆开 Prefill 与 Decode，按 Goodput 调度大模型
  *             推理" (pinghaoyang.com.cn): "KV Cache 跨实例传输：省下重算，付出通信"
  *             (bytes per request = 2 x prompt length x layers x KV heads x
@@ -84,7 +85,7 @@
 extern "C" {
 #endif
 
-#define KVX_ABI_VERSION 1
+#define KVX_ABI_VERSION 2
 
 typedef enum kvx_status {
     KVX_OK = 0,
@@ -172,6 +173,47 @@ kvx_status kvx_gather_scatter(const kvx_layout* layout,
                               const kvx_reqs* reqs,
                               const kvx_pool* dst, const kvx_table* dst_table,
                               unsigned long long* skipped, hipStream_t stream);
+
+/* Block layout of a page in a head-sliced copy ([survey] 7.7: for P and D
+ * with different tensor-parallel sizes, non-MLA models keep each block
+ * head-major, so that one head of one block is contiguous). */
+typedef enum kvx_block_layout {
+    KVX_NHD = 0,            /* page = [page_size][kv_heads][head_dim] (token-major) */
+    KVX_HND = 1             /* page = [kv_heads][page_size][head_dim] (head-major) */
+} kvx_block_layout;
+
+/* Which heads of every token row a head-sliced copy reads or writes in one
+ * pool.  With that pool's kvx_pool, slot_stride is the bytes of one token row
+ * (>= kv_heads * head_dim * element size), so a page spans page_size *
+ * slot_stride bytes; head h of token t of a page then starts at
+ *   NHD: (page * page_size + t % page_size) * slot_stride + h * Db
+ *   HND: page * page_size * slot_stride + (h * page_size + t % page_size) * Db
+ * from the plane base, Db = head_dim * element size.  Each plane of a pool
+ * used in a head-sliced copy must span whole pages: num_pages * page_size *
+ * slot_stride bytes. */
+typedef struct kvx_heads {
+    int32_t kv_heads;       /* heads per token row in this pool (one TP shard's count) */
+    int32_t head0;          /* first head of the slice; head0 + slice width <= kv_heads */
+    int32_t block_layout;   /* a kvx_block_layout */
+} kvx_heads;
+
+/* Head-sliced gather-scatter ([survey] 7.7): when P and D shard the KV heads
+ * over different tensor-parallel sizes, a P rank and a D rank move only the
+ * heads they share -- a contiguous range starting at src_heads->head0 in the
+ * source rows and at dst_heads->head0 in the destination rows.  For every
+ * request, plane and token, layout->kv_heads heads (the slice width) are
+ * copied, head by head, from pool `src` to pool `dst`; either side may use
+ * NHD or HND blocks (so a whole-row slice also converts between the two).
+ * A token whose page id is out of range on either side is skipped and
+ * counted once.  Requires head_dim * element size to be a multiple of 16
+ * bytes.  One launch (two or more only when Q > 128). */
+kvx_status kvx_gather_scatter_heads(const kvx_layout* layout,
+                                    const kvx_pool* src, const kvx_table* src_table,
+                                    const kvx_heads* src_heads,
+                                    const kvx_reqs* reqs,
+                                    const kvx_pool* dst, const kvx_table* dst_table,
+                                    const kvx_heads* dst_heads,
+                                    unsigned long long* skipped, hipStream_t stream);
 
 /* Extract permute ([mini]): for each plane q, hf_planes[q] is a DEVICE
  * [1][H][s_cap][D] tensor (batch 1, contiguous); write

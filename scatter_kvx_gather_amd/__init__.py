@@ -17,9 +17,9 @@ from typing import Optional, Sequence, Union
 
 import torch
 
-__all__ = ["KvxError", "Layout", "Pool", "Requests", "Table", "gather", "scatter",
-           "gather_scatter", "extract_permute", "rebuild_permute", "library_path",
-           "DTYPE_CODES", "load_library"]
+__all__ = ["KvxError", "Layout", "Pool", "Requests", "Table", "Heads", "gather", "scatter",
+           "gather_scatter", "gather_scatter_heads", "extract_permute", "rebuild_permute",
+           "library_path", "DTYPE_CODES", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkvx.so")
@@ -58,6 +58,11 @@ class _CTable(ctypes.Structure):
                 ("num_ids", ctypes.c_int64)]
 
 
+class _CHeads(ctypes.Structure):
+    _fields_ = [("kv_heads", ctypes.c_int32), ("head0", ctypes.c_int32),
+                ("block_layout", ctypes.c_int32)]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -76,10 +81,13 @@ def load_library():
     lib.kvx_scatter.argtypes = [P(_CLayout), vp, p64, P(_CReqs), P(_CPool), P(_CTable), vp, vp]
     lib.kvx_gather_scatter.argtypes = [P(_CLayout), P(_CPool), P(_CTable), P(_CReqs),
                                        P(_CPool), P(_CTable), vp, vp]
+    lib.kvx_gather_scatter_heads.argtypes = [P(_CLayout), P(_CPool), P(_CTable), P(_CHeads),
+                                             P(_CReqs), P(_CPool), P(_CTable), P(_CHeads), vp,
+                                             vp]
     lib.kvx_extract_permute.argtypes = [P(_CLayout), P(vp), p64, p64, vp, p64, vp]
     lib.kvx_rebuild_permute.argtypes = [P(_CLayout), vp, p64, p64, P(vp), p64, vp]
     for f in (lib.kvx_gather, lib.kvx_scatter, lib.kvx_gather_scatter,
-              lib.kvx_extract_permute, lib.kvx_rebuild_permute):
+              lib.kvx_gather_scatter_heads, lib.kvx_extract_permute, lib.kvx_rebuild_permute):
         f.restype = ctypes.c_int
     lib.kvx_status_str.argtypes = [ctypes.c_int]
     lib.kvx_status_str.restype = ctypes.c_char_p
@@ -175,7 +183,10 @@ class Pool:
             if row_bytes is None:
                 if not isinstance(planes, torch.Tensor):
                     raise ValueError("slot_stride or row_bytes is needed for pointer lists")
-                row_bytes = planes[0].numel() * planes.element_size() // (num_pages * page_size)
+                slots = num_pages * page_size
+                if slots <= 0:
+                    raise ValueError("an empty pool needs an explicit slot_stride")
+                row_bytes = planes[0].numel() * planes.element_size() // slots
             slot_stride = row_bytes
         self.num_pages, self.page_size, self.slot_stride = num_pages, page_size, slot_stride
         self._c = _CPool(ctypes.cast(self._arr, ctypes.POINTER(ctypes.c_void_p)), num_pages,
@@ -203,6 +214,18 @@ class Table:
         self.pg_off, self.page_ids = pg_off, page_ids
         self._c = _CTable(_ptr(pg_off), _ptr(page_ids) if page_ids.numel() else 0,
                           page_ids.numel())
+
+
+class Heads:
+    """The head slice one pool side of a head-sliced copy reads or writes:
+    ``kv_heads`` per token row in that pool, slice start ``head0``, and the
+    block layout, "nhd" ([page_size][H][D]) or "hnd" ([H][page_size][D])."""
+
+    def __init__(self, kv_heads: int, head0: int = 0, block_layout: str = "nhd"):
+        if block_layout not in ("nhd", "hnd"):
+            raise ValueError('block_layout is "nhd" or "hnd"')
+        self.kv_heads, self.head0, self.block_layout = kv_heads, head0, block_layout
+        self._c = _CHeads(kv_heads, head0, 0 if block_layout == "nhd" else 1)
 
 
 def gather(layout: Layout, src: Pool, src_table: Table, reqs: Requests, staging: torch.Tensor,
@@ -233,6 +256,21 @@ def gather_scatter(layout: Layout, src: Pool, src_table: Table, reqs: Requests, 
                                   ctypes.byref(src_table._c), ctypes.byref(reqs._c),
                                   ctypes.byref(dst._c), ctypes.byref(dst_table._c),
                                   _ptr(skipped), _stream(stream)), "kvx_gather_scatter")
+
+
+def gather_scatter_heads(layout: Layout, src: Pool, src_table: Table, src_heads: Heads,
+                         reqs: Requests, dst: Pool, dst_table: Table, dst_heads: Heads,
+                         skipped: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Pool -> pool, layout.kv_heads heads of every token row, from heads
+    src_heads.head0.. to dst_heads.head0.. (kvx_gather_scatter_heads).  The
+    pools' slot_stride is the bytes of one token row in that pool."""
+    lib = load_library()
+    _check(lib.kvx_gather_scatter_heads(ctypes.byref(layout._c), ctypes.byref(src._c),
+                                        ctypes.byref(src_table._c), ctypes.byref(src_heads._c),
+                                        ctypes.byref(reqs._c), ctypes.byref(dst._c),
+                                        ctypes.byref(dst_table._c), ctypes.byref(dst_heads._c),
+                                        _ptr(skipped), _stream(stream)),
+           "kvx_gather_scatter_heads")
 
 
 def extract_permute(layout: Layout, hf_planes: Union[torch.Tensor, Sequence], s_cap: int,

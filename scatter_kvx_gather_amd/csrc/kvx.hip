@@ -330,6 +330,79 @@ kvx_status run_permute(const Geom& g, void* const* hf, int64_t s_cap, int64_t se
     return KVX_OK;
 }
 
+kvx_status check_heads(const kvx_heads* h, const kvx_pool* p, const Geom& g) {
+    if (h == nullptr) return KVX_E_NULL;
+    if (h->block_layout != KVX_NHD && h->block_layout != KVX_HND) return KVX_E_SHAPE;
+    if (h->kv_heads < 1 || h->head0 < 0 || static_cast<int64_t>(h->head0) + g.H > h->kv_heads)
+        return KVX_E_SHAPE;
+    if (p->slot_stride < static_cast<int64_t>(h->kv_heads) * g.Db) return KVX_E_SHAPE;
+    int64_t page_bytes = 0, pool_bytes = 0;
+    if (!mul_ok(p->slot_stride, p->page_size, &page_bytes) ||
+        !mul_ok(page_bytes, p->num_pages, &pool_bytes))
+        return KVX_E_RANGE;
+    return KVX_OK;
+}
+
+kvx_status run_heads(const Geom& g, const kvx_reqs* reqs, const kvx_pool* src,
+                     const kvx_table* st, const kvx_heads* sh, const kvx_pool* dst,
+                     const kvx_table* dt, const kvx_heads* dh, unsigned long long* skipped,
+                     hipStream_t stream) {
+    if (reqs->total_tokens == 0) return KVX_OK;
+    int cus = 0;
+    kvx_status s = device_cus(&cus);
+    if (s != KVX_OK) return s;
+    // Chunk = Ut tokens x nhc heads of Db bytes, about kChunkBytes, <= 64 units.
+    int64_t units = kChunkBytes / g.Db;
+    if (units < 1) units = 1;
+    if (units > kWave) units = kWave;
+    const int32_t nhc = static_cast<int32_t>(g.H < units ? g.H : units);
+    const int32_t Ut = static_cast<int32_t>(units / nhc);
+    const int32_t hblocks = (g.H + nhc - 1) / nhc;
+    const uint64_t tblocks = (static_cast<uint64_t>(reqs->total_tokens) + Ut - 1) / Ut;
+    for (int32_t q0 = 0; q0 < g.Q; q0 += kTab) {
+        const int32_t nq = g.Q - q0 < kTab ? g.Q - q0 : kTab;
+        HeadArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.c.tok_off = reqs->tok_off;
+        a.c.skipped = skipped;
+        a.c.T = reqs->total_tokens;
+        a.c.num_reqs = reqs->num_reqs;
+        a.c.q0 = q0;
+        a.c.Q = g.Q;
+        a.c.R = static_cast<int32_t>(g.Db);
+        a.c.U = static_cast<uint32_t>(Ut * nhc);
+        const uint64_t cpp = tblocks * static_cast<uint64_t>(hblocks);
+        const uint64_t n = cpp * static_cast<uint64_t>(nq);
+        if (n >= (uint64_t(1) << 31)) return KVX_E_RANGE;
+        a.c.chunks_per_plane = static_cast<uint32_t>(cpp);
+        a.c.nchunks = static_cast<uint32_t>(n);
+        a.c.V = static_cast<uint32_t>(g.Db / 16);
+        a.c.v_magic = a.c.V == 1 ? 0u
+                                 : static_cast<uint32_t>(((uint64_t(1) << 32) + a.c.V - 1) / a.c.V);
+        fill_pool_ref(&a.src, src, st, q0, nq);
+        fill_pool_ref(&a.dst, dst, dt, q0, nq);
+        a.hs = HeadSide{sh->kv_heads, sh->head0, sh->block_layout == KVX_HND ? 1 : 0};
+        a.hd = HeadSide{dh->kv_heads, dh->head0, dh->block_layout == KVX_HND ? 1 : 0};
+        a.nh = g.H;
+        a.nhc = nhc;
+        a.Ut = Ut;
+        a.hblocks = hblocks;
+        a.head_major = (a.hs.hnd && a.hd.hnd) ? 1 : 0;
+        const uint32_t grid = grid_for(a.c.nchunks, cus);
+        if (log_enabled())
+            std::fprintf(stderr,
+                         "kvx: gather_scatter_heads Q=%d planes[%d,%d) nh=%d Db=%lld T=%lld "
+                         "src(H=%d h0=%d %s) dst(H=%d h0=%d %s) Ut=%d nhc=%d chunks=%u grid=%u\n",
+                         g.Q, q0, q0 + nq, g.H, static_cast<long long>(g.Db),
+                         static_cast<long long>(reqs->total_tokens), a.hs.H, a.hs.h0,
+                         a.hs.hnd ? "HND" : "NHD", a.hd.H, a.hd.h0, a.hd.hnd ? "HND" : "NHD",
+                         Ut, nhc, a.c.nchunks, grid);
+        s = launch(reinterpret_cast<const void*>(&k_heads), grid, a, stream);
+        if (s != KVX_OK) return s;
+    }
+    return KVX_OK;
+}
+
 kvx_status check_staging(const void* p, int64_t bytes, const Geom& g, const kvx_reqs* r) {
     int64_t need = 0;
     if (!mul_ok(r->total_tokens, static_cast<int64_t>(g.Q) * g.R, &need)) return KVX_E_RANGE;
@@ -403,6 +476,27 @@ kvx_status kvx_gather_scatter(const kvx_layout* layout,
     KVX_TRY(check_table(dst_table, reqs));
     return run_paged<PoolRef, PoolRef>(2, g, reqs, src, src_table, nullptr, dst, dst_table,
                                        nullptr, skipped, stream);
+}
+
+kvx_status kvx_gather_scatter_heads(const kvx_layout* layout,
+                                    const kvx_pool* src, const kvx_table* src_table,
+                                    const kvx_heads* src_heads,
+                                    const kvx_reqs* reqs,
+                                    const kvx_pool* dst, const kvx_table* dst_table,
+                                    const kvx_heads* dst_heads,
+                                    unsigned long long* skipped, hipStream_t stream) {
+    Geom g;
+    KVX_TRY(check_layout(layout, &g));
+    if (g.Db % 16 != 0) return KVX_E_ALIGN;
+    KVX_TRY(check_reqs(reqs));
+    KVX_TRY(check_pool(src, g));
+    KVX_TRY(check_table(src_table, reqs));
+    KVX_TRY(check_heads(src_heads, src, g));
+    KVX_TRY(check_pool(dst, g));
+    KVX_TRY(check_table(dst_table, reqs));
+    KVX_TRY(check_heads(dst_heads, dst, g));
+    return run_heads(g, reqs, src, src_table, src_heads, dst, dst_table, dst_heads, skipped,
+                     stream);
 }
 
 kvx_status kvx_extract_permute(const kvx_layout* layout, const void* const* hf_planes,

@@ -213,13 +213,10 @@ __device__ __forceinline__ const int64_t* pg_off_of<PoolRef>(const PoolRef& p) {
 // start from the lane that holds it.  No dependent loads.
 // Larger batches: a binary search for the chunk's first request, then a
 // per-lane walk, both over memory.
-template <class Src, class Dst>
-__device__ __forceinline__ ReqOf request_lookup(const PagedArgs<Src, Dst>& a, int64_t tok0,
-                                                int64_t tok, bool active, int lane) {
-    const Common& c = a.c;
+__device__ __forceinline__ ReqOf request_lookup(const Common& c, const int64_t* ps,
+                                                const int64_t* pd, int64_t tok0, int64_t tok,
+                                                bool active, int lane) {
     const int32_t nr = c.num_reqs;
-    const int64_t* ps = pg_off_of(a.src);
-    const int64_t* pd = pg_off_of(a.dst);
     ReqOf q;
     if (nr <= kWave) {
         const int64_t tv = lane < nr ? c.tok_off[lane] : (lane == nr ? c.T : INT64_MAX);
@@ -312,7 +309,8 @@ __device__ __forceinline__ int resolve(const PagedArgs<Src, Dst>& a, const Paged
     const Common& c = a.c;
     const int64_t tok = k.tok0 + u;
     const bool active = u < c.U && tok < c.T;
-    const ReqOf q = request_lookup(a, k.tok0, tok, active, static_cast<int>(u));
+    const ReqOf q = request_lookup(c, pg_off_of(a.src), pg_off_of(a.dst), k.tok0, tok, active,
+                                   static_cast<int>(u));
     if (!active) return kNone;
     // a token range that contradicts total_tokens is never dereferenced
     if (q.off < 0 || tok < q.off || tok >= q.end || q.end > c.T) return kSkip;
@@ -320,6 +318,94 @@ __device__ __forceinline__ int resolve(const PagedArgs<Src, Dst>& a, const Paged
     const int64_t n_r = q.end - q.off;
     bool ok = SideAddr<Src>::get(a.src, c, k.ql, q.pg_src, q.off, n_r, t, s);
     ok = SideAddr<Dst>::get(a.dst, c, k.ql, q.pg_dst, q.off, n_r, t, d) && ok;
+    return ok ? kCopy : kSkip;
+}
+
+// ------------------------------------------------- head-sliced resolver --
+
+// One side of a head-sliced copy: heads per token row, slice start, layout.
+struct HeadSide {
+    int32_t H;
+    int32_t h0;
+    int32_t hnd;                // 1: head-major blocks [H][B][D]; 0: [B][H][D]
+};
+
+struct HeadArgs {
+    Common c;                   // R = head bytes Db, V = Db / 16, U = Ut * nhc
+    PoolRef src, dst;
+    HeadSide hs, hd;
+    int32_t nh;                 // heads moved per token row
+    int32_t nhc;                // heads per chunk
+    int32_t Ut;                 // tokens per chunk
+    int32_t hblocks;            // chunks across the heads of one token block
+    int32_t head_major;         // unit order within a chunk
+};
+
+// Address of head h of token t (page list of its request at pg_off_r) in
+// plane ql of a pool laid out in NHD or HND blocks; false when an index is
+// out of range.
+__device__ __forceinline__ bool head_addr(const PoolRef& p, int32_t ql, int64_t pg_off_r,
+                                          int64_t t, int64_t h, bool hnd, uint64_t Db,
+                                          uint64_t& addr) {
+    int64_t pidx, row;
+    if (p.page_shift >= 0) {
+        pidx = t >> p.page_shift;
+        row = t & ((int64_t(1) << p.page_shift) - 1);
+    } else {
+        pidx = t / p.page_size;
+        row = t - pidx * p.page_size;
+    }
+    int64_t idx = pg_off_r + pidx;
+    if (idx < 0 || idx >= p.num_ids) return false;
+    int64_t page = p.ids[idx];
+    if (page < 0 || page >= p.num_pages) return false;
+    const uint64_t base = reinterpret_cast<uint64_t>(p.plane[ql]);
+    const uint64_t B = static_cast<uint64_t>(p.page_size);
+    const uint64_t stride = static_cast<uint64_t>(p.stride);
+    if (hnd)
+        addr = base + static_cast<uint64_t>(page) * B * stride +
+               (static_cast<uint64_t>(h) * B + static_cast<uint64_t>(row)) * Db;
+    else
+        addr = base + (static_cast<uint64_t>(page) * B + static_cast<uint64_t>(row)) * stride +
+               static_cast<uint64_t>(h) * Db;
+    return true;
+}
+
+// Resolve unit u of a head-sliced chunk: (token, head) of Db bytes.  Called
+// with every lane active.  `first` is set for the slice's first head, so a
+// skipped token row is counted once.
+__device__ __forceinline__ int resolve_heads(const HeadArgs& a, uint32_t chunk, uint32_t u,
+                                             uint64_t& s, uint64_t& d, bool& first) {
+    const Common& c = a.c;
+    const uint32_t ql = chunk / c.chunks_per_plane;
+    const uint32_t rem = chunk - ql * c.chunks_per_plane;
+    const uint32_t tb = rem / static_cast<uint32_t>(a.hblocks);
+    const uint32_t hb = rem - tb * static_cast<uint32_t>(a.hblocks);
+    const int64_t t0 = static_cast<int64_t>(tb) * a.Ut;
+    const int32_t j0 = static_cast<int32_t>(hb) * a.nhc;
+    const int32_t nhc_here = a.nh - j0 < a.nhc ? a.nh - j0 : a.nhc;
+    uint32_t tt, jl;
+    if (a.head_major) {
+        jl = u / static_cast<uint32_t>(a.Ut);
+        tt = u - jl * static_cast<uint32_t>(a.Ut);
+    } else {
+        tt = u / static_cast<uint32_t>(a.nhc);
+        jl = u - tt * static_cast<uint32_t>(a.nhc);
+    }
+    const int64_t tok = t0 + tt;
+    const bool active = u < c.U && static_cast<int32_t>(jl) < nhc_here && tok < c.T;
+    const ReqOf q = request_lookup(c, a.src.pg_off, a.dst.pg_off, t0, tok, active,
+                                   static_cast<int>(u));
+    first = (j0 + static_cast<int32_t>(jl)) == 0;
+    if (!active) return kNone;
+    if (q.off < 0 || tok < q.off || tok >= q.end || q.end > c.T) return kSkip;
+    const int64_t t = tok - q.off;
+    const int64_t j = j0 + static_cast<int64_t>(jl);
+    const uint64_t Db = static_cast<uint64_t>(c.R);
+    bool ok = head_addr(a.src, static_cast<int32_t>(ql), q.pg_src, t, a.hs.h0 + j, a.hs.hnd != 0,
+                        Db, s);
+    ok = head_addr(a.dst, static_cast<int32_t>(ql), q.pg_dst, t, a.hd.h0 + j, a.hd.hnd != 0, Db,
+                   d) && ok;
     return ok ? kCopy : kSkip;
 }
 
@@ -451,6 +537,21 @@ __global__ __launch_bounds__(kBlock) void k_paged(PagedArgs<Src, Dst> a) {
         constexpr bool nts = std::is_same<Dst, PoolRef>::value;
         if constexpr (VPL > 0) copy_wide<VPL, U, nts>(s, d, code, lane);
         else copy_flat<nts>(a.c, s, d, code, lane);
+    }
+    count_skips(a.c.skipped, nskip, lane);
+}
+
+// Head-sliced gather-scatter (flat copy of Db-byte units).
+__global__ __launch_bounds__(kBlock) void k_heads(HeadArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t nwaves = gridDim.x * kWavesPerBlock;
+    unsigned long long nskip = 0;
+    for (uint32_t chunk = wave_id(); chunk < a.c.nchunks; chunk += nwaves) {
+        uint64_t s = 0, d = 0;
+        bool first = false;
+        const int code = resolve_heads(a, chunk, static_cast<uint32_t>(lane), s, d, first);
+        nskip += __popcll(__ballot(code == kSkip && first));
+        copy_flat<true>(a.c, s, d, code, lane);
     }
     count_skips(a.c.skipped, nskip, lane);
 }

@@ -29,8 +29,8 @@ def declared_functions():
 def test_exports_every_declared_function():
     names = declared_functions()
     assert names == sorted(["kvx_gather", "kvx_scatter", "kvx_gather_scatter",
-                            "kvx_extract_permute", "kvx_rebuild_permute", "kvx_status_str",
-                            "kvx_abi_version"])
+                            "kvx_gather_scatter_heads", "kvx_extract_permute",
+                            "kvx_rebuild_permute", "kvx_status_str", "kvx_abi_version"])
     lib = ctypes.CDLL(kvx.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -42,7 +42,7 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_strings():
     lib = kvx.load_library()
-    assert lib.kvx_abi_version() == 1
+    assert lib.kvx_abi_version() == 2
     for s in range(8):
         assert lib.kvx_status_str(s).startswith(b"KVX_")
     assert lib.kvx_status_str(99) == b"unknown kvx_status"
@@ -138,6 +138,36 @@ def test_permute_validation():
     assert rb(101) == E_SHAPE
     assert rb(100, nb=need - 1) == E_SHAPE
     assert rb(100, inp=None) == E_NULL
+
+
+def test_heads_validation():
+    lib = kvx.load_library()
+    lay = _layout(L=1, kv=2, H=2, D=128)                 # slice of 2 heads, Db = 256
+    pool, keep = _pool(2, stride=4 * 256)                 # 4 heads per token row
+    tab, reqs = _table(), _reqs()
+
+    def call(sh, dh, src=pool):
+        return lib.kvx_gather_scatter_heads(ctypes.byref(lay), ctypes.byref(src),
+                                            ctypes.byref(tab), ctypes.byref(sh) if sh else None,
+                                            ctypes.byref(reqs), ctypes.byref(pool),
+                                            ctypes.byref(tab), ctypes.byref(dh), None, None)
+    ok = kvx._CHeads(4, 2, 1)
+    assert call(None, ok) == E_NULL
+    assert call(kvx._CHeads(4, 3, 0), ok) == E_SHAPE          # 3 + 2 > 4 heads
+    assert call(kvx._CHeads(4, -1, 0), ok) == E_SHAPE
+    assert call(kvx._CHeads(4, 0, 7), ok) == E_SHAPE          # unknown block layout
+    assert call(kvx._CHeads(8, 0, 0), ok) == E_SHAPE          # row stride < 8 heads
+    lay_odd = _layout(L=1, kv=2, H=2, D=4)                    # Db = 8 bytes
+    assert lib.kvx_gather_scatter_heads(ctypes.byref(lay_odd), ctypes.byref(pool),
+                                        ctypes.byref(tab), ctypes.byref(ok), ctypes.byref(reqs),
+                                        ctypes.byref(pool), ctypes.byref(tab),
+                                        ctypes.byref(ok), None, None) == E_ALIGN
+    empty = _reqs(0, 0)
+    assert lib.kvx_gather_scatter_heads(ctypes.byref(lay), ctypes.byref(pool),
+                                        ctypes.byref(_table(0)), ctypes.byref(ok),
+                                        ctypes.byref(empty), ctypes.byref(pool),
+                                        ctypes.byref(_table(0)), ctypes.byref(ok),
+                                        None, None) == OK
 
 
 def test_python_binding_raises():

@@ -1,0 +1,152 @@
+"""GPU parity of the head-sliced gather-scatter (P and D with different
+tensor-parallel sizes, NHD and HND blocks) against the CPU oracle, byte for
+byte over the whole destination pool."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scatter_kvx_gather_amd as kvx
+import workloads as wl
+from tests.gpu_util import DEV, assert_bytes_equal, d, requests, say, table
+from workloads import device as wdev
+
+pytestmark = pytest.mark.gpu
+
+# (src kv_heads, dst kv_heads, slice width, src head0, dst head0, head_dim)
+SLICES = [
+    (8, 4, 4, 4, 0, 128),     # P TP=1 -> D TP=2, rank 1
+    (4, 8, 4, 0, 4, 128),     # P TP=2 rank 0 -> D TP=1: merge into heads 4..7
+    (8, 8, 8, 0, 0, 128),     # whole row (layout conversion when layouts differ)
+    (2, 8, 2, 0, 6, 64),      # P TP=4 -> D TP=1
+    (4, 2, 2, 2, 0, 128),     # P TP=2 -> D TP=4
+    (3, 5, 2, 1, 3, 16),      # odd head counts
+    (100, 100, 100, 0, 0, 8), # more heads than one chunk holds
+    (1, 1, 1, 0, 0, 512),     # one 1 KiB head
+]
+LAYOUTS = [(0, 0), (1, 1), (0, 1), (1, 0)]     # (src HND?, dst HND?)
+
+
+def run_heads(case, sH, dH, nh, sh0, dh0, D, shnd, dhnd, seed):
+    Q = case.geom.planes
+    Db = D * 2
+    rng = np.random.default_rng(seed)
+    src_h = rng.integers(0, 256, (Q, case.src.num_slots * sH * Db), dtype=np.uint8)
+    dst_h = rng.integers(0, 256, (Q, case.dst.num_slots * dH * Db), dtype=np.uint8)
+    src_d, dst_d = d(src_h), d(dst_h)
+    lay = kvx.Layout(case.geom.num_layers, case.geom.num_kv, nh, D, "bf16")
+    src = kvx.Pool(src_d, case.src.num_pages, case.src.page_size, slot_stride=sH * Db)
+    dst = kvx.Pool(dst_d, case.dst.num_pages, case.dst.page_size, slot_stride=dH * Db)
+    skipped = torch.zeros(1, dtype=torch.int64, device=DEV)
+    say(case.name, f"heads src(H={sH} h0={sh0} hnd={shnd}) dst(H={dH} h0={dh0} hnd={dhnd}) "
+        f"nh={nh} D={D} T={case.total_tokens} pages {case.src.page_size}/{case.dst.page_size}")
+    kvx.gather_scatter_heads(lay, src, table(case.src), kvx.Heads(sH, sh0, "hnd" if shnd else "nhd"),
+                             requests(case), dst, table(case.dst),
+                             kvx.Heads(dH, dh0, "hnd" if dhnd else "nhd"), skipped)
+    torch.cuda.synchronize()
+    exp = dst_h.copy()
+    n = oracle.gather_scatter_heads(
+        [src_h[q] for q in range(Q)], sH * Db, case.src.page_size, case.src.num_pages,
+        case.src.pg_off, case.src.ids, (sH, sh0, shnd), Db, nh, case.tok_off,
+        [exp[q] for q in range(Q)], dH * Db, case.dst.page_size, case.dst.num_pages,
+        case.dst.pg_off, case.dst.ids, (dH, dh0, dhnd))
+    assert_bytes_equal(dst_d.cpu().numpy(), exp, case.name)
+    assert int(skipped.item()) == n
+
+
+@pytest.mark.parametrize("li", range(len(LAYOUTS)))
+@pytest.mark.parametrize("si", range(len(SLICES)))
+def test_heads(si, li):
+    sH, dH, nh, sh0, dh0, D = SLICES[si]
+    shnd, dhnd = LAYOUTS[li]
+    pages = [(16, 16), (1, 16), (16, 1), (3, 2)][(si + li) % 4]
+    case = wl.random_case(7000 + 10 * si + li, geom=wl.Geometry(2, 2, nh, D), max_reqs=4,
+                          max_len=90 if D <= 128 else 30, src_page=pages[0], dst_page=pages[1])
+    run_heads(case, sH, dH, nh, sh0, dh0, D, shnd, dhnd, 10 * si + li)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_heads_out_of_range(seed):
+    sH, dH, nh, sh0, dh0, D = SLICES[seed]
+    case = wl.random_case(7100 + seed, geom=wl.Geometry(1, 2, nh, D), max_reqs=5, max_len=60,
+                          oor_frac=0.2)
+    run_heads(case, sH, dH, nh, sh0, dh0, D, seed % 2, (seed // 2) % 2, 100 + seed)
+
+
+def test_heads_many_requests():
+    # 70 requests (beyond the 64-request fast lookup) with empty ones
+    rng = np.random.default_rng(5)
+    lens = rng.integers(0, 12, 70)
+    lens[::5] = 0
+    B = 4
+    pages = [-(-int(n) // B) for n in lens]
+    P = sum(pages) + 3
+    perm_s, perm_d = rng.permutation(P), rng.permutation(P)
+    ls, ld, pos = [], [], 0
+    for p in pages:
+        ls.append(perm_s[pos:pos + p])
+        ld.append(perm_d[pos:pos + p])
+        pos += p
+    case = wl.PagedCase("heads_70req", wl.Geometry(1, 2, 2, 128), wl.csr_from_lengths(lens),
+                        wl.side_from_page_lists(ls, P, B), wl.side_from_page_lists(ld, P, B),
+                        0, 0, 0)
+    run_heads(case, 4, 2, 2, 2, 0, 128, 1, 1, 5)
+
+
+def test_hetero_tp_full_size():
+    """The full-size workload: P TP=1 (8 heads, HND page 16) -> two D ranks
+    at TP=2 (4 heads each).  Six planes compared with the oracle per rank;
+    every plane checked on the device: written heads equal their source heads
+    and the rest of each destination pool is unchanged."""
+    case = wl.hetero_tp_case()
+    Q, D, B = case.geom.planes, 128, 16
+    Db = D * 2
+    Ps, Pd = case.src.num_pages, case.dst.num_pages
+    say("hetero_tp fill")
+    # int16 views of the bf16 payload: every comparison below is bitwise (the
+    # hash fill holds NaN patterns, which a floating-point compare rejects)
+    src = torch.empty((Q, Ps, 8, B, D), dtype=torch.int16, device=DEV)
+    wdev.fill_hash(src, case.value_seed)
+    lay = kvx.Layout(36, 2, 4, D, "bf16")
+    reqs, st, dt = requests(case), table(case.src), table(case.dst)
+    # slot maps (whole pages laid out, truncated to each request's length)
+    def slots(side):
+        out = []
+        for r in range(case.num_reqs):
+            pg = side.ids[side.pg_off[r]:side.pg_off[r + 1]].astype(np.int64)
+            out.append((pg[:, None] * B + np.arange(B)[None, :]).reshape(-1)[:case.lengths[r]])
+        return np.concatenate(out)
+    ss, ds = slots(case.src), slots(case.dst)
+    for rank in range(2):
+        dst = torch.empty((Q, Pd, 4, B, D), dtype=torch.int16, device=DEV)
+        wdev.fill_hash(dst, case.sentinel_seed + rank)
+        before = dst.clone()
+        skipped = torch.zeros(1, dtype=torch.int64, device=DEV)
+        say(f"hetero_tp rank {rank}")
+        kvx.gather_scatter_heads(lay, kvx.Pool(src, Ps, B, slot_stride=8 * Db), st,
+                                 kvx.Heads(8, 4 * rank, "hnd"), reqs,
+                                 kvx.Pool(dst, Pd, B, slot_stride=4 * Db), dt,
+                                 kvx.Heads(4, 0, "hnd"), skipped)
+        torch.cuda.synchronize()
+        assert int(skipped.item()) == 0
+        s_pg, s_row = torch.from_numpy(ss // B).to(DEV), torch.from_numpy(ss % B).to(DEV)
+        d_pg, d_row = torch.from_numpy(ds // B).to(DEV), torch.from_numpy(ds % B).to(DEV)
+        touched = torch.zeros((Pd, B), dtype=torch.bool, device=DEV)
+        touched[d_pg, d_row] = True
+        for q in range(Q):
+            got = dst[q][d_pg, :, d_row]                      # [tokens, 4, D]
+            want = src[q][s_pg, 4 * rank:4 * rank + 4, s_row]
+            assert torch.equal(got, want), (rank, q)
+            keep = ~touched
+            assert torch.equal(dst[q].permute(0, 2, 1, 3)[keep], before[q].permute(0, 2, 1, 3)[keep])
+        for q in (0, 35, 36, 71):
+            exp = before[q].cpu().view(torch.uint8).numpy().reshape(-1).copy()
+            srcq = src[q].cpu().view(torch.uint8).numpy().reshape(-1)
+            one = wl.PagedCase(case.name, wl.Geometry(1, 1, 4, D), case.tok_off, case.src,
+                               case.dst, 0, 0, 0)
+            oracle.gather_scatter_heads([srcq], 8 * Db, B, Ps, case.src.pg_off, case.src.ids,
+                                        (8, 4 * rank, 1), Db, 4, case.tok_off, [exp], 4 * Db,
+                                        B, Pd, case.dst.pg_off, case.dst.ids, (4, 0, 1), 16)
+            assert_bytes_equal(dst[q].cpu().view(torch.uint8).numpy().reshape(-1), exp,
+                               f"rank {rank} plane {q}")
+        del dst, before

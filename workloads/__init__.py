@@ -326,6 +326,26 @@ def config5(num_reqs: int = 64, num_blocks: int = 16384, page_size: int = 16) ->
                      value_seed=2005, sentinel_seed=3005, table_seed=1005)
 
 
+def hetero_tp_case(num_reqs: int = 16, num_blocks: int = 4096, page_size: int = 16) -> PagedCase:
+    """P and D with different tensor-parallel sizes: 36 layers x {K,V},
+    head_dim 128, bf16, 8 KV heads in total; P runs TP=1 (8 heads per token
+    row) and D runs TP=2 (4 heads per row per rank).  Block pools of 4096
+    HND blocks of 16 tokens; 16 requests of 2032 + U{1..16} tokens with block
+    tables drawn from seeded permutations.  The geometry's kv_heads is the
+    slice width moved per call (4: one D rank's share)."""
+    rng = np.random.default_rng(1006)
+    pages_per_req = 128
+    fill = rng.integers(1, page_size + 1, size=num_reqs)
+    lens = (pages_per_req - 1) * page_size + fill
+    src_perm = rng.permutation(num_blocks)[: num_reqs * pages_per_req]
+    dst_perm = rng.permutation(num_blocks)[: num_reqs * pages_per_req]
+    src = side_from_page_lists(np.split(src_perm, num_reqs), num_blocks, page_size)
+    dst = side_from_page_lists(np.split(dst_perm, num_reqs), num_blocks, page_size)
+    return PagedCase("kv144k_16req_page16_hnd_tp1_to_tp2", Geometry(36, 2, 4, 128, "bf16"),
+                     csr_from_lengths(lens), src, dst,
+                     value_seed=2006, sentinel_seed=3006, table_seed=1006)
+
+
 def random_case(seed: int, geom: Optional[Geometry] = None, max_reqs: int = 6,
                 max_len: int = 70, src_page: Optional[int] = None,
                 dst_page: Optional[int] = None, oor_frac: float = 0.0,
