@@ -371,6 +371,28 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
             del hf, fl
             torch.cuda.empty_cache()
 
+        # MLA single-plane pools, 1152-byte rows, page 1 and page 16
+        for page in (1, 16):
+            cs = [wl.mla_case(page, k) for k in range(NREQ)]
+            c = cs[0]
+            g = c.geom
+            A, B = pool_of(c, c.src, 1), pool_of(c, c.dst, 2)
+            st = torch.empty(c.total_tokens * g.token_bytes, dtype=torch.uint8, device=dev)
+            reqs = kvx.Requests(d(c.tok_off), c.total_tokens)
+            tabs = [(kvx.Table(d(x.src.pg_off), d(x.src.ids)),
+                     kvx.Table(d(x.dst.pg_off), d(x.dst.ids))) for x in cs]
+            lay = lay_of(g)
+            PA, PB = kvx.Pool(A, c.src.num_pages, page), kvx.Pool(B, c.dst.num_pages, page)
+            nb = 2 * c.payload_bytes()
+            emit(c.name, "gather_scatter", timed(lambda i: kvx.gather_scatter(
+                lay, PA, tabs[i % NREQ][0], reqs, PB, tabs[i % NREQ][1], stream=stream),
+                reps * 8), nb, "16 disjoint requests rotated")
+            emit(c.name, "gather", timed(lambda i: kvx.gather(
+                lay, PA, tabs[i % NREQ][0], reqs, st, stream=stream), reps * 8), nb,
+                 "16 disjoint requests rotated")
+            del A, B, st, PA, PB
+            torch.cuda.empty_cache()
+
         # head-sliced: P at TP=1 (8 heads, HND page 16) -> two D ranks at TP=2
         c = wl.hetero_tp_case()
         D, B = c.geom.head_dim, c.src.page_size
@@ -405,6 +427,163 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
              f"{c.num_reqs} requests, {c.total_tokens} tokens, page 16")
         del A, B
         torch.cuda.empty_cache()
+
+
+# ----------------------------------------------- load and comparators --
+
+def concurrent_load(torch, kvx, wl, wdev, dev, reps=32):
+    """Gather-scatter of the 2048-token request while a decode-like reader
+    streams a 16 GiB buffer on a second stream (both default priority), at
+    three reader intensities (workgroups per launch)."""
+    wk_stream = torch.cuda.Stream(device=dev)
+    rd_stream = torch.cuda.Stream(device=dev)
+    wk = Workload(torch, kvx, wl, wdev, dev, wk_stream)
+    rd_buf = torch.empty(16 * 2 ** 30, dtype=torch.uint8, device=dev)
+    wdev.fill_hash(rd_buf, 9, stream=rd_stream)
+    sink = torch.zeros(2048, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def run_gs(n):
+        e0, e1 = ev(), ev()
+        e0.record(wk_stream)
+        for i in range(n):
+            k = i % NREQ
+            kvx.gather_scatter(wk.lay, wk.PA, wk.src_tabs[k], wk.reqs, wk.PB, wk.dst_tabs[k],
+                               stream=wk_stream)
+        e1.record(wk_stream)
+        return e0, e1
+
+    def run_reader(n, blocks):
+        e0, e1 = ev(), ev()
+        e0.record(rd_stream)
+        for _ in range(n):
+            wdev.read_stream(rd_buf, sink, blocks=blocks, stream=rd_stream)
+        e1.record(rd_stream)
+        return e0, e1
+
+    def gbps(nbytes, e):
+        return nbytes / (e[0].elapsed_time(e[1]) * 1e6)
+
+    for _ in range(8):                                   # warm up clocks and caches
+        run_gs(4)
+    torch.cuda.synchronize()
+    eg = run_gs(reps)
+    torch.cuda.synchronize()
+    result = {"gather_scatter_alone_GBps": round(gbps(wk.op_bytes * reps, eg), 1),
+              "readers": []}
+    for blocks in (2048, 256, 64):
+        er = run_reader(2, blocks)
+        torch.cuda.synchronize()
+        alone = gbps(rd_buf.numel() * 2, er)
+        # enough reader launches to outlast the gather-scatter launches even
+        # if those slow down to 0.2 TB/s
+        launch_ms = rd_buf.numel() / (alone * 1e6)
+        n_rd = int(wk.op_bytes * reps / 0.2e12 * 1e3 / launch_ms) + 2
+        er = run_reader(n_rd, blocks)
+        eg = run_gs(reps)
+        torch.cuda.synchronize()
+        result["readers"].append({
+            "reader_blocks": blocks,
+            "reader_alone_GBps": round(alone, 1),
+            "reader_loaded_GBps": round(gbps(rd_buf.numel() * n_rd, er), 1),
+            "gather_scatter_loaded_GBps": round(gbps(wk.op_bytes * reps, eg), 1),
+            "reader_outlasts_gather_scatter": bool(er[0].elapsed_time(er[1]) >=
+                                                   eg[0].elapsed_time(eg[1]))})
+    result["note"] = ("reader: 16 GiB per launch, nontemporal 16-byte loads, 256-thread "
+                      "workgroups; gather-scatter: the 2048-token, 144 KiB/token request, 16 "
+                      "disjoint requests rotated; GB/s counts bytes read + written")
+    print(json.dumps(result), flush=True)
+
+
+def comparators(torch, kvx, wl, wdev, dev):
+    """The same 2048-token request moved by per-block runtime copies."""
+    import ctypes
+    import numpy as np
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_int, ctypes.c_void_p]
+    hip.hipMemcpyAsync.restype = ctypes.c_int
+    d2d = 3                                        # hipMemcpyDeviceToDevice
+    stream = torch.cuda.Stream(device=dev)
+    wk = Workload(torch, kvx, wl, wdev, dev, stream)
+    sh = stream.cuda_stream
+    Q, R, S = wk.Q, wk.R, wk.S
+    a0, b0 = wk.A.data_ptr(), wk.B.data_ptr()
+    plane = S * R
+    torch.cuda.synchronize()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def per_block(case, runs):
+        """One hipMemcpyAsync per run of consecutive slots (per (token, plane)
+        block when runs are single slots)."""
+        s_ids = case.src.ids.astype(np.int64)
+        d_ids = case.dst.ids.astype(np.int64)
+        if runs:
+            brk = np.flatnonzero((np.diff(s_ids) != 1) | (np.diff(d_ids) != 1)) + 1
+            starts = np.concatenate([[0], brk])
+            lens = np.diff(np.concatenate([starts, [len(s_ids)]]))
+        else:
+            starts = np.arange(len(s_ids))
+            lens = np.ones(len(s_ids), np.int64)
+        calls = 0
+        e0, e1 = ev(), ev()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for q in range(Q):
+            for st, n in zip(starts.tolist(), lens.tolist()):
+                rc = hip.hipMemcpyAsync(b0 + q * plane + int(d_ids[st]) * R,
+                                        a0 + q * plane + int(s_ids[st]) * R, n * R, d2d, sh)
+                if rc != 0:
+                    raise RuntimeError(f"hipMemcpyAsync failed ({rc})")
+                calls += 1
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return calls, e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3
+
+    out = {}
+    rnd = wl.config2(3)
+    calls, ms, wall = per_block(rnd, runs=False)
+    out["per_block_random"] = {"calls": calls, "ms": round(ms, 2), "wall_ms": round(wall, 2),
+                               "GBps": round(wk.op_bytes / (ms * 1e6), 1)}
+    fresh = wl.PagedCase("fresh", wl.KV144K, wl.csr_from_lengths([2048]),
+                         wl.side_from_slot_lists([np.arange(4096, 6144)], S),
+                         wl.side_from_slot_lists([np.arange(8192, 10240)], S), 0, 0, 0)
+    calls, ms, wall = per_block(fresh, runs=True)
+    out["per_run_fresh_pool"] = {"calls": calls, "ms": round(ms, 3), "wall_ms": round(wall, 2),
+                                 "GBps": round(wk.op_bytes / (ms * 1e6), 1)}
+    calls, ms, wall = per_block(rnd, runs=True)
+    out["per_run_random"] = {"calls": calls, "ms": round(ms, 2)}
+    # the runtime's contiguous copy of a 288 MiB staging buffer
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for k in range(8):
+        rc = hip.hipMemcpyAsync(wk.S2.data_ptr(), wk.S1.data_ptr(), wk.S1.numel(), d2d, sh)
+        if rc != 0:
+            raise RuntimeError(f"hipMemcpyAsync failed ({rc})")
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 8
+    out["runtime_copy_of_staging"] = {"ms": round(ms, 4),
+                                      "GBps": round(2 * wk.S1.numel() / (ms * 1e6), 1)}
+    for k in range(32):                                  # clocks back up after the idle copies
+        kvx.gather_scatter(wk.lay, wk.PA, wk.src_tabs[k % NREQ], wk.reqs, wk.PB,
+                           wk.dst_tabs[k % NREQ], stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for k in range(8):
+        kvx.gather_scatter(wk.lay, wk.PA, wk.src_tabs[k], wk.reqs, wk.PB, wk.dst_tabs[k],
+                           stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 8
+    out["kvx_gather_scatter"] = {"ms": round(ms, 4), "GBps": round(wk.op_bytes / (ms * 1e6), 1)}
+    print(json.dumps(out), flush=True)
 
 
 def summarize_trace(trace_dir, out_path, title, command):
@@ -448,6 +627,10 @@ def main():
                     help="a short run for counter collection (no JSON line)")
     ap.add_argument("--all-configs", action="store_true",
                     help="time every op on all five workloads (JSON line per op)")
+    ap.add_argument("--concurrent", action="store_true",
+                    help="gather-scatter while a decode-like HBM reader runs on another stream")
+    ap.add_argument("--comparators", action="store_true",
+                    help="the same request moved by one runtime copy per block / per run")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "OUT", "TITLE", "CMD"),
                     help="markdown summary of a rocprofv3 --kernel-trace --stats run")
@@ -479,6 +662,12 @@ def main():
     stream = torch.cuda.Stream(device=dev)
     if args.all_configs:
         all_configs(torch, kvx, wl, wdev, dev, stream, reps=5)
+        return 0
+    if args.concurrent:
+        concurrent_load(torch, kvx, wl, wdev, dev)
+        return 0
+    if args.comparators:
+        comparators(torch, kvx, wl, wdev, dev)
         return 0
     log("setup: 2 pools of 4.5 GiB, 16 request tables")
     wk = Workload(torch, kvx, wl, wdev, dev, stream)

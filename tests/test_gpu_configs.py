@@ -204,3 +204,37 @@ def test_config5_block_pools():
                            case.tok_off, case.src, case.dst, 0, 0, 0)
         assert oracle_gather_scatter(one, src_h, exp, NT) == 0
         assert_bytes_equal(b_d[q].cpu().numpy(), exp[0], f"config5 plane {q}")
+
+
+@pytest.mark.parametrize("page", [1, 16])
+def test_mla_single_plane_pools(page):
+    """Single-plane MLA pools (27 planes of 1152-byte rows): gather,
+    gather-scatter and scatter of a 2048-token request, whole destinations
+    compared with the oracle."""
+    case = wl.mla_case(page)
+    g = case.geom
+    Q, R, S = g.planes, g.row_bytes, case.src.num_slots
+    say(f"mla page {page} fill")
+    a_d = hash_pool(Q, S, R, case.value_seed)
+    b_d = hash_pool(Q, S, R, case.sentinel_seed)
+    b_before = b_d.cpu().numpy()
+    lay, reqs = layout_of(g), requests(case)
+    st, dt = table(case.src), table(case.dst)
+    staging = torch.zeros(case.total_tokens * Q * R, dtype=torch.uint8, device=DEV)
+    c_d = b_d.clone()
+    say(f"mla page {page} gather_scatter / gather / scatter")
+    kvx.gather_scatter(lay, kvx.Pool(a_d, case.src.num_pages, page), st, reqs,
+                       kvx.Pool(b_d, case.dst.num_pages, page), dt)
+    kvx.gather(lay, kvx.Pool(a_d, case.src.num_pages, page), st, reqs, staging)
+    kvx.scatter(lay, staging, reqs, kvx.Pool(c_d, case.dst.num_pages, page), dt)
+    torch.cuda.synchronize()
+    a_h = a_d.cpu().numpy()
+    exp_st = np.zeros(staging.numel(), np.uint8)
+    oracle_gather(case, a_h, exp_st, NT)
+    assert exp_st.nbytes == oracle.kv_bytes(2048, 27, 1, 576, 2, num_kv=1)
+    assert_bytes_equal(staging.cpu().numpy(), exp_st, "mla gather")
+    exp_b = b_before.copy()
+    oracle_gather_scatter(case, a_h, exp_b, NT)
+    assert_bytes_equal(b_d.cpu().numpy(), exp_b, "mla gather_scatter")
+    oracle_scatter(case, exp_st, b_before, NT)
+    assert_bytes_equal(c_d.cpu().numpy(), b_before, "mla scatter")

@@ -326,6 +326,29 @@ def config5(num_reqs: int = 64, num_blocks: int = 16384, page_size: int = 16) ->
                      value_seed=2005, sentinel_seed=3005, table_seed=1005)
 
 
+MLA_LITE = Geometry(27, 1, 1, 576, "bf16")   # one 576-element latent+rope row per layer
+
+
+def mla_case(page_size: int = 1, request: int = 0, tokens: int = 2048,
+             num_slots: int = 32768) -> PagedCase:
+    """Single-plane (MLA) pools, DeepSeek-V2-Lite-sized rows: 27 layers, one
+    576-element bf16 vector per token and layer (1152-byte rows, 30.4 KiB per
+    token).  One request of ``tokens`` tokens; its source and destination
+    pages are slice ``request`` (of 16 disjoint ones) of independent seeded
+    permutations of pools of ``num_slots`` token slots."""
+    rng = np.random.default_rng(1007 + page_size)
+    pages = num_slots // page_size
+    need = -(-tokens // page_size)
+    if not 0 <= request < pages // need:
+        raise ValueError("request index out of range")
+    sl = slice(need * request, need * (request + 1))
+    src = side_from_page_lists([rng.permutation(pages)[sl]], pages, page_size)
+    dst = side_from_page_lists([rng.permutation(pages)[sl]], pages, page_size)
+    return PagedCase(f"mla27x576_{tokens}tok_page{page_size}", MLA_LITE,
+                     csr_from_lengths([tokens]), src, dst,
+                     value_seed=2007, sentinel_seed=3007, table_seed=1007 + page_size)
+
+
 def hetero_tp_case(num_reqs: int = 16, num_blocks: int = 4096, page_size: int = 16) -> PagedCase:
     """P and D with different tensor-parallel sizes: 36 layers x {K,V},
     head_dim 128, bf16, 8 KV heads in total; P runs TP=1 (8 heads per token

@@ -8,6 +8,8 @@
 //   wl_copy: a plain 16-byte-per-lane copy of nbytes, used to calibrate HBM
 //     byte counters (FETCH_SIZE / WRITE_SIZE) against a kernel of known
 //     traffic.
+//   wl_read_stream: a streaming HBM reader standing in for decode attention
+//     reading its KV, to load the memory system while the kvx path runs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -42,6 +44,23 @@ __global__ void k_copy16(uint4* __restrict__ dst, const uint4* __restrict__ src,
         dst[i] = src[i];
 }
 
+// A decode-like HBM reader: streams through the buffer with 16-byte loads and
+// folds the words together; the fold is stored only if it equals a value the
+// data practically never produces, so the loads cannot be dropped.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ void k_read_stream(const u32x4* __restrict__ src, int64_t n16,
+                              unsigned long long* __restrict__ sink) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    uint32_t acc = 0;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
+         i += stride) {
+        const u32x4 v = __builtin_nontemporal_load(src + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9e3779b9u && threadIdx.x == 0) sink[blockIdx.x] = acc;
+}
+
 int grid_for(int64_t items) {
     int64_t g = (items + 255) / 256;
     if (g > 65536) g = 65536;
@@ -72,6 +91,19 @@ int wl_copy(void* dst, const void* src, int64_t nbytes, hipStream_t stream) {
         return -1;
     hipLaunchKernelGGL(k_copy16, dim3(grid_for(nbytes / 16)), dim3(256), 0, stream,
                        static_cast<uint4*>(dst), static_cast<const uint4*>(src), nbytes / 16);
+    return static_cast<int>(hipGetLastError());
+}
+
+// Reads nbytes (multiple of 16) of src once with `blocks` workgroups of 256
+// threads (1..2048; fewer blocks, lighter load); sink must hold 2048 words.
+int wl_read_stream(const void* src, int64_t nbytes, void* sink, int blocks, hipStream_t stream) {
+    if (nbytes == 0) return 0;
+    if (src == nullptr || sink == nullptr || nbytes < 0 || nbytes % 16 != 0 ||
+        (reinterpret_cast<uintptr_t>(src) & 15u) != 0 || blocks < 1 || blocks > 2048)
+        return -1;
+    hipLaunchKernelGGL(k_read_stream, dim3(blocks), dim3(256), 0, stream,
+                       static_cast<const u32x4*>(src), nbytes / 16,
+                       static_cast<unsigned long long*>(sink));
     return static_cast<int>(hipGetLastError());
 }
 

@@ -22,7 +22,9 @@ def _load():
                                      ctypes.c_uint64, ctypes.c_void_p]
         lib.wl_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                 ctypes.c_void_p]
-        lib.wl_fill_hash.restype = lib.wl_copy.restype = ctypes.c_int
+        lib.wl_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                       ctypes.c_int, ctypes.c_void_p]
+        lib.wl_fill_hash.restype = lib.wl_copy.restype = lib.wl_read_stream.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -48,3 +50,15 @@ def copy_bytes(dst: torch.Tensor, src: torch.Tensor, nbytes: int, stream=None) -
     rc = _load().wl_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream))
     if rc != 0:
         raise RuntimeError(f"wl_copy failed ({rc})")
+
+
+def read_stream(src: torch.Tensor, sink: torch.Tensor, blocks: int = 2048, stream=None) -> None:
+    """Stream once through ``src`` (a decode-like HBM read load) with
+    ``blocks`` workgroups; ``sink`` is a device tensor of at least 2048 int64
+    words."""
+    if sink.numel() * sink.element_size() < 2048 * 8:
+        raise ValueError("sink too small")
+    rc = _load().wl_read_stream(src.data_ptr(), src.numel() * src.element_size(),
+                                sink.data_ptr(), blocks, _stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"wl_read_stream failed ({rc})")
