@@ -119,7 +119,10 @@ typedef struct kvx_layout {
 /* A paged pool ([survey] 7.4: per-layer cache base addresses, each cut into
  * num_blocks equal blocks).  planes is a HOST array of Q DEVICE pointers,
  * each 16-byte aligned and addressing at least
- * (num_pages * page_size - 1) * slot_stride + R bytes. */
+ * (num_pages * page_size - 1) * slot_stride + R bytes.  A pool that is the
+ * source of kvx_gather or kvx_gather_scatter must hold at least one slot
+ * when the batch has tokens (KVX_E_SHAPE otherwise): rows that are skipped
+ * read the plane's first slot and discard it. */
 typedef struct kvx_pool {
     void* const* planes;
     int64_t num_pages;      /* >= 0 */

@@ -116,6 +116,14 @@ kvx_status check_pool(const kvx_pool* p, const Geom& g) {
     return KVX_OK;
 }
 
+// A source pool must hold at least one slot when there are tokens to move:
+// rows that are not copied load the plane's first slot instead of a computed
+// address.
+kvx_status check_source_nonempty(const kvx_pool* p, const kvx_reqs* r) {
+    if (r->total_tokens > 0 && (p->num_pages == 0 || p->page_size == 0)) return KVX_E_SHAPE;
+    return KVX_OK;
+}
+
 kvx_status check_reqs(const kvx_reqs* r) {
     if (r == nullptr) return KVX_E_NULL;
     if (r->num_reqs < 0 || r->total_tokens < 0) return KVX_E_SHAPE;
@@ -179,6 +187,21 @@ Shape shape_for(int64_t unit_bytes) {
     return {0, static_cast<uint32_t>(u)};
 }
 
+// Paged ops only: rows of 512 B .. 16 KiB that are not a power-of-two number
+// of KiB use the row-loop copy (vpl = -KMAX, U rows per chunk, U <= the
+// instance's maximum).
+Shape paged_shape_for(int64_t R) {
+    Shape sh = shape_for(R);
+    if (sh.vpl != 0 || R <= 512 || R > 16384) return sh;
+    int kmax = 1;
+    while (static_cast<int64_t>(kmax) * 1024 < R) kmax *= 2;
+    int64_t umax = KVX_CHUNK_KIB / kmax > 0 ? KVX_CHUNK_KIB / kmax : 1;
+    int64_t u = kChunkBytes / R;
+    if (u < 1) u = 1;
+    if (u > umax) u = umax;
+    return {-kmax, static_cast<uint32_t>(u)};
+}
+
 // Fill the shape-dependent fields of Common; false if the chunk count overflows.
 bool set_chunks(Common* c, const Shape& sh, uint32_t units_per_plane, int32_t nq) {
     c->U = sh.U;
@@ -221,6 +244,11 @@ const void* paged_kernel(int vpl) {
         case 4: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 4, wide_rows<4>()>);
         case 8: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 8, wide_rows<8>()>);
         case 16: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 16, wide_rows<16>()>);
+        case -1: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -1, wide_rows<1>()>);
+        case -2: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -2, wide_rows<2>()>);
+        case -4: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -4, wide_rows<4>()>);
+        case -8: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -8, wide_rows<8>()>);
+        case -16: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -16, wide_rows<16>()>);
         default: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 0, 0>);
     }
 }
@@ -255,7 +283,7 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
     int cus = 0;
     kvx_status s = device_cus(&cus);
     if (s != KVX_OK) return s;
-    const Shape sh = shape_for(g.R);
+    const Shape sh = paged_shape_for(g.R);
     for (int32_t q0 = 0; q0 < g.Q; q0 += kTab) {
         const int32_t nq = g.Q - q0 < kTab ? g.Q - q0 : kTab;
         PagedArgs<Src, Dst> a;
@@ -280,7 +308,8 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
                          "chunks=%u grid=%u\n",
                          op_name(op), g.Q, q0, q0 + nq, static_cast<long long>(g.R),
                          static_cast<long long>(reqs->total_tokens), reqs->num_reqs,
-                         sh.vpl ? "wide" : "flat", sh.U, a.c.nchunks, grid);
+                         sh.vpl > 0 ? "wide" : (sh.vpl < 0 ? "row-loop" : "flat"), sh.U,
+                         a.c.nchunks, grid);
         s = launch(paged_kernel<Src, Dst>(sh.vpl), grid, a, stream);
         if (s != KVX_OK) return s;
     }
@@ -443,6 +472,7 @@ kvx_status kvx_gather(const kvx_layout* layout, const kvx_pool* src, const kvx_t
     KVX_TRY(check_layout(layout, &g));
     KVX_TRY(check_reqs(reqs));
     KVX_TRY(check_pool(src, g));
+    KVX_TRY(check_source_nonempty(src, reqs));
     KVX_TRY(check_table(src_table, reqs));
     KVX_TRY(check_staging(staging, staging_bytes, g, reqs));
     return run_paged<PoolRef, StageRef>(0, g, reqs, src, src_table, nullptr, nullptr, nullptr,
@@ -471,6 +501,7 @@ kvx_status kvx_gather_scatter(const kvx_layout* layout,
     KVX_TRY(check_layout(layout, &g));
     KVX_TRY(check_reqs(reqs));
     KVX_TRY(check_pool(src, g));
+    KVX_TRY(check_source_nonempty(src, reqs));
     KVX_TRY(check_table(src_table, reqs));
     KVX_TRY(check_pool(dst, g));
     KVX_TRY(check_table(dst_table, reqs));

@@ -291,6 +291,10 @@ struct SideAddr<PoolRef> {
                                int64_t, int64_t, int64_t t, uint64_t& a) {
         return pool_addr(p, ql, pg_off_r, t, a);
     }
+    // An address that is always safe to read: the plane's first slot.
+    __device__ static uint64_t base(const PoolRef& p, int32_t ql) {
+        return reinterpret_cast<uint64_t>(p.plane[ql]);
+    }
 };
 
 template <>
@@ -300,9 +304,14 @@ struct SideAddr<StageRef> {
         a = stage_addr(s, c, ql, off_r, n_r, t);
         return true;
     }
+    __device__ static uint64_t base(const StageRef& s, int32_t) {
+        return reinterpret_cast<uint64_t>(s.base);
+    }
 };
 
 // Resolve unit u (one lane) of a paged chunk.  Called with every lane active.
+// A unit that is not copied gets the source's base as its source address, so
+// the copy may load it unconditionally (the call never writes its source).
 template <class Src, class Dst>
 __device__ __forceinline__ int resolve(const PagedArgs<Src, Dst>& a, const PagedChunk& k,
                                        uint32_t u, uint64_t& s, uint64_t& d) {
@@ -311,13 +320,16 @@ __device__ __forceinline__ int resolve(const PagedArgs<Src, Dst>& a, const Paged
     const bool active = u < c.U && tok < c.T;
     const ReqOf q = request_lookup(c, pg_off_of(a.src), pg_off_of(a.dst), k.tok0, tok, active,
                                    static_cast<int>(u));
+    s = SideAddr<Src>::base(a.src, k.ql);
     if (!active) return kNone;
     // a token range that contradicts total_tokens is never dereferenced
     if (q.off < 0 || tok < q.off || tok >= q.end || q.end > c.T) return kSkip;
     const int64_t t = tok - q.off;
     const int64_t n_r = q.end - q.off;
-    bool ok = SideAddr<Src>::get(a.src, c, k.ql, q.pg_src, q.off, n_r, t, s);
+    uint64_t sa = 0;
+    bool ok = SideAddr<Src>::get(a.src, c, k.ql, q.pg_src, q.off, n_r, t, sa);
     ok = SideAddr<Dst>::get(a.dst, c, k.ql, q.pg_dst, q.off, n_r, t, d) && ok;
+    if (ok) s = sa;
     return ok ? kCopy : kSkip;
 }
 
@@ -446,18 +458,18 @@ __device__ __forceinline__ int resolve_perm(const PermuteArgs& a, const PermChun
 
 // ------------------------------------------------------------ copy phase --
 
-// Rows of VPL KiB, U rows per chunk; row addresses broadcast to SGPRs.
+// Rows of VPL KiB, U rows per chunk; row addresses broadcast to SGPRs.  Every
+// row's source is loaded (rows that are not copied point at a safe address),
+// so the loads are straight-line code; only the stores test the status.
 template <int VPL, int U, bool NTS>
 __device__ __forceinline__ void copy_wide(uint64_t s_l, uint64_t d_l, int code_l, int lane) {
     v4u x[U][VPL];
     const uint32_t off = static_cast<uint32_t>(lane) * 16u;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        if (__builtin_amdgcn_readlane(code_l, u) == kCopy) {
-            const uint64_t s = readlane64(s_l, u);
+        const uint64_t s = readlane64(s_l, u);
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) x[u][v] = load_nt(s, off + v * 1024);
-        }
+        for (int v = 0; v < VPL; ++v) x[u][v] = load_nt(s, off + v * 1024);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -465,6 +477,43 @@ __device__ __forceinline__ void copy_wide(uint64_t s_l, uint64_t d_l, int code_l
             const uint64_t d = readlane64(d_l, u);
 #pragma unroll
             for (int v = 0; v < VPL; ++v) store_v<NTS>(d, off + v * 1024, x[u][v]);
+        }
+    }
+}
+
+// Rows of R bytes with 64*(KMAX-1) < V <= 64*KMAX vectors (V = R/16, not a
+// whole number of KiB), up to UMAX rows per chunk (U at run time); row
+// addresses broadcast to SGPRs as in the wide copy, lanes stride a row in
+// 1 KiB steps and the last step is masked to the row's end.
+template <int KMAX, int UMAX, bool NTS>
+__device__ __forceinline__ void copy_rows(const Common& c, uint64_t s_l, uint64_t d_l,
+                                          int code_l, int lane) {
+    v4u x[UMAX][KMAX];
+    // Vector lane + 64k of a row; lanes past the row's end load the row's
+    // first vector again (in bounds, same cache line) and store nothing, so
+    // only the stores are predicated per lane.
+    uint32_t off[KMAX];
+    bool in_row[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        in_row[k] = static_cast<uint32_t>(lane + kWave * k) < c.V;
+        off[k] = in_row[k] ? static_cast<uint32_t>(lane + kWave * k) * 16u : 0u;
+    }
+    // rows u >= U resolved to kNone (safe source address), so every row is
+    // loaded unconditionally and the loop needs no run-time bound
+#pragma unroll
+    for (int u = 0; u < UMAX; ++u) {
+        const uint64_t s = readlane64(s_l, u);
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) x[u][k] = load_nt(s, off[k]);
+    }
+#pragma unroll
+    for (int u = 0; u < UMAX; ++u) {
+        if (__builtin_amdgcn_readlane(code_l, u) == kCopy) {
+            const uint64_t d = readlane64(d_l, u);
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k)
+                if (in_row[k]) store_v<NTS>(d, off[k], x[u][k]);
         }
     }
 }
@@ -523,7 +572,8 @@ __device__ __forceinline__ void count_skips(unsigned long long* counter, unsigne
     if (counter != nullptr && n != 0 && lane == 0) atomicAdd(counter, n);
 }
 
-// VPL > 0: wide copy with U rows per chunk; VPL == 0: flat copy.
+// VPL > 0: wide copy with U rows per chunk; VPL < 0: row-loop copy with
+// KMAX = -VPL and at most U rows per chunk; VPL == 0: flat copy.
 template <class Src, class Dst, int VPL, int U>
 __global__ __launch_bounds__(kBlock) void k_paged(PagedArgs<Src, Dst> a) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -536,6 +586,7 @@ __global__ __launch_bounds__(kBlock) void k_paged(PagedArgs<Src, Dst> a) {
         nskip += __popcll(__ballot(code == kSkip));
         constexpr bool nts = std::is_same<Dst, PoolRef>::value;
         if constexpr (VPL > 0) copy_wide<VPL, U, nts>(s, d, code, lane);
+        else if constexpr (VPL < 0) copy_rows<-VPL, U, nts>(a.c, s, d, code, lane);
         else copy_flat<nts>(a.c, s, d, code, lane);
     }
     count_skips(a.c.skipped, nskip, lane);

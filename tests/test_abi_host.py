@@ -101,6 +101,8 @@ def test_gather_validation():
     assert gather(lay, pool, tab, reqs, staging=None) == E_NULL
     zero_pages, k5 = _pool(4, num_pages=-1)
     assert gather(lay, zero_pages, tab, reqs) == E_SHAPE
+    empty_src, k7 = _pool(4, num_pages=0)                    # no slot to read
+    assert gather(lay, empty_src, tab, reqs) == E_SHAPE
     huge, k6 = _pool(4, num_pages=1 << 62, page_size=16)
     assert gather(lay, huge, tab, reqs) == E_RANGE
     # a NULL plane pointer
