@@ -115,13 +115,15 @@ class Workload:
         self.op_bytes = 2 * T * Q * R               # read + write per op
         self.kvx = kvx
 
-    def step(self, i, stream, ev=None):
+    def step(self, i, stream, ev=None, marks=(0, 1, 2, 3, 4, 5)):
+        """One pass of the path; event ev[j] is recorded before op j (after the
+        last op for j = 5) for every j in marks."""
         kvx, lay = self.kvx, self.lay
         k1, k2 = (2 * i) % NREQ, (2 * i + 1) % NREQ
         T = self.T
 
         def mark(j):
-            if ev is not None:
+            if ev is not None and j in marks:
                 ev[j].record(stream)
         mark(0)
         kvx.gather_scatter(lay, self.PA, self.src_tabs[k1], self.reqs, self.PB,
@@ -618,8 +620,8 @@ def summarize_trace(trace_dir, out_path, title, command):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="time budget per oracle thread count")
@@ -686,23 +688,44 @@ def main():
     K, W = args.steps, args.warmup
     for i in range(W):
         wk.step(i, stream)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    # timed region: events around the two slowest kernels -- the
+    # gather-scatter on even steps, the scatter on odd steps -- and around the
+    # whole region; events around every op would cost ~4% of the step, so the
+    # other ops are timed in a later diagnostic pass
+    live_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()                       # barrier: one rank
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(K):
-        wk.step(W + i, stream, events[i])
+        wk.step(W + i, stream, live_ev[i], marks=(0, 1) if i % 2 == 0 else (4, 5))
     t_end.record(stream)
+    issue = time.perf_counter() - wall0             # host time to enqueue the K steps
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / K
-    op_ms = {op: sum(e[j].elapsed_time(e[j + 1]) for e in events) / K
-             for j, op in enumerate(OPS)}
+    live_ms = {
+        "gather_scatter": sum(live_ev[i][0].elapsed_time(live_ev[i][1])
+                              for i in range(0, K, 2)) / len(range(0, K, 2)),
+        "scatter": sum(live_ev[i][4].elapsed_time(live_ev[i][5])
+                       for i in range(1, K, 2)) / max(1, len(range(1, K, 2))),
+    }
     step_bytes = wk.op_bytes * len(OPS)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    log(f"timed {K} steps: {ms_step:.4f} ms/step (wall {wall * 1e3 / K:.4f} ms/step)")
+    log(f"timed {K} steps: {ms_step:.4f} ms/step (wall {wall * 1e3 / K:.4f} ms/step), "
+        f"gather_scatter {live_ms['gather_scatter'] * 1e3:.1f} us, "
+        f"scatter {live_ms['scatter'] * 1e3:.1f} us")
+
+    # per-op diagnostic pass (events around every op; not part of the value)
+    nd = 50
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(nd)]
+    torch.cuda.synchronize()
+    for i in range(nd):
+        wk.step(W + K + i, stream, events[i])
+    torch.cuda.synchronize()
+    op_ms = {op: sum(e[j].elapsed_time(e[j + 1]) for e in events) / nd
+             for j, op in enumerate(OPS)}
     for op in OPS:
         log(f"  {op:15s} {op_ms[op] * 1e3:8.1f} us  {wk.op_bytes / op_ms[op] / 1e6:8.1f} GB/s")
 
@@ -735,12 +758,18 @@ def main():
     torch.cuda.synchronize()
     ident_ms = ce[0].elapsed_time(ce[1]) / ncopy
 
-    dom = max(OPS, key=lambda o: op_ms[o])
+    # the dominant kernel: the slower of the two live-timed kernels (the other
+    # ops are ~25% faster in the diagnostic pass); its achieved rate uses the
+    # live events of the timed region
+    dom = max(live_ms, key=lambda o: live_ms[o])
+    if op_ms[max(OPS, key=lambda o: op_ms[o])] > 1.05 * live_ms[dom]:
+        log("warning: an op without live events is the slowest in the diagnostic pass")
+    dom_ms = live_ms[dom]
     kernel_of = {"gather_scatter": "k_paged<PoolRef, PoolRef, 2, 4>",
                  "gather": "k_paged<PoolRef, StageRef, 2, 4>",
                  "scatter": "k_paged<StageRef, PoolRef, 2, 4>",
                  "rebuild": "k_permute_rows<true, 2, 4>", "extract": "k_permute_rows<false, 2, 4>"}
-    achieved = wk.op_bytes / (op_ms[dom] * 1e-3) / 1e9
+    achieved = wk.op_bytes / (dom_ms * 1e-3) / 1e9
     traffic, traffic_kernel = read_traffic()
     if traffic is not None and traffic_kernel and "PoolRef, kvx::PoolRef" not in traffic_kernel:
         traffic = None
@@ -748,6 +777,8 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic if dom == "gather_scatter" else None,
                 "kernel": kernel_of[dom], "op": dom,
+                "launch_ms": round(dom_ms, 5),
+                "timing": "HIP events around its launches in the timed region",
                 "algorithmic_bytes_per_launch": wk.op_bytes}
 
     result = {
@@ -772,14 +803,16 @@ def main():
             "bytes_per_step": step_bytes,
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "ms_per_288MiB_request": round(op_ms["gather_scatter"], 5),
+        "ms_per_288MiB_request": round(live_ms["gather_scatter"], 5),
         "ops": {op: {"ms": round(op_ms[op], 5),
                      "GBps": round(wk.op_bytes / (op_ms[op] * 1e-3) / 1e9, 1)} for op in OPS},
+        "ops_timing": "diagnostic pass after the timed region, events around every op",
         "copy_ceiling": {"plain_copy_GBps": round(copy_gbps, 1),
                          "plain_copy_bytes": 2 * chunk,
                          "gather_contiguous_rows_GBps":
                              round(wk.op_bytes / (ident_ms * 1e-3) / 1e9, 1)},
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
+        "host_issue_ms_per_step": round(issue * 1e3 / K, 5),
         "roofline": roofline,
         "cpu_baseline": None,
     }

@@ -153,14 +153,15 @@ class Layout:
 
 
 def _plane_array(planes) -> ctypes.Array:
+    """Host array of plane base pointers: planes[q] of a tensor (from its base
+    pointer and first-dimension stride, without indexing it Q times), or the
+    given tensors / pointers."""
     if isinstance(planes, torch.Tensor):
-        ptrs = [planes[q].data_ptr() for q in range(planes.shape[0])]
+        base, step = planes.data_ptr(), planes.stride(0) * planes.element_size()
+        ptrs = [base + q * step for q in range(planes.shape[0])]
     else:
         ptrs = [_ptr(p) for p in planes]
-    arr = (ctypes.c_void_p * max(len(ptrs), 1))()
-    for i, p in enumerate(ptrs):
-        arr[i] = p
-    return arr
+    return (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
 
 
 class Pool:
