@@ -85,7 +85,7 @@
 extern "C" {
 #endif
 
-#define KVX_ABI_VERSION 2
+#define KVX_ABI_VERSION 3
 
 typedef enum kvx_status {
     KVX_OK = 0,
@@ -95,7 +95,8 @@ typedef enum kvx_status {
     KVX_E_DTYPE = 4,        /* unknown kvx_dtype code */
     KVX_E_RANGE = 5,        /* a size beyond what one call supports (see each limit below) */
     KVX_E_UNSUPPORTED = 6,  /* a valid request this build does not implement */
-    KVX_E_HIP = 7           /* the HIP runtime refused a launch or a device query */
+    KVX_E_HIP = 7,          /* the HIP runtime refused a launch or a device query */
+    KVX_E_DUPLICATE = 8     /* kvx_check_tables: two tokens map to the same destination row */
 } kvx_status;
 
 typedef enum kvx_dtype {
@@ -234,6 +235,26 @@ kvx_status kvx_extract_permute(const kvx_layout* layout, const void* const* hf_p
 kvx_status kvx_rebuild_permute(const kvx_layout* layout, const void* in, int64_t in_bytes,
                                int64_t seq_len, void* const* hf_planes, int64_t s_cap,
                                hipStream_t stream);
+
+/* Precondition checker (debug aid; not on the data path).  Takes HOST copies
+ * of a batch's token CSR and of one pool's page table and checks what the
+ * data-movement calls assume but cannot check without reading device
+ * memory: tok_off starts at 0, never decreases and ends at total_tokens;
+ * pg_off starts at >= 0, never decreases, stays within num_ids, and gives
+ * every request at least ceil(n_r / page_size) page ids; every page id a
+ * token uses is in [0, num_pages); and, when `as_destination` is nonzero,
+ * no two tokens map to the same slot (the rows a scatter or gather-scatter
+ * writes must be pairwise distinct; [budget]'s failure-handling section:
+ * two writers landing in the same page is the failure to rule out).
+ * Returns KVX_OK, KVX_E_SHAPE (inconsistent offsets), KVX_E_RANGE (a page
+ * id out of range) or KVX_E_DUPLICATE; *bad_token (if not NULL) receives the
+ * offending batch token, or -1.  Unlike the data-movement calls it
+ * allocates host memory (one bit per slot for the duplicate test) and
+ * reads only host memory. */
+kvx_status kvx_check_tables(int32_t num_reqs, int64_t total_tokens, const int64_t* tok_off,
+                            const int64_t* pg_off, const int32_t* page_ids, int64_t num_ids,
+                            int64_t num_pages, int32_t page_size, int32_t as_destination,
+                            int64_t* bad_token);
 
 /* Static string naming a status code (never NULL). */
 const char* kvx_status_str(kvx_status status);

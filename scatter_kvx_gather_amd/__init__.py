@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["KvxError", "Layout", "Pool", "Requests", "Table", "Heads", "gather", "scatter",
            "gather_scatter", "gather_scatter_heads", "extract_permute", "rebuild_permute",
-           "library_path", "DTYPE_CODES", "load_library"]
+           "check_tables", "library_path", "DTYPE_CODES", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkvx.so")
@@ -89,6 +89,9 @@ def load_library():
     for f in (lib.kvx_gather, lib.kvx_scatter, lib.kvx_gather_scatter,
               lib.kvx_gather_scatter_heads, lib.kvx_extract_permute, lib.kvx_rebuild_permute):
         f.restype = ctypes.c_int
+    lib.kvx_check_tables.argtypes = [ctypes.c_int32, p64, vp, vp, vp, p64, p64, ctypes.c_int32,
+                                     ctypes.c_int32, P(p64)]
+    lib.kvx_check_tables.restype = ctypes.c_int
     lib.kvx_status_str.argtypes = [ctypes.c_int]
     lib.kvx_status_str.restype = ctypes.c_char_p
     lib.kvx_abi_version.argtypes = []
@@ -293,3 +296,22 @@ def rebuild_permute(layout: Layout, flat: torch.Tensor, seq_len: int,
     _check(lib.kvx_rebuild_permute(ctypes.byref(layout._c), _ptr(flat), _nbytes(flat), seq_len,
                                    ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), s_cap,
                                    _stream(stream)), "kvx_rebuild_permute")
+
+
+def check_tables(reqs: Requests, table: Table, pool: Pool, as_destination: bool = True) -> None:
+    """Debug check of a batch's tables against a pool (kvx_check_tables).
+    Copies the device tables to the host (this synchronises) and raises
+    KvxError naming the first offending batch token when the offsets are
+    inconsistent, a page id is out of range, or -- for a destination --
+    two tokens map to the same row."""
+    import numpy as np
+    tok = np.ascontiguousarray(reqs.tok_off.cpu().numpy(), dtype=np.int64)
+    pg = np.ascontiguousarray(table.pg_off.cpu().numpy(), dtype=np.int64)
+    ids = np.ascontiguousarray(table.page_ids.cpu().numpy(), dtype=np.int32)
+    bad = ctypes.c_int64(-1)
+    st = load_library().kvx_check_tables(
+        reqs.num_reqs, reqs.total_tokens, tok.ctypes.data, pg.ctypes.data,
+        ids.ctypes.data if ids.size else None, ids.size, pool.num_pages, pool.page_size,
+        1 if as_destination else 0, ctypes.byref(bad))
+    if st != 0:
+        raise KvxError(st, f"kvx_check_tables (batch token {bad.value})")

@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <cstdio>
+#include <vector>
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
@@ -559,6 +560,50 @@ kvx_status kvx_rebuild_permute(const kvx_layout* layout, const void* in, int64_t
     return run_permute<true>(g, hf_planes, s_cap, seq_len, const_cast<void*>(in), stream);
 }
 
+kvx_status kvx_check_tables(int32_t num_reqs, int64_t total_tokens, const int64_t* tok_off,
+                            const int64_t* pg_off, const int32_t* page_ids, int64_t num_ids,
+                            int64_t num_pages, int32_t page_size, int32_t as_destination,
+                            int64_t* bad_token) {
+    if (bad_token != nullptr) *bad_token = -1;
+    if (num_reqs < 0 || total_tokens < 0 || num_ids < 0 || num_pages < 0 || page_size < 1)
+        return KVX_E_SHAPE;
+    if (num_reqs > 0 && (tok_off == nullptr || pg_off == nullptr)) return KVX_E_NULL;
+    if (num_ids > 0 && page_ids == nullptr) return KVX_E_NULL;
+    if (num_reqs == 0) return total_tokens == 0 ? KVX_OK : KVX_E_SHAPE;
+    if (tok_off[0] != 0 || tok_off[num_reqs] != total_tokens || pg_off[0] < 0)
+        return KVX_E_SHAPE;
+    int64_t slots = 0;
+    if (!mul_ok(num_pages, page_size, &slots)) return KVX_E_RANGE;
+    std::vector<uint64_t> seen;
+    if (as_destination) seen.assign(static_cast<size_t>((slots + 63) / 64), 0);
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        const int64_t n = tok_off[r + 1] - tok_off[r];
+        const int64_t pages = pg_off[r + 1] - pg_off[r];
+        if (n < 0 || pages < 0 || pg_off[r + 1] > num_ids || pages < (n + page_size - 1) / page_size) {
+            if (bad_token != nullptr) *bad_token = tok_off[r];
+            return KVX_E_SHAPE;
+        }
+        for (int64_t t = 0; t < n; ++t) {
+            const int64_t page = page_ids[pg_off[r] + t / page_size];
+            if (page < 0 || page >= num_pages) {
+                if (bad_token != nullptr) *bad_token = tok_off[r] + t;
+                return KVX_E_RANGE;
+            }
+            if (as_destination) {
+                const int64_t slot = page * page_size + t % page_size;
+                uint64_t& w = seen[static_cast<size_t>(slot / 64)];
+                const uint64_t bit = uint64_t(1) << (slot % 64);
+                if (w & bit) {
+                    if (bad_token != nullptr) *bad_token = tok_off[r] + t;
+                    return KVX_E_DUPLICATE;
+                }
+                w |= bit;
+            }
+        }
+    }
+    return KVX_OK;
+}
+
 const char* kvx_status_str(kvx_status status) {
     switch (status) {
         case KVX_OK: return "KVX_OK";
@@ -569,6 +614,7 @@ const char* kvx_status_str(kvx_status status) {
         case KVX_E_RANGE: return "KVX_E_RANGE: a size exceeds what one call supports";
         case KVX_E_UNSUPPORTED: return "KVX_E_UNSUPPORTED: not implemented by this build";
         case KVX_E_HIP: return "KVX_E_HIP: the HIP runtime refused a launch or a device query";
+        case KVX_E_DUPLICATE: return "KVX_E_DUPLICATE: two tokens map to the same destination row";
         default: return "unknown kvx_status";
     }
 }

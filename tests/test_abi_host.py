@@ -30,7 +30,8 @@ def test_exports_every_declared_function():
     names = declared_functions()
     assert names == sorted(["kvx_gather", "kvx_scatter", "kvx_gather_scatter",
                             "kvx_gather_scatter_heads", "kvx_extract_permute",
-                            "kvx_rebuild_permute", "kvx_status_str", "kvx_abi_version"])
+                            "kvx_rebuild_permute", "kvx_check_tables", "kvx_status_str",
+                            "kvx_abi_version"])
     lib = ctypes.CDLL(kvx.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -42,8 +43,8 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_strings():
     lib = kvx.load_library()
-    assert lib.kvx_abi_version() == 2
-    for s in range(8):
+    assert lib.kvx_abi_version() == 3
+    for s in range(9):
         assert lib.kvx_status_str(s).startswith(b"KVX_")
     assert lib.kvx_status_str(99) == b"unknown kvx_status"
 
@@ -196,3 +197,64 @@ def test_flat_copy_row_division_is_exact():
             magic = np.uint64(((1 << 32) + V - 1) // V)
             u = (i * magic) >> np.uint64(32)
         assert np.array_equal(u, i // np.uint64(V)), V
+
+
+def _check(case_side, tok_off, total, as_dst=True):
+    import numpy as np
+    import torch
+    reqs = kvx.Requests(torch.from_numpy(np.asarray(tok_off, np.int64)), total)
+    tab = kvx.Table(torch.from_numpy(np.asarray(case_side.pg_off, np.int64)),
+                    torch.from_numpy(np.asarray(case_side.ids, np.int32)))
+    pool = kvx.Pool([A], case_side.num_pages, case_side.page_size, slot_stride=16)
+    try:
+        kvx.check_tables(reqs, tab, pool, as_destination=as_dst)
+        return 0, None
+    except kvx.KvxError as e:
+        return e.status, int(str(e).split("batch token ")[1].split(")")[0])
+
+
+def _brute(case_side, tok_off, as_dst):
+    """First offending batch token by the plain definition."""
+    seen = set()
+    for r in range(len(tok_off) - 1):
+        for t in range(int(tok_off[r + 1] - tok_off[r])):
+            page = int(case_side.ids[case_side.pg_off[r] + t // case_side.page_size])
+            if not 0 <= page < case_side.num_pages:
+                return 5, int(tok_off[r]) + t
+            slot = page * case_side.page_size + t % case_side.page_size
+            if as_dst and slot in seen:
+                return 8, int(tok_off[r]) + t
+            seen.add(slot)
+    return 0, None
+
+
+def test_check_tables_against_brute_force():
+    import numpy as np
+    import workloads as wl
+    for seed in range(40):
+        case = wl.random_case(9000 + seed, max_reqs=6, max_len=40,
+                              oor_frac=0.05 if seed % 4 == 0 else 0.0)
+        side = case.dst
+        if seed % 3 == 1 and side.ids.size > 2:          # plant a duplicate destination page
+            ids = side.ids.copy()
+            ids[-1] = ids[0]
+            side = wl.Side(side.num_pages, side.page_size, side.pg_off, ids)
+        for as_dst in (True, False):
+            got = _check(side, case.tok_off, case.total_tokens, as_dst)
+            exp = _brute(side, case.tok_off, as_dst)
+            assert got == exp, (seed, as_dst, got, exp)
+    # the five workloads' destination tables are valid
+    for case in (wl.config1(), wl.config2(3), wl.config5()):
+        assert _check(case.dst, case.tok_off, case.total_tokens) == (0, None)
+
+
+def test_check_tables_shapes():
+    import numpy as np
+    import workloads as wl
+    side = wl.side_from_page_lists([np.array([0, 1]), np.array([2])], 4, 4)
+    ok_tok = [0, 5, 9]
+    assert _check(side, ok_tok, 9) == (0, None)
+    assert _check(side, [0, 5, 9], 10)[0] == 2              # total disagrees
+    assert _check(side, [0, 9, 5], 5)[0] == 2               # decreasing
+    short = wl.side_from_page_lists([np.array([0]), np.array([2])], 4, 4)
+    assert _check(short, ok_tok, 9) == (2, 0)               # request 0 needs 2 pages
