@@ -236,9 +236,9 @@ def summarize_pmc(fetch_dir, write_dir, out_path):
         f.write("median per dispatch, scaled by the plain copy kernel `k_copy16` of\n")
         f.write(f"{COPY_CALIB_BYTES} bytes run in the same process.\n\n")
         f.write("Commands (from the repository root, on the GPU box):\n\n")
-        f.write("    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch --output-format csv "
+        f.write("    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o pmc --output-format csv "
                 "-- python3 bench.py --pmc-pass\n")
-        f.write("    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write --output-format csv "
+        f.write("    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o pmc --output-format csv "
                 "-- python3 bench.py --pmc-pass\n")
         f.write("    python3 bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write "
                 "--pmc-out profiles/kv144k_2048tok_page1_hbm_traffic.md\n\n")
@@ -262,7 +262,8 @@ def summarize_pmc(fetch_dir, write_dir, out_path):
 # ------------------------------------------------------ all workloads --
 
 def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
-    """Time every op on every workload at full size (one JSON line each)."""
+    """Time every op on every workload at full size (one JSON line each),
+    beside a plain contiguous copy of the same bytes timed the same way."""
     def d(a):
         return torch.from_numpy(a).to(dev)
 
@@ -289,11 +290,34 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
         del graph
         return e0.elapsed_time(e1) / n
 
-    def emit(cfg, op, ms, nbytes, note=""):
+    copy_rates = {}
+
+    def copy_rate(nbytes, rot):
+        """Plain contiguous copy (k_copy16) of nbytes / 2 bytes, graph-timed
+        like the ops: `rot` disjoint slices rotated when the op rotates its
+        requests (so neither finds its data in the MALL), copies above 4 GiB
+        timed at 4 GiB.  GB/s counted r+w."""
+        n = min(nbytes // 2, 4 << 30) // 16 * 16
+        k = max(1, min(rot, (4 << 30) // max(n, 1)))
+        if (n, k) not in copy_rates:
+            a = torch.empty(n * k, dtype=torch.uint8, device=dev)
+            b = torch.empty(n * k, dtype=torch.uint8, device=dev)
+            wdev.fill_hash(a, 9, stream=stream)
+            ms = timed(lambda i: wdev.copy_bytes(b[(i % k) * n:], a[(i % k) * n:], n,
+                                                 stream=stream), max(8 * k, 32))
+            copy_rates[(n, k)] = 2 * n / (ms * 1e-3) / 1e9
+            del a, b
+            torch.cuda.empty_cache()
+        return copy_rates[(n, k)]
+
+    def emit(cfg, op, ms, nbytes, note="", rot=1):
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        cp = copy_rate(nbytes, rot)
         print(json.dumps({"workload": cfg, "op": op, "ms": round(ms, 5),
-                          "bytes_rw": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                          "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 /
-                                                HBM_PEAK_GBPS, 2), "note": note}), flush=True)
+                          "bytes_rw": nbytes, "GBps": round(gbps, 1),
+                          "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+                          "plain_copy_GBps": round(cp, 1), "vs_plain_copy": round(gbps / cp, 3),
+                          "note": note}), flush=True)
 
     def pool_of(case, side, seed):
         g = case.geom
@@ -333,11 +357,12 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
         PA, PB = kvx.Pool(A, 32768), kvx.Pool(B, 32768)
         nb = 2 * cs[0].payload_bytes()
         emit(cs[0].name, "gather_scatter", timed(lambda i: kvx.gather_scatter(
-            lay, PA, tabs[i % NREQ][0], reqs, PB, tabs[i % NREQ][1], stream=stream), reps * 4), nb)
+            lay, PA, tabs[i % NREQ][0], reqs, PB, tabs[i % NREQ][1], stream=stream), reps * 4), nb,
+             rot=NREQ)
         emit(cs[0].name, "gather", timed(lambda i: kvx.gather(
-            lay, PA, tabs[i % NREQ][0], reqs, st, stream=stream), reps * 4), nb)
+            lay, PA, tabs[i % NREQ][0], reqs, st, stream=stream), reps * 4), nb, rot=NREQ)
         emit(cs[0].name, "scatter", timed(lambda i: kvx.scatter(
-            lay, st, reqs, PB, tabs[i % NREQ][1], stream=stream), reps * 4), nb)
+            lay, st, reqs, PB, tabs[i % NREQ][1], stream=stream), reps * 4), nb, rot=NREQ)
         del A, B, st, PA, PB
         torch.cuda.empty_cache()
 
@@ -367,9 +392,9 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
                 wdev.fill_hash(t, 3, stream=stream)
             nb = 2 * c.payload_bytes()
             emit(c.name, "extract", timed(lambda i: kvx.extract_permute(
-                lay, hf[i % 2], seq, seq, fl[i % 2], stream=stream), reps * 4), nb)
+                lay, hf[i % 2], seq, seq, fl[i % 2], stream=stream), reps * 4), nb, rot=2)
             emit(c.name, "rebuild", timed(lambda i: kvx.rebuild_permute(
-                lay, fl[i % 2], seq, hf[i % 2], seq, stream=stream), reps * 4), nb)
+                lay, fl[i % 2], seq, hf[i % 2], seq, stream=stream), reps * 4), nb, rot=2)
             del hf, fl
             torch.cuda.empty_cache()
 
@@ -388,10 +413,10 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
             nb = 2 * c.payload_bytes()
             emit(c.name, "gather_scatter", timed(lambda i: kvx.gather_scatter(
                 lay, PA, tabs[i % NREQ][0], reqs, PB, tabs[i % NREQ][1], stream=stream),
-                reps * 8), nb, "16 disjoint requests rotated")
+                reps * 8), nb, "16 disjoint requests rotated", rot=NREQ)
             emit(c.name, "gather", timed(lambda i: kvx.gather(
                 lay, PA, tabs[i % NREQ][0], reqs, st, stream=stream), reps * 8), nb,
-                 "16 disjoint requests rotated")
+                 "16 disjoint requests rotated", rot=NREQ)
             del A, B, st, PA, PB
             torch.cuda.empty_cache()
 
@@ -413,7 +438,7 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
         emit(c.name, "gather_scatter_heads", timed(lambda i: kvx.gather_scatter_heads(
             lay, PA, ts, kvx.Heads(8, 4 * (i % 2), "hnd"), reqs, PD[i % 2], td,
             kvx.Heads(4, 0, "hnd"), stream=stream), reps * 2), 2 * c.payload_bytes(),
-             f"{c.num_reqs} requests, {c.total_tokens} tokens, 4 of 8 heads per launch")
+             f"{c.num_reqs} requests, {c.total_tokens} tokens, 4 of 8 heads per launch", rot=2)
         del A, Ds, PA, PD
         torch.cuda.empty_cache()
 

@@ -210,7 +210,9 @@ typedef struct kvx_heads {
  * NHD or HND blocks (so a whole-row slice also converts between the two).
  * A token whose page id is out of range on either side is skipped and
  * counted once.  Requires head_dim * element size to be a multiple of 16
- * bytes.  One launch (two or more only when Q > 128). */
+ * bytes, and a source pool with at least one slot when total_tokens > 0
+ * (rows that are not copied read the plane's first bytes; KVX_E_SHAPE
+ * otherwise).  One launch (two or more only when Q > 128). */
 kvx_status kvx_gather_scatter_heads(const kvx_layout* layout,
                                     const kvx_pool* src, const kvx_table* src_table,
                                     const kvx_heads* src_heads,

@@ -373,20 +373,58 @@ kvx_status check_heads(const kvx_heads* h, const kvx_pool* p, const Geom& g) {
     return KVX_OK;
 }
 
+// Both sides NHD: a head slice of a token row is nh * Db contiguous bytes at
+// offset head0 * Db of the row, so the slice copy is the row copy with plane
+// bases moved by head0 * Db (each pool's slot stride unchanged).
+kvx_status run_heads_as_rows(const Geom& g, const kvx_reqs* reqs, const kvx_pool* src,
+                             const kvx_table* st, const kvx_heads* sh, const kvx_pool* dst,
+                             const kvx_table* dt, const kvx_heads* dh,
+                             unsigned long long* skipped, hipStream_t stream) {
+    std::vector<void*> sp(static_cast<size_t>(g.Q)), dp(static_cast<size_t>(g.Q));
+    for (int32_t q = 0; q < g.Q; ++q) {
+        sp[q] = static_cast<char*>(src->planes[q]) + static_cast<int64_t>(sh->head0) * g.Db;
+        dp[q] = static_cast<char*>(dst->planes[q]) + static_cast<int64_t>(dh->head0) * g.Db;
+    }
+    kvx_pool s2 = *src, d2 = *dst;
+    s2.planes = sp.data();
+    d2.planes = dp.data();
+    return run_paged<PoolRef, PoolRef>(2, g, reqs, &s2, st, nullptr, &d2, dt, nullptr, skipped,
+                                       stream);
+}
+
 kvx_status run_heads(const Geom& g, const kvx_reqs* reqs, const kvx_pool* src,
                      const kvx_table* st, const kvx_heads* sh, const kvx_pool* dst,
                      const kvx_table* dt, const kvx_heads* dh, unsigned long long* skipped,
                      hipStream_t stream) {
     if (reqs->total_tokens == 0) return KVX_OK;
+    if (sh->block_layout == KVX_NHD && dh->block_layout == KVX_NHD)
+        return run_heads_as_rows(g, reqs, src, st, sh, dst, dt, dh, skipped, stream);
     int cus = 0;
     kvx_status s = device_cus(&cus);
     if (s != KVX_OK) return s;
-    // Chunk = Ut tokens x nhc heads of Db bytes, about kChunkBytes, <= 64 units.
+    // HND on both sides with one page size B <= 64: chunks of B tokens x nhc
+    // heads (k_heads_hnd) when B * Db / 16 is 64, 128, 256 or 512 vectors and
+    // Db / 16 is a power of two; otherwise chunks of Ut tokens x nhc heads of
+    // Db-byte units with the flat copy (k_heads).
+    const int64_t vd = g.Db / 16;
+    const int64_t bv = static_cast<int64_t>(src->page_size) * vd;
+    int kt = 0;
+    if (sh->block_layout == KVX_HND && dh->block_layout == KVX_HND &&
+        src->page_size == dst->page_size && src->page_size <= kWave &&
+        (vd & (vd - 1)) == 0 && (bv == 64 || bv == 128 || bv == 256 || bv == 512))
+        kt = static_cast<int>(bv / 64);
     int64_t units = kChunkBytes / g.Db;
     if (units < 1) units = 1;
     if (units > kWave) units = kWave;
-    const int32_t nhc = static_cast<int32_t>(g.H < units ? g.H : units);
-    const int32_t Ut = static_cast<int32_t>(units / nhc);
+    int32_t nhc = static_cast<int32_t>(g.H < units ? g.H : units);
+    int32_t Ut = static_cast<int32_t>(units / nhc);
+    if (kt > 0) {
+        Ut = src->page_size;                               // one page of tokens
+        const int64_t per_head = Ut * g.Db;
+        int64_t hc = kChunkBytes / per_head;
+        if (hc < 1) hc = 1;
+        nhc = static_cast<int32_t>(g.H < hc ? g.H : hc);
+    }
     const int32_t hblocks = (g.H + nhc - 1) / nhc;
     const uint64_t tblocks = (static_cast<uint64_t>(reqs->total_tokens) + Ut - 1) / Ut;
     for (int32_t q0 = 0; q0 < g.Q; q0 += kTab) {
@@ -418,16 +456,26 @@ kvx_status run_heads(const Geom& g, const kvx_reqs* reqs, const kvx_pool* src,
         a.Ut = Ut;
         a.hblocks = hblocks;
         a.head_major = (a.hs.hnd && a.hd.hnd) ? 1 : 0;
+        if (kt > 0) a.c.U = static_cast<uint32_t>(Ut);
         const uint32_t grid = grid_for(a.c.nchunks, cus);
         if (log_enabled())
             std::fprintf(stderr,
                          "kvx: gather_scatter_heads Q=%d planes[%d,%d) nh=%d Db=%lld T=%lld "
-                         "src(H=%d h0=%d %s) dst(H=%d h0=%d %s) Ut=%d nhc=%d chunks=%u grid=%u\n",
+                         "src(H=%d h0=%d %s) dst(H=%d h0=%d %s) Ut=%d nhc=%d kt=%d chunks=%u "
+                         "grid=%u\n",
                          g.Q, q0, q0 + nq, g.H, static_cast<long long>(g.Db),
                          static_cast<long long>(reqs->total_tokens), a.hs.H, a.hs.h0,
                          a.hs.hnd ? "HND" : "NHD", a.hd.H, a.hd.h0, a.hd.hnd ? "HND" : "NHD",
-                         Ut, nhc, a.c.nchunks, grid);
-        s = launch(reinterpret_cast<const void*>(&k_heads), grid, a, stream);
+                         Ut, nhc, kt, a.c.nchunks, grid);
+        const void* fn = reinterpret_cast<const void*>(&k_heads);
+        switch (kt) {
+            case 1: fn = reinterpret_cast<const void*>(&k_heads_hnd<1>); break;
+            case 2: fn = reinterpret_cast<const void*>(&k_heads_hnd<2>); break;
+            case 4: fn = reinterpret_cast<const void*>(&k_heads_hnd<4>); break;
+            case 8: fn = reinterpret_cast<const void*>(&k_heads_hnd<8>); break;
+            default: break;
+        }
+        s = launch(fn, grid, a, stream);
         if (s != KVX_OK) return s;
     }
     return KVX_OK;
@@ -522,6 +570,7 @@ kvx_status kvx_gather_scatter_heads(const kvx_layout* layout,
     if (g.Db % 16 != 0) return KVX_E_ALIGN;
     KVX_TRY(check_reqs(reqs));
     KVX_TRY(check_pool(src, g));
+    KVX_TRY(check_source_nonempty(src, reqs));
     KVX_TRY(check_table(src_table, reqs));
     KVX_TRY(check_heads(src_heads, src, g));
     KVX_TRY(check_pool(dst, g));

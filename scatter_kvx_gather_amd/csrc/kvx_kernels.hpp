@@ -607,6 +607,99 @@ __global__ __launch_bounds__(kBlock) void k_heads(HeadArgs a) {
     count_skips(a.c.skipped, nskip, lane);
 }
 
+// Head-sliced copy between two HND pools with the same page size B <= 64: a
+// chunk is one block of B batch tokens x nhc heads.  Lane u < B resolves
+// token u of the block (its source and destination page base plus row
+// offset); lanes then fetch, once per chunk, the bases of the tokens their
+// vectors belong to (vector i = lane + 64k covers token i / VD, 16 bytes at
+// (i % VD) * 16 of its head row, VD = Db / 16) and reuse them for every head:
+// head h of a token sits at its head-0 address + h * B * Db.  When the block
+// is one page of one request on both sides, each head's B tokens are one
+// contiguous run of B * Db bytes.  KT = B * VD / 64.  Rows that are not
+// copied load the plane's first bytes instead and store nothing.
+template <int KT>
+__global__ __launch_bounds__(kBlock) void k_heads_hnd(HeadArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t nwaves = gridDim.x * kWavesPerBlock;
+    const Common& c = a.c;
+    const uint64_t Db = static_cast<uint64_t>(c.R);
+    const uint32_t vd = c.V;
+    const uint32_t vd_shift = static_cast<uint32_t>(__builtin_ctz(vd));   // VD is a power of two
+    const uint64_t B = static_cast<uint64_t>(a.Ut);
+    unsigned long long nskip = 0;
+    for (uint32_t chunk = wave_id(); chunk < c.nchunks; chunk += nwaves) {
+        const uint32_t ql = chunk / c.chunks_per_plane;
+        const uint32_t rem = chunk - ql * c.chunks_per_plane;
+        const uint32_t tb = rem / static_cast<uint32_t>(a.hblocks);
+        const uint32_t hb = rem - tb * static_cast<uint32_t>(a.hblocks);
+        const int64_t t0 = static_cast<int64_t>(tb) * a.Ut;
+        const int32_t j0 = static_cast<int32_t>(hb) * a.nhc;
+        const int32_t nhc_here = a.nh - j0 < a.nhc ? a.nh - j0 : a.nhc;
+
+        // resolve token u = lane of the block
+        const int64_t tok = t0 + lane;
+        const bool active = static_cast<uint32_t>(lane) < static_cast<uint32_t>(a.Ut) &&
+                            tok < c.T;
+        const ReqOf q = request_lookup(c, a.src.pg_off, a.dst.pg_off, t0, tok, active, lane);
+        int code = kNone;
+        uint64_t sb = 0, db = 0;
+        if (active) {
+            code = kSkip;
+            if (q.off >= 0 && tok >= q.off && tok < q.end && q.end <= c.T) {
+                const int64_t t = tok - q.off;
+                uint64_t s0 = 0, d0 = 0;
+                // head 0 of the token: page base + row * Db
+                if (head_addr(a.src, static_cast<int32_t>(ql), q.pg_src, t, 0, true, Db, s0) &&
+                    head_addr(a.dst, static_cast<int32_t>(ql), q.pg_dst, t, 0, true, Db, d0)) {
+                    code = kCopy;
+                    sb = s0;
+                    db = d0;
+                }
+            }
+        }
+        if (hb == 0) nskip += __popcll(__ballot(code == kSkip));
+
+        // per-lane vector -> token bases (fetched once, reused for every head)
+        uint64_t sv[KT], dv[KT];
+        bool okv[KT];
+        const uint64_t safe = reinterpret_cast<uint64_t>(a.src.plane[ql]);
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            const uint32_t i = static_cast<uint32_t>(lane + kWave * k);
+            const uint32_t tt = i >> vd_shift;
+            const uint64_t voff = static_cast<uint64_t>(i & (vd - 1)) * 16u;
+            const uint64_t s_t = bperm64(sb, tt);
+            const uint64_t d_t = bperm64(db, tt);
+            const int code_t = static_cast<int>(bperm32(static_cast<uint32_t>(code), tt));
+            okv[k] = code_t == kCopy;
+            sv[k] = s_t + voff;
+            dv[k] = d_t + voff;
+            if (!okv[k]) sv[k] = safe;       // never stored; keeps the load in bounds
+        }
+        // heads, two at a time: all loads of both, then all stores
+        for (int32_t j = 0; j < nhc_here; j += 2) {
+            const bool two = j + 1 < nhc_here;
+            const uint64_t hs0 = static_cast<uint64_t>(a.hs.h0 + j0 + j) * B * Db;
+            const uint64_t hd0 = static_cast<uint64_t>(a.hd.h0 + j0 + j) * B * Db;
+            const uint64_t hstep = B * Db;
+            v4u x0[KT], x1[KT];
+#pragma unroll
+            for (int k = 0; k < KT; ++k) {
+                x0[k] = load_nt(okv[k] ? sv[k] + hs0 : safe, 0);
+                x1[k] = load_nt(okv[k] && two ? sv[k] + hs0 + hstep : safe, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < KT; ++k) {
+                if (okv[k]) {
+                    store_v<true>(dv[k] + hd0, 0, x0[k]);
+                    if (two) store_v<true>(dv[k] + hd0 + hstep, 0, x1[k]);
+                }
+            }
+        }
+    }
+    count_skips(c.skipped, nskip, lane);
+}
+
 // Permute with head rows as units (any head row size, flat copy).
 template <bool REBUILD>
 __global__ __launch_bounds__(kBlock) void k_permute(PermuteArgs a) {

@@ -160,6 +160,8 @@ def test_heads_validation():
     assert call(kvx._CHeads(4, -1, 0), ok) == E_SHAPE
     assert call(kvx._CHeads(4, 0, 7), ok) == E_SHAPE          # unknown block layout
     assert call(kvx._CHeads(8, 0, 0), ok) == E_SHAPE          # row stride < 8 heads
+    empty_src, keep2 = _pool(2, num_pages=0, stride=4 * 256)   # no slot to read
+    assert call(ok, ok, src=empty_src) == E_SHAPE
     lay_odd = _layout(L=1, kv=2, H=2, D=4)                    # Db = 8 bytes
     assert lib.kvx_gather_scatter_heads(ctypes.byref(lay_odd), ctypes.byref(pool),
                                         ctypes.byref(tab), ctypes.byref(ok), ctypes.byref(reqs),

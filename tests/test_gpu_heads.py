@@ -150,3 +150,33 @@ def test_hetero_tp_full_size():
             assert_bytes_equal(dst[q].cpu().view(torch.uint8).numpy().reshape(-1), exp,
                                f"rank {rank} plane {q}")
         del dst, before
+
+
+# HND on both sides with one page size B <= 64: the page-run kernel (a chunk
+# is B tokens x a few heads).  (B, head_dim, src heads, dst heads, slice width,
+# src head0, dst head0): 1, 2, 4 and 8 vectors per lane per head, an odd slice
+# width (last head of a chunk alone), more heads than one chunk holds, and
+# blocks of batch tokens that straddle requests.
+PAGE_RUNS = [
+    (4, 128, 8, 4, 4, 4, 0),
+    (8, 128, 4, 8, 3, 1, 5),
+    (16, 128, 8, 4, 4, 0, 0),
+    (32, 128, 2, 2, 2, 0, 0),
+    (8, 64, 16, 16, 11, 5, 2),
+    (64, 64, 3, 3, 1, 2, 0),
+    (64, 8, 12, 9, 9, 3, 0),
+    (1, 512, 4, 2, 2, 2, 0),
+    (2, 512, 5, 7, 5, 0, 2),
+    (8, 512, 2, 2, 1, 1, 1),
+    (16, 256, 4, 4, 3, 1, 0),
+]
+
+
+@pytest.mark.parametrize("oor", [0.0, 0.15])
+@pytest.mark.parametrize("pi", range(len(PAGE_RUNS)))
+def test_heads_hnd_page_runs(pi, oor):
+    B, D, sH, dH, nh, sh0, dh0 = PAGE_RUNS[pi]
+    case = wl.random_case(7200 + 10 * pi + int(oor > 0), geom=wl.Geometry(2, 2, nh, D),
+                          max_reqs=6, max_len=4 * B + 37, src_page=B, dst_page=B,
+                          oor_frac=oor)
+    run_heads(case, sH, dH, nh, sh0, dh0, D, 1, 1, 200 + pi)
