@@ -70,10 +70,12 @@
  * in pages that were already given to another request is the failure to rule
  * out).
  *
- * Preconditions the library does not check (they would need the device
- * tables on the host): within one call the destination rows are pairwise
- * distinct, and source and destination bytes do not overlap.  Under them the
- * result is unique and equals the row-by-row definition above.
+ * Preconditions the data-movement calls do not check (they would need the
+ * device tables on the host): within one call the destination rows are
+ * pairwise distinct, and source and destination bytes do not overlap.  Under
+ * them the result is unique and equals the row-by-row definition above.
+ * kvx_check_tables and kvx_check_disjoint (below) check them on host copies
+ * of the tables, as a debug aid.
  */
 #ifndef KVX_H
 #define KVX_H
@@ -85,7 +87,7 @@
 extern "C" {
 #endif
 
-#define KVX_ABI_VERSION 3
+#define KVX_ABI_VERSION 4
 
 typedef enum kvx_status {
     KVX_OK = 0,
@@ -96,7 +98,8 @@ typedef enum kvx_status {
     KVX_E_RANGE = 5,        /* a size beyond what one call supports (see each limit below) */
     KVX_E_UNSUPPORTED = 6,  /* a valid request this build does not implement */
     KVX_E_HIP = 7,          /* the HIP runtime refused a launch or a device query */
-    KVX_E_DUPLICATE = 8     /* kvx_check_tables: two tokens map to the same destination row */
+    KVX_E_DUPLICATE = 8,    /* checkers: two written rows are the same row or overlap */
+    KVX_E_OVERLAP = 9       /* kvx_check_disjoint: a written row overlaps a row the call reads */
 } kvx_status;
 
 typedef enum kvx_dtype {
@@ -257,6 +260,31 @@ kvx_status kvx_check_tables(int32_t num_reqs, int64_t total_tokens, const int64_
                             const int64_t* pg_off, const int32_t* page_ids, int64_t num_ids,
                             int64_t num_pages, int32_t page_size, int32_t as_destination,
                             int64_t* bad_token);
+
+/* Overlap checker (debug aid; not on the data path).  For one kvx_gather,
+ * kvx_scatter or kvx_gather_scatter call, described with HOST copies of its
+ * token CSR (reqs->tok_off) and page tables (pg_off, page_ids), checks that
+ * the rows the call writes are pairwise disjoint and that none of them
+ * overlaps a row the call reads: the two preconditions under which the
+ * result is unique.  A side is a pool (kvx_pool plus its kvx_table) or, when
+ * both of that side's pointers are NULL, the staging buffer `staging` of
+ * staging_bytes bytes (its row of plane q of token t of request r at
+ * (tok_off[r] * Q + q * n_r + t) * R, as in kvx_gather).  Plane pointers and
+ * `staging` are compared as addresses and never dereferenced, so DEVICE
+ * pointers are fine here.  A token with an out-of-range page id on a pool
+ * side is left out (the call skips it and touches neither of its rows).
+ * Returns KVX_OK, KVX_E_DUPLICATE (two written rows share a byte),
+ * KVX_E_OVERLAP (a written row shares a byte with a read row; checked only
+ * when no written rows overlap), or an argument status: KVX_E_NULL,
+ * KVX_E_SHAPE (inconsistent offsets, tables or staging too small),
+ * KVX_E_UNSUPPORTED (both sides staging).  *bad_token (if not NULL) receives
+ * one batch token whose written row is at fault, or -1.  Host cost: 24 bytes
+ * and O(log) sorting work per row on each side (Q * total_tokens rows). */
+kvx_status kvx_check_disjoint(const kvx_layout* layout, const kvx_reqs* reqs,
+                              const kvx_pool* src, const kvx_table* src_table,
+                              const kvx_pool* dst, const kvx_table* dst_table,
+                              const void* staging, int64_t staging_bytes,
+                              int64_t* bad_token);
 
 /* Static string naming a status code (never NULL). */
 const char* kvx_status_str(kvx_status status);

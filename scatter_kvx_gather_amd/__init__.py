@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["KvxError", "Layout", "Pool", "Requests", "Table", "Heads", "gather", "scatter",
            "gather_scatter", "gather_scatter_heads", "extract_permute", "rebuild_permute",
-           "check_tables", "library_path", "DTYPE_CODES", "load_library"]
+           "check_tables", "check_disjoint", "library_path", "DTYPE_CODES", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkvx.so")
@@ -92,6 +92,9 @@ def load_library():
     lib.kvx_check_tables.argtypes = [ctypes.c_int32, p64, vp, vp, vp, p64, p64, ctypes.c_int32,
                                      ctypes.c_int32, P(p64)]
     lib.kvx_check_tables.restype = ctypes.c_int
+    lib.kvx_check_disjoint.argtypes = [P(_CLayout), P(_CReqs), P(_CPool), P(_CTable), P(_CPool),
+                                       P(_CTable), vp, p64, P(p64)]
+    lib.kvx_check_disjoint.restype = ctypes.c_int
     lib.kvx_status_str.argtypes = [ctypes.c_int]
     lib.kvx_status_str.restype = ctypes.c_char_p
     lib.kvx_abi_version.argtypes = []
@@ -315,3 +318,37 @@ def check_tables(reqs: Requests, table: Table, pool: Pool, as_destination: bool 
         1 if as_destination else 0, ctypes.byref(bad))
     if st != 0:
         raise KvxError(st, f"kvx_check_tables (batch token {bad.value})")
+
+
+def check_disjoint(layout: Layout, reqs: Requests, src: Optional[Pool] = None,
+                   src_table: Optional[Table] = None, dst: Optional[Pool] = None,
+                   dst_table: Optional[Table] = None,
+                   staging: Optional[torch.Tensor] = None) -> None:
+    """Debug check that a gather, scatter or gather-scatter call writes
+    pairwise disjoint rows, none of which overlaps a row it reads
+    (kvx_check_disjoint).  Pass a pool and its table for each pool side and
+    ``staging`` for the other side of a gather or scatter.  Copies the device
+    tables to the host (this synchronises) and raises KvxError naming one
+    offending batch token."""
+    import numpy as np
+    tok = np.ascontiguousarray(reqs.tok_off.cpu().numpy(), dtype=np.int64)
+    host_reqs = _CReqs(reqs.num_reqs, reqs.total_tokens, tok.ctypes.data)
+    keep = [tok]
+
+    def host_table(t):
+        if t is None:
+            return None
+        pg = np.ascontiguousarray(t.pg_off.cpu().numpy(), dtype=np.int64)
+        ids = np.ascontiguousarray(t.page_ids.cpu().numpy(), dtype=np.int32)
+        keep.extend([pg, ids])
+        return ctypes.byref(_CTable(pg.ctypes.data, ids.ctypes.data if ids.size else None,
+                                    ids.size))
+
+    bad = ctypes.c_int64(-1)
+    st = load_library().kvx_check_disjoint(
+        ctypes.byref(layout._c), ctypes.byref(host_reqs),
+        ctypes.byref(src._c) if src is not None else None, host_table(src_table),
+        ctypes.byref(dst._c) if dst is not None else None, host_table(dst_table),
+        _ptr(staging), _nbytes(staging), ctypes.byref(bad))
+    if st != 0:
+        raise KvxError(st, f"kvx_check_disjoint (batch token {bad.value})")

@@ -4,6 +4,7 @@
 #include "kvx.h"
 #include "kvx_kernels.hpp"
 
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <vector>
@@ -653,6 +654,130 @@ kvx_status kvx_check_tables(int32_t num_reqs, int64_t total_tokens, const int64_
     return KVX_OK;
 }
 
+namespace {
+
+// One row a call touches: bytes [lo, hi) for batch token `tok`.
+struct Span {
+    uint64_t lo, hi;
+    int64_t tok;
+};
+
+// Slot of every batch token in one pool side, or -1 where the call skips the
+// token (page-table index or page id out of range, as the kernels decide).
+kvx_status side_slots(const kvx_reqs* reqs, const kvx_pool* p, const kvx_table* t,
+                      std::vector<int64_t>* slot) {
+    if (p->planes == nullptr) return KVX_E_NULL;
+    if (p->num_pages < 0 || p->page_size < 1) return KVX_E_SHAPE;
+    if (t->num_ids < 0) return KVX_E_SHAPE;
+    if (reqs->num_reqs > 0 && t->pg_off == nullptr) return KVX_E_NULL;
+    if (t->num_ids > 0 && t->page_ids == nullptr) return KVX_E_NULL;
+    slot->assign(static_cast<size_t>(reqs->total_tokens), -1);
+    for (int32_t r = 0; r < reqs->num_reqs; ++r) {
+        const int64_t off = reqs->tok_off[r], n = reqs->tok_off[r + 1] - off;
+        for (int64_t k = 0; k < n; ++k) {
+            const int64_t idx = t->pg_off[r] + k / p->page_size;
+            if (idx < 0 || idx >= t->num_ids) continue;
+            const int64_t page = t->page_ids[idx];
+            if (page < 0 || page >= p->num_pages) continue;
+            (*slot)[static_cast<size_t>(off + k)] = page * p->page_size + k % p->page_size;
+        }
+    }
+    return KVX_OK;
+}
+
+// Rows of the live tokens on one side (Q per token).
+void side_spans(const Geom& g, const kvx_reqs* reqs, const kvx_pool* p,
+                const std::vector<int64_t>& slot, const void* staging,
+                const std::vector<char>& live, std::vector<Span>* out) {
+    out->clear();
+    for (int32_t r = 0; r < reqs->num_reqs; ++r) {
+        const int64_t off = reqs->tok_off[r], n = reqs->tok_off[r + 1] - off;
+        for (int64_t k = 0; k < n; ++k) {
+            const int64_t tok = off + k;
+            if (!live[static_cast<size_t>(tok)]) continue;
+            for (int32_t q = 0; q < g.Q; ++q) {
+                uint64_t lo;
+                if (p != nullptr)
+                    lo = reinterpret_cast<uint64_t>(p->planes[q]) +
+                         static_cast<uint64_t>(slot[static_cast<size_t>(tok)]) *
+                             static_cast<uint64_t>(p->slot_stride);
+                else
+                    lo = reinterpret_cast<uint64_t>(staging) +
+                         static_cast<uint64_t>((off * g.Q + q * n + k) * g.R);
+                out->push_back(Span{lo, lo + static_cast<uint64_t>(g.R), tok});
+            }
+        }
+    }
+}
+
+bool by_lo(const Span& a, const Span& b) { return a.lo < b.lo || (a.lo == b.lo && a.tok < b.tok); }
+
+}  // namespace
+
+kvx_status kvx_check_disjoint(const kvx_layout* layout, const kvx_reqs* reqs,
+                              const kvx_pool* src, const kvx_table* src_table,
+                              const kvx_pool* dst, const kvx_table* dst_table,
+                              const void* staging, int64_t staging_bytes,
+                              int64_t* bad_token) {
+    if (bad_token != nullptr) *bad_token = -1;
+    Geom g;
+    KVX_TRY(check_layout(layout, &g));
+    KVX_TRY(check_reqs(reqs));
+    const int32_t nr = reqs->num_reqs;
+    if (nr > 0 && (reqs->tok_off[0] != 0 || reqs->tok_off[nr] != reqs->total_tokens))
+        return KVX_E_SHAPE;
+    for (int32_t r = 0; r < nr; ++r)
+        if (reqs->tok_off[r + 1] < reqs->tok_off[r]) return KVX_E_SHAPE;
+    if ((src == nullptr) != (src_table == nullptr) || (dst == nullptr) != (dst_table == nullptr))
+        return KVX_E_NULL;
+    if (src == nullptr && dst == nullptr) return KVX_E_UNSUPPORTED;
+    const int64_t T = reqs->total_tokens;
+    if (src == nullptr || dst == nullptr) {
+        int64_t need = 0;
+        if (!mul_ok(T, static_cast<int64_t>(g.Q) * g.R, &need)) return KVX_E_RANGE;
+        if (need > 0 && staging == nullptr) return KVX_E_NULL;
+        if (staging_bytes < need) return KVX_E_SHAPE;
+    }
+    std::vector<int64_t> ss, ds;
+    if (src != nullptr) KVX_TRY(side_slots(reqs, src, src_table, &ss));
+    if (dst != nullptr) KVX_TRY(side_slots(reqs, dst, dst_table, &ds));
+    std::vector<char> live(static_cast<size_t>(T), 1);
+    for (int64_t t = 0; t < T; ++t)
+        if ((src != nullptr && ss[static_cast<size_t>(t)] < 0) ||
+            (dst != nullptr && ds[static_cast<size_t>(t)] < 0))
+            live[static_cast<size_t>(t)] = 0;
+    std::vector<Span> w, rd;
+    side_spans(g, reqs, dst, ds, staging, live, &w);
+    std::sort(w.begin(), w.end(), by_lo);
+    // written rows pairwise disjoint: each starts at or after every earlier end
+    uint64_t hi = 0;
+    for (const Span& x : w) {
+        if (x.lo < hi) {
+            if (bad_token != nullptr) *bad_token = x.tok;
+            return KVX_E_DUPLICATE;
+        }
+        hi = x.hi;
+    }
+    side_spans(g, reqs, src, ss, staging, live, &rd);
+    std::sort(rd.begin(), rd.end(), by_lo);
+    std::vector<uint64_t> max_hi(rd.size());
+    uint64_t m = 0;
+    for (size_t i = 0; i < rd.size(); ++i) max_hi[i] = m = std::max(m, rd[i].hi);
+    // a written row [lo, hi) meets a read row iff some read row starting
+    // before hi ends after lo
+    for (const Span& x : w) {
+        const size_t i = static_cast<size_t>(
+            std::lower_bound(rd.begin(), rd.end(), x.hi,
+                             [](const Span& a, uint64_t v) { return a.lo < v; }) -
+            rd.begin());
+        if (i > 0 && max_hi[i - 1] > x.lo) {
+            if (bad_token != nullptr) *bad_token = x.tok;
+            return KVX_E_OVERLAP;
+        }
+    }
+    return KVX_OK;
+}
+
 const char* kvx_status_str(kvx_status status) {
     switch (status) {
         case KVX_OK: return "KVX_OK";
@@ -663,7 +788,8 @@ const char* kvx_status_str(kvx_status status) {
         case KVX_E_RANGE: return "KVX_E_RANGE: a size exceeds what one call supports";
         case KVX_E_UNSUPPORTED: return "KVX_E_UNSUPPORTED: not implemented by this build";
         case KVX_E_HIP: return "KVX_E_HIP: the HIP runtime refused a launch or a device query";
-        case KVX_E_DUPLICATE: return "KVX_E_DUPLICATE: two tokens map to the same destination row";
+        case KVX_E_DUPLICATE: return "KVX_E_DUPLICATE: two written rows are the same row or overlap";
+        case KVX_E_OVERLAP: return "KVX_E_OVERLAP: a written row overlaps a row the call reads";
         default: return "unknown kvx_status";
     }
 }

@@ -30,8 +30,8 @@ def test_exports_every_declared_function():
     names = declared_functions()
     assert names == sorted(["kvx_gather", "kvx_scatter", "kvx_gather_scatter",
                             "kvx_gather_scatter_heads", "kvx_extract_permute",
-                            "kvx_rebuild_permute", "kvx_check_tables", "kvx_status_str",
-                            "kvx_abi_version"])
+                            "kvx_rebuild_permute", "kvx_check_tables", "kvx_check_disjoint",
+                            "kvx_status_str", "kvx_abi_version"])
     lib = ctypes.CDLL(kvx.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -43,8 +43,8 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_strings():
     lib = kvx.load_library()
-    assert lib.kvx_abi_version() == 3
-    for s in range(9):
+    assert lib.kvx_abi_version() == 4
+    for s in range(10):
         assert lib.kvx_status_str(s).startswith(b"KVX_")
     assert lib.kvx_status_str(99) == b"unknown kvx_status"
 

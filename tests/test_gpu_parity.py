@@ -32,6 +32,10 @@ GEOMS = [
     (wl.Geometry(1, 1, 64, 128, "bf16"), 12),    # R = 16 KiB (wide)
     (wl.Geometry(1, 1, 128, 128, "bf16"), 8),    # R = 32 KiB (flat, several passes)
     (wl.Geometry(1, 2, 2, 8, "fp8"), 300),       # R = 16, 1-byte elements
+    (wl.Geometry(1, 2, 33, 8, "bf16"), 100),     # R = 528: smallest row-loop row
+    (wl.Geometry(1, 1, 1023, 8, "bf16"), 10),    # R = 16368: largest row-loop row
+    (wl.Geometry(1, 1, 4095, 8, "bf16"), 5),     # R = 65520 (flat)
+    (wl.Geometry(1, 1, 256, 128, "bf16"), 5),    # R = 64 KiB: the largest row accepted
     (wl.Geometry(2, 2, 2, 128, "f32"), 80),      # R = 1 KiB, 4-byte elements
 ]
 
