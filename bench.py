@@ -790,14 +790,25 @@ def main():
     if op_ms[max(OPS, key=lambda o: op_ms[o])] > 1.05 * live_ms[dom]:
         log("warning: an op without live events is the slowest in the diagnostic pass")
     dom_ms = live_ms[dom]
-    kernel_of = {"gather_scatter": "k_paged<PoolRef, PoolRef, 2, 4>",
-                 "gather": "k_paged<PoolRef, StageRef, 2, 4>",
-                 "scatter": "k_paged<StageRef, PoolRef, 2, 4>",
-                 "rebuild": "k_permute_rows<true, 2, 4>", "extract": "k_permute_rows<false, 2, 4>"}
+    # kernel instance the library picks for these 2 KiB rows: one row per
+    # wave when a launch moves more than one round of resident waves at
+    # 8 KiB chunks (32 waves per CU), otherwise 4 rows per 8 KiB chunk
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    u = 1 if wk.op_bytes // 2 > cus * 32 * 8192 else 4
+    kernel_of = {"gather_scatter": f"k_paged<PoolRef, PoolRef, 2, {u}>",
+                 "gather": f"k_paged<PoolRef, StageRef, 2, {u}>",
+                 "scatter": f"k_paged<StageRef, PoolRef, 2, {u}>",
+                 "rebuild": f"k_permute_rows<true, 2, {u}>",
+                 "extract": f"k_permute_rows<false, 2, {u}>"}
     achieved = wk.op_bytes / (dom_ms * 1e-3) / 1e9
     traffic, traffic_kernel = read_traffic()
     if traffic is not None and traffic_kernel and "PoolRef, kvx::PoolRef" not in traffic_kernel:
         traffic = None
+    if traffic is not None and traffic_kernel and dom == "gather_scatter":
+        measured = traffic_kernel.split("(")[0].replace("void ", "").replace("kvx::", "")
+        if measured != kernel_of[dom]:
+            log(f"warning: counter summary names {measured}, expected {kernel_of[dom]}")
+            kernel_of[dom] = measured
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic if dom == "gather_scatter" else None,

@@ -189,6 +189,25 @@ Shape shape_for(int64_t unit_bytes) {
     return {0, static_cast<uint32_t>(u)};
 }
 
+// Waves of these kernels (<= 64 VGPRs) that one compute unit holds at once.
+constexpr int64_t kResidentWavesPerCu = 32;
+
+// Rows per chunk for the wide copies (paged rows and permute token rows of
+// 1..16 KiB).  A launch that fits in one round of resident waves at 8 KiB
+// chunks keeps them (every wave runs at once, with the most loads in flight
+// per lane); a larger one moves one row per wave, so that the waves still
+// running when the launch drains are short.  Measured on MI355X (same
+// process, alternating): 8 KiB chunks win below one round (gather of 128
+// 144 KiB tokens: 3610 vs 3373 GB/s; extract of 58.7 MB: 6253 vs 5877),
+// one row per wave wins above it (extract of 470 MB: 5380 -> 5924-6045;
+// rebuild 5414 -> 6192; scatter of 302 MB 5214 -> 5378; fragmented gather of
+// 7 GB 5127 -> 5314; just over one round, extract of 75 MB: 5364 -> 6444).
+uint32_t wide_rows_for(const Shape& sh, int64_t rows, int64_t row_bytes, int cus) {
+    if (sh.vpl <= 0 || sh.U == 1) return sh.U;
+    const int64_t round_bytes = static_cast<int64_t>(cus) * kResidentWavesPerCu * kChunkBytes;
+    return rows * row_bytes > round_bytes ? 1u : sh.U;
+}
+
 // Paged ops only: rows of 512 B .. 16 KiB that are not a power-of-two number
 // of KiB use the row-loop copy (vpl = -KMAX, U rows per chunk, U <= the
 // instance's maximum).
@@ -239,11 +258,15 @@ kvx_status launch(const void* fn, uint32_t grid, Args& a, hipStream_t stream) {
 }
 
 template <class Src, class Dst>
-const void* paged_kernel(int vpl) {
+const void* paged_kernel(int vpl, uint32_t U) {
+    const bool one = U == 1;
     switch (vpl) {
-        case 1: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, wide_rows<1>()>);
-        case 2: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 2, wide_rows<2>()>);
-        case 4: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 4, wide_rows<4>()>);
+        case 1: return one ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, 1>)
+                           : reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, wide_rows<1>()>);
+        case 2: return one ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 2, 1>)
+                           : reinterpret_cast<const void*>(&k_paged<Src, Dst, 2, wide_rows<2>()>);
+        case 4: return one ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 4, 1>)
+                           : reinterpret_cast<const void*>(&k_paged<Src, Dst, 4, wide_rows<4>()>);
         case 8: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 8, wide_rows<8>()>);
         case 16: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 16, wide_rows<16>()>);
         case -1: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -1, wide_rows<1>()>);
@@ -258,11 +281,15 @@ const void* paged_kernel(int vpl) {
 // Token-row permute kernel for rows of vpl KiB; nullptr for the head-row
 // (flat) kernel.
 template <bool REBUILD>
-const void* permute_rows_kernel(int vpl) {
+const void* permute_rows_kernel(int vpl, uint32_t U) {
+    const bool one = U == 1;
     switch (vpl) {
-        case 1: return reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 1, wide_rows<1>()>);
-        case 2: return reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 2, wide_rows<2>()>);
-        case 4: return reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 4, wide_rows<4>()>);
+        case 1: return one ? reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 1, 1>)
+                           : reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 1, wide_rows<1>()>);
+        case 2: return one ? reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 2, 1>)
+                           : reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 2, wide_rows<2>()>);
+        case 4: return one ? reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 4, 1>)
+                           : reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 4, wide_rows<4>()>);
         case 8: return reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 8, wide_rows<8>()>);
         case 16: return reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 16, wide_rows<16>()>);
         default: return nullptr;
@@ -285,9 +312,11 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
     int cus = 0;
     kvx_status s = device_cus(&cus);
     if (s != KVX_OK) return s;
-    const Shape sh = paged_shape_for(g.R);
+    const Shape sh0 = paged_shape_for(g.R);
     for (int32_t q0 = 0; q0 < g.Q; q0 += kTab) {
         const int32_t nq = g.Q - q0 < kTab ? g.Q - q0 : kTab;
+        Shape sh = sh0;
+        sh.U = wide_rows_for(sh0, reqs->total_tokens * nq, g.R, cus);
         PagedArgs<Src, Dst> a;
         std::memset(&a, 0, sizeof(a));
         a.c.tok_off = reqs->tok_off;
@@ -312,7 +341,7 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
                          static_cast<long long>(reqs->total_tokens), reqs->num_reqs,
                          sh.vpl > 0 ? "wide" : (sh.vpl < 0 ? "row-loop" : "flat"), sh.U,
                          a.c.nchunks, grid);
-        s = launch(paged_kernel<Src, Dst>(sh.vpl), grid, a, stream);
+        s = launch(paged_kernel<Src, Dst>(sh.vpl, sh.U), grid, a, stream);
         if (s != KVX_OK) return s;
     }
     return KVX_OK;
@@ -329,10 +358,12 @@ kvx_status run_permute(const Geom& g, void* const* hf, int64_t s_cap, int64_t se
     // otherwise head rows of Db bytes with the flat copy.
     const Shape tok = shape_for(g.R);
     const bool rows = tok.vpl > 0;
-    const Shape sh = rows ? tok : shape_for(g.Db);
+    const Shape sh0 = rows ? tok : shape_for(g.Db);
     const uint32_t units = static_cast<uint32_t>(rows ? seq : seq * g.H);
     for (int32_t q0 = 0; q0 < g.Q; q0 += kTab) {
         const int32_t nq = g.Q - q0 < kTab ? g.Q - q0 : kTab;
+        Shape sh = sh0;
+        if (rows) sh.U = wide_rows_for(sh0, seq * nq, g.R, cus);
         PermuteArgs a;
         std::memset(&a, 0, sizeof(a));
         a.c.T = seq;
@@ -353,7 +384,7 @@ kvx_status run_permute(const Geom& g, void* const* hf, int64_t s_cap, int64_t se
                          static_cast<long long>(g.Db), static_cast<long long>(seq),
                          static_cast<long long>(s_cap), rows ? "token-row" : "head-row", sh.U,
                          a.c.nchunks, grid);
-        const void* fn = rows ? permute_rows_kernel<REBUILD>(sh.vpl)
+        const void* fn = rows ? permute_rows_kernel<REBUILD>(sh.vpl, sh.U)
                               : reinterpret_cast<const void*>(&k_permute<REBUILD>);
         s = launch(fn, grid, a, stream);
         if (s != KVX_OK) return s;

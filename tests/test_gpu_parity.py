@@ -120,6 +120,44 @@ def test_many_requests_and_empty_ones():
     run_paged_case(case, 3)
 
 
+def big_case(name, g, lens, src_page, dst_page, seed, oor_frac=0.0):
+    """Ragged batch of given lengths: source pages drawn with replacement,
+    distinct destination pages, optionally some ids out of range."""
+    rng = np.random.default_rng(seed)
+    ps = [-(-int(n) // src_page) for n in lens]
+    pd = [-(-int(n) // dst_page) for n in lens]
+    ns, nd = sum(ps) + 5, sum(pd) + 5
+    src = wl.side_from_page_lists([rng.integers(0, ns, p) for p in ps], ns, src_page)
+    perm = rng.permutation(nd)
+    dl, pos = [], 0
+    for p in pd:
+        dl.append(perm[pos:pos + p])
+        pos += p
+    dst = wl.side_from_page_lists(dl, nd, dst_page)
+    for side in (src, dst):
+        if oor_frac:
+            m = rng.random(side.ids.size) < oor_frac
+            side.ids = np.where(m, side.num_pages + 3, side.ids).astype(np.int32)
+    return wl.PagedCase(name, g, wl.csr_from_lengths(lens), src, dst, 0, 0, 0)
+
+
+# Launches above 64 MiB each way move one row per wave (below it, 8 KiB
+# chunks): 1, 2 and 4 KiB rows, ragged and empty requests, mixed page sizes.
+BIG = [
+    (wl.Geometry(8, 2, 4, 128, "bf16"), [1500, 0, 2333, 1801], 1, 1, 0.0),     # R = 1 KiB
+    (wl.Geometry(8, 2, 4, 128, "bf16"), [2600, 2, 2100], 16, 3, 0.02),         # R = 1 KiB
+    (wl.Geometry(4, 2, 8, 128, "bf16"), [3000, 1700, 7], 1, 16, 0.02),         # R = 2 KiB
+    (wl.Geometry(2, 2, 16, 128, "bf16"), [2100, 1, 2500], 16, 16, 0.0),        # R = 4 KiB
+]
+
+
+@pytest.mark.parametrize("bi", range(len(BIG)))
+def test_one_row_per_wave_launches(bi):
+    g, lens, sp, dp, oor = BIG[bi]
+    assert sum(lens) * g.planes * g.row_bytes > 64 << 20
+    run_paged_case(big_case(f"big{bi}", g, lens, sp, dp, 700 + bi, oor), 700 + bi)
+
+
 @pytest.mark.parametrize("nreq", [1, 2, 63, 64, 65, 130])
 @pytest.mark.parametrize("R", [2048, 512])
 def test_request_lookup_limits(nreq, R):
@@ -197,6 +235,10 @@ PERMS = [
     (1, 32, 128, "bf16", 9, 5),       # token rows of 8 KiB
     (2, 64, 128, "bf16", 9, 9),       # token rows of 16 KiB (one token per chunk)
     (3, 12, 128, "bf16", 40, 40),     # token rows of 3 KiB: head-row kernel
+    # launches above 64 MiB each way: one token row per wave
+    (72, 4, 128, "f16", 1200, 1111),  # token rows of 1 KiB (s_cap > seq)
+    (20, 8, 128, "bf16", 2000, 2000), # token rows of 2 KiB
+    (6, 16, 128, "bf16", 3100, 2999), # token rows of 4 KiB
 ]
 
 
