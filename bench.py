@@ -623,6 +623,23 @@ def comparators(torch, kvx, wl, wdev, dev):
     ms = e0.elapsed_time(e1) / 8
     out["runtime_copy_of_staging"] = {"ms": round(ms, 4),
                                       "GBps": round(2 * wk.S1.numel() / (ms * 1e6), 1)}
+    # the same copy on the DMA engines (hipMemcpyDeviceToDeviceNoCU: no
+    # compute units), the engine a cross-GPU staging copy would use
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    rc = 0
+    for k in range(4):
+        rc = hip.hipMemcpyAsync(wk.S2.data_ptr(), wk.S1.data_ptr(), wk.S1.numel(), 1024, sh)
+        if rc != 0:
+            break
+    e1.record(stream)
+    torch.cuda.synchronize()
+    if rc == 0:
+        ms = e0.elapsed_time(e1) / 4
+        out["dma_copy_of_staging"] = {"ms": round(ms, 4),
+                                      "GBps": round(2 * wk.S1.numel() / (ms * 1e6), 1)}
+    else:
+        out["dma_copy_of_staging"] = {"error": f"hipMemcpyAsync returned {rc}"}
     for k in range(32):                                  # clocks back up after the idle copies
         kvx.gather_scatter(wk.lay, wk.PA, wk.src_tabs[k % NREQ], wk.reqs, wk.PB,
                            wk.dst_tabs[k % NREQ], stream=stream)

@@ -93,11 +93,14 @@ def test_heads_many_requests():
     run_heads(case, 4, 2, 2, 2, 0, 128, 1, 1, 5)
 
 
-def test_hetero_tp_full_size():
-    """The full-size workload: P TP=1 (8 heads, HND page 16) -> two D ranks
-    at TP=2 (4 heads each).  Six planes compared with the oracle per rank;
-    every plane checked on the device: written heads equal their source heads
-    and the rest of each destination pool is unchanged."""
+@pytest.mark.parametrize("layout", ["hnd", "nhd"])
+def test_hetero_tp_full_size(layout):
+    """The full-size workload: P TP=1 (8 heads, page 16) -> two D ranks at
+    TP=2 (4 heads each), with HND blocks (the page-run kernel) or NHD blocks
+    (the row kernel on shifted plane bases).  Four planes compared with the
+    oracle per rank; every plane checked on the device: written heads equal
+    their source heads and the rest of each destination pool is unchanged."""
+    hnd = layout == "hnd"
     case = wl.hetero_tp_case()
     Q, D, B = case.geom.planes, 128, 16
     Db = D * 2
@@ -105,7 +108,8 @@ def test_hetero_tp_full_size():
     say("hetero_tp fill")
     # int16 views of the bf16 payload: every comparison below is bitwise (the
     # hash fill holds NaN patterns, which a floating-point compare rejects)
-    src = torch.empty((Q, Ps, 8, B, D), dtype=torch.int16, device=DEV)
+    src = torch.empty((Q, Ps, 8, B, D) if hnd else (Q, Ps, B, 8, D), dtype=torch.int16,
+                      device=DEV)
     wdev.fill_hash(src, case.value_seed)
     lay = kvx.Layout(36, 2, 4, D, "bf16")
     reqs, st, dt = requests(case), table(case.src), table(case.dst)
@@ -118,15 +122,16 @@ def test_hetero_tp_full_size():
         return np.concatenate(out)
     ss, ds = slots(case.src), slots(case.dst)
     for rank in range(2):
-        dst = torch.empty((Q, Pd, 4, B, D), dtype=torch.int16, device=DEV)
+        dst = torch.empty((Q, Pd, 4, B, D) if hnd else (Q, Pd, B, 4, D), dtype=torch.int16,
+                          device=DEV)
         wdev.fill_hash(dst, case.sentinel_seed + rank)
         before = dst.clone()
         skipped = torch.zeros(1, dtype=torch.int64, device=DEV)
-        say(f"hetero_tp rank {rank}")
+        say(f"hetero_tp {layout} rank {rank}")
         kvx.gather_scatter_heads(lay, kvx.Pool(src, Ps, B, slot_stride=8 * Db), st,
-                                 kvx.Heads(8, 4 * rank, "hnd"), reqs,
+                                 kvx.Heads(8, 4 * rank, layout), reqs,
                                  kvx.Pool(dst, Pd, B, slot_stride=4 * Db), dt,
-                                 kvx.Heads(4, 0, "hnd"), skipped)
+                                 kvx.Heads(4, 0, layout), skipped)
         torch.cuda.synchronize()
         assert int(skipped.item()) == 0
         s_pg, s_row = torch.from_numpy(ss // B).to(DEV), torch.from_numpy(ss % B).to(DEV)
@@ -134,19 +139,24 @@ def test_hetero_tp_full_size():
         touched = torch.zeros((Pd, B), dtype=torch.bool, device=DEV)
         touched[d_pg, d_row] = True
         for q in range(Q):
-            got = dst[q][d_pg, :, d_row]                      # [tokens, 4, D]
-            want = src[q][s_pg, 4 * rank:4 * rank + 4, s_row]
+            if hnd:
+                got = dst[q][d_pg, :, d_row]                  # [tokens, 4, D]
+                want = src[q][s_pg, 4 * rank:4 * rank + 4, s_row]
+            else:
+                got = dst[q][d_pg, d_row]
+                want = src[q][s_pg, s_row, 4 * rank:4 * rank + 4]
             assert torch.equal(got, want), (rank, q)
             keep = ~touched
-            assert torch.equal(dst[q].permute(0, 2, 1, 3)[keep], before[q].permute(0, 2, 1, 3)[keep])
+            dq, bq = (dst[q].permute(0, 2, 1, 3), before[q].permute(0, 2, 1, 3)) if hnd else \
+                (dst[q], before[q])
+            assert torch.equal(dq[keep], bq[keep])
         for q in (0, 35, 36, 71):
             exp = before[q].cpu().view(torch.uint8).numpy().reshape(-1).copy()
             srcq = src[q].cpu().view(torch.uint8).numpy().reshape(-1)
-            one = wl.PagedCase(case.name, wl.Geometry(1, 1, 4, D), case.tok_off, case.src,
-                               case.dst, 0, 0, 0)
             oracle.gather_scatter_heads([srcq], 8 * Db, B, Ps, case.src.pg_off, case.src.ids,
-                                        (8, 4 * rank, 1), Db, 4, case.tok_off, [exp], 4 * Db,
-                                        B, Pd, case.dst.pg_off, case.dst.ids, (4, 0, 1), 16)
+                                        (8, 4 * rank, int(hnd)), Db, 4, case.tok_off, [exp],
+                                        4 * Db, B, Pd, case.dst.pg_off, case.dst.ids,
+                                        (4, 0, int(hnd)), 16)
             assert_bytes_equal(dst[q].cpu().view(torch.uint8).numpy().reshape(-1), exp,
                                f"rank {rank} plane {q}")
         del dst, before
