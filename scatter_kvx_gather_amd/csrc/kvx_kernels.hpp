@@ -1,9 +1,12 @@
 // kvx_kernels.hpp -- HIP kernels (gfx950 / CDNA4) behind libkvx.so.
 //
-// All five calls are one row-moving kernel with a different address
-// resolver.  The work of a call is split into chunks of U units (a unit is
-// one row of R bytes, or one head row of head_dim elements for the permutes),
-// each chunk sized to about 8 KiB.  A wave takes one chunk at a time:
+// Every data-movement call is a row-moving kernel with an address resolver
+// for its op (gather, scatter, gather-scatter, head-sliced copy, extract and
+// rebuild permute).  The work of a call is split into chunks of U units (a
+// unit is one row of R bytes, a token row or head row for the permutes, or a
+// (token, head) pair for head-sliced copies), each chunk sized to about
+// 8 KiB; the host lets a large launch of 1..16 KiB rows move one row per
+// chunk instead.  A wave takes one chunk at a time:
 //
 //   1. resolve: lane u < U computes unit u's source and destination byte
 //      addresses from the tables (token -> request by a search over tok_off,
@@ -11,15 +14,20 @@
 //      or none (past the end);
 //   2. copy: every 16-byte vector of the chunk's rows is loaded with a
 //      nontemporal dwordx4 load (all loads of the chunk are issued before the
-//      first store), then stored with a nontemporal dwordx4 store.
+//      first store), then stored with a dwordx4 store: nontemporal into
+//      scattered pool rows, ordinary into contiguous outputs (staging and
+//      permute outputs, which the next op often reads back from the MALL).
 //
 // Rows of 1, 2, 4, 8 or 16 KiB use the "wide" copy: the row addresses are
 // broadcast into scalar registers (readlane) and each lane moves 16 bytes at
 // lane*16 + v*1024 of every row, so all 64 lanes of an instruction cover one
-// contiguous 1 KiB of one row.  Other row sizes use the "flat" copy: the
-// chunk's U*V vectors (V = R/16) are numbered and dealt round-robin to lanes,
-// and each lane fetches its row's addresses from the resolving lane with a
-// cross-lane permute.
+// contiguous 1 KiB of one row.  Other rows of 0.5..16 KiB use the "row-loop"
+// copy (scalar row addresses, lanes step through the row 1 KiB at a time,
+// the last step masked).  Remaining sizes use the "flat" copy: the chunk's
+// U*V vectors (V = R/16) are numbered and dealt round-robin to lanes, and each
+// lane fetches its row's addresses from the resolving lane with a cross-lane
+// permute.  Rows that are not copied load from a safe source address and
+// store nothing, so the loads carry no branches.
 //
 // Waves grid-stride over the chunks (by default the grid has one wave per
 // chunk; the host can cap it at a few workgroups per compute unit), and
@@ -41,7 +49,8 @@ namespace kvx {
 // Tuning knobs (compile-time; the defaults are the measured best).  Chunk
 // size, averaged over repeated runs of all five workloads: 4, 8 and 12 KiB
 // are within noise of each other and 6% ahead of 16 KiB on the five-op step
-// of the 2048-token request; 8 KiB has the best mean.
+// of the 2048-token request; 8 KiB has the best mean.  (The host still lets
+// large wide-row launches move one row per chunk.)
 #ifndef KVX_CHUNK_KIB
 #define KVX_CHUNK_KIB 8            // bytes a wave moves per chunk, in KiB
 #endif

@@ -1,0 +1,165 @@
+/* The C ABI used from plain C: no Python, no torch.  Builds two small paged
+ * pools in device memory, runs kvx_gather_scatter and kvx_gather on a HIP
+ * stream, and compares every destination byte with the CPU oracle run on
+ * host copies of the same bytes (the oracle is linked as test
+ * infrastructure).  Also checks that a bad argument returns its status and
+ * enqueues nothing.  Prints "abi_smoke ok" and exits 0 on success. */
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "kvx.h"
+
+/* oracle/kvx_oracle.c (test infrastructure) */
+int64_t oracle_gather(int32_t Q, int64_t R, uint8_t* const* src_planes, int64_t src_stride,
+                      int32_t src_page_size, int64_t src_num_pages, int32_t num_reqs,
+                      const int64_t* tok_off, const int64_t* src_pg_off, const int32_t* src_ids,
+                      uint8_t* staging, int nthreads);
+int64_t oracle_gather_scatter(int32_t Q, int64_t R, uint8_t* const* src_planes,
+                              int64_t src_stride, int32_t src_page_size, int64_t src_num_pages,
+                              const int64_t* src_pg_off, const int32_t* src_ids, int32_t num_reqs,
+                              const int64_t* tok_off, uint8_t* const* dst_planes,
+                              int64_t dst_stride, int32_t dst_page_size, int64_t dst_num_pages,
+                              const int64_t* dst_pg_off, const int32_t* dst_ids, int nthreads);
+
+#define CHECK_HIP(x)                                                              \
+    do {                                                                          \
+        hipError_t e_ = (x);                                                      \
+        if (e_ != hipSuccess) {                                                   \
+            fprintf(stderr, "%s:%d: %s\n", __FILE__, __LINE__, hipGetErrorString(e_)); \
+            return 2;                                                             \
+        }                                                                         \
+    } while (0)
+
+#define CHECK_KVX(x)                                                              \
+    do {                                                                          \
+        kvx_status s_ = (x);                                                      \
+        if (s_ != KVX_OK) {                                                       \
+            fprintf(stderr, "%s:%d: %s\n", __FILE__, __LINE__, kvx_status_str(s_)); \
+            return 3;                                                             \
+        }                                                                         \
+    } while (0)
+
+enum { L = 3, KV = 2, Q = L * KV, H = 4, D = 128, R = H * D * 2 };
+enum { SRC_PAGE = 4, SRC_PAGES = 40, DST_PAGE = 16, DST_PAGES = 12, NREQ = 3 };
+
+static uint64_t lcg = 0x9E3779B97F4A7C15ull;
+static uint32_t next_u32(void) {
+    lcg = lcg * 6364136223846793005ull + 1442695040888963407ull;
+    return (uint32_t)(lcg >> 33);
+}
+
+static void shuffle(int32_t* a, int n) {
+    for (int i = n - 1; i > 0; --i) {
+        int j = (int)(next_u32() % (uint32_t)(i + 1));
+        int32_t t = a[i]; a[i] = a[j]; a[j] = t;
+    }
+}
+
+int main(void) {
+    const int64_t lens[NREQ] = {37, 0, 61};          /* ragged, one empty request */
+    int64_t tok_off[NREQ + 1] = {0};
+    for (int r = 0; r < NREQ; ++r) tok_off[r + 1] = tok_off[r] + lens[r];
+    const int64_t T = tok_off[NREQ];
+
+    /* page tables: source pages from a permutation of 40, destination from 12 */
+    int32_t sperm[SRC_PAGES], dperm[DST_PAGES];
+    for (int i = 0; i < SRC_PAGES; ++i) sperm[i] = i;
+    for (int i = 0; i < DST_PAGES; ++i) dperm[i] = i;
+    shuffle(sperm, SRC_PAGES);
+    shuffle(dperm, DST_PAGES);
+    int64_t spg[NREQ + 1] = {0}, dpg[NREQ + 1] = {0};
+    for (int r = 0; r < NREQ; ++r) {
+        spg[r + 1] = spg[r] + (lens[r] + SRC_PAGE - 1) / SRC_PAGE;
+        dpg[r + 1] = dpg[r] + (lens[r] + DST_PAGE - 1) / DST_PAGE;
+    }
+    const int64_t n_sids = spg[NREQ], n_dids = dpg[NREQ];
+
+    const size_t splane = (size_t)SRC_PAGES * SRC_PAGE * R, dplane = (size_t)DST_PAGES * DST_PAGE * R;
+    const size_t stage_bytes = (size_t)T * Q * R;
+    uint8_t* src_h = malloc(Q * splane);
+    uint8_t* dst_h = malloc(Q * dplane);
+    uint8_t* exp_dst = malloc(Q * dplane);
+    uint8_t* got_dst = malloc(Q * dplane);
+    uint8_t* exp_st = calloc(stage_bytes, 1);
+    uint8_t* got_st = malloc(stage_bytes);
+    if (!src_h || !dst_h || !exp_dst || !got_dst || !exp_st || !got_st) return 4;
+    for (size_t i = 0; i < Q * splane; ++i) src_h[i] = (uint8_t)next_u32();
+    for (size_t i = 0; i < Q * dplane; ++i) dst_h[i] = (uint8_t)next_u32();
+
+    uint8_t *src_d, *dst_d, *st_d;
+    int64_t *tok_d, *spg_d, *dpg_d;
+    int32_t *sid_d, *did_d;
+    CHECK_HIP(hipMalloc((void**)&src_d, Q * splane));
+    CHECK_HIP(hipMalloc((void**)&dst_d, Q * dplane));
+    CHECK_HIP(hipMalloc((void**)&st_d, stage_bytes));
+    CHECK_HIP(hipMalloc((void**)&tok_d, sizeof tok_off));
+    CHECK_HIP(hipMalloc((void**)&spg_d, sizeof spg));
+    CHECK_HIP(hipMalloc((void**)&dpg_d, sizeof dpg));
+    CHECK_HIP(hipMalloc((void**)&sid_d, sizeof sperm));
+    CHECK_HIP(hipMalloc((void**)&did_d, sizeof dperm));
+    CHECK_HIP(hipMemcpy(src_d, src_h, Q * splane, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dst_d, dst_h, Q * dplane, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemset(st_d, 0, stage_bytes));
+    CHECK_HIP(hipMemcpy(tok_d, tok_off, sizeof tok_off, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(spg_d, spg, sizeof spg, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dpg_d, dpg, sizeof dpg, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(sid_d, sperm, sizeof sperm, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(did_d, dperm, sizeof dperm, hipMemcpyHostToDevice));
+
+    void* splanes[Q];
+    void* dplanes[Q];
+    uint8_t* splanes_h[Q];
+    uint8_t* dplanes_h[Q];
+    for (int q = 0; q < Q; ++q) {
+        splanes[q] = src_d + q * splane;
+        dplanes[q] = dst_d + q * dplane;
+        splanes_h[q] = src_h + q * splane;
+        dplanes_h[q] = exp_dst + q * dplane;
+    }
+    const kvx_layout lay = {L, KV, H, D, KVX_BF16};
+    const kvx_pool sp = {splanes, SRC_PAGES, SRC_PAGE, R};
+    const kvx_pool dp = {dplanes, DST_PAGES, DST_PAGE, R};
+    const kvx_reqs reqs = {NREQ, T, tok_d};
+    const kvx_table st = {spg_d, sid_d, n_sids};
+    const kvx_table dt = {dpg_d, did_d, n_dids};
+    unsigned long long* skipped_d;
+    CHECK_HIP(hipMalloc((void**)&skipped_d, sizeof *skipped_d));
+    CHECK_HIP(hipMemset(skipped_d, 0, sizeof *skipped_d));
+
+    hipStream_t stream;
+    CHECK_HIP(hipStreamCreate(&stream));
+    if (kvx_abi_version() != KVX_ABI_VERSION) { fprintf(stderr, "ABI mismatch\n"); return 5; }
+    /* a bad argument: a status, nothing enqueued */
+    if (kvx_gather_scatter(NULL, &sp, &st, &reqs, &dp, &dt, skipped_d, stream) != KVX_E_NULL) {
+        fprintf(stderr, "NULL layout not rejected\n");
+        return 6;
+    }
+    CHECK_KVX(kvx_gather_scatter(&lay, &sp, &st, &reqs, &dp, &dt, skipped_d, stream));
+    CHECK_KVX(kvx_gather(&lay, &sp, &st, &reqs, st_d, (int64_t)stage_bytes, skipped_d, stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    unsigned long long skipped = 1;
+    CHECK_HIP(hipMemcpy(got_dst, dst_d, Q * dplane, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(got_st, st_d, stage_bytes, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(&skipped, skipped_d, sizeof skipped, hipMemcpyDeviceToHost));
+
+    memcpy(exp_dst, dst_h, Q * dplane);
+    int64_t s1 = oracle_gather_scatter(Q, R, splanes_h, R, SRC_PAGE, SRC_PAGES, spg, sperm, NREQ,
+                                       tok_off, dplanes_h, R, DST_PAGE, DST_PAGES, dpg, dperm, 1);
+    int64_t s2 = oracle_gather(Q, R, splanes_h, R, SRC_PAGE, SRC_PAGES, NREQ, tok_off, spg, sperm,
+                               exp_st, 1);
+    if (memcmp(got_dst, exp_dst, Q * dplane) != 0) { fprintf(stderr, "gather_scatter differs\n"); return 7; }
+    if (memcmp(got_st, exp_st, stage_bytes) != 0) { fprintf(stderr, "gather differs\n"); return 8; }
+    if ((int64_t)skipped != s1 + s2 || skipped != 0) { fprintf(stderr, "skip count %llu\n", skipped); return 9; }
+
+    hipStreamDestroy(stream);
+    hipFree(src_d); hipFree(dst_d); hipFree(st_d); hipFree(tok_d); hipFree(spg_d); hipFree(dpg_d);
+    hipFree(sid_d); hipFree(did_d); hipFree(skipped_d);
+    free(src_h); free(dst_h); free(exp_dst); free(got_dst); free(exp_st); free(got_st);
+    printf("abi_smoke ok: %lld tokens, %d planes, rows of %d bytes, pages %d -> %d\n",
+           (long long)T, Q, R, SRC_PAGE, DST_PAGE);
+    return 0;
+}

@@ -260,3 +260,13 @@ def test_check_tables_shapes():
     assert _check(side, [0, 9, 5], 5)[0] == 2               # decreasing
     short = wl.side_from_page_lists([np.array([0]), np.array([2])], 4, 4)
     assert _check(short, ok_tok, 9) == (2, 0)               # request 0 needs 2 pages
+
+
+def test_header_is_plain_c():
+    """include/kvx.h compiles as C99 (with the platform define every HIP host
+    program built by a plain C compiler needs)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    p = subprocess.run(["gcc", "-x", "c", "-std=c99", "-Wall", "-Wextra", "-Werror",
+                        "-fsyntax-only", "-D__HIP_PLATFORM_AMD__", "-I",
+                        os.path.join(rocm, "include"), HEADER], capture_output=True, text=True)
+    assert p.returncode == 0, p.stderr
