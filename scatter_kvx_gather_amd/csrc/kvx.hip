@@ -208,6 +208,29 @@ uint32_t wide_rows_for(const Shape& sh, int64_t rows, int64_t row_bytes, int cus
     return rows * row_bytes > round_bytes ? 1u : sh.U;
 }
 
+// XCD-aware renumbering pays when a launch spans more memory than the
+// translation caches reach: then each XCD, working on ~1/8 of the planes,
+// touches ~1/8 of the translations.  Below that it costs a few percent.
+// Measured (same process, alternating): the 2048-token request in 4.5 GiB
+// pools, gather-scatter 5015 GB/s without vs 4880 with; the same request
+// spread over 36 GiB pools 4632 without vs 4798 with; 36 GiB page-16 pools
+// 5456 vs 5924; the fragmented gather from an 18 GiB pool 5040 vs 5289; a
+// head-sliced copy over 14.4 GiB 5259 vs 5091; permutes of 0.1-0.9 GB 3-9%
+// faster without.
+constexpr double kRemapSpanBytes = 16.0 * (1ull << 30);
+
+uint32_t remap_for(double span_bytes) {
+    if (KVX_XCD_REMAP == 0) return 0;
+    if (KVX_XCD_REMAP == 1) return 1;
+    return span_bytes > kRemapSpanBytes ? 1u : 0u;
+}
+
+// Bytes of the nq planes of a pool that a launch may touch.
+double pool_span(const kvx_pool* p, int32_t nq) {
+    return static_cast<double>(p->num_pages) * p->page_size * static_cast<double>(p->slot_stride) *
+           nq;
+}
+
 // Paged ops only: rows of 512 B .. 16 KiB that are not a power-of-two number
 // of KiB use the row-loop copy (vpl = -KMAX, U rows per chunk, U <= the
 // instance's maximum).
@@ -332,15 +355,18 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
         else a.src.base = static_cast<char*>(src_stage);
         if constexpr (std::is_same<Dst, PoolRef>::value) fill_pool_ref(&a.dst, dst, dt, q0, nq);
         else a.dst.base = static_cast<char*>(dst_stage);
+        const double stage = static_cast<double>(reqs->total_tokens) * g.Q * g.R;
+        a.c.remap = remap_for((src != nullptr ? pool_span(src, nq) : stage) +
+                              (dst != nullptr ? pool_span(dst, nq) : stage));
         const uint32_t grid = grid_for(a.c.nchunks, cus);
         if (log_enabled())
             std::fprintf(stderr,
                          "kvx: %s Q=%d planes[%d,%d) R=%lld T=%lld reqs=%d copy=%s U=%u "
-                         "chunks=%u grid=%u\n",
+                         "chunks=%u grid=%u remap=%u\n",
                          op_name(op), g.Q, q0, q0 + nq, static_cast<long long>(g.R),
                          static_cast<long long>(reqs->total_tokens), reqs->num_reqs,
                          sh.vpl > 0 ? "wide" : (sh.vpl < 0 ? "row-loop" : "flat"), sh.U,
-                         a.c.nchunks, grid);
+                         a.c.nchunks, grid, a.c.remap);
         s = launch(paged_kernel<Src, Dst>(sh.vpl, sh.U), grid, a, stream);
         if (s != KVX_OK) return s;
     }
@@ -375,6 +401,8 @@ kvx_status run_permute(const Geom& g, void* const* hf, int64_t s_cap, int64_t se
         a.flat = static_cast<char*>(flat);
         a.s_cap = s_cap;
         a.H = g.H;
+        a.c.remap = remap_for(static_cast<double>(nq) * g.H * s_cap * g.Db +
+                              static_cast<double>(nq) * seq * g.R);
         const uint32_t grid = grid_for(a.c.nchunks, cus);
         if (log_enabled())
             std::fprintf(stderr,
@@ -488,6 +516,7 @@ kvx_status run_heads(const Geom& g, const kvx_reqs* reqs, const kvx_pool* src,
         a.Ut = Ut;
         a.hblocks = hblocks;
         a.head_major = (a.hs.hnd && a.hd.hnd) ? 1 : 0;
+        a.c.remap = remap_for(pool_span(src, nq) + pool_span(dst, nq));
         if (kt > 0) a.c.U = static_cast<uint32_t>(Ut);
         const uint32_t grid = grid_for(a.c.nchunks, cus);
         if (log_enabled())

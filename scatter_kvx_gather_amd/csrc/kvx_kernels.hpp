@@ -30,7 +30,8 @@
 // store nothing, so the loads carry no branches.
 //
 // Waves grid-stride over the chunks (by default the grid has one wave per
-// chunk; the host can cap it at a few workgroups per compute unit), and
+// chunk; the host can cap it at a few workgroups per compute unit).  In
+// launches that span more memory than the translation caches reach,
 // workgroup ids are renumbered so that consecutive chunks (the same plane,
 // adjacent tokens) run on the same XCD: gfx950 deals workgroups to its 8 XCDs
 // round-robin, and each XCD has its own L2 and translation caches.
@@ -58,8 +59,8 @@ namespace kvx {
 #define KVX_LOAD_NT 1              // nontemporal loads
 #endif
 #ifndef KVX_XCD_REMAP
-#define KVX_XCD_REMAP 1            // XCD-aware workgroup renumbering
-#endif
+#define KVX_XCD_REMAP 2            // XCD-aware workgroup renumbering: 0 never,
+#endif                             // 1 always, 2 when a launch spans > 16 GiB
 
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
@@ -90,6 +91,7 @@ struct Common {
     uint32_t nchunks;
     uint32_t V;                 // 16-byte vectors per unit
     uint32_t v_magic;           // ceil(2^32 / V)
+    uint32_t remap;             // 1: XCD-aware workgroup renumbering
 };
 
 // One side of a paged move that is a pool.
@@ -565,14 +567,16 @@ __device__ __forceinline__ void copy_flat(const Common& c, uint64_t s_l, uint64_
 
 // --------------------------------------------------------------- kernels --
 
-// Wave number with XCD-aware workgroup renumbering: with G % 8 == 0, logical
-// block (b % 8) * (G / 8) + b / 8 puts logical blocks [x*G/8, (x+1)*G/8) on
-// XCD x, so the chunks a grid-stride round hands to one XCD are contiguous.
-__device__ __forceinline__ uint32_t wave_id() {
+// Wave number, with XCD-aware workgroup renumbering when c.remap is set: with
+// G % 8 == 0, logical block (b % 8) * (G / 8) + b / 8 puts logical blocks
+// [x*G/8, (x+1)*G/8) on XCD x, so the chunks a grid-stride round hands to one
+// XCD are contiguous (one XCD then touches about 1/8 of the planes, and of
+// the address translations).
+__device__ __forceinline__ uint32_t wave_id(const Common& c) {
     const uint32_t G = gridDim.x;
     const uint32_t b = blockIdx.x;
     const uint32_t lb =
-        (KVX_XCD_REMAP && G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
+        (c.remap && G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
     return __builtin_amdgcn_readfirstlane(lb * kWavesPerBlock + (threadIdx.x >> 6));
 }
 
@@ -588,7 +592,7 @@ __global__ __launch_bounds__(kBlock) void k_paged(PagedArgs<Src, Dst> a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t nwaves = gridDim.x * kWavesPerBlock;
     unsigned long long nskip = 0;
-    for (uint32_t chunk = wave_id(); chunk < a.c.nchunks; chunk += nwaves) {
+    for (uint32_t chunk = wave_id(a.c); chunk < a.c.nchunks; chunk += nwaves) {
         const PagedChunk k = paged_chunk(a.c, chunk);
         uint64_t s = 0, d = 0;
         const int code = resolve(a, k, static_cast<uint32_t>(lane), s, d);
@@ -606,7 +610,7 @@ __global__ __launch_bounds__(kBlock) void k_heads(HeadArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t nwaves = gridDim.x * kWavesPerBlock;
     unsigned long long nskip = 0;
-    for (uint32_t chunk = wave_id(); chunk < a.c.nchunks; chunk += nwaves) {
+    for (uint32_t chunk = wave_id(a.c); chunk < a.c.nchunks; chunk += nwaves) {
         uint64_t s = 0, d = 0;
         bool first = false;
         const int code = resolve_heads(a, chunk, static_cast<uint32_t>(lane), s, d, first);
@@ -636,7 +640,7 @@ __global__ __launch_bounds__(kBlock) void k_heads_hnd(HeadArgs a) {
     const uint32_t vd_shift = static_cast<uint32_t>(__builtin_ctz(vd));   // VD is a power of two
     const uint64_t B = static_cast<uint64_t>(a.Ut);
     unsigned long long nskip = 0;
-    for (uint32_t chunk = wave_id(); chunk < c.nchunks; chunk += nwaves) {
+    for (uint32_t chunk = wave_id(c); chunk < c.nchunks; chunk += nwaves) {
         const uint32_t ql = chunk / c.chunks_per_plane;
         const uint32_t rem = chunk - ql * c.chunks_per_plane;
         const uint32_t tb = rem / static_cast<uint32_t>(a.hblocks);
@@ -714,7 +718,7 @@ template <bool REBUILD>
 __global__ __launch_bounds__(kBlock) void k_permute(PermuteArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t nwaves = gridDim.x * kWavesPerBlock;
-    for (uint32_t chunk = wave_id(); chunk < a.c.nchunks; chunk += nwaves) {
+    for (uint32_t chunk = wave_id(a.c); chunk < a.c.nchunks; chunk += nwaves) {
         const PermChunk k = perm_chunk(a.c, chunk);
         uint64_t s = 0, d = 0;
         const int code = resolve_perm<REBUILD>(a, k, static_cast<uint32_t>(lane), s, d);
@@ -743,7 +747,7 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(PermuteArgs a) {
         hf_off[j] = static_cast<uint64_t>(h) * a.s_cap * Db + (idx - h * vd) * 16u;
     }
     const uint32_t seq = a.c.units_per_plane;
-    for (uint32_t chunk = wave_id(); chunk < a.c.nchunks; chunk += nwaves) {
+    for (uint32_t chunk = wave_id(a.c); chunk < a.c.nchunks; chunk += nwaves) {
         const uint32_t ql = chunk / a.c.chunks_per_plane;
         const uint32_t s0 = (chunk - ql * a.c.chunks_per_plane) * U;
         const uint64_t hf = reinterpret_cast<uint64_t>(a.hf[ql]);
