@@ -287,11 +287,36 @@ def summarize_pmc(fetch_dir, write_dir, out_path):
 
 # ------------------------------------------------------ all workloads --
 
-def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
+def all_configs(torch, kvx, wl, wdev, dev, stream, reps, cpu=True):
     """Time every op on every workload at full size (one JSON line each),
-    beside a plain contiguous copy of the same bytes timed the same way."""
+    beside a plain contiguous copy of the same bytes timed the same way and
+    (cpu baseline leg) the oracle on a bounded host sample of the same
+    workload."""
+    import numpy as np
+    import oracle
+    nt = min(16, os.cpu_count() or 1)
+
     def d(a):
         return torch.from_numpy(a).to(dev)
+
+    def host(t):
+        """Host uint8 copy of a device tensor (one plane per row)."""
+        return t.cpu().view(torch.uint8).numpy().reshape(t.shape[0], -1)
+
+    def cpu_rate(run, nbytes, sample, budget_s=1.0):
+        """Oracle GB/s (r+w) of `run` (one op on the host sample moving
+        nbytes), repeated for about budget_s after one untimed call."""
+        if not cpu:
+            return None
+        run(0)
+        n, t0 = 0, time.perf_counter()
+        while True:
+            run(n + 1)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or n >= 100:
+                break
+        return {"GBps": round(nbytes * n / el / 1e9, 2), "threads": nt, "sample": sample}
 
     def lay_of(g):
         return kvx.Layout(g.num_layers, g.num_kv, g.kv_heads, g.head_dim, g.dtype)
@@ -336,14 +361,17 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
             torch.cuda.empty_cache()
         return copy_rates[(n, k)]
 
-    def emit(cfg, op, ms, nbytes, note="", rot=1):
+    def emit(cfg, op, ms, nbytes, note="", rot=1, oracle_cpu=None):
         gbps = nbytes / (ms * 1e-3) / 1e9
         cp = copy_rate(nbytes, rot)
-        print(json.dumps({"workload": cfg, "op": op, "ms": round(ms, 5),
-                          "bytes_rw": nbytes, "GBps": round(gbps, 1),
-                          "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-                          "plain_copy_GBps": round(cp, 1), "vs_plain_copy": round(gbps / cp, 3),
-                          "note": note}), flush=True)
+        line = {"workload": cfg, "op": op, "ms": round(ms, 5),
+                "bytes_rw": nbytes, "GBps": round(gbps, 1),
+                "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+                "plain_copy_GBps": round(cp, 1), "vs_plain_copy": round(gbps / cp, 3),
+                "note": note}
+        if oracle_cpu is not None:
+            line["cpu_oracle"] = oracle_cpu
+        print(json.dumps(line), flush=True)
 
     def pool_of(case, side, seed):
         g = case.geom
@@ -361,12 +389,20 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
         ts, td = kvx.Table(d(c.src.pg_off), d(c.src.ids)), kvx.Table(d(c.dst.pg_off), d(c.dst.ids))
         lay = lay_of(g)
         nb = 2 * c.payload_bytes()
+        R = g.row_bytes
+        hA, hB = host(A), host(B)
+        hst = np.zeros(c.total_tokens * g.token_bytes, np.uint8)
+        smp = f"the whole request, {g.planes} planes"
+        cpu_g = cpu_rate(lambda i: oracle.gather(list(hA), R, 1, 1024, R, c.tok_off, c.src.pg_off,
+                                                 c.src.ids, hst, nt), nb, smp)
+        cpu_s = cpu_rate(lambda i: oracle.scatter(hst, R, c.tok_off, c.dst.pg_off, c.dst.ids,
+                                                  list(hB), R, 1, 1024, nt), nb, smp)
         emit(c.name, "gather", timed(lambda i: kvx.gather(lay, kvx.Pool(A, 1024), ts, reqs, st,
                                                          stream=stream), reps * 10), nb,
-             "3.5 MiB request: launch-latency bound, cache resident")
+             "3.5 MiB request: launch-latency bound, cache resident", oracle_cpu=cpu_g)
         emit(c.name, "scatter", timed(lambda i: kvx.scatter(lay, st, reqs, kvx.Pool(B, 1024), td,
                                                            stream=stream), reps * 10), nb,
-             "launch-latency bound")
+             "launch-latency bound", oracle_cpu=cpu_s)
         del A, B, st
         torch.cuda.empty_cache()
 
@@ -382,13 +418,30 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
         lay = lay_of(g)
         PA, PB = kvx.Pool(A, 32768), kvx.Pool(B, 32768)
         nb = 2 * cs[0].payload_bytes()
+        k, R = 8, g.row_bytes
+        pa, pb = list(host(A[:k])), list(host(B[:k]))
+        hst = np.zeros(2048 * k * R, np.uint8)
+        nbk = 2 * 2048 * k * R
+        smp = f"{k} of {g.planes} planes, the 16 requests rotated"
+        cpu_gs = cpu_rate(lambda i: oracle.gather_scatter(
+            pa, R, 1, 32768, cs[i % NREQ].src.pg_off, cs[i % NREQ].src.ids, R, cs[0].tok_off, pb, R,
+            1, 32768, cs[i % NREQ].dst.pg_off, cs[i % NREQ].dst.ids, nt), nbk, smp)
+        cpu_g = cpu_rate(lambda i: oracle.gather(
+            pa, R, 1, 32768, R, cs[0].tok_off, cs[i % NREQ].src.pg_off, cs[i % NREQ].src.ids, hst,
+            nt), nbk, smp)
+        cpu_s = cpu_rate(lambda i: oracle.scatter(
+            hst, R, cs[0].tok_off, cs[i % NREQ].dst.pg_off, cs[i % NREQ].dst.ids, pb, R, 1, 32768,
+            nt), nbk, smp)
+        del pa, pb, hst
         emit(cs[0].name, "gather_scatter", timed(lambda i: kvx.gather_scatter(
             lay, PA, tabs[i % NREQ][0], reqs, PB, tabs[i % NREQ][1], stream=stream), reps * 4), nb,
-             rot=NREQ)
+             rot=NREQ, oracle_cpu=cpu_gs)
         emit(cs[0].name, "gather", timed(lambda i: kvx.gather(
-            lay, PA, tabs[i % NREQ][0], reqs, st, stream=stream), reps * 4), nb, rot=NREQ)
+            lay, PA, tabs[i % NREQ][0], reqs, st, stream=stream), reps * 4), nb, rot=NREQ,
+             oracle_cpu=cpu_g)
         emit(cs[0].name, "scatter", timed(lambda i: kvx.scatter(
-            lay, st, reqs, PB, tabs[i % NREQ][1], stream=stream), reps * 4), nb, rot=NREQ)
+            lay, st, reqs, PB, tabs[i % NREQ][1], stream=stream), reps * 4), nb, rot=NREQ,
+             oracle_cpu=cpu_s)
         del A, B, st, PA, PB
         torch.cuda.empty_cache()
 
@@ -399,9 +452,17 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
         st = torch.empty(c.total_tokens * g.token_bytes, dtype=torch.uint8, device=dev)
         reqs = kvx.Requests(d(c.tok_off), c.total_tokens)
         ts = kvx.Table(d(c.src.pg_off), d(c.src.ids))
+        k, R = 8, g.row_bytes
+        pa = list(host(A[:k]))
+        hst = np.zeros(c.total_tokens * k * R, np.uint8)
+        cpu_g = cpu_rate(lambda i: oracle.gather(pa, R, 1, c.src.num_slots, R, c.tok_off,
+                                                 c.src.pg_off, c.src.ids, hst, nt),
+                         2 * c.total_tokens * k * R, f"{k} of {g.planes} planes, all 32 requests")
+        del pa, hst
         emit(c.name, "gather", timed(lambda i: kvx.gather(lay_of(g), kvx.Pool(A, c.src.num_slots),
                                                          ts, reqs, st, stream=stream), reps),
-             2 * c.payload_bytes(), f"{c.num_reqs} requests, {c.total_tokens} tokens")
+             2 * c.payload_bytes(), f"{c.num_reqs} requests, {c.total_tokens} tokens",
+             oracle_cpu=cpu_g)
         del A, st
         torch.cuda.empty_cache()
 
@@ -417,10 +478,22 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
             for t in hf + fl:
                 wdev.fill_hash(t, 3, stream=stream)
             nb = 2 * c.payload_bytes()
+            k, H, Db = 8, g.kv_heads, g.head_bytes
+            hh = list(host(hf[0][:k]))
+            hfl = np.zeros(k * seq * g.row_bytes, np.uint8)
+            nbk = 2 * k * seq * g.row_bytes
+            smp = f"{k} of {g.planes} planes"
+            cpu_e = cpu_rate(lambda i: oracle.extract_permute(hh, H, Db, seq, seq, hfl, nt), nbk,
+                             smp)
+            cpu_r = cpu_rate(lambda i: oracle.rebuild_permute(hfl, H, Db, seq, hh, seq, nt), nbk,
+                             smp)
+            del hh, hfl
             emit(c.name, "extract", timed(lambda i: kvx.extract_permute(
-                lay, hf[i % 2], seq, seq, fl[i % 2], stream=stream), reps * 4), nb, rot=2)
+                lay, hf[i % 2], seq, seq, fl[i % 2], stream=stream), reps * 4), nb, rot=2,
+                 oracle_cpu=cpu_e)
             emit(c.name, "rebuild", timed(lambda i: kvx.rebuild_permute(
-                lay, fl[i % 2], seq, hf[i % 2], seq, stream=stream), reps * 4), nb, rot=2)
+                lay, fl[i % 2], seq, hf[i % 2], seq, stream=stream), reps * 4), nb, rot=2,
+                 oracle_cpu=cpu_r)
             del hf, fl
             torch.cuda.empty_cache()
 
@@ -437,12 +510,24 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
             lay = lay_of(g)
             PA, PB = kvx.Pool(A, c.src.num_pages, page), kvx.Pool(B, c.dst.num_pages, page)
             nb = 2 * c.payload_bytes()
+            R = g.row_bytes
+            pa, pb = list(host(A)), list(host(B))
+            hst = np.zeros(c.total_tokens * g.token_bytes, np.uint8)
+            smp = f"all {g.planes} planes, the 16 requests rotated"
+            cpu_gs = cpu_rate(lambda i: oracle.gather_scatter(
+                pa, R, page, c.src.num_pages, cs[i % NREQ].src.pg_off, cs[i % NREQ].src.ids, R,
+                c.tok_off, pb, R, page, c.dst.num_pages, cs[i % NREQ].dst.pg_off,
+                cs[i % NREQ].dst.ids, nt), nb, smp)
+            cpu_g = cpu_rate(lambda i: oracle.gather(
+                pa, R, page, c.src.num_pages, R, c.tok_off, cs[i % NREQ].src.pg_off,
+                cs[i % NREQ].src.ids, hst, nt), nb, smp)
+            del pa, pb, hst
             emit(c.name, "gather_scatter", timed(lambda i: kvx.gather_scatter(
                 lay, PA, tabs[i % NREQ][0], reqs, PB, tabs[i % NREQ][1], stream=stream),
-                reps * 8), nb, "16 disjoint requests rotated", rot=NREQ)
+                reps * 8), nb, "16 disjoint requests rotated", rot=NREQ, oracle_cpu=cpu_gs)
             emit(c.name, "gather", timed(lambda i: kvx.gather(
                 lay, PA, tabs[i % NREQ][0], reqs, st, stream=stream), reps * 8), nb,
-                 "16 disjoint requests rotated", rot=NREQ)
+                 "16 disjoint requests rotated", rot=NREQ, oracle_cpu=cpu_g)
             del A, B, st, PA, PB
             torch.cuda.empty_cache()
 
@@ -461,10 +546,18 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
         lay = lay_of(c.geom)
         PA = kvx.Pool(A, c.src.num_pages, B, slot_stride=8 * Db)
         PD = [kvx.Pool(t, c.dst.num_pages, B, slot_stride=4 * Db) for t in Ds]
+        k = 8
+        pa, pd = list(host(A[:k])), list(host(Ds[0][:k]))
+        cpu_h = cpu_rate(lambda i: oracle.gather_scatter_heads(
+            pa, 8 * Db, B, c.src.num_pages, c.src.pg_off, c.src.ids, (8, 4 * (i % 2), 1), Db, 4,
+            c.tok_off, pd, 4 * Db, B, c.dst.num_pages, c.dst.pg_off, c.dst.ids, (4, 0, 1), nt),
+            2 * c.total_tokens * k * 4 * Db, f"{k} of {c.geom.planes} planes")
+        del pa, pd
         emit(c.name, "gather_scatter_heads", timed(lambda i: kvx.gather_scatter_heads(
             lay, PA, ts, kvx.Heads(8, 4 * (i % 2), "hnd"), reqs, PD[i % 2], td,
             kvx.Heads(4, 0, "hnd"), stream=stream), reps * 2), 2 * c.payload_bytes(),
-             f"{c.num_reqs} requests, {c.total_tokens} tokens, 4 of 8 heads per launch", rot=2)
+             f"{c.num_reqs} requests, {c.total_tokens} tokens, 4 of 8 heads per launch", rot=2,
+             oracle_cpu=cpu_h)
         del A, Ds, PA, PD
         torch.cuda.empty_cache()
 
@@ -474,10 +567,17 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps):
         A, B = pool_of(c, c.src, 1), pool_of(c, c.dst, 2)
         reqs = kvx.Requests(d(c.tok_off), c.total_tokens)
         ts, td = kvx.Table(d(c.src.pg_off), d(c.src.ids)), kvx.Table(d(c.dst.pg_off), d(c.dst.ids))
+        k, R = 4, g.row_bytes
+        pa, pb = list(host(A[:k])), list(host(B[:k]))
+        cpu_gs = cpu_rate(lambda i: oracle.gather_scatter(
+            pa, R, 16, c.src.num_pages, c.src.pg_off, c.src.ids, R, c.tok_off, pb, R, 16,
+            c.dst.num_pages, c.dst.pg_off, c.dst.ids, nt), 2 * c.total_tokens * k * R,
+            f"{k} of {g.planes} planes, all 64 requests")
+        del pa, pb
         emit(c.name, "gather_scatter", timed(lambda i: kvx.gather_scatter(
             lay_of(g), kvx.Pool(A, c.src.num_pages, 16), ts, reqs, kvx.Pool(B, c.dst.num_pages, 16),
             td, stream=stream), reps), 2 * c.payload_bytes(),
-             f"{c.num_reqs} requests, {c.total_tokens} tokens, page 16")
+             f"{c.num_reqs} requests, {c.total_tokens} tokens, page 16", oracle_cpu=cpu_gs)
         del A, B
         torch.cuda.empty_cache()
 
@@ -731,7 +831,7 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)
     if args.all_configs:
-        all_configs(torch, kvx, wl, wdev, dev, stream, reps=5)
+        all_configs(torch, kvx, wl, wdev, dev, stream, reps=5, cpu=not args.no_cpu_baseline)
         return 0
     if args.concurrent:
         concurrent_load(torch, kvx, wl, wdev, dev)
