@@ -113,6 +113,10 @@ class Workload:
         self.PA = kvx.Pool(self.A, S)
         self.PB = kvx.Pool(self.B, S)
         self.op_bytes = 2 * T * Q * R               # read + write per op
+        self.seeds = {"tables": c0.table_seed, "source_values": c0.value_seed,
+                      "destination_values": c0.sentinel_seed}
+        self.tables_sha256 = hashlib.sha256(
+            "".join(c.table_sha256() for c in self.cases).encode()).hexdigest()
         # page tables the kernels read per step (not in the payload bytes):
         # tok_off once per paged op, pg_off + page ids once per pool side
         # (gather-scatter two sides, gather and scatter one each)
@@ -873,12 +877,18 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / K
-    live_ms = {
-        "gather_scatter": sum(live_ev[i][0].elapsed_time(live_ev[i][1])
-                              for i in range(0, K, 2)) / len(range(0, K, 2)),
-        "scatter": sum(live_ev[i][4].elapsed_time(live_ev[i][5])
-                       for i in range(1, K, 2)) / max(1, len(range(1, K, 2))),
-    }
+    gs_ms = sorted(live_ev[i][0].elapsed_time(live_ev[i][1]) for i in range(0, K, 2))
+    sc_ms = sorted(live_ev[i][4].elapsed_time(live_ev[i][5]) for i in range(1, K, 2))
+    live_ms = {"gather_scatter": sum(gs_ms) / len(gs_ms),
+               "scatter": sum(sc_ms) / max(1, len(sc_ms))}
+
+    def pct(v, q):
+        return v[min(len(v) - 1, int(round(q * (len(v) - 1))))] if v else None
+
+    launch_stats = {op: {"mean": round(sum(v) / len(v), 5), "median": round(pct(v, 0.5), 5),
+                         "p95": round(pct(v, 0.95), 5), "max": round(v[-1], 5),
+                         "launches": len(v)}
+                    for op, v in (("gather_scatter", gs_ms), ("scatter", sc_ms)) if v}
     step_bytes = wk.op_bytes * len(OPS)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"timed {K} steps: {ms_step:.4f} ms/step (wall {wall * 1e3 / K:.4f} ms/step), "
@@ -980,11 +990,14 @@ def main():
                         "disjoint requests rotated",
             "step": "gather_scatter + gather + rebuild_permute + extract_permute + scatter",
             "bytes_per_step": step_bytes,
+            "seeds": wk.seeds,
+            "tables_sha256": wk.tables_sha256,
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "GiBps": round(value * 1e9 / 2 ** 30, 1),
         "table_bytes_per_step": wk.table_bytes_per_step,
         "ms_per_288MiB_request": round(live_ms["gather_scatter"], 5),
+        "launch_ms": launch_stats,
         "ops": {op: {"ms": round(op_ms[op], 5),
                      "GBps": round(wk.op_bytes / (op_ms[op] * 1e-3) / 1e9, 1)} for op in OPS},
         "ops_timing": "diagnostic pass after the timed region, events around every op",

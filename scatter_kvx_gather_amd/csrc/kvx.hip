@@ -573,6 +573,154 @@ kvx_status check_hf(const Geom& g, const void* const* hf, int64_t s_cap, int64_t
 
 }  // namespace
 
+namespace {
+
+// One row a call touches: bytes [lo, hi) for batch token `tok`.
+struct Span {
+    uint64_t lo, hi;
+    int64_t tok;
+};
+
+// Slot of every batch token in one pool side, or -1 where the call skips the
+// token (page-table index or page id out of range, as the kernels decide).
+kvx_status side_slots(const kvx_reqs* reqs, const kvx_pool* p, const kvx_table* t,
+                      std::vector<int64_t>* slot) {
+    if (p->planes == nullptr) return KVX_E_NULL;
+    if (p->num_pages < 0 || p->page_size < 1) return KVX_E_SHAPE;
+    if (t->num_ids < 0) return KVX_E_SHAPE;
+    if (reqs->num_reqs > 0 && t->pg_off == nullptr) return KVX_E_NULL;
+    if (t->num_ids > 0 && t->page_ids == nullptr) return KVX_E_NULL;
+    slot->assign(static_cast<size_t>(reqs->total_tokens), -1);
+    for (int32_t r = 0; r < reqs->num_reqs; ++r) {
+        const int64_t off = reqs->tok_off[r], n = reqs->tok_off[r + 1] - off;
+        for (int64_t k = 0; k < n; ++k) {
+            const int64_t idx = t->pg_off[r] + k / p->page_size;
+            if (idx < 0 || idx >= t->num_ids) continue;
+            const int64_t page = t->page_ids[idx];
+            if (page < 0 || page >= p->num_pages) continue;
+            (*slot)[static_cast<size_t>(off + k)] = page * p->page_size + k % p->page_size;
+        }
+    }
+    return KVX_OK;
+}
+
+// Rows of the live tokens on one side (Q per token).
+void side_spans(const Geom& g, const kvx_reqs* reqs, const kvx_pool* p,
+                const std::vector<int64_t>& slot, const void* staging,
+                const std::vector<char>& live, std::vector<Span>* out) {
+    out->clear();
+    for (int32_t r = 0; r < reqs->num_reqs; ++r) {
+        const int64_t off = reqs->tok_off[r], n = reqs->tok_off[r + 1] - off;
+        for (int64_t k = 0; k < n; ++k) {
+            const int64_t tok = off + k;
+            if (!live[static_cast<size_t>(tok)]) continue;
+            for (int32_t q = 0; q < g.Q; ++q) {
+                uint64_t lo;
+                if (p != nullptr)
+                    lo = reinterpret_cast<uint64_t>(p->planes[q]) +
+                         static_cast<uint64_t>(slot[static_cast<size_t>(tok)]) *
+                             static_cast<uint64_t>(p->slot_stride);
+                else
+                    lo = reinterpret_cast<uint64_t>(staging) +
+                         static_cast<uint64_t>((off * g.Q + q * n + k) * g.R);
+                out->push_back(Span{lo, lo + static_cast<uint64_t>(g.R), tok});
+            }
+        }
+    }
+}
+
+bool by_lo(const Span& a, const Span& b) { return a.lo < b.lo || (a.lo == b.lo && a.tok < b.tok); }
+
+}  // namespace
+
+namespace {
+
+// KVX_VALIDATE=1 (debug): before enqueueing, every data-movement call
+// synchronizes its stream, copies its tables to the host and checks the
+// preconditions the kernels assume: written rows pairwise disjoint and, for
+// the row ops, disjoint from the rows read.  Out-of-range ids stay legal
+// (those rows are skipped and counted).  It costs a synchronization and
+// O(Q * tokens) host work per call, so it is for debugging, not production;
+// it cannot run on a stream under graph capture (KVX_E_HIP).
+bool validate_enabled() {
+    static const bool on = [] {
+        const char* e = std::getenv("KVX_VALIDATE");
+        return e != nullptr && e[0] == '1';
+    }();
+    return on;
+}
+
+template <class T>
+kvx_status to_host(const T* d, int64_t n, std::vector<T>* h) {
+    h->assign(static_cast<size_t>(n), T());
+    if (n == 0) return KVX_OK;
+    if (d == nullptr) return KVX_E_NULL;
+    return hipMemcpy(h->data(), d, sizeof(T) * static_cast<size_t>(n), hipMemcpyDeviceToHost) ==
+                   hipSuccess
+               ? KVX_OK
+               : KVX_E_HIP;
+}
+
+struct HostTable {
+    std::vector<int64_t> pg;
+    std::vector<int32_t> ids;
+    kvx_table t;
+};
+
+kvx_status host_table(const kvx_table* t, int32_t nr, HostTable* h) {
+    KVX_TRY(to_host(t->pg_off, static_cast<int64_t>(nr) + 1, &h->pg));
+    KVX_TRY(to_host(t->page_ids, t->num_ids, &h->ids));
+    h->t = kvx_table{h->pg.data(), h->ids.data(), t->num_ids};
+    return KVX_OK;
+}
+
+// Head-sliced copies: destination slots of the live tokens pairwise distinct.
+kvx_status distinct_slots(const kvx_reqs* r, const kvx_pool* src, const kvx_table* st,
+                          const kvx_pool* dst, const kvx_table* dt, int64_t* bad) {
+    std::vector<int64_t> ss, ds;
+    KVX_TRY(side_slots(r, src, st, &ss));
+    KVX_TRY(side_slots(r, dst, dt, &ds));
+    std::vector<uint64_t> seen(static_cast<size_t>((dst->num_pages * dst->page_size + 63) / 64), 0);
+    for (int64_t t = 0; t < r->total_tokens; ++t) {
+        const int64_t d = ds[static_cast<size_t>(t)];
+        if (d < 0 || ss[static_cast<size_t>(t)] < 0) continue;
+        uint64_t& w = seen[static_cast<size_t>(d / 64)];
+        const uint64_t bit = uint64_t(1) << (d % 64);
+        if (w & bit) {
+            *bad = t;
+            return KVX_E_DUPLICATE;
+        }
+        w |= bit;
+    }
+    return KVX_OK;
+}
+
+kvx_status validate_call(const kvx_layout* layout, const kvx_reqs* reqs, const kvx_pool* src,
+                         const kvx_table* st, const kvx_pool* dst, const kvx_table* dt,
+                         const void* staging, int64_t staging_bytes, bool heads,
+                         hipStream_t stream) {
+    if (reqs->num_reqs == 0 || reqs->total_tokens == 0) return KVX_OK;
+    if (hipStreamSynchronize(stream) != hipSuccess) return KVX_E_HIP;
+    std::vector<int64_t> tok;
+    KVX_TRY(to_host(reqs->tok_off, static_cast<int64_t>(reqs->num_reqs) + 1, &tok));
+    const kvx_reqs hr{reqs->num_reqs, reqs->total_tokens, tok.data()};
+    HostTable hs, hd;
+    if (src != nullptr) KVX_TRY(host_table(st, reqs->num_reqs, &hs));
+    if (dst != nullptr) KVX_TRY(host_table(dt, reqs->num_reqs, &hd));
+    int64_t bad = -1;
+    const kvx_status s =
+        heads ? distinct_slots(&hr, src, &hs.t, dst, &hd.t, &bad)
+              : kvx_check_disjoint(layout, &hr, src, src != nullptr ? &hs.t : nullptr, dst,
+                                   dst != nullptr ? &hd.t : nullptr, staging, staging_bytes,
+                                   &bad);
+    if (s != KVX_OK)
+        std::fprintf(stderr, "kvx: KVX_VALIDATE: %s (batch token %lld); nothing enqueued\n",
+                     kvx_status_str(s), static_cast<long long>(bad));
+    return s;
+}
+
+}  // namespace
+
 extern "C" {
 
 kvx_status kvx_gather(const kvx_layout* layout, const kvx_pool* src, const kvx_table* src_table,
@@ -585,6 +733,9 @@ kvx_status kvx_gather(const kvx_layout* layout, const kvx_pool* src, const kvx_t
     KVX_TRY(check_source_nonempty(src, reqs));
     KVX_TRY(check_table(src_table, reqs));
     KVX_TRY(check_staging(staging, staging_bytes, g, reqs));
+    if (validate_enabled())
+        KVX_TRY(validate_call(layout, reqs, src, src_table, nullptr, nullptr, staging,
+                              staging_bytes, false, stream));
     return run_paged<PoolRef, StageRef>(0, g, reqs, src, src_table, nullptr, nullptr, nullptr,
                                         staging, skipped, stream);
 }
@@ -598,6 +749,9 @@ kvx_status kvx_scatter(const kvx_layout* layout, const void* staging, int64_t st
     KVX_TRY(check_pool(dst, g));
     KVX_TRY(check_table(dst_table, reqs));
     KVX_TRY(check_staging(staging, staging_bytes, g, reqs));
+    if (validate_enabled())
+        KVX_TRY(validate_call(layout, reqs, nullptr, nullptr, dst, dst_table, staging,
+                              staging_bytes, false, stream));
     return run_paged<StageRef, PoolRef>(1, g, reqs, nullptr, nullptr, const_cast<void*>(staging),
                                         dst, dst_table, nullptr, skipped, stream);
 }
@@ -615,6 +769,9 @@ kvx_status kvx_gather_scatter(const kvx_layout* layout,
     KVX_TRY(check_table(src_table, reqs));
     KVX_TRY(check_pool(dst, g));
     KVX_TRY(check_table(dst_table, reqs));
+    if (validate_enabled())
+        KVX_TRY(validate_call(layout, reqs, src, src_table, dst, dst_table, nullptr, 0, false,
+                              stream));
     return run_paged<PoolRef, PoolRef>(2, g, reqs, src, src_table, nullptr, dst, dst_table,
                                        nullptr, skipped, stream);
 }
@@ -637,6 +794,9 @@ kvx_status kvx_gather_scatter_heads(const kvx_layout* layout,
     KVX_TRY(check_pool(dst, g));
     KVX_TRY(check_table(dst_table, reqs));
     KVX_TRY(check_heads(dst_heads, dst, g));
+    if (validate_enabled())
+        KVX_TRY(validate_call(layout, reqs, src, src_table, dst, dst_table, nullptr, 0, true,
+                              stream));
     return run_heads(g, reqs, src, src_table, src_heads, dst, dst_table, dst_heads, skipped,
                      stream);
 }
@@ -713,66 +873,6 @@ kvx_status kvx_check_tables(int32_t num_reqs, int64_t total_tokens, const int64_
     }
     return KVX_OK;
 }
-
-namespace {
-
-// One row a call touches: bytes [lo, hi) for batch token `tok`.
-struct Span {
-    uint64_t lo, hi;
-    int64_t tok;
-};
-
-// Slot of every batch token in one pool side, or -1 where the call skips the
-// token (page-table index or page id out of range, as the kernels decide).
-kvx_status side_slots(const kvx_reqs* reqs, const kvx_pool* p, const kvx_table* t,
-                      std::vector<int64_t>* slot) {
-    if (p->planes == nullptr) return KVX_E_NULL;
-    if (p->num_pages < 0 || p->page_size < 1) return KVX_E_SHAPE;
-    if (t->num_ids < 0) return KVX_E_SHAPE;
-    if (reqs->num_reqs > 0 && t->pg_off == nullptr) return KVX_E_NULL;
-    if (t->num_ids > 0 && t->page_ids == nullptr) return KVX_E_NULL;
-    slot->assign(static_cast<size_t>(reqs->total_tokens), -1);
-    for (int32_t r = 0; r < reqs->num_reqs; ++r) {
-        const int64_t off = reqs->tok_off[r], n = reqs->tok_off[r + 1] - off;
-        for (int64_t k = 0; k < n; ++k) {
-            const int64_t idx = t->pg_off[r] + k / p->page_size;
-            if (idx < 0 || idx >= t->num_ids) continue;
-            const int64_t page = t->page_ids[idx];
-            if (page < 0 || page >= p->num_pages) continue;
-            (*slot)[static_cast<size_t>(off + k)] = page * p->page_size + k % p->page_size;
-        }
-    }
-    return KVX_OK;
-}
-
-// Rows of the live tokens on one side (Q per token).
-void side_spans(const Geom& g, const kvx_reqs* reqs, const kvx_pool* p,
-                const std::vector<int64_t>& slot, const void* staging,
-                const std::vector<char>& live, std::vector<Span>* out) {
-    out->clear();
-    for (int32_t r = 0; r < reqs->num_reqs; ++r) {
-        const int64_t off = reqs->tok_off[r], n = reqs->tok_off[r + 1] - off;
-        for (int64_t k = 0; k < n; ++k) {
-            const int64_t tok = off + k;
-            if (!live[static_cast<size_t>(tok)]) continue;
-            for (int32_t q = 0; q < g.Q; ++q) {
-                uint64_t lo;
-                if (p != nullptr)
-                    lo = reinterpret_cast<uint64_t>(p->planes[q]) +
-                         static_cast<uint64_t>(slot[static_cast<size_t>(tok)]) *
-                             static_cast<uint64_t>(p->slot_stride);
-                else
-                    lo = reinterpret_cast<uint64_t>(staging) +
-                         static_cast<uint64_t>((off * g.Q + q * n + k) * g.R);
-                out->push_back(Span{lo, lo + static_cast<uint64_t>(g.R), tok});
-            }
-        }
-    }
-}
-
-bool by_lo(const Span& a, const Span& b) { return a.lo < b.lo || (a.lo == b.lo && a.tok < b.tok); }
-
-}  // namespace
 
 kvx_status kvx_check_disjoint(const kvx_layout* layout, const kvx_reqs* reqs,
                               const kvx_pool* src, const kvx_table* src_table,

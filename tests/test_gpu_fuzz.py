@@ -1,0 +1,40 @@
+"""Randomized GPU parity against the oracle: geometries with rows of 16 B to
+4 KiB in every element size, pages drawn from {1, 2, 16, 32} on each side,
+1 to 64 requests with empty ones, some page ids out of range, random-bit
+payloads (NaN patterns included), sentinel-filled destinations and guard
+bytes after the staging.  Every case is compared byte for byte over the whole
+destination, and the skip counters must agree."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from tests.test_gpu_parity import big_case, run_paged_case
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["fp8", "f16", "bf16", "f32"]
+
+
+def random_geometry(rng):
+    while True:
+        dt = DTYPES[int(rng.integers(len(DTYPES)))]
+        H = int(rng.choice([1, 2, 3, 4, 8, 12, 16]))
+        D = int(rng.choice([8, 16, 24, 64, 128]))
+        g = wl.Geometry(int(rng.integers(1, 4)), int(rng.integers(1, 3)), H, D, dt)
+        if g.row_bytes % 16 == 0 and 16 <= g.row_bytes <= 4096:
+            return g
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_fuzz_paged_ops(seed):
+    rng = np.random.default_rng(88000 + seed)
+    g = random_geometry(rng)
+    nreq = int(rng.integers(1, 65))
+    lens = rng.integers(0, 40 if nreq > 16 else 120, size=nreq)
+    lens[rng.random(nreq) < 0.15] = 0
+    if lens.sum() == 0:
+        lens[0] = 1
+    sp, dp = (int(rng.choice([1, 2, 16, 32])) for _ in range(2))
+    oor = float(rng.choice([0.0, 0.0, 0.05]))
+    case = big_case(f"fuzz{seed}", g, list(lens), sp, dp, 88000 + seed, oor)
+    run_paged_case(case, 88000 + seed)
