@@ -286,8 +286,10 @@ kvx_status kvx_check_disjoint(const kvx_layout* layout, const kvx_reqs* reqs,
                               const void* staging, int64_t staging_bytes,
                               int64_t* bad_token);
 
-/* Static string naming a status code (never NULL). */
-const char* kvx_status_str(kvx_status status);
+/* Static string naming a status code (never NULL; "unknown kvx_status" for a
+ * code outside kvx_status).  Takes a plain int32_t so that any code a caller
+ * holds, valid or not, is a well-defined argument. */
+const char* kvx_status_str(int32_t status);
 
 /* KVX_ABI_VERSION of the built library. */
 int32_t kvx_abi_version(void);

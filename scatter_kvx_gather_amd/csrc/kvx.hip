@@ -938,7 +938,7 @@ kvx_status kvx_check_disjoint(const kvx_layout* layout, const kvx_reqs* reqs,
     return KVX_OK;
 }
 
-const char* kvx_status_str(kvx_status status) {
+const char* kvx_status_str(int32_t status) {
     switch (status) {
         case KVX_OK: return "KVX_OK";
         case KVX_E_NULL: return "KVX_E_NULL: a required pointer is NULL";
