@@ -35,6 +35,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -55,11 +56,26 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha256() -> str:
+def code_of(text: str) -> str:
+    """C++ source with comments and whitespace removed: what the compiler
+    sees, so an edit to a comment does not count as a kernel change."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", "", text)
+
+
+def kernel_source_sha256(sources=None) -> str:
+    """SHA-256 over the code (comments and whitespace removed) of the kernel
+    sources; `sources` maps a path in KERNEL_SOURCES to its text (default:
+    read the files)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        if sources is not None:
+            text = sources[rel]
+        else:
+            with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+                text = f.read()
+        h.update(code_of(text).encode())
     return h.hexdigest()
 
 
@@ -286,6 +302,8 @@ def summarize_pmc(fetch_dir, write_dir, out_path):
         f.write(f"- algorithmic_bytes_per_launch: {algo}\n")
         f.write(f"- traffic_over_algorithmic: {(fetch_b + write_b) / algo:.4f}\n")
         f.write(f"- kernel_source_sha256: {kernel_source_sha256()}\n")
+        f.write("- hash_of: the code of " + ", ".join(KERNEL_SOURCES)
+                + " with comments and whitespace removed\n")
     print(open(out_path).read())
 
 

@@ -30,10 +30,11 @@ bool log_enabled() {
 }
 
 // Cap on workgroups per compute unit; beyond it the waves grid-stride over
-// the chunks.  0 (the default) means no cap: one wave per chunk.  Measured on
-// the 2048-token, 144 KiB/token request: no cap and caps of 2-6 are within
-// 1-3% of each other; 8 or more (more waves than fit at once) is 5-25%
-// slower.  KVX_BLOCKS_PER_CU overrides it.
+// the chunks (a persistent grid).  0 (the default) means no cap: one wave per
+// chunk.  Measured (same process, alternating) with the final chunk sizes: a
+// cap of 2, 4 or 6 workgroups per CU makes the five-op step 8-21% slower
+// (5895 GB/s uncapped vs 5425 / 5279 / 4633) and single ops up to 32%
+// slower.  KVX_BLOCKS_PER_CU sets a cap, for experiments.
 int blocks_per_cu() {
     static const int n = [] {
         const char* e = std::getenv("KVX_BLOCKS_PER_CU");
