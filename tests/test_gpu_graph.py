@@ -80,3 +80,58 @@ def test_graph_replays_match_oracle():
         assert_bytes_equal(flat.cpu().numpy(), exp_flat, f"replay {rep} extract")
         assert_bytes_equal(hf.cpu().numpy(), exp_hf, f"replay {rep} rebuild")
         assert skipped.cpu().tolist() == [s0, s1], rep
+
+
+def test_graph_replays_full_size_request():
+    """The 2048-token, 144 KiB/token request (the one-row-per-wave launches):
+    gather-scatter, gather, extract and rebuild captured once and replayed on
+    four disjoint requests; every replay's bytes equal the eager calls'."""
+    cs = [wl.config2(k) for k in range(4)]
+    g = cs[0].geom
+    Q, R, T = g.planes, g.row_bytes, 2048
+    from workloads import device as wdev
+    A = torch.empty((Q, 32768, R), dtype=torch.uint8, device=DEV)
+    wdev.fill_hash(A, cs[0].value_seed)
+    B0 = torch.empty_like(A)
+    wdev.fill_hash(B0, cs[0].sentinel_seed)
+    lay, reqs = layout_of(g), requests(cs[0])
+    PA = kvx.Pool(A, 32768)
+    H, Db = g.kv_heads, g.head_bytes
+
+    tabs = [(table(c.src), table(c.dst)) for c in cs]   # uploaded before any capture
+
+    def run(k, B, st, hf, fl):
+        PB = kvx.Pool(B, 32768)
+        kvx.gather_scatter(lay, PA, tabs[k][0], reqs, PB, tabs[k][1])
+        kvx.gather(lay, PA, tabs[k][0], reqs, st)
+        kvx.rebuild_permute(lay, st, T, hf, T)
+        kvx.extract_permute(lay, hf, T, T, fl)
+
+    def buffers():
+        return (B0.clone(), torch.empty(T * Q * R, dtype=torch.uint8, device=DEV),
+                torch.zeros((Q, H * T * Db), dtype=torch.uint8, device=DEV),
+                torch.zeros(T * Q * R, dtype=torch.uint8, device=DEV))
+
+    eager = []
+    for k in range(4):
+        bufs = buffers()
+        say(f"eager request {k}")
+        run(k, *bufs)
+        torch.cuda.synchronize()
+        eager.append(bufs)
+    # one graph per request (tables are captured by address), replayed twice
+    for k in range(4):
+        bufs = buffers()
+        stream = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        say(f"capture request {k}")
+        with torch.cuda.graph(graph, stream=stream):
+            run(k, *bufs)
+        for rep in range(2):
+            say(f"replay request {k} #{rep}")
+            graph.replay()
+            torch.cuda.synchronize()
+            for got, want in zip(bufs, eager[k]):
+                assert torch.equal(got, want), (k, rep)
+        del graph
