@@ -673,6 +673,105 @@ def concurrent_load(torch, kvx, wl, wdev, dev, reps=32):
     print(json.dumps(result), flush=True)
 
 
+def cu_split(torch, kvx, wl, wdev, dev, reps=32):
+    """The compute units split between the transfer and a full-intensity
+    decode-like reader: each on a stream with its own CU mask
+    (hipExtStreamCreateWithCUMask).  Mask bit i selects a CU on XCD i mod 8,
+    and a mask that leaves an XCD without CUs is refused ("out of memory":
+    workgroups are dealt to every XCD), so both sides take whole groups of 8
+    consecutive bits -- one CU on each XCD per group -- the transfer every
+    m-th group and the reader the rest.  The pair of streams is created
+    before any other stream and destroyed before the next split."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                 ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint32)]
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    words = (ncu + 31) // 32
+
+    def masked_stream(cus):
+        mask = (ctypes.c_uint32 * words)()
+        for c in cus:
+            mask[c // 32] |= 1 << (c % 32)
+        h = ctypes.c_void_p()
+        rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), words, mask)
+        if rc != 0:
+            raise RuntimeError(f"hipExtStreamCreateWithCUMask returned {rc}")
+        return h, torch.cuda.ExternalStream(h.value, device=dev)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def gbps(nbytes, e):
+        return nbytes / (e[0].elapsed_time(e[1]) * 1e6)
+
+    result = {"splits": []}
+    wk = rd_buf = sink = None
+    for m in (8, 4, 2):                      # transfer on 1/8, 1/4, 1/2 of the CUs
+        t_cus = [c for c in range(ncu) if (c // 8) % m == 0]
+        r_cus = [c for c in range(ncu) if (c // 8) % m != 0]
+        ht, ts = masked_stream(t_cus)
+        hr, rs = masked_stream(r_cus)
+        try:
+            if wk is None:                   # buffers filled on the first masked stream
+                wk = Workload(torch, kvx, wl, wdev, dev, ts)
+                rd_buf = torch.empty(16 * 2 ** 30, dtype=torch.uint8, device=dev)
+                wdev.fill_hash(rd_buf, 9, stream=ts)
+                sink = torch.zeros(2048, dtype=torch.int64, device=dev)
+                torch.cuda.synchronize()
+
+            def gs_on(st, n):
+                e0, e1 = ev(), ev()
+                e0.record(st)
+                for i in range(n):
+                    k = i % NREQ
+                    kvx.gather_scatter(wk.lay, wk.PA, wk.src_tabs[k], wk.reqs, wk.PB,
+                                       wk.dst_tabs[k], stream=st)
+                e1.record(st)
+                return e0, e1
+
+            def rd_on(st, n):
+                e0, e1 = ev(), ev()
+                e0.record(st)
+                for _ in range(n):
+                    wdev.read_stream(rd_buf, sink, blocks=2048, stream=st)
+                e1.record(st)
+                return e0, e1
+
+            gs_on(ts, 8)
+            torch.cuda.synchronize()
+            eg = gs_on(ts, reps)
+            torch.cuda.synchronize()
+            g_alone = gbps(wk.op_bytes * reps, eg)
+            er = rd_on(rs, 2)
+            torch.cuda.synchronize()
+            r_alone = gbps(rd_buf.numel() * 2, er)
+            # enough reader launches to outlast the transfer at half its rate
+            n_rd = int(wk.op_bytes * reps / (0.5 * g_alone) / (rd_buf.numel() / r_alone)) + 2
+            er = rd_on(rs, n_rd)
+            eg = gs_on(ts, reps)
+            torch.cuda.synchronize()
+            result["splits"].append({
+                "transfer_cus": len(t_cus), "reader_cus": len(r_cus),
+                "gather_scatter_alone_GBps": round(g_alone, 1),
+                "reader_alone_GBps": round(r_alone, 1),
+                "gather_scatter_loaded_GBps": round(gbps(wk.op_bytes * reps, eg), 1),
+                "reader_loaded_GBps": round(gbps(rd_buf.numel() * n_rd, er), 1),
+                "reader_outlasts_gather_scatter": bool(er[0].elapsed_time(er[1]) >=
+                                                       eg[0].elapsed_time(eg[1]))})
+            log(f"cu split {len(t_cus)}/{len(r_cus)}: {result['splits'][-1]}")
+        finally:
+            torch.cuda.synchronize()
+            hip.hipStreamDestroy(ht)
+            hip.hipStreamDestroy(hr)
+    result["note"] = ("transfer: gather-scatter of the 2048-token, 144 KiB/token request, 16 "
+                      "disjoint requests rotated; reader: 16 GiB per launch, nontemporal "
+                      "16-byte loads, 2048 workgroups of 256 threads; each on its own CU "
+                      "mask; GB/s counts bytes read + written")
+    print(json.dumps(result), flush=True)
+
+
 def comparators(torch, kvx, wl, wdev, dev):
     """The same 2048-token request moved by per-block runtime copies."""
     import ctypes
@@ -821,6 +920,8 @@ def main():
                     help="time every op on all five workloads (JSON line per op)")
     ap.add_argument("--concurrent", action="store_true",
                     help="gather-scatter while a decode-like HBM reader runs on another stream")
+    ap.add_argument("--cu-split", action="store_true",
+                    help="the transfer and a full-intensity reader on complementary CU masks")
     ap.add_argument("--comparators", action="store_true",
                     help="the same request moved by one runtime copy per block / per run")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -851,6 +952,9 @@ def main():
         return 2
     kvx.load_library()
     dev = torch.device("cuda:0")
+    if args.cu_split:                      # before any other stream takes a hardware queue
+        cu_split(torch, kvx, wl, wdev, dev)
+        return 0
     stream = torch.cuda.Stream(device=dev)
     if args.all_configs:
         all_configs(torch, kvx, wl, wdev, dev, stream, reps=5, cpu=not args.no_cpu_baseline)
