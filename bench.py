@@ -24,8 +24,14 @@ contiguous-copy ceiling of equal bytes, the roofline of the dominant kernel,
 and the CPU oracle timed on the host on a bounded sample of the same steps.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+  python bench.py --all-configs         (every op on every workload, beside a plain
+                                         copy of equal bytes and the oracle on a sample)
+  python bench.py --concurrent          (the transfer under a decode-like HBM reader)
+  python bench.py --cu-split            (the two on complementary CU-masked streams)
+  python bench.py --comparators         (per-block runtime copies, DMA copy of staging)
   python bench.py --pmc-pass            (short run for rocprofv3 --pmc)
-  python bench.py --summarize-pmc DIR   (traffic summary from two pmc runs)
+  python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --pmc-out OUT
+  python bench.py --summarize-trace TRACE_DIR OUT TITLE COMMAND
 """
 from __future__ import annotations
 
