@@ -129,6 +129,28 @@ def _nbytes(x) -> int:
     return x.numel() * x.element_size() if isinstance(x, torch.Tensor) else 0
 
 
+def _on_device(*args) -> None:
+    """Every torch tensor a data-movement call will hand to the kernels must
+    live on the GPU (a host pointer there would fault): pools' plane tensors,
+    tables, token offsets, staging, counters.  Raw integer pointers are the
+    caller's responsibility."""
+    for a in args:
+        if a is None or isinstance(a, int):
+            continue
+        if isinstance(a, Pool):
+            _on_device(*(a._keep if isinstance(a._keep, (list, tuple)) else [a._keep]))
+        elif isinstance(a, Table):
+            _on_device(a.pg_off, a.page_ids)
+        elif isinstance(a, Requests):
+            _on_device(a.tok_off)
+        elif isinstance(a, (list, tuple)):
+            _on_device(*a)
+        elif isinstance(a, torch.Tensor):
+            if not a.is_cuda:
+                raise ValueError("kvx data-movement calls take device tensors; got a "
+                                 f"{a.device} tensor of shape {tuple(a.shape)}")
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -238,6 +260,7 @@ class Heads:
 def gather(layout: Layout, src: Pool, src_table: Table, reqs: Requests, staging: torch.Tensor,
            skipped: Optional[torch.Tensor] = None, stream=None) -> None:
     """Pool -> contiguous staging [request][plane][token][H][D] (kvx_gather)."""
+    _on_device(src, src_table, reqs, staging, skipped)
     lib = load_library()
     _check(lib.kvx_gather(ctypes.byref(layout._c), ctypes.byref(src._c),
                           ctypes.byref(src_table._c), ctypes.byref(reqs._c), _ptr(staging),
@@ -247,6 +270,7 @@ def gather(layout: Layout, src: Pool, src_table: Table, reqs: Requests, staging:
 def scatter(layout: Layout, staging: torch.Tensor, reqs: Requests, dst: Pool, dst_table: Table,
             skipped: Optional[torch.Tensor] = None, stream=None) -> None:
     """Contiguous staging -> pool (kvx_scatter)."""
+    _on_device(staging, reqs, dst, dst_table, skipped)
     lib = load_library()
     _check(lib.kvx_scatter(ctypes.byref(layout._c), _ptr(staging), _nbytes(staging),
                            ctypes.byref(reqs._c), ctypes.byref(dst._c),
@@ -258,6 +282,7 @@ def gather_scatter(layout: Layout, src: Pool, src_table: Table, reqs: Requests, 
                    dst_table: Table, skipped: Optional[torch.Tensor] = None,
                    stream=None) -> None:
     """Pool -> pool, row by row, no staging (kvx_gather_scatter)."""
+    _on_device(src, src_table, reqs, dst, dst_table, skipped)
     lib = load_library()
     _check(lib.kvx_gather_scatter(ctypes.byref(layout._c), ctypes.byref(src._c),
                                   ctypes.byref(src_table._c), ctypes.byref(reqs._c),
@@ -271,6 +296,7 @@ def gather_scatter_heads(layout: Layout, src: Pool, src_table: Table, src_heads:
     """Pool -> pool, layout.kv_heads heads of every token row, from heads
     src_heads.head0.. to dst_heads.head0.. (kvx_gather_scatter_heads).  The
     pools' slot_stride is the bytes of one token row in that pool."""
+    _on_device(src, src_table, reqs, dst, dst_table, skipped)
     lib = load_library()
     _check(lib.kvx_gather_scatter_heads(ctypes.byref(layout._c), ctypes.byref(src._c),
                                         ctypes.byref(src_table._c), ctypes.byref(src_heads._c),
@@ -283,6 +309,7 @@ def gather_scatter_heads(layout: Layout, src: Pool, src_table: Table, src_heads:
 def extract_permute(layout: Layout, hf_planes: Union[torch.Tensor, Sequence], s_cap: int,
                     seq_len: int, out: torch.Tensor, stream=None) -> None:
     """[1, H, s_cap, D] per plane -> out [Q][seq_len][H][D] (kvx_extract_permute)."""
+    _on_device(hf_planes, out)
     lib = load_library()
     arr = _plane_array(hf_planes)
     _check(lib.kvx_extract_permute(ctypes.byref(layout._c),
@@ -294,6 +321,7 @@ def extract_permute(layout: Layout, hf_planes: Union[torch.Tensor, Sequence], s_
 def rebuild_permute(layout: Layout, flat: torch.Tensor, seq_len: int,
                     hf_planes: Union[torch.Tensor, Sequence], s_cap: int, stream=None) -> None:
     """flat [Q][seq_len][H][D] -> [1, H, s_cap, D] per plane (kvx_rebuild_permute)."""
+    _on_device(flat, hf_planes)
     lib = load_library()
     arr = _plane_array(hf_planes)
     _check(lib.kvx_rebuild_permute(ctypes.byref(layout._c), _ptr(flat), _nbytes(flat), seq_len,

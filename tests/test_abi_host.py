@@ -270,3 +270,28 @@ def test_header_is_plain_c():
                         "-fsyntax-only", "-D__HIP_PLATFORM_AMD__", "-I",
                         os.path.join(rocm, "include"), HEADER], capture_output=True, text=True)
     assert p.returncode == 0, p.stderr
+
+
+def test_binding_refuses_host_tensors():
+    """A host tensor never reaches a kernel: the binding refuses it before the
+    library is called (on the GPU it would be dereferenced as a device
+    address)."""
+    import torch
+    lay = kvx.Layout(1, 2, 1, 8, "bf16")
+    pool = kvx.Pool(torch.zeros((2, 4, 16), dtype=torch.uint8), 4)
+    tab = kvx.Table(torch.zeros(2, dtype=torch.int64), torch.zeros(2, dtype=torch.int32))
+    reqs = kvx.Requests(torch.tensor([0, 2], dtype=torch.int64), 2)
+    st = torch.zeros(64, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="device tensors"):
+        kvx.gather(lay, pool, tab, reqs, st)
+    with pytest.raises(ValueError, match="device tensors"):
+        kvx.scatter(lay, st, reqs, pool, tab)
+    with pytest.raises(ValueError, match="device tensors"):
+        kvx.gather_scatter(lay, pool, tab, reqs, pool, tab)
+    with pytest.raises(ValueError, match="device tensors"):
+        kvx.gather_scatter_heads(lay, pool, tab, kvx.Heads(1, 0), reqs, pool, tab,
+                                 kvx.Heads(1, 0))
+    with pytest.raises(ValueError, match="device tensors"):
+        kvx.extract_permute(lay, torch.zeros((2, 16), dtype=torch.uint8), 1, 1, st)
+    with pytest.raises(ValueError, match="device tensors"):
+        kvx.rebuild_permute(lay, st, 1, [torch.zeros(16, dtype=torch.uint8)] * 2, 1)
