@@ -75,7 +75,13 @@
  * pairwise distinct, and source and destination bytes do not overlap.  Under
  * them the result is unique and equals the row-by-row definition above.
  * kvx_check_tables and kvx_check_disjoint (below) check them on host copies
- * of the tables, as a debug aid.
+ * of the tables, as a debug aid.  With KVX_VALIDATE=1 in the environment
+ * (read once per process) every data-movement call runs those checks itself
+ * before enqueueing: it synchronizes its stream, copies its tables to the
+ * host, and on a violation returns KVX_E_DUPLICATE or KVX_E_OVERLAP with
+ * nothing enqueued (out-of-range ids stay legal).  Debug only: it cannot run
+ * on a stream under graph capture (KVX_E_HIP).  KVX_LOG=1 prints each
+ * launch decision to stderr.
  */
 #ifndef KVX_H
 #define KVX_H
