@@ -29,6 +29,7 @@ and the CPU oracle timed on the host on a bounded sample of the same steps.
   python bench.py --concurrent          (the transfer under a decode-like HBM reader)
   python bench.py --cu-split            (the two on complementary CU-masked streams)
   python bench.py --comparators         (per-block runtime copies, DMA copy of staging)
+  python bench.py --sizes               (one request of 16 .. 8192 tokens: latency to bandwidth)
   python bench.py --pmc-pass            (short run for rocprofv3 --pmc)
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --pmc-out OUT
   python bench.py --summarize-trace TRACE_DIR OUT TITLE COMMAND
@@ -778,6 +779,66 @@ def cu_split(torch, kvx, wl, wdev, dev, reps=32):
     print(json.dumps(result), flush=True)
 
 
+def request_sizes(torch, kvx, wl, wdev, dev, stream):
+    """Gather-scatter and gather of one request of n tokens at 144 KiB/token
+    (page-1 pools of 65536 slots, slots from seeded permutations, 8 disjoint
+    requests rotated), n from 16 to 8192, graph-timed, beside a plain
+    contiguous copy of the same bytes: where per-launch latency gives way to
+    bandwidth."""
+    import numpy as np
+    g = wl.KV144K
+    Q, R, NS = g.planes, g.row_bytes, 65536
+    rng = np.random.default_rng(1010)
+    pa, pb = rng.permutation(NS), rng.permutation(NS)
+    A = torch.empty((Q, NS, R), dtype=torch.uint8, device=dev)
+    B = torch.empty_like(A)
+    wdev.fill_hash(A, 1, stream=stream)
+    wdev.fill_hash(B, 2, stream=stream)
+    lay = kvx.Layout(g.num_layers, g.num_kv, g.kv_heads, g.head_dim, g.dtype)
+    PA, PB = kvx.Pool(A, NS), kvx.Pool(B, NS)
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def timed(fn, n):
+        fn(0)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(n):
+                fn(i + 1)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):        # replay runs on the current stream
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for n in (16, 64, 256, 1024, 2048, 4096, 8192):
+        reqs = kvx.Requests(d(np.array([0, n], np.int64)), n)
+        pg = d(np.array([0, n], np.int64))
+        tabs = [(kvx.Table(pg, d(pa[k * n:(k + 1) * n].astype(np.int32))),
+                 kvx.Table(pg, d(pb[k * n:(k + 1) * n].astype(np.int32)))) for k in range(8)]
+        st = torch.empty(n * Q * R, dtype=torch.uint8, device=dev)
+        cp = torch.empty_like(st)
+        reps = 64 if n <= 1024 else 16
+        nb = 2 * n * Q * R
+        line = {"tokens": n, "bytes_rw": nb}
+        for op, fn in (("gather_scatter", lambda i: kvx.gather_scatter(
+                           lay, PA, tabs[i % 8][0], reqs, PB, tabs[i % 8][1], stream=stream)),
+                       ("gather", lambda i: kvx.gather(lay, PA, tabs[i % 8][0], reqs, st,
+                                                       stream=stream)),
+                       ("plain_copy", lambda i: wdev.copy_bytes(cp, st, st.numel(),
+                                                                stream=stream))):
+            ms = timed(fn, reps)
+            line[op] = {"us": round(ms * 1e3, 2), "GBps": round(nb / (ms * 1e6), 1)}
+        print(json.dumps(line), flush=True)
+        del st, cp
+
+
 def comparators(torch, kvx, wl, wdev, dev):
     """The same 2048-token request moved by per-block runtime copies."""
     import ctypes
@@ -928,6 +989,8 @@ def main():
                     help="gather-scatter while a decode-like HBM reader runs on another stream")
     ap.add_argument("--cu-split", action="store_true",
                     help="the transfer and a full-intensity reader on complementary CU masks")
+    ap.add_argument("--sizes", action="store_true",
+                    help="gather-scatter and gather of one request of 16 .. 8192 tokens")
     ap.add_argument("--comparators", action="store_true",
                     help="the same request moved by one runtime copy per block / per run")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -967,6 +1030,9 @@ def main():
         return 0
     if args.concurrent:
         concurrent_load(torch, kvx, wl, wdev, dev)
+        return 0
+    if args.sizes:
+        request_sizes(torch, kvx, wl, wdev, dev, stream)
         return 0
     if args.comparators:
         comparators(torch, kvx, wl, wdev, dev)
