@@ -38,3 +38,41 @@ def test_fuzz_paged_ops(seed):
     oor = float(rng.choice([0.0, 0.0, 0.05]))
     case = big_case(f"fuzz{seed}", g, list(lens), sp, dp, 88000 + seed, oor)
     run_paged_case(case, 88000 + seed)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_fuzz_head_slices(seed):
+    from tests.test_gpu_heads import run_heads
+    rng = np.random.default_rng(91000 + seed)
+    D = int(rng.choice([8, 16, 64, 128, 256]))
+    sH, dH = int(rng.integers(1, 13)), int(rng.integers(1, 13))
+    nh = int(rng.integers(1, min(sH, dH) + 1))
+    sh0, dh0 = int(rng.integers(0, sH - nh + 1)), int(rng.integers(0, dH - nh + 1))
+    shnd, dhnd = int(rng.integers(2)), int(rng.integers(2))
+    page = [int(rng.choice([1, 2, 4, 16, 32, 64])) for _ in range(2)]
+    if shnd and dhnd and rng.random() < 0.5:
+        page[1] = page[0]                       # the page-run kernel's case
+    case = wl.random_case(91000 + seed, geom=wl.Geometry(int(rng.integers(1, 3)), 2, nh, D),
+                          max_reqs=int(rng.integers(1, 9)), max_len=int(rng.integers(1, 150)),
+                          src_page=page[0], dst_page=page[1],
+                          oor_frac=float(rng.choice([0.0, 0.1])))
+    run_heads(case, sH, dH, nh, sh0, dh0, D, shnd, dhnd, 91000 + seed)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_fuzz_permutes(seed):
+    from tests.test_gpu_parity import test_permutes
+    rng = np.random.default_rng(92000 + seed)
+    dt = DTYPES[int(rng.integers(len(DTYPES)))]
+    eb = wl.ELEM_BYTES[dt]
+    while True:
+        D = int(rng.choice([8, 16, 32, 64, 128, 256]))
+        if (D * eb) % 16 == 0:
+            break
+    H = int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16]))
+    seq = int(rng.integers(0, 300))
+    s_cap = seq + int(rng.choice([0, 0, 1, 37]))
+    Q = int(rng.choice([1, 2, 3, 7, 130]))
+    if Q * H * max(s_cap, 1) * D * eb > (64 << 20):
+        seq = s_cap = 8
+    test_permutes((Q, H, D, dt, s_cap, seq))
