@@ -284,7 +284,8 @@ def summarize_pmc(fetch_dir, write_dir, out_path):
     write_b = w_kib * w_scale * 1024
     algo = 2 * 2048 * 72 * 2048
     with open(out_path, "w") as f:
-        f.write("# HBM traffic of the gather-scatter kernel, 288 MiB request (kv144k, page 1)\n\n")
+        f.write("# HBM traffic per launch, 288 MiB request (kv144k, page 1): the gather-scatter "
+                "kernel, then every kernel of the step\n\n")
         f.write("Two `rocprofv3 --pmc` runs of `python bench.py --pmc-pass` (one counter each);\n")
         f.write("median per dispatch, scaled by the plain copy kernel `k_copy16` of\n")
         f.write(f"{COPY_CALIB_BYTES} bytes run in the same process.\n\n")
@@ -311,6 +312,17 @@ def summarize_pmc(fetch_dir, write_dir, out_path):
         f.write(f"- kernel_source_sha256: {kernel_source_sha256()}\n")
         f.write("- hash_of: the code of " + ", ".join(KERNEL_SOURCES)
                 + " with comments and whitespace removed\n")
+        # every kernel of the step, from the same two runs
+        f.write("\nEvery kernel of the five-op step (same runs and scaling; each moves "
+                f"{algo} algorithmic bytes per launch):\n\n")
+        f.write("| kernel | fetch bytes | write bytes | traffic / algorithmic |\n")
+        f.write("|---|---:|---:|---:|\n")
+        for name in sorted(k for k in fetch if "kvx::k_" in k and k in write):
+            fv, wv = fetch[name], write[name]
+            fb = sorted(fv)[len(fv) // 2] * f_scale * 1024
+            wb = sorted(wv)[len(wv) // 2] * w_scale * 1024
+            short = name.split("(")[0].replace("void ", "").replace("kvx::", "")
+            f.write(f"| `{short}` | {int(fb)} | {int(wb)} | {(fb + wb) / algo:.4f} |\n")
     print(open(out_path).read())
 
 
