@@ -173,8 +173,13 @@ class Workload:
 
 # -------------------------------------------------------------- cpu side --
 
-def cpu_baseline(wk, budget_s):
-    """Time the oracle on host copies of the same pools and requests."""
+def cpu_baseline(wk, budget_s, parity_step=None):
+    """Time the oracle on host copies of the same pools and requests.  With
+    parity_step j (the last step run on the GPU before this call), first
+    check that step's results bitwise against the oracle: gather-scatter and
+    scatter rows of pool B equal the source rows of pool A, the gather's
+    staging equals the oracle's gather, and extract(rebuild(staging)) equals
+    the staging."""
     import numpy as np
 
     import oracle
@@ -191,6 +196,30 @@ def cpu_baseline(wk, budget_s):
     B_planes = [B_h[q].reshape(-1) for q in range(Q)]
     HF_planes = [HF[q] for q in range(Q)]
     c0 = wk.cases[0]
+    ncores = min(16, os.cpu_count() or 1)
+    parity = None
+    if parity_step is not None:
+        j = parity_step
+        a, b = wk.cases[(2 * j) % NREQ], wk.cases[(2 * j + 1) % NREQ]
+        S1_dev, S2_dev = wk.S1.cpu().numpy(), wk.S2.cpu().numpy()
+
+        def rows(planes, pg_off, ids):
+            out = np.zeros(T * Q * R, np.uint8)
+            oracle.gather(planes, R, 1, S, R, c0.tok_off, pg_off, ids, out, ncores)
+            return out
+        want_gs = rows(A_planes, a.src.pg_off, a.src.ids)
+        want_g = rows(A_planes, b.src.pg_off, b.src.ids)
+        parity = {
+            "step": j,
+            "gather_scatter_rows_equal_source_rows":
+                bool(np.array_equal(rows(B_planes, a.dst.pg_off, a.dst.ids), want_gs)),
+            "gather_equals_oracle": bool(np.array_equal(S1_dev, want_g)),
+            "extract_of_rebuild_equals_staging": bool(np.array_equal(S2_dev, S1_dev)),
+            "scatter_rows_equal_source_rows":
+                bool(np.array_equal(rows(B_planes, b.dst.pg_off, b.dst.ids), want_g)),
+        }
+        log(f"parity of step {j}: {parity}")
+        del S1_dev, S2_dev, want_gs, want_g
 
     def step(i, nt):
         a, b = wk.cases[(2 * i) % NREQ], wk.cases[(2 * i + 1) % NREQ]
@@ -202,7 +231,6 @@ def cpu_baseline(wk, budget_s):
         oracle.scatter(S2, R, c0.tok_off, b.dst.pg_off, b.dst.ids, B_planes, R, 1, S, nt)
 
     out = {}
-    ncores = min(16, os.cpu_count() or 1)
     for nt in sorted({1, ncores}):
         step(0, nt)                                # pre-fault staging and HF pages
         runs = []
@@ -219,7 +247,7 @@ def cpu_baseline(wk, budget_s):
         runs.sort(key=lambda r: r[0] / r[1])
         out[nt] = runs[len(runs) // 2]
     del A_h, B_h
-    return out, ncores
+    return out, ncores, parity
 
 
 def host_cpu():
@@ -1217,7 +1245,12 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        res, ncores = cpu_baseline(wk, args.cpu_seconds)
+        # one more step, then its results are checked against the oracle
+        j = W + K + 1000
+        wk.step(j, stream)
+        torch.cuda.synchronize()
+        res, ncores, parity = cpu_baseline(wk, args.cpu_seconds, parity_step=j)
+        result["parity"] = parity
         steps_n, el_n = res[ncores]
         steps_1, el_1 = res[1]
         model, sockets = host_cpu()
