@@ -1,5 +1,6 @@
-/* The C ABI used from plain C: no Python, no torch.  Builds two small paged
- * pools in device memory, runs kvx_gather_scatter and kvx_gather on a HIP
+/* The C ABI used from plain C: no Python, no torch.  Builds small paged
+ * pools in device memory, runs every data-movement call -- gather-scatter,
+ * gather, scatter, the head-sliced copy, extract and rebuild -- on a HIP
  * stream, and compares every destination byte with the CPU oracle run on
  * host copies of the same bytes (the oracle is linked as test
  * infrastructure).  Also checks that a bad argument returns its status and
@@ -18,6 +19,23 @@ int64_t oracle_gather(int32_t Q, int64_t R, uint8_t* const* src_planes, int64_t 
                       int32_t src_page_size, int64_t src_num_pages, int32_t num_reqs,
                       const int64_t* tok_off, const int64_t* src_pg_off, const int32_t* src_ids,
                       uint8_t* staging, int nthreads);
+int64_t oracle_scatter(int32_t Q, int64_t R, const uint8_t* staging, int32_t num_reqs,
+                       const int64_t* tok_off, const int64_t* dst_pg_off, const int32_t* dst_ids,
+                       uint8_t* const* dst_planes, int64_t dst_stride, int32_t dst_page_size,
+                       int64_t dst_num_pages, int nthreads);
+int64_t oracle_gather_scatter_heads(int32_t Q, int32_t nh, int64_t Db, uint8_t* const* src_planes,
+                                    int64_t src_stride, int32_t src_page_size,
+                                    int64_t src_num_pages, const int64_t* src_pg_off,
+                                    const int32_t* src_ids, int32_t src_H, int32_t src_h0,
+                                    int32_t src_hnd, int32_t num_reqs, const int64_t* tok_off,
+                                    uint8_t* const* dst_planes, int64_t dst_stride,
+                                    int32_t dst_page_size, int64_t dst_num_pages,
+                                    const int64_t* dst_pg_off, const int32_t* dst_ids,
+                                    int32_t dst_H, int32_t dst_h0, int32_t dst_hnd, int nthreads);
+int64_t oracle_extract_permute(int32_t Q, int32_t H, int64_t Db, uint8_t* const* hf_planes,
+                               int64_t s_cap, int64_t seq, uint8_t* out, int nthreads);
+int64_t oracle_rebuild_permute(int32_t Q, int32_t H, int64_t Db, const uint8_t* in, int64_t seq,
+                               uint8_t* const* hf_planes, int64_t s_cap, int nthreads);
 int64_t oracle_gather_scatter(int32_t Q, int64_t R, uint8_t* const* src_planes,
                               int64_t src_stride, int32_t src_page_size, int64_t src_num_pages,
                               const int64_t* src_pg_off, const int32_t* src_ids, int32_t num_reqs,
@@ -155,11 +173,104 @@ int main(void) {
     if (memcmp(got_st, exp_st, stage_bytes) != 0) { fprintf(stderr, "gather differs\n"); return 8; }
     if ((int64_t)skipped != s1 + s2 || skipped != 0) { fprintf(stderr, "skip count %llu\n", skipped); return 9; }
 
+    /* scatter the gathered staging into a third pool (destination layout) */
+    {
+        uint8_t* e_d;
+        uint8_t* got = malloc(Q * dplane);
+        uint8_t* exp = malloc(Q * dplane);
+        uint8_t* eplanes_h[Q];
+        void* eplanes[Q];
+        if (!got || !exp) return 4;
+        CHECK_HIP(hipMalloc((void**)&e_d, Q * dplane));
+        CHECK_HIP(hipMemcpy(e_d, dst_h, Q * dplane, hipMemcpyHostToDevice));
+        for (int q = 0; q < Q; ++q) { eplanes[q] = e_d + q * dplane; eplanes_h[q] = exp + q * dplane; }
+        const kvx_pool ep = {eplanes, DST_PAGES, DST_PAGE, R};
+        CHECK_KVX(kvx_scatter(&lay, st_d, (int64_t)stage_bytes, &reqs, &ep, &dt, NULL, stream));
+        CHECK_HIP(hipStreamSynchronize(stream));
+        CHECK_HIP(hipMemcpy(got, e_d, Q * dplane, hipMemcpyDeviceToHost));
+        memcpy(exp, dst_h, Q * dplane);
+        oracle_scatter(Q, R, got_st, NREQ, tok_off, dpg, dperm, eplanes_h, R, DST_PAGE, DST_PAGES, 1);
+        if (memcmp(got, exp, Q * dplane) != 0) { fprintf(stderr, "scatter differs\n"); return 10; }
+        hipFree(e_d); free(got); free(exp);
+    }
+
+    /* head-sliced copy: heads 1..2 of the 4-head source rows, read as HND
+       pages of SRC_PAGE tokens, into 2-head NHD rows of a new pool */
+    {
+        enum { NH = 2, DB = D * 2 };
+        const size_t hplane = (size_t)DST_PAGES * DST_PAGE * NH * DB;
+        uint8_t* h_d;
+        uint8_t* init = malloc(Q * hplane);
+        uint8_t* got = malloc(Q * hplane);
+        uint8_t* exp = malloc(Q * hplane);
+        uint8_t* hplanes_h[Q];
+        void* hplanes[Q];
+        if (!init || !got || !exp) return 4;
+        for (size_t i = 0; i < Q * hplane; ++i) init[i] = (uint8_t)next_u32();
+        CHECK_HIP(hipMalloc((void**)&h_d, Q * hplane));
+        CHECK_HIP(hipMemcpy(h_d, init, Q * hplane, hipMemcpyHostToDevice));
+        for (int q = 0; q < Q; ++q) { hplanes[q] = h_d + q * hplane; hplanes_h[q] = exp + q * hplane; }
+        const kvx_layout hl = {L, KV, NH, D, KVX_BF16};
+        const kvx_pool hp = {hplanes, DST_PAGES, DST_PAGE, NH * DB};
+        const kvx_heads sh = {H, 1, KVX_HND}, dh = {NH, 0, KVX_NHD};
+        CHECK_KVX(kvx_gather_scatter_heads(&hl, &sp, &st, &sh, &reqs, &hp, &dt, &dh, NULL, stream));
+        CHECK_HIP(hipStreamSynchronize(stream));
+        CHECK_HIP(hipMemcpy(got, h_d, Q * hplane, hipMemcpyDeviceToHost));
+        memcpy(exp, init, Q * hplane);
+        oracle_gather_scatter_heads(Q, NH, DB, splanes_h, R, SRC_PAGE, SRC_PAGES, spg, sperm, H, 1, 1,
+                                    NREQ, tok_off, hplanes_h, NH * DB, DST_PAGE, DST_PAGES, dpg,
+                                    dperm, NH, 0, 0, 1);
+        if (memcmp(got, exp, Q * hplane) != 0) { fprintf(stderr, "heads differ\n"); return 11; }
+        hipFree(h_d); free(init); free(got); free(exp);
+    }
+
+    /* extract [1][H][S_CAP][D] -> [Q][SEQ][H][D], then rebuild into fresh HF planes */
+    {
+        enum { S_CAP = 45, SEQ = 33, DB = D * 2 };
+        const size_t hfp = (size_t)H * S_CAP * DB, flat = (size_t)Q * SEQ * H * DB;
+        uint8_t* hf_h = malloc(Q * hfp);
+        uint8_t* hf2_h = malloc(Q * hfp);
+        uint8_t* exp_flat = calloc(flat, 1);
+        uint8_t* got_flat = malloc(flat);
+        uint8_t* exp_hf2 = malloc(Q * hfp);
+        uint8_t* got_hf2 = malloc(Q * hfp);
+        if (!hf_h || !hf2_h || !exp_flat || !got_flat || !exp_hf2 || !got_hf2) return 4;
+        for (size_t i = 0; i < Q * hfp; ++i) { hf_h[i] = (uint8_t)next_u32(); hf2_h[i] = (uint8_t)next_u32(); }
+        uint8_t *hf_d, *hf2_d, *flat_d;
+        CHECK_HIP(hipMalloc((void**)&hf_d, Q * hfp));
+        CHECK_HIP(hipMalloc((void**)&hf2_d, Q * hfp));
+        CHECK_HIP(hipMalloc((void**)&flat_d, flat));
+        CHECK_HIP(hipMemcpy(hf_d, hf_h, Q * hfp, hipMemcpyHostToDevice));
+        CHECK_HIP(hipMemcpy(hf2_d, hf2_h, Q * hfp, hipMemcpyHostToDevice));
+        void* hfs[Q];
+        void* hf2s[Q];
+        uint8_t* hfs_h[Q];
+        uint8_t* hf2s_h[Q];
+        for (int q = 0; q < Q; ++q) {
+            hfs[q] = hf_d + q * hfp; hf2s[q] = hf2_d + q * hfp;
+            hfs_h[q] = hf_h + q * hfp; hf2s_h[q] = exp_hf2 + q * hfp;
+        }
+        CHECK_KVX(kvx_extract_permute(&lay, (const void* const*)hfs, S_CAP, SEQ, flat_d,
+                                      (int64_t)flat, stream));
+        CHECK_KVX(kvx_rebuild_permute(&lay, flat_d, (int64_t)flat, SEQ, hf2s, S_CAP, stream));
+        CHECK_HIP(hipStreamSynchronize(stream));
+        CHECK_HIP(hipMemcpy(got_flat, flat_d, flat, hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(got_hf2, hf2_d, Q * hfp, hipMemcpyDeviceToHost));
+        oracle_extract_permute(Q, H, DB, hfs_h, S_CAP, SEQ, exp_flat, 1);
+        memcpy(exp_hf2, hf2_h, Q * hfp);
+        oracle_rebuild_permute(Q, H, DB, exp_flat, SEQ, hf2s_h, S_CAP, 1);
+        if (memcmp(got_flat, exp_flat, flat) != 0) { fprintf(stderr, "extract differs\n"); return 12; }
+        if (memcmp(got_hf2, exp_hf2, Q * hfp) != 0) { fprintf(stderr, "rebuild differs\n"); return 13; }
+        hipFree(hf_d); hipFree(hf2_d); hipFree(flat_d);
+        free(hf_h); free(hf2_h); free(exp_flat); free(got_flat); free(exp_hf2); free(got_hf2);
+    }
+
     hipStreamDestroy(stream);
     hipFree(src_d); hipFree(dst_d); hipFree(st_d); hipFree(tok_d); hipFree(spg_d); hipFree(dpg_d);
     hipFree(sid_d); hipFree(did_d); hipFree(skipped_d);
     free(src_h); free(dst_h); free(exp_dst); free(got_dst); free(exp_st); free(got_st);
-    printf("abi_smoke ok: %lld tokens, %d planes, rows of %d bytes, pages %d -> %d\n",
+    printf("abi_smoke ok: %lld tokens, %d planes, rows of %d bytes, pages %d -> %d; "
+           "gather_scatter, gather, scatter, heads, extract, rebuild\n",
            (long long)T, Q, R, SRC_PAGE, DST_PAGE);
     return 0;
 }
