@@ -42,6 +42,14 @@ MUTANTS = {
                                 "(page * s->page_size + row) * s->stride"),
     "dst_slice_uses_src_h0": ("head_offset(&j->dst, j->Db, r, t, j->dst.h0 + k)",
                               "head_offset(&j->dst, j->Db, r, t, j->src.h0 + k)"),
+    "hnd_head_scaled_by_stride": ("(h * s->page_size + row) * Db",
+                                  "(h * s->page_size + row) * s->stride"),
+    "hnd_page_base_missing_page_size": ("return page * s->page_size * s->stride + (h",
+                                        "return page * s->stride + (h"),
+    "heads_skip_counted_per_head": ("                ++skipped;\n                continue;\n            }\n            for (int32_t k = 0; k < j->nh; ++k)",
+                                    "                skipped += j->nh;\n                continue;\n            }\n            for (int32_t k = 0; k < j->nh; ++k)"),
+    "heads_last_head_dropped": ("for (int32_t k = 0; k < j->nh; ++k)",
+                                "for (int32_t k = 0; k + 1 < j->nh; ++k)"),
 }
 
 DRIVER = r"""
