@@ -1182,9 +1182,12 @@ def main():
     # 8 KiB chunks (32 waves per CU), otherwise 4 rows per 8 KiB chunk
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     u = 1 if wk.op_bytes // 2 > cus * 32 * 8192 else 4
-    kernel_of = {"gather_scatter": f"k_paged<PoolRef, PoolRef, 2, {u}>",
-                 "gather": f"k_paged<PoolRef, StageRef, 2, {u}>",
-                 "scatter": f"k_paged<StageRef, PoolRef, 2, {u}>",
+    # batches of more than 64 requests take the instances with the 64-way
+    # request search
+    m = "true" if wk.reqs.num_reqs > 64 else "false"
+    kernel_of = {"gather_scatter": f"k_paged<PoolRef, PoolRef, 2, {u}, {m}>",
+                 "gather": f"k_paged<PoolRef, StageRef, 2, {u}, {m}>",
+                 "scatter": f"k_paged<StageRef, PoolRef, 2, {u}, {m}>",
                  "rebuild": f"k_permute_rows<true, 2, {u}>",
                  "extract": f"k_permute_rows<false, 2, {u}>"}
     achieved = wk.op_bytes / (dom_ms * 1e-3) / 1e9

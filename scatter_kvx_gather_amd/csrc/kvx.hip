@@ -281,25 +281,39 @@ kvx_status launch(const void* fn, uint32_t grid, Args& a, hipStream_t stream) {
     return e == hipSuccess ? KVX_OK : KVX_E_HIP;
 }
 
-template <class Src, class Dst>
-const void* paged_kernel(int vpl, uint32_t U) {
+template <class Src, class Dst, bool MANY>
+const void* paged_kernel_of(int vpl, uint32_t U) {
     const bool one = U == 1;
     switch (vpl) {
-        case 1: return one ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, 1>)
-                           : reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, wide_rows<1>()>);
-        case 2: return one ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 2, 1>)
-                           : reinterpret_cast<const void*>(&k_paged<Src, Dst, 2, wide_rows<2>()>);
-        case 4: return one ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 4, 1>)
-                           : reinterpret_cast<const void*>(&k_paged<Src, Dst, 4, wide_rows<4>()>);
-        case 8: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 8, wide_rows<8>()>);
-        case 16: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 16, wide_rows<16>()>);
-        case -1: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -1, wide_rows<1>()>);
-        case -2: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -2, wide_rows<2>()>);
-        case -4: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -4, wide_rows<4>()>);
-        case -8: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -8, wide_rows<8>()>);
-        case -16: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -16, wide_rows<16>()>);
-        default: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 0, 0>);
+        case 1: return one ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, 1, MANY>)
+                           : reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, wide_rows<1>(), MANY>);
+        case 2: return one ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 2, 1, MANY>)
+                           : reinterpret_cast<const void*>(&k_paged<Src, Dst, 2, wide_rows<2>(), MANY>);
+        case 4: return one ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 4, 1, MANY>)
+                           : reinterpret_cast<const void*>(&k_paged<Src, Dst, 4, wide_rows<4>(), MANY>);
+        case 8: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 8, wide_rows<8>(), MANY>);
+        case 16: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 16, wide_rows<16>(), MANY>);
+        case -1: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -1, wide_rows<1>(), MANY>);
+        case -2: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -2, wide_rows<2>(), MANY>);
+        case -4: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -4, wide_rows<4>(), MANY>);
+        case -8: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -8, wide_rows<8>(), MANY>);
+        case -16: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -16, wide_rows<16>(), MANY>);
+        default: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 0, 0, MANY>);
     }
+}
+
+// Batches of more than 64 requests take the kernels with the 64-way request
+// search; smaller ones the kernels whose lookup window holds the whole batch.
+template <class Src, class Dst>
+const void* paged_kernel(int vpl, uint32_t U, int32_t num_reqs) {
+    return num_reqs > kWave ? paged_kernel_of<Src, Dst, true>(vpl, U)
+                            : paged_kernel_of<Src, Dst, false>(vpl, U);
+}
+
+template <int KT>
+const void* heads_hnd_kernel(bool many) {
+    return many ? reinterpret_cast<const void*>(&k_heads_hnd<KT, true>)
+                : reinterpret_cast<const void*>(&k_heads_hnd<KT, false>);
 }
 
 // Token-row permute kernel for rows of vpl KiB; nullptr for the head-row
@@ -368,7 +382,7 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
                          static_cast<long long>(reqs->total_tokens), reqs->num_reqs,
                          sh.vpl > 0 ? "wide" : (sh.vpl < 0 ? "row-loop" : "flat"), sh.U,
                          a.c.nchunks, grid, a.c.remap);
-        s = launch(paged_kernel<Src, Dst>(sh.vpl, sh.U), grid, a, stream);
+        s = launch(paged_kernel<Src, Dst>(sh.vpl, sh.U, a.c.num_reqs), grid, a, stream);
         if (s != KVX_OK) return s;
     }
     return KVX_OK;
@@ -529,12 +543,14 @@ kvx_status run_heads(const Geom& g, const kvx_reqs* reqs, const kvx_pool* src,
                          static_cast<long long>(reqs->total_tokens), a.hs.H, a.hs.h0,
                          a.hs.hnd ? "HND" : "NHD", a.hd.H, a.hd.h0, a.hd.hnd ? "HND" : "NHD",
                          Ut, nhc, kt, a.c.nchunks, grid);
-        const void* fn = reinterpret_cast<const void*>(&k_heads);
+        const bool many = a.c.num_reqs > kWave;
+        const void* fn = many ? reinterpret_cast<const void*>(&k_heads<true>)
+                              : reinterpret_cast<const void*>(&k_heads<false>);
         switch (kt) {
-            case 1: fn = reinterpret_cast<const void*>(&k_heads_hnd<1>); break;
-            case 2: fn = reinterpret_cast<const void*>(&k_heads_hnd<2>); break;
-            case 4: fn = reinterpret_cast<const void*>(&k_heads_hnd<4>); break;
-            case 8: fn = reinterpret_cast<const void*>(&k_heads_hnd<8>); break;
+            case 1: fn = heads_hnd_kernel<1>(many); break;
+            case 2: fn = heads_hnd_kernel<2>(many); break;
+            case 4: fn = heads_hnd_kernel<4>(many); break;
+            case 8: fn = heads_hnd_kernel<8>(many); break;
             default: break;
         }
         s = launch(fn, grid, a, stream);

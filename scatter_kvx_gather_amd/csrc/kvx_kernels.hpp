@@ -188,17 +188,6 @@ __device__ __forceinline__ PagedChunk paged_chunk(const Common& c, uint32_t chun
     return k;
 }
 
-// Largest r < num_reqs with tok_off[r] <= tok (tok < T): request of a token.
-__device__ __forceinline__ int32_t request_of(const int64_t* __restrict__ tok_off,
-                                              int32_t num_reqs, int64_t tok) {
-    int32_t lo = 0, hi = num_reqs - 1;
-    while (lo < hi) {
-        int32_t mid = (lo + hi + 1) >> 1;
-        if (tok_off[mid] <= tok) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
 // The request a lane's token belongs to, with its token range and the start
 // of its page list in each pool-side table.
 struct ReqOf {
@@ -214,54 +203,97 @@ __device__ __forceinline__ const int64_t* pg_off_of<PoolRef>(const PoolRef& p) {
     return p.pg_off;
 }
 
-// Request lookup for lane token `tok` of a chunk starting at tok0.  Must be
-// called with every lane active (it uses cross-lane reads).
-//
-// Batches of at most 64 requests: lane j loads tok_off[j] and the pg_off[j]
-// entries in one round trip (lane num_reqs holds T); a ballot counts the
-// request starts <= tok0, giving the chunk's first request, and each lane
-// steps forward past the request ends below its token by reading the next
-// start from the lane that holds it.  No dependent loads.
-// Larger batches: a binary search for the chunk's first request, then a
-// per-lane walk, both over memory.
+// Request lookup inside a window of 64 requests starting at `base`, which
+// holds the chunk's first request; edge is the start of request base + 64 (T
+// when there is none).  Lane j loads tok_off, and the pg_off entries, of
+// request base + j in one round trip; a ballot over the starts <= tok0 gives
+// the chunk's first request, and each lane steps forward past the request
+// ends at or below its token by reading the next start from the lane that
+// holds it.  A lane whose token lies past the window (a chunk crossing more
+// than 63 request starts: many tiny or empty requests) finishes with a walk
+// over memory.  WHOLE: the window holds the whole batch (base 0, at most 64
+// requests), so no lane can pass it.  Called with every lane active
+// (cross-lane reads).
+template <bool WHOLE>
+__device__ __forceinline__ ReqOf window_lookup(const Common& c, const int64_t* ps,
+                                               const int64_t* pd, int64_t tok0, int64_t tok,
+                                               bool active, int lane, int32_t base,
+                                               int64_t edge) {
+    const int32_t nr = c.num_reqs;
+    const int32_t w = base + lane;
+    const int64_t tv = w < nr ? c.tok_off[w] : (w == nr ? c.T : INT64_MAX);
+    const int64_t sv = (ps != nullptr && w < nr) ? ps[w] : 0;
+    const int64_t dv = (pd != nullptr && w < nr) ? pd[w] : 0;
+    int32_t r = static_cast<int32_t>(__popcll(__ballot(tv <= tok0))) - 1;
+    if (r < 0) r = 0;
+    for (;;) {
+        const int64_t nxt_l = static_cast<int64_t>(bperm64(static_cast<uint64_t>(tv),
+                                                           static_cast<uint32_t>(r + 1)));
+        bool adv;
+        if constexpr (WHOLE) {
+            // r + 1 == 64 only when nr == 64: then the next start is T
+            const int64_t nxt = r + 1 < kWave ? nxt_l : c.T;
+            adv = active && r + 1 < nr && nxt <= tok;
+        } else {
+            adv = active && r + 1 < kWave && base + r + 1 < nr && nxt_l <= tok;
+        }
+        if (__ballot(adv) == 0) break;
+        r += adv ? 1 : 0;
+    }
+    const uint32_t rl = static_cast<uint32_t>(r);
+    ReqOf q;
+    q.off = static_cast<int64_t>(bperm64(static_cast<uint64_t>(tv), rl));
+    const int64_t end_l = static_cast<int64_t>(bperm64(static_cast<uint64_t>(tv), rl + 1));
+    q.end = r + 1 < kWave ? end_l : edge;
+    q.pg_src = static_cast<int64_t>(bperm64(static_cast<uint64_t>(sv), rl));
+    q.pg_dst = static_cast<int64_t>(bperm64(static_cast<uint64_t>(dv), rl));
+    q.r = base + r;
+    if (!WHOLE && base + kWave < nr && active && q.end <= tok) {
+        // Only at the window's last request, with requests past the window.
+        int32_t ra = base + kWave;
+        while (ra + 1 < nr && c.tok_off[ra + 1] <= tok) ++ra;
+        q.off = c.tok_off[ra];
+        q.end = ra + 1 < nr ? c.tok_off[ra + 1] : c.T;
+        q.pg_src = ps != nullptr ? ps[ra] : 0;
+        q.pg_dst = pd != nullptr ? pd[ra] : 0;
+        q.r = ra;
+    }
+    return q;
+}
+
+// Request lookup for lane token `tok` of a chunk starting at tok0 (< T):
+// the chunk's first request is the largest r < num_reqs with
+// tok_off[r] <= tok0.  MANY is false only for batches of at most 64
+// requests, which the window holds whole.  With MANY, r is first narrowed
+// down with a 64-way search: lane j reads the start of every step-th request
+// of the current range, and a ballot over the starts <= tok0 keeps one
+// step-sized piece, so each round trip divides the range by 64 (one round up
+// to 4096 requests, two up to 262144).  The two are separate kernel
+// instances so that the small-batch kernels keep their register budget (the
+// search's scalar registers cost them a wave per SIMD).  Called with every
+// lane active (cross-lane reads).
+template <bool MANY>
 __device__ __forceinline__ ReqOf request_lookup(const Common& c, const int64_t* ps,
                                                 const int64_t* pd, int64_t tok0, int64_t tok,
                                                 bool active, int lane) {
-    const int32_t nr = c.num_reqs;
-    ReqOf q;
-    if (nr <= kWave) {
-        const int64_t tv = lane < nr ? c.tok_off[lane] : (lane == nr ? c.T : INT64_MAX);
-        const int64_t sv = (ps != nullptr && lane < nr) ? ps[lane] : 0;
-        const int64_t dv = (pd != nullptr && lane < nr) ? pd[lane] : 0;
-        int32_t r = static_cast<int32_t>(__popcll(__ballot(tv <= tok0))) - 1;
-        if (r < 0) r = 0;
-        for (;;) {
-            const int64_t nxt_l = static_cast<int64_t>(bperm64(static_cast<uint64_t>(tv),
-                                                               static_cast<uint32_t>(r + 1)));
-            const int64_t nxt = r + 1 < kWave ? nxt_l : c.T;
-            const bool adv = active && r + 1 < nr && nxt <= tok;
-            if (__ballot(adv) == 0) break;
-            r += adv ? 1 : 0;
-        }
-        const uint32_t rl = static_cast<uint32_t>(r);
-        q.off = static_cast<int64_t>(bperm64(static_cast<uint64_t>(tv), rl));
-        const int64_t end_l = static_cast<int64_t>(bperm64(static_cast<uint64_t>(tv), rl + 1));
-        q.end = r + 1 < kWave ? end_l : c.T;
-        q.pg_src = static_cast<int64_t>(bperm64(static_cast<uint64_t>(sv), rl));
-        q.pg_dst = static_cast<int64_t>(bperm64(static_cast<uint64_t>(dv), rl));
-        q.r = r;
+    if constexpr (!MANY) {
+        return window_lookup<true>(c, ps, pd, tok0, tok, active, lane, 0, c.T);
     } else {
-        int32_t r = request_of(c.tok_off, nr, tok0);
-        if (active) {
-            while (r + 1 < nr && c.tok_off[r + 1] <= tok) ++r;
+        const int32_t nr = c.num_reqs;
+        int32_t base = 0;
+        int64_t n = nr;   // candidates base .. base + n - 1; tok_off[base] <= tok0
+        while (n > kWave) {
+            const int64_t step = (n + kWave - 1) / kWave;
+            const int64_t p = static_cast<int64_t>(lane) * step;
+            const int64_t pv = p < n ? c.tok_off[base + p] : INT64_MAX;
+            int64_t k = static_cast<int64_t>(__popcll(__ballot(pv <= tok0)));
+            if (k < 1) k = 1;
+            base += static_cast<int32_t>((k - 1) * step);
+            n = n - (k - 1) * step < step ? n - (k - 1) * step : step;
         }
-        q.off = c.tok_off[r];
-        q.end = c.tok_off[r + 1];
-        q.pg_src = ps != nullptr ? ps[r] : 0;
-        q.pg_dst = pd != nullptr ? pd[r] : 0;
-        q.r = r;
+        const int64_t edge = base + kWave < nr ? c.tok_off[base + kWave] : c.T;
+        return window_lookup<false>(c, ps, pd, tok0, tok, active, lane, base, edge);
     }
-    return q;
 }
 
 // Address of token t of a request whose page list starts at pg_off_r, in
@@ -323,13 +355,13 @@ struct SideAddr<StageRef> {
 // Resolve unit u (one lane) of a paged chunk.  Called with every lane active.
 // A unit that is not copied gets the source's base as its source address, so
 // the copy may load it unconditionally (the call never writes its source).
-template <class Src, class Dst>
+template <bool MANY, class Src, class Dst>
 __device__ __forceinline__ int resolve(const PagedArgs<Src, Dst>& a, const PagedChunk& k,
                                        uint32_t u, uint64_t& s, uint64_t& d) {
     const Common& c = a.c;
     const int64_t tok = k.tok0 + u;
     const bool active = u < c.U && tok < c.T;
-    const ReqOf q = request_lookup(c, pg_off_of(a.src), pg_off_of(a.dst), k.tok0, tok, active,
+    const ReqOf q = request_lookup<MANY>(c, pg_off_of(a.src), pg_off_of(a.dst), k.tok0, tok, active,
                                    static_cast<int>(u));
     s = SideAddr<Src>::base(a.src, k.ql);
     if (!active) return kNone;
@@ -397,6 +429,7 @@ __device__ __forceinline__ bool head_addr(const PoolRef& p, int32_t ql, int64_t 
 // Resolve unit u of a head-sliced chunk: (token, head) of Db bytes.  Called
 // with every lane active.  `first` is set for the slice's first head, so a
 // skipped token row is counted once.
+template <bool MANY>
 __device__ __forceinline__ int resolve_heads(const HeadArgs& a, uint32_t chunk, uint32_t u,
                                              uint64_t& s, uint64_t& d, bool& first) {
     const Common& c = a.c;
@@ -417,7 +450,7 @@ __device__ __forceinline__ int resolve_heads(const HeadArgs& a, uint32_t chunk, 
     }
     const int64_t tok = t0 + tt;
     const bool active = u < c.U && static_cast<int32_t>(jl) < nhc_here && tok < c.T;
-    const ReqOf q = request_lookup(c, a.src.pg_off, a.dst.pg_off, t0, tok, active,
+    const ReqOf q = request_lookup<MANY>(c, a.src.pg_off, a.dst.pg_off, t0, tok, active,
                                    static_cast<int>(u));
     first = (j0 + static_cast<int32_t>(jl)) == 0;
     if (!active) return kNone;
@@ -586,8 +619,9 @@ __device__ __forceinline__ void count_skips(unsigned long long* counter, unsigne
 }
 
 // VPL > 0: wide copy with U rows per chunk; VPL < 0: row-loop copy with
-// KMAX = -VPL and at most U rows per chunk; VPL == 0: flat copy.
-template <class Src, class Dst, int VPL, int U>
+// KMAX = -VPL and at most U rows per chunk; VPL == 0: flat copy.  MANY: a
+// batch of more than 64 requests.
+template <class Src, class Dst, int VPL, int U, bool MANY>
 __global__ __launch_bounds__(kBlock) void k_paged(PagedArgs<Src, Dst> a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t nwaves = gridDim.x * kWavesPerBlock;
@@ -595,7 +629,7 @@ __global__ __launch_bounds__(kBlock) void k_paged(PagedArgs<Src, Dst> a) {
     for (uint32_t chunk = wave_id(a.c); chunk < a.c.nchunks; chunk += nwaves) {
         const PagedChunk k = paged_chunk(a.c, chunk);
         uint64_t s = 0, d = 0;
-        const int code = resolve(a, k, static_cast<uint32_t>(lane), s, d);
+        const int code = resolve<MANY>(a, k, static_cast<uint32_t>(lane), s, d);
         nskip += __popcll(__ballot(code == kSkip));
         constexpr bool nts = std::is_same<Dst, PoolRef>::value;
         if constexpr (VPL > 0) copy_wide<VPL, U, nts>(s, d, code, lane);
@@ -606,6 +640,7 @@ __global__ __launch_bounds__(kBlock) void k_paged(PagedArgs<Src, Dst> a) {
 }
 
 // Head-sliced gather-scatter (flat copy of Db-byte units).
+template <bool MANY>
 __global__ __launch_bounds__(kBlock) void k_heads(HeadArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t nwaves = gridDim.x * kWavesPerBlock;
@@ -613,7 +648,7 @@ __global__ __launch_bounds__(kBlock) void k_heads(HeadArgs a) {
     for (uint32_t chunk = wave_id(a.c); chunk < a.c.nchunks; chunk += nwaves) {
         uint64_t s = 0, d = 0;
         bool first = false;
-        const int code = resolve_heads(a, chunk, static_cast<uint32_t>(lane), s, d, first);
+        const int code = resolve_heads<MANY>(a, chunk, static_cast<uint32_t>(lane), s, d, first);
         nskip += __popcll(__ballot(code == kSkip && first));
         copy_flat<true>(a.c, s, d, code, lane);
     }
@@ -630,7 +665,7 @@ __global__ __launch_bounds__(kBlock) void k_heads(HeadArgs a) {
 // is one page of one request on both sides, each head's B tokens are one
 // contiguous run of B * Db bytes.  KT = B * VD / 64.  Rows that are not
 // copied load the plane's first bytes instead and store nothing.
-template <int KT>
+template <int KT, bool MANY>
 __global__ __launch_bounds__(kBlock) void k_heads_hnd(HeadArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t nwaves = gridDim.x * kWavesPerBlock;
@@ -653,7 +688,7 @@ __global__ __launch_bounds__(kBlock) void k_heads_hnd(HeadArgs a) {
         const int64_t tok = t0 + lane;
         const bool active = static_cast<uint32_t>(lane) < static_cast<uint32_t>(a.Ut) &&
                             tok < c.T;
-        const ReqOf q = request_lookup(c, a.src.pg_off, a.dst.pg_off, t0, tok, active, lane);
+        const ReqOf q = request_lookup<MANY>(c, a.src.pg_off, a.dst.pg_off, t0, tok, active, lane);
         int code = kNone;
         uint64_t sb = 0, db = 0;
         if (active) {

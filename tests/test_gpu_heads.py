@@ -73,24 +73,31 @@ def test_heads_out_of_range(seed):
     run_heads(case, sH, dH, nh, sh0, dh0, D, seed % 2, (seed // 2) % 2, 100 + seed)
 
 
-def test_heads_many_requests():
-    # 70 requests (beyond the 64-request fast lookup) with empty ones
-    rng = np.random.default_rng(5)
-    lens = rng.integers(0, 12, 70)
-    lens[::5] = 0
-    B = 4
+# Batches beyond the 64-request window of the request lookup, with empty
+# requests: (requests, fraction empty, page size, src HND?, dst HND?).  HND on
+# both sides with one page size <= 64 takes the page-run kernel.
+MANY_REQS = [
+    (70, 0.2, 4, 1, 1), (70, 0.2, 4, 0, 1),
+    (5000, 0.5, 4, 1, 1), (5000, 0.5, 4, 0, 0), (5000, 0.9, 1, 1, 1), (5000, 0.9, 1, 1, 0),
+]
+
+
+@pytest.mark.parametrize("mi", range(len(MANY_REQS)))
+def test_heads_many_requests(mi):
+    nreq, zf, B, shnd, dhnd = MANY_REQS[mi]
+    rng = np.random.default_rng(5 + mi)
+    lens = np.where(rng.random(nreq) < zf, 0, rng.integers(1, 12, nreq))
+    lens[-1] = max(int(lens[-1]), 1)
     pages = [-(-int(n) // B) for n in lens]
     P = sum(pages) + 3
     perm_s, perm_d = rng.permutation(P), rng.permutation(P)
-    ls, ld, pos = [], [], 0
-    for p in pages:
-        ls.append(perm_s[pos:pos + p])
-        ld.append(perm_d[pos:pos + p])
-        pos += p
-    case = wl.PagedCase("heads_70req", wl.Geometry(1, 2, 2, 128), wl.csr_from_lengths(lens),
+    offs = np.concatenate([[0], np.cumsum(pages)])
+    ls = np.split(perm_s[:offs[-1]], offs[1:-1])
+    ld = np.split(perm_d[:offs[-1]], offs[1:-1])
+    case = wl.PagedCase(f"heads_{nreq}req", wl.Geometry(1, 2, 2, 128), wl.csr_from_lengths(lens),
                         wl.side_from_page_lists(ls, P, B), wl.side_from_page_lists(ld, P, B),
                         0, 0, 0)
-    run_heads(case, 4, 2, 2, 2, 0, 128, 1, 1, 5)
+    run_heads(case, 4, 2, 2, 2, 0, 128, shnd, dhnd, 5 + mi)
 
 
 @pytest.mark.parametrize("layout", ["hnd", "nhd"])

@@ -180,6 +180,37 @@ def test_request_lookup_limits(nreq, R):
     run_paged_case(case, nreq)
 
 
+# Batches of more than 64 requests take the 64-way search for a chunk's first
+# request: one round up to 4096 requests, two up to 262144, three above.
+# Mostly-empty batches make one chunk (up to 64 tokens) cross more than 63
+# request starts, so some lanes finish past the 64-request window.
+# (requests, fraction empty, row bytes)
+LARGE_BATCHES = [
+    (256, 0.3, 2048), (256, 0.3, 16),
+    (4096, 0.3, 512), (4097, 0.3, 2048), (4097, 0.0, 16),
+    (9000, 0.5, 512), (70000, 0.3, 16), (70000, 0.3, 512),
+    (300000, 0.6, 16), (300000, 0.6, 512),
+    (700, 0.9, 16), (3000, 0.97, 16), (3000, 0.97, 512), (20000, 0.9, 2048),
+]
+
+
+@pytest.mark.parametrize("bi", range(len(LARGE_BATCHES)))
+def test_request_lookup_large_batches(bi):
+    nreq, zf, R = LARGE_BATCHES[bi]
+    rng = np.random.default_rng(9100 + bi)
+    lens = np.where(rng.random(nreq) < zf, 0, rng.integers(1, 4, nreq))
+    lens[-1] = max(int(lens[-1]), 1)
+    g = wl.Geometry(1, 2, 1, R // 2, "bf16")
+    S = int(lens.sum()) + 40
+    perm_s, perm_d = rng.permutation(S), rng.permutation(S)
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    ls = np.split(perm_s[:offs[-1]], offs[1:-1])
+    ld = np.split(perm_d[:offs[-1]], offs[1:-1])
+    case = wl.PagedCase(f"lookup_{nreq}_{zf}_{R}", g, wl.csr_from_lengths(lens),
+                        wl.side_from_slot_lists(ls, S), wl.side_from_slot_lists(ld, S), 0, 0, 0)
+    run_paged_case(case, 9100 + bi)
+
+
 def test_more_than_128_planes():
     # Q = 160 planes: the host splits the launch into plane ranges of 128
     case = wl.random_case(77, geom=wl.Geometry(80, 2, 1, 8, "bf16"), max_reqs=3, max_len=40,
