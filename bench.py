@@ -30,6 +30,7 @@ and the CPU oracle timed on the host on a bounded sample of the same steps.
   python bench.py --cu-split            (the two on complementary CU-masked streams)
   python bench.py --comparators         (per-block runtime copies, DMA copy of staging)
   python bench.py --sizes               (one request of 16 .. 8192 tokens: latency to bandwidth)
+  python bench.py --batches             (49152 tokens in 1 .. 49152 requests: request lookup)
   python bench.py --pmc-pass            (short run for rocprofv3 --pmc)
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --pmc-out OUT
   python bench.py --summarize-trace TRACE_DIR OUT TITLE COMMAND
@@ -819,6 +820,27 @@ def cu_split(torch, kvx, wl, wdev, dev, reps=32):
     print(json.dumps(result), flush=True)
 
 
+def graph_timed(torch, stream, fn, n):
+    """Milliseconds per call of fn(i), i = 1..n, captured in one graph on
+    `stream` and replayed once after a warm replay (fn(0) runs eagerly
+    first)."""
+    fn(0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(n):
+            fn(i + 1)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):        # replay runs on the current stream
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def request_sizes(torch, kvx, wl, wdev, dev, stream):
     """Gather-scatter and gather of one request of n tokens at 144 KiB/token
     (page-1 pools of 65536 slots, slots from seeded permutations, 8 disjoint
@@ -840,23 +862,6 @@ def request_sizes(torch, kvx, wl, wdev, dev, stream):
     def d(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    def timed(fn, n):
-        fn(0)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(n):
-                fn(i + 1)
-        graph.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):        # replay runs on the current stream
-            e0.record(stream)
-            graph.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
-
     for n in (16, 64, 256, 1024, 2048, 4096, 8192):
         reqs = kvx.Requests(d(np.array([0, n], np.int64)), n)
         pg = d(np.array([0, n], np.int64))
@@ -873,10 +878,63 @@ def request_sizes(torch, kvx, wl, wdev, dev, stream):
                                                        stream=stream)),
                        ("plain_copy", lambda i: wdev.copy_bytes(cp, st, st.numel(),
                                                                 stream=stream))):
-            ms = timed(fn, reps)
+            ms = graph_timed(torch, stream, fn, reps)
             line[op] = {"us": round(ms * 1e3, 2), "GBps": round(nb / (ms * 1e6), 1)}
         print(json.dumps(line), flush=True)
         del st, cp
+
+
+def batch_sizes(torch, kvx, wl, wdev, dev, stream):
+    """Gather and gather-scatter of 49152 tokens at 144 KiB/token (page-1
+    pools of 65536 slots, slots from seeded permutations) split into 1 to
+    49152 requests: equal lengths, and at 1024 and 4096 requests exponential
+    lengths with empty requests among them.  Graph-timed.  Batches above 64
+    requests take the kernels with the 64-way request search."""
+    import numpy as np
+    g = wl.KV144K
+    Q, R, NS, T = g.planes, g.row_bytes, 65536, 49152
+    rng = np.random.default_rng(2020)
+    pa, pb = rng.permutation(NS)[:T], rng.permutation(NS)[:T]
+    A = torch.empty((Q, NS, R), dtype=torch.uint8, device=dev)
+    B = torch.empty_like(A)
+    wdev.fill_hash(A, 1, stream=stream)
+    wdev.fill_hash(B, 2, stream=stream)
+    st = torch.empty(T * Q * R, dtype=torch.uint8, device=dev)
+    lay = kvx.Layout(g.num_layers, g.num_kv, g.kv_heads, g.head_dim, g.dtype)
+    PA, PB = kvx.Pool(A, NS), kvx.Pool(B, NS)
+    nb = 2 * T * Q * R
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def exp_lengths(n):
+        w = rng.exponential(1.0, n) * (rng.random(n) > 0.1)
+        w[-1] = max(w[-1], 1.0)
+        lens = np.floor(w / w.sum() * T).astype(np.int64)
+        lens[-1] += T - lens.sum()
+        return lens
+
+    cases = [(n, "equal") for n in (1, 16, 64, 65, 256, 1024, 4096, 16384, 49152)]
+    cases += [(1024, "exponential"), (4096, "exponential")]
+    for n, mix in cases:
+        if mix == "equal":
+            lens = np.full(n, T // n, np.int64)
+            lens[:T - lens.sum()] += 1
+        else:
+            lens = exp_lengths(n)
+        tok = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        reqs = kvx.Requests(d(tok), T)
+        ts = kvx.Table(d(tok), d(pa.astype(np.int32)))
+        td = kvx.Table(d(tok), d(pb.astype(np.int32)))
+        line = {"requests": n, "lengths": mix, "tokens": T, "bytes_rw": nb,
+                "empty": int((lens == 0).sum())}
+        for op, fn in (("gather", lambda i: kvx.gather(lay, PA, ts, reqs, st, stream=stream)),
+                       ("gather_scatter", lambda i: kvx.gather_scatter(lay, PA, ts, reqs, PB, td,
+                                                                       stream=stream))):
+            ms = graph_timed(torch, stream, fn, 8)
+            line[op] = {"us": round(ms * 1e3, 1), "GBps": round(nb / (ms * 1e6), 1)}
+        print(json.dumps(line), flush=True)
+    del A, B, st
 
 
 def comparators(torch, kvx, wl, wdev, dev):
@@ -1031,6 +1089,8 @@ def main():
                     help="the transfer and a full-intensity reader on complementary CU masks")
     ap.add_argument("--sizes", action="store_true",
                     help="gather-scatter and gather of one request of 16 .. 8192 tokens")
+    ap.add_argument("--batches", action="store_true",
+                    help="49152 tokens split into 1 .. 49152 requests (request lookup cost)")
     ap.add_argument("--comparators", action="store_true",
                     help="the same request moved by one runtime copy per block / per run")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -1073,6 +1133,9 @@ def main():
         return 0
     if args.sizes:
         request_sizes(torch, kvx, wl, wdev, dev, stream)
+        return 0
+    if args.batches:
+        batch_sizes(torch, kvx, wl, wdev, dev, stream)
         return 0
     if args.comparators:
         comparators(torch, kvx, wl, wdev, dev)

@@ -361,6 +361,8 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
         a.c.skipped = skipped;
         a.c.T = reqs->total_tokens;
         a.c.num_reqs = reqs->num_reqs;
+        a.c.req_rate = static_cast<double>(reqs->num_reqs) /
+                       static_cast<double>(reqs->total_tokens);
         a.c.q0 = q0;
         a.c.Q = g.Q;
         a.c.R = static_cast<int32_t>(g.R);
@@ -510,6 +512,8 @@ kvx_status run_heads(const Geom& g, const kvx_reqs* reqs, const kvx_pool* src,
         a.c.skipped = skipped;
         a.c.T = reqs->total_tokens;
         a.c.num_reqs = reqs->num_reqs;
+        a.c.req_rate = static_cast<double>(reqs->num_reqs) /
+                       static_cast<double>(reqs->total_tokens);
         a.c.q0 = q0;
         a.c.Q = g.Q;
         a.c.R = static_cast<int32_t>(g.Db);

@@ -92,6 +92,7 @@ struct Common {
     uint32_t V;                 // 16-byte vectors per unit
     uint32_t v_magic;           // ceil(2^32 / V)
     uint32_t remap;             // 1: XCD-aware workgroup renumbering
+    double req_rate;            // paged: num_reqs / T (requests per token)
 };
 
 // One side of a paged move that is a pool.
@@ -203,31 +204,43 @@ __device__ __forceinline__ const int64_t* pg_off_of<PoolRef>(const PoolRef& p) {
     return p.pg_off;
 }
 
-// Request lookup inside a window of 64 requests starting at `base`, which
-// holds the chunk's first request; edge is the start of request base + 64 (T
-// when there is none).  Lane j loads tok_off, and the pg_off entries, of
-// request base + j in one round trip; a ballot over the starts <= tok0 gives
-// the chunk's first request, and each lane steps forward past the request
-// ends at or below its token by reading the next start from the lane that
-// holds it.  A lane whose token lies past the window (a chunk crossing more
-// than 63 request starts: many tiny or empty requests) finishes with a walk
-// over memory.  WHOLE: the window holds the whole batch (base 0, at most 64
-// requests), so no lane can pass it.  Called with every lane active
-// (cross-lane reads).
-template <bool WHOLE>
-__device__ __forceinline__ ReqOf window_lookup(const Common& c, const int64_t* ps,
-                                               const int64_t* pd, int64_t tok0, int64_t tok,
-                                               bool active, int lane, int32_t base,
-                                               int64_t edge) {
+// A window of 64 requests starting at `base`: lane j holds tok_off, and the
+// pg_off entries, of request base + j (request num_reqs: T; past it
+// INT64_MAX), loaded in one round trip.
+struct Window {
+    int64_t tv, sv, dv;
+};
+
+__device__ __forceinline__ Window load_window(const Common& c, const int64_t* ps,
+                                              const int64_t* pd, int32_t base, int lane) {
     const int32_t nr = c.num_reqs;
     const int32_t w = base + lane;
-    const int64_t tv = w < nr ? c.tok_off[w] : (w == nr ? c.T : INT64_MAX);
-    const int64_t sv = (ps != nullptr && w < nr) ? ps[w] : 0;
-    const int64_t dv = (pd != nullptr && w < nr) ? pd[w] : 0;
-    int32_t r = static_cast<int32_t>(__popcll(__ballot(tv <= tok0))) - 1;
+    Window v;
+    v.tv = w < nr ? c.tok_off[w] : (w == nr ? c.T : INT64_MAX);
+    v.sv = (ps != nullptr && w < nr) ? ps[w] : 0;
+    v.dv = (pd != nullptr && w < nr) ? pd[w] : 0;
+    return v;
+}
+
+// Request lookup inside a window that holds the chunk's first request; edge
+// is the start of request base + 64 (T when there is none).  A ballot over
+// the starts <= tok0 gives the chunk's first request, and each lane steps
+// forward past the request ends at or below its token by reading the next
+// start from the lane that holds it.  A lane whose token lies past the
+// window (a chunk crossing more than 63 request starts: many tiny or empty
+// requests) finishes with a walk over memory.  WHOLE: the window holds the
+// whole batch (base 0, at most 64 requests), so no lane can pass it.  Called
+// with every lane active (cross-lane reads).
+template <bool WHOLE>
+__device__ __forceinline__ ReqOf walk_window(const Common& c, const Window& v,
+                                             const int64_t* ps, const int64_t* pd,
+                                             int64_t tok0, int64_t tok, bool active,
+                                             int32_t base, int64_t edge) {
+    const int32_t nr = c.num_reqs;
+    int32_t r = static_cast<int32_t>(__popcll(__ballot(v.tv <= tok0))) - 1;
     if (r < 0) r = 0;
     for (;;) {
-        const int64_t nxt_l = static_cast<int64_t>(bperm64(static_cast<uint64_t>(tv),
+        const int64_t nxt_l = static_cast<int64_t>(bperm64(static_cast<uint64_t>(v.tv),
                                                            static_cast<uint32_t>(r + 1)));
         bool adv;
         if constexpr (WHOLE) {
@@ -242,11 +255,11 @@ __device__ __forceinline__ ReqOf window_lookup(const Common& c, const int64_t* p
     }
     const uint32_t rl = static_cast<uint32_t>(r);
     ReqOf q;
-    q.off = static_cast<int64_t>(bperm64(static_cast<uint64_t>(tv), rl));
-    const int64_t end_l = static_cast<int64_t>(bperm64(static_cast<uint64_t>(tv), rl + 1));
+    q.off = static_cast<int64_t>(bperm64(static_cast<uint64_t>(v.tv), rl));
+    const int64_t end_l = static_cast<int64_t>(bperm64(static_cast<uint64_t>(v.tv), rl + 1));
     q.end = r + 1 < kWave ? end_l : edge;
-    q.pg_src = static_cast<int64_t>(bperm64(static_cast<uint64_t>(sv), rl));
-    q.pg_dst = static_cast<int64_t>(bperm64(static_cast<uint64_t>(dv), rl));
+    q.pg_src = static_cast<int64_t>(bperm64(static_cast<uint64_t>(v.sv), rl));
+    q.pg_dst = static_cast<int64_t>(bperm64(static_cast<uint64_t>(v.dv), rl));
     q.r = base + r;
     if (!WHOLE && base + kWave < nr && active && q.end <= tok) {
         // Only at the window's last request, with requests past the window.
@@ -264,35 +277,56 @@ __device__ __forceinline__ ReqOf window_lookup(const Common& c, const int64_t* p
 // Request lookup for lane token `tok` of a chunk starting at tok0 (< T):
 // the chunk's first request is the largest r < num_reqs with
 // tok_off[r] <= tok0.  MANY is false only for batches of at most 64
-// requests, which the window holds whole.  With MANY, r is first narrowed
-// down with a 64-way search: lane j reads the start of every step-th request
-// of the current range, and a ballot over the starts <= tok0 keeps one
-// step-sized piece, so each round trip divides the range by 64 (one round up
-// to 4096 requests, two up to 262144).  The two are separate kernel
-// instances so that the small-batch kernels keep their register budget (the
-// search's scalar registers cost them a wave per SIMD).  Called with every
-// lane active (cross-lane reads).
+// requests, which one window holds whole.
+//
+// With MANY the wave first loads a guessed window: the one starting 32
+// requests before the request that would hold tok0 if all requests had the
+// same length.  Beside it goes the first round of a 64-way search (lane j
+// reads the start of every step-th request).  If the guessed window brackets
+// tok0 (its first start <= tok0 < the start past it), the lookup took one
+// round trip.  Otherwise a ballot over the search's starts <= tok0 keeps one
+// step-sized piece of the range, each further round divides it by 64 (one
+// round up to 4096 requests, two up to 262144), and the window at the
+// piece's first request is loaded.  The two kinds are separate kernel
+// instances so that the small-batch kernels keep their register budget.
+// Called with every lane active (cross-lane reads).
 template <bool MANY>
 __device__ __forceinline__ ReqOf request_lookup(const Common& c, const int64_t* ps,
                                                 const int64_t* pd, int64_t tok0, int64_t tok,
                                                 bool active, int lane) {
     if constexpr (!MANY) {
-        return window_lookup<true>(c, ps, pd, tok0, tok, active, lane, 0, c.T);
+        return walk_window<true>(c, load_window(c, ps, pd, 0, lane), ps, pd, tok0, tok, active,
+                                 0, c.T);
     } else {
         const int32_t nr = c.num_reqs;
-        int32_t base = 0;
-        int64_t n = nr;   // candidates base .. base + n - 1; tok_off[base] <= tok0
-        while (n > kWave) {
-            const int64_t step = (n + kWave - 1) / kWave;
-            const int64_t p = static_cast<int64_t>(lane) * step;
-            const int64_t pv = p < n ? c.tok_off[base + p] : INT64_MAX;
-            int64_t k = static_cast<int64_t>(__popcll(__ballot(pv <= tok0)));
-            if (k < 1) k = 1;
-            base += static_cast<int32_t>((k - 1) * step);
-            n = n - (k - 1) * step < step ? n - (k - 1) * step : step;
+        int64_t g = static_cast<int64_t>(static_cast<double>(tok0) * c.req_rate) - kWave / 2;
+        g = g < 0 ? 0 : (g > nr - 1 ? nr - 1 : g);
+        int32_t base = static_cast<int32_t>(g);
+        Window v = load_window(c, ps, pd, base, lane);
+        int64_t edge = base + kWave < nr ? c.tok_off[base + kWave] : c.T;
+        // 32-bit search state: n <= num_reqs < 2^31 and lane * step < 2^31
+        int32_t n = nr;     // search range 0 .. n - 1
+        int32_t step = (n - 1) / kWave + 1;
+        int32_t p = lane * step;
+        int64_t pv = p < n ? c.tok_off[p] : INT64_MAX;
+        const bool hit = (__ballot(v.tv <= tok0) & 1ull) != 0 && edge > tok0;
+        if (!hit) {
+            int32_t b = 0;  // tok_off[b] <= tok0; candidates b .. b + n - 1
+            for (;;) {
+                int32_t k = static_cast<int32_t>(__popcll(__ballot(pv <= tok0)));
+                if (k < 1) k = 1;
+                b += (k - 1) * step;
+                n = n - (k - 1) * step < step ? n - (k - 1) * step : step;
+                if (n <= kWave) break;
+                step = (n - 1) / kWave + 1;
+                p = lane * step;
+                pv = p < n ? c.tok_off[b + p] : INT64_MAX;
+            }
+            base = b;
+            v = load_window(c, ps, pd, base, lane);
+            edge = base + kWave < nr ? c.tok_off[base + kWave] : c.T;
         }
-        const int64_t edge = base + kWave < nr ? c.tok_off[base + kWave] : c.T;
-        return window_lookup<false>(c, ps, pd, tok0, tok, active, lane, base, edge);
+        return walk_window<false>(c, v, ps, pd, tok0, tok, active, base, edge);
     }
 }
 
@@ -618,11 +652,23 @@ __device__ __forceinline__ void count_skips(unsigned long long* counter, unsigne
     if (counter != nullptr && n != 0 && lane == 0) atomicAdd(counter, n);
 }
 
+// Waves per SIMD the many-request instances are held to.  Their lookup
+// (guessed window, search state, window edge) needs more scalar registers
+// than 8 waves allow, which would leave them at 7; held to 8, the compiler
+// keeps the excess in VGPR lanes instead (no scratch), and gather-scatter of
+// 2 KiB rows in batches above 64 requests runs 1-13% faster than at 7
+// waves (measured).
+// Only instances whose VGPRs fit 8 waves anyway are held; 1 = no hold.  (The
+// head kernels are not held: there the excess would reach scratch memory.)
+constexpr int many_waves(bool many, bool light) { return many && light ? 8 : 1; }
+
 // VPL > 0: wide copy with U rows per chunk; VPL < 0: row-loop copy with
 // KMAX = -VPL and at most U rows per chunk; VPL == 0: flat copy.  MANY: a
 // batch of more than 64 requests.
 template <class Src, class Dst, int VPL, int U, bool MANY>
-__global__ __launch_bounds__(kBlock) void k_paged(PagedArgs<Src, Dst> a) {
+__global__ __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu(many_waves(MANY, VPL != 0 && VPL >= -4 && VPL <= 4))))
+void k_paged(PagedArgs<Src, Dst> a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t nwaves = gridDim.x * kWavesPerBlock;
     unsigned long long nskip = 0;
