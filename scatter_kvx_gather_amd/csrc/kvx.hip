@@ -212,18 +212,25 @@ uint32_t wide_rows_for(const Shape& sh, int64_t rows, int64_t row_bytes, int cus
 // XCD-aware renumbering pays when a launch spans more memory than the
 // translation caches reach: then each XCD, working on ~1/8 of the planes,
 // touches ~1/8 of the translations.  Below that it costs a few percent.
-// Measured (same process, alternating): the 2048-token request in 4.5 GiB
-// pools, gather-scatter 5015 GB/s without vs 4880 with; the same request
-// spread over 36 GiB pools 4632 without vs 4798 with; 36 GiB page-16 pools
-// 5456 vs 5924; the fragmented gather from an 18 GiB pool 5040 vs 5289; a
-// head-sliced copy over 14.4 GiB 5259 vs 5091; permutes of 0.1-0.9 GB 3-9%
-// faster without.
+// Measured (same process, alternating; a large pool's rate also moves by up
+// to 8% between allocations, so only same-process pairs are compared):
+// the 2048-token request in 4.5 GiB pools, gather-scatter 5015 GB/s without
+// vs 4880 with; the same request spread over 36 GiB pools 4632 without vs
+// 4798 with, and 131072 tokens there 5374 vs 5743; the fragmented gather
+// from an 18 GiB pool 5082 vs 5322; a head-sliced copy over 13.5 GiB 5330
+// vs 5114; permutes of 0.1-0.9 GB 3-9% faster without.  Pool-to-pool
+// launches (two pools) renumber above a 16 GiB span: with two 9 GiB pools
+// the page-1 gather-scatter is 4% faster without (5236 vs 5030).
 constexpr double kRemapSpanBytes = 16.0 * (1ull << 30);
+// Launches with one pool side (gather, scatter: the other side is staging)
+// renumber from a pool of 8 GiB: with a 9 GiB pool gather runs 5409 -> 5651
+// GB/s and scatter 5327 -> 5464 with it, and 4.5 GiB pools gain nothing.
+constexpr double kRemapOnePoolBytes = 8.0 * (1ull << 30);
 
-uint32_t remap_for(double span_bytes) {
+uint32_t remap_for(double span_bytes, double threshold = kRemapSpanBytes) {
     if (KVX_XCD_REMAP == 0) return 0;
     if (KVX_XCD_REMAP == 1) return 1;
-    return span_bytes > kRemapSpanBytes ? 1u : 0u;
+    return span_bytes > threshold ? 1u : 0u;
 }
 
 // Bytes of the nq planes of a pool that a launch may touch.
@@ -372,9 +379,9 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
         else a.src.base = static_cast<char*>(src_stage);
         if constexpr (std::is_same<Dst, PoolRef>::value) fill_pool_ref(&a.dst, dst, dt, q0, nq);
         else a.dst.base = static_cast<char*>(dst_stage);
-        const double stage = static_cast<double>(reqs->total_tokens) * g.Q * g.R;
-        a.c.remap = remap_for((src != nullptr ? pool_span(src, nq) : stage) +
-                              (dst != nullptr ? pool_span(dst, nq) : stage));
+        a.c.remap = src != nullptr && dst != nullptr
+                        ? remap_for(pool_span(src, nq) + pool_span(dst, nq))
+                        : remap_for(pool_span(src != nullptr ? src : dst, nq), kRemapOnePoolBytes);
         const uint32_t grid = grid_for(a.c.nchunks, cus);
         if (log_enabled())
             std::fprintf(stderr,
