@@ -1,6 +1,7 @@
 """Randomized GPU parity against the oracle: geometries with rows of 16 B to
 4 KiB in every element size, pages drawn from {1, 2, 16, 32} on each side,
-1 to 64 requests with empty ones, some page ids out of range, random-bit
+1 to 64 requests with empty ones (and 65 to 5000 in a second set), some page
+ids out of range, random-bit
 payloads (NaN patterns included), sentinel-filled destinations and guard
 bytes after the staging.  Every case is compared byte for byte over the whole
 destination, and the skip counters must agree."""
@@ -38,6 +39,25 @@ def test_fuzz_paged_ops(seed):
     oor = float(rng.choice([0.0, 0.0, 0.05]))
     case = big_case(f"fuzz{seed}", g, list(lens), sp, dp, 88000 + seed, oor)
     run_paged_case(case, 88000 + seed)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_fuzz_paged_many_requests(seed):
+    # 65 to 5000 requests: the guessed-window lookup and the 64-way search,
+    # with empty requests at a random rate
+    rng = np.random.default_rng(89000 + seed)
+    g = random_geometry(rng)
+    nreq = int(rng.integers(65, 5001))
+    zf = float(rng.choice([0.0, 0.2, 0.6, 0.9]))
+    lens = np.where(rng.random(nreq) < zf, 0, rng.integers(1, int(rng.integers(2, 12)), nreq))
+    while lens.sum() * g.planes * g.row_bytes > (192 << 20):     # bound the host work
+        lens //= 2
+    if lens.sum() == 0:
+        lens[0] = 1
+    sp, dp = (int(rng.choice([1, 2, 16, 32])) for _ in range(2))
+    oor = float(rng.choice([0.0, 0.0, 0.05]))
+    case = big_case(f"fuzzmany{seed}", g, list(lens), sp, dp, 89000 + seed, oor)
+    run_paged_case(case, 89000 + seed)
 
 
 @pytest.mark.parametrize("seed", range(24))

@@ -158,6 +158,31 @@ def test_one_row_per_wave_launches(bi):
     run_paged_case(big_case(f"big{bi}", g, lens, sp, dp, 700 + bi, oor), 700 + bi)
 
 
+# One-row-per-wave launches of batches above 64 requests (the kernels with
+# the guessed window and the 64-way search): equal lengths, where the guess
+# hits, and ragged lengths with empty requests, where it often misses.
+# (geometry, requests, max length, empty fraction, src page, dst page, oor)
+BIG_MANY = [
+    (wl.Geometry(4, 2, 8, 128, "bf16"), 6000, 3, 0.0, 1, 1, 0.0),       # R = 2 KiB, equal
+    (wl.Geometry(4, 2, 8, 128, "bf16"), 6000, 6, 0.3, 1, 1, 0.0),       # R = 2 KiB, ragged
+    (wl.Geometry(8, 2, 4, 128, "bf16"), 3000, 12, 0.2, 16, 3, 0.02),    # R = 1 KiB
+    (wl.Geometry(2, 2, 16, 128, "bf16"), 70000, 1, 0.6, 1, 2, 0.0),     # R = 4 KiB, 2 search rounds
+]
+
+
+@pytest.mark.parametrize("bi", range(len(BIG_MANY)))
+def test_one_row_per_wave_many_requests(bi):
+    g, nreq, maxlen, zf, sp, dp, oor = BIG_MANY[bi]
+    rng = np.random.default_rng(760 + bi)
+    if zf == 0.0:
+        lens = np.full(nreq, maxlen, np.int64)
+    else:
+        lens = np.where(rng.random(nreq) < zf, 0, rng.integers(1, maxlen + 1, nreq))
+    lens[-1] = max(int(lens[-1]), 1)
+    assert lens.sum() * g.planes * g.row_bytes > 64 << 20 and nreq > 64
+    run_paged_case(big_case(f"bigmany{bi}", g, list(lens), sp, dp, 760 + bi, oor), 760 + bi)
+
+
 @pytest.mark.parametrize("nreq", [1, 2, 63, 64, 65, 130])
 @pytest.mark.parametrize("R", [2048, 512])
 def test_request_lookup_limits(nreq, R):
