@@ -9,9 +9,10 @@
 // chunk instead.  A wave takes one chunk at a time:
 //
 //   1. resolve: lane u < U computes unit u's source and destination byte
-//      addresses from the tables (token -> request by a search over tok_off,
-//      page id lookup, bounds checks) and a status: copy, skip (out of range),
-//      or none (past the end);
+//      addresses from the tables (token -> request from a window of 64
+//      request starts held across the wave's lanes, page id lookup, bounds
+//      checks) and a status: copy, skip (out of range), or none (past the
+//      end);
 //   2. copy: every 16-byte vector of the chunk's rows is loaded with a
 //      nontemporal dwordx4 load (all loads of the chunk are issued before the
 //      first store), then stored with a dwordx4 store: nontemporal into
@@ -31,10 +32,12 @@
 //
 // Waves grid-stride over the chunks (by default the grid has one wave per
 // chunk; the host can cap it at a few workgroups per compute unit).  In
-// launches that span more memory than the translation caches reach,
-// workgroup ids are renumbered so that consecutive chunks (the same plane,
-// adjacent tokens) run on the same XCD: gfx950 deals workgroups to its 8 XCDs
-// round-robin, and each XCD has its own L2 and translation caches.
+// launches over large pools, workgroup ids are renumbered so that
+// consecutive chunks (the same plane, adjacent tokens) run on the same XCD:
+// gfx950 deals workgroups to its 8 XCDs round-robin, and each XCD has its
+// own L2 and translation caches.  Batches of more than 64 requests run
+// separate instances of the paged and head kernels (template flag MANY),
+// whose request lookup first finds the right 64-request window.
 //
 // There is no arithmetic on the KV values anywhere: the kernels are pure data
 // movement and are bound by HBM bandwidth.
