@@ -309,8 +309,9 @@ const void* paged_kernel_of(int vpl, uint32_t U) {
     }
 }
 
-// Batches of more than 64 requests take the kernels with the 64-way request
-// search; smaller ones the kernels whose lookup window holds the whole batch.
+// Batches of more than 64 requests take the kernels whose lookup first finds
+// the chunk's 64-request window (a guessed one, else by a 64-way search);
+// smaller ones the kernels whose one window holds the whole batch.
 template <class Src, class Dst>
 const void* paged_kernel(int vpl, uint32_t U, int32_t num_reqs) {
     return num_reqs > kWave ? paged_kernel_of<Src, Dst, true>(vpl, U)
