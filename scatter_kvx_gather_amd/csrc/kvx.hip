@@ -268,8 +268,9 @@ bool set_chunks(Common* c, const Shape& sh, uint32_t units_per_plane, int32_t nq
     return true;
 }
 
-uint32_t grid_for(uint32_t nchunks, int cus) {
-    uint64_t need = (static_cast<uint64_t>(nchunks) + kWavesPerBlock - 1) / kWavesPerBlock;
+// Workgroups of wpb waves for one wave per chunk (or the cap).
+uint32_t grid_for(uint32_t nchunks, int cus, int wpb) {
+    uint64_t need = (static_cast<uint64_t>(nchunks) + wpb - 1) / wpb;
     uint64_t g = need;
     int bpc = blocks_per_cu();
     if (bpc > 0) {
@@ -282,9 +283,9 @@ uint32_t grid_for(uint32_t nchunks, int cus) {
 }
 
 template <class Args>
-kvx_status launch(const void* fn, uint32_t grid, Args& a, hipStream_t stream) {
+kvx_status launch(const void* fn, uint32_t grid, int wpb, Args& a, hipStream_t stream) {
     void* params[] = {&a};
-    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kBlock), params, 0, stream);
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kWave * wpb), params, 0, stream);
     return e == hipSuccess ? KVX_OK : KVX_E_HIP;
 }
 
@@ -383,7 +384,7 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
         a.c.remap = src != nullptr && dst != nullptr
                         ? remap_for(pool_span(src, nq) + pool_span(dst, nq))
                         : remap_for(pool_span(src != nullptr ? src : dst, nq), kRemapOnePoolBytes);
-        const uint32_t grid = grid_for(a.c.nchunks, cus);
+        const uint32_t grid = grid_for(a.c.nchunks, cus, kPagedWaves);
         if (log_enabled())
             std::fprintf(stderr,
                          "kvx: %s Q=%d planes[%d,%d) R=%lld T=%lld reqs=%d copy=%s U=%u "
@@ -392,7 +393,7 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
                          static_cast<long long>(reqs->total_tokens), reqs->num_reqs,
                          sh.vpl > 0 ? "wide" : (sh.vpl < 0 ? "row-loop" : "flat"), sh.U,
                          a.c.nchunks, grid, a.c.remap);
-        s = launch(paged_kernel<Src, Dst>(sh.vpl, sh.U, a.c.num_reqs), grid, a, stream);
+        s = launch(paged_kernel<Src, Dst>(sh.vpl, sh.U, a.c.num_reqs), grid, kPagedWaves, a, stream);
         if (s != KVX_OK) return s;
     }
     return KVX_OK;
@@ -428,7 +429,7 @@ kvx_status run_permute(const Geom& g, void* const* hf, int64_t s_cap, int64_t se
         a.H = g.H;
         a.c.remap = remap_for(static_cast<double>(nq) * g.H * s_cap * g.Db +
                               static_cast<double>(nq) * seq * g.R);
-        const uint32_t grid = grid_for(a.c.nchunks, cus);
+        const uint32_t grid = grid_for(a.c.nchunks, cus, kPermuteWaves);
         if (log_enabled())
             std::fprintf(stderr,
                          "kvx: %s Q=%d planes[%d,%d) H=%d Db=%lld seq=%lld s_cap=%lld unit=%s "
@@ -439,7 +440,7 @@ kvx_status run_permute(const Geom& g, void* const* hf, int64_t s_cap, int64_t se
                          a.c.nchunks, grid);
         const void* fn = rows ? permute_rows_kernel<REBUILD>(sh.vpl, sh.U)
                               : reinterpret_cast<const void*>(&k_permute<REBUILD>);
-        s = launch(fn, grid, a, stream);
+        s = launch(fn, grid, kPermuteWaves, a, stream);
         if (s != KVX_OK) return s;
     }
     return KVX_OK;
@@ -545,7 +546,7 @@ kvx_status run_heads(const Geom& g, const kvx_reqs* reqs, const kvx_pool* src,
         a.head_major = (a.hs.hnd && a.hd.hnd) ? 1 : 0;
         a.c.remap = remap_for(pool_span(src, nq) + pool_span(dst, nq));
         if (kt > 0) a.c.U = static_cast<uint32_t>(Ut);
-        const uint32_t grid = grid_for(a.c.nchunks, cus);
+        const uint32_t grid = grid_for(a.c.nchunks, cus, kPagedWaves);
         if (log_enabled())
             std::fprintf(stderr,
                          "kvx: gather_scatter_heads Q=%d planes[%d,%d) nh=%d Db=%lld T=%lld "
@@ -565,7 +566,7 @@ kvx_status run_heads(const Geom& g, const kvx_reqs* reqs, const kvx_pool* src,
             case 8: fn = heads_hnd_kernel<8>(many); break;
             default: break;
         }
-        s = launch(fn, grid, a, stream);
+        s = launch(fn, grid, kPagedWaves, a, stream);
         if (s != KVX_OK) return s;
     }
     return KVX_OK;

@@ -66,8 +66,14 @@ namespace kvx {
 #endif                             // 1 always, 2 when a launch spans > 16 GiB
 
 constexpr int kWave = 64;
-constexpr int kWavesPerBlock = 4;
-constexpr int kBlock = kWave * kWavesPerBlock;
+// Waves per workgroup, per kernel family.  Measured (same process,
+// alternating, against 4 for every kernel): 2-wave workgroups make the paged
+// kernels 0-2% faster on large launches (scatter of the 2048-token request
+// 5311 -> 5413 GB/s) and 4-14% on small ones (a 16-token gather-scatter
+// 1125 -> 1246), and the permutes 2% slower (rebuild at seq 8192 6464 ->
+// 6315); 8 or 16 waves lose everywhere, up to 2x on small launches.
+constexpr int kPagedWaves = 2;     // paged and head-sliced kernels
+constexpr int kPermuteWaves = 4;   // extract / rebuild permutes
 constexpr int kTab = 128;          // plane pointers carried per side per launch
 constexpr int kChunkBytes = KVX_CHUNK_KIB * 1024;
 constexpr int kXcds = 8;           // XCDs on gfx950
@@ -642,12 +648,13 @@ __device__ __forceinline__ void copy_flat(const Common& c, uint64_t s_l, uint64_
 // [x*G/8, (x+1)*G/8) on XCD x, so the chunks a grid-stride round hands to one
 // XCD are contiguous (one XCD then touches about 1/8 of the planes, and of
 // the address translations).
+template <int WPB>
 __device__ __forceinline__ uint32_t wave_id(const Common& c) {
     const uint32_t G = gridDim.x;
     const uint32_t b = blockIdx.x;
     const uint32_t lb =
         (c.remap && G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
-    return __builtin_amdgcn_readfirstlane(lb * kWavesPerBlock + (threadIdx.x >> 6));
+    return __builtin_amdgcn_readfirstlane(lb * WPB + (threadIdx.x >> 6));
 }
 
 __device__ __forceinline__ void count_skips(unsigned long long* counter, unsigned long long n,
@@ -669,13 +676,13 @@ constexpr int many_waves(bool many, bool light) { return many && light ? 8 : 1; 
 // KMAX = -VPL and at most U rows per chunk; VPL == 0: flat copy.  MANY: a
 // batch of more than 64 requests.
 template <class Src, class Dst, int VPL, int U, bool MANY>
-__global__ __launch_bounds__(kBlock)
+__global__ __launch_bounds__(kWave * kPagedWaves)
 __attribute__((amdgpu_waves_per_eu(many_waves(MANY, VPL != 0 && VPL >= -4 && VPL <= 4))))
 void k_paged(PagedArgs<Src, Dst> a) {
     const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t nwaves = gridDim.x * kWavesPerBlock;
+    const uint32_t nwaves = gridDim.x * kPagedWaves;
     unsigned long long nskip = 0;
-    for (uint32_t chunk = wave_id(a.c); chunk < a.c.nchunks; chunk += nwaves) {
+    for (uint32_t chunk = wave_id<kPagedWaves>(a.c); chunk < a.c.nchunks; chunk += nwaves) {
         const PagedChunk k = paged_chunk(a.c, chunk);
         uint64_t s = 0, d = 0;
         const int code = resolve<MANY>(a, k, static_cast<uint32_t>(lane), s, d);
@@ -690,11 +697,11 @@ void k_paged(PagedArgs<Src, Dst> a) {
 
 // Head-sliced gather-scatter (flat copy of Db-byte units).
 template <bool MANY>
-__global__ __launch_bounds__(kBlock) void k_heads(HeadArgs a) {
+__global__ __launch_bounds__(kWave * kPagedWaves) void k_heads(HeadArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t nwaves = gridDim.x * kWavesPerBlock;
+    const uint32_t nwaves = gridDim.x * kPagedWaves;
     unsigned long long nskip = 0;
-    for (uint32_t chunk = wave_id(a.c); chunk < a.c.nchunks; chunk += nwaves) {
+    for (uint32_t chunk = wave_id<kPagedWaves>(a.c); chunk < a.c.nchunks; chunk += nwaves) {
         uint64_t s = 0, d = 0;
         bool first = false;
         const int code = resolve_heads<MANY>(a, chunk, static_cast<uint32_t>(lane), s, d, first);
@@ -715,16 +722,16 @@ __global__ __launch_bounds__(kBlock) void k_heads(HeadArgs a) {
 // contiguous run of B * Db bytes.  KT = B * VD / 64.  Rows that are not
 // copied load the plane's first bytes instead and store nothing.
 template <int KT, bool MANY>
-__global__ __launch_bounds__(kBlock) void k_heads_hnd(HeadArgs a) {
+__global__ __launch_bounds__(kWave * kPagedWaves) void k_heads_hnd(HeadArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t nwaves = gridDim.x * kWavesPerBlock;
+    const uint32_t nwaves = gridDim.x * kPagedWaves;
     const Common& c = a.c;
     const uint64_t Db = static_cast<uint64_t>(c.R);
     const uint32_t vd = c.V;
     const uint32_t vd_shift = static_cast<uint32_t>(__builtin_ctz(vd));   // VD is a power of two
     const uint64_t B = static_cast<uint64_t>(a.Ut);
     unsigned long long nskip = 0;
-    for (uint32_t chunk = wave_id(c); chunk < c.nchunks; chunk += nwaves) {
+    for (uint32_t chunk = wave_id<kPagedWaves>(c); chunk < c.nchunks; chunk += nwaves) {
         const uint32_t ql = chunk / c.chunks_per_plane;
         const uint32_t rem = chunk - ql * c.chunks_per_plane;
         const uint32_t tb = rem / static_cast<uint32_t>(a.hblocks);
@@ -799,10 +806,10 @@ __global__ __launch_bounds__(kBlock) void k_heads_hnd(HeadArgs a) {
 
 // Permute with head rows as units (any head row size, flat copy).
 template <bool REBUILD>
-__global__ __launch_bounds__(kBlock) void k_permute(PermuteArgs a) {
+__global__ __launch_bounds__(kWave * kPermuteWaves) void k_permute(PermuteArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t nwaves = gridDim.x * kWavesPerBlock;
-    for (uint32_t chunk = wave_id(a.c); chunk < a.c.nchunks; chunk += nwaves) {
+    const uint32_t nwaves = gridDim.x * kPermuteWaves;
+    for (uint32_t chunk = wave_id<kPermuteWaves>(a.c); chunk < a.c.nchunks; chunk += nwaves) {
         const PermChunk k = perm_chunk(a.c, chunk);
         uint64_t s = 0, d = 0;
         const int code = resolve_perm<REBUILD>(a, k, static_cast<uint32_t>(lane), s, d);
@@ -817,9 +824,9 @@ __global__ __launch_bounds__(kBlock) void k_permute(PermuteArgs a) {
 // kernel, so every address is a per-lane constant plus s * Db (HF) or
 // s * H * Db (flat): no cross-lane exchange is needed.  U tokens per chunk.
 template <bool REBUILD, int VPL, int U>
-__global__ __launch_bounds__(kBlock) void k_permute_rows(PermuteArgs a) {
+__global__ __launch_bounds__(kWave * kPermuteWaves) void k_permute_rows(PermuteArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t nwaves = gridDim.x * kWavesPerBlock;
+    const uint32_t nwaves = gridDim.x * kPermuteWaves;
     const uint64_t Db = static_cast<uint64_t>(a.c.R);
     const uint64_t row = Db * static_cast<uint64_t>(a.H);         // token row bytes
     const uint32_t vd = a.c.V;                                      // vectors per head row
@@ -831,7 +838,7 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(PermuteArgs a) {
         hf_off[j] = static_cast<uint64_t>(h) * a.s_cap * Db + (idx - h * vd) * 16u;
     }
     const uint32_t seq = a.c.units_per_plane;
-    for (uint32_t chunk = wave_id(a.c); chunk < a.c.nchunks; chunk += nwaves) {
+    for (uint32_t chunk = wave_id<kPermuteWaves>(a.c); chunk < a.c.nchunks; chunk += nwaves) {
         const uint32_t ql = chunk / a.c.chunks_per_plane;
         const uint32_t s0 = (chunk - ql * a.c.chunks_per_plane) * U;
         const uint64_t hf = reinterpret_cast<uint64_t>(a.hf[ql]);
