@@ -34,6 +34,8 @@ and the CPU oracle timed on the host on a bounded sample of the same steps.
   python bench.py --pmc-pass            (short run for rocprofv3 --pmc)
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --pmc-out OUT
   python bench.py --summarize-trace TRACE_DIR OUT TITLE COMMAND
+  python bench.py --counter-commands    (rocprofv3 commands of the memory/wave counter passes)
+  python bench.py --summarize-counters OUT TITLE
 """
 from __future__ import annotations
 
@@ -270,23 +272,25 @@ def host_cpu():
 
 # ----------------------------------------------------------------- pmc --
 
+def counter_rows(d):
+    """Rows of every rocprofv3 counter_collection.csv under directory d."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    out = []
+    for fn in files:
+        with open(fn) as f:
+            out.extend(csv.DictReader(f))
+    return out
+
+
 def summarize_pmc(fetch_dir, write_dir, out_path):
     """Traffic per launch of the dominant kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter reads
     for the plain copy kernel of COPY_CALIB_BYTES run in the same process."""
-    def rows(d):
-        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
-        if not files:
-            raise SystemExit(f"no counter_collection.csv under {d}")
-        out = []
-        for fn in files:
-            with open(fn) as f:
-                out.extend(csv.DictReader(f))
-        return out
-
     def per_kernel(d, counter):
         acc = {}
-        for r in rows(d):
+        for r in counter_rows(d):
             if r.get("Counter_Name") != counter:
                 continue
             name = r["Kernel_Name"]
@@ -1042,6 +1046,90 @@ def comparators(torch, kvx, wl, wdev, dev):
     print(json.dumps(out), flush=True)
 
 
+# TCC channels summed by the *_sum counters on MI355X: 16 per XCD x 8 XCDs
+TCC_CHANNELS = 128
+
+# Per-kernel memory-side and wave metrics from the counter passes that
+# --summarize-counters reads (each pass a separate rocprofv3 --pmc run of
+# `bench.py --pmc-pass`): (column, formula over per-dispatch medians).
+COUNTER_METRICS = [
+    ("EA read latency (TCC cycles)", lambda m: m["TCC_EA0_RDREQ_LEVEL_sum"] / m["TCC_EA0_RDREQ_sum"]),
+    ("EA write latency (TCC cycles)", lambda m: m["TCC_EA0_WRREQ_LEVEL_sum"] / m["TCC_EA0_WRREQ_sum"]),
+    ("EA reads in flight", lambda m: m["TCC_EA0_RDREQ_LEVEL_sum"] / (m["TCC_CYCLE_sum"] / TCC_CHANNELS)),
+    ("EA writes in flight", lambda m: m["TCC_EA0_WRREQ_LEVEL_sum"] / (m["TCC_CYCLE_sum"] / TCC_CHANNELS)),
+    ("EA write-stall cycles / TCC cycles", lambda m: m["TCC_EA0_WRREQ_STALL_sum"] / m["TCC_CYCLE_sum"]),
+    ("EA read DRAM-credit-stall cycles / TCC cycles",
+     lambda m: m["TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum"] / m["TCC_CYCLE_sum"]),
+    ("TCC busy", lambda m: m["TCC_BUSY_sum"] / m["TCC_CYCLE_sum"]),
+    ("TCP->TCC read latency", lambda m: m["TCP_TCC_READ_REQ_LATENCY_sum"] / m["TCP_TCC_READ_REQ_sum"]),
+    ("TCP->TCC write latency", lambda m: m["TCP_TCC_WRITE_REQ_LATENCY_sum"] / m["TCP_TCC_WRITE_REQ_sum"]),
+    ("waves", lambda m: m["SQ_WAVES"]),
+    ("wave life (cycles)", lambda m: 4 * m["SQ_WAVE_CYCLES"] / m["SQ_WAVES"]),
+    ("wave time waiting", lambda m: m["SQ_WAIT_ANY"] / m["SQ_WAVE_CYCLES"]),
+    ("waves resident (avg)", lambda m: 4 * m["SQ_WAVE_CYCLES"] / (m["TCC_CYCLE_sum"] / TCC_CHANNELS)),
+]
+
+
+# The counter passes (one rocprofv3 run each: at most 4 TCC, 4 TCP and 8 SQ
+# counters per run) and the command that makes each.
+COUNTER_PASSES = {
+    "ea_level": "TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_RDREQ_sum TCC_EA0_WRREQ_LEVEL_sum "
+                "TCC_EA0_WRREQ_sum",
+    "stalls": "TCC_EA0_WRREQ_STALL_sum TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum "
+              "TCC_TOO_MANY_EA_WRREQS_STALL_sum TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum",
+    "tcp_latency": "TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum "
+                   "TCP_TCC_WRITE_REQ_LATENCY_sum TCP_TCC_WRITE_REQ_sum",
+    "busy": "TCC_CYCLE_sum TCC_BUSY_sum GRBM_GUI_ACTIVE",
+    "sq": "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY "
+          "SQ_ACTIVE_INST_VMEM SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR",
+}
+
+
+def counter_pass_command(name, prefix="gpurun_out/pmcx_"):
+    return (f"rocprofv3 --pmc {COUNTER_PASSES[name]} -d {prefix}{name} -o pmc "
+            f"--output-format csv -- python3 bench.py --pmc-pass")
+
+
+def summarize_counters(out_path, title, prefix="gpurun_out/pmcx_"):
+    """Markdown table of COUNTER_METRICS per kernel from the COUNTER_PASSES runs."""
+    dirs = [prefix + n for n in COUNTER_PASSES]
+    commands = [counter_pass_command(n, prefix) for n in COUNTER_PASSES]
+    vals = {}
+    for d in dirs:
+        for r in counter_rows(d):
+            name = r["Kernel_Name"].split("(")[0] if not r["Kernel_Name"].startswith("(") \
+                else r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+            name = name.replace("void ", "").replace("kvx::", "")
+            vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    keep = [k for k in vals if k.startswith(("k_paged", "k_permute", "k_copy16"))]
+    with open(out_path, "w") as f:
+        f.write(f"# {title}\n\n")
+        f.write("Per-dispatch medians of hardware counters, one `rocprofv3 --pmc` run per "
+                "pass of `python3 bench.py --pmc-pass` (the five kernels of the step and "
+                "the plain copy `k_copy16` of 256 MiB, same process).  EA = the L2's "
+                f"requests to memory; *_sum counters add the {TCC_CHANNELS} L2 channels, so "
+                "average per-channel cycles are TCC_CYCLE_sum / "
+                f"{TCC_CHANNELS}; latencies are Little's-law averages (requests in flight "
+                "summed per cycle / requests).\n\n")
+        f.write("Commands (from the repository root, on the GPU box):\n\n")
+        for c in commands:
+            f.write(f"    {c}\n")
+        f.write("\n| metric | " + " | ".join(f"`{k}`" for k in keep) + " |\n")
+        f.write("|---|" + "---:|" * len(keep) + "\n")
+        for label, fn in COUNTER_METRICS:
+            cells = []
+            for k in keep:
+                m = {c: sorted(v)[len(v) // 2] for c, v in vals[k].items()}
+                try:
+                    x = fn(m)
+                    cells.append(f"{x:.3f}" if x < 10 else f"{x:,.0f}")
+                except (KeyError, ZeroDivisionError):
+                    cells.append("-")
+            f.write(f"| {label} | " + " | ".join(cells) + " |\n")
+    print(open(out_path).read())
+
+
 def summarize_trace(trace_dir, out_path, title, command):
     """Markdown summary of a rocprofv3 --kernel-trace --stats run."""
     files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
@@ -1097,6 +1185,10 @@ def main():
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "OUT", "TITLE", "CMD"),
                     help="markdown summary of a rocprofv3 --kernel-trace --stats run")
     ap.add_argument("--pmc-out", default=PMC_SUMMARY, help="where --summarize-pmc writes")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("OUT", "TITLE"),
+                    help="per-kernel memory and wave metrics from the counter passes")
+    ap.add_argument("--counter-commands", action="store_true",
+                    help="print the rocprofv3 command of every counter pass")
     args = ap.parse_args()
 
     if args.summarize_trace:
@@ -1104,6 +1196,13 @@ def main():
         return 0
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_out)
+        return 0
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return 0
+    if args.counter_commands:
+        for n in COUNTER_PASSES:
+            print(counter_pass_command(n))
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
