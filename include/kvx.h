@@ -144,7 +144,8 @@ typedef struct kvx_pool {
  * batch.  tok_off is a DEVICE array of num_reqs + 1 int64 values with
  * tok_off[0] = 0, non-decreasing, tok_off[num_reqs] = total_tokens (a host
  * copy of the last entry, used for sizing the launch).  Empty requests are
- * allowed. */
+ * allowed.  With num_reqs == 1 the kernels take tok_off = {0, total_tokens}
+ * from this contract and do not read it (KVX_VALIDATE=1 still checks it). */
 typedef struct kvx_reqs {
     int32_t num_reqs;       /* >= 0 */
     int64_t total_tokens;   /* >= 0 */

@@ -304,6 +304,18 @@ __device__ __forceinline__ ReqOf request_lookup(const Common& c, const int64_t* 
                                                 const int64_t* pd, int64_t tok0, int64_t tok,
                                                 bool active, int lane) {
     if constexpr (!MANY) {
+        if (c.num_reqs == 1) {
+            // One request: its tokens are [0, T) (tok_off = {0, T} by the call's
+            // contract, not read here) and only the starts of its page lists
+            // are loaded, uniform loads with nothing to wait for first.
+            ReqOf q;
+            q.off = 0;
+            q.end = c.T;
+            q.pg_src = ps != nullptr ? ps[0] : 0;
+            q.pg_dst = pd != nullptr ? pd[0] : 0;
+            q.r = 0;
+            return q;
+        }
         return walk_window<true>(c, load_window(c, ps, pd, 0, lane), ps, pd, tok0, tok, active,
                                  0, c.T);
     } else {
