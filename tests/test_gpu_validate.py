@@ -1,8 +1,9 @@
 """KVX_VALIDATE=1 (debug mode) on the GPU, in a child process (the flag is
 read once per process): valid calls run and match the oracle; a duplicate
 destination row, a source and destination that share rows, and staging laid
-over the pool it reads are refused with their status and nothing is written;
-out-of-range ids stay legal (skipped and counted)."""
+over the pool it reads, and a one-request batch whose tok_off breaks the
+contract are refused with their status and nothing is written; out-of-range
+ids stay legal (skipped and counted)."""
 import os
 import subprocess
 import sys
@@ -93,6 +94,15 @@ kvx.gather_scatter(lay, kvx.Pool(A, S), kvx.Table(d(pg), d(oor)), reqs, kvx.Pool
                    kvx.Table(d(pg), d(dids)), skipped)
 torch.cuda.synchronize()
 assert int(skipped.item()) == Q, int(skipped.item())
+
+# 7. a one-request batch whose tok_off breaks the contract (the kernels take
+#    {{0, total_tokens}} for one request without reading it): refused
+one_req = kvx.Requests(d(np.array([0, 20], np.int64)), 31)
+before = B.clone()
+expect(2, lambda: kvx.gather_scatter(lay, kvx.Pool(A, S), kvx.Table(d(pg[[0, 2]]), d(sids)),
+                                     one_req, kvx.Pool(B, S), kvx.Table(d(pg[[0, 2]]), d(dids))))
+torch.cuda.synchronize()
+assert torch.equal(B, before)
 print("validate ok", flush=True)
 """
 
