@@ -63,7 +63,7 @@ namespace kvx {
 #endif
 #ifndef KVX_XCD_REMAP
 #define KVX_XCD_REMAP 2            // XCD-aware workgroup renumbering: 0 never,
-#endif                             // 1 always, 2 when a launch spans > 16 GiB
+#endif                             // 1 always, 2 by the host's pool-size rules
 
 constexpr int kWave = 64;
 // Waves per workgroup, per kernel family.  Measured (same process,
@@ -286,7 +286,8 @@ __device__ __forceinline__ ReqOf walk_window(const Common& c, const Window& v,
 // Request lookup for lane token `tok` of a chunk starting at tok0 (< T):
 // the chunk's first request is the largest r < num_reqs with
 // tok_off[r] <= tok0.  MANY is false only for batches of at most 64
-// requests, which one window holds whole.
+// requests, which one window holds whole; a batch of one request needs no
+// window at all.
 //
 // With MANY the wave first loads a guessed window: the one starting 32
 // requests before the request that would hold tok0 if all requests had the
