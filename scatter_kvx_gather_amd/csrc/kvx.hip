@@ -196,18 +196,29 @@ constexpr int64_t kResidentWavesPerCu = 32;
 // Rows per chunk for the wide copies (paged rows and permute token rows of
 // 1..16 KiB).  A launch that fits in one round of resident waves at 8 KiB
 // chunks keeps them (every wave runs at once, with the most loads in flight
-// per lane); a larger one moves one row per wave, so that the waves still
-// running when the launch drains are short.  Measured on MI355X (same
-// process, alternating): 8 KiB chunks win below one round (gather of 128
-// 144 KiB tokens: 3610 vs 3373 GB/s; extract of 58.7 MB: 6253 vs 5877),
-// one row per wave wins above it (extract of 470 MB: 5380 -> 5924-6045;
-// rebuild 5414 -> 6192; scatter of 302 MB 5214 -> 5378; fragmented gather of
-// 7 GB 5127 -> 5314; just over one round, extract of 75 MB: 5364 -> 6444).
-uint32_t wide_rows_for(const Shape& sh, int64_t rows, int64_t row_bytes, int cus) {
+// per lane); a larger one moves the fewest rows that make wave_bytes per wave
+// (one row when the row is that large), so that the waves still running when
+// the launch drains are short.  Measured on MI355X (same process,
+// alternating): 8 KiB chunks win below one round (gather of 128 144 KiB
+// tokens: 3610 vs 3373 GB/s; extract of 58.7 MB: 6253 vs 5877), one row per
+// wave wins above it for the permutes (extract of 470 MB: 5380 -> 5924-6045;
+// rebuild 5414 -> 6192; just over one round, extract of 75 MB: 5364 -> 6444)
+// and 2 KiB per wave for the paged ops: 2 KiB rows one per wave (scatter of
+// 302 MB 5214 -> 5378; fragmented gather of 7 GB 5127 -> 5314; two per wave
+// loses 2-4%), 1 KiB rows two per wave (gather-scatter of 537 MB 3866 ->
+// 5192 against one per wave, gather 5092 -> 5791, scatter 5326 -> 5607; four
+// per wave 5185 / 5459 / 5416).
+uint32_t wide_rows_for(const Shape& sh, int64_t rows, int64_t row_bytes, int cus,
+                       int64_t wave_bytes) {
     if (sh.vpl <= 0 || sh.U == 1) return sh.U;
     const int64_t round_bytes = static_cast<int64_t>(cus) * kResidentWavesPerCu * kChunkBytes;
-    return rows * row_bytes > round_bytes ? 1u : sh.U;
+    if (rows * row_bytes <= round_bytes) return sh.U;
+    return row_bytes >= wave_bytes ? 1u : static_cast<uint32_t>(wave_bytes / row_bytes);
 }
+
+// Bytes a wave of a large paged launch moves (see wide_rows_for); permutes
+// move one row per wave.
+constexpr int64_t kPagedWaveBytes = 2048;
 
 // XCD-aware renumbering pays when a launch spans more memory than the
 // translation caches reach: then each XCD, working on ~1/8 of the planes,
@@ -293,8 +304,9 @@ template <class Src, class Dst, bool MANY>
 const void* paged_kernel_of(int vpl, uint32_t U) {
     const bool one = U == 1;
     switch (vpl) {
-        case 1: return one ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, 1, MANY>)
-                           : reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, wide_rows<1>(), MANY>);
+        case 1: return one      ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, 1, MANY>)
+                       : U == 2 ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, 2, MANY>)
+                                : reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, wide_rows<1>(), MANY>);
         case 2: return one ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 2, 1, MANY>)
                            : reinterpret_cast<const void*>(&k_paged<Src, Dst, 2, wide_rows<2>(), MANY>);
         case 4: return one ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 4, 1, MANY>)
@@ -363,7 +375,7 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
     for (int32_t q0 = 0; q0 < g.Q; q0 += kTab) {
         const int32_t nq = g.Q - q0 < kTab ? g.Q - q0 : kTab;
         Shape sh = sh0;
-        sh.U = wide_rows_for(sh0, reqs->total_tokens * nq, g.R, cus);
+        sh.U = wide_rows_for(sh0, reqs->total_tokens * nq, g.R, cus, kPagedWaveBytes);
         PagedArgs<Src, Dst> a;
         std::memset(&a, 0, sizeof(a));
         a.c.tok_off = reqs->tok_off;
@@ -415,7 +427,7 @@ kvx_status run_permute(const Geom& g, void* const* hf, int64_t s_cap, int64_t se
     for (int32_t q0 = 0; q0 < g.Q; q0 += kTab) {
         const int32_t nq = g.Q - q0 < kTab ? g.Q - q0 : kTab;
         Shape sh = sh0;
-        if (rows) sh.U = wide_rows_for(sh0, seq * nq, g.R, cus);
+        if (rows) sh.U = wide_rows_for(sh0, seq * nq, g.R, cus, 0);
         PermuteArgs a;
         std::memset(&a, 0, sizeof(a));
         a.c.T = seq;

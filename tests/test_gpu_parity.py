@@ -141,8 +141,9 @@ def big_case(name, g, lens, src_page, dst_page, seed, oor_frac=0.0):
     return wl.PagedCase(name, g, wl.csr_from_lengths(lens), src, dst, 0, 0, 0)
 
 
-# Launches above 64 MiB each way move one row per wave (below it, 8 KiB
-# chunks): 1, 2 and 4 KiB rows, ragged and empty requests, mixed page sizes.
+# Launches above 64 MiB each way move 2 KiB per wave (below it, 8 KiB
+# chunks): two 1 KiB rows, or one row of 2 or 4 KiB; ragged and empty
+# requests, mixed page sizes.
 BIG = [
     (wl.Geometry(8, 2, 4, 128, "bf16"), [1500, 0, 2333, 1801], 1, 1, 0.0),     # R = 1 KiB
     (wl.Geometry(8, 2, 4, 128, "bf16"), [2600, 2, 2100], 16, 3, 0.02),         # R = 1 KiB
