@@ -31,6 +31,7 @@ and the CPU oracle timed on the host on a bounded sample of the same steps.
   python bench.py --comparators         (per-block runtime copies, DMA copy of staging)
   python bench.py --sizes               (one request of 16 .. 8192 tokens: latency to bandwidth)
   python bench.py --batches             (49152 tokens in 1 .. 49152 requests: request lookup)
+  python bench.py --row-sizes           (rows of 256 B .. 16 KiB at ~256 MiB each way)
   python bench.py --pmc-pass            (short run for rocprofv3 --pmc)
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --pmc-out OUT
   python bench.py --summarize-trace TRACE_DIR OUT TITLE COMMAND
@@ -941,6 +942,57 @@ def batch_sizes(torch, kvx, wl, wdev, dev, stream):
     del A, B, st
 
 
+def row_sizes(torch, kvx, wl, wdev, dev, stream):
+    """Gather-scatter, gather and scatter of about 256 MiB each way at page 1
+    (random slots from seeded permutations, one request, four disjoint tables
+    rotated so that no launch finds its rows in the 256 MiB MALL) for rows of
+    256 B to 16 KiB: the flat, row-loop and wide copies, each beside a plain
+    contiguous copy of the same bytes.  Graph-timed."""
+    import numpy as np
+    target = 256 << 20
+    # (layers, kv_heads, head_dim, dtype): rows of H * D * 2 bytes, 2 planes a layer
+    shapes = [(28, 1, 128, "bf16"), (28, 2, 128, "bf16"), (28, 4, 128, "bf16"),
+              (27, 1, 576, "bf16"), (28, 6, 128, "bf16"), (36, 8, 128, "bf16"),
+              (16, 16, 128, "bf16"), (8, 32, 128, "bf16"), (4, 64, 128, "bf16")]
+    for L, H, D, dt in shapes:
+        g = wl.Geometry(L, 2 if D != 576 else 1, H, D, dt)
+        Q, R = g.planes, g.row_bytes
+        T = max(64, target // (Q * R))
+        NS = 4 * T + 64
+        A = torch.empty((Q, NS, R), dtype=torch.uint8, device=dev)
+        B = torch.empty_like(A)
+        wdev.fill_hash(A, 1, stream=stream)
+        wdev.fill_hash(B, 2, stream=stream)
+        st = torch.empty(T * Q * R, dtype=torch.uint8, device=dev)
+        cp = torch.empty_like(st)
+        rng = np.random.default_rng(3030 + R)
+        tok = np.array([0, T], np.int64)
+
+        def d(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        reqs = kvx.Requests(d(tok), T)
+        ps, pd = rng.permutation(NS), rng.permutation(NS)
+        tabs = [(kvx.Table(d(tok), d(ps[k * T:(k + 1) * T].astype(np.int32))),
+                 kvx.Table(d(tok), d(pd[k * T:(k + 1) * T].astype(np.int32)))) for k in range(4)]
+        lay = kvx.Layout(g.num_layers, g.num_kv, g.kv_heads, g.head_dim, g.dtype)
+        PA, PB = kvx.Pool(A, NS), kvx.Pool(B, NS)
+        nb = 2 * T * Q * R
+        line = {"row_bytes": R, "planes": Q, "tokens": T, "bytes_rw": nb}
+        for op, fn in (("gather_scatter", lambda i: kvx.gather_scatter(
+                           lay, PA, tabs[i % 4][0], reqs, PB, tabs[i % 4][1], stream=stream)),
+                       ("gather", lambda i: kvx.gather(lay, PA, tabs[i % 4][0], reqs, st,
+                                                       stream=stream)),
+                       ("scatter", lambda i: kvx.scatter(lay, st, reqs, PB, tabs[i % 4][1],
+                                                         stream=stream)),
+                       ("plain_copy", lambda i: wdev.copy_bytes(cp, st, st.numel(),
+                                                                stream=stream))):
+            ms = graph_timed(torch, stream, fn, 8)
+            line[op] = {"us": round(ms * 1e3, 1), "GBps": round(nb / (ms * 1e6), 1)}
+        print(json.dumps(line), flush=True)
+        del A, B, st, cp, PA, PB
+        torch.cuda.empty_cache()
+
+
 def comparators(torch, kvx, wl, wdev, dev):
     """The same 2048-token request moved by per-block runtime copies."""
     import ctypes
@@ -1177,6 +1229,8 @@ def main():
                     help="the transfer and a full-intensity reader on complementary CU masks")
     ap.add_argument("--sizes", action="store_true",
                     help="gather-scatter and gather of one request of 16 .. 8192 tokens")
+    ap.add_argument("--row-sizes", action="store_true",
+                    help="~256 MiB each way of rows of 256 B .. 16 KiB (every copy variant)")
     ap.add_argument("--batches", action="store_true",
                     help="49152 tokens split into 1 .. 49152 requests (request lookup cost)")
     ap.add_argument("--comparators", action="store_true",
@@ -1235,6 +1289,9 @@ def main():
         return 0
     if args.batches:
         batch_sizes(torch, kvx, wl, wdev, dev, stream)
+        return 0
+    if args.row_sizes:
+        row_sizes(torch, kvx, wl, wdev, dev, stream)
         return 0
     if args.comparators:
         comparators(torch, kvx, wl, wdev, dev)

@@ -208,12 +208,30 @@ constexpr int64_t kResidentWavesPerCu = 32;
 // loses 2-4%), 1 KiB rows two per wave (gather-scatter of 537 MB 3866 ->
 // 5192 against one per wave, gather 5092 -> 5791, scatter 5326 -> 5607; four
 // per wave 5185 / 5459 / 5416).
+bool above_one_round(int64_t bytes, int cus) {
+    return bytes > static_cast<int64_t>(cus) * kResidentWavesPerCu * kChunkBytes;
+}
+
 uint32_t wide_rows_for(const Shape& sh, int64_t rows, int64_t row_bytes, int cus,
                        int64_t wave_bytes) {
     if (sh.vpl <= 0 || sh.U == 1) return sh.U;
-    const int64_t round_bytes = static_cast<int64_t>(cus) * kResidentWavesPerCu * kChunkBytes;
-    if (rows * row_bytes <= round_bytes) return sh.U;
+    if (!above_one_round(rows * row_bytes, cus)) return sh.U;
     return row_bytes >= wave_bytes ? 1u : static_cast<uint32_t>(wave_bytes / row_bytes);
+}
+
+// Paged rows of 4, 8 or 16 KiB in a launch above one round move as 2 KiB
+// pieces (k_paged_sub): log2 of the pieces per row, 0 for whole rows (and when
+// the launch's piece count would not fit the chunk index).  Measured (same process,
+// the same bytes moved as 2 KiB rows against whole rows, 256 MiB each way):
+// 4 KiB rows gather-scatter 4815 -> 5274 GB/s, gather 6543 -> 6756, scatter
+// 5172 -> 5427; 8 KiB rows 4966 -> 5169, 6473 -> 6702, 5252 -> 5516; 16 KiB
+// rows 4965 -> 5081, 6432 -> 6648, 5250 -> 5377.
+uint32_t sub_shift_for(const Shape& sh, int64_t tokens, int32_t nq, int64_t row_bytes,
+                       int cus) {
+    if (sh.vpl < 4 || !above_one_round(tokens * nq * row_bytes, cus)) return 0;
+    const uint32_t shift = sh.vpl == 4 ? 1u : (sh.vpl == 8 ? 2u : 3u);
+    const uint64_t chunks = (static_cast<uint64_t>(tokens) << shift) * static_cast<uint64_t>(nq);
+    return chunks < (uint64_t(1) << 31) ? shift : 0u;
 }
 
 // Bytes a wave of a large paged launch moves (see wide_rows_for); permutes
@@ -331,6 +349,12 @@ const void* paged_kernel(int vpl, uint32_t U, int32_t num_reqs) {
                             : paged_kernel_of<Src, Dst, false>(vpl, U);
 }
 
+template <class Src, class Dst>
+const void* paged_sub_kernel(int32_t num_reqs) {
+    return num_reqs > kWave ? reinterpret_cast<const void*>(&k_paged_sub<Src, Dst, true>)
+                            : reinterpret_cast<const void*>(&k_paged_sub<Src, Dst, false>);
+}
+
 template <int KT>
 const void* heads_hnd_kernel(bool many) {
     return many ? reinterpret_cast<const void*>(&k_heads_hnd<KT, true>)
@@ -376,6 +400,8 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
         const int32_t nq = g.Q - q0 < kTab ? g.Q - q0 : kTab;
         Shape sh = sh0;
         sh.U = wide_rows_for(sh0, reqs->total_tokens * nq, g.R, cus, kPagedWaveBytes);
+        const uint32_t sub = sub_shift_for(sh0, reqs->total_tokens, nq, g.R, cus);
+        if (sub > 0) sh = {2, 1};                 // one 2 KiB piece per chunk
         PagedArgs<Src, Dst> a;
         std::memset(&a, 0, sizeof(a));
         a.c.tok_off = reqs->tok_off;
@@ -387,7 +413,8 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
         a.c.q0 = q0;
         a.c.Q = g.Q;
         a.c.R = static_cast<int32_t>(g.R);
-        if (!set_chunks(&a.c, sh, static_cast<uint32_t>(reqs->total_tokens), nq))
+        a.c.sub_shift = sub;
+        if (!set_chunks(&a.c, sh, static_cast<uint32_t>(reqs->total_tokens << sub), nq))
             return KVX_E_RANGE;
         if constexpr (std::is_same<Src, PoolRef>::value) fill_pool_ref(&a.src, src, st, q0, nq);
         else a.src.base = static_cast<char*>(src_stage);
@@ -400,12 +427,14 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
         if (log_enabled())
             std::fprintf(stderr,
                          "kvx: %s Q=%d planes[%d,%d) R=%lld T=%lld reqs=%d copy=%s U=%u "
-                         "chunks=%u grid=%u remap=%u\n",
+                         "pieces/row=%u chunks=%u grid=%u remap=%u\n",
                          op_name(op), g.Q, q0, q0 + nq, static_cast<long long>(g.R),
                          static_cast<long long>(reqs->total_tokens), reqs->num_reqs,
                          sh.vpl > 0 ? "wide" : (sh.vpl < 0 ? "row-loop" : "flat"), sh.U,
-                         a.c.nchunks, grid, a.c.remap);
-        s = launch(paged_kernel<Src, Dst>(sh.vpl, sh.U, a.c.num_reqs), grid, kPagedWaves, a, stream);
+                         1u << sub, a.c.nchunks, grid, a.c.remap);
+        const void* fn = sub > 0 ? paged_sub_kernel<Src, Dst>(a.c.num_reqs)
+                                 : paged_kernel<Src, Dst>(sh.vpl, sh.U, a.c.num_reqs);
+        s = launch(fn, grid, kPagedWaves, a, stream);
         if (s != KVX_OK) return s;
     }
     return KVX_OK;

@@ -101,6 +101,7 @@ struct Common {
     uint32_t V;                 // 16-byte vectors per unit
     uint32_t v_magic;           // ceil(2^32 / V)
     uint32_t remap;             // 1: XCD-aware workgroup renumbering
+    uint32_t sub_shift;         // k_paged_sub: log2 of the 2 KiB pieces of a row
     double req_rate;            // paged: num_reqs / T (requests per token)
 };
 
@@ -704,6 +705,39 @@ void k_paged(PagedArgs<Src, Dst> a) {
         if constexpr (VPL > 0) copy_wide<VPL, U, nts>(s, d, code, lane);
         else if constexpr (VPL < 0) copy_rows<-VPL, U, nts>(a.c, s, d, code, lane);
         else copy_flat<nts>(a.c, s, d, code, lane);
+    }
+    count_skips(a.c.skipped, nskip, lane);
+}
+
+// Rows of 4..16 KiB in launches above one round of resident waves, moved as
+// 2 KiB pieces: unit j of a plane is piece j & (2^sub_shift - 1) of batch
+// token j >> sub_shift, one unit per wave, so the pieces of a row run on
+// adjacent waves.  A skipped row is counted once, by its first piece.
+template <class Src, class Dst, bool MANY>
+__global__ __launch_bounds__(kWave * kPagedWaves)
+__attribute__((amdgpu_waves_per_eu(many_waves(MANY, true))))
+void k_paged_sub(PagedArgs<Src, Dst> a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t nwaves = gridDim.x * kPagedWaves;
+    const uint32_t last = (1u << a.c.sub_shift) - 1u;
+    unsigned long long nskip = 0;
+    for (uint32_t chunk = wave_id<kPagedWaves>(a.c); chunk < a.c.nchunks; chunk += nwaves) {
+        const uint32_t ql = chunk / a.c.chunks_per_plane;
+        const uint32_t j = chunk - ql * a.c.chunks_per_plane;
+        PagedChunk k;
+        k.ql = static_cast<int32_t>(ql);
+        k.tok0 = static_cast<int64_t>(j >> a.c.sub_shift);
+        const uint32_t piece = j & last;
+        uint64_t s = 0, d = 0;
+        int code = resolve<MANY>(a, k, static_cast<uint32_t>(lane), s, d);
+        if (code == kCopy) {
+            s += static_cast<uint64_t>(piece) * 2048u;
+            d += static_cast<uint64_t>(piece) * 2048u;
+        } else if (code == kSkip && piece != 0) {
+            code = kNone;
+        }
+        nskip += __popcll(__ballot(code == kSkip));
+        copy_wide<2, 1, std::is_same<Dst, PoolRef>::value>(s, d, code, lane);
     }
     count_skips(a.c.skipped, nskip, lane);
 }

@@ -142,13 +142,17 @@ def big_case(name, g, lens, src_page, dst_page, seed, oor_frac=0.0):
 
 
 # Launches above 64 MiB each way move 2 KiB per wave (below it, 8 KiB
-# chunks): two 1 KiB rows, or one row of 2 or 4 KiB; ragged and empty
-# requests, mixed page sizes.
+# chunks): two 1 KiB rows, one 2 KiB row, or a 2 KiB piece of a 4, 8 or
+# 16 KiB row (a skipped row counted once); ragged and empty requests, mixed
+# page sizes, out-of-range ids.
 BIG = [
     (wl.Geometry(8, 2, 4, 128, "bf16"), [1500, 0, 2333, 1801], 1, 1, 0.0),     # R = 1 KiB
     (wl.Geometry(8, 2, 4, 128, "bf16"), [2600, 2, 2100], 16, 3, 0.02),         # R = 1 KiB
     (wl.Geometry(4, 2, 8, 128, "bf16"), [3000, 1700, 7], 1, 16, 0.02),         # R = 2 KiB
     (wl.Geometry(2, 2, 16, 128, "bf16"), [2100, 1, 2500], 16, 16, 0.0),        # R = 4 KiB
+    (wl.Geometry(2, 2, 16, 128, "bf16"), [1900, 0, 2700], 1, 2, 0.03),         # R = 4 KiB
+    (wl.Geometry(1, 2, 32, 128, "bf16"), [3200, 1000, 17], 16, 3, 0.02),       # R = 8 KiB
+    (wl.Geometry(1, 1, 64, 128, "bf16"), [2500, 2000, 5], 1, 1, 0.0),          # R = 16 KiB
 ]
 
 
@@ -168,6 +172,7 @@ BIG_MANY = [
     (wl.Geometry(4, 2, 8, 128, "bf16"), 6000, 6, 0.3, 1, 1, 0.0),       # R = 2 KiB, ragged
     (wl.Geometry(8, 2, 4, 128, "bf16"), 3000, 12, 0.2, 16, 3, 0.02),    # R = 1 KiB
     (wl.Geometry(2, 2, 16, 128, "bf16"), 70000, 1, 0.6, 1, 2, 0.0),     # R = 4 KiB, 2 search rounds
+    (wl.Geometry(1, 2, 32, 128, "bf16"), 5000, 6, 0.3, 2, 1, 0.02),     # R = 8 KiB
 ]
 
 
