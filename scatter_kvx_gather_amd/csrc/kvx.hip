@@ -222,10 +222,10 @@ uint32_t wide_rows_for(const Shape& sh, int64_t rows, int64_t row_bytes, int cus
 // Paged rows of 4, 8 or 16 KiB in a launch above one round move as 2 KiB
 // pieces (k_paged_sub): log2 of the pieces per row, 0 for whole rows (and when
 // the launch's piece count would not fit the chunk index).  Measured (same process,
-// the same bytes moved as 2 KiB rows against whole rows, 256 MiB each way):
-// 4 KiB rows gather-scatter 4815 -> 5274 GB/s, gather 6543 -> 6756, scatter
-// 5172 -> 5427; 8 KiB rows 4966 -> 5169, 6473 -> 6702, 5252 -> 5516; 16 KiB
-// rows 4965 -> 5081, 6432 -> 6648, 5250 -> 5377.
+// alternating, whole rows against pieces, 256 MiB each way, page 1): 4 KiB
+// rows gather-scatter 4830 -> 5205 GB/s, gather 6547 -> 6654, scatter 5175 ->
+// 5321; 8 KiB rows 4984 -> 5152, 6498 -> 6710, 5269 -> 5463; 16 KiB rows
+// 5009 -> 5081, 6427 -> 6717, 5223 -> 5414.
 uint32_t sub_shift_for(const Shape& sh, int64_t tokens, int32_t nq, int64_t row_bytes,
                        int cus) {
     if (sh.vpl < 4 || !above_one_round(tokens * nq * row_bytes, cus)) return 0;
