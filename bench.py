@@ -323,12 +323,12 @@ def summarize_pmc(fetch_dir, write_dir, out_path):
         f.write("Two `rocprofv3 --pmc` runs of `python bench.py --pmc-pass` (one counter each);\n")
         f.write("median per dispatch, scaled by the plain copy kernel `k_copy16` of\n")
         f.write(f"{COPY_CALIB_BYTES} bytes run in the same process.\n\n")
-        f.write("Commands (from the repository root, on the GPU box):\n\n")
-        f.write("    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o pmc --output-format csv "
+        f.write("Commands (from the repository root, on an MI355X machine):\n\n")
+        f.write("    rocprofv3 --pmc FETCH_SIZE -d rocprof_out/pmc_fetch -o pmc --output-format csv "
                 "-- python3 bench.py --pmc-pass\n")
-        f.write("    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o pmc --output-format csv "
+        f.write("    rocprofv3 --pmc WRITE_SIZE -d rocprof_out/pmc_write -o pmc --output-format csv "
                 "-- python3 bench.py --pmc-pass\n")
-        f.write("    python3 bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write "
+        f.write("    python3 bench.py --summarize-pmc rocprof_out/pmc_fetch rocprof_out/pmc_write "
                 "--pmc-out profiles/kv144k_2048tok_page1_hbm_traffic.md\n\n")
         f.write(f"- kernel: `{kname}`\n")
         f.write(f"- fetch_kib_per_dispatch: {f_kib:.1f}\n")
@@ -1137,12 +1137,12 @@ COUNTER_PASSES = {
 }
 
 
-def counter_pass_command(name, prefix="gpurun_out/pmcx_"):
+def counter_pass_command(name, prefix="rocprof_out/pmcx_"):
     return (f"rocprofv3 --pmc {COUNTER_PASSES[name]} -d {prefix}{name} -o pmc "
             f"--output-format csv -- python3 bench.py --pmc-pass")
 
 
-def summarize_counters(out_path, title, prefix="gpurun_out/pmcx_"):
+def summarize_counters(out_path, title, prefix="rocprof_out/pmcx_"):
     """Markdown table of COUNTER_METRICS per kernel from the COUNTER_PASSES runs."""
     dirs = [prefix + n for n in COUNTER_PASSES]
     commands = [counter_pass_command(n, prefix) for n in COUNTER_PASSES]
@@ -1164,7 +1164,7 @@ def summarize_counters(out_path, title, prefix="gpurun_out/pmcx_"):
                 "average per-channel cycles are TCC_CYCLE_sum / "
                 f"{TCC_CHANNELS}; latencies are Little's-law averages (requests in flight "
                 "summed per cycle / requests).\n\n")
-        f.write("Commands (from the repository root, on the GPU box):\n\n")
+        f.write("Commands (from the repository root, on an MI355X machine):\n\n")
         for c in commands:
             f.write(f"    {c}\n")
         f.write("\n| metric | " + " | ".join(f"`{k}`" for k in keep) + " |\n")
@@ -1195,7 +1195,7 @@ def summarize_trace(trace_dir, out_path, title, command):
     with open(out_path, "w") as f:
         f.write(f"# {title}\n\n")
         f.write("Kernel durations from `rocprofv3 --kernel-trace --stats` (microseconds).\n\n")
-        f.write("Command (from the repository root, on the GPU box):\n\n")
+        f.write("Command (from the repository root, on an MI355X machine):\n\n")
         f.write(f"    {command}\n\n")
         f.write("| kernel | calls | avg us | min us | max us | share % |\n")
         f.write("|---|---:|---:|---:|---:|---:|\n")
