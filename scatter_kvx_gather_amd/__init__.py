@@ -151,6 +151,34 @@ def _on_device(*args) -> None:
                                  f"{a.device} tensor of shape {tuple(a.shape)}")
 
 
+def _dense(what: str, t) -> None:
+    """The library addresses a buffer from its base pointer and byte count,
+    so a strided view would be read or written as if it were contiguous (and
+    the bytes between its elements overwritten): refuse it."""
+    if isinstance(t, torch.Tensor) and not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous tensor (got strides {t.stride()} "
+                         f"for shape {tuple(t.shape)})")
+
+
+def _planes_dense(what: str, planes) -> None:
+    """Each plane of a tensor whose first dimension indexes planes, or each
+    tensor of a plane list, must be contiguous."""
+    if isinstance(planes, torch.Tensor):
+        if planes.dim() > 0 and planes.shape[0] > 0:
+            _dense(f"each plane of {what}", planes[0])
+    elif isinstance(planes, (list, tuple)):
+        for p in planes:
+            _dense(f"each plane of {what}", p)
+
+
+def _counter(skipped) -> None:
+    if skipped is None or isinstance(skipped, int):
+        return
+    if skipped.dtype not in (torch.int64, torch.uint64) or skipped.numel() < 1:
+        raise ValueError("skipped must be a tensor of at least one int64 or uint64 element "
+                         "(the library adds to its first element)")
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -212,6 +240,7 @@ class Pool:
             if row_bytes is None:
                 if not isinstance(planes, torch.Tensor):
                     raise ValueError("slot_stride or row_bytes is needed for pointer lists")
+                _planes_dense("a pool tensor (pass slot_stride for strided slots)", planes)
                 slots = num_pages * page_size
                 if slots <= 0:
                     raise ValueError("an empty pool needs an explicit slot_stride")
@@ -228,6 +257,7 @@ class Requests:
     def __init__(self, tok_off: torch.Tensor, total_tokens: int):
         if tok_off.dtype != torch.int64 or tok_off.dim() != 1:
             raise ValueError("tok_off must be a 1-D int64 tensor")
+        _dense("tok_off", tok_off)
         self.tok_off = tok_off
         self.num_reqs = tok_off.numel() - 1
         self.total_tokens = int(total_tokens)
@@ -240,6 +270,8 @@ class Table:
     def __init__(self, pg_off: torch.Tensor, page_ids: torch.Tensor):
         if pg_off.dtype != torch.int64 or page_ids.dtype != torch.int32:
             raise ValueError("pg_off must be int64 and page_ids int32")
+        _dense("pg_off", pg_off)
+        _dense("page_ids", page_ids)
         self.pg_off, self.page_ids = pg_off, page_ids
         self._c = _CTable(_ptr(pg_off), _ptr(page_ids) if page_ids.numel() else 0,
                           page_ids.numel())
@@ -260,6 +292,8 @@ class Heads:
 def gather(layout: Layout, src: Pool, src_table: Table, reqs: Requests, staging: torch.Tensor,
            skipped: Optional[torch.Tensor] = None, stream=None) -> None:
     """Pool -> contiguous staging [request][plane][token][H][D] (kvx_gather)."""
+    _dense("staging", staging)
+    _counter(skipped)
     _on_device(src, src_table, reqs, staging, skipped)
     lib = load_library()
     _check(lib.kvx_gather(ctypes.byref(layout._c), ctypes.byref(src._c),
@@ -270,6 +304,8 @@ def gather(layout: Layout, src: Pool, src_table: Table, reqs: Requests, staging:
 def scatter(layout: Layout, staging: torch.Tensor, reqs: Requests, dst: Pool, dst_table: Table,
             skipped: Optional[torch.Tensor] = None, stream=None) -> None:
     """Contiguous staging -> pool (kvx_scatter)."""
+    _dense("staging", staging)
+    _counter(skipped)
     _on_device(staging, reqs, dst, dst_table, skipped)
     lib = load_library()
     _check(lib.kvx_scatter(ctypes.byref(layout._c), _ptr(staging), _nbytes(staging),
@@ -282,6 +318,7 @@ def gather_scatter(layout: Layout, src: Pool, src_table: Table, reqs: Requests, 
                    dst_table: Table, skipped: Optional[torch.Tensor] = None,
                    stream=None) -> None:
     """Pool -> pool, row by row, no staging (kvx_gather_scatter)."""
+    _counter(skipped)
     _on_device(src, src_table, reqs, dst, dst_table, skipped)
     lib = load_library()
     _check(lib.kvx_gather_scatter(ctypes.byref(layout._c), ctypes.byref(src._c),
@@ -296,6 +333,7 @@ def gather_scatter_heads(layout: Layout, src: Pool, src_table: Table, src_heads:
     """Pool -> pool, layout.kv_heads heads of every token row, from heads
     src_heads.head0.. to dst_heads.head0.. (kvx_gather_scatter_heads).  The
     pools' slot_stride is the bytes of one token row in that pool."""
+    _counter(skipped)
     _on_device(src, src_table, reqs, dst, dst_table, skipped)
     lib = load_library()
     _check(lib.kvx_gather_scatter_heads(ctypes.byref(layout._c), ctypes.byref(src._c),
@@ -309,6 +347,8 @@ def gather_scatter_heads(layout: Layout, src: Pool, src_table: Table, src_heads:
 def extract_permute(layout: Layout, hf_planes: Union[torch.Tensor, Sequence], s_cap: int,
                     seq_len: int, out: torch.Tensor, stream=None) -> None:
     """[1, H, s_cap, D] per plane -> out [Q][seq_len][H][D] (kvx_extract_permute)."""
+    _planes_dense("hf_planes", hf_planes)
+    _dense("out", out)
     _on_device(hf_planes, out)
     lib = load_library()
     arr = _plane_array(hf_planes)
@@ -321,6 +361,8 @@ def extract_permute(layout: Layout, hf_planes: Union[torch.Tensor, Sequence], s_
 def rebuild_permute(layout: Layout, flat: torch.Tensor, seq_len: int,
                     hf_planes: Union[torch.Tensor, Sequence], s_cap: int, stream=None) -> None:
     """flat [Q][seq_len][H][D] -> [1, H, s_cap, D] per plane (kvx_rebuild_permute)."""
+    _dense("flat", flat)
+    _planes_dense("hf_planes", hf_planes)
     _on_device(flat, hf_planes)
     lib = load_library()
     arr = _plane_array(hf_planes)

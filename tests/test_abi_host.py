@@ -295,3 +295,41 @@ def test_binding_refuses_host_tensors():
         kvx.extract_permute(lay, torch.zeros((2, 16), dtype=torch.uint8), 1, 1, st)
     with pytest.raises(ValueError, match="device tensors"):
         kvx.rebuild_permute(lay, st, 1, [torch.zeros(16, dtype=torch.uint8)] * 2, 1)
+
+
+def test_binding_refuses_strided_views():
+    """The library takes a buffer as base pointer plus byte count, so the
+    binding refuses strided views (their elements are not the contiguous
+    bytes the kernels would write) and a skip counter it cannot add to."""
+    import torch
+    lay = kvx.Layout(1, 2, 1, 8, "bf16")
+    pool = kvx.Pool(torch.zeros((2, 4, 16), dtype=torch.uint8), 4)
+    tab = kvx.Table(torch.zeros(2, dtype=torch.int64), torch.zeros(2, dtype=torch.int32))
+    reqs = kvx.Requests(torch.tensor([0, 2], dtype=torch.int64), 2)
+    st = torch.zeros(64, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="tok_off must be a contiguous"):
+        kvx.Requests(torch.zeros(6, dtype=torch.int64)[::2], 0)
+    with pytest.raises(ValueError, match="pg_off must be a contiguous"):
+        kvx.Table(torch.zeros(4, dtype=torch.int64)[::2], torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="page_ids must be a contiguous"):
+        kvx.Table(torch.zeros(2, dtype=torch.int64), torch.zeros(4, dtype=torch.int32)[::2])
+    with pytest.raises(ValueError, match="each plane of a pool tensor"):
+        kvx.Pool(torch.zeros((4, 2, 16), dtype=torch.uint8).transpose(0, 1), 4)
+    # an explicit slot stride describes a strided (token-major) pool: accepted
+    kvx.Pool(torch.zeros((4, 2, 16), dtype=torch.uint8).transpose(0, 1), 4, slot_stride=32)
+    strided = torch.zeros(128, dtype=torch.uint8)[::2]
+    with pytest.raises(ValueError, match="staging must be a contiguous"):
+        kvx.gather(lay, pool, tab, reqs, strided)
+    with pytest.raises(ValueError, match="staging must be a contiguous"):
+        kvx.scatter(lay, strided, reqs, pool, tab)
+    with pytest.raises(ValueError, match="out must be a contiguous"):
+        kvx.extract_permute(lay, torch.zeros((2, 16), dtype=torch.uint8), 1, 1, strided)
+    with pytest.raises(ValueError, match="flat must be a contiguous"):
+        kvx.rebuild_permute(lay, strided, 1, torch.zeros((2, 16), dtype=torch.uint8), 1)
+    with pytest.raises(ValueError, match="each plane of hf_planes"):
+        kvx.extract_permute(lay, torch.zeros((16, 2), dtype=torch.uint8).t(), 1, 1, st)
+    with pytest.raises(ValueError, match="skipped must be"):
+        kvx.gather(lay, pool, tab, reqs, st, skipped=torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="skipped must be"):
+        kvx.gather_scatter(lay, pool, tab, reqs, pool, tab,
+                           skipped=torch.zeros(0, dtype=torch.int64))
