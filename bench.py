@@ -520,6 +520,44 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps, cpu=True):
         del A, B, st, PA, PB
         torch.cuda.empty_cache()
 
+        # 2, token-major pools: plane q of slot s at (s * Q + q) * R, so a
+        # slot's rows of all planes are one 144 KiB run (token-major chunk order)
+        Q = g.planes
+        A = torch.empty((32768, Q, R), dtype=torch.uint8, device=dev)
+        B = torch.empty((32768, Q, R), dtype=torch.uint8, device=dev)
+        wdev.fill_hash(A, 1, stream=stream)
+        wdev.fill_hash(B, 2, stream=stream)
+        st = torch.empty(2048 * g.token_bytes, dtype=torch.uint8, device=dev)
+        PA = kvx.Pool([A.data_ptr() + q * R for q in range(Q)], 32768, 1, slot_stride=Q * R)
+        PB = kvx.Pool([B.data_ptr() + q * R for q in range(Q)], 32768, 1, slot_stride=Q * R)
+        PA._keep, PB._keep = A, B
+        hA, hB = A.cpu().numpy().reshape(-1), B.cpu().numpy().reshape(-1)
+        pa, pb = [hA[q * R:] for q in range(k)], [hB[q * R:] for q in range(k)]
+        hst = np.zeros(2048 * k * R, np.uint8)
+        smp = f"{k} of {Q} planes, the 16 requests rotated"
+        cpu_gs = cpu_rate(lambda i: oracle.gather_scatter(
+            pa, Q * R, 1, 32768, cs[i % NREQ].src.pg_off, cs[i % NREQ].src.ids, R, cs[0].tok_off,
+            pb, Q * R, 1, 32768, cs[i % NREQ].dst.pg_off, cs[i % NREQ].dst.ids, nt), nbk, smp)
+        cpu_g = cpu_rate(lambda i: oracle.gather(
+            pa, Q * R, 1, 32768, R, cs[0].tok_off, cs[i % NREQ].src.pg_off, cs[i % NREQ].src.ids,
+            hst, nt), nbk, smp)
+        cpu_s = cpu_rate(lambda i: oracle.scatter(
+            hst, R, cs[0].tok_off, cs[i % NREQ].dst.pg_off, cs[i % NREQ].dst.ids, pb, Q * R, 1,
+            32768, nt), nbk, smp)
+        del pa, pb, hA, hB, hst
+        name = "kv144k_2048tok_page1_token_major"
+        emit(name, "gather_scatter", timed(lambda i: kvx.gather_scatter(
+            lay, PA, tabs[i % NREQ][0], reqs, PB, tabs[i % NREQ][1], stream=stream), reps * 4), nb,
+             "token-major pools (a slot's 72 rows contiguous)", rot=NREQ, oracle_cpu=cpu_gs)
+        emit(name, "gather", timed(lambda i: kvx.gather(
+            lay, PA, tabs[i % NREQ][0], reqs, st, stream=stream), reps * 4), nb,
+             "token-major pool", rot=NREQ, oracle_cpu=cpu_g)
+        emit(name, "scatter", timed(lambda i: kvx.scatter(
+            lay, st, reqs, PB, tabs[i % NREQ][1], stream=stream), reps * 4), nb,
+             "token-major pool", rot=NREQ, oracle_cpu=cpu_s)
+        del A, B, st, PA, PB
+        torch.cuda.empty_cache()
+
         # 3: 32 fragmented requests, one batched gather
         c = wl.config3()
         g = c.geom

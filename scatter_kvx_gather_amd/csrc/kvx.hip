@@ -262,10 +262,47 @@ uint32_t remap_for(double span_bytes, double threshold = kRemapSpanBytes) {
     return span_bytes > threshold ? 1u : 0u;
 }
 
-// Bytes of the nq planes of a pool that a launch may touch.
-double pool_span(const kvx_pool* p, int32_t nq) {
-    return static_cast<double>(p->num_pages) * p->page_size * static_cast<double>(p->slot_stride) *
-           nq;
+// Lowest and highest base address among planes q0 .. q0 + nq - 1 of a pool.
+void plane_range(const kvx_pool* p, int32_t q0, int32_t nq, uintptr_t* lo, uintptr_t* hi) {
+    *lo = *hi = reinterpret_cast<uintptr_t>(p->planes[q0]);
+    for (int32_t q = q0 + 1; q < q0 + nq; ++q) {
+        const uintptr_t b = reinterpret_cast<uintptr_t>(p->planes[q]);
+        *lo = b < *lo ? b : *lo;
+        *hi = b > *hi ? b : *hi;
+    }
+}
+
+// Bytes of planes q0 .. q0 + nq - 1 of a pool that a launch may touch: nq
+// planes of num_slots * slot_stride bytes, or less when the planes overlap
+// (a token-major pool, whose planes interleave slot by slot), where the
+// planes' own address range is the bound.
+double pool_span(const kvx_pool* p, int32_t q0, int32_t nq) {
+    const double plane = static_cast<double>(p->num_pages) * p->page_size *
+                         static_cast<double>(p->slot_stride);
+    uintptr_t lo = 0, hi = 0;
+    plane_range(p, q0, nq, &lo, &hi);
+    const double range = static_cast<double>(hi - lo) + plane;
+    return range < plane * nq ? range : plane * nq;
+}
+
+// True when every plane base of the launch lies within one slot stride of
+// the others: the rows of one slot in all planes then form one run of about
+// slot_stride bytes (a token-major pool).  The paged kernels take
+// token-major chunk order when the pool they write is such a pool, or, in a
+// pool-to-pool copy, when either pool is.  Measured on the 2048-token,
+// 144 KiB/token request with token-major 4.5 GiB pools (same process, the
+// two orders alternating launch by launch, GB/s plane-major -> token-major,
+// both with XCD renumbering): gather-scatter 4777 -> 5422, scatter 5135 ->
+// 5393, gather from such a pool into staging 6554 -> 6495 (so a gather
+// keeps plane-major order); token-major source into a layer-major pool
+// 4869 -> 5151, and the reverse 4850 -> 5300.  With both sides
+// layer-major, plane-major order is the faster one (five-op step 5902 vs
+// 5706).
+bool slot_interleaved(const kvx_pool* p, int32_t q0, int32_t nq) {
+    if (p == nullptr || nq < 2) return false;
+    uintptr_t lo = 0, hi = 0;
+    plane_range(p, q0, nq, &lo, &hi);
+    return static_cast<int64_t>(hi - lo) < p->slot_stride;
 }
 
 // Paged ops only: rows of 512 B .. 16 KiB that are not a power-of-two number
@@ -421,17 +458,27 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
         if constexpr (std::is_same<Dst, PoolRef>::value) fill_pool_ref(&a.dst, dst, dt, q0, nq);
         else a.dst.base = static_cast<char*>(dst_stage);
         a.c.remap = src != nullptr && dst != nullptr
-                        ? remap_for(pool_span(src, nq) + pool_span(dst, nq))
-                        : remap_for(pool_span(src != nullptr ? src : dst, nq), kRemapOnePoolBytes);
+                        ? remap_for(pool_span(src, q0, nq) + pool_span(dst, q0, nq))
+                        : remap_for(pool_span(src != nullptr ? src : dst, q0, nq),
+                                    kRemapOnePoolBytes);
+        a.c.tmajor = sub == 0 && (slot_interleaved(dst, q0, nq) ||
+                                  (dst != nullptr && slot_interleaved(src, q0, nq)))
+                         ? 1u : 0u;
+        // token-major order renumbers at any size, so that each XCD takes whole
+        // tokens' runs rather than every eighth row of each: measured on the
+        // token-major 4.5 GiB pools (alternating launch by launch), gather-
+        // scatter 5310 -> 5419 GB/s, scatter 5368 -> 5415
+        if (a.c.tmajor && KVX_XCD_REMAP != 0) a.c.remap = 1;
         const uint32_t grid = grid_for(a.c.nchunks, cus, kPagedWaves);
         if (log_enabled())
             std::fprintf(stderr,
                          "kvx: %s Q=%d planes[%d,%d) R=%lld T=%lld reqs=%d copy=%s U=%u "
-                         "pieces/row=%u chunks=%u grid=%u remap=%u\n",
+                         "pieces/row=%u chunks=%u grid=%u remap=%u order=%s\n",
                          op_name(op), g.Q, q0, q0 + nq, static_cast<long long>(g.R),
                          static_cast<long long>(reqs->total_tokens), reqs->num_reqs,
                          sh.vpl > 0 ? "wide" : (sh.vpl < 0 ? "row-loop" : "flat"), sh.U,
-                         1u << sub, a.c.nchunks, grid, a.c.remap);
+                         1u << sub, a.c.nchunks, grid, a.c.remap,
+                         a.c.tmajor ? "token-major" : "plane-major");
         const void* fn = sub > 0 ? paged_sub_kernel<Src, Dst>(a.c.num_reqs)
                                  : paged_kernel<Src, Dst>(sh.vpl, sh.U, a.c.num_reqs);
         s = launch(fn, grid, kPagedWaves, a, stream);
@@ -585,7 +632,7 @@ kvx_status run_heads(const Geom& g, const kvx_reqs* reqs, const kvx_pool* src,
         a.Ut = Ut;
         a.hblocks = hblocks;
         a.head_major = (a.hs.hnd && a.hd.hnd) ? 1 : 0;
-        a.c.remap = remap_for(pool_span(src, nq) + pool_span(dst, nq));
+        a.c.remap = remap_for(pool_span(src, q0, nq) + pool_span(dst, q0, nq));
         if (kt > 0) a.c.U = static_cast<uint32_t>(Ut);
         const uint32_t grid = grid_for(a.c.nchunks, cus, kPagedWaves);
         if (log_enabled())

@@ -31,11 +31,13 @@
 // store nothing, so the loads carry no branches.
 //
 // Waves grid-stride over the chunks (by default the grid has one wave per
-// chunk; the host can cap it at a few workgroups per compute unit).  In
-// launches over large pools, workgroup ids are renumbered so that
-// consecutive chunks (the same plane, adjacent tokens) run on the same XCD:
-// gfx950 deals workgroups to its 8 XCDs round-robin, and each XCD has its
-// own L2 and translation caches.  Batches of more than 64 requests run
+// chunk; the host can cap it at a few workgroups per compute unit).  Chunks
+// are numbered plane-major, or token-major when a pool the call writes keeps
+// a token's rows of all planes in one contiguous run (see paged_chunk).  In
+// launches over large pools, and in token-major order, workgroup ids are
+// renumbered so that consecutive chunks run on the same XCD: gfx950 deals
+// workgroups to its 8 XCDs round-robin, and each XCD has its own L2 and
+// translation caches.  Batches of more than 64 requests run
 // separate instances of the paged and head kernels (template flag MANY),
 // whose request lookup first finds the right 64-request window.
 //
@@ -102,6 +104,7 @@ struct Common {
     uint32_t v_magic;           // ceil(2^32 / V)
     uint32_t remap;             // 1: XCD-aware workgroup renumbering
     uint32_t sub_shift;         // k_paged_sub: log2 of the 2 KiB pieces of a row
+    uint32_t tmajor;            // paged: 1 = token-major chunk order (see paged_chunk)
     double req_rate;            // paged: num_reqs / T (requests per token)
 };
 
@@ -190,8 +193,22 @@ struct PagedChunk {
     int32_t ql;     // plane within this launch
 };
 
+// Chunk order.  Plane-major (chunk = plane * chunks_per_plane + token block)
+// keeps the waves in flight on a few planes at a time.  Token-major (chunk =
+// token block * planes + plane) puts the planes of a token block on adjacent
+// waves: the host picks it when the pool a call writes (or, pool to pool,
+// either pool) keeps the planes of one slot within one slot stride, so that
+// a token's rows of all planes are one contiguous run that adjacent waves
+// stream together.
 __device__ __forceinline__ PagedChunk paged_chunk(const Common& c, uint32_t chunk) {
     PagedChunk k;
+    if (c.tmajor) {
+        const uint32_t nq = c.nchunks / c.chunks_per_plane;
+        const uint32_t j = chunk / nq;
+        k.ql = static_cast<int32_t>(chunk - j * nq);
+        k.tok0 = static_cast<int64_t>(j) * c.U;
+        return k;
+    }
     uint32_t ql = chunk / c.chunks_per_plane;
     uint32_t j = chunk - ql * c.chunks_per_plane;
     k.ql = static_cast<int32_t>(ql);

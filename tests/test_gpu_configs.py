@@ -12,8 +12,9 @@ import torch
 import oracle
 import scatter_kvx_gather_amd as kvx
 import workloads as wl
-from tests.gpu_util import (DEV, assert_bytes_equal, d, layout_of, oracle_gather,
-                            oracle_gather_scatter, oracle_scatter, requests, say, table)
+from tests.gpu_util import (DEV, assert_bytes_equal, d, host_planes, layout_of,
+                            oracle_gather, oracle_gather_scatter, oracle_scatter, requests, say,
+                            table)
 from workloads import device as wdev
 
 pytestmark = pytest.mark.gpu
@@ -101,6 +102,68 @@ def test_config2_all_three_paged_ops():
     del exp_b
     oracle_scatter(case, exp_st, exp_c, NT)
     assert_bytes_equal(c_d.cpu().numpy(), exp_c, "config2 scatter")
+
+
+def test_config2_token_major_pools():
+    """The 2048-token request with token-major pools (plane q of slot s at
+    (s * Q + q) * R, so the rows of a slot in all planes are one 144 KiB run),
+    where the paged kernels take token-major chunk order: gather-scatter
+    between two such pools, gather, scatter back at another slot set, and
+    gather-scatter into a layer-major pool; every destination byte against
+    the oracle."""
+    case, case2 = wl.config2(1), wl.config2(2)
+    g = case.geom
+    Q, R, S = g.planes, g.row_bytes, case.src.num_slots
+    say("config2 token-major fill")
+    a_d = torch.empty((S, Q, R), dtype=torch.uint8, device=DEV)
+    b_d = torch.empty((S, Q, R), dtype=torch.uint8, device=DEV)
+    c_d = hash_pool(Q, S, R, case.sentinel_seed + 1)
+    wdev.fill_hash(a_d, case.value_seed)
+    wdev.fill_hash(b_d, case.sentinel_seed)
+    b_before = b_d.cpu().numpy().reshape(-1)
+    c_before = c_d.cpu().numpy()
+
+    def tm_pool(t):
+        p = kvx.Pool([t.data_ptr() + q * R for q in range(Q)], S, 1, slot_stride=Q * R)
+        p._keep = t
+        return p
+
+    def tm_planes(flat):
+        return [flat[q * R:] for q in range(Q)]
+
+    lay, reqs = layout_of(g), requests(case)
+    st, dt, dt2 = table(case.src), table(case.dst), table(case2.dst)
+    staging = torch.zeros(case.total_tokens * Q * R, dtype=torch.uint8, device=DEV)
+    skipped = torch.zeros(4, dtype=torch.int64, device=DEV)
+    say("config2 token-major gather_scatter")
+    kvx.gather_scatter(lay, tm_pool(a_d), st, reqs, tm_pool(b_d), dt, skipped[0:1])
+    say("config2 token-major gather")
+    kvx.gather(lay, tm_pool(a_d), st, reqs, staging, skipped[1:2])
+    say("config2 token-major scatter")
+    kvx.scatter(lay, staging, reqs, tm_pool(b_d), dt2, skipped[2:3])
+    say("config2 token-major -> layer-major gather_scatter")
+    kvx.gather_scatter(lay, tm_pool(a_d), st, reqs, kvx.Pool(c_d, S), dt, skipped[3:4])
+    torch.cuda.synchronize()
+    assert skipped.cpu().tolist() == [0, 0, 0, 0]
+    a_h = a_d.cpu().numpy().reshape(-1)
+    exp_st = np.zeros(staging.numel(), np.uint8)
+    oracle.gather(tm_planes(a_h), Q * R, 1, S, R, case.tok_off, case.src.pg_off, case.src.ids,
+                  exp_st, NT)
+    assert_bytes_equal(staging.cpu().numpy(), exp_st, "token-major gather")
+    exp_b = b_before
+    oracle.gather_scatter(tm_planes(a_h), Q * R, 1, S, case.src.pg_off, case.src.ids, R,
+                          case.tok_off, tm_planes(exp_b), Q * R, 1, S, case.dst.pg_off,
+                          case.dst.ids, NT)
+    oracle.scatter(exp_st, R, case.tok_off, case2.dst.pg_off, case2.dst.ids, tm_planes(exp_b),
+                   Q * R, 1, S, NT)
+    assert_bytes_equal(b_d.cpu().numpy().reshape(-1), exp_b,
+                       "token-major gather_scatter, then scatter")
+    del exp_b
+    exp_c = c_before
+    oracle.gather_scatter(tm_planes(a_h), Q * R, 1, S, case.src.pg_off, case.src.ids, R,
+                          case.tok_off, host_planes(exp_c), R, 1, S, case.dst.pg_off,
+                          case.dst.ids, NT)
+    assert_bytes_equal(c_d.cpu().numpy(), exp_c, "token-major -> layer-major gather_scatter")
 
 
 def test_config3_batched_gather():
