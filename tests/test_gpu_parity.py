@@ -242,6 +242,90 @@ def test_request_lookup_large_batches(bi):
     run_paged_case(case, 9100 + bi)
 
 
+def run_paged_case_token_major(case, seed):
+    """gather, scatter and gather-scatter with both pools token-major (plane q
+    of slot s at (s * Q + q) * R), which the kernels move in token-major chunk
+    order where they write such a pool; every byte against the oracle."""
+    g = case.geom
+    Q, R = g.planes, g.row_bytes
+    rng = np.random.default_rng(seed)
+    src_h = rng.integers(0, 256, case.src.num_slots * Q * R, dtype=np.uint8)
+    dst_h = rng.integers(0, 256, case.dst.num_slots * Q * R, dtype=np.uint8)
+    n = case.total_tokens * Q * R
+    stage_in = rng.integers(0, 256, n, dtype=np.uint8)
+    lay, reqs = layout_of(g), requests(case)
+    st, dt = table(case.src), table(case.dst)
+
+    def pool(t, side):
+        p = kvx.Pool([t.data_ptr() + q * R for q in range(Q)], side.num_pages, side.page_size,
+                     slot_stride=Q * R)
+        p._keep = t
+        return p
+
+    def planes(flat):
+        return [flat[q * R:] for q in range(Q)]
+
+    src_d = d(src_h)
+    skipped = torch.zeros(3, dtype=torch.int64, device=DEV)
+    say(case.name, f"token-major Q={Q} R={R} T={case.total_tokens} pages "
+        f"{case.src.page_size}/{case.dst.page_size}: gather")
+    staging = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    kvx.gather(lay, pool(src_d, case.src), st, reqs, staging, skipped=skipped[0:1])
+    say(case.name, "token-major scatter")
+    dst_d1 = d(dst_h)
+    kvx.scatter(lay, d(stage_in), reqs, pool(dst_d1, case.dst), dt, skipped=skipped[1:2])
+    say(case.name, "token-major gather_scatter")
+    dst_d2 = d(dst_h)
+    kvx.gather_scatter(lay, pool(src_d, case.src), st, reqs, pool(dst_d2, case.dst), dt,
+                       skipped=skipped[2:3])
+    torch.cuda.synchronize()
+
+    exp_stage = np.zeros(n, np.uint8)
+    s0 = oracle.gather(planes(src_h), Q * R, case.src.page_size, case.src.num_pages, R,
+                       case.tok_off, case.src.pg_off, case.src.ids, exp_stage)
+    exp_dst1 = dst_h.copy()
+    s1 = oracle.scatter(stage_in, R, case.tok_off, case.dst.pg_off, case.dst.ids,
+                        planes(exp_dst1), Q * R, case.dst.page_size, case.dst.num_pages)
+    exp_dst2 = dst_h.copy()
+    s2 = oracle.gather_scatter(planes(src_h), Q * R, case.src.page_size, case.src.num_pages,
+                               case.src.pg_off, case.src.ids, R, case.tok_off, planes(exp_dst2),
+                               Q * R, case.dst.page_size, case.dst.num_pages, case.dst.pg_off,
+                               case.dst.ids)
+    assert_bytes_equal(staging.cpu().numpy(), exp_stage, f"{case.name} token-major gather")
+    assert_bytes_equal(dst_d1.cpu().numpy(), exp_dst1, f"{case.name} token-major scatter")
+    assert_bytes_equal(dst_d2.cpu().numpy(), exp_dst2, f"{case.name} token-major gather_scatter")
+    assert skipped.cpu().tolist() == [s0, s1, s2], case.name
+
+
+def _ragged(rng, nreq, maxlen, zf):
+    lens = np.where(rng.random(nreq) < zf, 0, rng.integers(1, maxlen + 1, nreq))
+    lens[-1] = max(int(lens[-1]), 1)
+    return list(lens)
+
+
+# Token-major pools: small launches (8 KiB chunks), launches above 64 MiB each
+# way (one 2 KiB row or two 1 KiB rows per wave), batches above 64 requests,
+# mixed page sizes and out-of-range ids.
+# (geometry, requests, max length, empty fraction, src page, dst page, oor)
+TOKEN_MAJOR = [
+    (wl.Geometry(2, 2, 8, 128, "bf16"), 3, 60, 0.0, 1, 1, 0.0),
+    (wl.Geometry(2, 2, 4, 128, "f16"), 5, 50, 0.2, 16, 1, 0.05),
+    (wl.Geometry(3, 2, 1, 8, "bf16"), 4, 80, 0.0, 3, 2, 0.0),          # R = 16, flat copy
+    (wl.Geometry(3, 1, 1, 576, "bf16"), 4, 90, 0.0, 1, 16, 0.0),       # R = 1152, row loop
+    (wl.Geometry(4, 2, 8, 128, "bf16"), 200, 6, 0.3, 1, 1, 0.02),      # > 64 requests
+    (wl.Geometry(8, 2, 8, 128, "bf16"), 8, 700, 0.0, 1, 1, 0.0),       # > 64 MiB each way
+    (wl.Geometry(8, 2, 4, 128, "bf16"), 3000, 12, 0.2, 16, 3, 0.02),   # both, 1 KiB rows
+]
+
+
+@pytest.mark.parametrize("ti", range(len(TOKEN_MAJOR)))
+def test_token_major_pools(ti):
+    g, nreq, maxlen, zf, sp, dp, oor = TOKEN_MAJOR[ti]
+    rng = np.random.default_rng(8800 + ti)
+    lens = _ragged(rng, nreq, maxlen, zf)
+    run_paged_case_token_major(big_case(f"tm{ti}", g, lens, sp, dp, 8800 + ti, oor), 8800 + ti)
+
+
 def test_more_than_128_planes():
     # Q = 160 planes: the host splits the launch into plane ranges of 128
     case = wl.random_case(77, geom=wl.Geometry(80, 2, 1, 8, "bf16"), max_reqs=3, max_len=40,
