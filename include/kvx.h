@@ -129,7 +129,8 @@ typedef struct kvx_layout {
 /* A paged pool ([survey] 7.4: per-layer cache base addresses, each cut into
  * num_blocks equal blocks).  planes is a HOST array of Q DEVICE pointers,
  * each 16-byte aligned and addressing at least
- * (num_pages * page_size - 1) * slot_stride + R bytes.  A pool that is the
+ * (num_pages * page_size - 1) * slot_stride + R bytes (NULL allowed for an
+ * empty pool, num_pages = 0, whose rows are never dereferenced).  A pool that is the
  * source of kvx_gather or kvx_gather_scatter must hold at least one slot
  * when the batch has tokens (KVX_E_SHAPE otherwise): rows that are skipped
  * read the plane's first slot and discard it. */
@@ -236,7 +237,9 @@ kvx_status kvx_gather_scatter_heads(const kvx_layout* layout,
  * out[q][s][h][:] = hf_planes[q][0][h][s][:] for s < seq_len.  out is a
  * contiguous DEVICE [Q][seq_len][H][D] buffer of out_bytes >= Q * seq_len * R
  * bytes.  Requires seq_len <= s_cap and head_dim * element size a multiple of
- * 16 bytes.  hf_planes is a HOST array of Q DEVICE pointers. */
+ * 16 bytes.  hf_planes is a HOST array of Q DEVICE pointers.  A pointer to an
+ * empty buffer may be NULL: the planes when s_cap is 0, out when seq_len is
+ * 0 (with seq_len 0 nothing is read or written). */
 kvx_status kvx_extract_permute(const kvx_layout* layout, const void* const* hf_planes,
                                int64_t s_cap, int64_t seq_len,
                                void* out, int64_t out_bytes, hipStream_t stream);

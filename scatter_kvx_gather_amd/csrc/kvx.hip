@@ -113,7 +113,10 @@ kvx_status check_pool(const kvx_pool* p, const Geom& g) {
     if (!mul_ok(p->num_pages, p->page_size, &slots) || !mul_ok(slots, p->slot_stride, &bytes))
         return KVX_E_RANGE;
     for (int32_t q = 0; q < g.Q; ++q) {
-        if (p->planes[q] == nullptr) return KVX_E_NULL;
+        if (p->planes[q] == nullptr) {
+            if (bytes == 0) continue;            // an empty pool's planes may be NULL
+            return KVX_E_NULL;
+        }
         if (!aligned16(p->planes[q])) return KVX_E_ALIGN;
     }
     return KVX_OK;
@@ -677,7 +680,10 @@ kvx_status check_hf(const Geom& g, const void* const* hf, int64_t s_cap, int64_t
     int64_t plane_bytes = 0;
     if (!mul_ok(s_cap * g.H, g.Db, &plane_bytes)) return KVX_E_RANGE;
     for (int32_t q = 0; q < g.Q; ++q) {
-        if (hf[q] == nullptr) return KVX_E_NULL;
+        if (hf[q] == nullptr) {
+            if (plane_bytes == 0) continue;      // an empty plane (s_cap = 0) may be NULL
+            return KVX_E_NULL;
+        }
         if (!aligned16(hf[q])) return KVX_E_ALIGN;
     }
     return KVX_OK;

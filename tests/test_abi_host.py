@@ -110,6 +110,12 @@ def test_gather_validation():
     arr = (ctypes.c_void_p * 4)(A, None, A, A)
     p = kvx._CPool(ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), 16, 1, 2048)
     assert gather(lay, p, tab, reqs) == E_NULL
+    # an empty pool (no pages) may come with NULL planes; as the source of a
+    # batch with tokens it is still refused (skipped rows read its first slot)
+    nulls = (ctypes.c_void_p * 4)(None, None, None, None)
+    p0 = kvx._CPool(ctypes.cast(nulls, ctypes.POINTER(ctypes.c_void_p)), 0, 1, 2048)
+    assert gather(lay, p0, tab, reqs) == E_SHAPE
+    assert gather(lay, p0, _table(0), _reqs(0, 0), staging=None, nbytes=0) == OK
 
 
 def test_empty_batch_enqueues_nothing():
@@ -136,6 +142,14 @@ def test_permute_validation():
     lay_odd = _layout(L=1, kv=2, H=2, D=4, dtype=2)    # head row of 8 bytes
     assert lib.kvx_extract_permute(ctypes.byref(lay_odd), hf, 10, 10, A, 1 << 20, None) == E_ALIGN
     assert lib.kvx_extract_permute(ctypes.byref(lay), hf, 100, 0, None, 0, None) == OK
+    # empty HF planes (s_cap = 0, e.g. zero-size tensors) may be NULL; with
+    # s_cap > 0 a NULL plane is refused even when seq_len is 0
+    nulls = (ctypes.c_void_p * 4)(None, None, None, None)
+    hf0 = ctypes.cast(nulls, ctypes.POINTER(ctypes.c_void_p))
+    assert lib.kvx_extract_permute(ctypes.byref(lay), hf0, 0, 0, None, 0, None) == OK
+    assert lib.kvx_rebuild_permute(ctypes.byref(lay), None, 0, 0, hf0, 0, None) == OK
+    assert lib.kvx_extract_permute(ctypes.byref(lay), hf0, 1, 0, None, 0, None) == E_NULL
+    assert lib.kvx_rebuild_permute(ctypes.byref(lay), None, 0, 0, hf0, 1, None) == E_NULL
     rb = lambda seq, inp=A + 0x1000000, nb=need: lib.kvx_rebuild_permute(  # noqa: E731
         ctypes.byref(lay), inp, nb, seq, hf, 100, None)
     assert rb(101) == E_SHAPE

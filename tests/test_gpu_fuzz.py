@@ -4,16 +4,24 @@
 ids out of range, random-bit
 payloads (NaN patterns included), sentinel-filled destinations and guard
 bytes after the staging.  Every case is compared byte for byte over the whole
-destination, and the skip counters must agree."""
+destination, and the skip counters must agree.  KVX_FUZZ_SCALE=k multiplies
+the number of cases of each family (a longer campaign)."""
+import os
+
 import numpy as np
 import pytest
 
 import workloads as wl
-from tests.test_gpu_parity import big_case, run_paged_case
+from tests.test_gpu_parity import big_case, run_paged_case, run_paged_case_token_major
 
 pytestmark = pytest.mark.gpu
 
 DTYPES = ["fp8", "f16", "bf16", "f32"]
+SCALE = max(1, int(os.environ.get("KVX_FUZZ_SCALE", "1")))
+
+
+def seeds(n):
+    return range(n * SCALE)
 
 
 def random_geometry(rng):
@@ -26,7 +34,7 @@ def random_geometry(rng):
             return g
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", seeds(40))
 def test_fuzz_paged_ops(seed):
     rng = np.random.default_rng(88000 + seed)
     g = random_geometry(rng)
@@ -41,7 +49,7 @@ def test_fuzz_paged_ops(seed):
     run_paged_case(case, 88000 + seed)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", seeds(16))
 def test_fuzz_paged_many_requests(seed):
     # 65 to 5000 requests: the guessed-window lookup and the 64-way search,
     # with empty requests at a random rate
@@ -60,7 +68,23 @@ def test_fuzz_paged_many_requests(seed):
     run_paged_case(case, 89000 + seed)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", seeds(16))
+def test_fuzz_token_major_pools(seed):
+    # both pools token-major (token-major chunk order), 1 to 300 requests
+    rng = np.random.default_rng(93000 + seed)
+    g = random_geometry(rng)
+    nreq = int(rng.choice([1, 3, 17, 64, 65, 300]))
+    lens = rng.integers(0, 60 if nreq > 16 else 200, size=nreq)
+    lens[rng.random(nreq) < 0.15] = 0
+    if lens.sum() == 0:
+        lens[0] = 1
+    sp, dp = (int(rng.choice([1, 2, 16, 32])) for _ in range(2))
+    oor = float(rng.choice([0.0, 0.0, 0.05]))
+    case = big_case(f"fuzztm{seed}", g, list(lens), sp, dp, 93000 + seed, oor)
+    run_paged_case_token_major(case, 93000 + seed)
+
+
+@pytest.mark.parametrize("seed", seeds(24))
 def test_fuzz_head_slices(seed):
     from tests.test_gpu_heads import run_heads
     rng = np.random.default_rng(91000 + seed)
@@ -79,7 +103,7 @@ def test_fuzz_head_slices(seed):
     run_heads(case, sH, dH, nh, sh0, dh0, D, shnd, dhnd, 91000 + seed)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", seeds(24))
 def test_fuzz_permutes(seed):
     from tests.test_gpu_parity import test_permutes
     rng = np.random.default_rng(92000 + seed)
