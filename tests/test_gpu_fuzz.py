@@ -1,9 +1,10 @@
 """Randomized GPU parity against the oracle: geometries with rows of 16 B to
 4 KiB in every element size, pages drawn from {1, 2, 16, 32} on each side,
 1 to 64 requests with empty ones (and 65 to 5000 in a second set), some page
-ids out of range, random-bit
-payloads (NaN patterns included), sentinel-filled destinations and guard
-bytes after the staging.  Every case is compared byte for byte over the whole
+ids out of range, random-bit payloads (NaN patterns included),
+sentinel-filled destinations and guard bytes after the staging; token-major
+pools; launches of 65-160 MiB each way with rows of 1-16 KiB; head-sliced
+copies and permutes.  Every case is compared byte for byte over the whole
 destination, and the skip counters must agree.  KVX_FUZZ_SCALE=k multiplies
 the number of cases of each family (a longer campaign)."""
 import os
@@ -66,6 +67,33 @@ def test_fuzz_paged_many_requests(seed):
     oor = float(rng.choice([0.0, 0.0, 0.05]))
     case = big_case(f"fuzzmany{seed}", g, list(lens), sp, dp, 89000 + seed, oor)
     run_paged_case(case, 89000 + seed)
+
+
+@pytest.mark.parametrize("seed", seeds(6))
+def test_fuzz_large_launches(seed):
+    # 65-160 MiB each way: launches that move one row per wave (two 1 KiB
+    # rows, one 2 KiB row, or 2 KiB pieces of a 4-16 KiB row), 1-400
+    # requests, layer-major or token-major pools
+    rng = np.random.default_rng(94000 + seed)
+    R = int(rng.choice([1024, 2048, 4096, 8192, 16384]))
+    g = wl.Geometry(int(rng.integers(1, 5)), 2, R // 256, 128, "bf16")
+    T = (int(rng.integers(65, 161)) << 20) // (g.planes * R) + 1
+    nreq = int(rng.choice([1, 5, 64, 65, 400]))
+    cuts = np.sort(rng.integers(0, T + 1, nreq - 1))
+    lens = np.diff(np.concatenate([[0], cuts, [T]]))
+    if rng.random() < 0.3:                      # empty requests; the last takes their tokens
+        emptied = rng.random(nreq) < 0.2
+        emptied[-1] = False
+        lens[-1] += int(lens[emptied].sum())
+        lens[emptied] = 0
+    sp, dp = (int(rng.choice([1, 2, 16])) for _ in range(2))
+    oor = float(rng.choice([0.0, 0.0, 0.02]))
+    case = big_case(f"fuzzlarge{seed}", g, list(lens), sp, dp, 94000 + seed, oor)
+    assert case.total_tokens * g.planes * R > 64 << 20
+    if rng.random() < 0.3:
+        run_paged_case_token_major(case, 94000 + seed)
+    else:
+        run_paged_case(case, 94000 + seed)
 
 
 @pytest.mark.parametrize("seed", seeds(16))
