@@ -130,10 +130,13 @@ typedef struct kvx_layout {
  * num_blocks equal blocks).  planes is a HOST array of Q DEVICE pointers,
  * each 16-byte aligned and addressing at least
  * (num_pages * page_size - 1) * slot_stride + R bytes (NULL allowed for an
- * empty pool, num_pages = 0, whose rows are never dereferenced).  A pool that is the
- * source of kvx_gather or kvx_gather_scatter must hold at least one slot
- * when the batch has tokens (KVX_E_SHAPE otherwise): rows that are skipped
- * read the plane's first slot and discard it. */
+ * empty pool, num_pages = 0, whose rows are never dereferenced).  A pool
+ * that is the source of kvx_gather or kvx_gather_scatter must hold at least
+ * one slot when the batch has tokens (KVX_E_SHAPE otherwise): rows that are
+ * skipped read the plane's first slot and discard it.  Planes may be
+ * separate arrays (layer-major, slot_stride = R) or interleaved slot by slot
+ * (token-major, slot_stride = Q * R, planes[q] = base + q * R); the result
+ * is the same, and the kernels order their work to suit the layout. */
 typedef struct kvx_pool {
     void* const* planes;
     int64_t num_pages;      /* >= 0 */
