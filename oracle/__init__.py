@@ -41,12 +41,20 @@ def bind(path: str):
                                    ctypes.c_int]
     lib.oracle_gather_scatter.argtypes = [_i32, _i64, pp, _i64, _i32, _i64, _p, _p, _i32, _p,
                                           pp, _i64, _i32, _i64, _p, _p, ctypes.c_int]
+    lib.oracle_gather_ps.argtypes = [_i32, _i64, pp, _i64, _i64, _i32, _i64, _i32, _p, _p, _p,
+                                     _p, ctypes.c_int]
+    lib.oracle_scatter_ps.argtypes = [_i32, _i64, _p, _i32, _p, _p, _p, pp, _i64, _i64, _i32,
+                                      _i64, ctypes.c_int]
+    lib.oracle_gather_scatter_ps.argtypes = [_i32, _i64, pp, _i64, _i64, _i32, _i64, _p, _p,
+                                             _i32, _p, pp, _i64, _i64, _i32, _i64, _p, _p,
+                                             ctypes.c_int]
     lib.oracle_gather_scatter_heads.argtypes = [
         _i32, _i32, _i64, pp, _i64, _i32, _i64, _p, _p, _i32, _i32, _i32, _i32, _p,
         pp, _i64, _i32, _i64, _p, _p, _i32, _i32, _i32, ctypes.c_int]
     lib.oracle_extract_permute.argtypes = [_i32, _i32, _i64, pp, _i64, _i64, _p, ctypes.c_int]
     lib.oracle_rebuild_permute.argtypes = [_i32, _i32, _i64, _p, _i64, pp, _i64, ctypes.c_int]
     for f in (lib.oracle_gather, lib.oracle_scatter, lib.oracle_gather_scatter,
+              lib.oracle_gather_ps, lib.oracle_scatter_ps, lib.oracle_gather_scatter_ps,
               lib.oracle_gather_scatter_heads, lib.oracle_extract_permute,
               lib.oracle_rebuild_permute):
         f.restype = _i64
@@ -92,35 +100,39 @@ def _check_table(name, num_reqs, tok_off, pg_off, ids, page_size):
         raise ValueError(f"{name}: page table too short for the token counts")
 
 
-def _check_planes(name, planes, stride, page_size, num_pages, R):
-    """Every slot the loop may touch must lie inside each plane buffer."""
-    slots = int(num_pages) * int(page_size)
-    need = (slots - 1) * int(stride) + int(R) if slots > 0 else 0
+def _check_planes(name, planes, stride, page_size, num_pages, R, page_stride=0):
+    """Every row the loop may touch must lie inside each plane buffer."""
+    ps = int(page_stride) if page_stride else int(page_size) * int(stride)
+    need = ((int(num_pages) - 1) * ps + (int(page_size) - 1) * int(stride) + int(R)
+            if int(num_pages) > 0 else 0)
     for p in planes:
         if p.nbytes < need:
             raise ValueError(f"{name}: plane of {p.nbytes} B is smaller than {need} B")
 
 
 def gather(src_planes: Sequence[np.ndarray], stride: int, page_size: int, num_pages: int,
-           row_bytes: int, tok_off, pg_off, ids, staging: np.ndarray, nthreads: int = 1) -> int:
-    """Pool -> contiguous staging.  Returns the number of skipped rows."""
+           row_bytes: int, tok_off, pg_off, ids, staging: np.ndarray, nthreads: int = 1,
+           page_stride: int = 0) -> int:
+    """Pool -> contiguous staging.  Returns the number of skipped rows.
+    ``page_stride``: bytes between consecutive pages of a plane (0: page_size
+    * stride, pages of one plane's rows only)."""
     tok_off, pg_off = _csr(tok_off, np.int64), _csr(pg_off, np.int64)
     ids = _csr(ids, np.int32)
     reqs = len(tok_off) - 1
     _check_table("src", reqs, tok_off, pg_off, ids, page_size)
     Q = len(src_planes)
     R = int(row_bytes)
-    _check_planes("src", src_planes, stride, page_size, num_pages, R)
+    _check_planes("src", src_planes, stride, page_size, num_pages, R, page_stride)
     if staging.nbytes < int(tok_off[-1]) * Q * R:
         raise ValueError("staging too small")
-    return int(_load().oracle_gather(Q, R, _ptr_array(src_planes), stride, page_size, num_pages,
-                                     reqs, _ptr(tok_off), _ptr(pg_off), _ptr(ids),
-                                     _ptr(staging), nthreads))
+    return int(_load().oracle_gather_ps(Q, R, _ptr_array(src_planes), stride, page_stride,
+                                        page_size, num_pages, reqs, _ptr(tok_off), _ptr(pg_off),
+                                        _ptr(ids), _ptr(staging), nthreads))
 
 
 def scatter(staging: np.ndarray, row_bytes: int, tok_off, pg_off, ids,
             dst_planes: Sequence[np.ndarray], stride: int, page_size: int, num_pages: int,
-            nthreads: int = 1) -> int:
+            nthreads: int = 1, page_stride: int = 0) -> int:
     """Contiguous staging -> pool.  Returns the number of skipped rows."""
     tok_off, pg_off = _csr(tok_off, np.int64), _csr(pg_off, np.int64)
     ids = _csr(ids, np.int32)
@@ -128,18 +140,19 @@ def scatter(staging: np.ndarray, row_bytes: int, tok_off, pg_off, ids,
     _check_table("dst", reqs, tok_off, pg_off, ids, page_size)
     Q = len(dst_planes)
     R = int(row_bytes)
-    _check_planes("dst", dst_planes, stride, page_size, num_pages, R)
+    _check_planes("dst", dst_planes, stride, page_size, num_pages, R, page_stride)
     if staging.nbytes < int(tok_off[-1]) * Q * R:
         raise ValueError("staging too small")
-    return int(_load().oracle_scatter(Q, R, _ptr(staging), reqs, _ptr(tok_off), _ptr(pg_off),
-                                      _ptr(ids), _ptr_array(dst_planes), stride, page_size,
-                                      num_pages, nthreads))
+    return int(_load().oracle_scatter_ps(Q, R, _ptr(staging), reqs, _ptr(tok_off), _ptr(pg_off),
+                                         _ptr(ids), _ptr_array(dst_planes), stride, page_stride,
+                                         page_size, num_pages, nthreads))
 
 
 def gather_scatter(src_planes: Sequence[np.ndarray], src_stride: int, src_page_size: int,
                    src_num_pages: int, src_pg_off, src_ids, row_bytes: int, tok_off,
                    dst_planes: Sequence[np.ndarray], dst_stride: int, dst_page_size: int,
-                   dst_num_pages: int, dst_pg_off, dst_ids, nthreads: int = 1) -> int:
+                   dst_num_pages: int, dst_pg_off, dst_ids, nthreads: int = 1,
+                   src_page_stride: int = 0, dst_page_stride: int = 0) -> int:
     """Pool -> pool, row by row.  Returns the number of skipped rows."""
     tok_off = _csr(tok_off, np.int64)
     src_pg_off, dst_pg_off = _csr(src_pg_off, np.int64), _csr(dst_pg_off, np.int64)
@@ -149,13 +162,15 @@ def gather_scatter(src_planes: Sequence[np.ndarray], src_stride: int, src_page_s
     _check_table("dst", reqs, tok_off, dst_pg_off, dst_ids, dst_page_size)
     if len(src_planes) != len(dst_planes):
         raise ValueError("plane counts differ")
-    _check_planes("src", src_planes, src_stride, src_page_size, src_num_pages, row_bytes)
-    _check_planes("dst", dst_planes, dst_stride, dst_page_size, dst_num_pages, row_bytes)
-    return int(_load().oracle_gather_scatter(
-        len(src_planes), int(row_bytes), _ptr_array(src_planes), src_stride, src_page_size,
-        src_num_pages, _ptr(src_pg_off), _ptr(src_ids), reqs, _ptr(tok_off),
-        _ptr_array(dst_planes), dst_stride, dst_page_size, dst_num_pages, _ptr(dst_pg_off),
-        _ptr(dst_ids), nthreads))
+    _check_planes("src", src_planes, src_stride, src_page_size, src_num_pages, row_bytes,
+                  src_page_stride)
+    _check_planes("dst", dst_planes, dst_stride, dst_page_size, dst_num_pages, row_bytes,
+                  dst_page_stride)
+    return int(_load().oracle_gather_scatter_ps(
+        len(src_planes), int(row_bytes), _ptr_array(src_planes), src_stride, src_page_stride,
+        src_page_size, src_num_pages, _ptr(src_pg_off), _ptr(src_ids), reqs, _ptr(tok_off),
+        _ptr_array(dst_planes), dst_stride, dst_page_stride, dst_page_size, dst_num_pages,
+        _ptr(dst_pg_off), _ptr(dst_ids), nthreads))
 
 
 def gather_scatter_heads(src_planes: Sequence[np.ndarray], src_stride: int, src_page_size: int,

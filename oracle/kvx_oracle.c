@@ -28,8 +28,14 @@
  *   size); slot s of plane q sits at planes[q] + s*stride.
  *
  *   Paged blocks ([survey] 7.4).  Each per-layer cache tensor is cut into
- *   num_blocks equal blocks.  With B tokens per page, token t of request r
- *   lives in page ids[pg_off[r] + t/B], row t%B of it: slot page*B + t%B.
+ *   num_blocks equal blocks of block_len bytes.  With B tokens per page,
+ *   token t of request r lives in page ids[pg_off[r] + t/B], row t%B of it.
+ *   Page p of plane q starts at planes[q] + p*page_stride and its row i at
+ *   another i*stride bytes.  When a block holds only one plane's B rows,
+ *   page_stride = B*stride (0 selects this) and the row is slot p*B + t%B;
+ *   when a tensor's blocks hold K and V (or all layers) together,
+ *   page_stride is the block length and the planes' bases differ by where
+ *   their rows sit inside a block.
  *
  *   Gather / scatter ([budget], 5090 section).  P first collects the rows to
  *   be sent into one contiguous staging area, one transfer moves it, and D
@@ -67,25 +73,31 @@
 
 /* ---------------------------------------------------------------- tables -- */
 
-/* Slot of token t of request r in a pool with page_size tokens per page, or -1
- * when the page id is out of range. */
-static int64_t slot_of(const int64_t* pg_off, const int32_t* ids, int32_t page_size,
-                       int64_t num_pages, int64_t r, int64_t t)
-{
-    int64_t page = (int64_t)ids[pg_off[r] + t / page_size];
-    if (page < 0 || page >= num_pages) return -1;
-    return page * page_size + t % page_size;
-}
-
-/* A pool side of a move: Q plane base pointers, slot stride, paging. */
+/* A pool side of a move: Q plane base pointers, row and page strides, paging. */
 typedef struct {
     uint8_t* const* planes;
-    int64_t stride;
+    int64_t stride;         /* bytes between consecutive rows of a page */
+    int64_t page_stride;    /* bytes between consecutive pages of a plane */
     int32_t page_size;
     int64_t num_pages;
     const int64_t* pg_off;
     const int32_t* ids;
 } pool_side;
+
+/* Byte offset from its plane's base of token t of request r, or -1 when the
+ * page id is out of range. */
+static int64_t row_offset(const pool_side* s, int64_t r, int64_t t)
+{
+    int64_t page = (int64_t)s->ids[s->pg_off[r] + t / s->page_size];
+    if (page < 0 || page >= s->num_pages) return -1;
+    return page * s->page_stride + (t % s->page_size) * s->stride;
+}
+
+/* page_stride 0 stands for page_size * stride: pages of one plane's rows only. */
+static int64_t page_stride_of(int64_t page_stride, int32_t page_size, int64_t stride)
+{
+    return page_stride != 0 ? page_stride : (int64_t)page_size * stride;
+}
 
 enum { OP_GATHER = 0, OP_SCATTER = 1, OP_GATHER_SCATTER = 2 };
 
@@ -113,23 +125,18 @@ static void* run_rows(void* arg)
             uint8_t* staged = j->staging
                 ? j->staging + (j->tok_off[r] * j->Q + q * n + t) * j->R : NULL;
             if (j->op == OP_GATHER) {
-                int64_t s = slot_of(j->src.pg_off, j->src.ids, j->src.page_size,
-                                    j->src.num_pages, r, t);
+                int64_t s = row_offset(&j->src, r, t);
                 if (s < 0) { ++skipped; continue; }
-                memcpy(staged, j->src.planes[q] + s * j->src.stride, (size_t)j->R);
+                memcpy(staged, j->src.planes[q] + s, (size_t)j->R);
             } else if (j->op == OP_SCATTER) {
-                int64_t d = slot_of(j->dst.pg_off, j->dst.ids, j->dst.page_size,
-                                    j->dst.num_pages, r, t);
+                int64_t d = row_offset(&j->dst, r, t);
                 if (d < 0) { ++skipped; continue; }
-                memcpy(j->dst.planes[q] + d * j->dst.stride, staged, (size_t)j->R);
+                memcpy(j->dst.planes[q] + d, staged, (size_t)j->R);
             } else {
-                int64_t s = slot_of(j->src.pg_off, j->src.ids, j->src.page_size,
-                                    j->src.num_pages, r, t);
-                int64_t d = slot_of(j->dst.pg_off, j->dst.ids, j->dst.page_size,
-                                    j->dst.num_pages, r, t);
+                int64_t s = row_offset(&j->src, r, t);
+                int64_t d = row_offset(&j->dst, r, t);
                 if (s < 0 || d < 0) { ++skipped; continue; }
-                memcpy(j->dst.planes[q] + d * j->dst.stride,
-                       j->src.planes[q] + s * j->src.stride, (size_t)j->R);
+                memcpy(j->dst.planes[q] + d, j->src.planes[q] + s, (size_t)j->R);
             }
         }
     }
@@ -166,7 +173,24 @@ static int64_t run_split(row_job proto, int nthreads)
     return total;
 }
 
-/* Gather: staging(r, q, t) <- src plane q, slot of token t of request r. */
+/* Gather: staging(r, q, t) <- src plane q, row of token t of request r. */
+int64_t oracle_gather_ps(int32_t Q, int64_t R,
+                         uint8_t* const* src_planes, int64_t src_stride, int64_t src_page_stride,
+                         int32_t src_page_size, int64_t src_num_pages,
+                         int32_t num_reqs, const int64_t* tok_off,
+                         const int64_t* src_pg_off, const int32_t* src_ids,
+                         uint8_t* staging, int nthreads)
+{
+    row_job j;
+    memset(&j, 0, sizeof j);
+    j.op = OP_GATHER; j.Q = Q; j.R = R; j.num_reqs = num_reqs; j.tok_off = tok_off;
+    j.src.planes = src_planes; j.src.stride = src_stride; j.src.page_size = src_page_size;
+    j.src.page_stride = page_stride_of(src_page_stride, src_page_size, src_stride);
+    j.src.num_pages = src_num_pages; j.src.pg_off = src_pg_off; j.src.ids = src_ids;
+    j.staging = staging;
+    return run_split(j, nthreads);
+}
+
 int64_t oracle_gather(int32_t Q, int64_t R,
                       uint8_t* const* src_planes, int64_t src_stride,
                       int32_t src_page_size, int64_t src_num_pages,
@@ -174,34 +198,64 @@ int64_t oracle_gather(int32_t Q, int64_t R,
                       const int64_t* src_pg_off, const int32_t* src_ids,
                       uint8_t* staging, int nthreads)
 {
+    return oracle_gather_ps(Q, R, src_planes, src_stride, 0, src_page_size, src_num_pages,
+                            num_reqs, tok_off, src_pg_off, src_ids, staging, nthreads);
+}
+
+/* Scatter: dst plane q, row of token t of request r <- staging(r, q, t). */
+int64_t oracle_scatter_ps(int32_t Q, int64_t R, const uint8_t* staging,
+                          int32_t num_reqs, const int64_t* tok_off,
+                          const int64_t* dst_pg_off, const int32_t* dst_ids,
+                          uint8_t* const* dst_planes, int64_t dst_stride, int64_t dst_page_stride,
+                          int32_t dst_page_size, int64_t dst_num_pages, int nthreads)
+{
     row_job j;
     memset(&j, 0, sizeof j);
-    j.op = OP_GATHER; j.Q = Q; j.R = R; j.num_reqs = num_reqs; j.tok_off = tok_off;
-    j.src.planes = src_planes; j.src.stride = src_stride; j.src.page_size = src_page_size;
-    j.src.num_pages = src_num_pages; j.src.pg_off = src_pg_off; j.src.ids = src_ids;
-    j.staging = staging;
+    j.op = OP_SCATTER; j.Q = Q; j.R = R; j.num_reqs = num_reqs; j.tok_off = tok_off;
+    j.dst.planes = dst_planes; j.dst.stride = dst_stride; j.dst.page_size = dst_page_size;
+    j.dst.page_stride = page_stride_of(dst_page_stride, dst_page_size, dst_stride);
+    j.dst.num_pages = dst_num_pages; j.dst.pg_off = dst_pg_off; j.dst.ids = dst_ids;
+    j.staging = (uint8_t*)staging;
     return run_split(j, nthreads);
 }
 
-/* Scatter: dst plane q, slot of token t of request r <- staging(r, q, t). */
 int64_t oracle_scatter(int32_t Q, int64_t R, const uint8_t* staging,
                        int32_t num_reqs, const int64_t* tok_off,
                        const int64_t* dst_pg_off, const int32_t* dst_ids,
                        uint8_t* const* dst_planes, int64_t dst_stride,
                        int32_t dst_page_size, int64_t dst_num_pages, int nthreads)
 {
+    return oracle_scatter_ps(Q, R, staging, num_reqs, tok_off, dst_pg_off, dst_ids, dst_planes,
+                             dst_stride, 0, dst_page_size, dst_num_pages, nthreads);
+}
+
+/* Gather-scatter: dst plane q at the dst row of (r, t) <- src plane q at the
+ * src row of (r, t).  Both sides share the token CSR tok_off; each has its
+ * own page table, page size and strides. */
+int64_t oracle_gather_scatter_ps(int32_t Q, int64_t R,
+                                 uint8_t* const* src_planes, int64_t src_stride,
+                                 int64_t src_page_stride, int32_t src_page_size,
+                                 int64_t src_num_pages,
+                                 const int64_t* src_pg_off, const int32_t* src_ids,
+                                 int32_t num_reqs, const int64_t* tok_off,
+                                 uint8_t* const* dst_planes, int64_t dst_stride,
+                                 int64_t dst_page_stride, int32_t dst_page_size,
+                                 int64_t dst_num_pages,
+                                 const int64_t* dst_pg_off, const int32_t* dst_ids,
+                                 int nthreads)
+{
     row_job j;
     memset(&j, 0, sizeof j);
-    j.op = OP_SCATTER; j.Q = Q; j.R = R; j.num_reqs = num_reqs; j.tok_off = tok_off;
+    j.op = OP_GATHER_SCATTER; j.Q = Q; j.R = R; j.num_reqs = num_reqs; j.tok_off = tok_off;
+    j.src.planes = src_planes; j.src.stride = src_stride; j.src.page_size = src_page_size;
+    j.src.page_stride = page_stride_of(src_page_stride, src_page_size, src_stride);
+    j.src.num_pages = src_num_pages; j.src.pg_off = src_pg_off; j.src.ids = src_ids;
     j.dst.planes = dst_planes; j.dst.stride = dst_stride; j.dst.page_size = dst_page_size;
+    j.dst.page_stride = page_stride_of(dst_page_stride, dst_page_size, dst_stride);
     j.dst.num_pages = dst_num_pages; j.dst.pg_off = dst_pg_off; j.dst.ids = dst_ids;
-    j.staging = (uint8_t*)staging;
     return run_split(j, nthreads);
 }
 
-/* Gather-scatter: dst plane q at the dst slot of (r, t) <- src plane q at the
- * src slot of (r, t).  Both sides share the token CSR tok_off; each has its
- * own page table and page size. */
 int64_t oracle_gather_scatter(int32_t Q, int64_t R,
                               uint8_t* const* src_planes, int64_t src_stride,
                               int32_t src_page_size, int64_t src_num_pages,
@@ -212,14 +266,10 @@ int64_t oracle_gather_scatter(int32_t Q, int64_t R,
                               const int64_t* dst_pg_off, const int32_t* dst_ids,
                               int nthreads)
 {
-    row_job j;
-    memset(&j, 0, sizeof j);
-    j.op = OP_GATHER_SCATTER; j.Q = Q; j.R = R; j.num_reqs = num_reqs; j.tok_off = tok_off;
-    j.src.planes = src_planes; j.src.stride = src_stride; j.src.page_size = src_page_size;
-    j.src.num_pages = src_num_pages; j.src.pg_off = src_pg_off; j.src.ids = src_ids;
-    j.dst.planes = dst_planes; j.dst.stride = dst_stride; j.dst.page_size = dst_page_size;
-    j.dst.num_pages = dst_num_pages; j.dst.pg_off = dst_pg_off; j.dst.ids = dst_ids;
-    return run_split(j, nthreads);
+    return oracle_gather_scatter_ps(Q, R, src_planes, src_stride, 0, src_page_size,
+                                    src_num_pages, src_pg_off, src_ids, num_reqs, tok_off,
+                                    dst_planes, dst_stride, 0, dst_page_size, dst_num_pages,
+                                    dst_pg_off, dst_ids, nthreads);
 }
 
 /* ---------------------------------------------------- head-sliced copies -- */

@@ -400,6 +400,79 @@ def check_mixed_strides():
     assert (dstp[:, :, R:] == 0).all()
 
 
+def _page_of(side, r, t):
+    """Page id of token t of request r, or None when it is out of range."""
+    page = int(side.ids[side.pg_off[r] + t // side.page_size])
+    return page if 0 <= page < side.num_pages else None
+
+
+def check_block_interleaved_pools():
+    """Pools whose blocks hold K and V of a layer together ([blocks][2][B][H][D]
+    per layer) or every plane ([blocks][L][2][B][H][D]), addressed through a
+    page stride = the block length: gather, scatter and gather-scatter
+    against element-by-element reads and writes of those arrays, out-of-range
+    ids included."""
+    rng = np.random.default_rng(31)
+    for seed, (bs, bd) in enumerate([(4, 2), (2, 4), (1, 3), (3, 1)]):
+        case = wl.random_case(900 + seed, geom=wl.Geometry(2, 2, 2, 8), max_reqs=4, max_len=14,
+                              src_page=bs, dst_page=bd, oor_frac=0.1, slack_pages=3)
+        g = case.geom
+        L, H, D, Q = g.num_layers, g.kv_heads, g.head_dim, g.planes
+        R = H * D * 2
+        nbs, nbd = case.src.num_pages, case.dst.num_pages
+        # source: one [blocks][2][B][H][D] tensor per layer
+        src = [rng.integers(0, 1 << 16, (nbs, 2, bs, H, D), dtype=np.uint16) for _ in range(L)]
+        src_b = [a.reshape(-1).view(np.uint8) for a in src]
+        src_planes = [src_b[q // 2][(q % 2) * bs * R:] for q in range(Q)]
+        # destination: one [blocks][L][2][B][H][D] tensor
+        dst = rng.integers(0, 1 << 16, (nbd, L, 2, bd, H, D), dtype=np.uint16)
+        dst_planes_of = lambda a: [a.reshape(-1).view(np.uint8)[q * bd * R:]  # noqa: E731
+                                   for q in range(Q)]
+        n = case.total_tokens * Q * R
+        # expected staging and destination, element by element
+        exp_st = np.zeros((n // 2,), np.uint16)
+        exp_gs = dst.copy()
+        for r in range(case.num_reqs):
+            o, e = int(case.tok_off[r]), int(case.tok_off[r + 1])
+            for t in range(e - o):
+                ps, pd = _page_of(case.src, r, t), _page_of(case.dst, r, t)
+                for q in range(Q):
+                    l, kv = divmod(q, 2)
+                    base = ((o * Q + q * (e - o) + t) * R) // 2
+                    if ps is not None:
+                        exp_st[base:base + H * D] = src[l][ps, kv, t % bs].reshape(-1)
+                    if ps is not None and pd is not None:
+                        exp_gs[pd, l, kv, t % bd] = src[l][ps, kv, t % bs]
+        st = np.zeros(n, np.uint8)
+        oracle.gather(src_planes, R, bs, nbs, R, case.tok_off, case.src.pg_off, case.src.ids, st,
+                      page_stride=2 * bs * R)
+        assert np.array_equal(st.view(np.uint16), exp_st)
+        got = dst.copy()
+        oracle.gather_scatter(src_planes, R, bs, nbs, case.src.pg_off, case.src.ids, R,
+                              case.tok_off, dst_planes_of(got), R, bd, nbd, case.dst.pg_off,
+                              case.dst.ids, src_page_stride=2 * bs * R,
+                              dst_page_stride=L * 2 * bd * R)
+        assert np.array_equal(got, exp_gs)
+        # scatter of a random staging buffer into the [blocks][L][2][B][H][D] pool
+        stage_in = rng.integers(0, 256, n, dtype=np.uint8)
+        exp_sc = dst.copy()
+        s16 = stage_in.view(np.uint16)
+        for r in range(case.num_reqs):
+            o, e = int(case.tok_off[r]), int(case.tok_off[r + 1])
+            for t in range(e - o):
+                pd = _page_of(case.dst, r, t)
+                if pd is None:
+                    continue
+                for q in range(Q):
+                    l, kv = divmod(q, 2)
+                    base = ((o * Q + q * (e - o) + t) * R) // 2
+                    exp_sc[pd, l, kv, t % bd] = s16[base:base + H * D].reshape(H, D)
+        got = dst.copy()
+        oracle.scatter(stage_in, R, case.tok_off, case.dst.pg_off, case.dst.ids,
+                       dst_planes_of(got), R, bd, nbd, page_stride=L * 2 * bd * R)
+        assert np.array_equal(got, exp_sc)
+
+
 def check_threads_agree():
     rng = np.random.default_rng(19)
     case = wl.random_case(800, max_reqs=6, max_len=40, oor_frac=0.1)
@@ -678,6 +751,7 @@ ALL_CHECKS = [
     check_untouched_and_extent,
     check_token_major_pool,
     check_mixed_strides,
+    check_block_interleaved_pools,
     check_threads_agree,
     check_permute_torch,
     check_numpy_transpose,

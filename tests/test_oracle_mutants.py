@@ -16,18 +16,22 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "kvx_oracle.c")
 
 MUTANTS = {
-    "row_in_page_uses_div": ("page * page_size + t % page_size", "page * page_size + t / page_size"),
-    "page_index_uses_mod": ("ids[pg_off[r] + t / page_size]", "ids[pg_off[r] + t % page_size]"),
+    "row_in_page_uses_div": ("(t % s->page_size) * s->stride", "(t / s->page_size) * s->stride"),
+    "page_index_uses_mod": ("s->pg_off[r] + t / s->page_size];\n    if (page < 0 || page >= s->num_pages) return -1;\n    return page * s->page_stride",
+                            "s->pg_off[r] + t % s->page_size];\n    if (page < 0 || page >= s->num_pages) return -1;\n    return page * s->page_stride"),
+    "page_stride_ignored": ("return page * s->page_stride + (t % s->page_size) * s->stride;",
+                            "return page * s->page_size * s->stride + (t % s->page_size) * s->stride;"),
+    "page_stride_default_wrong": ("page_stride != 0 ? page_stride : (int64_t)page_size * stride",
+                                  "page_stride != 0 ? page_stride : stride"),
     "staging_drops_Q_factor": ("(j->tok_off[r] * j->Q + q * n + t)", "(j->tok_off[r] + q * n + t)"),
     "staging_token_major": ("(j->tok_off[r] * j->Q + q * n + t)",
                             "(j->tok_off[r] * j->Q + t * j->Q + q)"),
-    "bound_off_by_one": ("page >= num_pages", "page > num_pages"),
+    "bound_off_by_one": ("page >= s->num_pages) return -1;\n    return page * s->page_stride",
+                         "page > s->num_pages) return -1;\n    return page * s->page_stride"),
     "last_token_dropped": ("for (int64_t t = 0; t < n; ++t)", "for (int64_t t = 0; t + 1 < n; ++t)"),
     "gather_reads_plane0": ("memcpy(staged, j->src.planes[q]", "memcpy(staged, j->src.planes[0]"),
-    "gs_dst_uses_src_stride": ("memcpy(j->dst.planes[q] + d * j->dst.stride,\n"
-                               "                       j->src.planes[q]",
-                               "memcpy(j->dst.planes[q] + d * j->src.stride,\n"
-                               "                       j->src.planes[q]"),
+    "gs_dst_uses_src_side": ("int64_t d = row_offset(&j->dst, r, t);\n                if (s < 0 || d < 0)",
+                             "int64_t d = row_offset(&j->src, r, t);\n                if (s < 0 || d < 0)"),
     "gs_ignores_dst_oor": ("if (s < 0 || d < 0)", "if (s < 0)"),
     "hf_index_transposed": ("((int64_t)h * j->s_cap + s)", "((int64_t)s * j->H + h)"),
     "flat_index_transposed": ("(((int64_t)q * j->seq + s) * j->H + h)",
