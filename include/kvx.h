@@ -93,7 +93,7 @@
 extern "C" {
 #endif
 
-#define KVX_ABI_VERSION 4
+#define KVX_ABI_VERSION 5
 
 typedef enum kvx_status {
     KVX_OK = 0,
@@ -136,12 +136,24 @@ typedef struct kvx_layout {
  * skipped read the plane's first slot and discard it.  Planes may be
  * separate arrays (layer-major, slot_stride = R) or interleaved slot by slot
  * (token-major, slot_stride = Q * R, planes[q] = base + q * R); the result
- * is the same, and the kernels order their work to suit the layout. */
+ * is the same, and the kernels order their work to suit the layout.
+ *
+ * Row i of page p of plane q starts at planes[q] + p * page_stride +
+ * i * slot_stride.  page_stride 0 means page_size * slot_stride (a page holds
+ * one plane's rows only, so slot s = p * page_size + i is at s *
+ * slot_stride).  A nonzero page_stride is the block length of a tensor whose
+ * blocks hold several planes' pages ([survey] 7.4: block length = tensor
+ * bytes / num_blocks), e.g. a per-layer [num_blocks][2][page_size][H][D]
+ * tensor with planes[K] = base and planes[V] = base + page_size * R, or one
+ * [num_blocks][layers][2][page_size][H][D] tensor: a multiple of 16, at least
+ * (page_size - 1) * slot_stride + R (the pages of a plane do not overlap),
+ * and not accepted by kvx_gather_scatter_heads (KVX_E_UNSUPPORTED). */
 typedef struct kvx_pool {
     void* const* planes;
     int64_t num_pages;      /* >= 0 */
     int32_t page_size;      /* tokens per page, >= 1 */
-    int64_t slot_stride;    /* bytes between consecutive slots of a plane, >= R, multiple of 16 */
+    int64_t slot_stride;    /* bytes between consecutive rows of a page, >= R, multiple of 16 */
+    int64_t page_stride;    /* bytes between consecutive pages of a plane; 0: page_size * slot_stride */
 } kvx_pool;
 
 /* A batch of requests: request r owns tokens [tok_off[r], tok_off[r+1]) of the

@@ -45,7 +45,8 @@ class _CLayout(ctypes.Structure):
 
 class _CPool(ctypes.Structure):
     _fields_ = [("planes", ctypes.POINTER(ctypes.c_void_p)), ("num_pages", ctypes.c_int64),
-                ("page_size", ctypes.c_int32), ("slot_stride", ctypes.c_int64)]
+                ("page_size", ctypes.c_int32), ("slot_stride", ctypes.c_int64),
+                ("page_stride", ctypes.c_int64)]
 
 
 class _CReqs(ctypes.Structure):
@@ -225,14 +226,17 @@ class Pool:
 
     ``planes`` is a device tensor whose first dimension indexes planes (each
     ``planes[q]`` starting at slot 0), or a sequence of tensors / device
-    pointers, one per plane.  ``slot_stride`` defaults to the row size.
+    pointers, one per plane.  ``slot_stride`` (bytes between the rows of a
+    page) defaults to the row size; ``page_stride`` (bytes between the pages
+    of a plane) defaults to ``page_size * slot_stride`` and is the block
+    length when a tensor's blocks hold several planes' pages.
     The pool keeps references to its tensors; the caller keeps them unchanged
     until the stream has passed every call that uses them.
     """
 
     def __init__(self, planes: Union[torch.Tensor, Sequence], num_pages: int,
                  page_size: int = 1, slot_stride: Optional[int] = None,
-                 row_bytes: Optional[int] = None):
+                 row_bytes: Optional[int] = None, page_stride: int = 0):
         self._keep = planes
         self._arr = _plane_array(planes)
         self.num_planes = planes.shape[0] if isinstance(planes, torch.Tensor) else len(planes)
@@ -247,8 +251,9 @@ class Pool:
                 row_bytes = planes[0].numel() * planes.element_size() // slots
             slot_stride = row_bytes
         self.num_pages, self.page_size, self.slot_stride = num_pages, page_size, slot_stride
+        self.page_stride = page_stride
         self._c = _CPool(ctypes.cast(self._arr, ctypes.POINTER(ctypes.c_void_p)), num_pages,
-                         page_size, slot_stride)
+                         page_size, slot_stride, page_stride)
 
 
 class Requests:

@@ -105,13 +105,31 @@ kvx_status check_layout(const kvx_layout* l, Geom* g) {
     return KVX_OK;
 }
 
+// Bytes between consecutive pages of a plane (page_stride 0: page_size *
+// slot_stride); -1 when that product overflows.
+int64_t page_stride_of(const kvx_pool* p) {
+    if (p->page_stride != 0) return p->page_stride;
+    int64_t ps = 0;
+    return mul_ok(p->page_size, p->slot_stride, &ps) ? ps : -1;
+}
+
 kvx_status check_pool(const kvx_pool* p, const Geom& g) {
     if (p == nullptr || p->planes == nullptr) return KVX_E_NULL;
-    if (p->num_pages < 0 || p->page_size < 1 || p->slot_stride < g.R) return KVX_E_SHAPE;
-    if (p->slot_stride % 16 != 0) return KVX_E_ALIGN;
-    int64_t slots = 0, bytes = 0;
-    if (!mul_ok(p->num_pages, p->page_size, &slots) || !mul_ok(slots, p->slot_stride, &bytes))
+    if (p->num_pages < 0 || p->page_size < 1 || p->slot_stride < g.R || p->page_stride < 0)
+        return KVX_E_SHAPE;
+    if (p->slot_stride % 16 != 0 || p->page_stride % 16 != 0) return KVX_E_ALIGN;
+    // bytes of a page's rows; a nonzero page stride may not make pages overlap
+    int64_t rows = 0;
+    if (!mul_ok(p->page_size - 1, p->slot_stride, &rows) || rows > INT64_MAX - g.R)
         return KVX_E_RANGE;
+    rows += g.R;
+    if (p->page_stride != 0 && p->page_stride < rows) return KVX_E_SHAPE;
+    const int64_t ps = page_stride_of(p);
+    int64_t bytes = 0;                          // extent of one plane
+    if (ps < 0 || (p->num_pages > 0 && (!mul_ok(p->num_pages - 1, ps, &bytes) ||
+                                        bytes > INT64_MAX - rows)))
+        return KVX_E_RANGE;
+    if (p->num_pages > 0) bytes += rows;
     for (int32_t q = 0; q < g.Q; ++q) {
         if (p->planes[q] == nullptr) {
             if (bytes == 0) continue;            // an empty pool's planes may be NULL
@@ -151,6 +169,7 @@ void fill_pool_ref(PoolRef* ref, const kvx_pool* p, const kvx_table* t, int32_t 
     std::memset(ref, 0, sizeof(*ref));
     for (int32_t i = 0; i < nq; ++i) ref->plane[i] = static_cast<char*>(p->planes[q0 + i]);
     ref->stride = p->slot_stride;
+    ref->page_stride = page_stride_of(p);
     ref->num_pages = p->num_pages;
     ref->pg_off = t->pg_off;
     ref->ids = t->page_ids;
@@ -280,8 +299,8 @@ void plane_range(const kvx_pool* p, int32_t q0, int32_t nq, uintptr_t* lo, uintp
 // (a token-major pool, whose planes interleave slot by slot), where the
 // planes' own address range is the bound.
 double pool_span(const kvx_pool* p, int32_t q0, int32_t nq) {
-    const double plane = static_cast<double>(p->num_pages) * p->page_size *
-                         static_cast<double>(p->slot_stride);
+    const double plane = static_cast<double>(p->num_pages) *
+                         static_cast<double>(page_stride_of(p));
     uintptr_t lo = 0, hi = 0;
     plane_range(p, q0, nq, &lo, &hi);
     const double range = static_cast<double>(hi - lo) + plane;
@@ -547,6 +566,8 @@ kvx_status check_heads(const kvx_heads* h, const kvx_pool* p, const Geom& g) {
     if (!mul_ok(p->slot_stride, p->page_size, &page_bytes) ||
         !mul_ok(page_bytes, p->num_pages, &pool_bytes))
         return KVX_E_RANGE;
+    // head-sliced copies address whole pages of one plane's rows only
+    if (p->page_stride != 0 && p->page_stride != page_bytes) return KVX_E_UNSUPPORTED;
     return KVX_OK;
 }
 
@@ -740,10 +761,14 @@ void side_spans(const Geom& g, const kvx_reqs* reqs, const kvx_pool* p,
             if (!live[static_cast<size_t>(tok)]) continue;
             for (int32_t q = 0; q < g.Q; ++q) {
                 uint64_t lo;
-                if (p != nullptr)
+                if (p != nullptr) {
+                    const int64_t s = slot[static_cast<size_t>(tok)];
                     lo = reinterpret_cast<uint64_t>(p->planes[q]) +
-                         static_cast<uint64_t>(slot[static_cast<size_t>(tok)]) *
+                         static_cast<uint64_t>(s / p->page_size) *
+                             static_cast<uint64_t>(page_stride_of(p)) +
+                         static_cast<uint64_t>(s % p->page_size) *
                              static_cast<uint64_t>(p->slot_stride);
+                }
                 else
                     lo = reinterpret_cast<uint64_t>(staging) +
                          static_cast<uint64_t>((off * g.Q + q * n + k) * g.R);

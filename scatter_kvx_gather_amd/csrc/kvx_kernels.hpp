@@ -111,7 +111,8 @@ struct Common {
 // One side of a paged move that is a pool.
 struct PoolRef {
     char* plane[kTab];          // bases of planes q0 .. q0 + nq - 1
-    int64_t stride;
+    int64_t stride;             // bytes between the rows of a page
+    int64_t page_stride;        // bytes between the pages of a plane
     int64_t num_pages;
     const int64_t* pg_off;
     const int32_t* ids;
@@ -388,7 +389,8 @@ __device__ __forceinline__ bool pool_addr(const PoolRef& p, int32_t ql, int64_t 
     int64_t page = p.ids[idx];
     if (page < 0 || page >= p.num_pages) return false;
     addr = reinterpret_cast<uint64_t>(p.plane[ql]) +
-           static_cast<uint64_t>(page * p.page_size + row) * static_cast<uint64_t>(p.stride);
+           static_cast<uint64_t>(page) * static_cast<uint64_t>(p.page_stride) +
+           static_cast<uint64_t>(row) * static_cast<uint64_t>(p.stride);
     return true;
 }
 

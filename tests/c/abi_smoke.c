@@ -139,8 +139,8 @@ int main(void) {
         dplanes_h[q] = exp_dst + q * dplane;
     }
     const kvx_layout lay = {L, KV, H, D, KVX_BF16};
-    const kvx_pool sp = {splanes, SRC_PAGES, SRC_PAGE, R};
-    const kvx_pool dp = {dplanes, DST_PAGES, DST_PAGE, R};
+    const kvx_pool sp = {splanes, SRC_PAGES, SRC_PAGE, R, 0};
+    const kvx_pool dp = {dplanes, DST_PAGES, DST_PAGE, R, 0};
     const kvx_reqs reqs = {NREQ, T, tok_d};
     const kvx_table st = {spg_d, sid_d, n_sids};
     const kvx_table dt = {dpg_d, did_d, n_dids};
@@ -184,7 +184,7 @@ int main(void) {
         CHECK_HIP(hipMalloc((void**)&e_d, Q * dplane));
         CHECK_HIP(hipMemcpy(e_d, dst_h, Q * dplane, hipMemcpyHostToDevice));
         for (int q = 0; q < Q; ++q) { eplanes[q] = e_d + q * dplane; eplanes_h[q] = exp + q * dplane; }
-        const kvx_pool ep = {eplanes, DST_PAGES, DST_PAGE, R};
+        const kvx_pool ep = {eplanes, DST_PAGES, DST_PAGE, R, 0};
         CHECK_KVX(kvx_scatter(&lay, st_d, (int64_t)stage_bytes, &reqs, &ep, &dt, NULL, stream));
         CHECK_HIP(hipStreamSynchronize(stream));
         CHECK_HIP(hipMemcpy(got, e_d, Q * dplane, hipMemcpyDeviceToHost));
@@ -211,7 +211,7 @@ int main(void) {
         CHECK_HIP(hipMemcpy(h_d, init, Q * hplane, hipMemcpyHostToDevice));
         for (int q = 0; q < Q; ++q) { hplanes[q] = h_d + q * hplane; hplanes_h[q] = exp + q * hplane; }
         const kvx_layout hl = {L, KV, NH, D, KVX_BF16};
-        const kvx_pool hp = {hplanes, DST_PAGES, DST_PAGE, NH * DB};
+        const kvx_pool hp = {hplanes, DST_PAGES, DST_PAGE, NH * DB, 0};
         const kvx_heads sh = {H, 1, KVX_HND}, dh = {NH, 0, KVX_NHD};
         CHECK_KVX(kvx_gather_scatter_heads(&hl, &sp, &st, &sh, &reqs, &hp, &dt, &dh, NULL, stream));
         CHECK_HIP(hipStreamSynchronize(stream));

@@ -14,6 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvx.h")
 
 OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_RANGE = 0, 1, 2, 3, 4, 5
+E_UNSUPPORTED = 6
 
 # Fake, 16-byte aligned "device" addresses: validation only looks at their
 # values, never dereferences them, and every call below fails validation.
@@ -43,7 +44,7 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_strings():
     lib = kvx.load_library()
-    assert lib.kvx_abi_version() == 4
+    assert lib.kvx_abi_version() == 5
     for s in range(10):
         assert lib.kvx_status_str(s).startswith(b"KVX_")
     assert lib.kvx_status_str(99) == b"unknown kvx_status"
@@ -187,6 +188,38 @@ def test_heads_validation():
                                         ctypes.byref(empty), ctypes.byref(pool),
                                         ctypes.byref(_table(0)), ctypes.byref(ok),
                                         None, None) == OK
+
+
+def test_page_stride_validation():
+    """A nonzero page stride: a multiple of 16, non-negative, and at least
+    (page_size - 1) * slot_stride + R so a plane's pages never overlap; the
+    head-sliced copy takes only the default."""
+    lib = kvx.load_library()
+    lay = _layout()                                       # R = 2048
+    tab, empty = _table(0), _reqs(0, 0)
+
+    def pool_with(page_stride, page_size=4):
+        p, keep = _pool(4, page_size=page_size)
+        p.page_stride = page_stride
+        return p, keep
+
+    def gather(p):
+        return lib.kvx_gather(ctypes.byref(lay), ctypes.byref(p), ctypes.byref(tab),
+                              ctypes.byref(empty), None, 0, None, None)
+    for ps, want in [(0, OK), (4 * 2048, OK), (8 * 2048, OK), (3 * 2048 + 2048, OK),
+                     (3 * 2048 + 2032, E_SHAPE), (-16, E_SHAPE), (8 * 2048 + 8, E_ALIGN),
+                     (1 << 62, E_RANGE)]:
+        p, keep = pool_with(ps)
+        assert gather(p) == want, ps
+    lay_h = _layout(L=1, kv=2, H=2, D=128)
+    ok = kvx._CHeads(4, 0, 0)
+    for ps, want in [(0, OK), (4 * 1024, OK), (8 * 1024, E_UNSUPPORTED)]:
+        p, keep = _pool(2, page_size=4, stride=4 * 256)
+        p.page_stride = ps
+        st = lib.kvx_gather_scatter_heads(ctypes.byref(lay_h), ctypes.byref(p), ctypes.byref(tab),
+                                          ctypes.byref(ok), ctypes.byref(empty), ctypes.byref(p),
+                                          ctypes.byref(tab), ctypes.byref(ok), None, None)
+        assert st == want, ps
 
 
 def test_python_binding_raises():

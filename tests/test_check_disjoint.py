@@ -19,13 +19,14 @@ PLANE_GAP = 1 << 24
 class Side:
     """A pool side: fake plane bases plus a page table (host arrays)."""
 
-    def __init__(self, side, bases, stride):
+    def __init__(self, side, bases, stride, page_stride=0):
         self.side, self.bases, self.stride = side, [int(b) for b in bases], int(stride)
+        self.page_stride = int(page_stride) or side.page_size * self.stride
         self._planes = (ctypes.c_void_p * len(self.bases))(*self.bases)
         self._pg = np.ascontiguousarray(side.pg_off, dtype=np.int64)
         self._ids = np.ascontiguousarray(side.ids, dtype=np.int32)
         self.pool = kvx._CPool(ctypes.cast(self._planes, ctypes.POINTER(ctypes.c_void_p)),
-                               side.num_pages, side.page_size, self.stride)
+                               side.num_pages, side.page_size, self.stride, int(page_stride))
         self.table = kvx._CTable(self._pg.ctypes.data,
                                  self._ids.ctypes.data if self._ids.size else None,
                                  self._ids.size)
@@ -40,6 +41,11 @@ class Side:
         if page < 0 or page >= s.num_pages:
             return None
         return page * s.page_size + k % s.page_size
+
+    def offset(self, slot):
+        """Byte offset of a slot from its plane's base."""
+        return ((slot // self.side.page_size) * self.page_stride
+                + (slot % self.side.page_size) * self.stride)
 
 
 def call(geom, tok_off, src, dst, staging=0, staging_bytes=0):
@@ -70,8 +76,8 @@ def brute(geom, tok_off, src, dst, staging=0):
                 continue
             for q in range(Q):
                 stage = staging + ((off * Q + q * n + k) * R)
-                lo_r = src.bases[q] + ss * src.stride if src else stage
-                lo_w = dst.bases[q] + ds * dst.stride if dst else stage
+                lo_r = src.bases[q] + src.offset(ss) if src else stage
+                lo_w = dst.bases[q] + dst.offset(ds) if dst else stage
                 reads.append((lo_r, lo_r + R, off + k))
                 writes.append((lo_w, lo_w + R, off + k))
     dup = {t for i, (a, b, t) in enumerate(writes) for (c, e, u) in writes[:i] if a < e and c < b}
@@ -199,3 +205,23 @@ def test_python_binding():
     with pytest.raises(kvx.KvxError) as e:               # staging laid over the source pool
         kvx.check_disjoint(lay, reqs, pa, ts, staging=a.view(-1)[:st.numel()])
     assert e.value.status == E_OVERLAP
+
+
+@pytest.mark.parametrize("v_offset_rows,expect", [(4, OK), (2, E_DUPLICATE), (1, E_DUPLICATE)])
+def test_blocks_holding_k_and_v(v_offset_rows, expect):
+    """Destination blocks hold a layer's K and V pages together ([blocks][2][B]
+    rows, page stride 2 * B * R): V planes B rows after K do not collide;
+    placed fewer rows after K they overlap K's rows of the same block."""
+    g = wl.Geometry(2, 2, 1, 8, "bf16")
+    R, B = g.row_bytes, 4
+    case = wl.random_case(4242, geom=g, max_reqs=3, max_len=12, src_page=1, dst_page=B,
+                          slack_pages=2)
+    src = Side(case.src, [BASE + q * PLANE_GAP for q in range(g.planes)], R)
+    layer = [BASE + (16 + l) * PLANE_GAP for l in range(g.num_layers)]
+    dst_bases = [layer[q // 2] + (q % 2) * v_offset_rows * R for q in range(g.planes)]
+    dst = Side(case.dst, dst_bases, R, page_stride=2 * B * R)
+    st, bad = call(g, case.tok_off, src, dst)
+    want, toks = brute(g, case.tok_off, src, dst)
+    assert st == want == expect
+    if st != OK:
+        assert bad in toks

@@ -326,6 +326,94 @@ def test_token_major_pools(ti):
     run_paged_case_token_major(big_case(f"tm{ti}", g, lens, sp, dp, 8800 + ti, oor), 8800 + ti)
 
 
+def run_paged_case_blocks(case, seed):
+    """gather, scatter and gather-scatter between pools whose blocks hold
+    several planes' pages: the source one [blocks][2][B][R] tensor per layer
+    (K and V pages of a block together), the destination one
+    [blocks][layers][2][B][R] tensor; each plane addressed through the block
+    length as its page stride.  Every byte against the oracle."""
+    g = case.geom
+    Q, R, L = g.planes, g.row_bytes, g.num_layers
+    kv = g.num_kv
+    bs, bd = case.src.page_size, case.dst.page_size
+    rng = np.random.default_rng(seed)
+    src_h = [rng.integers(0, 256, case.src.num_pages * kv * bs * R, dtype=np.uint8)
+             for _ in range(L)]
+    dst_h = rng.integers(0, 256, case.dst.num_pages * Q * bd * R, dtype=np.uint8)
+    n = case.total_tokens * Q * R
+    stage_in = rng.integers(0, 256, n, dtype=np.uint8)
+    lay, reqs = layout_of(g), requests(case)
+    st, dt = table(case.src), table(case.dst)
+    src_d = [d(a) for a in src_h]
+    src = kvx.Pool([src_d[q // kv].data_ptr() + (q % kv) * bs * R for q in range(Q)],
+                   case.src.num_pages, bs, slot_stride=R, page_stride=kv * bs * R)
+    src._keep = src_d
+
+    def dst_pool(t):
+        p = kvx.Pool([t.data_ptr() + q * bd * R for q in range(Q)], case.dst.num_pages, bd,
+                     slot_stride=R, page_stride=Q * bd * R)
+        p._keep = t
+        return p
+
+    src_planes = [src_h[q // kv][(q % kv) * bs * R:] for q in range(Q)]
+
+    def dst_planes(flat):
+        return [flat[q * bd * R:] for q in range(Q)]
+
+    skipped = torch.zeros(3, dtype=torch.int64, device=DEV)
+    say(case.name, f"blocks Q={Q} R={R} T={case.total_tokens} pages {bs}/{bd}: gather")
+    staging = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    kvx.gather(lay, src, st, reqs, staging, skipped=skipped[0:1])
+    say(case.name, "blocks scatter")
+    dst_d1 = d(dst_h)
+    kvx.scatter(lay, d(stage_in), reqs, dst_pool(dst_d1), dt, skipped=skipped[1:2])
+    say(case.name, "blocks gather_scatter")
+    dst_d2 = d(dst_h)
+    kvx.gather_scatter(lay, src, st, reqs, dst_pool(dst_d2), dt, skipped=skipped[2:3])
+    torch.cuda.synchronize()
+
+    exp_stage = np.zeros(n, np.uint8)
+    s0 = oracle.gather(src_planes, R, bs, case.src.num_pages, R, case.tok_off, case.src.pg_off,
+                       case.src.ids, exp_stage, page_stride=kv * bs * R)
+    exp_dst1 = dst_h.copy()
+    s1 = oracle.scatter(stage_in, R, case.tok_off, case.dst.pg_off, case.dst.ids,
+                        dst_planes(exp_dst1), R, bd, case.dst.num_pages,
+                        page_stride=Q * bd * R)
+    exp_dst2 = dst_h.copy()
+    s2 = oracle.gather_scatter(src_planes, R, bs, case.src.num_pages, case.src.pg_off,
+                               case.src.ids, R, case.tok_off, dst_planes(exp_dst2), R, bd,
+                               case.dst.num_pages, case.dst.pg_off, case.dst.ids,
+                               src_page_stride=kv * bs * R, dst_page_stride=Q * bd * R)
+    assert_bytes_equal(staging.cpu().numpy(), exp_stage, f"{case.name} blocks gather")
+    assert_bytes_equal(dst_d1.cpu().numpy(), exp_dst1, f"{case.name} blocks scatter")
+    assert_bytes_equal(dst_d2.cpu().numpy(), exp_dst2, f"{case.name} blocks gather_scatter")
+    assert skipped.cpu().tolist() == [s0, s1, s2], case.name
+
+
+# Pools whose blocks hold several planes' pages (page stride = block length):
+# small launches, launches above 64 MiB each way, batches above 64 requests,
+# page sizes 1 to 16 and out-of-range ids.
+# (geometry, requests, max length, empty fraction, src page, dst page, oor)
+BLOCKS = [
+    (wl.Geometry(2, 2, 8, 128, "bf16"), 3, 60, 0.0, 16, 16, 0.0),
+    (wl.Geometry(2, 2, 4, 128, "f16"), 5, 50, 0.2, 16, 1, 0.05),
+    (wl.Geometry(3, 2, 1, 8, "bf16"), 4, 80, 0.0, 3, 2, 0.0),          # R = 16, flat copy
+    (wl.Geometry(3, 1, 1, 576, "bf16"), 4, 90, 0.0, 1, 16, 0.0),       # R = 1152, row loop
+    (wl.Geometry(4, 2, 8, 128, "bf16"), 200, 6, 0.3, 16, 16, 0.02),    # > 64 requests
+    (wl.Geometry(8, 2, 8, 128, "bf16"), 8, 700, 0.0, 16, 16, 0.0),     # > 64 MiB each way
+    (wl.Geometry(8, 2, 4, 128, "bf16"), 3000, 12, 0.2, 16, 2, 0.02),   # both, 1 KiB rows
+    (wl.Geometry(2, 2, 32, 128, "bf16"), 12, 700, 0.0, 16, 4, 0.0),    # R = 8 KiB, 2 KiB pieces
+]
+
+
+@pytest.mark.parametrize("bi", range(len(BLOCKS)))
+def test_block_interleaved_pools(bi):
+    g, nreq, maxlen, zf, sp, dp, oor = BLOCKS[bi]
+    rng = np.random.default_rng(8900 + bi)
+    lens = _ragged(rng, nreq, maxlen, zf)
+    run_paged_case_blocks(big_case(f"blocks{bi}", g, lens, sp, dp, 8900 + bi, oor), 8900 + bi)
+
+
 def test_more_than_128_planes():
     # Q = 160 planes: the host splits the launch into plane ranges of 128
     case = wl.random_case(77, geom=wl.Geometry(80, 2, 1, 8, "bf16"), max_reqs=3, max_len=40,
