@@ -146,8 +146,10 @@ typedef struct kvx_layout {
  * bytes / num_blocks), e.g. a per-layer [num_blocks][2][page_size][H][D]
  * tensor with planes[K] = base and planes[V] = base + page_size * R, or one
  * [num_blocks][layers][2][page_size][H][D] tensor: a multiple of 16, at least
- * (page_size - 1) * slot_stride + R (the pages of a plane do not overlap),
- * and not accepted by kvx_gather_scatter_heads (KVX_E_UNSUPPORTED). */
+ * (page_size - 1) * slot_stride + R (the pages of a plane do not overlap;
+ * KVX_E_SHAPE otherwise), a multiple of slot_stride (KVX_E_UNSUPPORTED
+ * otherwise), and not accepted by kvx_gather_scatter_heads
+ * (KVX_E_UNSUPPORTED). */
 typedef struct kvx_pool {
     void* const* planes;
     int64_t num_pages;      /* >= 0 */

@@ -112,13 +112,13 @@ struct Common {
 struct PoolRef {
     char* plane[kTab];          // bases of planes q0 .. q0 + nq - 1
     int64_t stride;             // bytes between the rows of a page
-    int64_t page_stride;        // bytes between the pages of a plane
     int64_t num_pages;
     const int64_t* pg_off;
     const int32_t* ids;
     int64_t num_ids;
     int32_t page_size;
-    int32_t page_shift;         // log2(page_size) when a power of two, else -1
+    int32_t page_rows;          // row strides from one page of a plane to the next
+                                // (page_size, unless pages interleave with other planes)
 };
 
 // One side of a paged move that is the contiguous staging buffer.
@@ -184,6 +184,13 @@ __device__ __forceinline__ void store_v(uint64_t base, uint32_t off, v4u x) {
     gchar* p = reinterpret_cast<gchar*>(base) + off;
     if constexpr (NT) __builtin_nontemporal_store(x, reinterpret_cast<gv4u*>(p));
     else *reinterpret_cast<gv4u*>(p) = x;
+}
+
+// log2(page_size) when it is a power of two (wave-uniform: a scalar
+// find-first-set), else -1.
+__device__ __forceinline__ int page_shift_of(int32_t page_size) {
+    return (page_size & (page_size - 1)) == 0 ? __builtin_ctz(static_cast<uint32_t>(page_size))
+                                              : -1;
 }
 
 // ------------------------------------------------------- paged resolvers --
@@ -377,9 +384,10 @@ __device__ __forceinline__ ReqOf request_lookup(const Common& c, const int64_t* 
 __device__ __forceinline__ bool pool_addr(const PoolRef& p, int32_t ql, int64_t pg_off_r,
                                           int64_t t, uint64_t& addr) {
     int64_t pidx, row;
-    if (p.page_shift >= 0) {
-        pidx = t >> p.page_shift;
-        row = t & ((int64_t(1) << p.page_shift) - 1);
+    const int shift = page_shift_of(p.page_size);
+    if (shift >= 0) {
+        pidx = t >> shift;
+        row = t & ((int64_t(1) << shift) - 1);
     } else {
         pidx = t / p.page_size;
         row = t - pidx * p.page_size;
@@ -389,8 +397,7 @@ __device__ __forceinline__ bool pool_addr(const PoolRef& p, int32_t ql, int64_t 
     int64_t page = p.ids[idx];
     if (page < 0 || page >= p.num_pages) return false;
     addr = reinterpret_cast<uint64_t>(p.plane[ql]) +
-           static_cast<uint64_t>(page) * static_cast<uint64_t>(p.page_stride) +
-           static_cast<uint64_t>(row) * static_cast<uint64_t>(p.stride);
+           static_cast<uint64_t>(page * p.page_rows + row) * static_cast<uint64_t>(p.stride);
     return true;
 }
 
@@ -479,9 +486,10 @@ __device__ __forceinline__ bool head_addr(const PoolRef& p, int32_t ql, int64_t 
                                           int64_t t, int64_t h, bool hnd, uint64_t Db,
                                           uint64_t& addr) {
     int64_t pidx, row;
-    if (p.page_shift >= 0) {
-        pidx = t >> p.page_shift;
-        row = t & ((int64_t(1) << p.page_shift) - 1);
+    const int shift = page_shift_of(p.page_size);
+    if (shift >= 0) {
+        pidx = t >> shift;
+        row = t & ((int64_t(1) << shift) - 1);
     } else {
         pidx = t / p.page_size;
         row = t - pidx * p.page_size;

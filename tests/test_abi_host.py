@@ -191,9 +191,9 @@ def test_heads_validation():
 
 
 def test_page_stride_validation():
-    """A nonzero page stride: a multiple of 16, non-negative, and at least
-    (page_size - 1) * slot_stride + R so a plane's pages never overlap; the
-    head-sliced copy takes only the default."""
+    """A nonzero page stride: a multiple of 16 and of the slot stride,
+    non-negative, and at least (page_size - 1) * slot_stride + R so a plane's
+    pages never overlap; the head-sliced copy takes only the default."""
     lib = kvx.load_library()
     lay = _layout()                                       # R = 2048
     tab, empty = _table(0), _reqs(0, 0)
@@ -208,7 +208,7 @@ def test_page_stride_validation():
                               ctypes.byref(empty), None, 0, None, None)
     for ps, want in [(0, OK), (4 * 2048, OK), (8 * 2048, OK), (3 * 2048 + 2048, OK),
                      (3 * 2048 + 2032, E_SHAPE), (-16, E_SHAPE), (8 * 2048 + 8, E_ALIGN),
-                     (1 << 62, E_RANGE)]:
+                     (8 * 2048 + 16, E_UNSUPPORTED), (1 << 62, E_RANGE)]:
         p, keep = pool_with(ps)
         assert gather(p) == want, ps
     lay_h = _layout(L=1, kv=2, H=2, D=128)
