@@ -3,7 +3,7 @@
 1 to 64 requests with empty ones (and 65 to 5000 in a second set), some page
 ids out of range, random-bit payloads (NaN patterns included),
 sentinel-filled destinations and guard bytes after the staging; token-major
-pools; launches of 65-160 MiB each way with rows of 1-16 KiB; head-sliced
+pools; pools whose blocks hold several planes' pages; launches of 65-160 MiB each way with rows of 1-16 KiB; head-sliced
 copies and permutes.  Every case is compared byte for byte over the whole
 destination, and the skip counters must agree.  KVX_FUZZ_SCALE=k multiplies
 the number of cases of each family (a longer campaign)."""
@@ -13,7 +13,8 @@ import numpy as np
 import pytest
 
 import workloads as wl
-from tests.test_gpu_parity import big_case, run_paged_case, run_paged_case_token_major
+from tests.test_gpu_parity import (big_case, run_paged_case, run_paged_case_blocks,
+                                   run_paged_case_token_major)
 
 pytestmark = pytest.mark.gpu
 
@@ -67,6 +68,23 @@ def test_fuzz_paged_many_requests(seed):
     oor = float(rng.choice([0.0, 0.0, 0.05]))
     case = big_case(f"fuzzmany{seed}", g, list(lens), sp, dp, 89000 + seed, oor)
     run_paged_case(case, 89000 + seed)
+
+
+@pytest.mark.parametrize("seed", seeds(16))
+def test_fuzz_block_pools(seed):
+    # blocks holding several planes' pages: [blocks][num_kv][B][R] per layer
+    # on the source side, [blocks][planes][B][R] on the destination side
+    rng = np.random.default_rng(95000 + seed)
+    g = random_geometry(rng)
+    nreq = int(rng.choice([1, 3, 17, 64, 65, 300]))
+    lens = rng.integers(0, 60 if nreq > 16 else 200, size=nreq)
+    lens[rng.random(nreq) < 0.15] = 0
+    if lens.sum() == 0:
+        lens[0] = 1
+    sp, dp = (int(rng.choice([1, 2, 16, 32])) for _ in range(2))
+    oor = float(rng.choice([0.0, 0.0, 0.05]))
+    case = big_case(f"fuzzblk{seed}", g, list(lens), sp, dp, 95000 + seed, oor)
+    run_paged_case_blocks(case, 95000 + seed)
 
 
 @pytest.mark.parametrize("seed", seeds(6))
