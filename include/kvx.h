@@ -61,14 +61,30 @@
  * HIP kernel.  There is no fallback to a slower path: an unsupported case is
  * an error status.
  *
- * Out-of-range ids.  A page id < 0 or >= num_pages, a page-table index
- * outside [0, num_ids), or a token range that contradicts total_tokens is
- * never dereferenced: that row is skipped, its destination bytes keep their
- * prior contents, and (when `skipped` is not NULL) the row is added to
- * *skipped with a device atomic.  No write can land outside the destination
- * pool or staging ([budget], failure-handling section: a late write landing
- * in pages that were already given to another request is the failure to rule
- * out).
+ * Page-table reads.  Token t of request r takes its page id from
+ * page_ids[pg_off[r] + t / page_size]: a request's list is read from its
+ * start onward, one entry per page of its tokens, and the data-movement
+ * calls never read pg_off[r + 1], so a list shorter than ceil(n_r /
+ * page_size) entries runs on into the entries after it (kvx_check_tables
+ * reports such a list).
+ *
+ * Out-of-range rows.  A row whose page-table index pg_off[r] + t /
+ * page_size falls outside [0, num_ids), or whose page id falls outside
+ * [0, num_pages), is never dereferenced: it is skipped, its destination
+ * bytes keep their prior contents, and (when `skipped` is not NULL) it is
+ * added to *skipped with a device atomic.  A token of a pool-to-pool copy
+ * that is out of range on either side is skipped in every plane.  No write
+ * can land outside the destination pool or staging, whatever the tables
+ * hold ([budget], failure-handling section: a late write landing in pages
+ * that were already given to another request is the failure to rule out).
+ *
+ * Token offsets.  tok_off must follow its contract (kvx_reqs below).  The
+ * calls cannot check it without reading device memory; KVX_VALIDATE=1 does,
+ * and refuses a violation with KVX_E_SHAPE.  With a tok_off that breaks the
+ * contract the kernels still address nothing outside the pools and the
+ * staging (every staging row they form lies below total_tokens * Q * R
+ * bytes, and pool rows are bounded as above), but which rows are copied is
+ * then unspecified.
  *
  * Preconditions the data-movement calls do not check (they would need the
  * device tables on the host): within one call the destination rows are
@@ -78,10 +94,11 @@
  * of the tables, as a debug aid.  With KVX_VALIDATE=1 in the environment
  * (read once per process) every data-movement call runs those checks itself
  * before enqueueing: it synchronizes its stream, copies its tables to the
- * host, and on a violation returns KVX_E_DUPLICATE or KVX_E_OVERLAP with
- * nothing enqueued (out-of-range ids stay legal).  Debug only: it cannot run
- * on a stream under graph capture (KVX_E_HIP).  KVX_LOG=1 prints each
- * launch decision to stderr.
+ * host, and returns KVX_E_SHAPE for a tok_off that breaks its contract, or
+ * KVX_E_DUPLICATE or KVX_E_OVERLAP for rows that violate the preconditions,
+ * with nothing enqueued (out-of-range rows stay legal).  Debug only: it
+ * cannot run on a stream under graph capture (KVX_E_HIP).  KVX_LOG=1 prints
+ * each launch decision to stderr.
  */
 #ifndef KVX_H
 #define KVX_H
@@ -171,8 +188,10 @@ typedef struct kvx_reqs {
 } kvx_reqs;
 
 /* Where a batch's tokens live in one pool ([survey] 7.5/7.6: per-request
- * block id lists).  Request r's page ids are page_ids[pg_off[r] ..
- * pg_off[r+1]); it needs at least ceil(n_r / page_size) of them. */
+ * block id lists).  Request r's page ids start at page_ids[pg_off[r]], one
+ * per page of its tokens (ceil(n_r / page_size) of them); how indices past
+ * the list or outside page_ids are read is stated under "Page-table reads"
+ * and "Out-of-range rows" above.  pg_off values may be any int64. */
 typedef struct kvx_table {
     const int64_t* pg_off;   /* DEVICE [num_reqs + 1] */
     const int32_t* page_ids; /* DEVICE [num_ids] */

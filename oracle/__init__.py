@@ -35,26 +35,19 @@ def bind(path: str):
     """Open a build of kvx_oracle.c at ``path`` and declare its signatures."""
     lib = ctypes.CDLL(path)
     pp = ctypes.POINTER(ctypes.c_void_p)
-    lib.oracle_gather.argtypes = [_i32, _i64, pp, _i64, _i32, _i64, _i32, _p, _p, _p, _p,
-                                  ctypes.c_int]
-    lib.oracle_scatter.argtypes = [_i32, _i64, _p, _i32, _p, _p, _p, pp, _i64, _i32, _i64,
-                                   ctypes.c_int]
-    lib.oracle_gather_scatter.argtypes = [_i32, _i64, pp, _i64, _i32, _i64, _p, _p, _i32, _p,
-                                          pp, _i64, _i32, _i64, _p, _p, ctypes.c_int]
-    lib.oracle_gather_ps.argtypes = [_i32, _i64, pp, _i64, _i64, _i32, _i64, _i32, _p, _p, _p,
-                                     _p, ctypes.c_int]
-    lib.oracle_scatter_ps.argtypes = [_i32, _i64, _p, _i32, _p, _p, _p, pp, _i64, _i64, _i32,
-                                      _i64, ctypes.c_int]
-    lib.oracle_gather_scatter_ps.argtypes = [_i32, _i64, pp, _i64, _i64, _i32, _i64, _p, _p,
-                                             _i32, _p, pp, _i64, _i64, _i32, _i64, _p, _p,
-                                             ctypes.c_int]
+    lib.oracle_gather.argtypes = [_i32, _i64, pp, _i64, _i64, _i32, _i64, _i32, _p, _p, _p,
+                                  _i64, _p, ctypes.c_int]
+    lib.oracle_scatter.argtypes = [_i32, _i64, _p, _i32, _p, _p, _p, _i64, pp, _i64, _i64,
+                                   _i32, _i64, ctypes.c_int]
+    lib.oracle_gather_scatter.argtypes = [_i32, _i64, pp, _i64, _i64, _i32, _i64, _p, _p, _i64,
+                                          _i32, _p, pp, _i64, _i64, _i32, _i64, _p, _p, _i64,
+                                          ctypes.c_int]
     lib.oracle_gather_scatter_heads.argtypes = [
-        _i32, _i32, _i64, pp, _i64, _i32, _i64, _p, _p, _i32, _i32, _i32, _i32, _p,
-        pp, _i64, _i32, _i64, _p, _p, _i32, _i32, _i32, ctypes.c_int]
+        _i32, _i32, _i64, pp, _i64, _i32, _i64, _p, _p, _i64, _i32, _i32, _i32, _i32, _p,
+        pp, _i64, _i32, _i64, _p, _p, _i64, _i32, _i32, _i32, ctypes.c_int]
     lib.oracle_extract_permute.argtypes = [_i32, _i32, _i64, pp, _i64, _i64, _p, ctypes.c_int]
     lib.oracle_rebuild_permute.argtypes = [_i32, _i32, _i64, _p, _i64, pp, _i64, ctypes.c_int]
     for f in (lib.oracle_gather, lib.oracle_scatter, lib.oracle_gather_scatter,
-              lib.oracle_gather_ps, lib.oracle_scatter_ps, lib.oracle_gather_scatter_ps,
               lib.oracle_gather_scatter_heads, lib.oracle_extract_permute,
               lib.oracle_rebuild_permute):
         f.restype = _i64
@@ -88,16 +81,18 @@ def _csr(a, dtype) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=dtype)
 
 
-def _check_table(name, num_reqs, tok_off, pg_off, ids, page_size):
-    """Table sanity the C loop relies on (so it never reads past ids)."""
+def _check_table(name, num_reqs, tok_off, pg_off):
+    """What the C loop relies on to stay inside its buffers.  The token CSR
+    must follow its contract (starts at 0, never decreases): the oracle
+    defines no result for one that does not.  The page table may hold
+    anything -- start offsets anywhere, lists shorter than their tokens need,
+    ids out of range: the loop reads entry pg_off[r] + t / page_size only when
+    it lies in [0, len(ids)) and skips the row otherwise."""
     if tok_off.shape != (num_reqs + 1,) or pg_off.shape != (num_reqs + 1,):
         raise ValueError(f"{name}: offsets must have num_reqs+1 entries")
     n = np.diff(tok_off)
-    pages = np.diff(pg_off)
-    if tok_off[0] != 0 or (n < 0).any() or pg_off[0] < 0 or (pages < 0).any():
-        raise ValueError(f"{name}: offsets must start at 0 and be non-decreasing")
-    if (pages * page_size < n).any() or pg_off[-1] > ids.size:
-        raise ValueError(f"{name}: page table too short for the token counts")
+    if tok_off[0] != 0 or (n < 0).any():
+        raise ValueError(f"{name}: token offsets must start at 0 and be non-decreasing")
 
 
 def _check_planes(name, planes, stride, page_size, num_pages, R, page_stride=0):
@@ -119,15 +114,15 @@ def gather(src_planes: Sequence[np.ndarray], stride: int, page_size: int, num_pa
     tok_off, pg_off = _csr(tok_off, np.int64), _csr(pg_off, np.int64)
     ids = _csr(ids, np.int32)
     reqs = len(tok_off) - 1
-    _check_table("src", reqs, tok_off, pg_off, ids, page_size)
+    _check_table("src", reqs, tok_off, pg_off)
     Q = len(src_planes)
     R = int(row_bytes)
     _check_planes("src", src_planes, stride, page_size, num_pages, R, page_stride)
     if staging.nbytes < int(tok_off[-1]) * Q * R:
         raise ValueError("staging too small")
-    return int(_load().oracle_gather_ps(Q, R, _ptr_array(src_planes), stride, page_stride,
-                                        page_size, num_pages, reqs, _ptr(tok_off), _ptr(pg_off),
-                                        _ptr(ids), _ptr(staging), nthreads))
+    return int(_load().oracle_gather(Q, R, _ptr_array(src_planes), stride, page_stride,
+                                     page_size, num_pages, reqs, _ptr(tok_off), _ptr(pg_off),
+                                     _ptr(ids), ids.size, _ptr(staging), nthreads))
 
 
 def scatter(staging: np.ndarray, row_bytes: int, tok_off, pg_off, ids,
@@ -137,15 +132,15 @@ def scatter(staging: np.ndarray, row_bytes: int, tok_off, pg_off, ids,
     tok_off, pg_off = _csr(tok_off, np.int64), _csr(pg_off, np.int64)
     ids = _csr(ids, np.int32)
     reqs = len(tok_off) - 1
-    _check_table("dst", reqs, tok_off, pg_off, ids, page_size)
+    _check_table("dst", reqs, tok_off, pg_off)
     Q = len(dst_planes)
     R = int(row_bytes)
     _check_planes("dst", dst_planes, stride, page_size, num_pages, R, page_stride)
     if staging.nbytes < int(tok_off[-1]) * Q * R:
         raise ValueError("staging too small")
-    return int(_load().oracle_scatter_ps(Q, R, _ptr(staging), reqs, _ptr(tok_off), _ptr(pg_off),
-                                         _ptr(ids), _ptr_array(dst_planes), stride, page_stride,
-                                         page_size, num_pages, nthreads))
+    return int(_load().oracle_scatter(Q, R, _ptr(staging), reqs, _ptr(tok_off), _ptr(pg_off),
+                                      _ptr(ids), ids.size, _ptr_array(dst_planes), stride,
+                                      page_stride, page_size, num_pages, nthreads))
 
 
 def gather_scatter(src_planes: Sequence[np.ndarray], src_stride: int, src_page_size: int,
@@ -158,19 +153,19 @@ def gather_scatter(src_planes: Sequence[np.ndarray], src_stride: int, src_page_s
     src_pg_off, dst_pg_off = _csr(src_pg_off, np.int64), _csr(dst_pg_off, np.int64)
     src_ids, dst_ids = _csr(src_ids, np.int32), _csr(dst_ids, np.int32)
     reqs = len(tok_off) - 1
-    _check_table("src", reqs, tok_off, src_pg_off, src_ids, src_page_size)
-    _check_table("dst", reqs, tok_off, dst_pg_off, dst_ids, dst_page_size)
+    _check_table("src", reqs, tok_off, src_pg_off)
+    _check_table("dst", reqs, tok_off, dst_pg_off)
     if len(src_planes) != len(dst_planes):
         raise ValueError("plane counts differ")
     _check_planes("src", src_planes, src_stride, src_page_size, src_num_pages, row_bytes,
                   src_page_stride)
     _check_planes("dst", dst_planes, dst_stride, dst_page_size, dst_num_pages, row_bytes,
                   dst_page_stride)
-    return int(_load().oracle_gather_scatter_ps(
+    return int(_load().oracle_gather_scatter(
         len(src_planes), int(row_bytes), _ptr_array(src_planes), src_stride, src_page_stride,
-        src_page_size, src_num_pages, _ptr(src_pg_off), _ptr(src_ids), reqs, _ptr(tok_off),
-        _ptr_array(dst_planes), dst_stride, dst_page_stride, dst_page_size, dst_num_pages,
-        _ptr(dst_pg_off), _ptr(dst_ids), nthreads))
+        src_page_size, src_num_pages, _ptr(src_pg_off), _ptr(src_ids), src_ids.size, reqs,
+        _ptr(tok_off), _ptr_array(dst_planes), dst_stride, dst_page_stride, dst_page_size,
+        dst_num_pages, _ptr(dst_pg_off), _ptr(dst_ids), dst_ids.size, nthreads))
 
 
 def gather_scatter_heads(src_planes: Sequence[np.ndarray], src_stride: int, src_page_size: int,
@@ -186,8 +181,8 @@ def gather_scatter_heads(src_planes: Sequence[np.ndarray], src_stride: int, src_
     src_pg_off, dst_pg_off = _csr(src_pg_off, np.int64), _csr(dst_pg_off, np.int64)
     src_ids, dst_ids = _csr(src_ids, np.int32), _csr(dst_ids, np.int32)
     reqs = len(tok_off) - 1
-    _check_table("src", reqs, tok_off, src_pg_off, src_ids, src_page_size)
-    _check_table("dst", reqs, tok_off, dst_pg_off, dst_ids, dst_page_size)
+    _check_table("src", reqs, tok_off, src_pg_off)
+    _check_table("dst", reqs, tok_off, dst_pg_off)
     for name, (H, h0, hnd), stride in (("src", src_heads, src_stride),
                                         ("dst", dst_heads, dst_stride)):
         if h0 < 0 or h0 + nh > H or stride < H * head_bytes:
@@ -196,9 +191,9 @@ def gather_scatter_heads(src_planes: Sequence[np.ndarray], src_stride: int, src_
     _check_planes("dst", dst_planes, dst_stride, dst_page_size, dst_num_pages, dst_stride)
     return int(_load().oracle_gather_scatter_heads(
         len(src_planes), nh, head_bytes, _ptr_array(src_planes), src_stride, src_page_size,
-        src_num_pages, _ptr(src_pg_off), _ptr(src_ids), *src_heads, reqs, _ptr(tok_off),
-        _ptr_array(dst_planes), dst_stride, dst_page_size, dst_num_pages, _ptr(dst_pg_off),
-        _ptr(dst_ids), *dst_heads, nthreads))
+        src_num_pages, _ptr(src_pg_off), _ptr(src_ids), src_ids.size, *src_heads, reqs,
+        _ptr(tok_off), _ptr_array(dst_planes), dst_stride, dst_page_size, dst_num_pages,
+        _ptr(dst_pg_off), _ptr(dst_ids), dst_ids.size, *dst_heads, nthreads))
 
 
 def extract_permute(hf_planes: Sequence[np.ndarray], kv_heads: int, head_bytes: int,

@@ -55,11 +55,18 @@
  *   [1, H, seq, D].  The Q per-plane [seq, H, D] results are stacked as one
  *   [Q][seq][H][D] buffer.
  *
- *   Out-of-range page ids (page < 0 or page >= num_pages) are never
- *   dereferenced: the row is skipped, counted, and its destination bytes keep
- *   their prior contents ([budget], failure-handling section: the failure to
- *   rule out is a late write landing in pages already handed to someone
- *   else).
+ *   Page-table reads.  Token t of request r takes its page id from entry
+ *   pg_off[r] + t/B of the side's page-id array of num_ids entries: a
+ *   request's list is read from its start onward, one entry per page of its
+ *   tokens, and the start of the next request's list is never consulted (a
+ *   list shorter than its tokens need runs on into the entries after it).
+ *
+ *   Out-of-range rows.  A row whose table index pg_off[r] + t/B falls outside
+ *   [0, num_ids), or whose page id falls outside [0, num_pages), is never
+ *   dereferenced: it is skipped, counted, and its destination bytes keep their
+ *   prior contents ([budget], failure-handling section: the failure to rule
+ *   out is a late write landing in pages already handed to someone else, so
+ *   nothing outside the pool may be addressed, whatever the tables say).
  *
  * Every function returns the number of skipped rows (>= 0).  Work may be
  * split over nthreads POSIX threads by (request, plane) pairs; the result does
@@ -82,14 +89,26 @@ typedef struct {
     int64_t num_pages;
     const int64_t* pg_off;
     const int32_t* ids;
+    int64_t num_ids;        /* entries of ids */
 } pool_side;
 
+/* Page id of token t of request r, or -1 when its table index or the id it
+ * holds is out of range. */
+static int64_t page_of(const pool_side* s, int64_t r, int64_t t)
+{
+    int64_t idx = s->pg_off[r] + t / s->page_size;
+    if (idx < 0 || idx >= s->num_ids) return -1;
+    int64_t page = (int64_t)s->ids[idx];
+    if (page < 0 || page >= s->num_pages) return -1;
+    return page;
+}
+
 /* Byte offset from its plane's base of token t of request r, or -1 when the
- * page id is out of range. */
+ * row is out of range. */
 static int64_t row_offset(const pool_side* s, int64_t r, int64_t t)
 {
-    int64_t page = (int64_t)s->ids[s->pg_off[r] + t / s->page_size];
-    if (page < 0 || page >= s->num_pages) return -1;
+    int64_t page = page_of(s, r, t);
+    if (page < 0) return -1;
     return page * s->page_stride + (t % s->page_size) * s->stride;
 }
 
@@ -174,12 +193,12 @@ static int64_t run_split(row_job proto, int nthreads)
 }
 
 /* Gather: staging(r, q, t) <- src plane q, row of token t of request r. */
-int64_t oracle_gather_ps(int32_t Q, int64_t R,
-                         uint8_t* const* src_planes, int64_t src_stride, int64_t src_page_stride,
-                         int32_t src_page_size, int64_t src_num_pages,
-                         int32_t num_reqs, const int64_t* tok_off,
-                         const int64_t* src_pg_off, const int32_t* src_ids,
-                         uint8_t* staging, int nthreads)
+int64_t oracle_gather(int32_t Q, int64_t R,
+                      uint8_t* const* src_planes, int64_t src_stride, int64_t src_page_stride,
+                      int32_t src_page_size, int64_t src_num_pages,
+                      int32_t num_reqs, const int64_t* tok_off,
+                      const int64_t* src_pg_off, const int32_t* src_ids, int64_t src_num_ids,
+                      uint8_t* staging, int nthreads)
 {
     row_job j;
     memset(&j, 0, sizeof j);
@@ -187,27 +206,17 @@ int64_t oracle_gather_ps(int32_t Q, int64_t R,
     j.src.planes = src_planes; j.src.stride = src_stride; j.src.page_size = src_page_size;
     j.src.page_stride = page_stride_of(src_page_stride, src_page_size, src_stride);
     j.src.num_pages = src_num_pages; j.src.pg_off = src_pg_off; j.src.ids = src_ids;
+    j.src.num_ids = src_num_ids;
     j.staging = staging;
     return run_split(j, nthreads);
 }
 
-int64_t oracle_gather(int32_t Q, int64_t R,
-                      uint8_t* const* src_planes, int64_t src_stride,
-                      int32_t src_page_size, int64_t src_num_pages,
-                      int32_t num_reqs, const int64_t* tok_off,
-                      const int64_t* src_pg_off, const int32_t* src_ids,
-                      uint8_t* staging, int nthreads)
-{
-    return oracle_gather_ps(Q, R, src_planes, src_stride, 0, src_page_size, src_num_pages,
-                            num_reqs, tok_off, src_pg_off, src_ids, staging, nthreads);
-}
-
 /* Scatter: dst plane q, row of token t of request r <- staging(r, q, t). */
-int64_t oracle_scatter_ps(int32_t Q, int64_t R, const uint8_t* staging,
-                          int32_t num_reqs, const int64_t* tok_off,
-                          const int64_t* dst_pg_off, const int32_t* dst_ids,
-                          uint8_t* const* dst_planes, int64_t dst_stride, int64_t dst_page_stride,
-                          int32_t dst_page_size, int64_t dst_num_pages, int nthreads)
+int64_t oracle_scatter(int32_t Q, int64_t R, const uint8_t* staging,
+                       int32_t num_reqs, const int64_t* tok_off,
+                       const int64_t* dst_pg_off, const int32_t* dst_ids, int64_t dst_num_ids,
+                       uint8_t* const* dst_planes, int64_t dst_stride, int64_t dst_page_stride,
+                       int32_t dst_page_size, int64_t dst_num_pages, int nthreads)
 {
     row_job j;
     memset(&j, 0, sizeof j);
@@ -215,34 +224,27 @@ int64_t oracle_scatter_ps(int32_t Q, int64_t R, const uint8_t* staging,
     j.dst.planes = dst_planes; j.dst.stride = dst_stride; j.dst.page_size = dst_page_size;
     j.dst.page_stride = page_stride_of(dst_page_stride, dst_page_size, dst_stride);
     j.dst.num_pages = dst_num_pages; j.dst.pg_off = dst_pg_off; j.dst.ids = dst_ids;
+    j.dst.num_ids = dst_num_ids;
     j.staging = (uint8_t*)staging;
     return run_split(j, nthreads);
 }
 
-int64_t oracle_scatter(int32_t Q, int64_t R, const uint8_t* staging,
-                       int32_t num_reqs, const int64_t* tok_off,
-                       const int64_t* dst_pg_off, const int32_t* dst_ids,
-                       uint8_t* const* dst_planes, int64_t dst_stride,
-                       int32_t dst_page_size, int64_t dst_num_pages, int nthreads)
-{
-    return oracle_scatter_ps(Q, R, staging, num_reqs, tok_off, dst_pg_off, dst_ids, dst_planes,
-                             dst_stride, 0, dst_page_size, dst_num_pages, nthreads);
-}
-
 /* Gather-scatter: dst plane q at the dst row of (r, t) <- src plane q at the
  * src row of (r, t).  Both sides share the token CSR tok_off; each has its
- * own page table, page size and strides. */
-int64_t oracle_gather_scatter_ps(int32_t Q, int64_t R,
-                                 uint8_t* const* src_planes, int64_t src_stride,
-                                 int64_t src_page_stride, int32_t src_page_size,
-                                 int64_t src_num_pages,
-                                 const int64_t* src_pg_off, const int32_t* src_ids,
-                                 int32_t num_reqs, const int64_t* tok_off,
-                                 uint8_t* const* dst_planes, int64_t dst_stride,
-                                 int64_t dst_page_stride, int32_t dst_page_size,
-                                 int64_t dst_num_pages,
-                                 const int64_t* dst_pg_off, const int32_t* dst_ids,
-                                 int nthreads)
+ * own page table, page size and strides.  A token out of range on either
+ * side is skipped (and counted) in every plane. */
+int64_t oracle_gather_scatter(int32_t Q, int64_t R,
+                              uint8_t* const* src_planes, int64_t src_stride,
+                              int64_t src_page_stride, int32_t src_page_size,
+                              int64_t src_num_pages,
+                              const int64_t* src_pg_off, const int32_t* src_ids,
+                              int64_t src_num_ids,
+                              int32_t num_reqs, const int64_t* tok_off,
+                              uint8_t* const* dst_planes, int64_t dst_stride,
+                              int64_t dst_page_stride, int32_t dst_page_size,
+                              int64_t dst_num_pages,
+                              const int64_t* dst_pg_off, const int32_t* dst_ids,
+                              int64_t dst_num_ids, int nthreads)
 {
     row_job j;
     memset(&j, 0, sizeof j);
@@ -250,26 +252,12 @@ int64_t oracle_gather_scatter_ps(int32_t Q, int64_t R,
     j.src.planes = src_planes; j.src.stride = src_stride; j.src.page_size = src_page_size;
     j.src.page_stride = page_stride_of(src_page_stride, src_page_size, src_stride);
     j.src.num_pages = src_num_pages; j.src.pg_off = src_pg_off; j.src.ids = src_ids;
+    j.src.num_ids = src_num_ids;
     j.dst.planes = dst_planes; j.dst.stride = dst_stride; j.dst.page_size = dst_page_size;
     j.dst.page_stride = page_stride_of(dst_page_stride, dst_page_size, dst_stride);
     j.dst.num_pages = dst_num_pages; j.dst.pg_off = dst_pg_off; j.dst.ids = dst_ids;
+    j.dst.num_ids = dst_num_ids;
     return run_split(j, nthreads);
-}
-
-int64_t oracle_gather_scatter(int32_t Q, int64_t R,
-                              uint8_t* const* src_planes, int64_t src_stride,
-                              int32_t src_page_size, int64_t src_num_pages,
-                              const int64_t* src_pg_off, const int32_t* src_ids,
-                              int32_t num_reqs, const int64_t* tok_off,
-                              uint8_t* const* dst_planes, int64_t dst_stride,
-                              int32_t dst_page_size, int64_t dst_num_pages,
-                              const int64_t* dst_pg_off, const int32_t* dst_ids,
-                              int nthreads)
-{
-    return oracle_gather_scatter_ps(Q, R, src_planes, src_stride, 0, src_page_size,
-                                    src_num_pages, src_pg_off, src_ids, num_reqs, tok_off,
-                                    dst_planes, dst_stride, 0, dst_page_size, dst_num_pages,
-                                    dst_pg_off, dst_ids, nthreads);
 }
 
 /* ---------------------------------------------------- head-sliced copies -- */
@@ -298,6 +286,7 @@ typedef struct {
     int64_t num_pages;
     const int64_t* pg_off;
     const int32_t* ids;
+    int64_t num_ids;
     int32_t H, h0, hnd;
 } head_side;
 
@@ -312,10 +301,12 @@ typedef struct {
 } head_job;
 
 /* Byte offset of head h of token t of request r within its plane, or -1 when
- * the page id is out of range. */
+ * its table index or page id is out of range (as for whole rows). */
 static int64_t head_offset(const head_side* s, int64_t Db, int64_t r, int64_t t, int64_t h)
 {
-    int64_t page = (int64_t)s->ids[s->pg_off[r] + t / s->page_size];
+    int64_t idx = s->pg_off[r] + t / s->page_size;
+    if (idx < 0 || idx >= s->num_ids) return -1;
+    int64_t page = (int64_t)s->ids[idx];
     if (page < 0 || page >= s->num_pages) return -1;
     int64_t row = t % s->page_size;
     if (s->hnd) return page * s->page_size * s->stride + (h * s->page_size + row) * Db;
@@ -351,11 +342,13 @@ int64_t oracle_gather_scatter_heads(int32_t Q, int32_t nh, int64_t Db,
                                     uint8_t* const* src_planes, int64_t src_stride,
                                     int32_t src_page_size, int64_t src_num_pages,
                                     const int64_t* src_pg_off, const int32_t* src_ids,
+                                    int64_t src_num_ids,
                                     int32_t src_H, int32_t src_h0, int32_t src_hnd,
                                     int32_t num_reqs, const int64_t* tok_off,
                                     uint8_t* const* dst_planes, int64_t dst_stride,
                                     int32_t dst_page_size, int64_t dst_num_pages,
                                     const int64_t* dst_pg_off, const int32_t* dst_ids,
+                                    int64_t dst_num_ids,
                                     int32_t dst_H, int32_t dst_h0, int32_t dst_hnd,
                                     int nthreads)
 {
@@ -363,9 +356,9 @@ int64_t oracle_gather_scatter_heads(int32_t Q, int32_t nh, int64_t Db,
     memset(&proto, 0, sizeof proto);
     proto.Q = Q; proto.nh = nh; proto.Db = Db; proto.num_reqs = num_reqs; proto.tok_off = tok_off;
     head_side s = {src_planes, src_stride, src_page_size, src_num_pages, src_pg_off, src_ids,
-                   src_H, src_h0, src_hnd};
+                   src_num_ids, src_H, src_h0, src_hnd};
     head_side d = {dst_planes, dst_stride, dst_page_size, dst_num_pages, dst_pg_off, dst_ids,
-                   dst_H, dst_h0, dst_hnd};
+                   dst_num_ids, dst_H, dst_h0, dst_hnd};
     proto.src = s;
     proto.dst = d;
     int64_t pairs = (int64_t)num_reqs * Q;

@@ -180,6 +180,65 @@ def _counter(skipped) -> None:
                          "(the library adds to its first element)")
 
 
+def _bytes_from(t: torch.Tensor, ptr: int) -> int:
+    """Bytes of t's storage from address ptr to the storage's end."""
+    st = t.untyped_storage()
+    return st.data_ptr() + st.nbytes() - ptr
+
+
+def _plane_tensors(planes, ptrs):
+    """(tensor, plane address) for each plane that is backed by a tensor."""
+    if isinstance(planes, torch.Tensor):
+        return [(planes, p) for p in ptrs]
+    return [(p, a) for p, a in zip(planes, ptrs) if isinstance(p, torch.Tensor)]
+
+
+def _check_pool(what: str, layout: "Layout", pool: "Pool", whole_pages: bool = False) -> None:
+    """The C side reads planes[q] for every plane of the layout and addresses
+    each plane from its base: the pool must have exactly layout.planes planes,
+    and each tensor-backed plane must hold every byte a row of the pool can
+    occupy -- (num_pages - 1) * page_stride + (page_size - 1) * slot_stride +
+    R from its base, or num_pages * page_size * slot_stride for a pool of a
+    head-sliced copy (whole pages) -- inside its tensor's storage."""
+    if pool.num_planes != layout.planes:
+        raise ValueError(f"{what}: the pool has {pool.num_planes} planes, the layout "
+                         f"{layout.planes}")
+    if pool.num_pages <= 0 or pool.page_size <= 0:
+        return
+    if whole_pages:
+        need = pool.num_pages * pool.page_size * pool.slot_stride
+    else:
+        ps = pool.page_stride or pool.page_size * pool.slot_stride
+        need = ((pool.num_pages - 1) * ps + (pool.page_size - 1) * pool.slot_stride
+                + layout.row_bytes)
+    for t, ptr in _plane_tensors(pool._keep, list(pool._arr)[:pool.num_planes]):
+        if _bytes_from(t, ptr) < need:
+            raise ValueError(f"{what}: a plane holds {_bytes_from(t, ptr)} bytes from its "
+                             f"base, the pool's pages need {need}")
+
+
+def _check_hf(layout: "Layout", hf_planes, s_cap: int) -> None:
+    """Extract / rebuild: one [1, H, s_cap, D] plane per plane of the layout,
+    each tensor-backed plane holding H * s_cap * D elements from its base."""
+    n = hf_planes.shape[0] if isinstance(hf_planes, torch.Tensor) else len(hf_planes)
+    if n != layout.planes:
+        raise ValueError(f"hf_planes has {n} planes, the layout {layout.planes}")
+    need = layout.kv_heads * max(int(s_cap), 0) * layout.head_dim * _ELEM[layout.dtype]
+    if need == 0:
+        return
+    arr = _plane_array(hf_planes)
+    for t, ptr in _plane_tensors(hf_planes, list(arr)[:n]):
+        if _bytes_from(t, ptr) < need:
+            raise ValueError(f"an hf plane holds {_bytes_from(t, ptr)} bytes from its base, "
+                             f"[1, H, s_cap, D] needs {need}")
+
+
+def _check_table(what: str, table: "Table", reqs: "Requests") -> None:
+    if table.pg_off.dim() != 1 or table.pg_off.numel() < reqs.num_reqs + 1:
+        raise ValueError(f"{what}: pg_off needs num_reqs + 1 = {reqs.num_reqs + 1} entries, "
+                         f"got {table.pg_off.numel()}")
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -297,6 +356,8 @@ class Heads:
 def gather(layout: Layout, src: Pool, src_table: Table, reqs: Requests, staging: torch.Tensor,
            skipped: Optional[torch.Tensor] = None, stream=None) -> None:
     """Pool -> contiguous staging [request][plane][token][H][D] (kvx_gather)."""
+    _check_pool("src", layout, src)
+    _check_table("src_table", src_table, reqs)
     _dense("staging", staging)
     _counter(skipped)
     _on_device(src, src_table, reqs, staging, skipped)
@@ -309,6 +370,8 @@ def gather(layout: Layout, src: Pool, src_table: Table, reqs: Requests, staging:
 def scatter(layout: Layout, staging: torch.Tensor, reqs: Requests, dst: Pool, dst_table: Table,
             skipped: Optional[torch.Tensor] = None, stream=None) -> None:
     """Contiguous staging -> pool (kvx_scatter)."""
+    _check_pool("dst", layout, dst)
+    _check_table("dst_table", dst_table, reqs)
     _dense("staging", staging)
     _counter(skipped)
     _on_device(staging, reqs, dst, dst_table, skipped)
@@ -323,6 +386,10 @@ def gather_scatter(layout: Layout, src: Pool, src_table: Table, reqs: Requests, 
                    dst_table: Table, skipped: Optional[torch.Tensor] = None,
                    stream=None) -> None:
     """Pool -> pool, row by row, no staging (kvx_gather_scatter)."""
+    _check_pool("src", layout, src)
+    _check_pool("dst", layout, dst)
+    _check_table("src_table", src_table, reqs)
+    _check_table("dst_table", dst_table, reqs)
     _counter(skipped)
     _on_device(src, src_table, reqs, dst, dst_table, skipped)
     lib = load_library()
@@ -338,6 +405,10 @@ def gather_scatter_heads(layout: Layout, src: Pool, src_table: Table, src_heads:
     """Pool -> pool, layout.kv_heads heads of every token row, from heads
     src_heads.head0.. to dst_heads.head0.. (kvx_gather_scatter_heads).  The
     pools' slot_stride is the bytes of one token row in that pool."""
+    _check_pool("src", layout, src, whole_pages=True)
+    _check_pool("dst", layout, dst, whole_pages=True)
+    _check_table("src_table", src_table, reqs)
+    _check_table("dst_table", dst_table, reqs)
     _counter(skipped)
     _on_device(src, src_table, reqs, dst, dst_table, skipped)
     lib = load_library()
@@ -352,6 +423,7 @@ def gather_scatter_heads(layout: Layout, src: Pool, src_table: Table, src_heads:
 def extract_permute(layout: Layout, hf_planes: Union[torch.Tensor, Sequence], s_cap: int,
                     seq_len: int, out: torch.Tensor, stream=None) -> None:
     """[1, H, s_cap, D] per plane -> out [Q][seq_len][H][D] (kvx_extract_permute)."""
+    _check_hf(layout, hf_planes, s_cap)
     _planes_dense("hf_planes", hf_planes)
     _dense("out", out)
     _on_device(hf_planes, out)
@@ -366,6 +438,7 @@ def extract_permute(layout: Layout, hf_planes: Union[torch.Tensor, Sequence], s_
 def rebuild_permute(layout: Layout, flat: torch.Tensor, seq_len: int,
                     hf_planes: Union[torch.Tensor, Sequence], s_cap: int, stream=None) -> None:
     """flat [Q][seq_len][H][D] -> [1, H, s_cap, D] per plane (kvx_rebuild_permute)."""
+    _check_hf(layout, hf_planes, s_cap)
     _dense("flat", flat)
     _planes_dense("hf_planes", hf_planes)
     _on_device(flat, hf_planes)

@@ -726,6 +726,19 @@ struct Span {
     int64_t tok;
 };
 
+// A HOST copy of a batch's token CSR follows its contract: tok_off[0] = 0,
+// never decreasing, tok_off[num_reqs] = total_tokens (KVX_E_SHAPE otherwise).
+// Everything that indexes per-token arrays by tok_off checks this first.
+kvx_status check_tok_off(const kvx_reqs* reqs) {
+    const int32_t nr = reqs->num_reqs;
+    if (nr == 0) return reqs->total_tokens == 0 ? KVX_OK : KVX_E_SHAPE;
+    if (reqs->tok_off == nullptr) return KVX_E_NULL;
+    if (reqs->tok_off[0] != 0 || reqs->tok_off[nr] != reqs->total_tokens) return KVX_E_SHAPE;
+    for (int32_t r = 0; r < nr; ++r)
+        if (reqs->tok_off[r + 1] < reqs->tok_off[r]) return KVX_E_SHAPE;
+    return KVX_OK;
+}
+
 // Slot of every batch token in one pool side, or -1 where the call skips the
 // token (page-table index or page id out of range, as the kernels decide).
 kvx_status side_slots(const kvx_reqs* reqs, const kvx_pool* p, const kvx_table* t,
@@ -735,6 +748,7 @@ kvx_status side_slots(const kvx_reqs* reqs, const kvx_pool* p, const kvx_table* 
     if (t->num_ids < 0) return KVX_E_SHAPE;
     if (reqs->num_reqs > 0 && t->pg_off == nullptr) return KVX_E_NULL;
     if (t->num_ids > 0 && t->page_ids == nullptr) return KVX_E_NULL;
+    KVX_TRY(check_tok_off(reqs));
     slot->assign(static_cast<size_t>(reqs->total_tokens), -1);
     for (int32_t r = 0; r < reqs->num_reqs; ++r) {
         const int64_t off = reqs->tok_off[r], n = reqs->tok_off[r + 1] - off;
@@ -780,6 +794,64 @@ void side_spans(const Geom& g, const kvx_reqs* reqs, const kvx_pool* p,
 
 bool by_lo(const Span& a, const Span& b) { return a.lo < b.lo || (a.lo == b.lo && a.tok < b.tok); }
 
+// Written spans pairwise disjoint (else KVX_E_DUPLICATE), then no written span
+// sharing a byte with a read span (else KVX_E_OVERLAP); *bad receives the
+// batch token of an offending written span.  Sorts both vectors.
+kvx_status spans_disjoint(std::vector<Span>* w, std::vector<Span>* rd, int64_t* bad) {
+    std::sort(w->begin(), w->end(), by_lo);
+    uint64_t hi = 0;
+    for (const Span& x : *w) {
+        if (x.lo < hi) {
+            if (bad != nullptr) *bad = x.tok;
+            return KVX_E_DUPLICATE;
+        }
+        hi = x.hi;
+    }
+    std::sort(rd->begin(), rd->end(), by_lo);
+    std::vector<uint64_t> max_hi(rd->size());
+    uint64_t m = 0;
+    for (size_t i = 0; i < rd->size(); ++i) max_hi[i] = m = std::max(m, (*rd)[i].hi);
+    // a written span [lo, hi) meets a read span iff some read span starting
+    // before hi ends after lo
+    for (const Span& x : *w) {
+        const size_t i = static_cast<size_t>(
+            std::lower_bound(rd->begin(), rd->end(), x.hi,
+                             [](const Span& a, uint64_t v) { return a.lo < v; }) -
+            rd->begin());
+        if (i > 0 && max_hi[i - 1] > x.lo) {
+            if (bad != nullptr) *bad = x.tok;
+            return KVX_E_OVERLAP;
+        }
+    }
+    return KVX_OK;
+}
+
+// Head rows of the live tokens on one side of a head-sliced copy: for each
+// plane and each of the nh heads of the slice, Db bytes at the address the
+// kernels use (NHD or HND blocks, slice starting at h->head0).
+void head_spans(const Geom& g, const kvx_reqs* reqs, const kvx_pool* p, const kvx_heads* h,
+                const std::vector<int64_t>& slot, const std::vector<char>& live,
+                std::vector<Span>* out) {
+    out->clear();
+    const uint64_t B = static_cast<uint64_t>(p->page_size);
+    const uint64_t stride = static_cast<uint64_t>(p->slot_stride);
+    const uint64_t Db = static_cast<uint64_t>(g.Db);
+    for (int64_t tok = 0; tok < reqs->total_tokens; ++tok) {
+        if (!live[static_cast<size_t>(tok)]) continue;
+        const uint64_t s = static_cast<uint64_t>(slot[static_cast<size_t>(tok)]);
+        const uint64_t page = s / B, row = s % B;
+        for (int32_t q = 0; q < g.Q; ++q)
+            for (int32_t j = 0; j < g.H; ++j) {
+                const uint64_t hd = static_cast<uint64_t>(h->head0 + j);
+                const uint64_t off = h->block_layout == KVX_HND
+                                         ? page * B * stride + (hd * B + row) * Db
+                                         : (page * B + row) * stride + hd * Db;
+                const uint64_t lo = reinterpret_cast<uint64_t>(p->planes[q]) + off;
+                out->push_back(Span{lo, lo + Db, tok});
+            }
+    }
+}
+
 }  // namespace
 
 namespace {
@@ -823,31 +895,31 @@ kvx_status host_table(const kvx_table* t, int32_t nr, HostTable* h) {
     return KVX_OK;
 }
 
-// Head-sliced copies: destination slots of the live tokens pairwise distinct.
-kvx_status distinct_slots(const kvx_reqs* r, const kvx_pool* src, const kvx_table* st,
-                          const kvx_pool* dst, const kvx_table* dt, int64_t* bad) {
+// Head-sliced copies: the head rows the call writes pairwise disjoint and
+// none of them overlapping a head row it reads (tokens out of range on
+// either side are left out, as the kernels skip them).
+kvx_status heads_disjoint(const kvx_layout* layout, const kvx_reqs* r, const kvx_pool* src,
+                          const kvx_table* st, const kvx_heads* sh, const kvx_pool* dst,
+                          const kvx_table* dt, const kvx_heads* dh, int64_t* bad) {
+    Geom g;
+    KVX_TRY(check_layout(layout, &g));
     std::vector<int64_t> ss, ds;
     KVX_TRY(side_slots(r, src, st, &ss));
     KVX_TRY(side_slots(r, dst, dt, &ds));
-    std::vector<uint64_t> seen(static_cast<size_t>((dst->num_pages * dst->page_size + 63) / 64), 0);
-    for (int64_t t = 0; t < r->total_tokens; ++t) {
-        const int64_t d = ds[static_cast<size_t>(t)];
-        if (d < 0 || ss[static_cast<size_t>(t)] < 0) continue;
-        uint64_t& w = seen[static_cast<size_t>(d / 64)];
-        const uint64_t bit = uint64_t(1) << (d % 64);
-        if (w & bit) {
-            *bad = t;
-            return KVX_E_DUPLICATE;
-        }
-        w |= bit;
-    }
-    return KVX_OK;
+    std::vector<char> live(static_cast<size_t>(r->total_tokens), 1);
+    for (int64_t t = 0; t < r->total_tokens; ++t)
+        if (ss[static_cast<size_t>(t)] < 0 || ds[static_cast<size_t>(t)] < 0)
+            live[static_cast<size_t>(t)] = 0;
+    std::vector<Span> w, rd;
+    head_spans(g, r, dst, dh, ds, live, &w);
+    head_spans(g, r, src, sh, ss, live, &rd);
+    return spans_disjoint(&w, &rd, bad);
 }
 
 kvx_status validate_call(const kvx_layout* layout, const kvx_reqs* reqs, const kvx_pool* src,
                          const kvx_table* st, const kvx_pool* dst, const kvx_table* dt,
-                         const void* staging, int64_t staging_bytes, bool heads,
-                         hipStream_t stream) {
+                         const void* staging, int64_t staging_bytes, const kvx_heads* sh,
+                         const kvx_heads* dh, hipStream_t stream) {
     if (reqs->num_reqs == 0 || reqs->total_tokens == 0) return KVX_OK;
     if (hipStreamSynchronize(stream) != hipSuccess) return KVX_E_HIP;
     std::vector<int64_t> tok;
@@ -857,11 +929,13 @@ kvx_status validate_call(const kvx_layout* layout, const kvx_reqs* reqs, const k
     if (src != nullptr) KVX_TRY(host_table(st, reqs->num_reqs, &hs));
     if (dst != nullptr) KVX_TRY(host_table(dt, reqs->num_reqs, &hd));
     int64_t bad = -1;
-    const kvx_status s =
-        heads ? distinct_slots(&hr, src, &hs.t, dst, &hd.t, &bad)
-              : kvx_check_disjoint(layout, &hr, src, src != nullptr ? &hs.t : nullptr, dst,
-                                   dst != nullptr ? &hd.t : nullptr, staging, staging_bytes,
-                                   &bad);
+    kvx_status s = check_tok_off(&hr);
+    if (s == KVX_OK)
+        s = sh != nullptr
+                ? heads_disjoint(layout, &hr, src, &hs.t, sh, dst, &hd.t, dh, &bad)
+                : kvx_check_disjoint(layout, &hr, src, src != nullptr ? &hs.t : nullptr, dst,
+                                     dst != nullptr ? &hd.t : nullptr, staging, staging_bytes,
+                                     &bad);
     if (s != KVX_OK)
         std::fprintf(stderr, "kvx: KVX_VALIDATE: %s (batch token %lld); nothing enqueued\n",
                      kvx_status_str(s), static_cast<long long>(bad));
@@ -884,7 +958,7 @@ kvx_status kvx_gather(const kvx_layout* layout, const kvx_pool* src, const kvx_t
     KVX_TRY(check_staging(staging, staging_bytes, g, reqs));
     if (validate_enabled())
         KVX_TRY(validate_call(layout, reqs, src, src_table, nullptr, nullptr, staging,
-                              staging_bytes, false, stream));
+                              staging_bytes, nullptr, nullptr, stream));
     return run_paged<PoolRef, StageRef>(0, g, reqs, src, src_table, nullptr, nullptr, nullptr,
                                         staging, skipped, stream);
 }
@@ -900,7 +974,7 @@ kvx_status kvx_scatter(const kvx_layout* layout, const void* staging, int64_t st
     KVX_TRY(check_staging(staging, staging_bytes, g, reqs));
     if (validate_enabled())
         KVX_TRY(validate_call(layout, reqs, nullptr, nullptr, dst, dst_table, staging,
-                              staging_bytes, false, stream));
+                              staging_bytes, nullptr, nullptr, stream));
     return run_paged<StageRef, PoolRef>(1, g, reqs, nullptr, nullptr, const_cast<void*>(staging),
                                         dst, dst_table, nullptr, skipped, stream);
 }
@@ -919,8 +993,8 @@ kvx_status kvx_gather_scatter(const kvx_layout* layout,
     KVX_TRY(check_pool(dst, g));
     KVX_TRY(check_table(dst_table, reqs));
     if (validate_enabled())
-        KVX_TRY(validate_call(layout, reqs, src, src_table, dst, dst_table, nullptr, 0, false,
-                              stream));
+        KVX_TRY(validate_call(layout, reqs, src, src_table, dst, dst_table, nullptr, 0, nullptr,
+                              nullptr, stream));
     return run_paged<PoolRef, PoolRef>(2, g, reqs, src, src_table, nullptr, dst, dst_table,
                                        nullptr, skipped, stream);
 }
@@ -944,8 +1018,8 @@ kvx_status kvx_gather_scatter_heads(const kvx_layout* layout,
     KVX_TRY(check_table(dst_table, reqs));
     KVX_TRY(check_heads(dst_heads, dst, g));
     if (validate_enabled())
-        KVX_TRY(validate_call(layout, reqs, src, src_table, dst, dst_table, nullptr, 0, true,
-                              stream));
+        KVX_TRY(validate_call(layout, reqs, src, src_table, dst, dst_table, nullptr, 0,
+                              src_heads, dst_heads, stream));
     return run_heads(g, reqs, src, src_table, src_heads, dst, dst_table, dst_heads, skipped,
                      stream);
 }
@@ -1032,11 +1106,7 @@ kvx_status kvx_check_disjoint(const kvx_layout* layout, const kvx_reqs* reqs,
     Geom g;
     KVX_TRY(check_layout(layout, &g));
     KVX_TRY(check_reqs(reqs));
-    const int32_t nr = reqs->num_reqs;
-    if (nr > 0 && (reqs->tok_off[0] != 0 || reqs->tok_off[nr] != reqs->total_tokens))
-        return KVX_E_SHAPE;
-    for (int32_t r = 0; r < nr; ++r)
-        if (reqs->tok_off[r + 1] < reqs->tok_off[r]) return KVX_E_SHAPE;
+    KVX_TRY(check_tok_off(reqs));
     if ((src == nullptr) != (src_table == nullptr) || (dst == nullptr) != (dst_table == nullptr))
         return KVX_E_NULL;
     if (src == nullptr && dst == nullptr) return KVX_E_UNSUPPORTED;
@@ -1057,34 +1127,8 @@ kvx_status kvx_check_disjoint(const kvx_layout* layout, const kvx_reqs* reqs,
             live[static_cast<size_t>(t)] = 0;
     std::vector<Span> w, rd;
     side_spans(g, reqs, dst, ds, staging, live, &w);
-    std::sort(w.begin(), w.end(), by_lo);
-    // written rows pairwise disjoint: each starts at or after every earlier end
-    uint64_t hi = 0;
-    for (const Span& x : w) {
-        if (x.lo < hi) {
-            if (bad_token != nullptr) *bad_token = x.tok;
-            return KVX_E_DUPLICATE;
-        }
-        hi = x.hi;
-    }
     side_spans(g, reqs, src, ss, staging, live, &rd);
-    std::sort(rd.begin(), rd.end(), by_lo);
-    std::vector<uint64_t> max_hi(rd.size());
-    uint64_t m = 0;
-    for (size_t i = 0; i < rd.size(); ++i) max_hi[i] = m = std::max(m, rd[i].hi);
-    // a written row [lo, hi) meets a read row iff some read row starting
-    // before hi ends after lo
-    for (const Span& x : w) {
-        const size_t i = static_cast<size_t>(
-            std::lower_bound(rd.begin(), rd.end(), x.hi,
-                             [](const Span& a, uint64_t v) { return a.lo < v; }) -
-            rd.begin());
-        if (i > 0 && max_hi[i - 1] > x.lo) {
-            if (bad_token != nullptr) *bad_token = x.tok;
-            return KVX_E_OVERLAP;
-        }
-    }
-    return KVX_OK;
+    return spans_disjoint(&w, &rd, bad_token);
 }
 
 const char* kvx_status_str(int32_t status) {

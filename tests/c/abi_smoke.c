@@ -16,32 +16,37 @@
 
 /* oracle/kvx_oracle.c (test infrastructure) */
 int64_t oracle_gather(int32_t Q, int64_t R, uint8_t* const* src_planes, int64_t src_stride,
-                      int32_t src_page_size, int64_t src_num_pages, int32_t num_reqs,
-                      const int64_t* tok_off, const int64_t* src_pg_off, const int32_t* src_ids,
-                      uint8_t* staging, int nthreads);
+                      int64_t src_page_stride, int32_t src_page_size, int64_t src_num_pages,
+                      int32_t num_reqs, const int64_t* tok_off, const int64_t* src_pg_off,
+                      const int32_t* src_ids, int64_t src_num_ids, uint8_t* staging,
+                      int nthreads);
 int64_t oracle_scatter(int32_t Q, int64_t R, const uint8_t* staging, int32_t num_reqs,
                        const int64_t* tok_off, const int64_t* dst_pg_off, const int32_t* dst_ids,
-                       uint8_t* const* dst_planes, int64_t dst_stride, int32_t dst_page_size,
-                       int64_t dst_num_pages, int nthreads);
+                       int64_t dst_num_ids, uint8_t* const* dst_planes, int64_t dst_stride,
+                       int64_t dst_page_stride, int32_t dst_page_size, int64_t dst_num_pages,
+                       int nthreads);
 int64_t oracle_gather_scatter_heads(int32_t Q, int32_t nh, int64_t Db, uint8_t* const* src_planes,
                                     int64_t src_stride, int32_t src_page_size,
                                     int64_t src_num_pages, const int64_t* src_pg_off,
-                                    const int32_t* src_ids, int32_t src_H, int32_t src_h0,
-                                    int32_t src_hnd, int32_t num_reqs, const int64_t* tok_off,
-                                    uint8_t* const* dst_planes, int64_t dst_stride,
-                                    int32_t dst_page_size, int64_t dst_num_pages,
-                                    const int64_t* dst_pg_off, const int32_t* dst_ids,
-                                    int32_t dst_H, int32_t dst_h0, int32_t dst_hnd, int nthreads);
+                                    const int32_t* src_ids, int64_t src_num_ids, int32_t src_H,
+                                    int32_t src_h0, int32_t src_hnd, int32_t num_reqs,
+                                    const int64_t* tok_off, uint8_t* const* dst_planes,
+                                    int64_t dst_stride, int32_t dst_page_size,
+                                    int64_t dst_num_pages, const int64_t* dst_pg_off,
+                                    const int32_t* dst_ids, int64_t dst_num_ids, int32_t dst_H,
+                                    int32_t dst_h0, int32_t dst_hnd, int nthreads);
 int64_t oracle_extract_permute(int32_t Q, int32_t H, int64_t Db, uint8_t* const* hf_planes,
                                int64_t s_cap, int64_t seq, uint8_t* out, int nthreads);
 int64_t oracle_rebuild_permute(int32_t Q, int32_t H, int64_t Db, const uint8_t* in, int64_t seq,
                                uint8_t* const* hf_planes, int64_t s_cap, int nthreads);
 int64_t oracle_gather_scatter(int32_t Q, int64_t R, uint8_t* const* src_planes,
-                              int64_t src_stride, int32_t src_page_size, int64_t src_num_pages,
-                              const int64_t* src_pg_off, const int32_t* src_ids, int32_t num_reqs,
+                              int64_t src_stride, int64_t src_page_stride, int32_t src_page_size,
+                              int64_t src_num_pages, const int64_t* src_pg_off,
+                              const int32_t* src_ids, int64_t src_num_ids, int32_t num_reqs,
                               const int64_t* tok_off, uint8_t* const* dst_planes,
-                              int64_t dst_stride, int32_t dst_page_size, int64_t dst_num_pages,
-                              const int64_t* dst_pg_off, const int32_t* dst_ids, int nthreads);
+                              int64_t dst_stride, int64_t dst_page_stride, int32_t dst_page_size,
+                              int64_t dst_num_pages, const int64_t* dst_pg_off,
+                              const int32_t* dst_ids, int64_t dst_num_ids, int nthreads);
 
 #define CHECK_HIP(x)                                                              \
     do {                                                                          \
@@ -165,10 +170,11 @@ int main(void) {
     CHECK_HIP(hipMemcpy(&skipped, skipped_d, sizeof skipped, hipMemcpyDeviceToHost));
 
     memcpy(exp_dst, dst_h, Q * dplane);
-    int64_t s1 = oracle_gather_scatter(Q, R, splanes_h, R, SRC_PAGE, SRC_PAGES, spg, sperm, NREQ,
-                                       tok_off, dplanes_h, R, DST_PAGE, DST_PAGES, dpg, dperm, 1);
-    int64_t s2 = oracle_gather(Q, R, splanes_h, R, SRC_PAGE, SRC_PAGES, NREQ, tok_off, spg, sperm,
-                               exp_st, 1);
+    int64_t s1 = oracle_gather_scatter(Q, R, splanes_h, R, 0, SRC_PAGE, SRC_PAGES, spg, sperm,
+                                       SRC_PAGES, NREQ, tok_off, dplanes_h, R, 0, DST_PAGE,
+                                       DST_PAGES, dpg, dperm, DST_PAGES, 1);
+    int64_t s2 = oracle_gather(Q, R, splanes_h, R, 0, SRC_PAGE, SRC_PAGES, NREQ, tok_off, spg,
+                               sperm, SRC_PAGES, exp_st, 1);
     if (memcmp(got_dst, exp_dst, Q * dplane) != 0) { fprintf(stderr, "gather_scatter differs\n"); return 7; }
     if (memcmp(got_st, exp_st, stage_bytes) != 0) { fprintf(stderr, "gather differs\n"); return 8; }
     if ((int64_t)skipped != s1 + s2 || skipped != 0) { fprintf(stderr, "skip count %llu\n", skipped); return 9; }
@@ -189,7 +195,8 @@ int main(void) {
         CHECK_HIP(hipStreamSynchronize(stream));
         CHECK_HIP(hipMemcpy(got, e_d, Q * dplane, hipMemcpyDeviceToHost));
         memcpy(exp, dst_h, Q * dplane);
-        oracle_scatter(Q, R, got_st, NREQ, tok_off, dpg, dperm, eplanes_h, R, DST_PAGE, DST_PAGES, 1);
+        oracle_scatter(Q, R, got_st, NREQ, tok_off, dpg, dperm, DST_PAGES, eplanes_h, R, 0,
+                       DST_PAGE, DST_PAGES, 1);
         if (memcmp(got, exp, Q * dplane) != 0) { fprintf(stderr, "scatter differs\n"); return 10; }
         hipFree(e_d); free(got); free(exp);
     }
@@ -217,9 +224,9 @@ int main(void) {
         CHECK_HIP(hipStreamSynchronize(stream));
         CHECK_HIP(hipMemcpy(got, h_d, Q * hplane, hipMemcpyDeviceToHost));
         memcpy(exp, init, Q * hplane);
-        oracle_gather_scatter_heads(Q, NH, DB, splanes_h, R, SRC_PAGE, SRC_PAGES, spg, sperm, H, 1, 1,
-                                    NREQ, tok_off, hplanes_h, NH * DB, DST_PAGE, DST_PAGES, dpg,
-                                    dperm, NH, 0, 0, 1);
+        oracle_gather_scatter_heads(Q, NH, DB, splanes_h, R, SRC_PAGE, SRC_PAGES, spg, sperm,
+                                    SRC_PAGES, H, 1, 1, NREQ, tok_off, hplanes_h, NH * DB,
+                                    DST_PAGE, DST_PAGES, dpg, dperm, DST_PAGES, NH, 0, 0, 1);
         if (memcmp(got, exp, Q * hplane) != 0) { fprintf(stderr, "heads differ\n"); return 11; }
         hipFree(h_d); free(init); free(got); free(exp);
     }

@@ -39,19 +39,25 @@ def planes_of(pool):
     return [pool[q].reshape(-1).view(np.uint8) for q in range(pool.shape[0])]
 
 
+def slot_of(side, r, t):
+    """Slot of token t of request r, written out from the definition: entry
+    pg_off[r] + t // B of the page-id list (-1 when that index is outside the
+    list), page id out of [0, num_pages) -> -1, else page * B + t % B."""
+    idx = int(side.pg_off[r]) + t // side.page_size
+    if idx < 0 or idx >= side.ids.size:
+        return -1
+    page = int(side.ids[idx])
+    if page < 0 or page >= side.num_pages:
+        return -1
+    return page * side.page_size + t % side.page_size
+
+
 def slot_lists(case, side):
-    """Expanded per-request slot lists: whole pages laid out, then truncated."""
+    """Per-request slot lists, token by token (-1 marks a skipped token)."""
     out = []
     for r in range(case.num_reqs):
         n = int(case.tok_off[r + 1] - case.tok_off[r])
-        pages = side.ids[side.pg_off[r]:side.pg_off[r + 1]].astype(np.int64)
-        full = [np.arange(p * side.page_size, (p + 1) * side.page_size) for p in pages]
-        flat = np.concatenate(full) if full else np.zeros(0, np.int64)
-        # an out-of-range page expands to slots that are flagged -1
-        bad = np.concatenate([np.full(side.page_size, (p < 0) or (p >= side.num_pages))
-                              for p in pages]) if full else np.zeros(0, bool)
-        flat = np.where(bad, -1, flat)
-        out.append(flat[:n])
+        out.append(np.array([slot_of(side, r, t) for t in range(n)], dtype=np.int64))
     return out
 
 
@@ -121,14 +127,20 @@ def o_gather_scatter(src_pool, case, dst_pool, nthreads=1):
                                  case.dst.pg_off, case.dst.ids, nthreads)
 
 
-def tiny_cases(oor=0.0):
+def tiny_cases(oor=0.0, index_faults=False):
     geoms = [wl.Geometry(1, 2, 1, 8), wl.Geometry(2, 1, 3, 8), wl.Geometry(1, 2, 2, 16)]
     cases = []
     for i, g in enumerate(geoms):
         for bs, bd in [(1, 1), (2, 4), (4, 2), (3, 1)]:
-            cases.append(wl.random_case(100 * i + 10 * bs + bd, geom=g, max_reqs=3, max_len=9,
-                                        src_page=bs, dst_page=bd, oor_frac=oor, slack_pages=2))
+            cases.append(wl.random_case(100 * i + 10 * bs + bd + (7 if index_faults else 0),
+                                        geom=g, max_reqs=4 if index_faults else 3, max_len=9,
+                                        src_page=bs, dst_page=bd, oor_frac=oor, slack_pages=2,
+                                        index_faults=index_faults))
     return cases
+
+
+# (out-of-range page-id fraction, page-table index faults) of the brute-force sweeps
+FAULTS = [(0.0, False), (0.2, False), (0.0, True), (0.2, True)]
 
 
 def pools_for(case, rng):
@@ -142,8 +154,8 @@ def pools_for(case, rng):
 
 def check_gather_bruteforce():
     rng = np.random.default_rng(7)
-    for oor in (0.0, 0.2):
-        for case in tiny_cases(oor):
+    for oor, faults in FAULTS:
+        for case in tiny_cases(oor, faults):
             src, _ = pools_for(case, rng)
             g = case.geom
             expect, bf_skip = bf_gather(src, case, case.src)
@@ -167,8 +179,8 @@ def _skipped_mask(case, side, g):
 
 def check_scatter_bruteforce():
     rng = np.random.default_rng(8)
-    for oor in (0.0, 0.2):
-        for case in tiny_cases(oor):
+    for oor, faults in FAULTS:
+        for case in tiny_cases(oor, faults):
             g = case.geom
             _, dst = pools_for(case, rng)
             stage = rng.integers(0, 1 << 16, size=case.total_tokens * g.planes * g.kv_heads
@@ -183,8 +195,8 @@ def check_scatter_bruteforce():
 
 def check_gather_scatter_bruteforce():
     rng = np.random.default_rng(9)
-    for oor in (0.0, 0.2):
-        for case in tiny_cases(oor):
+    for oor, faults in FAULTS:
+        for case in tiny_cases(oor, faults):
             g = case.geom
             src, dst = pools_for(case, rng)
             got = dst.copy()
@@ -401,8 +413,12 @@ def check_mixed_strides():
 
 
 def _page_of(side, r, t):
-    """Page id of token t of request r, or None when it is out of range."""
-    page = int(side.ids[side.pg_off[r] + t // side.page_size])
+    """Page id of token t of request r, or None when its page-table index or
+    the id there is out of range."""
+    idx = int(side.pg_off[r]) + t // side.page_size
+    if idx < 0 or idx >= side.ids.size:
+        return None
+    page = int(side.ids[idx])
     return page if 0 <= page < side.num_pages else None
 
 
@@ -515,6 +531,67 @@ def check_oor_boundaries():
     assert np.array_equal(out2[:, P * B:], pool[:, P * B:])
 
 
+def check_table_index_boundaries():
+    """A worked example of the page-table reads (pages of B = 2 tokens, five
+    requests, three page ids held between two guard entries that name real
+    pages): request 0's list starts one entry before the array (its first
+    page is skipped), request 1's second page lies one past the end
+    (skipped), request 2 has an empty list and reads on into the entries
+    after its start, and requests 3 and 4 start 2**62 entries before and
+    after the array (skipped).  Expected rows are written out by hand; every
+    skipped row is counted and leaves its destination untouched, and the
+    guards are never read."""
+    rng = np.random.default_rng(27)
+    Q, H, D, B, P = 2, 1, 8, 2, 4
+    big = 1 << 62
+    lens = [4, 4, 2, 2, 2]
+    tok_off = wl.csr_from_lengths(lens)
+    guard = 2                                   # a real page: reading a guard copies rows
+    s_buf = np.array([guard, 1, 3, 0, guard], np.int32)
+    d_buf = np.array([guard, 1, 3, 0, guard], np.int32)
+    src_side = wl.Side(P, B, np.array([-1, 2, 0, -big, big, 3], np.int64), s_buf[1:4])
+    dst_side = wl.Side(P, B, np.array([-1, 2, 1, -big, big, 3], np.int64), d_buf[1:4])
+    assert src_side.ids.base is s_buf          # a view: the guards sit around it in memory
+    case = wl.PagedCase("idx", wl.Geometry(1, 2, H, D), tok_off, src_side, dst_side, 0, 0, 0)
+    # (request, token) -> slot, by hand
+    src_slots = {(0, 2): 2, (0, 3): 3, (1, 0): 0, (1, 1): 1, (2, 0): 2, (2, 1): 3}
+    dst_slots = {(0, 2): 2, (0, 3): 3, (1, 0): 0, (1, 1): 1, (2, 0): 6, (2, 1): 7}
+    tokens = [(r, t) for r, n in enumerate(lens) for t in range(n)]
+    pool = rand_pool(rng, Q, P * B, H, D)
+    # gather
+    n = sum(lens)
+    st = np.full((n * Q, H, D), 0x7E7E, np.uint16)
+    assert o_gather(pool, case, case.src, st.reshape(-1)) == Q * (n - len(src_slots))
+    exp = np.full_like(st, 0x7E7E)
+    for (r, t) in tokens:
+        if (r, t) in src_slots:
+            for q in range(Q):
+                exp[tok_off[r] * Q + q * lens[r] + t] = pool[q, src_slots[(r, t)]]
+    assert np.array_equal(st, exp)
+    # scatter
+    stage = rng.integers(0, 1 << 16, size=(n * Q, H, D), dtype=np.uint16)
+    dst = rand_pool(rng, Q, P * B, H, D)
+    got = dst.copy()
+    assert o_scatter(stage.reshape(-1), case, case.dst, got) == Q * (n - len(dst_slots))
+    exp = dst.copy()
+    for (r, t), slot in dst_slots.items():
+        for q in range(Q):
+            exp[q, slot] = stage[tok_off[r] * Q + q * lens[r] + t]
+    assert np.array_equal(got, exp)
+    # gather-scatter, and the head-sliced copy of the whole row
+    both = [k for k in tokens if k in src_slots and k in dst_slots]
+    exp = dst.copy()
+    for (r, t) in both:
+        exp[:, dst_slots[(r, t)]] = pool[:, src_slots[(r, t)]]
+    got = dst.copy()
+    assert o_gather_scatter(pool, case, got) == Q * (n - len(both))
+    assert np.array_equal(got, exp)
+    got = dst.copy()
+    assert o_heads(case, pool.reshape(Q, -1).view(np.uint8), got.reshape(Q, -1).view(np.uint8),
+                   H, 0, 0, H, 0, 0, H, D) == Q * (n - len(both))
+    assert np.array_equal(got, exp)
+
+
 # -------------------------------------------------- head-sliced copies --
 
 def head_view(pool_bytes, Q, P, B, H, D, hnd):
@@ -533,7 +610,7 @@ def o_heads(case, src_b, dst_b, sH, sh0, shnd, dH, dh0, dhnd, nh, D, nthreads=1)
         case.dst.pg_off, case.dst.ids, (dH, dh0, dhnd), nthreads)
 
 
-def heads_case(seed, oor=0.0):
+def heads_case(seed, oor=0.0, index_faults=False):
     rng = np.random.default_rng(seed)
     D = int(rng.choice([8, 16]))
     sH, dH = int(rng.integers(1, 6)), int(rng.integers(1, 6))
@@ -542,15 +619,16 @@ def heads_case(seed, oor=0.0):
     shnd, dhnd = int(rng.integers(0, 2)), int(rng.integers(0, 2))
     case = wl.random_case(seed, geom=wl.Geometry(int(rng.integers(1, 3)), 2, nh, D), max_reqs=3,
                           max_len=12, src_page=int(rng.choice([1, 2, 4])),
-                          dst_page=int(rng.choice([1, 3, 4])), oor_frac=oor, slack_pages=2)
+                          dst_page=int(rng.choice([1, 3, 4])), oor_frac=oor, slack_pages=2,
+                          index_faults=index_faults)
     return case, D, (sH, sh0, shnd), (dH, dh0, dhnd), nh
 
 
 def check_heads_bruteforce():
     """Element by element over NHD / HND views of both pools."""
-    for seed in range(24):
-        case, D, (sH, sh0, shnd), (dH, dh0, dhnd), nh = heads_case(900 + seed,
-                                                                   oor=0.2 if seed % 3 else 0)
+    for seed in range(32):
+        case, D, (sH, sh0, shnd), (dH, dh0, dhnd), nh = heads_case(
+            900 + seed, oor=0.2 if seed % 3 else 0, index_faults=seed >= 16)
         rng = np.random.default_rng(seed)
         Q = case.geom.planes
         Ps, Pd, Bs, Bd = case.src.num_pages, case.dst.num_pages, case.src.page_size, \
@@ -565,10 +643,9 @@ def check_heads_bruteforce():
         bf_skip = 0
         for r in range(case.num_reqs):
             for t in range(int(case.lengths[r])):
-                ps = int(case.src.ids[case.src.pg_off[r] + t // Bs])
-                pd = int(case.dst.ids[case.dst.pg_off[r] + t // Bd])
+                ps, pd = _page_of(case.src, r, t), _page_of(case.dst, r, t)
                 for q in range(Q):
-                    if not (0 <= ps < Ps and 0 <= pd < Pd):
+                    if ps is None or pd is None:
                         bf_skip += 1
                         continue
                     for j in range(nh):
@@ -757,6 +834,7 @@ ALL_CHECKS = [
     check_numpy_transpose,
     check_closed_form_sizes,
     check_oor_boundaries,
+    check_table_index_boundaries,
     check_heads_bruteforce,
     check_heads_full_row_is_row_copy,
     check_heads_layout_conversion,

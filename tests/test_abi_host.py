@@ -380,3 +380,53 @@ def test_binding_refuses_strided_views():
     with pytest.raises(ValueError, match="skipped must be"):
         kvx.gather_scatter(lay, pool, tab, reqs, pool, tab,
                            skipped=torch.zeros(0, dtype=torch.int64))
+
+
+def test_binding_checks_plane_counts_and_extents():
+    """The C side reads one plane pointer per plane of the layout and
+    addresses each plane from its base, so the binding refuses a pool or an
+    HF plane list with another plane count, a tensor-backed plane whose
+    storage ends before the pool's last row (or last whole page, for a
+    head-sliced copy) or before [1, H, s_cap, D], and a page-offset array
+    shorter than num_reqs + 1 -- before anything reaches the library."""
+    import torch
+    lay = kvx.Layout(1, 2, 1, 8, "bf16")                      # Q = 2, R = 16
+    reqs = kvx.Requests(torch.tensor([0, 2], dtype=torch.int64), 2)
+    tab = kvx.Table(torch.zeros(2, dtype=torch.int64), torch.zeros(2, dtype=torch.int32))
+    st = torch.zeros(64, dtype=torch.uint8)
+    three = kvx.Pool(torch.zeros((3, 4, 16), dtype=torch.uint8), 4)
+    with pytest.raises(ValueError, match="3 planes, the layout 2"):
+        kvx.gather(lay, three, tab, reqs, st)
+    with pytest.raises(ValueError, match="3 planes, the layout 2"):
+        kvx.gather_scatter(lay, three, tab, reqs, three, tab)
+    one = kvx.Pool([torch.zeros(64, dtype=torch.uint8)], 4, slot_stride=16)
+    with pytest.raises(ValueError, match="1 planes, the layout 2"):
+        kvx.scatter(lay, st, reqs, one, tab)
+    # a pool that claims more pages than its tensor holds
+    big = kvx.Pool(torch.zeros((2, 4, 16), dtype=torch.uint8), 5, slot_stride=16)
+    with pytest.raises(ValueError, match="the pool's pages need 80"):
+        kvx.gather(lay, big, tab, reqs, st)
+    planes = [torch.zeros(64, dtype=torch.uint8), torch.zeros(48, dtype=torch.uint8)]
+    with pytest.raises(ValueError, match="holds 48 bytes"):
+        kvx.gather(lay, kvx.Pool(planes, 4, slot_stride=16), tab, reqs, st)
+    # token-major planes (stride Q * R, bases R apart) fit in their storage
+    tm = torch.zeros((4, 2, 16), dtype=torch.uint8)
+    kvx._check_pool("tm", lay, kvx.Pool(tm.transpose(0, 1), 4, slot_stride=32))
+    with pytest.raises(ValueError, match="the pool's pages need"):
+        kvx._check_pool("tm", lay, kvx.Pool(tm.transpose(0, 1), 5, slot_stride=32))
+    # head-sliced copies address whole pages: 4 pages x 2 rows x 32 bytes per plane
+    hp = kvx.Pool(torch.zeros((2, 255), dtype=torch.uint8), 4, page_size=2, slot_stride=32)
+    with pytest.raises(ValueError, match="need 256"):
+        kvx.gather_scatter_heads(lay, hp, tab, kvx.Heads(2, 0), reqs, hp, tab, kvx.Heads(2, 0))
+    # page offsets for every request plus one
+    with pytest.raises(ValueError, match="pg_off needs num_reqs \\+ 1 = 2"):
+        kvx.gather(lay, kvx.Pool(torch.zeros((2, 4, 16), dtype=torch.uint8), 4),
+                   kvx.Table(torch.zeros(1, dtype=torch.int64), torch.zeros(2, dtype=torch.int32)),
+                   reqs, st)
+    # HF planes: one per plane, each [1, H, s_cap, D]
+    with pytest.raises(ValueError, match="hf_planes has 3 planes"):
+        kvx.extract_permute(lay, torch.zeros((3, 32), dtype=torch.uint8), 2, 1, st)
+    with pytest.raises(ValueError, match="hf_planes has 1 planes"):
+        kvx.rebuild_permute(lay, st, 1, [torch.zeros(32, dtype=torch.uint8)], 2)
+    with pytest.raises(ValueError, match="needs 48"):
+        kvx.extract_permute(lay, torch.zeros((2, 32), dtype=torch.uint8), 3, 1, st)

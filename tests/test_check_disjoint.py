@@ -139,6 +139,41 @@ def test_against_brute_force(seed):
     assert OK in seen
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_index_faults_against_brute_force(seed):
+    """Page-table offsets that send lookups outside the page-id array or into
+    another request's list: those tokens are left out on both sides."""
+    case = wl.random_case(9700 + seed, max_reqs=5, max_len=20, src_page=1 + seed % 3,
+                          dst_page=1 + seed % 2, slack_pages=3, index_faults=True)
+    g = case.geom
+    Q, R = g.planes, g.row_bytes
+    a = Side(case.src, planes(Q, BASE), R)
+    b = Side(case.dst, planes(Q, BASE + (1 << 36)), R)
+    check(g, case, a, b)
+    check(g, case, a, None, staging=BASE + (1 << 38), nbytes=case.total_tokens * Q * R)
+    check(g, case, a, Side(case.dst, planes(Q, BASE), R))
+
+
+@pytest.mark.parametrize("tok_off,total", [([0, 9 + 7], 7), ([0, 5, 3, 7], 7), ([1, 7], 7),
+                                           ([0, 6], 7)])
+def test_token_offsets_breaking_the_contract(tok_off, total):
+    """A token CSR that runs past total_tokens, decreases, starts above 0 or
+    ends short is refused with KVX_E_SHAPE before anything is indexed by it."""
+    g = wl.Geometry(1, 2, 1, 8)
+    side = wl.Side(16, 1, np.zeros(len(tok_off), np.int64), np.arange(16, dtype=np.int32))
+    a = Side(side, planes(g.planes, BASE), g.row_bytes)
+    b = Side(side, planes(g.planes, BASE + (1 << 36)), g.row_bytes)
+    lib = kvx.load_library()
+    lay = kvx._CLayout(1, 2, 1, 8, 2)
+    tok = np.ascontiguousarray(tok_off, dtype=np.int64)
+    reqs = kvx._CReqs(tok.size - 1, total, tok.ctypes.data)
+    bad = ctypes.c_int64(-7)
+    assert lib.kvx_check_disjoint(ctypes.byref(lay), ctypes.byref(reqs), ctypes.byref(a.pool),
+                                  ctypes.byref(a.table), ctypes.byref(b.pool),
+                                  ctypes.byref(b.table), None, 0, ctypes.byref(bad)) == E_SHAPE
+    assert bad.value == -1
+
+
 def test_workload_tables_are_disjoint():
     # the two-pool workloads, with pools laid out as the bench allocates them
     for case in (wl.config1(), wl.config2(5), wl.config5()):

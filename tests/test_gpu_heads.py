@@ -73,6 +73,16 @@ def test_heads_out_of_range(seed):
     run_heads(case, sH, dH, nh, sh0, dh0, D, seed % 2, (seed // 2) % 2, 100 + seed)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_heads_table_index_faults(seed):
+    """Page-table offsets outside the page-id array or into another request's
+    list, on both sides of a head-sliced copy, every layout pair."""
+    sH, dH, nh, sh0, dh0, D = SLICES[seed % 6]
+    case = wl.random_case(7200 + seed, geom=wl.Geometry(1, 2, nh, D), max_reqs=6, max_len=50,
+                          oor_frac=0.1 if seed % 2 else 0.0, index_faults=True)
+    run_heads(case, sH, dH, nh, sh0, dh0, D, seed % 2, (seed // 2) % 2, 200 + seed)
+
+
 # Batches beyond the 64-request window of the request lookup, with empty
 # requests: (requests, fraction empty, page size, src HND?, dst HND?).  HND on
 # both sides with one page size <= 64 takes the page-run kernel.

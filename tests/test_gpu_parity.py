@@ -100,6 +100,43 @@ def test_paged_out_of_range_ids(seed):
     run_paged_case(case, seed)
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_paged_table_index_faults(seed):
+    """Page-table offsets that send lookups below 0, past the end of the
+    page-id array or into another request's list (random_case's
+    index_faults), alone and with out-of-range ids: whole destinations and
+    skip counts against the oracle.  Seeds 12-15 take batches above 64
+    requests (the many-request lookup)."""
+    g, max_len = GEOMS[(3 * seed) % len(GEOMS)]
+    many = seed >= 12
+    k = 0
+    while True:                     # the first seed of the family that fits
+        case = wl.random_case(5600 + 100 * k + seed, geom=g, max_reqs=120 if many else 6,
+                              max_len=min(max_len, 6) if many else max_len,
+                              oor_frac=0.1 if seed % 2 else 0.0, index_faults=True)
+        if not many or case.num_reqs > 64:
+            break
+        k += 1
+    run_paged_case(case, seed)
+
+
+def test_paged_table_index_worked_example():
+    """The oracle pin's worked example of the page-table reads on the GPU:
+    a list starting one entry early, a page one past the end of the array, an
+    empty list that reads on into the next entries, and offsets 2**62 before
+    and after the array."""
+    big = 1 << 62
+    lens = [4, 4, 2, 2, 2]
+    src = wl.Side(4, 2, np.array([-1, 2, 0, -big, big, 3], np.int64),
+                  np.array([1, 3, 0], np.int32))
+    dst = wl.Side(4, 2, np.array([-1, 2, 1, -big, big, 3], np.int64),
+                  np.array([1, 3, 0], np.int32))
+    for g in (wl.Geometry(1, 2, 1, 8), wl.Geometry(2, 2, 8, 128)):
+        case = wl.PagedCase(f"idx_example_R{g.row_bytes}", g, wl.csr_from_lengths(lens), src,
+                            dst, 0, 0, 0)
+        run_paged_case(case, 11)
+
+
 def test_many_requests_and_empty_ones():
     # 300 requests, a third of them empty: the token -> request search and the
     # chunks that straddle request boundaries

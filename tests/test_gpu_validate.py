@@ -1,9 +1,11 @@
 """KVX_VALIDATE=1 (debug mode) on the GPU, in a child process (the flag is
 read once per process): valid calls run and match the oracle; a duplicate
 destination row, a source and destination that share rows, and staging laid
-over the pool it reads, and a one-request batch whose tok_off breaks the
-contract are refused with their status and nothing is written; out-of-range
-ids stay legal (skipped and counted)."""
+over the pool it reads, a one-request batch whose tok_off breaks the
+contract, a head-sliced copy whose tok_off runs past total_tokens, and a
+head-sliced copy that writes a head row it reads are refused with their
+status and nothing is written; out-of-range ids stay legal (skipped and
+counted)."""
 import os
 import subprocess
 import sys
@@ -103,6 +105,26 @@ expect(2, lambda: kvx.gather_scatter(lay, kvx.Pool(A, S), kvx.Table(d(pg[[0, 2]]
                                      one_req, kvx.Pool(B, S), kvx.Table(d(pg[[0, 2]]), d(dids))))
 torch.cuda.synchronize()
 assert torch.equal(B, before)
+
+# 8. a head-sliced copy whose tok_off runs past total_tokens: refused before
+#    the host checker indexes its per-token arrays by it
+bad_end = kvx.Requests(d(np.array([0, 31 + 9], np.int64)), 31)
+before = B.clone()
+expect(2, lambda: kvx.gather_scatter_heads(
+    one, kvx.Pool(A, S, slot_stride=R), kvx.Table(d(pg[[0, 2]]), d(sids)), kvx.Heads(2, 1, "hnd"),
+    bad_end, kvx.Pool(B, S, slot_stride=R), kvx.Table(d(pg[[0, 2]]), d(dids)),
+    kvx.Heads(2, 0, "nhd")))
+torch.cuda.synchronize()
+assert torch.equal(B, before)
+
+# 9. a head-sliced copy inside one pool whose written head row is a head row
+#    it reads (token 7 writes head 1 of page sids[12], token 12 reads it): refused
+before = A.clone()
+expect(9, lambda: kvx.gather_scatter_heads(
+    one, kvx.Pool(A, S, slot_stride=R), kvx.Table(d(pg), d(sids)), kvx.Heads(2, 1, "hnd"),
+    reqs, kvx.Pool(A, S, slot_stride=R), kvx.Table(d(pg), d(shared)), kvx.Heads(2, 1, "nhd")))
+torch.cuda.synchronize()
+assert torch.equal(A, before)
 print("validate ok", flush=True)
 """
 
@@ -115,3 +137,4 @@ def test_validate_mode_refuses_broken_preconditions():
     assert "validate ok" in p.stdout
     assert "KVX_VALIDATE: KVX_E_DUPLICATE" in p.stderr      # the refusals are reported
     assert "KVX_VALIDATE: KVX_E_OVERLAP" in p.stderr
+    assert "KVX_VALIDATE: KVX_E_SHAPE" in p.stderr

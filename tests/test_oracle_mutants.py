@@ -15,10 +15,20 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "kvx_oracle.c")
 
+# the page-table index range checks of the row and head-sliced lookups
+_ROWS_INDEX = ("    if (idx < 0 || idx >= s->num_ids) return -1;\n"
+               "    int64_t page = (int64_t)s->ids[idx];\n"
+               "    if (page < 0 || page >= s->num_pages) return -1;\n"
+               "    return page;")
+_HEADS_INDEX = ("    if (idx < 0 || idx >= s->num_ids) return -1;\n"
+                "    int64_t page = (int64_t)s->ids[idx];\n"
+                "    if (page < 0 || page >= s->num_pages) return -1;\n"
+                "    int64_t row")
+
 MUTANTS = {
     "row_in_page_uses_div": ("(t % s->page_size) * s->stride", "(t / s->page_size) * s->stride"),
-    "page_index_uses_mod": ("s->pg_off[r] + t / s->page_size];\n    if (page < 0 || page >= s->num_pages) return -1;\n    return page * s->page_stride",
-                            "s->pg_off[r] + t % s->page_size];\n    if (page < 0 || page >= s->num_pages) return -1;\n    return page * s->page_stride"),
+    "page_index_uses_mod": ("int64_t idx = s->pg_off[r] + t / s->page_size;\n" + _ROWS_INDEX,
+                            "int64_t idx = s->pg_off[r] + t % s->page_size;\n" + _ROWS_INDEX),
     "page_stride_ignored": ("return page * s->page_stride + (t % s->page_size) * s->stride;",
                             "return page * s->page_size * s->stride + (t % s->page_size) * s->stride;"),
     "page_stride_default_wrong": ("page_stride != 0 ? page_stride : (int64_t)page_size * stride",
@@ -26,8 +36,8 @@ MUTANTS = {
     "staging_drops_Q_factor": ("(j->tok_off[r] * j->Q + q * n + t)", "(j->tok_off[r] + q * n + t)"),
     "staging_token_major": ("(j->tok_off[r] * j->Q + q * n + t)",
                             "(j->tok_off[r] * j->Q + t * j->Q + q)"),
-    "bound_off_by_one": ("page >= s->num_pages) return -1;\n    return page * s->page_stride",
-                         "page > s->num_pages) return -1;\n    return page * s->page_stride"),
+    "bound_off_by_one": ("page >= s->num_pages) return -1;\n    return page;",
+                         "page > s->num_pages) return -1;\n    return page;"),
     "last_token_dropped": ("for (int64_t t = 0; t < n; ++t)", "for (int64_t t = 0; t + 1 < n; ++t)"),
     "gather_reads_plane0": ("memcpy(staged, j->src.planes[q]", "memcpy(staged, j->src.planes[0]"),
     "gs_dst_uses_src_side": ("int64_t d = row_offset(&j->dst, r, t);\n                if (s < 0 || d < 0)",
@@ -54,6 +64,15 @@ MUTANTS = {
                                     "                skipped += j->nh;\n                continue;\n            }\n            for (int32_t k = 0; k < j->nh; ++k)"),
     "heads_last_head_dropped": ("for (int32_t k = 0; k < j->nh; ++k)",
                                 "for (int32_t k = 0; k + 1 < j->nh; ++k)"),
+    "index_upper_unchecked": (_ROWS_INDEX, _ROWS_INDEX.replace(" || idx >= s->num_ids", "")),
+    "index_upper_off_by_one": (_ROWS_INDEX, _ROWS_INDEX.replace("idx >= s->num_ids",
+                                                                "idx > s->num_ids")),
+    "index_lower_unchecked": (_ROWS_INDEX, _ROWS_INDEX.replace("idx < 0 || ", "")),
+    "list_bounded_by_next_start": (_ROWS_INDEX, _ROWS_INDEX.replace(
+        "idx >= s->num_ids)", "idx >= s->num_ids || idx >= s->pg_off[r + 1])")),
+    "heads_index_upper_unchecked": (_HEADS_INDEX, _HEADS_INDEX.replace(" || idx >= s->num_ids",
+                                                                       "")),
+    "heads_index_lower_unchecked": (_HEADS_INDEX, _HEADS_INDEX.replace("idx < 0 || ", "")),
 }
 
 DRIVER = r"""

@@ -372,11 +372,21 @@ def hetero_tp_case(num_reqs: int = 16, num_blocks: int = 4096, page_size: int = 
 def random_case(seed: int, geom: Optional[Geometry] = None, max_reqs: int = 6,
                 max_len: int = 70, src_page: Optional[int] = None,
                 dst_page: Optional[int] = None, oor_frac: float = 0.0,
-                slack_pages: int = 7) -> PagedCase:
+                slack_pages: int = 7, index_faults: bool = False) -> PagedCase:
     """Small random paged case for fuzzing: ragged requests (empty ones
     included), page sizes drawn from {1, 2, 3, 4, 16}, distinct destination
     pages, source pages drawn with replacement, and optionally a fraction of
-    page ids made out of range (negative or >= num_pages)."""
+    page ids made out of range (negative or >= num_pages).
+
+    ``index_faults``: page-table offsets that send some lookups outside the
+    page-id array or into another request's list, with the destination's
+    written rows still distinct.  Source side: one request's list starts
+    1-3 entries early (negative indices for request 0, else the previous
+    request's last entries), one request (of three or more) starts past the
+    end of the array, and the array loses its last 1-2 entries.  Destination
+    side: request 0's list starts 1-3 entries early (its first pages'
+    lookups fall below 0, later ones reuse its own earlier entries) and the
+    array loses its last 1-2 entries (the last pages' lookups run past it)."""
     rng = np.random.default_rng(seed)
     if geom is None:
         geom = Geometry(int(rng.integers(1, 4)), int(rng.choice([1, 2])),
@@ -405,5 +415,23 @@ def random_case(seed: int, geom: Optional[Geometry] = None, max_reqs: int = 6,
             bad = np.where(rng.random(side.ids.size) < 0.5, -1 - rng.integers(0, 5, side.ids.size),
                            side.num_pages + rng.integers(0, 5, side.ids.size))
             side.ids = np.where(m, bad, side.ids).astype(np.int32)
+    if index_faults:
+        _index_faults(rng, src, source=True)
+        _index_faults(rng, dst, source=False)
     return PagedCase(f"random_{seed}", geom, csr_from_lengths(lens), src, dst,
                      value_seed=5000 + seed, sentinel_seed=6000 + seed, table_seed=seed)
+
+
+def _index_faults(rng: np.random.Generator, side: Side, source: bool) -> None:
+    """Move page-table offsets as random_case's ``index_faults`` describes."""
+    nreq = len(side.pg_off) - 1
+    pg = side.pg_off.copy()
+    if source and nreq >= 1:
+        pg[int(rng.integers(nreq))] -= int(rng.integers(1, 4))
+        if nreq >= 3:
+            pg[int(rng.integers(nreq))] = side.ids.size + int(rng.integers(0, 3))
+    elif nreq >= 1:
+        pg[0] -= int(rng.integers(1, 4))
+    cut = int(rng.integers(1, 3))
+    side.ids = side.ids[:max(0, side.ids.size - cut)].copy()
+    side.pg_off = pg
