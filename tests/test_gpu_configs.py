@@ -1,10 +1,10 @@
 """GPU parity on the five workloads at full size, in the launch configuration
 bench.py times (default grid).  Every destination byte is compared with the
-oracle on host copies of the same inputs, except for the 2 x 36 GiB block pools
-of the last workload, where a sample of planes is compared with the oracle
-and every plane is checked on the device for two properties that hold at any
-size: each written row equals its source row, and every other row still holds
-its prefill."""
+oracle on host copies of the same inputs.  The 2 x 36 GiB block pools of the
+last workload are compared one 512 MiB plane at a time (all 72 planes,
+through pinned host buffers), and every plane is also checked on the device
+for two properties that hold at any size: each written row equals its
+source row, and every other row still holds its prefill."""
 import numpy as np
 import pytest
 import torch
@@ -257,16 +257,23 @@ def test_config5_block_pools():
         assert torch.equal(b_d[q].index_select(0, dst_idx), a_d[q].index_select(0, src_idx)), q
         assert torch.equal(b_d[q].index_select(0, keep_idx), scratch.index_select(0, keep_idx)), q
 
-    # sampled planes, with the oracle on host copies
-    for q in [0, 1, 35, 36, 70, 71]:
-        say(f"config5 oracle plane {q}")
+    # every plane with the oracle, one plane at a time: host copies of the
+    # source plane and of the regenerated prefill, the oracle's gather-scatter
+    # into the latter, and the whole destination plane compared
+    say(f"config5 oracle on all {Q} planes")
+    pin_src = torch.empty((S, R), dtype=torch.uint8, pin_memory=True)
+    pin_exp = torch.empty((S, R), dtype=torch.uint8, pin_memory=True)
+    pin_got = torch.empty((S, R), dtype=torch.uint8, pin_memory=True)
+    one = wl.PagedCase(case.name, wl.Geometry(1, 1, g.kv_heads, g.head_dim, g.dtype),
+                       case.tok_off, case.src, case.dst, 0, 0, 0)
+    for q in range(Q):
         wdev.fill_hash(scratch, case.sentinel_seed, ctr0=q * plane_bytes // 8)
-        src_h = a_d[q].cpu().numpy().reshape(1, S, R)
-        exp = scratch.cpu().numpy().reshape(1, S, R)
-        one = wl.PagedCase(case.name, wl.Geometry(1, 1, g.kv_heads, g.head_dim, g.dtype),
-                           case.tok_off, case.src, case.dst, 0, 0, 0)
-        assert oracle_gather_scatter(one, src_h, exp, NT) == 0
-        assert_bytes_equal(b_d[q].cpu().numpy(), exp[0], f"config5 plane {q}")
+        pin_src.copy_(a_d[q])
+        pin_exp.copy_(scratch)
+        pin_got.copy_(b_d[q])
+        exp = pin_exp.numpy().reshape(1, S, R)
+        assert oracle_gather_scatter(one, pin_src.numpy().reshape(1, S, R), exp, NT) == 0
+        assert_bytes_equal(pin_got.numpy(), exp[0], f"config5 plane {q}")
 
 
 @pytest.mark.parametrize("page", [1, 16])

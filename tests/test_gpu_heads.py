@@ -78,7 +78,7 @@ def test_heads_table_index_faults(seed):
     """Page-table offsets outside the page-id array or into another request's
     list, on both sides of a head-sliced copy, every layout pair."""
     sH, dH, nh, sh0, dh0, D = SLICES[seed % 6]
-    case = wl.random_case(7200 + seed, geom=wl.Geometry(1, 2, nh, D), max_reqs=6, max_len=50,
+    case = wl.random_case(7300 + seed, geom=wl.Geometry(1, 2, nh, D), max_reqs=6, max_len=50,
                           oor_frac=0.1 if seed % 2 else 0.0, index_faults=True)
     run_heads(case, sH, dH, nh, sh0, dh0, D, seed % 2, (seed // 2) % 2, 200 + seed)
 
@@ -114,8 +114,9 @@ def test_heads_many_requests(mi):
 def test_hetero_tp_full_size(layout):
     """The full-size workload: P TP=1 (8 heads, page 16) -> two D ranks at
     TP=2 (4 heads each), with HND blocks (the page-run kernel) or NHD blocks
-    (the row kernel on shifted plane bases).  Four planes compared with the
-    oracle per rank; every plane checked on the device: written heads equal
+    (the row kernel on shifted plane bases).  Every plane of every rank
+    compared with the oracle, one plane at a time through pinned host
+    buffers; every plane also checked on the device: written heads equal
     their source heads and the rest of each destination pool is unchanged."""
     hnd = layout == "hnd"
     case = wl.hetero_tp_case()
@@ -167,15 +168,22 @@ def test_hetero_tp_full_size(layout):
             dq, bq = (dst[q].permute(0, 2, 1, 3), before[q].permute(0, 2, 1, 3)) if hnd else \
                 (dst[q], before[q])
             assert torch.equal(dq[keep], bq[keep])
-        for q in (0, 35, 36, 71):
-            exp = before[q].cpu().view(torch.uint8).numpy().reshape(-1).copy()
-            srcq = src[q].cpu().view(torch.uint8).numpy().reshape(-1)
-            oracle.gather_scatter_heads([srcq], 8 * Db, B, Ps, case.src.pg_off, case.src.ids,
-                                        (8, 4 * rank, int(hnd)), Db, 4, case.tok_off, [exp],
-                                        4 * Db, B, Pd, case.dst.pg_off, case.dst.ids,
-                                        (4, 0, int(hnd)), 16)
-            assert_bytes_equal(dst[q].cpu().view(torch.uint8).numpy().reshape(-1), exp,
-                               f"rank {rank} plane {q}")
+        say(f"hetero_tp {layout} rank {rank}: oracle on all {Q} planes")
+        pin_src = torch.empty(src[0].numel(), dtype=torch.int16, pin_memory=True)
+        pin_exp = torch.empty(dst[0].numel(), dtype=torch.int16, pin_memory=True)
+        pin_got = torch.empty(dst[0].numel(), dtype=torch.int16, pin_memory=True)
+        for q in range(Q):
+            pin_src.copy_(src[q].reshape(-1))
+            pin_exp.copy_(before[q].reshape(-1))
+            pin_got.copy_(dst[q].reshape(-1))
+            exp = pin_exp.numpy().view(np.uint8)
+            n = oracle.gather_scatter_heads([pin_src.numpy().view(np.uint8)], 8 * Db, B, Ps,
+                                            case.src.pg_off, case.src.ids,
+                                            (8, 4 * rank, int(hnd)), Db, 4, case.tok_off, [exp],
+                                            4 * Db, B, Pd, case.dst.pg_off, case.dst.ids,
+                                            (4, 0, int(hnd)), 16)
+            assert n == 0
+            assert_bytes_equal(pin_got.numpy().view(np.uint8), exp, f"rank {rank} plane {q}")
         del dst, before
 
 
