@@ -4,7 +4,7 @@
 Workload: one 2048-token request at 144 KiB per token (36 layers x {K,V} x 8
 KV heads x 128, bf16; 288 MiB), in token-paged pools of 32768 slots (4.5 GiB
 each), two pools in the one GPU's HBM, slots a seeded random subset of each
-pool.  A step is one pass of the whole path over one such request:
+pool.  A step is one pass of the whole path:
 
   gather_scatter  pool A -> pool B directly ("P writes D's pages")
   gather          pool A -> contiguous staging [plane][token][H][D]
@@ -13,15 +13,22 @@ pool.  A step is one pass of the whole path over one such request:
   scatter         second staging -> pool B
 
 Each op moves 288 MiB in and 288 MiB out (603,979,776 bytes read + written).
-Steps rotate over 16 disjoint requests of the pools, so no launch finds its
-rows in the 256 MiB Infinity Cache from an earlier launch.  Inputs are
-resident in HBM before the timed region.
+Steps rotate over 16 disjoint requests of the pools, and the staging and HF
+buffers the ops hand to each other are double-buffered: rebuild reads the
+staging the previous step's gather wrote, extract the HF tensors the
+previous step's rebuild wrote, scatter the staging the previous step's
+extract wrote (the rows gathered three steps earlier).  About 1.4 GB is
+written between producing a buffer and reading it back, so no op finds its
+input in the 256 MiB Infinity Cache: every byte counted is an HBM byte.
+Inputs are resident in HBM before the timed region.
 
 Printed (one JSON line on stdout): step throughput in GB/s (read + write,
 decimal), its fraction of the 8 TB/s HBM peak, ms per 288 MiB request for the
-gather-scatter, per-op times from HIP events recorded on the launch stream, a
-contiguous-copy ceiling of equal bytes, the roofline of the dominant kernel,
-and the CPU oracle timed on the host on a bounded sample of the same steps.
+gather-scatter, per-op times from HIP events recorded on the launch stream,
+each op timed alone (per launch, rotated inputs, nothing reading its output)
+with its fraction of peak against the 70% bar, a contiguous-copy ceiling of
+equal bytes, the roofline of the dominant kernel, and the CPU oracle timed
+on the host on a bounded sample of the same steps.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
   python bench.py --all-configs         (every op on every workload, beside a plain
@@ -37,6 +44,7 @@ and the CPU oracle timed on the host on a bounded sample of the same steps.
   python bench.py --summarize-trace TRACE_DIR OUT TITLE COMMAND
   python bench.py --counter-commands    (rocprofv3 commands of the memory/wave counter passes)
   python bench.py --summarize-counters OUT TITLE
+  python bench.py --summarize-json LOG OUT TITLE COMMAND   (f3 / f4 JSON lines -> markdown)
 """
 from __future__ import annotations
 
@@ -112,13 +120,32 @@ def read_traffic():
 # ------------------------------------------------------------------ setup --
 
 class Workload:
-    def __init__(self, torch, kvx, wl, wdev, dev, stream):
+    """The 2048-token, 144 KiB/token request in two token-paged pools.  With
+    the default 32768-slot pools (4.5 GiB each) it is the bench workload
+    (16 disjoint requests); smaller pools (the translation-counter runs) hold
+    slots // 2048 disjoint requests drawn from seeded permutations."""
+
+    def __init__(self, torch, kvx, wl, wdev, dev, stream, slots=32768):
         self.torch = torch
         g = wl.KV144K
         self.geom = g
-        self.Q, self.R, self.S = g.planes, g.row_bytes, 32768
+        self.Q, self.R, self.S = g.planes, g.row_bytes, slots
         self.T = 2048
-        self.cases = [wl.config2(k) for k in range(NREQ)]
+        if slots == 32768:
+            self.cases = [wl.config2(k) for k in range(NREQ)]
+        else:
+            import numpy as np
+            rng = np.random.default_rng(1002 + slots)
+            pa, pb = rng.permutation(slots), rng.permutation(slots)
+            self.cases = [wl.PagedCase(f"kv144k_2048tok_page1_{slots}slots_req{k}", g,
+                                       wl.csr_from_lengths([2048]),
+                                       wl.side_from_slot_lists([pa[2048 * k:2048 * (k + 1)]],
+                                                               slots),
+                                       wl.side_from_slot_lists([pb[2048 * k:2048 * (k + 1)]],
+                                                               slots),
+                                       2002, 3002, 1002 + slots)
+                          for k in range(slots // 2048)]
+        self.nreq = len(self.cases)
         c0 = self.cases[0]
         Q, R, S, T = self.Q, self.R, self.S, self.T
         with torch.cuda.stream(stream):
@@ -126,10 +153,13 @@ class Workload:
             self.B = torch.empty((Q, S, R), dtype=torch.uint8, device=dev)
             wdev.fill_hash(self.A, c0.value_seed, stream=stream)
             wdev.fill_hash(self.B, c0.sentinel_seed, stream=stream)
-            self.S1 = torch.zeros(T * Q * R, dtype=torch.uint8, device=dev)
-            self.S2 = torch.zeros(T * Q * R, dtype=torch.uint8, device=dev)
-            self.HF = torch.zeros((Q, g.kv_heads * T * g.head_bytes), dtype=torch.uint8,
-                                  device=dev)
+            # double-buffered hand-offs: gather -> S1[i % 2] -> rebuild (next
+            # step) -> HF[.] -> extract (next step) -> S2[.] -> scatter (next step)
+            self.S1s = [torch.zeros(T * Q * R, dtype=torch.uint8, device=dev) for _ in range(2)]
+            self.S2s = [torch.zeros(T * Q * R, dtype=torch.uint8, device=dev) for _ in range(2)]
+            self.HFs = [torch.zeros((Q, g.kv_heads * T * g.head_bytes), dtype=torch.uint8,
+                                    device=dev) for _ in range(2)]
+            self.S1, self.S2, self.HF = self.S1s[0], self.S2s[0], self.HFs[0]
 
             def d(a):
                 return torch.from_numpy(a).to(dev)
@@ -151,97 +181,198 @@ class Workload:
         self.table_bytes_per_step = 3 * c0.tok_off.nbytes + 4 * side
         self.kvx = kvx
 
+    def requests_of(self, i):
+        """Requests of step i: gather-scatter k_gs, gather k_g, and the
+        request whose rows the scatter writes back, k_sc -- the one gathered
+        three steps earlier (its rows reach the scatter through rebuild,
+        extract and the double buffers).  k_gs is even and k_sc odd, so the
+        two writes into pool B never share a row."""
+        n = self.nreq
+        return (2 * i) % n, (2 * i + 1) % n, (2 * i - 5) % n
+
     def step(self, i, stream, ev=None, marks=(0, 1, 2, 3, 4, 5)):
         """One pass of the path; event ev[j] is recorded before op j (after the
         last op for j = 5) for every j in marks."""
         kvx, lay = self.kvx, self.lay
-        k1, k2 = (2 * i) % NREQ, (2 * i + 1) % NREQ
+        k_gs, k_g, k_sc = self.requests_of(i)
+        cur, prev = i % 2, (i - 1) % 2
         T = self.T
 
         def mark(j):
             if ev is not None and j in marks:
                 ev[j].record(stream)
         mark(0)
-        kvx.gather_scatter(lay, self.PA, self.src_tabs[k1], self.reqs, self.PB,
-                           self.dst_tabs[k1], stream=stream)
+        kvx.gather_scatter(lay, self.PA, self.src_tabs[k_gs], self.reqs, self.PB,
+                           self.dst_tabs[k_gs], stream=stream)
         mark(1)
-        kvx.gather(lay, self.PA, self.src_tabs[k2], self.reqs, self.S1, stream=stream)
+        kvx.gather(lay, self.PA, self.src_tabs[k_g], self.reqs, self.S1s[cur], stream=stream)
         mark(2)
-        kvx.rebuild_permute(lay, self.S1, T, self.HF, T, stream=stream)
+        kvx.rebuild_permute(lay, self.S1s[prev], T, self.HFs[cur], T, stream=stream)
         mark(3)
-        kvx.extract_permute(lay, self.HF, T, T, self.S2, stream=stream)
+        kvx.extract_permute(lay, self.HFs[prev], T, T, self.S2s[cur], stream=stream)
         mark(4)
-        kvx.scatter(lay, self.S2, self.reqs, self.PB, self.dst_tabs[k2], stream=stream)
+        kvx.scatter(lay, self.S2s[prev], self.reqs, self.PB, self.dst_tabs[k_sc], stream=stream)
         mark(5)
+
+    def isolated(self, op, k, stream):
+        """Launch k of `op` timed alone: rotated requests, inputs read from
+        buffers written long before (four staging buffers, two HF sets), and
+        nothing reads the output."""
+        kvx, lay, T = self.kvx, self.lay, self.T
+        stages = self.S1s + self.S2s
+        n = self.nreq
+        if op == "gather_scatter":
+            kvx.gather_scatter(lay, self.PA, self.src_tabs[k % n], self.reqs, self.PB,
+                               self.dst_tabs[k % n], stream=stream)
+        elif op == "gather":
+            kvx.gather(lay, self.PA, self.src_tabs[k % n], self.reqs, self.S1s[k % 2],
+                       stream=stream)
+        elif op == "rebuild":
+            kvx.rebuild_permute(lay, stages[k % 4], T, self.HFs[k % 2], T, stream=stream)
+        elif op == "extract":
+            kvx.extract_permute(lay, self.HFs[k % 2], T, T, stages[(k + 1) % 4], stream=stream)
+        elif op == "scatter":
+            kvx.scatter(lay, stages[k % 4], self.reqs, self.PB, self.dst_tabs[k % n],
+                        stream=stream)
+
+
+def time_isolated(torch, wk, stream, n=24, warm=8):
+    """Each op alone, two ways, after `warm` launches: n launches back to back
+    between two HIP events on the launch stream (the sustained rate of a
+    stream of such calls: ms per launch, GB/s, fraction of the HBM peak), and
+    n launches with events around each one (one launch from start to end,
+    its ramp-up and drain included: median ms and fraction)."""
+    out = {}
+    ev = torch.cuda.Event
+    for op in OPS:
+        for k in range(warm):
+            wk.isolated(op, k, stream)
+        e0, e1 = ev(enable_timing=True), ev(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for k in range(n):
+            wk.isolated(op, warm + k, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sustained = e0.elapsed_time(e1) / n
+        evs = [(ev(enable_timing=True), ev(enable_timing=True)) for _ in range(n)]
+        for k, (a, b) in enumerate(evs):
+            a.record(stream)
+            wk.isolated(op, warm + n + k, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in evs)
+        med = ms[len(ms) // 2]
+        gbps = wk.op_bytes / (sustained * 1e-3) / 1e9
+        one = wk.op_bytes / (med * 1e-3) / 1e9
+        out[op] = {"ms_per_launch": round(sustained, 5), "GBps": round(gbps, 1),
+                   "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                   "single_launch_ms_median": round(med, 5),
+                   "single_launch_frac_hbm_peak": round(one / HBM_PEAK_GBPS, 4),
+                   "launches": n}
+    return out
 
 
 # -------------------------------------------------------------- cpu side --
 
+def cpu_share():
+    """Cores this process may use: the affinity mask, capped by a cgroup CPU
+    quota when one is set (cgroup v2 cpu.max, else v1 cfs quota / period)."""
+    import math
+    nproc = os.cpu_count() or 1
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else nproc
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, period = f.read().split()[:2]
+            if q != "max":
+                quota = int(q) / int(period)
+    except (OSError, ValueError):
+        try:
+            with open("/sys/fs/cgroup/cpu/cpu.cfs_quota_us") as f:
+                q = int(f.read())
+            with open("/sys/fs/cgroup/cpu/cpu.cfs_period_us") as f:
+                period = int(f.read())
+            if q > 0:
+                quota = q / period
+        except (OSError, ValueError):
+            pass
+    cg = math.ceil(quota) if quota else None
+    usable = min(aff, cg) if cg else aff
+    return {"nproc": nproc, "affinity": aff, "cgroup_cpus": cg, "usable": max(1, usable)}
+
+
 def cpu_baseline(wk, budget_s, parity_step=None):
-    """Time the oracle on host copies of the same pools and requests.  With
-    parity_step j (the last step run on the GPU before this call), first
-    check that step's results bitwise against the oracle: gather-scatter and
-    scatter rows of pool B equal the source rows of pool A, the gather's
-    staging equals the oracle's gather, and extract(rebuild(staging)) equals
-    the staging."""
+    """Time the oracle on host copies of the same pools and requests, running
+    the same step as the GPU (same ops, requests and double buffers) at one
+    thread and at every usable core.  With parity_step j (>= 3, the last step
+    run on the GPU before this call), first check that step's results
+    bitwise against the oracle: the gather-scatter's and the scatter's
+    destination rows of pool B equal the source rows of pool A, the gather's
+    staging equals the oracle's gather, and extract(rebuild(.)) returned the
+    staging gathered two steps earlier."""
     import numpy as np
 
     import oracle
-    torch = wk.torch
     Q, R, S, T = wk.Q, wk.R, wk.S, wk.T
     g = wk.geom
     log("cpu baseline: reading pools back to host")
     A_h = wk.A.cpu().numpy()
     B_h = wk.B.cpu().numpy()
-    S1 = np.zeros(T * Q * R, np.uint8)
-    S2 = np.zeros(T * Q * R, np.uint8)
-    HF = np.zeros((Q, g.kv_heads * T * g.head_bytes), np.uint8)
+    S1 = [np.zeros(T * Q * R, np.uint8) for _ in range(2)]
+    S2 = [np.zeros(T * Q * R, np.uint8) for _ in range(2)]
+    HF = [np.zeros((Q, g.kv_heads * T * g.head_bytes), np.uint8) for _ in range(2)]
     A_planes = [A_h[q].reshape(-1) for q in range(Q)]
     B_planes = [B_h[q].reshape(-1) for q in range(Q)]
-    HF_planes = [HF[q] for q in range(Q)]
+    HF_planes = [[h[q] for q in range(Q)] for h in HF]
     c0 = wk.cases[0]
-    ncores = min(16, os.cpu_count() or 1)
+    share = cpu_share()
+    ncores = share["usable"]
     parity = None
     if parity_step is not None:
         j = parity_step
-        a, b = wk.cases[(2 * j) % NREQ], wk.cases[(2 * j + 1) % NREQ]
-        S1_dev, S2_dev = wk.S1.cpu().numpy(), wk.S2.cpu().numpy()
+        k_gs, k_g, k_sc = wk.requests_of(j)
+        _, k_g2, _ = wk.requests_of(j - 2)
+        S1_dev, S2_dev = wk.S1s[j % 2].cpu().numpy(), wk.S2s[j % 2].cpu().numpy()
 
-        def rows(planes, pg_off, ids):
+        def rows(planes, side):
             out = np.zeros(T * Q * R, np.uint8)
-            oracle.gather(planes, R, 1, S, R, c0.tok_off, pg_off, ids, out, ncores)
+            oracle.gather(planes, R, 1, S, R, c0.tok_off, side.pg_off, side.ids, out, ncores)
             return out
-        want_gs = rows(A_planes, a.src.pg_off, a.src.ids)
-        want_g = rows(A_planes, b.src.pg_off, b.src.ids)
+        cs = wk.cases
         parity = {
             "step": j,
             "gather_scatter_rows_equal_source_rows":
-                bool(np.array_equal(rows(B_planes, a.dst.pg_off, a.dst.ids), want_gs)),
-            "gather_equals_oracle": bool(np.array_equal(S1_dev, want_g)),
-            "extract_of_rebuild_equals_staging": bool(np.array_equal(S2_dev, S1_dev)),
+                bool(np.array_equal(rows(B_planes, cs[k_gs].dst), rows(A_planes, cs[k_gs].src))),
+            "gather_equals_oracle": bool(np.array_equal(S1_dev, rows(A_planes, cs[k_g].src))),
+            "extract_of_rebuild_equals_staging_of_two_steps_before":
+                bool(np.array_equal(S2_dev, rows(A_planes, cs[k_g2].src))),
             "scatter_rows_equal_source_rows":
-                bool(np.array_equal(rows(B_planes, b.dst.pg_off, b.dst.ids), want_g)),
+                bool(np.array_equal(rows(B_planes, cs[k_sc].dst), rows(A_planes, cs[k_sc].src))),
         }
         log(f"parity of step {j}: {parity}")
-        del S1_dev, S2_dev, want_gs, want_g
+        del S1_dev, S2_dev
 
     def step(i, nt):
-        a, b = wk.cases[(2 * i) % NREQ], wk.cases[(2 * i + 1) % NREQ]
+        k_gs, k_g, k_sc = wk.requests_of(i)
+        a, b, c = wk.cases[k_gs], wk.cases[k_g], wk.cases[k_sc]
+        cur, prev = i % 2, (i - 1) % 2
         oracle.gather_scatter(A_planes, R, 1, S, a.src.pg_off, a.src.ids, R, c0.tok_off,
                               B_planes, R, 1, S, a.dst.pg_off, a.dst.ids, nt)
-        oracle.gather(A_planes, R, 1, S, R, c0.tok_off, b.src.pg_off, b.src.ids, S1, nt)
-        oracle.rebuild_permute(S1, g.kv_heads, g.head_bytes, T, HF_planes, T, nt)
-        oracle.extract_permute(HF_planes, g.kv_heads, g.head_bytes, T, T, S2, nt)
-        oracle.scatter(S2, R, c0.tok_off, b.dst.pg_off, b.dst.ids, B_planes, R, 1, S, nt)
+        oracle.gather(A_planes, R, 1, S, R, c0.tok_off, b.src.pg_off, b.src.ids, S1[cur], nt)
+        oracle.rebuild_permute(S1[prev], g.kv_heads, g.head_bytes, T, HF_planes[cur], T, nt)
+        oracle.extract_permute(HF_planes[prev], g.kv_heads, g.head_bytes, T, T, S2[cur], nt)
+        oracle.scatter(S2[prev], R, c0.tok_off, c.dst.pg_off, c.dst.ids, B_planes, R, 1, S, nt)
 
     out = {}
     for nt in sorted({1, ncores}):
         step(0, nt)                                # pre-fault staging and HF pages
+        step(1, nt)
         runs = []
         for _ in range(1 if nt == 1 else 3):       # the threaded rate: median of 3 runs
             steps, t0 = 0, time.perf_counter()
             while True:
-                step(steps + 1, nt)
+                step(steps + 2, nt)
                 steps += 1
                 el = time.perf_counter() - t0
                 if el >= (budget_s if nt == 1 else budget_s / 3) or steps >= 200:
@@ -251,24 +382,41 @@ def cpu_baseline(wk, budget_s, parity_step=None):
         runs.sort(key=lambda r: r[0] / r[1])
         out[nt] = runs[len(runs) // 2]
     del A_h, B_h
-    return out, ncores, parity
+    return out, ncores, parity, share
 
 
 def host_cpu():
-    """Model name and socket count of the host CPU (from /proc/cpuinfo)."""
-    model, sockets = "unknown", set()
+    """Model name and socket count of the host CPU: lscpu's "Model name" and
+    "Socket(s)" when lscpu runs, else /proc/cpuinfo's model name and physical
+    ids."""
+    import subprocess
+    model, sockets = None, None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            key, _, val = line.partition(":")
+            if key.strip() == "Model name" and model is None:
+                model = val.strip()
+            elif key.strip() == "Socket(s)":
+                try:
+                    sockets = int(val.strip())
+                except ValueError:
+                    pass
+    except (OSError, subprocess.SubprocessError):
+        pass
+    ids = set()
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 key, _, val = line.partition(":")
                 key = key.strip()
-                if key == "model name" and model == "unknown":
+                if key == "model name" and model is None:
                     model = val.strip()
                 elif key == "physical id":
-                    sockets.add(val.strip())
+                    ids.add(val.strip())
     except OSError:
         pass
-    return model, max(1, len(sockets))
+    return model or "unknown", sockets or max(1, len(ids))
 
 
 # ----------------------------------------------------------------- pmc --
@@ -1136,11 +1284,13 @@ def comparators(torch, kvx, wl, wdev, dev):
     print(json.dumps(out), flush=True)
 
 
-# TCC channels summed by the *_sum counters on MI355X: 16 per XCD x 8 XCDs
+# TCC channels summed by the *_sum counters on MI355X: 16 per XCD x 8 XCDs;
+# TCP and TA instances summed by *_sum counters: one per compute unit
 TCC_CHANNELS = 128
+CU_COUNT = 256
 
-# Per-kernel memory-side and wave metrics from the counter passes that
-# --summarize-counters reads (each pass a separate rocprofv3 --pmc run of
+# Per-kernel memory-side, translation and wave metrics from the counter passes
+# that --summarize-counters reads (each pass a separate rocprofv3 --pmc run of
 # `bench.py --pmc-pass`): (column, formula over per-dispatch medians).
 COUNTER_METRICS = [
     ("EA read latency (TCC cycles)", lambda m: m["TCC_EA0_RDREQ_LEVEL_sum"] / m["TCC_EA0_RDREQ_sum"]),
@@ -1151,8 +1301,24 @@ COUNTER_METRICS = [
     ("EA read DRAM-credit-stall cycles / TCC cycles",
      lambda m: m["TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum"] / m["TCC_CYCLE_sum"]),
     ("TCC busy", lambda m: m["TCC_BUSY_sum"] / m["TCC_CYCLE_sum"]),
+    ("TCC tag-stall cycles / TCC cycles", lambda m: m["TCC_TAG_STALL_sum"] / m["TCC_CYCLE_sum"]),
     ("TCP->TCC read latency", lambda m: m["TCP_TCC_READ_REQ_LATENCY_sum"] / m["TCP_TCC_READ_REQ_sum"]),
     ("TCP->TCC write latency", lambda m: m["TCP_TCC_WRITE_REQ_LATENCY_sum"] / m["TCP_TCC_WRITE_REQ_sum"]),
+    ("UTCL1 requests", lambda m: m["TCP_UTCL1_REQUEST_sum"]),
+    ("UTCL1 translation misses", lambda m: m["TCP_UTCL1_TRANSLATION_MISS_sum"]),
+    ("UTCL1 miss rate", lambda m: m["TCP_UTCL1_TRANSLATION_MISS_sum"] / m["TCP_UTCL1_REQUEST_sum"]),
+    ("UTCL1 misses under a miss", lambda m: m["TCP_UTCL1_TRANSLATION_MISS_UNDER_MISS_sum"]),
+    ("UTCL1 stalls: UTCL2 out of credits (per CU cycle)",
+     lambda m: m["TCP_UTCL1_STALL_UTCL2_REQ_OUT_OF_CREDITS_sum"] / (CU_COUNT * m["GRBM_GUI_ACTIVE"])),
+    ("UTCL1 stalls: in-flight max (per CU cycle)",
+     lambda m: m["TCP_UTCL1_STALL_INFLIGHT_MAX_sum"] / (CU_COUNT * m["GRBM_GUI_ACTIVE"])),
+    ("UTCL2 busy / GPU-active cycles", lambda m: m["GRBM_UTCL2_BUSY"] / m["GRBM_GUI_ACTIVE"]),
+    ("TCP pending-stall cycles (per CU cycle)",
+     lambda m: m["TCP_PENDING_STALL_CYCLES_sum"] / (CU_COUNT * m["GRBM_GUI_ACTIVE"])),
+    ("TA address stalled by TC (per CU cycle)",
+     lambda m: m["TA_ADDR_STALLED_BY_TC_CYCLES_sum"] / (CU_COUNT * m["GRBM_GUI_ACTIVE"])),
+    ("TA data stalled by TC (per CU cycle)",
+     lambda m: m["TA_DATA_STALLED_BY_TC_CYCLES_sum"] / (CU_COUNT * m["GRBM_GUI_ACTIVE"])),
     ("waves", lambda m: m["SQ_WAVES"]),
     ("wave life (cycles)", lambda m: 4 * m["SQ_WAVE_CYCLES"] / m["SQ_WAVES"]),
     ("wave time waiting", lambda m: m["SQ_WAIT_ANY"] / m["SQ_WAVE_CYCLES"]),
@@ -1160,8 +1326,8 @@ COUNTER_METRICS = [
 ]
 
 
-# The counter passes (one rocprofv3 run each: at most 4 TCC, 4 TCP and 8 SQ
-# counters per run) and the command that makes each.
+# The counter passes (one rocprofv3 run each: at most 4 TCC, 4 TCP, 2 TA,
+# 2 GRBM and 8 SQ counters per run) and the command that makes each.
 COUNTER_PASSES = {
     "ea_level": "TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_RDREQ_sum TCC_EA0_WRREQ_LEVEL_sum "
                 "TCC_EA0_WRREQ_sum",
@@ -1169,54 +1335,83 @@ COUNTER_PASSES = {
               "TCC_TOO_MANY_EA_WRREQS_STALL_sum TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum",
     "tcp_latency": "TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum "
                    "TCP_TCC_WRITE_REQ_LATENCY_sum TCP_TCC_WRITE_REQ_sum",
-    "busy": "TCC_CYCLE_sum TCC_BUSY_sum GRBM_GUI_ACTIVE",
+    "busy": "TCC_CYCLE_sum TCC_BUSY_sum TCC_TAG_STALL_sum GRBM_GUI_ACTIVE",
     "sq": "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY "
           "SQ_ACTIVE_INST_VMEM SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR",
+    "utcl1": "TCP_UTCL1_TRANSLATION_MISS_sum TCP_UTCL1_TRANSLATION_HIT_sum TCP_UTCL1_REQUEST_sum "
+             "TCP_UTCL1_STALL_UTCL2_REQ_OUT_OF_CREDITS_sum GRBM_UTCL2_BUSY GRBM_GUI_ACTIVE",
+    "tcp_stalls": "TCP_PENDING_STALL_CYCLES_sum TCP_UTCL1_TRANSLATION_MISS_UNDER_MISS_sum "
+                  "TCP_UTCL1_STALL_INFLIGHT_MAX_sum TCP_TCR_TCP_STALL_CYCLES_sum "
+                  "TA_ADDR_STALLED_BY_TC_CYCLES_sum TA_DATA_STALLED_BY_TC_CYCLES_sum "
+                  "GRBM_GUI_ACTIVE",
+}
+
+# Workloads a counter pass can run (bench.py --pmc-pass --pmc-workload W):
+# the bench step on the 4.5 GiB pools, the same step on 1 GiB pools (8192
+# slots: the translation comparison), and the MLA single-plane request.
+PMC_WORKLOADS = {
+    "kv144k": "the five-op step of the 2048-token, 144 KiB/token request, 4.5 GiB pools",
+    "kv144k_1gib": "the same step, 1 GiB pools (8192 slots, 4 disjoint requests)",
+    "mla": "gather-scatter, gather and scatter of the 2048-token MLA request (27 planes of "
+           "1152-byte rows, page 1, 32768-slot pools)",
 }
 
 
-def counter_pass_command(name, prefix="rocprof_out/pmcx_"):
-    return (f"rocprofv3 --pmc {COUNTER_PASSES[name]} -d {prefix}{name} -o pmc "
-            f"--output-format csv -- python3 bench.py --pmc-pass")
+def counter_pass_command(name, tag="kv144k", prefix="rocprof_out/pmcx_"):
+    return (f"rocprofv3 --pmc {COUNTER_PASSES[name]} -d {prefix}{tag}_{name} -o pmc "
+            f"--output-format csv -- python3 bench.py --pmc-pass --pmc-workload {tag}")
 
 
-def summarize_counters(out_path, title, prefix="rocprof_out/pmcx_"):
-    """Markdown table of COUNTER_METRICS per kernel from the COUNTER_PASSES runs."""
-    dirs = [prefix + n for n in COUNTER_PASSES]
-    commands = [counter_pass_command(n, prefix) for n in COUNTER_PASSES]
-    vals = {}
-    for d in dirs:
-        for r in counter_rows(d):
-            name = r["Kernel_Name"].split("(")[0] if not r["Kernel_Name"].startswith("(") \
-                else r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
-            name = name.replace("void ", "").replace("kvx::", "")
-            vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(
-                float(r["Counter_Value"]))
-    keep = [k for k in vals if k.startswith(("k_paged", "k_permute", "k_copy16"))]
+def summarize_counters(out_path, title, tags="kv144k", prefix="rocprof_out/pmcx_"):
+    """Markdown table of COUNTER_METRICS per (workload, kernel) from the
+    COUNTER_PASSES runs of each workload tag (comma-separated)."""
+    tags = [t for t in tags.split(",") if t]
+    commands = [counter_pass_command(n, t, prefix) for t in tags for n in COUNTER_PASSES]
+    cols = {}
+    for t in tags:
+        for n in COUNTER_PASSES:
+            d = f"{prefix}{t}_{n}"
+            if not os.path.isdir(d):
+                continue
+            for r in counter_rows(d):
+                name = r["Kernel_Name"].split("(")[0] if not r["Kernel_Name"].startswith("(") \
+                    else r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+                name = name.replace("void ", "").replace("kvx::", "")
+                if not name.startswith(("k_paged", "k_permute", "k_copy16")):
+                    continue
+                key = f"`{name}` ({t})" if len(tags) > 1 else f"`{name}`"
+                cols.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    keep = list(cols)
     with open(out_path, "w") as f:
         f.write(f"# {title}\n\n")
         f.write("Per-dispatch medians of hardware counters, one `rocprofv3 --pmc` run per "
-                "pass of `python3 bench.py --pmc-pass` (the five kernels of the step and "
-                "the plain copy `k_copy16` of 256 MiB, same process).  EA = the L2's "
-                f"requests to memory; *_sum counters add the {TCC_CHANNELS} L2 channels, so "
-                "average per-channel cycles are TCC_CYCLE_sum / "
-                f"{TCC_CHANNELS}; latencies are Little's-law averages (requests in flight "
-                "summed per cycle / requests).\n\n")
+                "pass of `python3 bench.py --pmc-pass --pmc-workload W`; workloads: "
+                + "; ".join(f"{t}: {PMC_WORKLOADS[t]}" for t in tags)
+                + " (each run also launches the plain copy `k_copy16` of 256 MiB).  EA = the "
+                "L2's requests to memory; TCC *_sum counters add the "
+                f"{TCC_CHANNELS} L2 channels (per-channel cycles = TCC_CYCLE_sum / "
+                f"{TCC_CHANNELS}), TCP and TA *_sum counters the {CU_COUNT} compute units "
+                "(per-CU shares divide by that and GRBM_GUI_ACTIVE); latencies are "
+                "Little's-law averages (requests in flight summed per cycle / requests).\n\n")
         f.write("Commands (from the repository root, on an MI355X machine):\n\n")
         for c in commands:
             f.write(f"    {c}\n")
-        f.write("\n| metric | " + " | ".join(f"`{k}`" for k in keep) + " |\n")
+        f.write(f"    python3 bench.py --summarize-counters {out_path} '{title}' "
+                f"{','.join(tags)}\n")
+        f.write("\n| metric | " + " | ".join(keep) + " |\n")
         f.write("|---|" + "---:|" * len(keep) + "\n")
         for label, fn in COUNTER_METRICS:
             cells = []
             for k in keep:
-                m = {c: sorted(v)[len(v) // 2] for c, v in vals[k].items()}
+                m = {c: sorted(v)[len(v) // 2] for c, v in cols[k].items()}
                 try:
                     x = fn(m)
                     cells.append(f"{x:.3f}" if x < 10 else f"{x:,.0f}")
                 except (KeyError, ZeroDivisionError):
                     cells.append("-")
-            f.write(f"| {label} | " + " | ".join(cells) + " |\n")
+            if any(c != "-" for c in cells):
+                f.write(f"| {label} | " + " | ".join(cells) + " |\n")
     print(open(out_path).read())
 
 
@@ -1245,6 +1440,124 @@ def summarize_trace(trace_dir, out_path, title, command):
                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                     f"{float(r['Percentage']):.2f} |\n")
     print(open(out_path).read())
+
+
+COMPARATOR_ROWS = [
+    ("per_block_random", "one hipMemcpyAsync per (token, plane) row, random slots"),
+    ("per_run_random", "the same, contiguous runs merged (random slots: none to merge)"),
+    ("per_run_fresh_pool", "runs merged on a fresh pool (2048 consecutive slots per plane)"),
+    ("runtime_copy_of_staging", "runtime copy of the 288 MiB staging buffer (blit kernel)"),
+    ("dma_copy_of_staging", "the same copy on the DMA engines (hipMemcpyDeviceToDeviceNoCU)"),
+    ("kvx_gather_scatter", "kvx_gather_scatter, random slots, one launch"),
+]
+
+
+def summarize_json(log_path, out_path, title, command):
+    """Markdown tables from the JSON lines that --concurrent, --cu-split and
+    --comparators print (any of them, in one log)."""
+    lines = []
+    with open(log_path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{"):
+                try:
+                    lines.append(json.loads(line))
+                except json.JSONDecodeError:
+                    pass
+    if not lines:
+        raise SystemExit(f"no JSON line in {log_path}")
+    with open(out_path, "w") as f:
+        f.write(f"# {title}\n\n")
+        f.write("GB/s count bytes read + written (decimal).  Made by (from the repository root, "
+                "on an MI355X machine):\n\n")
+        f.write(f"    {command}\n\n")
+        for d in lines:
+            if "readers" in d:
+                f.write("Gather-scatter of the 2048-token, 144 KiB/token request (16 disjoint "
+                        "requests rotated) while a decode-like reader streams a 16 GiB buffer "
+                        "on a second stream at the same priority; gather-scatter alone: "
+                        f"{d['gather_scatter_alone_GBps']} GB/s.\n\n")
+                f.write("| reader workgroups per launch | reader alone | reader under load | "
+                        "gather-scatter under load | together | reader outlasts transfer |\n")
+                f.write("|---:|---:|---:|---:|---:|---|\n")
+                for r in d["readers"]:
+                    tog = r["reader_loaded_GBps"] + r["gather_scatter_loaded_GBps"]
+                    f.write(f"| {r['reader_blocks']} | {r['reader_alone_GBps']} | "
+                            f"{r['reader_loaded_GBps']} | {r['gather_scatter_loaded_GBps']} | "
+                            f"{tog:.1f} | {r['reader_outlasts_gather_scatter']} |\n")
+                f.write("\n")
+            if "splits" in d:
+                f.write("The transfer and a full-intensity reader (2048 workgroups) on "
+                        "complementary CU masks (hipExtStreamCreateWithCUMask, whole groups "
+                        "of 8 CUs, one per XCD).\n\n")
+                f.write("| transfer / reader CUs | gather-scatter alone | reader alone | "
+                        "gather-scatter under load | reader under load | together |\n")
+                f.write("|---|---:|---:|---:|---:|---:|\n")
+                for r in d["splits"]:
+                    tog = r["reader_loaded_GBps"] + r["gather_scatter_loaded_GBps"]
+                    f.write(f"| {r['transfer_cus']} / {r['reader_cus']} | "
+                            f"{r['gather_scatter_alone_GBps']} | {r['reader_alone_GBps']} | "
+                            f"{r['gather_scatter_loaded_GBps']} | {r['reader_loaded_GBps']} | "
+                            f"{tog:.1f} |\n")
+                f.write("\n")
+            if "kvx_gather_scatter" in d:
+                f.write("The 2048-token, 144 KiB/token request (288 MiB each way) moved by "
+                        "runtime copies and by one batched launch.\n\n")
+                f.write("| method | launches | ms | GB/s |\n|---|---:|---:|---:|\n")
+                for key, label in COMPARATOR_ROWS:
+                    r = d.get(key)
+                    if not r:
+                        continue
+                    if "error" in r:
+                        f.write(f"| {label} | - | {r['error']} | - |\n")
+                        continue
+                    calls = r.get("calls", 1)
+                    gbps = r.get("GBps", round(603979776 / (r["ms"] * 1e6), 1))
+                    f.write(f"| {label} | {calls} | {r['ms']} | {gbps} |\n")
+                f.write("\n")
+            if "note" in d:
+                f.write(f"Note: {d['note']}\n\n")
+    print(open(out_path).read())
+
+
+def pmc_pass(torch, kvx, wl, wdev, dev, stream, workload):
+    """A short run for rocprofv3 --pmc: three of each kernel of the workload
+    (PMC_WORKLOADS), then three plain copies of COPY_CALIB_BYTES (the
+    counters' calibration)."""
+    if workload == "mla":
+        import numpy as np
+        cases = [wl.mla_case(1, k) for k in range(4)]
+        g = cases[0].geom
+        Q, R, S = g.planes, g.row_bytes, cases[0].src.num_slots
+        A = torch.empty((Q, S, R), dtype=torch.uint8, device=dev)
+        B = torch.empty((Q, S, R), dtype=torch.uint8, device=dev)
+        wdev.fill_hash(A, cases[0].value_seed, stream=stream)
+        wdev.fill_hash(B, cases[0].sentinel_seed, stream=stream)
+        st = torch.zeros(2048 * Q * R, dtype=torch.uint8, device=dev)
+        lay = kvx.Layout(g.num_layers, g.num_kv, g.kv_heads, g.head_dim, g.dtype)
+
+        def dv(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        reqs = kvx.Requests(dv(cases[0].tok_off), 2048)
+        tabs = [(kvx.Table(dv(c.src.pg_off), dv(c.src.ids)),
+                 kvx.Table(dv(c.dst.pg_off), dv(c.dst.ids))) for c in cases]
+        PA, PB = kvx.Pool(A, S), kvx.Pool(B, S)
+        for i in range(3):
+            kvx.gather_scatter(lay, PA, tabs[i][0], reqs, PB, tabs[i][1], stream=stream)
+            kvx.gather(lay, PA, tabs[(i + 1) % 4][0], reqs, st, stream=stream)
+            kvx.scatter(lay, st, reqs, PB, tabs[(i + 2) % 4][1], stream=stream)
+    else:
+        wk = Workload(torch, kvx, wl, wdev, dev, stream,
+                      slots=8192 if workload == "kv144k_1gib" else 32768)
+        A, B = wk.A, wk.B
+        for i in range(3):
+            wk.step(i, stream)
+    a, b = A.reshape(-1), B.reshape(-1)
+    for k in range(3):
+        wdev.copy_bytes(b[k * COPY_CALIB_BYTES:], a[k * COPY_CALIB_BYTES:], COPY_CALIB_BYTES,
+                        stream=stream)
+    torch.cuda.synchronize()
+    log(f"pmc pass done ({workload})")
 
 
 # ----------------------------------------------------------------- main --
@@ -1277,8 +1590,14 @@ def main():
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "OUT", "TITLE", "CMD"),
                     help="markdown summary of a rocprofv3 --kernel-trace --stats run")
     ap.add_argument("--pmc-out", default=PMC_SUMMARY, help="where --summarize-pmc writes")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("OUT", "TITLE"),
-                    help="per-kernel memory and wave metrics from the counter passes")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="OUT TITLE [TAGS]",
+                    help="per-kernel memory, translation and wave metrics from the counter "
+                         "passes of the workload tags (comma-separated, default kv144k)")
+    ap.add_argument("--pmc-workload", default="kv144k", choices=sorted(PMC_WORKLOADS),
+                    help="what --pmc-pass runs")
+    ap.add_argument("--summarize-json", nargs=4, metavar=("LOG", "OUT", "TITLE", "CMD"),
+                    help="markdown tables from the JSON lines of --concurrent / --cu-split / "
+                         "--comparators")
     ap.add_argument("--counter-commands", action="store_true",
                     help="print the rocprofv3 command of every counter pass")
     args = ap.parse_args()
@@ -1289,12 +1608,18 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_out)
         return 0
+    if args.summarize_json:
+        summarize_json(*args.summarize_json)
+        return 0
     if args.summarize_counters:
+        if len(args.summarize_counters) not in (2, 3):
+            ap.error("--summarize-counters OUT TITLE [TAGS]")
         summarize_counters(*args.summarize_counters)
         return 0
     if args.counter_commands:
-        for n in COUNTER_PASSES:
-            print(counter_pass_command(n))
+        for t in PMC_WORKLOADS:
+            for n in COUNTER_PASSES:
+                print(counter_pass_command(n, t))
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -1334,19 +1659,12 @@ def main():
     if args.comparators:
         comparators(torch, kvx, wl, wdev, dev)
         return 0
+    if args.pmc_pass:
+        pmc_pass(torch, kvx, wl, wdev, dev, stream, args.pmc_workload)
+        return 0
     log("setup: 2 pools of 4.5 GiB, 16 request tables")
     wk = Workload(torch, kvx, wl, wdev, dev, stream)
     torch.cuda.synchronize()
-
-    if args.pmc_pass:
-        for i in range(3):
-            wk.step(i, stream)
-        for k in range(3):
-            wdev.copy_bytes(wk.B[k * 4:(k + 1) * 4].reshape(-1), wk.A[k * 4:(k + 1) * 4]
-                            .reshape(-1), COPY_CALIB_BYTES, stream=stream)
-        torch.cuda.synchronize()
-        log("pmc pass done")
-        return 0
 
     K, W = args.steps, args.warmup
     for i in range(W):
@@ -1427,6 +1745,13 @@ def main():
     torch.cuda.synchronize()
     ident_ms = ce[0].elapsed_time(ce[1]) / ncopy
 
+    # every op alone: per launch, rotated inputs, nothing reading the output
+    iso = time_isolated(torch, wk, stream)
+    for op in OPS:
+        log(f"  alone {op:15s} {iso[op]['ms_per_launch'] * 1e3:8.1f} us  {iso[op]['GBps']:8.1f} GB/s"
+            f"  {100 * iso[op]['frac_hbm_peak']:.1f}% of peak (one launch: "
+            f"{100 * iso[op]['single_launch_frac_hbm_peak']:.1f}%)")
+
     # the dominant kernel: the slower of the two live-timed kernels (the other
     # ops are ~25% faster in the diagnostic pass); its achieved rate uses the
     # live events of the timed region
@@ -1482,7 +1807,10 @@ def main():
                         "8 kv_heads x 128 (144 KiB/token, 288 MiB), bf16 payload copied "
                         "bitwise; token-paged pools of 32768 slots (4.5 GiB each), 16 "
                         "disjoint requests rotated",
-            "step": "gather_scatter + gather + rebuild_permute + extract_permute + scatter",
+            "step": "gather_scatter + gather + rebuild_permute + extract_permute + scatter; "
+                    "staging and HF hand-offs double-buffered (each op reads what the "
+                    "previous step produced), so no op reads its input from the Infinity "
+                    "Cache",
             "bytes_per_step": step_bytes,
             "seeds": wk.seeds,
             "tables_sha256": wk.tables_sha256,
@@ -1502,14 +1830,29 @@ def main():
         "wall_ms_per_step": round(wall * 1e3 / K, 5),
         "host_issue_ms_per_step": round(issue * 1e3 / K, 5),
         "roofline": roofline,
+        "ops_isolated": iso,
+        "ops_isolated_timing": "each op alone, rotated requests and inputs, nothing reading "
+                               "the output; after 8 warm launches: 24 launches back to back "
+                               "between two HIP events on the launch stream (ms_per_launch, "
+                               "GBps, frac_hbm_peak: the sustained rate), and 24 with events "
+                               "around each launch (single_launch_*: median)",
+        "bar": {"target_frac_hbm_peak": 0.70,
+                "gather": {"frac": iso["gather"]["frac_hbm_peak"],
+                           "met": iso["gather"]["frac_hbm_peak"] >= 0.70},
+                "gather_scatter": {"frac": iso["gather_scatter"]["frac_hbm_peak"],
+                                   "met": iso["gather_scatter"]["frac_hbm_peak"] >= 0.70}},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        # one more step, then its results are checked against the oracle
+        # four more steps (the isolated timing above wrote into the double
+        # buffers, and the last step's scatter carries rows gathered three
+        # steps before it), then the last step's results are checked against
+        # the oracle
         j = W + K + 1000
-        wk.step(j, stream)
+        for i in range(j - 3, j + 1):
+            wk.step(i, stream)
         torch.cuda.synchronize()
-        res, ncores, parity = cpu_baseline(wk, args.cpu_seconds, parity_step=j)
+        res, ncores, parity, share = cpu_baseline(wk, args.cpu_seconds, parity_step=j)
         result["parity"] = parity
         steps_n, el_n = res[ncores]
         steps_1, el_1 = res[1]
@@ -1517,10 +1860,14 @@ def main():
         result["cpu_baseline"] = {
             "value": round(steps_n * step_bytes / el_n / 1e9, 2), "unit": "GB/s",
             "cores": ncores, "kind": "oracle",
-            "sample": f"{steps_n} full steps (the same 5 ops on rotating 2048-token "
-                      f"requests of host copies of the same 4.5 GiB pools) in {el_n:.1f} s "
-                      f"with {ncores} threads (median of 3 runs)",
+            "sample": f"{steps_n} full steps (the same 5 ops, requests and double buffers on "
+                      f"host copies of the same 4.5 GiB pools) in {el_n:.1f} s with {ncores} "
+                      f"threads (median of 3 runs)",
             "cpu_model": model, "sockets": sockets,
+            "nproc": share["nproc"], "affinity_cpus": share["affinity"],
+            "cgroup_cpus": share["cgroup_cpus"],
+            "threads_rule": "every usable core: the affinity mask, capped by the cgroup CPU "
+                            "quota when one is set",
             "one_thread_GBps": round(steps_1 * step_bytes / el_1 / 1e9, 2),
             "ms_per_step": round(el_n / steps_n * 1e3, 2),
         }

@@ -186,11 +186,25 @@ def _bytes_from(t: torch.Tensor, ptr: int) -> int:
     return st.data_ptr() + st.nbytes() - ptr
 
 
-def _plane_tensors(planes, ptrs):
-    """(tensor, plane address) for each plane that is backed by a tensor."""
-    if isinstance(planes, torch.Tensor):
-        return [(planes, p) for p in ptrs]
-    return [(p, a) for p, a in zip(planes, ptrs) if isinstance(p, torch.Tensor)]
+def _plane_tensors(keep, ptrs):
+    """(tensor, plane address) for each plane address that lies inside the
+    storage of one of the tensors in `keep` (a tensor or a sequence of them
+    and raw pointers); addresses in no kept tensor are the caller's own."""
+    tensors = [keep] if isinstance(keep, torch.Tensor) else \
+        [t for t in keep if isinstance(t, torch.Tensor)]
+    spans = []
+    for t in tensors:
+        st = t.untyped_storage()
+        spans.append((t, st.data_ptr(), st.data_ptr() + st.nbytes()))
+    out = []
+    for a in ptrs:
+        if a is None:
+            continue
+        for t, lo, hi in spans:
+            if lo <= a < hi:
+                out.append((t, a))
+                break
+    return out
 
 
 def _check_pool(what: str, layout: "Layout", pool: "Pool", whole_pages: bool = False) -> None:

@@ -370,12 +370,25 @@ uint32_t grid_for(uint32_t nchunks, int cus, int wpb) {
     return static_cast<uint32_t>(g);
 }
 
+// lds: dynamic LDS bytes per workgroup.  The kernels use no LDS; a nonzero
+// value only limits how many workgroups a compute unit holds at once.
 template <class Args>
-kvx_status launch(const void* fn, uint32_t grid, int wpb, Args& a, hipStream_t stream) {
+kvx_status launch(const void* fn, uint32_t grid, int wpb, Args& a, hipStream_t stream,
+                  size_t lds = 0) {
     void* params[] = {&a};
-    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kWave * wpb), params, 0, stream);
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kWave * wpb), params, lds, stream);
     return e == hipSuccess ? KVX_OK : KVX_E_HIP;
 }
+
+// Scatters above one round of resident waves run at 10 workgroups (20 waves)
+// per compute unit instead of 16: 16 KiB of LDS per workgroup, out of 160 KiB
+// per CU.  Fewer scattered row writes in flight at once go faster: measured
+// on the 2048-token, 144 KiB/token request (same process, alternating,
+// 4.5 GiB pools), scatter 5378 GB/s at full occupancy, 5439 / 5612 / 5570 at
+// 13 / 10 / 8 workgroups per CU, and the five-op step 5585 -> 5644.  The
+// other paged ops lose with the same cap (gather-scatter 5061 -> 4699 at 10,
+// gather 5739 -> 5556).
+constexpr size_t kScatterLdsPad = 16384;
 
 template <class Src, class Dst, bool MANY>
 const void* paged_kernel_of(int vpl, uint32_t U) {
@@ -492,18 +505,21 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
         // scatter 5310 -> 5419 GB/s, scatter 5368 -> 5415
         if (a.c.tmajor && KVX_XCD_REMAP != 0) a.c.remap = 1;
         const uint32_t grid = grid_for(a.c.nchunks, cus, kPagedWaves);
+        const size_t lds = std::is_same<Src, StageRef>::value &&
+                                   above_one_round(reqs->total_tokens * nq * g.R, cus)
+                               ? kScatterLdsPad : 0;
         if (log_enabled())
             std::fprintf(stderr,
                          "kvx: %s Q=%d planes[%d,%d) R=%lld T=%lld reqs=%d copy=%s U=%u "
-                         "pieces/row=%u chunks=%u grid=%u remap=%u order=%s\n",
+                         "pieces/row=%u chunks=%u grid=%u remap=%u order=%s lds_pad=%d\n",
                          op_name(op), g.Q, q0, q0 + nq, static_cast<long long>(g.R),
                          static_cast<long long>(reqs->total_tokens), reqs->num_reqs,
                          sh.vpl > 0 ? "wide" : (sh.vpl < 0 ? "row-loop" : "flat"), sh.U,
                          1u << sub, a.c.nchunks, grid, a.c.remap,
-                         a.c.tmajor ? "token-major" : "plane-major");
+                         a.c.tmajor ? "token-major" : "plane-major", static_cast<int>(lds));
         const void* fn = sub > 0 ? paged_sub_kernel<Src, Dst>(a.c.num_reqs)
                                  : paged_kernel<Src, Dst>(sh.vpl, sh.U, a.c.num_reqs);
-        s = launch(fn, grid, kPagedWaves, a, stream);
+        s = launch(fn, grid, kPagedWaves, a, stream, lds);
         if (s != KVX_OK) return s;
     }
     return KVX_OK;

@@ -430,3 +430,21 @@ def test_binding_checks_plane_counts_and_extents():
         kvx.rebuild_permute(lay, st, 1, [torch.zeros(32, dtype=torch.uint8)], 2)
     with pytest.raises(ValueError, match="needs 48"):
         kvx.extract_permute(lay, torch.zeros((2, 32), dtype=torch.uint8), 3, 1, st)
+
+
+def test_binding_extent_check_follows_plane_addresses():
+    """Planes given as raw addresses inside kept tensors (blocks holding K and
+    V of a layer: plane q inside layer tensor q // 2) are checked against the
+    tensor that holds them, whatever the order of the kept list."""
+    import torch
+    lay = kvx.Layout(2, 2, 1, 8, "bf16")                      # Q = 4, R = 16
+    B, P = 2, 3
+    layers = [torch.zeros(P * 2 * B * 16, dtype=torch.uint8) for _ in range(2)]
+    ptrs = [layers[q // 2].data_ptr() + (q % 2) * B * 16 for q in range(4)]
+    pool = kvx.Pool(ptrs, P, B, slot_stride=16, page_stride=2 * B * 16)
+    pool._keep = layers
+    kvx._check_pool("blocks", lay, pool)                     # V's last row ends at the tensor end
+    pool = kvx.Pool(ptrs, P + 1, B, slot_stride=16, page_stride=2 * B * 16)
+    pool._keep = layers[::-1]
+    with pytest.raises(ValueError, match="the pool's pages need"):
+        kvx._check_pool("blocks", lay, pool)
