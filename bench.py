@@ -1319,6 +1319,8 @@ COUNTER_METRICS = [
      lambda m: m["TA_ADDR_STALLED_BY_TC_CYCLES_sum"] / (CU_COUNT * m["GRBM_GUI_ACTIVE"])),
     ("TA data stalled by TC (per CU cycle)",
      lambda m: m["TA_DATA_STALLED_BY_TC_CYCLES_sum"] / (CU_COUNT * m["GRBM_GUI_ACTIVE"])),
+    ("VMEM instruction latency (SQ cycles)", lambda m: m["VmemLatency"]),
+    ("SMEM instruction latency (SQ cycles)", lambda m: m["SmemLatency"]),
     ("waves", lambda m: m["SQ_WAVES"]),
     ("wave life (cycles)", lambda m: 4 * m["SQ_WAVE_CYCLES"] / m["SQ_WAVES"]),
     ("wave time waiting", lambda m: m["SQ_WAIT_ANY"] / m["SQ_WAVE_CYCLES"]),
@@ -1340,6 +1342,8 @@ COUNTER_PASSES = {
           "SQ_ACTIVE_INST_VMEM SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR",
     "utcl1": "TCP_UTCL1_TRANSLATION_MISS_sum TCP_UTCL1_TRANSLATION_HIT_sum TCP_UTCL1_REQUEST_sum "
              "TCP_UTCL1_STALL_UTCL2_REQ_OUT_OF_CREDITS_sum GRBM_UTCL2_BUSY GRBM_GUI_ACTIVE",
+    "vmem_latency": "VmemLatency SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR",
+    "smem_latency": "SmemLatency",
     "tcp_stalls": "TCP_PENDING_STALL_CYCLES_sum TCP_UTCL1_TRANSLATION_MISS_UNDER_MISS_sum "
                   "TCP_UTCL1_STALL_INFLIGHT_MAX_sum TCP_TCR_TCP_STALL_CYCLES_sum "
                   "TA_ADDR_STALLED_BY_TC_CYCLES_sum TA_DATA_STALLED_BY_TC_CYCLES_sum "
