@@ -110,7 +110,7 @@
 extern "C" {
 #endif
 
-#define KVX_ABI_VERSION 5
+#define KVX_ABI_VERSION 6
 
 typedef enum kvx_status {
     KVX_OK = 0,
@@ -198,14 +198,26 @@ typedef struct kvx_table {
     int64_t num_ids;         /* host: length of page_ids (reads never go past it) */
 } kvx_table;
 
+/* Output flags of the calls that write a contiguous output (kvx_gather's
+ * staging, the permutes' outputs).  By default such an output is written with
+ * nontemporal stores, the faster choice when nothing on this GPU reads it
+ * back soon (it is sent to another GPU or host, or consumed much later).
+ * KVX_OUT_CACHED asks for ordinary stores instead, which leave what fits of
+ * the output in the L2 and the 256 MiB Infinity Cache for a consumer on the
+ * same GPU that runs right after (e.g. a rebuild of the staging a gather has
+ * just written).  The bytes written are the same either way.  Any other bit
+ * is refused with KVX_E_UNSUPPORTED. */
+#define KVX_OUT_CACHED 1u
+
 /* Gather ([budget] 5090 section; [survey] 6.1): copy every row of every
  * request, all Q planes, from pool `src` into contiguous staging laid out as
  * described above.  staging_bytes must be >= total_tokens * Q * R.  Staging
- * rows of skipped tokens keep their prior contents.  One launch for the whole
- * batch (two or more only when Q > 128). */
+ * rows of skipped tokens keep their prior contents.  flags: 0 or
+ * KVX_OUT_CACHED (above).  One launch for the whole batch (two or more only
+ * when Q > 128). */
 kvx_status kvx_gather(const kvx_layout* layout, const kvx_pool* src, const kvx_table* src_table,
                       const kvx_reqs* reqs, void* staging, int64_t staging_bytes,
-                      unsigned long long* skipped, hipStream_t stream);
+                      unsigned long long* skipped, uint32_t flags, hipStream_t stream);
 
 /* Scatter ([budget] 5090 section): the inverse of kvx_gather -- copy staging
  * rows into pool `dst` at the slots of dst_table.  Every destination byte
@@ -278,14 +290,16 @@ kvx_status kvx_gather_scatter_heads(const kvx_layout* layout,
  * 0 (with seq_len 0 nothing is read or written). */
 kvx_status kvx_extract_permute(const kvx_layout* layout, const void* const* hf_planes,
                                int64_t s_cap, int64_t seq_len,
-                               void* out, int64_t out_bytes, hipStream_t stream);
+                               void* out, int64_t out_bytes, uint32_t flags, hipStream_t stream);
 
 /* Rebuild permute ([mini]): the inverse of extract --
  * hf_planes[q][0][h][s][:] = in[q][s][h][:] for s < seq_len; positions
- * s >= seq_len keep their prior contents. */
+ * s >= seq_len keep their prior contents.  flags (both permutes): 0 or
+ * KVX_OUT_CACHED, for the output (out of extract, the HF planes of
+ * rebuild). */
 kvx_status kvx_rebuild_permute(const kvx_layout* layout, const void* in, int64_t in_bytes,
                                int64_t seq_len, void* const* hf_planes, int64_t s_cap,
-                               hipStream_t stream);
+                               uint32_t flags, hipStream_t stream);
 
 /* Precondition checker (debug aid; not on the data path).  Takes HOST copies
  * of a batch's token CSR and of one pool's page table and checks what the

@@ -26,6 +26,7 @@ _LIB_PATH = os.path.join(_PKG, "libkvx.so")
 _lib = None
 
 DTYPE_CODES = {"f16": 1, "bf16": 2, "fp8": 3, "f32": 4}
+OUT_CACHED = 1          # kvx.h KVX_OUT_CACHED
 _ELEM = {"f16": 2, "bf16": 2, "fp8": 1, "f32": 4}
 
 
@@ -78,15 +79,17 @@ def load_library():
                            "(python -c 'import __graft_entry__ as g; g.build()')")
     lib = ctypes.CDLL(_LIB_PATH)
     P, p64, vp = ctypes.POINTER, ctypes.c_int64, ctypes.c_void_p
-    lib.kvx_gather.argtypes = [P(_CLayout), P(_CPool), P(_CTable), P(_CReqs), vp, p64, vp, vp]
+    u32 = ctypes.c_uint32
+    lib.kvx_gather.argtypes = [P(_CLayout), P(_CPool), P(_CTable), P(_CReqs), vp, p64, vp, u32,
+                               vp]
     lib.kvx_scatter.argtypes = [P(_CLayout), vp, p64, P(_CReqs), P(_CPool), P(_CTable), vp, vp]
     lib.kvx_gather_scatter.argtypes = [P(_CLayout), P(_CPool), P(_CTable), P(_CReqs),
                                        P(_CPool), P(_CTable), vp, vp]
     lib.kvx_gather_scatter_heads.argtypes = [P(_CLayout), P(_CPool), P(_CTable), P(_CHeads),
                                              P(_CReqs), P(_CPool), P(_CTable), P(_CHeads), vp,
                                              vp]
-    lib.kvx_extract_permute.argtypes = [P(_CLayout), P(vp), p64, p64, vp, p64, vp]
-    lib.kvx_rebuild_permute.argtypes = [P(_CLayout), vp, p64, p64, P(vp), p64, vp]
+    lib.kvx_extract_permute.argtypes = [P(_CLayout), P(vp), p64, p64, vp, p64, u32, vp]
+    lib.kvx_rebuild_permute.argtypes = [P(_CLayout), vp, p64, p64, P(vp), p64, u32, vp]
     for f in (lib.kvx_gather, lib.kvx_scatter, lib.kvx_gather_scatter,
               lib.kvx_gather_scatter_heads, lib.kvx_extract_permute, lib.kvx_rebuild_permute):
         f.restype = ctypes.c_int
@@ -368,8 +371,10 @@ class Heads:
 
 
 def gather(layout: Layout, src: Pool, src_table: Table, reqs: Requests, staging: torch.Tensor,
-           skipped: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Pool -> contiguous staging [request][plane][token][H][D] (kvx_gather)."""
+           skipped: Optional[torch.Tensor] = None, stream=None, cached_out: bool = False) -> None:
+    """Pool -> contiguous staging [request][plane][token][H][D] (kvx_gather).
+    ``cached_out``: the staging is read back soon on this GPU, so write it
+    with ordinary stores (KVX_OUT_CACHED) instead of nontemporal ones."""
     _check_pool("src", layout, src)
     _check_table("src_table", src_table, reqs)
     _dense("staging", staging)
@@ -378,7 +383,8 @@ def gather(layout: Layout, src: Pool, src_table: Table, reqs: Requests, staging:
     lib = load_library()
     _check(lib.kvx_gather(ctypes.byref(layout._c), ctypes.byref(src._c),
                           ctypes.byref(src_table._c), ctypes.byref(reqs._c), _ptr(staging),
-                          _nbytes(staging), _ptr(skipped), _stream(stream)), "kvx_gather")
+                          _nbytes(staging), _ptr(skipped), OUT_CACHED if cached_out else 0,
+                          _stream(stream)), "kvx_gather")
 
 
 def scatter(layout: Layout, staging: torch.Tensor, reqs: Requests, dst: Pool, dst_table: Table,
@@ -435,8 +441,10 @@ def gather_scatter_heads(layout: Layout, src: Pool, src_table: Table, src_heads:
 
 
 def extract_permute(layout: Layout, hf_planes: Union[torch.Tensor, Sequence], s_cap: int,
-                    seq_len: int, out: torch.Tensor, stream=None) -> None:
-    """[1, H, s_cap, D] per plane -> out [Q][seq_len][H][D] (kvx_extract_permute)."""
+                    seq_len: int, out: torch.Tensor, stream=None,
+                    cached_out: bool = False) -> None:
+    """[1, H, s_cap, D] per plane -> out [Q][seq_len][H][D] (kvx_extract_permute);
+    ``cached_out`` as for gather."""
     _check_hf(layout, hf_planes, s_cap)
     _planes_dense("hf_planes", hf_planes)
     _dense("out", out)
@@ -445,13 +453,16 @@ def extract_permute(layout: Layout, hf_planes: Union[torch.Tensor, Sequence], s_
     arr = _plane_array(hf_planes)
     _check(lib.kvx_extract_permute(ctypes.byref(layout._c),
                                    ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), s_cap,
-                                   seq_len, _ptr(out), _nbytes(out), _stream(stream)),
+                                   seq_len, _ptr(out), _nbytes(out),
+                                   OUT_CACHED if cached_out else 0, _stream(stream)),
            "kvx_extract_permute")
 
 
 def rebuild_permute(layout: Layout, flat: torch.Tensor, seq_len: int,
-                    hf_planes: Union[torch.Tensor, Sequence], s_cap: int, stream=None) -> None:
-    """flat [Q][seq_len][H][D] -> [1, H, s_cap, D] per plane (kvx_rebuild_permute)."""
+                    hf_planes: Union[torch.Tensor, Sequence], s_cap: int, stream=None,
+                    cached_out: bool = False) -> None:
+    """flat [Q][seq_len][H][D] -> [1, H, s_cap, D] per plane (kvx_rebuild_permute);
+    ``cached_out`` as for gather."""
     _check_hf(layout, hf_planes, s_cap)
     _dense("flat", flat)
     _planes_dense("hf_planes", hf_planes)
@@ -460,7 +471,8 @@ def rebuild_permute(layout: Layout, flat: torch.Tensor, seq_len: int,
     arr = _plane_array(hf_planes)
     _check(lib.kvx_rebuild_permute(ctypes.byref(layout._c), _ptr(flat), _nbytes(flat), seq_len,
                                    ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), s_cap,
-                                   _stream(stream)), "kvx_rebuild_permute")
+                                   OUT_CACHED if cached_out else 0, _stream(stream)),
+           "kvx_rebuild_permute")
 
 
 def check_tables(reqs: Requests, table: Table, pool: Pool, as_destination: bool = True) -> None:

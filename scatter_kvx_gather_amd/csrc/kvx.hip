@@ -390,41 +390,54 @@ kvx_status launch(const void* fn, uint32_t grid, int wpb, Args& a, hipStream_t s
 // gather 5739 -> 5556).
 constexpr size_t kScatterLdsPad = 16384;
 
-template <class Src, class Dst, bool MANY>
+template <class Src, class Dst, bool MANY, bool NTS>
 const void* paged_kernel_of(int vpl, uint32_t U) {
     const bool one = U == 1;
     switch (vpl) {
-        case 1: return one      ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, 1, MANY>)
-                       : U == 2 ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, 2, MANY>)
-                                : reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, wide_rows<1>(), MANY>);
-        case 2: return one ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 2, 1, MANY>)
-                           : reinterpret_cast<const void*>(&k_paged<Src, Dst, 2, wide_rows<2>(), MANY>);
-        case 4: return one ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 4, 1, MANY>)
-                           : reinterpret_cast<const void*>(&k_paged<Src, Dst, 4, wide_rows<4>(), MANY>);
-        case 8: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 8, wide_rows<8>(), MANY>);
-        case 16: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 16, wide_rows<16>(), MANY>);
-        case -1: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -1, wide_rows<1>(), MANY>);
-        case -2: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -2, wide_rows<2>(), MANY>);
-        case -4: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -4, wide_rows<4>(), MANY>);
-        case -8: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -8, wide_rows<8>(), MANY>);
-        case -16: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -16, wide_rows<16>(), MANY>);
-        default: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 0, 0, MANY>);
+        case 1: return one      ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, 1, MANY, NTS>)
+                       : U == 2 ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, 2, MANY, NTS>)
+                                : reinterpret_cast<const void*>(&k_paged<Src, Dst, 1, wide_rows<1>(), MANY, NTS>);
+        case 2: return one ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 2, 1, MANY, NTS>)
+                           : reinterpret_cast<const void*>(&k_paged<Src, Dst, 2, wide_rows<2>(), MANY, NTS>);
+        case 4: return one ? reinterpret_cast<const void*>(&k_paged<Src, Dst, 4, 1, MANY, NTS>)
+                           : reinterpret_cast<const void*>(&k_paged<Src, Dst, 4, wide_rows<4>(), MANY, NTS>);
+        case 8: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 8, wide_rows<8>(), MANY, NTS>);
+        case 16: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 16, wide_rows<16>(), MANY, NTS>);
+        case -1: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -1, wide_rows<1>(), MANY, NTS>);
+        case -2: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -2, wide_rows<2>(), MANY, NTS>);
+        case -4: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -4, wide_rows<4>(), MANY, NTS>);
+        case -8: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -8, wide_rows<8>(), MANY, NTS>);
+        case -16: return reinterpret_cast<const void*>(&k_paged<Src, Dst, -16, wide_rows<16>(), MANY, NTS>);
+        default: return reinterpret_cast<const void*>(&k_paged<Src, Dst, 0, 0, MANY, NTS>);
     }
 }
 
 // Batches of more than 64 requests take the kernels whose lookup first finds
 // the chunk's 64-request window (a guessed one, else by a 64-way search);
-// smaller ones the kernels whose one window holds the whole batch.
+// smaller ones the kernels whose one window holds the whole batch.  Stores
+// are nontemporal unless the output is a staging the caller asked to be
+// written with ordinary stores (`cached`; pool rows are never).
 template <class Src, class Dst>
-const void* paged_kernel(int vpl, uint32_t U, int32_t num_reqs) {
-    return num_reqs > kWave ? paged_kernel_of<Src, Dst, true>(vpl, U)
-                            : paged_kernel_of<Src, Dst, false>(vpl, U);
+const void* paged_kernel(int vpl, uint32_t U, int32_t num_reqs, bool cached) {
+    if constexpr (std::is_same<Dst, StageRef>::value) {
+        if (cached)
+            return num_reqs > kWave ? paged_kernel_of<Src, Dst, true, false>(vpl, U)
+                                    : paged_kernel_of<Src, Dst, false, false>(vpl, U);
+    }
+    return num_reqs > kWave ? paged_kernel_of<Src, Dst, true, true>(vpl, U)
+                            : paged_kernel_of<Src, Dst, false, true>(vpl, U);
 }
 
 template <class Src, class Dst>
-const void* paged_sub_kernel(int32_t num_reqs) {
-    return num_reqs > kWave ? reinterpret_cast<const void*>(&k_paged_sub<Src, Dst, true>)
-                            : reinterpret_cast<const void*>(&k_paged_sub<Src, Dst, false>);
+const void* paged_sub_kernel(int32_t num_reqs, bool cached) {
+    if constexpr (std::is_same<Dst, StageRef>::value) {
+        if (cached)
+            return num_reqs > kWave
+                       ? reinterpret_cast<const void*>(&k_paged_sub<Src, Dst, true, false>)
+                       : reinterpret_cast<const void*>(&k_paged_sub<Src, Dst, false, false>);
+    }
+    return num_reqs > kWave ? reinterpret_cast<const void*>(&k_paged_sub<Src, Dst, true, true>)
+                            : reinterpret_cast<const void*>(&k_paged_sub<Src, Dst, false, true>);
 }
 
 template <int KT>
@@ -435,18 +448,18 @@ const void* heads_hnd_kernel(bool many) {
 
 // Token-row permute kernel for rows of vpl KiB; nullptr for the head-row
 // (flat) kernel.
-template <bool REBUILD>
+template <bool REBUILD, bool NTS>
 const void* permute_rows_kernel(int vpl, uint32_t U) {
     const bool one = U == 1;
     switch (vpl) {
-        case 1: return one ? reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 1, 1>)
-                           : reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 1, wide_rows<1>()>);
-        case 2: return one ? reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 2, 1>)
-                           : reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 2, wide_rows<2>()>);
-        case 4: return one ? reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 4, 1>)
-                           : reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 4, wide_rows<4>()>);
-        case 8: return reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 8, wide_rows<8>()>);
-        case 16: return reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 16, wide_rows<16>()>);
+        case 1: return one ? reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 1, 1, NTS>)
+                           : reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 1, wide_rows<1>(), NTS>);
+        case 2: return one ? reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 2, 1, NTS>)
+                           : reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 2, wide_rows<2>(), NTS>);
+        case 4: return one ? reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 4, 1, NTS>)
+                           : reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 4, wide_rows<4>(), NTS>);
+        case 8: return reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 8, wide_rows<8>(), NTS>);
+        case 16: return reinterpret_cast<const void*>(&k_permute_rows<REBUILD, 16, wide_rows<16>(), NTS>);
         default: return nullptr;
     }
 }
@@ -462,7 +475,8 @@ template <class Src, class Dst>
 kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
                      const kvx_pool* src, const kvx_table* st, void* src_stage,
                      const kvx_pool* dst, const kvx_table* dt, void* dst_stage,
-                     unsigned long long* skipped, hipStream_t stream) {
+                     unsigned long long* skipped, hipStream_t stream,
+                     uint32_t out_cached = 0) {
     if (reqs->total_tokens == 0) return KVX_OK;           // nothing to move
     int cus = 0;
     kvx_status s = device_cus(&cus);
@@ -511,14 +525,18 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
         if (log_enabled())
             std::fprintf(stderr,
                          "kvx: %s Q=%d planes[%d,%d) R=%lld T=%lld reqs=%d copy=%s U=%u "
-                         "pieces/row=%u chunks=%u grid=%u remap=%u order=%s lds_pad=%d\n",
+                         "pieces/row=%u chunks=%u grid=%u remap=%u order=%s lds_pad=%d "
+                         "stores=%s\n",
                          op_name(op), g.Q, q0, q0 + nq, static_cast<long long>(g.R),
                          static_cast<long long>(reqs->total_tokens), reqs->num_reqs,
                          sh.vpl > 0 ? "wide" : (sh.vpl < 0 ? "row-loop" : "flat"), sh.U,
                          1u << sub, a.c.nchunks, grid, a.c.remap,
-                         a.c.tmajor ? "token-major" : "plane-major", static_cast<int>(lds));
-        const void* fn = sub > 0 ? paged_sub_kernel<Src, Dst>(a.c.num_reqs)
-                                 : paged_kernel<Src, Dst>(sh.vpl, sh.U, a.c.num_reqs);
+                         a.c.tmajor ? "token-major" : "plane-major", static_cast<int>(lds),
+                         std::is_same<Dst, StageRef>::value && out_cached != 0 ? "cached"
+                                                                                : "nontemporal");
+        const void* fn = sub > 0 ? paged_sub_kernel<Src, Dst>(a.c.num_reqs, out_cached != 0)
+                                 : paged_kernel<Src, Dst>(sh.vpl, sh.U, a.c.num_reqs,
+                                                          out_cached != 0);
         s = launch(fn, grid, kPagedWaves, a, stream, lds);
         if (s != KVX_OK) return s;
     }
@@ -527,7 +545,7 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
 
 template <bool REBUILD>
 kvx_status run_permute(const Geom& g, void* const* hf, int64_t s_cap, int64_t seq, void* flat,
-                       hipStream_t stream) {
+                       uint32_t out_cached, hipStream_t stream) {
     if (seq == 0) return KVX_OK;
     int cus = 0;
     kvx_status s = device_cus(&cus);
@@ -559,13 +577,18 @@ kvx_status run_permute(const Geom& g, void* const* hf, int64_t s_cap, int64_t se
         if (log_enabled())
             std::fprintf(stderr,
                          "kvx: %s Q=%d planes[%d,%d) H=%d Db=%lld seq=%lld s_cap=%lld unit=%s "
-                         "U=%u chunks=%u grid=%u\n",
+                         "U=%u chunks=%u grid=%u stores=%s\n",
                          REBUILD ? "rebuild" : "extract", g.Q, q0, q0 + nq, g.H,
                          static_cast<long long>(g.Db), static_cast<long long>(seq),
                          static_cast<long long>(s_cap), rows ? "token-row" : "head-row", sh.U,
-                         a.c.nchunks, grid);
-        const void* fn = rows ? permute_rows_kernel<REBUILD>(sh.vpl, sh.U)
-                              : reinterpret_cast<const void*>(&k_permute<REBUILD>);
+                         a.c.nchunks, grid, out_cached != 0 ? "cached" : "nontemporal");
+        // nontemporal stores unless the caller reads the output back soon
+        const void* fn =
+            out_cached == 0
+                ? (rows ? permute_rows_kernel<REBUILD, true>(sh.vpl, sh.U)
+                        : reinterpret_cast<const void*>(&k_permute<REBUILD, true>))
+                : (rows ? permute_rows_kernel<REBUILD, false>(sh.vpl, sh.U)
+                        : reinterpret_cast<const void*>(&k_permute<REBUILD, false>));
         s = launch(fn, grid, kPermuteWaves, a, stream);
         if (s != KVX_OK) return s;
     }
@@ -698,6 +721,11 @@ kvx_status run_heads(const Geom& g, const kvx_reqs* reqs, const kvx_pool* src,
         if (s != KVX_OK) return s;
     }
     return KVX_OK;
+}
+
+// Output flags a call accepts (KVX_E_UNSUPPORTED for any other bit).
+kvx_status check_out_flags(uint32_t flags) {
+    return (flags & ~static_cast<uint32_t>(KVX_OUT_CACHED)) == 0 ? KVX_OK : KVX_E_UNSUPPORTED;
 }
 
 kvx_status check_staging(const void* p, int64_t bytes, const Geom& g, const kvx_reqs* r) {
@@ -964,8 +992,9 @@ extern "C" {
 
 kvx_status kvx_gather(const kvx_layout* layout, const kvx_pool* src, const kvx_table* src_table,
                       const kvx_reqs* reqs, void* staging, int64_t staging_bytes,
-                      unsigned long long* skipped, hipStream_t stream) {
+                      unsigned long long* skipped, uint32_t flags, hipStream_t stream) {
     Geom g;
+    KVX_TRY(check_out_flags(flags));
     KVX_TRY(check_layout(layout, &g));
     KVX_TRY(check_reqs(reqs));
     KVX_TRY(check_pool(src, g));
@@ -976,7 +1005,8 @@ kvx_status kvx_gather(const kvx_layout* layout, const kvx_pool* src, const kvx_t
         KVX_TRY(validate_call(layout, reqs, src, src_table, nullptr, nullptr, staging,
                               staging_bytes, nullptr, nullptr, stream));
     return run_paged<PoolRef, StageRef>(0, g, reqs, src, src_table, nullptr, nullptr, nullptr,
-                                        staging, skipped, stream);
+                                        staging, skipped, stream,
+                                        (flags & KVX_OUT_CACHED) ? 1u : 0u);
 }
 
 kvx_status kvx_scatter(const kvx_layout* layout, const void* staging, int64_t staging_bytes,
@@ -1042,8 +1072,9 @@ kvx_status kvx_gather_scatter_heads(const kvx_layout* layout,
 
 kvx_status kvx_extract_permute(const kvx_layout* layout, const void* const* hf_planes,
                                int64_t s_cap, int64_t seq_len, void* out, int64_t out_bytes,
-                               hipStream_t stream) {
+                               uint32_t flags, hipStream_t stream) {
     Geom g;
+    KVX_TRY(check_out_flags(flags));
     KVX_TRY(check_layout(layout, &g));
     KVX_TRY(check_hf(g, hf_planes, s_cap, seq_len));
     int64_t need = 0;
@@ -1052,13 +1083,14 @@ kvx_status kvx_extract_permute(const kvx_layout* layout, const void* const* hf_p
     if (!aligned16(out)) return KVX_E_ALIGN;
     if (out_bytes < need) return KVX_E_SHAPE;
     return run_permute<false>(g, const_cast<void* const*>(hf_planes), s_cap, seq_len, out,
-                              stream);
+                              (flags & KVX_OUT_CACHED) ? 1u : 0u, stream);
 }
 
 kvx_status kvx_rebuild_permute(const kvx_layout* layout, const void* in, int64_t in_bytes,
                                int64_t seq_len, void* const* hf_planes, int64_t s_cap,
-                               hipStream_t stream) {
+                               uint32_t flags, hipStream_t stream) {
     Geom g;
+    KVX_TRY(check_out_flags(flags));
     KVX_TRY(check_layout(layout, &g));
     KVX_TRY(check_hf(g, hf_planes, s_cap, seq_len));
     int64_t need = 0;
@@ -1066,7 +1098,8 @@ kvx_status kvx_rebuild_permute(const kvx_layout* layout, const void* in, int64_t
     if (need > 0 && in == nullptr) return KVX_E_NULL;
     if (!aligned16(in)) return KVX_E_ALIGN;
     if (in_bytes < need) return KVX_E_SHAPE;
-    return run_permute<true>(g, hf_planes, s_cap, seq_len, const_cast<void*>(in), stream);
+    return run_permute<true>(g, hf_planes, s_cap, seq_len, const_cast<void*>(in),
+                             (flags & KVX_OUT_CACHED) ? 1u : 0u, stream);
 }
 
 kvx_status kvx_check_tables(int32_t num_reqs, int64_t total_tokens, const int64_t* tok_off,

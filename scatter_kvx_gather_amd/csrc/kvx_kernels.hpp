@@ -15,9 +15,10 @@
 //      end);
 //   2. copy: every 16-byte vector of the chunk's rows is loaded with a
 //      nontemporal dwordx4 load (all loads of the chunk are issued before the
-//      first store), then stored with a dwordx4 store: nontemporal into
-//      scattered pool rows, ordinary into contiguous outputs (staging and
-//      permute outputs, which the next op often reads back from the MALL).
+//      first store), then stored with a nontemporal dwordx4 store -- or, for
+//      a contiguous output (staging, permute outputs) the caller will read
+//      back soon on this GPU, an ordinary store that leaves what fits in the
+//      L2 and the Infinity Cache (the kernels' NTS template parameter).
 //
 // Rows of 1, 2, 4, 8 or 16 KiB use the "wide" copy: the row addresses are
 // broadcast into scalar registers (readlane) and each lane moves 16 bytes at
@@ -174,11 +175,15 @@ __device__ __forceinline__ v4u load_nt(uint64_t base, uint32_t off) {
 #endif
 }
 
-// NT: nontemporal store.  Stores to scattered pool rows use it; stores to a
-// contiguous destination (staging, permute outputs) are ordinary, which lets
-// L2 hand whole runs of lines to memory (measured ~6.4 TB/s for contiguous
-// ordinary stores vs ~5.6 TB/s nontemporal; scattered 2 KiB rows ~4.9 TB/s
-// with any cache policy).
+// NT: nontemporal store.  Every output is stored nontemporally unless it is
+// a contiguous output (staging, permute outputs) that the caller reads back
+// soon on this GPU: then ordinary stores leave what fits in the L2 and the
+// 256 MiB Infinity Cache for that read.  Measured on the 2048-token,
+// 144 KiB/token request (same process, alternating) with outputs not read
+// back within the cache's reach: nontemporal gather 5727 -> 6041 GB/s,
+// rebuild 6155 -> 6407, extract 6215 -> 6436; scattered pool rows gain
+// 3-4% from it as well.  Read back by the next op, ordinary stores won
+// (a chained five-op step 13% faster).
 template <bool NT>
 __device__ __forceinline__ void store_v(uint64_t base, uint32_t off, v4u x) {
     gchar* p = reinterpret_cast<gchar*>(base) + off;
@@ -715,11 +720,15 @@ constexpr int many_waves(bool many, bool light) { return many && light ? 8 : 1; 
 
 // VPL > 0: wide copy with U rows per chunk; VPL < 0: row-loop copy with
 // KMAX = -VPL and at most U rows per chunk; VPL == 0: flat copy.  MANY: a
-// batch of more than 64 requests.
-template <class Src, class Dst, int VPL, int U, bool MANY>
+// batch of more than 64 requests.  NTS: nontemporal stores (always, into a
+// pool; into the staging unless the caller asked for cached stores).  The
+// store policy is a template parameter, not a run-time branch: the compiler
+// merges the two arms of such a branch into one ordinary store.
+template <class Src, class Dst, int VPL, int U, bool MANY, bool NTS>
 __global__ __launch_bounds__(kWave * kPagedWaves)
 __attribute__((amdgpu_waves_per_eu(many_waves(MANY, VPL != 0 && VPL >= -4 && VPL <= 4))))
 void k_paged(PagedArgs<Src, Dst> a) {
+    static_assert(NTS || !std::is_same<Dst, PoolRef>::value, "pool rows are stored nontemporally");
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t nwaves = gridDim.x * kPagedWaves;
     unsigned long long nskip = 0;
@@ -728,10 +737,9 @@ void k_paged(PagedArgs<Src, Dst> a) {
         uint64_t s = 0, d = 0;
         const int code = resolve<MANY>(a, k, static_cast<uint32_t>(lane), s, d);
         nskip += __popcll(__ballot(code == kSkip));
-        constexpr bool nts = std::is_same<Dst, PoolRef>::value;
-        if constexpr (VPL > 0) copy_wide<VPL, U, nts>(s, d, code, lane);
-        else if constexpr (VPL < 0) copy_rows<-VPL, U, nts>(a.c, s, d, code, lane);
-        else copy_flat<nts>(a.c, s, d, code, lane);
+        if constexpr (VPL > 0) copy_wide<VPL, U, NTS>(s, d, code, lane);
+        else if constexpr (VPL < 0) copy_rows<-VPL, U, NTS>(a.c, s, d, code, lane);
+        else copy_flat<NTS>(a.c, s, d, code, lane);
     }
     count_skips(a.c.skipped, nskip, lane);
 }
@@ -739,11 +747,13 @@ void k_paged(PagedArgs<Src, Dst> a) {
 // Rows of 4..16 KiB in launches above one round of resident waves, moved as
 // 2 KiB pieces: unit j of a plane is piece j & (2^sub_shift - 1) of batch
 // token j >> sub_shift, one unit per wave, so the pieces of a row run on
-// adjacent waves.  A skipped row is counted once, by its first piece.
-template <class Src, class Dst, bool MANY>
+// adjacent waves.  A skipped row is counted once, by its first piece.  NTS
+// as for k_paged.
+template <class Src, class Dst, bool MANY, bool NTS>
 __global__ __launch_bounds__(kWave * kPagedWaves)
 __attribute__((amdgpu_waves_per_eu(many_waves(MANY, true))))
 void k_paged_sub(PagedArgs<Src, Dst> a) {
+    static_assert(NTS || !std::is_same<Dst, PoolRef>::value, "pool rows are stored nontemporally");
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t nwaves = gridDim.x * kPagedWaves;
     const uint32_t last = (1u << a.c.sub_shift) - 1u;
@@ -764,7 +774,7 @@ void k_paged_sub(PagedArgs<Src, Dst> a) {
             code = kNone;
         }
         nskip += __popcll(__ballot(code == kSkip));
-        copy_wide<2, 1, std::is_same<Dst, PoolRef>::value>(s, d, code, lane);
+        copy_wide<2, 1, NTS>(s, d, code, lane);
     }
     count_skips(a.c.skipped, nskip, lane);
 }
@@ -878,8 +888,9 @@ __global__ __launch_bounds__(kWave * kPagedWaves) void k_heads_hnd(HeadArgs a) {
     count_skips(c.skipped, nskip, lane);
 }
 
-// Permute with head rows as units (any head row size, flat copy).
-template <bool REBUILD>
+// Permute with head rows as units (any head row size, flat copy).  NTS:
+// nontemporal stores (else ordinary ones, for an output read back soon).
+template <bool REBUILD, bool NTS>
 __global__ __launch_bounds__(kWave * kPermuteWaves) void k_permute(PermuteArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t nwaves = gridDim.x * kPermuteWaves;
@@ -887,7 +898,7 @@ __global__ __launch_bounds__(kWave * kPermuteWaves) void k_permute(PermuteArgs a
         const PermChunk k = perm_chunk(a.c, chunk);
         uint64_t s = 0, d = 0;
         const int code = resolve_perm<REBUILD>(a, k, static_cast<uint32_t>(lane), s, d);
-        copy_flat<false>(a.c, s, d, code, lane);
+        copy_flat<NTS>(a.c, s, d, code, lane);
     }
 }
 
@@ -896,8 +907,9 @@ __global__ __launch_bounds__(kWave * kPermuteWaves) void k_permute(PermuteArgs a
 // Lane l always moves the 16-byte vectors l + 64*j (j < VPL) of a token row;
 // their head h_j and offset within the head row are fixed for the whole
 // kernel, so every address is a per-lane constant plus s * Db (HF) or
-// s * H * Db (flat): no cross-lane exchange is needed.  U tokens per chunk.
-template <bool REBUILD, int VPL, int U>
+// s * H * Db (flat): no cross-lane exchange is needed.  U tokens per chunk;
+// NTS as for k_permute.
+template <bool REBUILD, int VPL, int U, bool NTS>
 __global__ __launch_bounds__(kWave * kPermuteWaves) void k_permute_rows(PermuteArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t nwaves = gridDim.x * kPermuteWaves;
@@ -939,9 +951,9 @@ __global__ __launch_bounds__(kWave * kPermuteWaves) void k_permute_rows(PermuteA
                 for (int j = 0; j < VPL; ++j) {
                     const uint32_t foff = static_cast<uint32_t>(lane + kWave * j) * 16u;
                     if constexpr (REBUILD)
-                        store_v<false>(hf + hf_off[j] + (s0 + u) * Db, 0, x[u][j]);
+                        store_v<NTS>(hf + hf_off[j] + (s0 + u) * Db, 0, x[u][j]);
                     else
-                        store_v<false>(fl + u * row, foff, x[u][j]);
+                        store_v<NTS>(fl + u * row, foff, x[u][j]);
                 }
             }
         }

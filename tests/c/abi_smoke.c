@@ -162,7 +162,7 @@ int main(void) {
         return 6;
     }
     CHECK_KVX(kvx_gather_scatter(&lay, &sp, &st, &reqs, &dp, &dt, skipped_d, stream));
-    CHECK_KVX(kvx_gather(&lay, &sp, &st, &reqs, st_d, (int64_t)stage_bytes, skipped_d, stream));
+    CHECK_KVX(kvx_gather(&lay, &sp, &st, &reqs, st_d, (int64_t)stage_bytes, skipped_d, 0, stream));
     CHECK_HIP(hipStreamSynchronize(stream));
     unsigned long long skipped = 1;
     CHECK_HIP(hipMemcpy(got_dst, dst_d, Q * dplane, hipMemcpyDeviceToHost));
@@ -258,8 +258,9 @@ int main(void) {
             hfs_h[q] = hf_h + q * hfp; hf2s_h[q] = exp_hf2 + q * hfp;
         }
         CHECK_KVX(kvx_extract_permute(&lay, (const void* const*)hfs, S_CAP, SEQ, flat_d,
-                                      (int64_t)flat, stream));
-        CHECK_KVX(kvx_rebuild_permute(&lay, flat_d, (int64_t)flat, SEQ, hf2s, S_CAP, stream));
+                                      (int64_t)flat, 0, stream));
+        CHECK_KVX(kvx_rebuild_permute(&lay, flat_d, (int64_t)flat, SEQ, hf2s, S_CAP,
+                                      KVX_OUT_CACHED, stream));
         CHECK_HIP(hipStreamSynchronize(stream));
         CHECK_HIP(hipMemcpy(got_flat, flat_d, flat, hipMemcpyDeviceToHost));
         CHECK_HIP(hipMemcpy(got_hf2, hf2_d, Q * hfp, hipMemcpyDeviceToHost));

@@ -44,7 +44,7 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_strings():
     lib = kvx.load_library()
-    assert lib.kvx_abi_version() == 5
+    assert lib.kvx_abi_version() == 6
     for s in range(10):
         assert lib.kvx_status_str(s).startswith(b"KVX_")
     assert lib.kvx_status_str(99) == b"unknown kvx_status"
@@ -68,13 +68,13 @@ def _table(n_ids=4):
     return kvx._CTable(A + 0x200000, A + 0x300000, n_ids)
 
 
-def gather(layout, pool, table, reqs, staging=A + 0x400000, nbytes=1 << 30):
+def gather(layout, pool, table, reqs, staging=A + 0x400000, nbytes=1 << 30, flags=0):
     lib = kvx.load_library()
     return lib.kvx_gather(ctypes.byref(layout) if layout is not None else None,
                           ctypes.byref(pool) if pool is not None else None,
                           ctypes.byref(table) if table is not None else None,
                           ctypes.byref(reqs) if reqs is not None else None,
-                          staging, nbytes, None, None)
+                          staging, nbytes, None, flags, None)
 
 
 def test_gather_validation():
@@ -101,6 +101,8 @@ def test_gather_validation():
     assert gather(lay, pool, tab, reqs, staging=A + 0x400008) == E_ALIGN
     assert gather(lay, pool, tab, reqs, nbytes=4 * 4 * 2048 - 16) == E_SHAPE
     assert gather(lay, pool, tab, reqs, staging=None) == E_NULL
+    assert gather(lay, pool, tab, reqs, flags=2) == E_UNSUPPORTED          # unknown output flag
+    assert gather(None, pool, tab, reqs, flags=4) == E_UNSUPPORTED
     zero_pages, k5 = _pool(4, num_pages=-1)
     assert gather(lay, zero_pages, tab, reqs) == E_SHAPE
     empty_src, k7 = _pool(4, num_pages=0)                    # no slot to read
@@ -133,29 +135,37 @@ def test_permute_validation():
     hf = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
     need = 4 * 100 * 4 * 256
     ex = lambda s_cap, seq, out=A + 0x1000000, nb=need: lib.kvx_extract_permute(  # noqa: E731
-        ctypes.byref(lay), hf, s_cap, seq, out, nb, None)
+        ctypes.byref(lay), hf, s_cap, seq, out, nb, 0, None)
     assert ex(50, 100) == E_SHAPE                  # seq > s_cap
     assert ex(100, -1) == E_SHAPE
     assert ex(100, 100, nb=need - 16) == E_SHAPE
     assert ex(100, 100, out=A + 4) == E_ALIGN
     assert ex(100, 100, out=None) == E_NULL
-    assert lib.kvx_extract_permute(ctypes.byref(lay), None, 100, 100, A, need, None) == E_NULL
+    assert lib.kvx_extract_permute(ctypes.byref(lay), None, 100, 100, A, need, 0, None) == E_NULL
     lay_odd = _layout(L=1, kv=2, H=2, D=4, dtype=2)    # head row of 8 bytes
-    assert lib.kvx_extract_permute(ctypes.byref(lay_odd), hf, 10, 10, A, 1 << 20, None) == E_ALIGN
-    assert lib.kvx_extract_permute(ctypes.byref(lay), hf, 100, 0, None, 0, None) == OK
+    assert lib.kvx_extract_permute(ctypes.byref(lay_odd), hf, 10, 10, A, 1 << 20, 0, None) == E_ALIGN
+    assert lib.kvx_extract_permute(ctypes.byref(lay), hf, 100, 0, None, 0, 0, None) == OK
     # empty HF planes (s_cap = 0, e.g. zero-size tensors) may be NULL; with
     # s_cap > 0 a NULL plane is refused even when seq_len is 0
     nulls = (ctypes.c_void_p * 4)(None, None, None, None)
     hf0 = ctypes.cast(nulls, ctypes.POINTER(ctypes.c_void_p))
-    assert lib.kvx_extract_permute(ctypes.byref(lay), hf0, 0, 0, None, 0, None) == OK
-    assert lib.kvx_rebuild_permute(ctypes.byref(lay), None, 0, 0, hf0, 0, None) == OK
-    assert lib.kvx_extract_permute(ctypes.byref(lay), hf0, 1, 0, None, 0, None) == E_NULL
-    assert lib.kvx_rebuild_permute(ctypes.byref(lay), None, 0, 0, hf0, 1, None) == E_NULL
-    rb = lambda seq, inp=A + 0x1000000, nb=need: lib.kvx_rebuild_permute(  # noqa: E731
-        ctypes.byref(lay), inp, nb, seq, hf, 100, None)
+    assert lib.kvx_extract_permute(ctypes.byref(lay), hf0, 0, 0, None, 0, 0, None) == OK
+    assert lib.kvx_rebuild_permute(ctypes.byref(lay), None, 0, 0, hf0, 0, 0, None) == OK
+    assert lib.kvx_extract_permute(ctypes.byref(lay), hf0, 1, 0, None, 0, 0, None) == E_NULL
+    assert lib.kvx_rebuild_permute(ctypes.byref(lay), None, 0, 0, hf0, 1, 0, None) == E_NULL
+    rb = lambda seq, inp=A + 0x1000000, nb=need, flags=0: lib.kvx_rebuild_permute(  # noqa: E731
+        ctypes.byref(lay), inp, nb, seq, hf, 100, flags, None)
     assert rb(101) == E_SHAPE
     assert rb(100, nb=need - 1) == E_SHAPE
     assert rb(100, inp=None) == E_NULL
+    # output flags: KVX_OUT_CACHED (1) is the only one; others are refused
+    # before anything else is looked at
+    assert ex(100, 0) == OK
+    assert lib.kvx_extract_permute(ctypes.byref(lay), hf, 100, 0, None, 0, 1, None) == OK
+    assert lib.kvx_extract_permute(ctypes.byref(lay), hf, 100, 0, None, 0, 2, None) == \
+        E_UNSUPPORTED
+    assert rb(0, flags=1) == OK
+    assert rb(0, flags=1 << 31) == E_UNSUPPORTED
 
 
 def test_heads_validation():
@@ -205,7 +215,7 @@ def test_page_stride_validation():
 
     def gather(p):
         return lib.kvx_gather(ctypes.byref(lay), ctypes.byref(p), ctypes.byref(tab),
-                              ctypes.byref(empty), None, 0, None, None)
+                              ctypes.byref(empty), None, 0, None, 0, None)
     for ps, want in [(0, OK), (4 * 2048, OK), (8 * 2048, OK), (3 * 2048 + 2048, OK),
                      (3 * 2048 + 2032, E_SHAPE), (-16, E_SHAPE), (8 * 2048 + 8, E_ALIGN),
                      (8 * 2048 + 16, E_UNSUPPORTED), (1 << 62, E_RANGE)]:

@@ -60,6 +60,10 @@ def run_paged_case(case, seed, guard=256):
         f"{case.dst.page_size}: gather")
     staging = d(stage_prefill)
     kvx.gather(lay, src, st, reqs, staging, skipped=skipped[0:1])
+    # the same gather with ordinary stores for the staging (KVX_OUT_CACHED)
+    say(case.name, "gather, cached output")
+    staging_c = d(stage_prefill)
+    kvx.gather(lay, src, st, reqs, staging_c, cached_out=True)
     say(case.name, "scatter")
     dst_d1 = d(dst_h)
     kvx.scatter(lay, d(stage_in), reqs, kvx.Pool(dst_d1, case.dst.num_pages, case.dst.page_size),
@@ -78,6 +82,7 @@ def run_paged_case(case, seed, guard=256):
     exp_dst2 = dst_h.copy()
     s2 = oracle_gather_scatter(case, src_h, exp_dst2)
     assert_bytes_equal(staging.cpu().numpy(), exp_stage, f"{case.name} gather")
+    assert_bytes_equal(staging_c.cpu().numpy(), exp_stage, f"{case.name} gather, cached output")
     assert_bytes_equal(dst_d1.cpu().numpy(), exp_dst1, f"{case.name} scatter")
     assert_bytes_equal(dst_d2.cpu().numpy(), exp_dst2, f"{case.name} gather_scatter")
     assert skipped.cpu().tolist() == [s0, s1, s2], case.name
@@ -526,10 +531,14 @@ def test_permutes(case):
     tgt_h = rng.integers(0, 256, (Q, H * s_cap * Db), dtype=np.uint8)
     flat_in = rng.integers(0, 256, Q * seq * H * Db, dtype=np.uint8)
     hf_d, out_d, tgt_d, flat_d = d(hf_h), d(out_pre), d(tgt_h), d(flat_in)
+    out_c, tgt_c = d(out_pre), d(tgt_h)
     say(f"extract Q={Q} H={H} Db={Db} s_cap={s_cap} seq={seq}")
     kvx.extract_permute(lay, hf_d, s_cap, seq, out_d)
     say("rebuild")
     kvx.rebuild_permute(lay, flat_d, seq, tgt_d, s_cap)
+    say("extract and rebuild, cached outputs")
+    kvx.extract_permute(lay, hf_d, s_cap, seq, out_c, cached_out=True)
+    kvx.rebuild_permute(lay, flat_d, seq, tgt_c, s_cap, cached_out=True)
     torch.cuda.synchronize()
     exp_out = out_pre.copy()
     oracle.extract_permute([hf_h[q] for q in range(Q)], H, Db, s_cap, seq, exp_out)
@@ -537,6 +546,8 @@ def test_permutes(case):
     oracle.rebuild_permute(flat_in, H, Db, seq, [exp_tgt[q] for q in range(Q)], s_cap)
     assert_bytes_equal(out_d.cpu().numpy(), exp_out, "extract")
     assert_bytes_equal(tgt_d.cpu().numpy(), exp_tgt, "rebuild")
+    assert_bytes_equal(out_c.cpu().numpy(), exp_out, "extract, cached output")
+    assert_bytes_equal(tgt_c.cpu().numpy(), exp_tgt, "rebuild, cached output")
 
 
 def test_device_fill_matches_host_hash():

@@ -1,0 +1,70 @@
+"""The store policy of contiguous outputs reaches the kernel choice: with
+KVX_LOG=1 (read once per process, so in a child) every gather, extract and
+rebuild launch reports nontemporal stores by default and cached stores with
+KVX_OUT_CACHED, scatter and gather-scatter always nontemporal; both policies
+write the same bytes."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+CHILD = r"""
+import sys
+sys.path.insert(0, {root!r})
+import numpy as np
+import torch
+import scatter_kvx_gather_amd as kvx
+
+dev = torch.device("cuda:0")
+d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+rng = np.random.default_rng(3)
+for (L, H, Db, T, nreq) in [(2, 8, 128, 300, 3), (1, 16, 256, 5000, 70), (1, 3, 48, 90, 2)]:
+    lay = kvx.Layout(L, 2, H, Db // 2, "bf16")
+    Q, R, S = 2 * L, H * Db, T + 17
+    tok = np.linspace(0, T, nreq + 1).astype(np.int64)
+    reqs = kvx.Requests(d(tok), T)
+    ids = rng.permutation(S)[:T].astype(np.int32)
+    A = d(rng.integers(0, 256, (Q, S, R), dtype=np.uint8))
+    B = d(rng.integers(0, 256, (Q, S, R), dtype=np.uint8))
+    tab = kvx.Table(d(tok), d(ids))
+    outs = []
+    for cached in (False, True):
+        st = torch.zeros(Q * T * R, dtype=torch.uint8, device=dev)
+        hf = torch.zeros((Q, H * T * Db), dtype=torch.uint8, device=dev)
+        fl = torch.zeros_like(st)
+        print(f"case L={{L}} H={{H}} Db={{Db}} T={{T}} cached={{cached}}", file=sys.stderr, flush=True)
+        kvx.gather(lay, kvx.Pool(A, S), tab, reqs, st, cached_out=cached)
+        kvx.rebuild_permute(lay, st, T, hf, T, cached_out=cached)
+        kvx.extract_permute(lay, hf, T, T, fl, cached_out=cached)
+        kvx.scatter(lay, fl, reqs, kvx.Pool(B, S), tab)
+        torch.cuda.synchronize()
+        outs.append((st.clone(), hf.clone(), fl.clone()))
+    assert all(torch.equal(a, b) for a, b in zip(*outs))
+    assert torch.equal(outs[0][0], outs[0][2])      # extract of rebuild is the staging
+print("store policy ok", flush=True)
+"""
+
+
+def test_store_policy_reaches_the_kernels():
+    env = dict(os.environ, KVX_LOG="1")
+    p = subprocess.run([sys.executable, "-c", CHILD.format(root=ROOT)], capture_output=True,
+                       text=True, timeout=180, env=env, cwd=ROOT)
+    assert p.returncode == 0, p.stdout + p.stderr
+    assert "store policy ok" in p.stdout
+    policy = {}
+    case = None
+    for line in p.stderr.splitlines():
+        if line.startswith("case "):
+            case = line.split("cached=")[1]
+        elif line.startswith("kvx: ") and "stores=" in line:
+            op = line.split()[1]
+            policy.setdefault((op, case), set()).add(line.rsplit("stores=", 1)[1].strip())
+    for op in ("gather", "rebuild", "extract"):
+        assert policy[(op, "False")] == {"nontemporal"}, (op, policy)
+        assert policy[(op, "True")] == {"cached"}, (op, policy)
+    assert policy[("scatter", "False")] == policy[("scatter", "True")] == {"nontemporal"}
