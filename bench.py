@@ -1771,11 +1771,12 @@ def main():
     # batches of more than 64 requests take the instances with the 64-way
     # request search
     m = "true" if wk.reqs.num_reqs > 64 else "false"
-    kernel_of = {"gather_scatter": f"k_paged<PoolRef, PoolRef, 2, {u}, {m}>",
-                 "gather": f"k_paged<PoolRef, StageRef, 2, {u}, {m}>",
-                 "scatter": f"k_paged<StageRef, PoolRef, 2, {u}, {m}>",
-                 "rebuild": f"k_permute_rows<true, 2, {u}>",
-                 "extract": f"k_permute_rows<false, 2, {u}>"}
+    # (the last template argument: nontemporal stores, the default)
+    kernel_of = {"gather_scatter": f"k_paged<PoolRef, PoolRef, 2, {u}, {m}, true>",
+                 "gather": f"k_paged<PoolRef, StageRef, 2, {u}, {m}, true>",
+                 "scatter": f"k_paged<StageRef, PoolRef, 2, {u}, {m}, true>",
+                 "rebuild": f"k_permute_rows<true, 2, {u}, true>",
+                 "extract": f"k_permute_rows<false, 2, {u}, true>"}
     achieved = wk.op_bytes / (dom_ms * 1e-3) / 1e9
     traffic, traffic_kernel = read_traffic()
     if traffic is not None and traffic_kernel and "PoolRef, kvx::PoolRef" not in traffic_kernel:
