@@ -676,9 +676,10 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps, cpu=True):
         wdev.fill_hash(A, 1, stream=stream)
         wdev.fill_hash(B, 2, stream=stream)
         st = torch.empty(2048 * g.token_bytes, dtype=torch.uint8, device=dev)
-        PA = kvx.Pool([A.data_ptr() + q * R for q in range(Q)], 32768, 1, slot_stride=Q * R)
-        PB = kvx.Pool([B.data_ptr() + q * R for q in range(Q)], 32768, 1, slot_stride=Q * R)
-        PA._keep, PB._keep = A, B
+        PA = kvx.Pool([A.data_ptr() + q * R for q in range(Q)], 32768, 1, slot_stride=Q * R,
+                      keep=A)
+        PB = kvx.Pool([B.data_ptr() + q * R for q in range(Q)], 32768, 1, slot_stride=Q * R,
+                      keep=B)
         hA, hB = A.cpu().numpy().reshape(-1), B.cpu().numpy().reshape(-1)
         pa, pb = [hA[q * R:] for q in range(k)], [hB[q * R:] for q in range(k)]
         hst = np.zeros(2048 * k * R, np.uint8)

@@ -11,10 +11,12 @@ exception is raised.
 """
 from __future__ import annotations
 
+import bisect
 import ctypes
 import os
 from typing import Optional, Sequence, Union
 
+import numpy as np
 import torch
 
 __all__ = ["KvxError", "Layout", "Pool", "Requests", "Table", "Heads", "gather", "scatter",
@@ -195,19 +197,49 @@ def _plane_tensors(keep, ptrs):
     and raw pointers); addresses in no kept tensor are the caller's own."""
     tensors = [keep] if isinstance(keep, torch.Tensor) else \
         [t for t in keep if isinstance(t, torch.Tensor)]
-    spans = []
-    for t in tensors:
+    spans = {}
+    for t in tensors:                       # one entry per storage
         st = t.untyped_storage()
-        spans.append((t, st.data_ptr(), st.data_ptr() + st.nbytes()))
+        spans.setdefault(st.data_ptr(), (st.data_ptr() + st.nbytes(), t))
+    los = sorted(spans)
     out = []
     for a in ptrs:
         if a is None:
             continue
-        for t, lo, hi in spans:
-            if lo <= a < hi:
-                out.append((t, a))
-                break
+        i = bisect.bisect_right(los, a) - 1     # the storage starting at or below a
+        if i >= 0 and a < spans[los[i]][0]:
+            out.append((spans[los[i]][1], a))
     return out
+
+
+def _min_plane_bytes(planes, ptrs) -> Optional[int]:
+    """Fewest bytes any tensor-backed plane holds from its base to the end of
+    its tensor's storage (None when no plane is tensor-backed).  ptrs None:
+    `planes` is one tensor whose first dimension indexes the planes, and the
+    plane furthest into the storage, the shortest, decides.  Otherwise each
+    plane address in `ptrs` is matched with the tensor of `planes` (a tensor
+    or a sequence of tensors and pointers) whose storage holds it."""
+    if ptrs is None:
+        n = planes.shape[0]
+        if n == 0:
+            return None
+        step = planes.stride(0) * planes.element_size()
+        last = planes.data_ptr() + max(0, (n - 1) * step)
+        st = planes.untyped_storage()
+        return st.data_ptr() + st.nbytes() - last
+    m = None
+    if not isinstance(planes, torch.Tensor) and len(planes) == len(ptrs) and \
+            all(isinstance(e, torch.Tensor) for e in planes):
+        # one tensor per plane, ptrs[q] its base: each plane against its own storage
+        for e, ptr in zip(planes, ptrs):
+            st = e.untyped_storage()
+            b = st.data_ptr() + st.nbytes() - ptr
+            m = b if m is None else min(m, b)
+        return m
+    for t, ptr in _plane_tensors(planes, ptrs):
+        b = _bytes_from(t, ptr)
+        m = b if m is None else min(m, b)
+    return m
 
 
 def _check_pool(what: str, layout: "Layout", pool: "Pool", whole_pages: bool = False) -> None:
@@ -228,26 +260,26 @@ def _check_pool(what: str, layout: "Layout", pool: "Pool", whole_pages: bool = F
         ps = pool.page_stride or pool.page_size * pool.slot_stride
         need = ((pool.num_pages - 1) * ps + (pool.page_size - 1) * pool.slot_stride
                 + layout.row_bytes)
-    for t, ptr in _plane_tensors(pool._keep, list(pool._arr)[:pool.num_planes]):
-        if _bytes_from(t, ptr) < need:
-            raise ValueError(f"{what}: a plane holds {_bytes_from(t, ptr)} bytes from its "
-                             f"base, the pool's pages need {need}")
+    if pool._min_bytes is not None and pool._min_bytes < need:
+        raise ValueError(f"{what}: a plane holds {pool._min_bytes} bytes from its base, the "
+                         f"pool's pages need {need}")
 
 
-def _check_hf(layout: "Layout", hf_planes, s_cap: int) -> None:
+def _check_hf(layout: "Layout", hf_planes, s_cap: int, arr) -> None:
     """Extract / rebuild: one [1, H, s_cap, D] plane per plane of the layout,
-    each tensor-backed plane holding H * s_cap * D elements from its base."""
+    each tensor-backed plane holding H * s_cap * D elements from its base
+    (`arr`: the planes' base pointers)."""
     n = hf_planes.shape[0] if isinstance(hf_planes, torch.Tensor) else len(hf_planes)
     if n != layout.planes:
         raise ValueError(f"hf_planes has {n} planes, the layout {layout.planes}")
     need = layout.kv_heads * max(int(s_cap), 0) * layout.head_dim * _ELEM[layout.dtype]
     if need == 0:
         return
-    arr = _plane_array(hf_planes)
-    for t, ptr in _plane_tensors(hf_planes, list(arr)[:n]):
-        if _bytes_from(t, ptr) < need:
-            raise ValueError(f"an hf plane holds {_bytes_from(t, ptr)} bytes from its base, "
-                             f"[1, H, s_cap, D] needs {need}")
+    have = _min_plane_bytes(hf_planes, None if isinstance(hf_planes, torch.Tensor)
+                            else list(arr)[:n])
+    if have is not None and have < need:
+        raise ValueError(f"an hf plane holds {have} bytes from its base, [1, H, s_cap, D] "
+                         f"needs {need}")
 
 
 def _check_table(what: str, table: "Table", reqs: "Requests") -> None:
@@ -291,7 +323,11 @@ def _plane_array(planes) -> ctypes.Array:
     given tensors / pointers."""
     if isinstance(planes, torch.Tensor):
         base, step = planes.data_ptr(), planes.stride(0) * planes.element_size()
-        ptrs = [base + q * step for q in range(planes.shape[0])]
+        n = planes.shape[0]
+        if n > 0:
+            a = np.arange(n, dtype=np.uint64) * np.uint64(step) + np.uint64(base)
+            return (ctypes.c_void_p * n).from_buffer_copy(a.tobytes())
+        ptrs = []
     else:
         ptrs = [_ptr(p) for p in planes]
     return (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
@@ -306,14 +342,17 @@ class Pool:
     page) defaults to the row size; ``page_stride`` (bytes between the pages
     of a plane) defaults to ``page_size * slot_stride`` and is the block
     length when a tensor's blocks hold several planes' pages.
+    ``keep``: for planes given as pointers, the tensor (or tensors) that hold
+    them; each plane's extent is checked inside the tensor that holds it.
     The pool keeps references to its tensors; the caller keeps them unchanged
     until the stream has passed every call that uses them.
     """
 
     def __init__(self, planes: Union[torch.Tensor, Sequence], num_pages: int,
                  page_size: int = 1, slot_stride: Optional[int] = None,
-                 row_bytes: Optional[int] = None, page_stride: int = 0):
-        self._keep = planes
+                 row_bytes: Optional[int] = None, page_stride: int = 0,
+                 keep: Union[None, torch.Tensor, Sequence[torch.Tensor]] = None):
+        self._keep = planes if keep is None else keep
         self._arr = _plane_array(planes)
         self.num_planes = planes.shape[0] if isinstance(planes, torch.Tensor) else len(planes)
         if slot_stride is None:
@@ -328,6 +367,11 @@ class Pool:
             slot_stride = row_bytes
         self.num_pages, self.page_size, self.slot_stride = num_pages, page_size, slot_stride
         self.page_stride = page_stride
+        # the extent check of every call compares with this (the pool's
+        # tensors stay as they are while the pool is in use)
+        self._min_bytes = (_min_plane_bytes(planes, None) if isinstance(planes, torch.Tensor)
+                           else _min_plane_bytes(self._keep,
+                                                 list(self._arr)[:self.num_planes]))
         self._c = _CPool(ctypes.cast(self._arr, ctypes.POINTER(ctypes.c_void_p)), num_pages,
                          page_size, slot_stride, page_stride)
 
@@ -445,12 +489,12 @@ def extract_permute(layout: Layout, hf_planes: Union[torch.Tensor, Sequence], s_
                     cached_out: bool = False) -> None:
     """[1, H, s_cap, D] per plane -> out [Q][seq_len][H][D] (kvx_extract_permute);
     ``cached_out`` as for gather."""
-    _check_hf(layout, hf_planes, s_cap)
+    arr = _plane_array(hf_planes)
+    _check_hf(layout, hf_planes, s_cap, arr)
     _planes_dense("hf_planes", hf_planes)
     _dense("out", out)
     _on_device(hf_planes, out)
     lib = load_library()
-    arr = _plane_array(hf_planes)
     _check(lib.kvx_extract_permute(ctypes.byref(layout._c),
                                    ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), s_cap,
                                    seq_len, _ptr(out), _nbytes(out),
@@ -463,12 +507,12 @@ def rebuild_permute(layout: Layout, flat: torch.Tensor, seq_len: int,
                     cached_out: bool = False) -> None:
     """flat [Q][seq_len][H][D] -> [1, H, s_cap, D] per plane (kvx_rebuild_permute);
     ``cached_out`` as for gather."""
-    _check_hf(layout, hf_planes, s_cap)
+    arr = _plane_array(hf_planes)
+    _check_hf(layout, hf_planes, s_cap, arr)
     _dense("flat", flat)
     _planes_dense("hf_planes", hf_planes)
     _on_device(flat, hf_planes)
     lib = load_library()
-    arr = _plane_array(hf_planes)
     _check(lib.kvx_rebuild_permute(ctypes.byref(layout._c), _ptr(flat), _nbytes(flat), seq_len,
                                    ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), s_cap,
                                    OUT_CACHED if cached_out else 0, _stream(stream)),

@@ -451,10 +451,33 @@ def test_binding_extent_check_follows_plane_addresses():
     B, P = 2, 3
     layers = [torch.zeros(P * 2 * B * 16, dtype=torch.uint8) for _ in range(2)]
     ptrs = [layers[q // 2].data_ptr() + (q % 2) * B * 16 for q in range(4)]
-    pool = kvx.Pool(ptrs, P, B, slot_stride=16, page_stride=2 * B * 16)
-    pool._keep = layers
+    pool = kvx.Pool(ptrs, P, B, slot_stride=16, page_stride=2 * B * 16, keep=layers)
     kvx._check_pool("blocks", lay, pool)                     # V's last row ends at the tensor end
-    pool = kvx.Pool(ptrs, P + 1, B, slot_stride=16, page_stride=2 * B * 16)
-    pool._keep = layers[::-1]
+    pool = kvx.Pool(ptrs, P + 1, B, slot_stride=16, page_stride=2 * B * 16, keep=layers[::-1])
     with pytest.raises(ValueError, match="the pool's pages need"):
         kvx._check_pool("blocks", lay, pool)
+
+
+def test_binding_plane_pointers_and_cached_extent(monkeypatch):
+    """Plane base pointers of a strided tensor are planes[q]'s addresses; a
+    pool's extent is measured once, when it is made, so the check of each
+    call does not walk its planes again (it is on every call's host path)."""
+    import torch
+    t = torch.zeros((5, 3, 32), dtype=torch.uint8)[:, 1:]
+    arr = kvx._plane_array(t)
+    assert [arr[q] for q in range(5)] == [t[q].data_ptr() for q in range(5)]
+    lay = kvx.Layout(1, 2, 1, 8, "bf16")                          # Q = 2, R = 16
+    A = torch.zeros((2, 8, 16), dtype=torch.uint8)
+    pool = kvx.Pool(A, 8)
+    assert pool._min_bytes == 8 * 16                              # the last plane's extent
+    tensors = [torch.zeros(8 * 16, dtype=torch.uint8), torch.zeros(7 * 16, dtype=torch.uint8)]
+    short = kvx.Pool(tensors, 8, slot_stride=16)
+    assert short._min_bytes == 7 * 16
+
+    def walk(*a):
+        raise AssertionError("plane walk on the per-call path")
+    monkeypatch.setattr(kvx, "_plane_tensors", walk)
+    monkeypatch.setattr(kvx, "_min_plane_bytes", walk)
+    kvx._check_pool("src", lay, pool)
+    with pytest.raises(ValueError, match="the pool's pages need"):
+        kvx._check_pool("src", lay, short)

@@ -124,8 +124,7 @@ def test_config2_token_major_pools():
     c_before = c_d.cpu().numpy()
 
     def tm_pool(t):
-        p = kvx.Pool([t.data_ptr() + q * R for q in range(Q)], S, 1, slot_stride=Q * R)
-        p._keep = t
+        p = kvx.Pool([t.data_ptr() + q * R for q in range(Q)], S, 1, slot_stride=Q * R, keep=t)
         return p
 
     def tm_planes(flat):

@@ -300,8 +300,7 @@ def run_paged_case_token_major(case, seed):
 
     def pool(t, side):
         p = kvx.Pool([t.data_ptr() + q * R for q in range(Q)], side.num_pages, side.page_size,
-                     slot_stride=Q * R)
-        p._keep = t
+                     slot_stride=Q * R, keep=t)
         return p
 
     def planes(flat):
@@ -388,13 +387,12 @@ def run_paged_case_blocks(case, seed):
     st, dt = table(case.src), table(case.dst)
     src_d = [d(a) for a in src_h]
     src = kvx.Pool([src_d[q // kv].data_ptr() + (q % kv) * bs * R for q in range(Q)],
-                   case.src.num_pages, bs, slot_stride=R, page_stride=kv * bs * R)
-    src._keep = src_d
+                   case.src.num_pages, bs, slot_stride=R, page_stride=kv * bs * R,
+                   keep=src_d)
 
     def dst_pool(t):
         p = kvx.Pool([t.data_ptr() + q * bd * R for q in range(Q)], case.dst.num_pages, bd,
-                     slot_stride=R, page_stride=Q * bd * R)
-        p._keep = t
+                     slot_stride=R, page_stride=Q * bd * R, keep=t)
         return p
 
     src_planes = [src_h[q // kv][(q % kv) * bs * R:] for q in range(Q)]
@@ -475,11 +473,9 @@ def test_token_major_pools_and_mixed_strides():
     src_d, dst_d = d(src_tm), d(dst_pad)
     lay, reqs = layout_of(g), requests(case)
     src = kvx.Pool([src_d.data_ptr() + q * R for q in range(Q)], case.src.num_pages,
-                   case.src.page_size, slot_stride=Q * R)
-    src._keep = src_d
+                   case.src.page_size, slot_stride=Q * R, keep=src_d)
     dst = kvx.Pool([dst_d[q].data_ptr() for q in range(Q)], case.dst.num_pages,
-                   case.dst.page_size, slot_stride=3 * R)
-    dst._keep = dst_d
+                   case.dst.page_size, slot_stride=3 * R, keep=dst_d)
     say("token_major gather_scatter")
     kvx.gather_scatter(lay, src, table(case.src), reqs, dst, table(case.dst))
     torch.cuda.synchronize()
