@@ -4,7 +4,8 @@
 ids out of range, random-bit payloads (NaN patterns included),
 sentinel-filled destinations and guard bytes after the staging; token-major
 pools; pools whose blocks hold several planes' pages; launches of 65-160 MiB each way with rows of 1-16 KiB; head-sliced
-copies and permutes.  Every case is compared byte for byte over the whole
+copies and permutes; page-table offsets that read outside their request's
+list.  Every case is compared byte for byte over the whole
 destination, and the skip counters must agree.  KVX_FUZZ_SCALE=k multiplies
 the number of cases of each family (a longer campaign)."""
 import os
@@ -68,6 +69,22 @@ def test_fuzz_paged_many_requests(seed):
     oor = float(rng.choice([0.0, 0.0, 0.05]))
     case = big_case(f"fuzzmany{seed}", g, list(lens), sp, dp, 89000 + seed, oor)
     run_paged_case(case, 89000 + seed)
+
+
+@pytest.mark.parametrize("seed", seeds(24))
+def test_fuzz_table_index_faults(seed):
+    # page-table offsets that send lookups below 0, past the page-id array or
+    # into another request's list, in random geometries, with and without
+    # out-of-range ids; a third of the cases with up to 200 requests
+    rng = np.random.default_rng(87000 + seed)
+    g = random_geometry(rng)
+    many = seed % 3 == 2
+    case = wl.random_case(87000 + seed, geom=g, max_reqs=int(rng.integers(70, 200)) if many
+                          else int(rng.integers(1, 9)), max_len=4 if many else 60,
+                          src_page=int(rng.choice([1, 2, 3, 16])),
+                          dst_page=int(rng.choice([1, 2, 3, 16])),
+                          oor_frac=float(rng.choice([0.0, 0.1])), index_faults=True)
+    run_paged_case(case, 87000 + seed)
 
 
 @pytest.mark.parametrize("seed", seeds(16))
