@@ -36,6 +36,7 @@ on the host on a bounded sample of the same steps.
   python bench.py --concurrent          (the transfer under a decode-like HBM reader)
   python bench.py --cu-split            (the two on complementary CU-masked streams)
   python bench.py --comparators         (per-block runtime copies, DMA copy of staging)
+  python bench.py --patterns            (the request's row patterns moved without tables)
   python bench.py --sizes               (one request of 16 .. 8192 tokens: latency to bandwidth)
   python bench.py --batches             (49152 tokens in 1 .. 49152 requests: request lookup)
   python bench.py --row-sizes           (rows of 256 B .. 16 KiB at ~256 MiB each way)
@@ -1180,6 +1181,60 @@ def row_sizes(torch, kvx, wl, wdev, dev, stream):
         torch.cuda.empty_cache()
 
 
+# (name, mode bits of wdev.row_pattern): the access patterns of the paged ops
+# on the 2048-token request's 72 x 2048 rows of 2 KiB, with no table read
+PATTERNS = [("random source -> random destination (gather-scatter)", 15),
+            ("random source -> contiguous (gather)", 7),
+            ("contiguous -> random destination (scatter)", 11),
+            ("contiguous -> contiguous (plain copy)", 3),
+            ("random reads only", 5), ("random writes only", 10),
+            ("contiguous reads only", 1), ("contiguous writes only", 2)]
+
+
+def row_patterns(torch, kvx, wl, wdev, dev, stream, rounds=3, n=32):
+    """The 2048-token request's access patterns moved by a table-free kernel
+    (wl_row_pattern: each row's slot a bijective hash of its token, 16
+    disjoint slot sets rotated, in the same two 4.5 GiB pools), 1, 2 and 4
+    rows per wave, beside the library's ops timed alone in the same process:
+    what the patterns cost by themselves, against what the paged kernels with
+    their table reads achieve."""
+    wk = Workload(torch, kvx, wl, wdev, dev, stream)
+    Q, T, S = wk.Q, wk.T, wk.S
+    if wk.R != 2048:
+        raise SystemExit("the pattern kernel moves 2 KiB rows")
+    sink = torch.zeros(2048, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    res = {}
+    for _ in range(rounds):
+        for name, mode in PATTERNS:
+            nbytes = Q * T * 2048 * ((mode & 1) + ((mode >> 1) & 1))
+            for K in (1, 2, 4):
+                for i in range(4):
+                    wdev.row_pattern(wk.A, wk.B, sink, Q, T, S, K, i % (S // T), mode, stream)
+                ev[0].record(stream)
+                for i in range(n):
+                    wdev.row_pattern(wk.A, wk.B, sink, Q, T, S, K, i % (S // T), mode, stream)
+                ev[1].record(stream)
+                torch.cuda.synchronize()
+                ms = ev[0].elapsed_time(ev[1]) / n
+                res.setdefault((name, K), []).append(nbytes / (ms * 1e-3) / 1e9)
+    pats = []
+    for name, mode in PATTERNS:
+        row = {"pattern": name, "mode": mode}
+        for K in (1, 2, 4):
+            v = sorted(res[(name, K)])
+            row[f"rows_per_wave_{K}_GBps"] = round(v[len(v) // 2], 1)
+        pats.append(row)
+        log(f"  {name:55s} " + "  ".join(f"{row[f'rows_per_wave_{K}_GBps']:7.1f}" for K in (1, 2, 4)))
+    iso = time_isolated(torch, wk, stream)
+    out = {"row_patterns": pats,
+           "library_ops_alone_GBps": {op: iso[op]["GBps"] for op in OPS},
+           "note": "rates count bytes read + written; each pattern launch moves the request's "
+                   "72 x 2048 rows of 2 KiB (302 MB each way it reads or writes)"}
+    print(json.dumps(out), flush=True)
+
+
 def comparators(torch, kvx, wl, wdev, dev):
     """The same 2048-token request moved by per-block runtime copies."""
     import ctypes
@@ -1458,8 +1513,8 @@ COMPARATOR_ROWS = [
 
 
 def summarize_json(log_path, out_path, title, command):
-    """Markdown tables from the JSON lines that --concurrent, --cu-split and
-    --comparators print (any of them, in one log)."""
+    """Markdown tables from the JSON lines that --concurrent, --cu-split,
+    --comparators and --patterns print (any of them, in one log)."""
     lines = []
     with open(log_path) as f:
         for line in f:
@@ -1519,6 +1574,21 @@ def summarize_json(log_path, out_path, title, command):
                     calls = r.get("calls", 1)
                     gbps = r.get("GBps", round(603979776 / (r["ms"] * 1e6), 1))
                     f.write(f"| {label} | {calls} | {r['ms']} | {gbps} |\n")
+                f.write("\n")
+            if "row_patterns" in d:
+                f.write("The 2048-token request's 72 x 2048 rows of 2 KiB moved by a table-free "
+                        "kernel (each row's slot a bijective hash of its token in the same two "
+                        "4.5 GiB page-1 pools, 16 disjoint slot sets rotated), by access "
+                        "pattern and rows per wave.\n\n")
+                f.write("| pattern | 1 row / wave | 2 rows / wave | 4 rows / wave |\n"
+                        "|---|---:|---:|---:|\n")
+                for r in d["row_patterns"]:
+                    f.write(f"| {r['pattern']} | {r['rows_per_wave_1_GBps']} | "
+                            f"{r['rows_per_wave_2_GBps']} | {r['rows_per_wave_4_GBps']} |\n")
+                f.write("\nThe library's ops on the same request, timed alone in the same "
+                        "process (with their page-table reads):\n\n| op | GB/s |\n|---|---:|\n")
+                for op, v in d["library_ops_alone_GBps"].items():
+                    f.write(f"| {op} | {v} |\n")
                 f.write("\n")
             if "note" in d:
                 f.write(f"Note: {d['note']}\n\n")
@@ -1591,6 +1661,9 @@ def main():
                     help="49152 tokens split into 1 .. 49152 requests (request lookup cost)")
     ap.add_argument("--comparators", action="store_true",
                     help="the same request moved by one runtime copy per block / per run")
+    ap.add_argument("--patterns", action="store_true",
+                    help="the request's row patterns moved by a table-free kernel, beside "
+                         "the library's ops")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "OUT", "TITLE", "CMD"),
                     help="markdown summary of a rocprofv3 --kernel-trace --stats run")
@@ -1602,7 +1675,7 @@ def main():
                     help="what --pmc-pass runs")
     ap.add_argument("--summarize-json", nargs=4, metavar=("LOG", "OUT", "TITLE", "CMD"),
                     help="markdown tables from the JSON lines of --concurrent / --cu-split / "
-                         "--comparators")
+                         "--comparators / --patterns")
     ap.add_argument("--counter-commands", action="store_true",
                     help="print the rocprofv3 command of every counter pass")
     args = ap.parse_args()
@@ -1663,6 +1736,9 @@ def main():
         return 0
     if args.comparators:
         comparators(torch, kvx, wl, wdev, dev)
+        return 0
+    if args.patterns:
+        row_patterns(torch, kvx, wl, wdev, dev, stream)
         return 0
     if args.pmc_pass:
         pmc_pass(torch, kvx, wl, wdev, dev, stream, args.pmc_workload)

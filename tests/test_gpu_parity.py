@@ -556,3 +556,33 @@ def test_device_fill_matches_host_hash():
     assert_bytes_equal(t.cpu().numpy(), wl.hash_fill_host(1234567, t.numel()), "fill_hash")
     w = t[:40].cpu().numpy().view("<u8")
     assert int(w[0]) == 6457827717110365317
+
+
+@pytest.mark.parametrize("K", [1, 2, 4])
+def test_row_pattern_moves_the_rows_it_names(K):
+    """The measurement helper wl_row_pattern (a table-free row mover used only
+    to time access patterns) touches exactly the rows its slot map names:
+    random to random copies slot f(q, t) of each plane to the same slot,
+    random to contiguous and contiguous to random follow the same map, and
+    every other byte stays as it was."""
+    from workloads import device as wdev
+    Q, T, S, st = 3, 8, 32, 2
+    rng = np.random.default_rng(K)
+    src_h = rng.integers(0, 256, (Q, S, 2048), dtype=np.uint8)
+    dst_h = rng.integers(0, 256, (Q, S, 2048), dtype=np.uint8)
+    slot = [[((t + st * T) * 40503 + q * 977) % S for t in range(T)] for q in range(Q)]
+    sink = torch.zeros(2048, dtype=torch.int32, device=DEV)
+    for mode in (15, 7, 11):
+        a, b = torch.from_numpy(src_h).to(DEV), torch.from_numpy(dst_h).to(DEV)
+        say(f"row_pattern K={K} mode={mode}")
+        wdev.row_pattern(a, b, sink, Q, T, S, K, st, mode)
+        torch.cuda.synchronize()
+        exp = dst_h.copy()
+        flat_exp, flat_src = exp.reshape(-1, 2048), src_h.reshape(-1, 2048)
+        for q in range(Q):
+            for t in range(T):
+                s_row = q * S + slot[q][t] if mode & 4 else q * T + t
+                d_row = q * S + slot[q][t] if mode & 8 else q * T + t
+                flat_exp[d_row] = flat_src[s_row]
+        assert_bytes_equal(b.cpu().numpy(), exp, f"row_pattern mode {mode}")
+        assert_bytes_equal(a.cpu().numpy(), src_h, "row_pattern source untouched")

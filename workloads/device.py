@@ -1,5 +1,7 @@
 """Device-side generators: fill torch device buffers with the hash words of
-workloads.splitmix64, and a plain copy kernel for counter calibration."""
+workloads.splitmix64, a plain copy kernel for counter calibration, a
+streaming reader (a concurrent load) and a table-free row-pattern mover (the
+cost of the paged ops' access patterns by themselves)."""
 from __future__ import annotations
 
 import ctypes
@@ -24,7 +26,11 @@ def _load():
                                 ctypes.c_void_p]
         lib.wl_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                        ctypes.c_int, ctypes.c_void_p]
+        lib.wl_row_pattern.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_void_p] + [ctypes.c_int32] * 5 + [
+                                       ctypes.c_uint32, ctypes.c_void_p]
         lib.wl_fill_hash.restype = lib.wl_copy.restype = lib.wl_read_stream.restype = ctypes.c_int
+        lib.wl_row_pattern.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -62,3 +68,21 @@ def read_stream(src: torch.Tensor, sink: torch.Tensor, blocks: int = 2048, strea
                                 sink.data_ptr(), blocks, _stream(stream))
     if rc != 0:
         raise RuntimeError(f"wl_read_stream failed ({rc})")
+
+
+PATTERN_READ, PATTERN_WRITE, PATTERN_RANDOM_SRC, PATTERN_RANDOM_DST = 1, 2, 4, 8
+
+
+def row_pattern(src: torch.Tensor, dst: torch.Tensor, sink: torch.Tensor, Q: int, T: int, S: int,
+                K: int, slot_set: int, mode: int, stream=None) -> None:
+    """Table-free mover of Q x T rows of 2 KiB (wl_row_pattern): read and/or
+    write each row at a random slot of a [Q][S][2048] buffer or at its
+    contiguous place in a [Q][T][2048] buffer, per the mode bits; slot sets
+    0 .. S/T - 1 are disjoint.  ``sink``: at least 2048 int32 words."""
+    if sink.numel() * sink.element_size() < 2048 * 4:
+        raise ValueError("sink too small")
+    rc = _load().wl_row_pattern(src.data_ptr(), src.numel() * src.element_size(),
+                                dst.data_ptr(), dst.numel() * dst.element_size(),
+                                sink.data_ptr(), Q, T, S, K, slot_set, mode, _stream(stream))
+    if rc != 0:
+        raise RuntimeError(f"wl_row_pattern failed ({rc})")
