@@ -1191,47 +1191,94 @@ PATTERNS = [("random source -> random destination (gather-scatter)", 15),
             ("contiguous reads only", 1), ("contiguous writes only", 2)]
 
 
+def _pattern_rates(torch, wdev, A, B, Q, T, S, R, patterns, stream, rounds, n):
+    """Median GB/s (r+w) of each (pattern, rows per wave) of wl_row_pattern."""
+    sink = torch.zeros(2048, dtype=torch.int32, device=A.device)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    res = {}
+    for _ in range(rounds):
+        for name, mode in patterns:
+            nbytes = Q * T * R * ((mode & 1) + ((mode >> 1) & 1))
+            for K in (1, 2, 4):
+                for i in range(4):
+                    wdev.row_pattern(A, B, sink, Q, T, S, K, i % (S // T), mode, stream, R)
+                ev[0].record(stream)
+                for i in range(n):
+                    wdev.row_pattern(A, B, sink, Q, T, S, K, i % (S // T), mode, stream, R)
+                ev[1].record(stream)
+                torch.cuda.synchronize()
+                ms = ev[0].elapsed_time(ev[1]) / n
+                res.setdefault((name, K), []).append(nbytes / (ms * 1e-3) / 1e9)
+    rows = []
+    for name, mode in patterns:
+        row = {"pattern": name, "mode": mode}
+        for K in (1, 2, 4):
+            v = sorted(res[(name, K)])
+            row[f"rows_per_wave_{K}_GBps"] = round(v[len(v) // 2], 1)
+        rows.append(row)
+        log(f"  {name:55s} " + "  ".join(f"{row[f'rows_per_wave_{K}_GBps']:7.1f}" for K in (1, 2, 4)))
+    return rows
+
+
 def row_patterns(torch, kvx, wl, wdev, dev, stream, rounds=3, n=32):
     """The 2048-token request's access patterns moved by a table-free kernel
     (wl_row_pattern: each row's slot a bijective hash of its token, 16
     disjoint slot sets rotated, in the same two 4.5 GiB pools), 1, 2 and 4
     rows per wave, beside the library's ops timed alone in the same process:
     what the patterns cost by themselves, against what the paged kernels with
-    their table reads achieve."""
+    their table reads achieve.  Then the same for the MLA request (27 planes
+    of 1152-byte rows, 2048 tokens, 32768-slot page-1 pools)."""
     wk = Workload(torch, kvx, wl, wdev, dev, stream)
     Q, T, S = wk.Q, wk.T, wk.S
-    if wk.R != 2048:
-        raise SystemExit("the pattern kernel moves 2 KiB rows")
-    sink = torch.zeros(2048, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    res = {}
-    for _ in range(rounds):
-        for name, mode in PATTERNS:
-            nbytes = Q * T * 2048 * ((mode & 1) + ((mode >> 1) & 1))
-            for K in (1, 2, 4):
-                for i in range(4):
-                    wdev.row_pattern(wk.A, wk.B, sink, Q, T, S, K, i % (S // T), mode, stream)
-                ev[0].record(stream)
-                for i in range(n):
-                    wdev.row_pattern(wk.A, wk.B, sink, Q, T, S, K, i % (S // T), mode, stream)
-                ev[1].record(stream)
-                torch.cuda.synchronize()
-                ms = ev[0].elapsed_time(ev[1]) / n
-                res.setdefault((name, K), []).append(nbytes / (ms * 1e-3) / 1e9)
-    pats = []
-    for name, mode in PATTERNS:
-        row = {"pattern": name, "mode": mode}
-        for K in (1, 2, 4):
-            v = sorted(res[(name, K)])
-            row[f"rows_per_wave_{K}_GBps"] = round(v[len(v) // 2], 1)
-        pats.append(row)
-        log(f"  {name:55s} " + "  ".join(f"{row[f'rows_per_wave_{K}_GBps']:7.1f}" for K in (1, 2, 4)))
+    pats = _pattern_rates(torch, wdev, wk.A, wk.B, Q, T, S, wk.R, PATTERNS, stream, rounds, n)
     iso = time_isolated(torch, wk, stream)
+    del wk
+    torch.cuda.empty_cache()
+    # MLA: the library's gather-scatter, gather and scatter of 16 disjoint
+    # requests rotated, and the same rows without tables
+    cs = [wl.mla_case(1, k) for k in range(NREQ)]
+    c, g = cs[0], cs[0].geom
+    Qm, Rm, Sm = g.planes, g.row_bytes, c.src.num_slots
+    A = torch.zeros((Qm, Sm, Rm), dtype=torch.uint8, device=dev)
+    B = torch.zeros((Qm, Sm, Rm), dtype=torch.uint8, device=dev)
+    d = lambda a: torch.from_numpy(a).to(dev)
+    reqs = kvx.Requests(d(c.tok_off), c.total_tokens)
+    tabs = [(kvx.Table(d(x.src.pg_off), d(x.src.ids)), kvx.Table(d(x.dst.pg_off), d(x.dst.ids)))
+            for x in cs]
+    lay = kvx.Layout(g.num_layers, g.num_kv, g.kv_heads, g.head_dim, g.dtype)
+    PA, PB = kvx.Pool(A, c.src.num_pages), kvx.Pool(B, c.dst.num_pages)
+    st = torch.empty(c.total_tokens * g.token_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    mla_ops = {
+        "gather_scatter": lambda i: kvx.gather_scatter(lay, PA, tabs[i % NREQ][0], reqs, PB,
+                                                       tabs[i % NREQ][1], stream=stream),
+        "gather": lambda i: kvx.gather(lay, PA, tabs[i % NREQ][0], reqs, st, stream=stream),
+        "scatter": lambda i: kvx.scatter(lay, st, reqs, PB, tabs[i % NREQ][1], stream=stream)}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    mla_lib = {}
+    for _ in range(rounds):
+        for op, fn in mla_ops.items():
+            for i in range(4):
+                fn(i)
+            ev[0].record(stream)
+            for i in range(n):
+                fn(i)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ms = ev[0].elapsed_time(ev[1]) / n
+            mla_lib.setdefault(op, []).append(2 * c.payload_bytes() / (ms * 1e-3) / 1e9)
+    mla_lib = {op: round(sorted(v)[len(v) // 2], 1) for op, v in mla_lib.items()}
+    log(f"  MLA library ops: {mla_lib}")
+    mla_pats = _pattern_rates(torch, wdev, A, B, Qm, c.total_tokens, Sm, Rm, PATTERNS[:3] +
+                              PATTERNS[4:6], stream, rounds, n)
     out = {"row_patterns": pats,
            "library_ops_alone_GBps": {op: iso[op]["GBps"] for op in OPS},
-           "note": "rates count bytes read + written; each pattern launch moves the request's "
-                   "72 x 2048 rows of 2 KiB (302 MB each way it reads or writes)"}
+           "mla_row_patterns": mla_pats, "library_mla_ops_GBps": mla_lib,
+           "note": "rates count bytes read + written; a pattern launch moves the request's "
+                   "rows: 72 x 2048 of 2 KiB (302 MB each way it reads or writes), or for "
+                   "MLA 27 x 2048 of 1152 bytes (64 MB each way); the library's ops are "
+                   "launched back to back on rotated requests, nothing reading their output"}
     print(json.dumps(out), flush=True)
 
 
@@ -1588,6 +1635,19 @@ def summarize_json(log_path, out_path, title, command):
                 f.write("\nThe library's ops on the same request, timed alone in the same "
                         "process (with their page-table reads):\n\n| op | GB/s |\n|---|---:|\n")
                 for op, v in d["library_ops_alone_GBps"].items():
+                    f.write(f"| {op} | {v} |\n")
+                f.write("\n")
+            if "mla_row_patterns" in d:
+                f.write("The MLA request (27 planes of 1152-byte rows, 2048 tokens, 32768-slot "
+                        "page-1 pools, 64 MB each way) moved the same ways without tables:\n\n")
+                f.write("| pattern | 1 row / wave | 2 rows / wave | 4 rows / wave |\n"
+                        "|---|---:|---:|---:|\n")
+                for r in d["mla_row_patterns"]:
+                    f.write(f"| {r['pattern']} | {r['rows_per_wave_1_GBps']} | "
+                            f"{r['rows_per_wave_2_GBps']} | {r['rows_per_wave_4_GBps']} |\n")
+                f.write("\nThe library's MLA ops in the same process (16 disjoint requests "
+                        "rotated):\n\n| op | GB/s |\n|---|---:|\n")
+                for op, v in d["library_mla_ops_GBps"].items():
                     f.write(f"| {op} | {v} |\n")
                 f.write("\n")
             if "note" in d:

@@ -558,8 +558,8 @@ def test_device_fill_matches_host_hash():
     assert int(w[0]) == 6457827717110365317
 
 
-@pytest.mark.parametrize("K", [1, 2, 4])
-def test_row_pattern_moves_the_rows_it_names(K):
+@pytest.mark.parametrize("K,R", [(1, 2048), (2, 2048), (4, 2048), (4, 1152), (1, 48), (2, 4096)])
+def test_row_pattern_moves_the_rows_it_names(K, R):
     """The measurement helper wl_row_pattern (a table-free row mover used only
     to time access patterns) touches exactly the rows its slot map names:
     random to random copies slot f(q, t) of each plane to the same slot,
@@ -568,17 +568,17 @@ def test_row_pattern_moves_the_rows_it_names(K):
     from workloads import device as wdev
     Q, T, S, st = 3, 8, 32, 2
     rng = np.random.default_rng(K)
-    src_h = rng.integers(0, 256, (Q, S, 2048), dtype=np.uint8)
-    dst_h = rng.integers(0, 256, (Q, S, 2048), dtype=np.uint8)
+    src_h = rng.integers(0, 256, (Q, S, R), dtype=np.uint8)
+    dst_h = rng.integers(0, 256, (Q, S, R), dtype=np.uint8)
     slot = [[((t + st * T) * 40503 + q * 977) % S for t in range(T)] for q in range(Q)]
     sink = torch.zeros(2048, dtype=torch.int32, device=DEV)
     for mode in (15, 7, 11):
         a, b = torch.from_numpy(src_h).to(DEV), torch.from_numpy(dst_h).to(DEV)
-        say(f"row_pattern K={K} mode={mode}")
-        wdev.row_pattern(a, b, sink, Q, T, S, K, st, mode)
+        say(f"row_pattern K={K} R={R} mode={mode}")
+        wdev.row_pattern(a, b, sink, Q, T, S, K, st, mode, row_bytes=R)
         torch.cuda.synchronize()
         exp = dst_h.copy()
-        flat_exp, flat_src = exp.reshape(-1, 2048), src_h.reshape(-1, 2048)
+        flat_exp, flat_src = exp.reshape(-1, R), src_h.reshape(-1, R)
         for q in range(Q):
             for t in range(T):
                 s_row = q * S + slot[q][t] if mode & 4 else q * T + t

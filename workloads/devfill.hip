@@ -10,7 +10,7 @@
 //     traffic.
 //   wl_read_stream: a streaming HBM reader standing in for decode attention
 //     reading its KV, to load the memory system while the kvx path runs.
-//   wl_row_pattern: a table-free mover of 2 KiB rows that measures what the
+//   wl_row_pattern: a table-free mover of rows that measures what the
 //     paged ops' access patterns cost by themselves (random slots on either
 //     side, no page tables read).
 #include <hip/hip_runtime.h>
@@ -66,16 +66,17 @@ __global__ void k_read_stream(const u32x4* __restrict__ src, int64_t n16,
 
 // Row r of a pattern launch is row t = r % T of plane q = r / T.  Its place
 // on a random side is slot ((t + set * T) * 40503 + q * 977) mod S of plane q
-// in a [Q][S][2048] buffer -- a bijection of the plane's S slots (S a power
-// of two, the multiplier odd), so sets 0 .. S/T - 1 touch disjoint slots; on
-// a contiguous side it is row q * T + t of a [Q][T][2048] buffer.  K rows per
-// wave, two-wave workgroups; loads and stores are 16-byte nontemporal, all K
-// rows' loads issued before the first store.
+// in a [Q][S][R] buffer -- a bijection of the plane's S slots (S a power of
+// two, the multiplier odd), so sets 0 .. S/T - 1 touch disjoint slots; on a
+// contiguous side it is row q * T + t of a [Q][T][R] buffer.  Rows of R
+// bytes (a multiple of 16, at most 4 KiB: lane l moves bytes 16 l + 1024 v
+// of a row), K rows per wave, two-wave workgroups; loads and stores are
+// 16-byte nontemporal, all K rows' loads issued before the first store.
 struct PatternArgs {
     const char* src;
     char* dst;
     unsigned* sink;
-    int32_t Q, T, S, set;
+    int32_t Q, T, S, set, R;
     uint32_t mode;              // 1 read, 2 write, 4 random source, 8 random destination
 };
 
@@ -86,18 +87,20 @@ __device__ __forceinline__ uint64_t pattern_row(uint64_t base, bool rnd, uint32_
     if (rnd) {
         const uint32_t slot = ((t + static_cast<uint32_t>(a.set) * a.T) * 40503u + q * 977u) &
                               static_cast<uint32_t>(a.S - 1);
-        return base + (static_cast<uint64_t>(q) * a.S + slot) * 2048u;
+        return base + (static_cast<uint64_t>(q) * a.S + slot) * static_cast<uint64_t>(a.R);
     }
-    return base + (static_cast<uint64_t>(q) * a.T + t) * 2048u;
+    return base + (static_cast<uint64_t>(q) * a.T + t) * static_cast<uint64_t>(a.R);
 }
 
 template <int K>
 __global__ __launch_bounds__(128) void k_row_pattern(PatternArgs a) {
+    constexpr int V = 4;                                   // 1 KiB steps of a row
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t w = blockIdx.x * 2u + (threadIdx.x >> 6);
     const uint32_t rows = static_cast<uint32_t>(a.Q) * static_cast<uint32_t>(a.T);
+    const uint32_t R = static_cast<uint32_t>(a.R);
     uint64_t sa[K], da[K];
-    u32x4 x[K][2];
+    u32x4 x[K][V];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
         const uint32_t r = w * K + j;
@@ -107,28 +110,34 @@ __global__ __launch_bounds__(128) void k_row_pattern(PatternArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-        if (a.mode & 1u) {
-            x[j][0] = __builtin_nontemporal_load(reinterpret_cast<const g_u32x4*>(sa[j] + lane * 16u));
-            x[j][1] = __builtin_nontemporal_load(
-                reinterpret_cast<const g_u32x4*>(sa[j] + 1024u + lane * 16u));
-        } else {
-            x[j][0] = u32x4{w, lane, 1u, 2u};
-            x[j][1] = u32x4{w, lane, 3u, 4u};
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const uint32_t off = v * 1024u + lane * 16u;
+            if ((a.mode & 1u) && off < R)
+                x[j][v] = __builtin_nontemporal_load(reinterpret_cast<const g_u32x4*>(sa[j] + off));
+            else
+                x[j][v] = u32x4{w, lane, static_cast<uint32_t>(j), static_cast<uint32_t>(v)};
         }
     }
     if (a.mode & 2u) {
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             if (w * K + j < rows) {
-                __builtin_nontemporal_store(x[j][0], reinterpret_cast<g_u32x4*>(da[j] + lane * 16u));
-                __builtin_nontemporal_store(x[j][1],
-                                            reinterpret_cast<g_u32x4*>(da[j] + 1024u + lane * 16u));
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const uint32_t off = v * 1024u + lane * 16u;
+                    if (off < R)
+                        __builtin_nontemporal_store(x[j][v],
+                                                    reinterpret_cast<g_u32x4*>(da[j] + off));
+                }
             }
         }
     } else {
         uint32_t acc = 0;
 #pragma unroll
-        for (int j = 0; j < K; ++j) acc ^= x[j][0].x ^ x[j][0].w ^ x[j][1].y ^ x[j][1].z;
+        for (int j = 0; j < K; ++j)
+#pragma unroll
+            for (int v = 0; v < V; ++v) acc ^= x[j][v].x ^ x[j][v].w;
         if (acc == 0x9e3779b9u && lane == 0) a.sink[w & 2047u] = acc;   // keeps the loads
     }
 }
@@ -179,28 +188,29 @@ int wl_read_stream(const void* src, int64_t nbytes, void* sink, int blocks, hipS
     return static_cast<int>(hipGetLastError());
 }
 
-// Table-free row pattern (see k_row_pattern): Q planes of T rows of 2 KiB,
-// S slots per plane on a random side (a power of two >= T), slot set `set`
-// (0 .. S/T - 1), K rows per wave (1, 2 or 4), mode bits 1 read, 2 write,
-// 4 random source, 8 random destination.  src_bytes / dst_bytes must hold
-// what the mode addresses ([Q][S][2048] random, [Q][T][2048] contiguous);
-// sink must hold 2048 words.
+// Table-free row pattern (see k_row_pattern): Q planes of T rows of R bytes
+// (16 .. 4096, a multiple of 16), S slots per plane on a random side (a power
+// of two >= T), slot set `set` (0 .. S/T - 1), K rows per wave (1, 2 or 4),
+// mode bits 1 read, 2 write, 4 random source, 8 random destination.
+// src_bytes / dst_bytes must hold what the mode addresses ([Q][S][R] random,
+// [Q][T][R] contiguous); sink must hold 2048 words.
 int wl_row_pattern(const void* src, int64_t src_bytes, void* dst, int64_t dst_bytes, void* sink,
-                   int32_t Q, int32_t T, int32_t S, int32_t K, int32_t set, uint32_t mode,
-                   hipStream_t stream) {
+                   int32_t Q, int32_t T, int32_t S, int32_t R, int32_t K, int32_t set,
+                   uint32_t mode, hipStream_t stream) {
     if (Q < 1 || T < 1 || S < T || (S & (S - 1)) != 0 || set < 0 ||
         static_cast<int64_t>(set + 1) * T > S || (K != 1 && K != 2 && K != 4) ||
+        R < 16 || R > 4096 || R % 16 != 0 ||
         (mode & 3u) == 0 || mode > 15u || sink == nullptr ||
         static_cast<int64_t>(Q) * T > (int64_t(1) << 30))
         return -1;
-    const int64_t rnd = static_cast<int64_t>(Q) * S * 2048, cont = static_cast<int64_t>(Q) * T * 2048;
+    const int64_t rnd = static_cast<int64_t>(Q) * S * R, cont = static_cast<int64_t>(Q) * T * R;
     // the source is addressed in every mode (a write-only launch computes but never reads it)
     if (src == nullptr || src_bytes < ((mode & 4u) ? rnd : cont)) return -1;
     if ((mode & 2u) && (dst == nullptr || dst_bytes < ((mode & 8u) ? rnd : cont))) return -1;
     if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) != 0)
         return -1;
     PatternArgs a{static_cast<const char*>(src), static_cast<char*>(dst),
-                  static_cast<unsigned*>(sink), Q, T, S, set, mode};
+                  static_cast<unsigned*>(sink), Q, T, S, set, R, mode};
     const int64_t waves = (static_cast<int64_t>(Q) * T + K - 1) / K;
     const dim3 grid(static_cast<unsigned>((waves + 1) / 2));
     switch (K) {

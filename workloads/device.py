@@ -27,7 +27,7 @@ def _load():
         lib.wl_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                        ctypes.c_int, ctypes.c_void_p]
         lib.wl_row_pattern.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                       ctypes.c_int64, ctypes.c_void_p] + [ctypes.c_int32] * 5 + [
+                                       ctypes.c_int64, ctypes.c_void_p] + [ctypes.c_int32] * 6 + [
                                        ctypes.c_uint32, ctypes.c_void_p]
         lib.wl_fill_hash.restype = lib.wl_copy.restype = lib.wl_read_stream.restype = ctypes.c_int
         lib.wl_row_pattern.restype = ctypes.c_int
@@ -74,15 +74,16 @@ PATTERN_READ, PATTERN_WRITE, PATTERN_RANDOM_SRC, PATTERN_RANDOM_DST = 1, 2, 4, 8
 
 
 def row_pattern(src: torch.Tensor, dst: torch.Tensor, sink: torch.Tensor, Q: int, T: int, S: int,
-                K: int, slot_set: int, mode: int, stream=None) -> None:
-    """Table-free mover of Q x T rows of 2 KiB (wl_row_pattern): read and/or
-    write each row at a random slot of a [Q][S][2048] buffer or at its
-    contiguous place in a [Q][T][2048] buffer, per the mode bits; slot sets
+                K: int, slot_set: int, mode: int, stream=None, row_bytes: int = 2048) -> None:
+    """Table-free mover of Q x T rows of ``row_bytes`` (wl_row_pattern): read
+    and/or write each row at a random slot of a [Q][S][R] buffer or at its
+    contiguous place in a [Q][T][R] buffer, per the mode bits; slot sets
     0 .. S/T - 1 are disjoint.  ``sink``: at least 2048 int32 words."""
     if sink.numel() * sink.element_size() < 2048 * 4:
         raise ValueError("sink too small")
     rc = _load().wl_row_pattern(src.data_ptr(), src.numel() * src.element_size(),
                                 dst.data_ptr(), dst.numel() * dst.element_size(),
-                                sink.data_ptr(), Q, T, S, K, slot_set, mode, _stream(stream))
+                                sink.data_ptr(), Q, T, S, row_bytes, K, slot_set, mode,
+                                _stream(stream))
     if rc != 0:
         raise RuntimeError(f"wl_row_pattern failed ({rc})")
