@@ -256,6 +256,25 @@ uint32_t sub_shift_for(const Shape& sh, int64_t tokens, int32_t nq, int64_t row_
     return chunks < (uint64_t(1) << 31) ? shift : 0u;
 }
 
+// A gather's staging holds each request's planes one after another, n_r
+// rows per plane.  When requests are short -- on average at most 64 KiB of
+// rows per plane -- token-major chunk order (the planes of a token block on
+// adjacent waves) writes each request's block in longer runs than
+// plane-major order does.  Measured (same process, alternating; 49152 or
+// 65536 tokens in 64 .. 24576 equal requests, page-1 pools of 65536 slots):
+// 2 KiB rows, 32 tokens per request 5164 -> 5672 GB/s, 16 tokens 4991 ->
+// 5580, one token 4905 -> 5696, while 96 tokens lose (5679 -> 5261) and one
+// request of 49152 tokens loses 16%; 512-byte rows, 128 tokens 5431 -> 5789,
+// 256 tokens 5566 -> 5448; 1152-byte rows, 32 tokens 5207 -> 5463.  The
+// scatter, which reads the staging, gains at most 5% and loses up to 5%
+// (512-byte rows), so it keeps plane-major order.
+constexpr int64_t kShortStageRunBytes = 64 << 10;
+
+bool short_stage_runs(const kvx_reqs* reqs, int64_t row_bytes) {
+    return reqs->num_reqs > 1 &&
+           reqs->total_tokens * row_bytes <= kShortStageRunBytes * reqs->num_reqs;
+}
+
 // Bytes a wave of a large paged launch moves (see wide_rows_for); permutes
 // move one row per wave.
 constexpr int64_t kPagedWaveBytes = 2048;
@@ -511,7 +530,9 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
                         : remap_for(pool_span(src != nullptr ? src : dst, q0, nq),
                                     kRemapOnePoolBytes);
         a.c.tmajor = sub == 0 && (slot_interleaved(dst, q0, nq) ||
-                                  (dst != nullptr && slot_interleaved(src, q0, nq)))
+                                  (dst != nullptr && slot_interleaved(src, q0, nq)) ||
+                                  (std::is_same<Dst, StageRef>::value &&
+                                   short_stage_runs(reqs, g.R)))
                          ? 1u : 0u;
         // token-major order renumbers at any size, so that each XCD takes whole
         // tokens' runs rather than every eighth row of each: measured on the

@@ -34,7 +34,8 @@
 // Waves grid-stride over the chunks (by default the grid has one wave per
 // chunk; the host can cap it at a few workgroups per compute unit).  Chunks
 // are numbered plane-major, or token-major when a pool the call writes keeps
-// a token's rows of all planes in one contiguous run (see paged_chunk).  In
+// a token's rows of all planes in one contiguous run, or when a gather's
+// requests are short enough that its staging blocks are (see paged_chunk).  In
 // launches over large pools, and in token-major order, workgroup ids are
 // renumbered so that consecutive chunks run on the same XCD: gfx950 deals
 // workgroups to its 8 XCDs round-robin, and each XCD has its own L2 and
@@ -212,7 +213,8 @@ struct PagedChunk {
 // waves: the host picks it when the pool a call writes (or, pool to pool,
 // either pool) keeps the planes of one slot within one slot stride, so that
 // a token's rows of all planes are one contiguous run that adjacent waves
-// stream together.
+// stream together, and for a gather whose requests average at most 64 KiB
+// of rows per plane, whose staging blocks are then written in longer runs.
 __device__ __forceinline__ PagedChunk paged_chunk(const Common& c, uint32_t chunk) {
     PagedChunk k;
     if (c.tmajor) {

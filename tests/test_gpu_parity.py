@@ -231,6 +231,33 @@ def test_one_row_per_wave_many_requests(bi):
     run_paged_case(big_case(f"bigmany{bi}", g, list(lens), sp, dp, 760 + bi, oor), 760 + bi)
 
 
+# Gathers of short requests (at most 64 KiB of rows per plane on average)
+# run in token-major chunk order: every copy shape (flat, row-loop, wide with
+# several rows or one row per chunk, 2 KiB pieces of larger rows), ragged
+# lengths with empty requests, below and above 64 requests, page sizes 1-16,
+# some ids out of range.  (geometry, requests, max length, src page, dst page)
+SHORT = [
+    (wl.Geometry(1, 2, 1, 8, "bf16"), 40, 30, 1, 1),          # R = 16, flat
+    (wl.Geometry(2, 2, 3, 128, "bf16"), 90, 40, 2, 16),       # R = 768, row-loop
+    (wl.Geometry(3, 1, 1, 576, "bf16"), 300, 50, 1, 3),       # R = 1152, row-loop
+    (wl.Geometry(2, 2, 4, 128, "bf16"), 70, 60, 16, 1),       # R = 1 KiB, wide
+    (wl.Geometry(2, 2, 8, 128, "bf16"), 2000, 20, 1, 2),      # R = 2 KiB, wide
+    (wl.Geometry(1, 2, 32, 128, "bf16"), 400, 12, 1, 1),      # R = 8 KiB
+    (wl.Geometry(4, 2, 8, 128, "bf16"), 6000, 3, 1, 1),       # R = 2 KiB, above one round
+    (wl.Geometry(2, 2, 16, 128, "bf16"), 3000, 8, 1, 1),      # R = 4 KiB, 2 KiB pieces
+]
+
+
+@pytest.mark.parametrize("si", range(len(SHORT)))
+def test_gather_short_requests(si):
+    g, nreq, maxlen, sp, dp = SHORT[si]
+    rng = np.random.default_rng(940 + si)
+    lens = np.where(rng.random(nreq) < 0.15, 0, rng.integers(1, maxlen + 1, nreq))
+    lens[-1] = max(int(lens[-1]), 1)
+    assert lens.sum() * g.row_bytes <= (64 << 10) * nreq      # the short-request order
+    run_paged_case(big_case(f"short{si}", g, list(lens), sp, dp, 940 + si, 0.02), 940 + si)
+
+
 @pytest.mark.parametrize("nreq", [1, 2, 63, 64, 65, 130])
 @pytest.mark.parametrize("R", [2048, 512])
 def test_request_lookup_limits(nreq, R):
