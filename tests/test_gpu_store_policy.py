@@ -2,7 +2,8 @@
 KVX_LOG=1 (read once per process, so in a child) every gather, extract and
 rebuild launch reports nontemporal stores by default and cached stores with
 KVX_OUT_CACHED, scatter and gather-scatter always nontemporal; both policies
-write the same bytes."""
+write the same bytes.  A gather takes token-major chunk order exactly when
+its requests average at most 64 KiB of rows per plane."""
 import os
 import subprocess
 import sys
@@ -46,6 +47,26 @@ for (L, H, Db, T, nreq) in [(2, 8, 128, 300, 3), (1, 16, 256, 5000, 70), (1, 3, 
         outs.append((st.clone(), hf.clone(), fl.clone()))
     assert all(torch.equal(a, b) for a, b in zip(*outs))
     assert torch.equal(outs[0][0], outs[0][2])      # extract of rebuild is the staging
+# chunk order of a gather: token-major when its requests average at most
+# 64 KiB of rows per plane, plane-major otherwise
+lay = kvx.Layout(2, 2, 8, 64, "bf16")                        # Q = 4, R = 1 KiB
+A = d(rng.integers(0, 256, (4, 4096, 1024), dtype=np.uint8))
+for nreq, T in ((64, 4096), (63, 4096)):                     # 64 KiB, then just above
+    tok = np.linspace(0, T, nreq + 1).astype(np.int64)
+    st = torch.zeros(4 * T * 1024, dtype=torch.uint8, device=dev)
+    print(f"order case nreq={{nreq}} T={{T}}", file=sys.stderr, flush=True)
+    kvx.gather(lay, kvx.Pool(A, 4096), kvx.Table(d(tok), d(np.arange(T, dtype=np.int32))),
+               kvx.Requests(d(tok), T), st)
+tok = np.array([0, 4096], np.int64)                          # one request: plane-major
+print("order case nreq=1 T=4096", file=sys.stderr, flush=True)
+kvx.gather(lay, kvx.Pool(A, 4096), kvx.Table(d(tok), d(np.arange(4096, dtype=np.int32))),
+           kvx.Requests(d(tok), 4096), torch.zeros(4 * 4096 * 1024, dtype=torch.uint8, device=dev))
+nreq, T = 16, 4096                                           # 256 tokens = 256 KiB: plane-major
+tok = np.linspace(0, T, nreq + 1).astype(np.int64)
+print(f"order case nreq={{nreq}} T={{T}}", file=sys.stderr, flush=True)
+kvx.gather(lay, kvx.Pool(A, 4096), kvx.Table(d(tok), d(np.arange(T, dtype=np.int32))),
+           kvx.Requests(d(tok), T), torch.zeros(4 * T * 1024, dtype=torch.uint8, device=dev))
+torch.cuda.synchronize()
 print("store policy ok", flush=True)
 """
 
@@ -61,10 +82,21 @@ def test_store_policy_reaches_the_kernels():
     for line in p.stderr.splitlines():
         if line.startswith("case "):
             case = line.split("cached=")[1]
-        elif line.startswith("kvx: ") and "stores=" in line:
+        elif line.startswith("order case "):
+            case = None
+        elif case is not None and line.startswith("kvx: ") and "stores=" in line:
             op = line.split()[1]
             policy.setdefault((op, case), set()).add(line.rsplit("stores=", 1)[1].strip())
     for op in ("gather", "rebuild", "extract"):
         assert policy[(op, "False")] == {"nontemporal"}, (op, policy)
         assert policy[(op, "True")] == {"cached"}, (op, policy)
     assert policy[("scatter", "False")] == policy[("scatter", "True")] == {"nontemporal"}
+    order = {}
+    case = None
+    for line in p.stderr.splitlines():
+        if line.startswith("order case "):
+            case = line[len("order case "):]
+        elif case and line.startswith("kvx: gather") and "order=" in line:
+            order[case] = line.split("order=")[1].split()[0]
+    assert order == {"nreq=64 T=4096": "token-major", "nreq=63 T=4096": "plane-major",
+                     "nreq=1 T=4096": "plane-major", "nreq=16 T=4096": "plane-major"}, order
