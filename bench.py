@@ -133,7 +133,7 @@ class Workload:
         self.Q, self.R, self.S = g.planes, g.row_bytes, slots
         self.T = 2048
         if slots == 32768:
-            self.cases = [wl.config2(k) for k in range(NREQ)]
+            self.cases = [wl.kv144k_2048tok_page1(k) for k in range(NREQ)]
         else:
             import numpy as np
             rng = np.random.default_rng(1002 + slots)
@@ -605,7 +605,7 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps, cpu=True):
 
     with torch.cuda.stream(stream):
         # 1: 128 tokens x 28 KiB, page 1, 1024-slot pools (fits in cache)
-        c = wl.config1()
+        c = wl.qwen15b_128tok_page1()
         g = c.geom
         A, B = pool_of(c, c.src, 1), pool_of(c, c.dst, 2)
         st = torch.empty(c.total_tokens * g.token_bytes, dtype=torch.uint8, device=dev)
@@ -631,7 +631,7 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps, cpu=True):
         torch.cuda.empty_cache()
 
         # 2: the bench request, each op alone, rotating 16 disjoint requests
-        cs = [wl.config2(k) for k in range(NREQ)]
+        cs = [wl.kv144k_2048tok_page1(k) for k in range(NREQ)]
         g = cs[0].geom
         A, B = pool_of(cs[0], cs[0].src, 1), pool_of(cs[0], cs[0].dst, 2)
         st = torch.empty(2048 * g.token_bytes, dtype=torch.uint8, device=dev)
@@ -709,7 +709,7 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps, cpu=True):
         torch.cuda.empty_cache()
 
         # 3: 32 fragmented requests, one batched gather
-        c = wl.config3()
+        c = wl.kv144k_32req_fragmented()
         g = c.geom
         A = pool_of(c, c.src, 1)
         st = torch.empty(c.total_tokens * g.token_bytes, dtype=torch.uint8, device=dev)
@@ -731,7 +731,7 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps, cpu=True):
 
         # 4: HF permutes, seq 1024 and 8192 (two buffer sets alternate)
         for seq in (1024, 8192):
-            c = wl.config4(seq)
+            c = wl.qwen7b_permute(seq)
             g = c.geom
             lay = lay_of(g)
             hf = [torch.empty((g.planes, g.kv_heads * seq * g.head_bytes), dtype=torch.uint8,
@@ -825,7 +825,7 @@ def all_configs(torch, kvx, wl, wdev, dev, stream, reps, cpu=True):
         torch.cuda.empty_cache()
 
         # 5: 64 requests, page-16 block pools of 36 GiB, one gather-scatter
-        c = wl.config5()
+        c = wl.kv144k_64req_page16()
         g = c.geom
         A, B = pool_of(c, c.src, 1), pool_of(c, c.dst, 2)
         reqs = kvx.Requests(d(c.tok_off), c.total_tokens)
@@ -1330,7 +1330,7 @@ def comparators(torch, kvx, wl, wdev, dev):
         return calls, e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3
 
     out = {}
-    rnd = wl.config2(3)
+    rnd = wl.kv144k_2048tok_page1(3)
     calls, ms, wall = per_block(rnd, runs=False)
     out["per_block_random"] = {"calls": calls, "ms": round(ms, 2), "wall_ms": round(wall, 2),
                                "GBps": round(wk.op_bytes / (ms * 1e6), 1)}

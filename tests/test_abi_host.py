@@ -303,7 +303,7 @@ def test_check_tables_against_brute_force():
             exp = _brute(side, case.tok_off, as_dst)
             assert got == exp, (seed, as_dst, got, exp)
     # the five workloads' destination tables are valid
-    for case in (wl.config1(), wl.config2(3), wl.config5()):
+    for case in (wl.qwen15b_128tok_page1(), wl.kv144k_2048tok_page1(3), wl.kv144k_64req_page16()):
         assert _check(case.dst, case.tok_off, case.total_tokens) == (0, None)
 
 

@@ -176,7 +176,7 @@ def test_token_offsets_breaking_the_contract(tok_off, total):
 
 def test_workload_tables_are_disjoint():
     # the two-pool workloads, with pools laid out as the bench allocates them
-    for case in (wl.config1(), wl.config2(5), wl.config5()):
+    for case in (wl.qwen15b_128tok_page1(), wl.kv144k_2048tok_page1(5), wl.kv144k_64req_page16()):
         g = case.geom
         Q, R = g.planes, g.row_bytes
         span = case.src.num_slots * R
@@ -186,7 +186,7 @@ def test_workload_tables_are_disjoint():
         st, bad = call(g, case.tok_off, a, a)     # the same table read and written: every row
         assert st == E_OVERLAP and 0 <= bad < case.total_tokens
     # the fragmented batch gathered into a staging buffer after its pool
-    case = wl.config3()
+    case = wl.kv144k_32req_fragmented()
     g = case.geom
     span = case.src.num_slots * g.row_bytes
     a = Side(case.src, planes(g.planes, BASE, span), g.row_bytes)
@@ -221,7 +221,7 @@ def test_arguments():
 
 def test_python_binding():
     import torch
-    case = wl.config1()
+    case = wl.qwen15b_128tok_page1()
     g = case.geom
     lay = kvx.Layout(g.num_layers, g.num_kv, g.kv_heads, g.head_dim, g.dtype)
     a = torch.empty((g.planes, case.src.num_slots * g.row_bytes), dtype=torch.uint8)

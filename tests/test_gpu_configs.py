@@ -43,8 +43,8 @@ def check_fill_sample(pool_d, seed, rng, nrows=64):
         assert_bytes_equal(got, wl.hash_rows_host(seed, int(q), slots, R, S), "fill sample")
 
 
-def test_config1_gather_then_scatter():
-    case = wl.config1()
+def test_qwen15b_128tok_gather_then_scatter():
+    case = wl.qwen15b_128tok_page1()
     g = case.geom
     Q, R, S = g.planes, g.row_bytes, case.src.num_slots
     shape = (Q, S, g.kv_heads, g.head_dim)
@@ -53,9 +53,9 @@ def test_config1_gather_then_scatter():
     lay, reqs = layout_of(g), requests(case)
     src_d, dst_d = d(src_h), d(dst_h)
     staging = torch.zeros(case.total_tokens * Q * R, dtype=torch.uint8, device=DEV)
-    say("config1 gather")
+    say("qwen15b_128tok_page1 gather")
     kvx.gather(lay, kvx.Pool(src_d, S), table(case.src), reqs, staging)
-    say("config1 scatter")
+    say("qwen15b_128tok_page1 scatter")
     kvx.scatter(lay, staging, reqs, kvx.Pool(dst_d, S), table(case.dst))
     torch.cuda.synchronize()
     exp_st = np.zeros(case.total_tokens * Q * R, np.uint8)
@@ -63,16 +63,16 @@ def test_config1_gather_then_scatter():
     exp_dst = dst_h.copy()
     oracle_scatter(case, exp_st, exp_dst)
     assert exp_st.nbytes == oracle.kv_bytes(128, 28, 2, 128, 2) == int(3.5 * 2 ** 20)
-    assert_bytes_equal(staging.cpu().numpy(), exp_st, "config1 staging")
-    assert_bytes_equal(dst_d.cpu().numpy(), exp_dst, "config1 destination pool")
+    assert_bytes_equal(staging.cpu().numpy(), exp_st, "qwen15b_128tok_page1 staging")
+    assert_bytes_equal(dst_d.cpu().numpy(), exp_dst, "qwen15b_128tok_page1 destination pool")
 
 
-def test_config2_all_three_paged_ops():
-    case = wl.config2(0)
+def test_kv144k_2048tok_all_three_paged_ops():
+    case = wl.kv144k_2048tok_page1(0)
     g = case.geom
     Q, R, S = g.planes, g.row_bytes, case.src.num_slots
     rng = np.random.default_rng(2)
-    say("config2 fill")
+    say("kv144k_2048tok_page1 fill")
     a_d = hash_pool(Q, S, R, case.value_seed)
     b_d = hash_pool(Q, S, R, case.sentinel_seed)
     c_d = hash_pool(Q, S, R, case.sentinel_seed)
@@ -83,38 +83,38 @@ def test_config2_all_three_paged_ops():
     st, dt = table(case.src), table(case.dst)
     staging = torch.zeros(case.total_tokens * Q * R, dtype=torch.uint8, device=DEV)
     skipped = torch.zeros(3, dtype=torch.int64, device=DEV)
-    say("config2 gather_scatter")
+    say("kv144k_2048tok_page1 gather_scatter")
     kvx.gather_scatter(lay, kvx.Pool(a_d, S), st, reqs, kvx.Pool(b_d, S), dt, skipped[0:1])
-    say("config2 gather")
+    say("kv144k_2048tok_page1 gather")
     kvx.gather(lay, kvx.Pool(a_d, S), st, reqs, staging, skipped[1:2])
-    say("config2 scatter")
+    say("kv144k_2048tok_page1 scatter")
     kvx.scatter(lay, staging, reqs, kvx.Pool(c_d, S), dt, skipped[2:3])
     torch.cuda.synchronize()
     assert skipped.cpu().tolist() == [0, 0, 0]
     a_h = a_d.cpu().numpy()
     exp_st = np.zeros(staging.numel(), np.uint8)
     oracle_gather(case, a_h, exp_st, NT)
-    assert_bytes_equal(staging.cpu().numpy(), exp_st, "config2 gather")
+    assert_bytes_equal(staging.cpu().numpy(), exp_st, "kv144k_2048tok_page1 gather")
     exp_b = b_before.copy()
     exp_c = b_before
     oracle_gather_scatter(case, a_h, exp_b, NT)
-    assert_bytes_equal(b_d.cpu().numpy(), exp_b, "config2 gather_scatter")
+    assert_bytes_equal(b_d.cpu().numpy(), exp_b, "kv144k_2048tok_page1 gather_scatter")
     del exp_b
     oracle_scatter(case, exp_st, exp_c, NT)
-    assert_bytes_equal(c_d.cpu().numpy(), exp_c, "config2 scatter")
+    assert_bytes_equal(c_d.cpu().numpy(), exp_c, "kv144k_2048tok_page1 scatter")
 
 
-def test_config2_token_major_pools():
+def test_kv144k_2048tok_token_major_pools():
     """The 2048-token request with token-major pools (plane q of slot s at
     (s * Q + q) * R, so the rows of a slot in all planes are one 144 KiB run),
     where the paged kernels take token-major chunk order: gather-scatter
     between two such pools, gather, scatter back at another slot set, and
     gather-scatter into a layer-major pool; every destination byte against
     the oracle."""
-    case, case2 = wl.config2(1), wl.config2(2)
+    case, case2 = wl.kv144k_2048tok_page1(1), wl.kv144k_2048tok_page1(2)
     g = case.geom
     Q, R, S = g.planes, g.row_bytes, case.src.num_slots
-    say("config2 token-major fill")
+    say("kv144k_2048tok_page1 token-major fill")
     a_d = torch.empty((S, Q, R), dtype=torch.uint8, device=DEV)
     b_d = torch.empty((S, Q, R), dtype=torch.uint8, device=DEV)
     c_d = hash_pool(Q, S, R, case.sentinel_seed + 1)
@@ -134,13 +134,13 @@ def test_config2_token_major_pools():
     st, dt, dt2 = table(case.src), table(case.dst), table(case2.dst)
     staging = torch.zeros(case.total_tokens * Q * R, dtype=torch.uint8, device=DEV)
     skipped = torch.zeros(4, dtype=torch.int64, device=DEV)
-    say("config2 token-major gather_scatter")
+    say("kv144k_2048tok_page1 token-major gather_scatter")
     kvx.gather_scatter(lay, tm_pool(a_d), st, reqs, tm_pool(b_d), dt, skipped[0:1])
-    say("config2 token-major gather")
+    say("kv144k_2048tok_page1 token-major gather")
     kvx.gather(lay, tm_pool(a_d), st, reqs, staging, skipped[1:2])
-    say("config2 token-major scatter")
+    say("kv144k_2048tok_page1 token-major scatter")
     kvx.scatter(lay, staging, reqs, tm_pool(b_d), dt2, skipped[2:3])
-    say("config2 token-major -> layer-major gather_scatter")
+    say("kv144k_2048tok_page1 token-major -> layer-major gather_scatter")
     kvx.gather_scatter(lay, tm_pool(a_d), st, reqs, kvx.Pool(c_d, S), dt, skipped[3:4])
     torch.cuda.synchronize()
     assert skipped.cpu().tolist() == [0, 0, 0, 0]
@@ -165,11 +165,11 @@ def test_config2_token_major_pools():
     assert_bytes_equal(c_d.cpu().numpy(), exp_c, "token-major -> layer-major gather_scatter")
 
 
-def test_config3_batched_gather():
-    case = wl.config3()
+def test_kv144k_32req_fragmented_gather():
+    case = wl.kv144k_32req_fragmented()
     g = case.geom
     Q, R, S = g.planes, g.row_bytes, case.src.num_slots
-    say("config3 fill", f"pool {Q * S * R / 2**30:.1f} GiB")
+    say("kv144k_32req_fragmented fill", f"pool {Q * S * R / 2**30:.1f} GiB")
     a_d = hash_pool(Q, S, R, case.value_seed)
     check_fill_sample(a_d, case.value_seed, np.random.default_rng(3))
     n = case.total_tokens * Q * R
@@ -177,19 +177,19 @@ def test_config3_batched_gather():
     staging = torch.empty(n + guard, dtype=torch.uint8, device=DEV)
     wdev.fill_hash(staging, case.sentinel_seed)
     exp = staging.cpu().numpy()
-    say("config3 gather", f"{case.num_reqs} requests, {case.total_tokens} tokens")
+    say("kv144k_32req_fragmented gather", f"{case.num_reqs} requests, {case.total_tokens} tokens")
     kvx.gather(layout_of(g), kvx.Pool(a_d, S), table(case.src), requests(case), staging)
     torch.cuda.synchronize()
     a_h = a_d.cpu().numpy()
     del a_d
     oracle_gather(case, a_h, exp, NT)
     del a_h
-    assert_bytes_equal(staging.cpu().numpy(), exp, "config3 staging")
+    assert_bytes_equal(staging.cpu().numpy(), exp, "kv144k_32req_fragmented staging")
 
 
 @pytest.mark.parametrize("seq", [1024, 8192])
-def test_config4_extract_rebuild(seq):
-    case = wl.config4(seq)
+def test_qwen7b_extract_rebuild(seq):
+    case = wl.qwen7b_permute(seq)
     g = case.geom
     Q, H, Dm = g.planes, g.kv_heads, g.head_dim
     Db = g.head_bytes
@@ -198,9 +198,9 @@ def test_config4_extract_rebuild(seq):
     tgt_h = wl.normal_f16(case.sentinel_seed, (Q, 1, H, seq, Dm))
     hf_d, tgt_d = d(hf_h), d(tgt_h)
     out_d = torch.empty((Q, seq, H, Dm), dtype=torch.float16, device=DEV)
-    say(f"config4 seq={seq} extract")
+    say(f"qwen7b_permute seq={seq} extract")
     kvx.extract_permute(lay, hf_d, seq, seq, out_d)
-    say(f"config4 seq={seq} rebuild")
+    say(f"qwen7b_permute seq={seq} rebuild")
     kvx.rebuild_permute(lay, out_d, seq, tgt_d, seq)
     torch.cuda.synchronize()
     hf_b = hf_h.view(np.uint8).reshape(Q, -1)
@@ -215,18 +215,18 @@ def test_config4_extract_rebuild(seq):
     assert_bytes_equal(got_tgt.view(np.uint8), hf_h.view(np.uint8), "round trip")
 
 
-def test_config5_block_pools():
-    case = wl.config5()
+def test_kv144k_64req_page16_block_pools():
+    case = wl.kv144k_64req_page16()
     g = case.geom
     Q, R = g.planes, g.row_bytes
     S = case.src.num_slots
     plane_bytes = S * R
-    say("config5 fill", f"2 x {Q * plane_bytes / 2**30:.0f} GiB")
+    say("kv144k_64req_page16 fill", f"2 x {Q * plane_bytes / 2**30:.0f} GiB")
     a_d = hash_pool(Q, S, R, case.value_seed)
     b_d = hash_pool(Q, S, R, case.sentinel_seed)
     check_fill_sample(a_d, case.value_seed, np.random.default_rng(5))
     skipped = torch.zeros(1, dtype=torch.int64, device=DEV)
-    say("config5 gather_scatter", f"{case.num_reqs} requests, {case.total_tokens} tokens")
+    say("kv144k_64req_page16 gather_scatter", f"{case.num_reqs} requests, {case.total_tokens} tokens")
     kvx.gather_scatter(layout_of(g), kvx.Pool(a_d, case.src.num_pages, 16), table(case.src),
                        requests(case), kvx.Pool(b_d, case.dst.num_pages, 16), table(case.dst),
                        skipped)
@@ -250,7 +250,7 @@ def test_config5_block_pools():
 
     # every plane, on the device: written rows equal their source rows, all
     # other rows equal the regenerated prefill
-    say("config5 device-side checks")
+    say("kv144k_64req_page16 device-side checks")
     for q in range(Q):
         wdev.fill_hash(scratch, case.sentinel_seed, ctr0=q * plane_bytes // 8)
         assert torch.equal(b_d[q].index_select(0, dst_idx), a_d[q].index_select(0, src_idx)), q
@@ -259,7 +259,7 @@ def test_config5_block_pools():
     # every plane with the oracle, one plane at a time: host copies of the
     # source plane and of the regenerated prefill, the oracle's gather-scatter
     # into the latter, and the whole destination plane compared
-    say(f"config5 oracle on all {Q} planes")
+    say(f"kv144k_64req_page16 oracle on all {Q} planes")
     pin_src = torch.empty((S, R), dtype=torch.uint8, pin_memory=True)
     pin_exp = torch.empty((S, R), dtype=torch.uint8, pin_memory=True)
     pin_got = torch.empty((S, R), dtype=torch.uint8, pin_memory=True)
@@ -272,7 +272,7 @@ def test_config5_block_pools():
         pin_got.copy_(b_d[q])
         exp = pin_exp.numpy().reshape(1, S, R)
         assert oracle_gather_scatter(one, pin_src.numpy().reshape(1, S, R), exp, NT) == 0
-        assert_bytes_equal(pin_got.numpy(), exp[0], f"config5 plane {q}")
+        assert_bytes_equal(pin_got.numpy(), exp[0], f"kv144k_64req_page16 plane {q}")
 
 
 @pytest.mark.parametrize("page", [1, 16])

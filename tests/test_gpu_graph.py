@@ -86,7 +86,7 @@ def test_graph_replays_full_size_request():
     """The 2048-token, 144 KiB/token request (the one-row-per-wave launches):
     gather-scatter, gather, extract and rebuild captured once and replayed on
     four disjoint requests; every replay's bytes equal the eager calls'."""
-    cs = [wl.config2(k) for k in range(4)]
+    cs = [wl.kv144k_2048tok_page1(k) for k in range(4)]
     g = cs[0].geom
     Q, R, T = g.planes, g.row_bytes, 2048
     from workloads import device as wdev

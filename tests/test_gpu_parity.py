@@ -518,7 +518,7 @@ def test_token_major_pools_and_mixed_strides():
 
 PERMS = [
     # (Q, H, D, dtype, s_cap, seq)
-    (4, 4, 128, "f16", 300, 300),     # head rows of 256 B (config-4 shape)
+    (4, 4, 128, "f16", 300, 300),     # head rows of 256 B (the Qwen2.5-7B permute shape)
     (3, 4, 128, "f16", 300, 173),     # s_cap > seq: rebuild leaves s >= seq alone
     (2, 1, 128, "bf16", 100, 100),    # H = 1: a plain copy
     (2, 8, 64, "bf16", 64, 1),        # seq = 1

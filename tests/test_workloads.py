@@ -23,24 +23,24 @@ def test_hash_rows_match_dense_fill():
         assert np.array_equal(wl.hash_rows_host(99, q, slots, R, S), dense[q, slots])
 
 
-def test_configs_deterministic():
-    for make in (wl.config1, wl.config2, wl.config5):
+def test_workloads_deterministic():
+    for make in (wl.qwen15b_128tok_page1, wl.kv144k_2048tok_page1, wl.kv144k_64req_page16):
         assert make().table_sha256() == make().table_sha256()
-    assert wl.config2(0).table_sha256() != wl.config2(1).table_sha256()
+    assert wl.kv144k_2048tok_page1(0).table_sha256() != wl.kv144k_2048tok_page1(1).table_sha256()
 
 
-def test_config1_shape():
-    c = wl.config1()
+def test_qwen15b_128tok_shape():
+    c = wl.qwen15b_128tok_page1()
     assert c.geom.row_bytes == 512 and c.geom.token_bytes == 28 * 1024
     assert c.total_tokens == 128 and c.src.num_slots == 1024 == c.dst.num_slots
     assert len(set(c.src.ids)) == 128 and len(set(c.dst.ids)) == 128
     assert c.payload_bytes() == 3670016
 
 
-def test_config2_rotation_disjoint():
+def test_kv144k_2048tok_rotation_disjoint():
     seen_s, seen_d = set(), set()
     for k in range(16):
-        c = wl.config2(k)
+        c = wl.kv144k_2048tok_page1(k)
         assert c.payload_bytes() == 288 * 2 ** 20
         s, d = set(c.src.ids.tolist()), set(c.dst.ids.tolist())
         assert len(s) == len(d) == 2048
@@ -50,8 +50,8 @@ def test_config2_rotation_disjoint():
     assert seen_s == set(range(32768))
 
 
-def test_config3_fragmented():
-    c = wl.config3()
+def test_kv144k_32req_fragmented_pool():
+    c = wl.kv144k_32req_fragmented()
     assert c.num_reqs == 32
     assert (c.lengths >= 1024).all() and (c.lengths <= 2048).all()
     ids = c.src.ids.astype(np.int64)
@@ -68,8 +68,8 @@ def test_churn_is_a_permutation():
     assert np.array_equal(np.sort(free), np.arange(4096))
 
 
-def test_config5_blocks():
-    c = wl.config5()
+def test_kv144k_64req_page16_blocks():
+    c = wl.kv144k_64req_page16()
     assert c.num_reqs == 64 and c.src.page_size == 16 and c.src.num_pages == 16384
     assert (np.diff(c.src.pg_off) == 128).all() and (np.diff(c.dst.pg_off) == 128).all()
     tails = c.lengths - 127 * 16
@@ -89,6 +89,6 @@ def test_random_case_destinations_distinct(seed):
         assert (pages * side.page_size >= c.lengths).all()
 
 
-def test_config4_sizes():
-    assert wl.config4(1024).payload_bytes() == 56 * 2 ** 20
-    assert wl.config4(8192).payload_bytes() == 448 * 2 ** 20
+def test_qwen7b_permute_sizes():
+    assert wl.qwen7b_permute(1024).payload_bytes() == 56 * 2 ** 20
+    assert wl.qwen7b_permute(8192).payload_bytes() == 448 * 2 ** 20

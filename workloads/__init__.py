@@ -196,7 +196,7 @@ KV144K = Geometry(36, 2, 8, 128, "bf16")      # 144 KiB per token, 2 KiB rows
 QWEN7B = Geometry(28, 2, 4, 128, "f16")       # 56 KiB per token
 
 
-def config1() -> PagedCase:
+def qwen15b_128tok_page1() -> PagedCase:
     """Qwen2.5-1.5B-shaped KV (fp16, 28 layers x {K,V} x 2 heads x 128): one
     128-token request whose slots are a seeded random 128-subset of a 1024-slot
     token-paged pool; the scatter target is an independent 128-subset of a
@@ -209,7 +209,7 @@ def config1() -> PagedCase:
                      value_seed=2001, sentinel_seed=3001, table_seed=1001, values="uniform_f16")
 
 
-def config2(request: int = 0, num_requests_in_pool: int = 16) -> PagedCase:
+def kv144k_2048tok_page1(request: int = 0, num_requests_in_pool: int = 16) -> PagedCase:
     """One 2048-token request at 144 KiB/token (36 layers x {K,V} x 8 heads x
     128, bf16, 288 MiB): source slots are a slice of a seeded permutation of a
     32768-slot token-paged pool, destination slots a slice of an independent
@@ -267,7 +267,7 @@ def churned_free_list(rng: np.random.Generator, num_slots: int, cycles: int = 10
     return take(count)
 
 
-def config3(num_slots: int = 131072, num_reqs: int = 32) -> PagedCase:
+def kv144k_32req_fragmented(num_slots: int = 131072, num_reqs: int = 32) -> PagedCase:
     """Fragmented layer-major pool (one [slots, 8, 128] bf16 tensor per layer
     per K/V, 36 layers, 2 KiB rows): 32 requests with lengths U{1024..2048},
     slots allocated in order from a free list shuffled by 10k seeded
@@ -298,7 +298,7 @@ class PermuteCase:
         return self.geom.planes * self.seq * self.geom.row_bytes
 
 
-def config4(seq: int = 1024) -> PermuteCase:
+def qwen7b_permute(seq: int = 1024) -> PermuteCase:
     """Qwen2.5-7B shape (28 layers x {K,V}, 4 heads, 128, fp16): HF layout
     [1, heads, seq, dim] <-> [seq, heads, dim], seq in {1024, 8192}, values
     normal(0, 1) rounded to fp16."""
@@ -308,7 +308,7 @@ def config4(seq: int = 1024) -> PermuteCase:
                        value_seed=2004 + seq, sentinel_seed=3004 + seq)
 
 
-def config5(num_reqs: int = 64, num_blocks: int = 16384, page_size: int = 16) -> PagedCase:
+def kv144k_64req_page16(num_reqs: int = 64, num_blocks: int = 16384, page_size: int = 16) -> PagedCase:
     """vLLM-style block pools, page 16, bf16, 144 KiB/token, 16384 blocks of 16
     tokens (262144 token slots, 36 GiB) per pool: 64 requests of 2032 + f
     tokens, f ~ U{1..16} (so 128 pages each, the last partly filled); block
