@@ -65,6 +65,13 @@ namespace kvx {
 #ifndef KVX_LOAD_NT
 #define KVX_LOAD_NT 1              // nontemporal loads
 #endif
+// Scatter of wide rows: issue the staging rows' loads before the destination
+// page table is read.  Measured (same process, alternating; 49152 tokens at
+// 144 KiB/token, 2 KiB rows): one request 5472 -> 5517 GB/s, 16 requests
+// 5304 -> 5539, 256 requests 5126 -> 5301, 1024 and more within 1%.
+#ifndef KVX_SCATTER_EARLY
+#define KVX_SCATTER_EARLY 1
+#endif
 #ifndef KVX_XCD_REMAP
 #define KVX_XCD_REMAP 2            // XCD-aware workgroup renumbering: 0 never,
 #endif                             // 1 always, 2 by the host's pool-size rules
@@ -466,6 +473,38 @@ __device__ __forceinline__ int resolve(const PagedArgs<Src, Dst>& a, const Paged
     return ok ? kCopy : kSkip;
 }
 
+// A scatter's staging half of resolve: the lane's request and its staging
+// row, which need no page-table read, so that the row's loads can be issued
+// before the destination's page table is read.  code: kCopy (pending the
+// destination), kSkip or kNone.
+struct StageRow {
+    int64_t off, n_r, t, pg_dst;
+    int code;
+};
+
+template <bool MANY, class Dst>
+__device__ __forceinline__ StageRow resolve_stage_row(const PagedArgs<StageRef, Dst>& a,
+                                                      const PagedChunk& k, uint32_t u,
+                                                      uint64_t& s) {
+    const Common& c = a.c;
+    const int64_t tok = k.tok0 + u;
+    const bool active = u < c.U && tok < c.T;
+    const ReqOf q = request_lookup<MANY>(c, nullptr, pg_off_of(a.dst), k.tok0, tok, active,
+                                         static_cast<int>(u));
+    s = SideAddr<StageRef>::base(a.src, k.ql);
+    StageRow r{0, 0, 0, 0, kNone};
+    if (!active) return r;
+    r.code = kSkip;
+    if (q.off < 0 || tok < q.off || tok >= q.end || q.end > c.T) return r;
+    r.off = q.off;
+    r.n_r = q.end - q.off;
+    r.t = tok - q.off;
+    r.pg_dst = q.pg_dst;
+    s = stage_addr(a.src, c, k.ql, r.off, r.n_r, r.t);
+    r.code = kCopy;
+    return r;
+}
+
 // ------------------------------------------------- head-sliced resolver --
 
 // One side of a head-sliced copy: heads per token row, slice start, layout.
@@ -736,6 +775,34 @@ void k_paged(PagedArgs<Src, Dst> a) {
     unsigned long long nskip = 0;
     for (uint32_t chunk = wave_id<kPagedWaves>(a.c); chunk < a.c.nchunks; chunk += nwaves) {
         const PagedChunk k = paged_chunk(a.c, chunk);
+        if constexpr (KVX_SCATTER_EARLY != 0 && std::is_same<Src, StageRef>::value && VPL > 0) {
+            // scatter of whole 1..16 KiB rows: the staging rows' loads go out
+            // before the destination page table is read, so their latency
+            // overlaps the table reads
+            uint64_t s = 0, d = 0;
+            StageRow r = resolve_stage_row<MANY>(a, k, static_cast<uint32_t>(lane), s);
+            v4u x[U][VPL];
+            const uint32_t off = static_cast<uint32_t>(lane) * 16u;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint64_t su = readlane64(s, u);
+#pragma unroll
+                for (int v = 0; v < VPL; ++v) x[u][v] = load_nt(su, off + v * 1024);
+            }
+            if (r.code == kCopy &&
+                !SideAddr<Dst>::get(a.dst, a.c, k.ql, r.pg_dst, r.off, r.n_r, r.t, d))
+                r.code = kSkip;
+            nskip += __popcll(__ballot(r.code == kSkip));
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (__builtin_amdgcn_readlane(r.code, u) == kCopy) {
+                    const uint64_t du = readlane64(d, u);
+#pragma unroll
+                    for (int v = 0; v < VPL; ++v) store_v<NTS>(du, off + v * 1024, x[u][v]);
+                }
+            }
+            continue;
+        }
         uint64_t s = 0, d = 0;
         const int code = resolve<MANY>(a, k, static_cast<uint32_t>(lane), s, d);
         nskip += __popcll(__ballot(code == kSkip));
