@@ -392,11 +392,20 @@ __device__ __forceinline__ ReqOf request_lookup(const Common& c, const int64_t* 
     }
 }
 
-// Address of token t of a request whose page list starts at pg_off_r, in
-// plane ql of a pool; false when any index is out of range (the row is then
-// skipped, never dereferenced).
-__device__ __forceinline__ bool pool_addr(const PoolRef& p, int32_t ql, int64_t pg_off_r,
-                                          int64_t t, uint64_t& addr) {
+// The address of a row, in two steps so that a call's page-id reads on both
+// sides are issued before either is used: look() finds token t's page-table
+// entry and reads it (a pool), or the staging address; done() checks the
+// page and forms the row address, false when an index is out of range (the
+// row is then skipped, never dereferenced).
+struct SideLook {
+    int64_t row;        // pool: row within the page
+    uint64_t addr;      // staging: the row address
+    int32_t page;       // pool: the page id read (-1: its index was out of range);
+                        // kept 32-bit so nothing uses the read before done()
+};
+
+// Token t of a request whose page list starts at pg_off_r, in a pool.
+__device__ __forceinline__ SideLook pool_look(const PoolRef& p, int64_t pg_off_r, int64_t t) {
     int64_t pidx, row;
     const int shift = page_shift_of(p.page_size);
     if (shift >= 0) {
@@ -406,12 +415,21 @@ __device__ __forceinline__ bool pool_addr(const PoolRef& p, int32_t ql, int64_t 
         pidx = t / p.page_size;
         row = t - pidx * p.page_size;
     }
-    int64_t idx = pg_off_r + pidx;
-    if (idx < 0 || idx >= p.num_ids) return false;
-    int64_t page = p.ids[idx];
+    const int64_t idx = pg_off_r + pidx;
+    SideLook l;
+    l.row = row;
+    l.addr = 0;
+    l.page = -1;
+    if (idx >= 0 && idx < p.num_ids) l.page = p.ids[idx];
+    return l;
+}
+
+__device__ __forceinline__ bool pool_done(const PoolRef& p, int32_t ql, const SideLook& l,
+                                          uint64_t& addr) {
+    const int64_t page = l.page;
     if (page < 0 || page >= p.num_pages) return false;
     addr = reinterpret_cast<uint64_t>(p.plane[ql]) +
-           static_cast<uint64_t>(page * p.page_rows + row) * static_cast<uint64_t>(p.stride);
+           static_cast<uint64_t>(page * p.page_rows + l.row) * static_cast<uint64_t>(p.stride);
     return true;
 }
 
@@ -427,9 +445,12 @@ struct SideAddr;
 
 template <>
 struct SideAddr<PoolRef> {
-    __device__ static bool get(const PoolRef& p, const Common&, int32_t ql, int64_t pg_off_r,
-                               int64_t, int64_t, int64_t t, uint64_t& a) {
-        return pool_addr(p, ql, pg_off_r, t, a);
+    __device__ static SideLook look(const PoolRef& p, const Common&, int32_t, int64_t pg_off_r,
+                                    int64_t, int64_t, int64_t t) {
+        return pool_look(p, pg_off_r, t);
+    }
+    __device__ static bool done(const PoolRef& p, int32_t ql, const SideLook& l, uint64_t& a) {
+        return pool_done(p, ql, l, a);
     }
     // An address that is always safe to read: the plane's first slot.
     __device__ static uint64_t base(const PoolRef& p, int32_t ql) {
@@ -439,9 +460,16 @@ struct SideAddr<PoolRef> {
 
 template <>
 struct SideAddr<StageRef> {
-    __device__ static bool get(const StageRef& s, const Common& c, int32_t ql, int64_t,
-                               int64_t off_r, int64_t n_r, int64_t t, uint64_t& a) {
-        a = stage_addr(s, c, ql, off_r, n_r, t);
+    __device__ static SideLook look(const StageRef& s, const Common& c, int32_t ql, int64_t,
+                                    int64_t off_r, int64_t n_r, int64_t t) {
+        SideLook l;
+        l.row = 0;
+        l.addr = stage_addr(s, c, ql, off_r, n_r, t);
+        l.page = 0;
+        return l;
+    }
+    __device__ static bool done(const StageRef&, int32_t, const SideLook& l, uint64_t& a) {
+        a = l.addr;
         return true;
     }
     __device__ static uint64_t base(const StageRef& s, int32_t) {
@@ -466,9 +494,12 @@ __device__ __forceinline__ int resolve(const PagedArgs<Src, Dst>& a, const Paged
     if (q.off < 0 || tok < q.off || tok >= q.end || q.end > c.T) return kSkip;
     const int64_t t = tok - q.off;
     const int64_t n_r = q.end - q.off;
+    // both sides' page-id reads go out before either is waited for
+    const SideLook ls = SideAddr<Src>::look(a.src, c, k.ql, q.pg_src, q.off, n_r, t);
+    const SideLook ld = SideAddr<Dst>::look(a.dst, c, k.ql, q.pg_dst, q.off, n_r, t);
     uint64_t sa = 0;
-    bool ok = SideAddr<Src>::get(a.src, c, k.ql, q.pg_src, q.off, n_r, t, sa);
-    ok = SideAddr<Dst>::get(a.dst, c, k.ql, q.pg_dst, q.off, n_r, t, d) && ok;
+    bool ok = SideAddr<Src>::done(a.src, k.ql, ls, sa);
+    ok = SideAddr<Dst>::done(a.dst, k.ql, ld, d) && ok;
     if (ok) s = sa;
     return ok ? kCopy : kSkip;
 }
@@ -525,33 +556,23 @@ struct HeadArgs {
     int32_t head_major;         // unit order within a chunk
 };
 
-// Address of head h of token t (page list of its request at pg_off_r) in
-// plane ql of a pool laid out in NHD or HND blocks; false when an index is
-// out of range.
-__device__ __forceinline__ bool head_addr(const PoolRef& p, int32_t ql, int64_t pg_off_r,
-                                          int64_t t, int64_t h, bool hnd, uint64_t Db,
-                                          uint64_t& addr) {
-    int64_t pidx, row;
-    const int shift = page_shift_of(p.page_size);
-    if (shift >= 0) {
-        pidx = t >> shift;
-        row = t & ((int64_t(1) << shift) - 1);
-    } else {
-        pidx = t / p.page_size;
-        row = t - pidx * p.page_size;
-    }
-    int64_t idx = pg_off_r + pidx;
-    if (idx < 0 || idx >= p.num_ids) return false;
-    int64_t page = p.ids[idx];
+// Address of head h of a token whose page entry pool_look() read, in plane
+// ql of a pool laid out in NHD or HND blocks; false when an index is out of
+// range.  (Both sides' pool_look() come first, so their page-id reads are in
+// flight together.)
+__device__ __forceinline__ bool head_done(const PoolRef& p, int32_t ql, const SideLook& l,
+                                          int64_t h, bool hnd, uint64_t Db, uint64_t& addr) {
+    const int64_t page = l.page;
     if (page < 0 || page >= p.num_pages) return false;
     const uint64_t base = reinterpret_cast<uint64_t>(p.plane[ql]);
     const uint64_t B = static_cast<uint64_t>(p.page_size);
     const uint64_t stride = static_cast<uint64_t>(p.stride);
+    const uint64_t row = static_cast<uint64_t>(l.row);
     if (hnd)
         addr = base + static_cast<uint64_t>(page) * B * stride +
-               (static_cast<uint64_t>(h) * B + static_cast<uint64_t>(row)) * Db;
+               (static_cast<uint64_t>(h) * B + row) * Db;
     else
-        addr = base + (static_cast<uint64_t>(page) * B + static_cast<uint64_t>(row)) * stride +
+        addr = base + (static_cast<uint64_t>(page) * B + row) * stride +
                static_cast<uint64_t>(h) * Db;
     return true;
 }
@@ -588,10 +609,10 @@ __device__ __forceinline__ int resolve_heads(const HeadArgs& a, uint32_t chunk, 
     const int64_t t = tok - q.off;
     const int64_t j = j0 + static_cast<int64_t>(jl);
     const uint64_t Db = static_cast<uint64_t>(c.R);
-    bool ok = head_addr(a.src, static_cast<int32_t>(ql), q.pg_src, t, a.hs.h0 + j, a.hs.hnd != 0,
-                        Db, s);
-    ok = head_addr(a.dst, static_cast<int32_t>(ql), q.pg_dst, t, a.hd.h0 + j, a.hd.hnd != 0, Db,
-                   d) && ok;
+    const SideLook ls = pool_look(a.src, q.pg_src, t);
+    const SideLook ld = pool_look(a.dst, q.pg_dst, t);
+    bool ok = head_done(a.src, static_cast<int32_t>(ql), ls, a.hs.h0 + j, a.hs.hnd != 0, Db, s);
+    ok = head_done(a.dst, static_cast<int32_t>(ql), ld, a.hd.h0 + j, a.hd.hnd != 0, Db, d) && ok;
     return ok ? kCopy : kSkip;
 }
 
@@ -789,9 +810,11 @@ void k_paged(PagedArgs<Src, Dst> a) {
 #pragma unroll
                 for (int v = 0; v < VPL; ++v) x[u][v] = load_nt(su, off + v * 1024);
             }
-            if (r.code == kCopy &&
-                !SideAddr<Dst>::get(a.dst, a.c, k.ql, r.pg_dst, r.off, r.n_r, r.t, d))
-                r.code = kSkip;
+            if (r.code == kCopy) {
+                const SideLook ld =
+                    SideAddr<Dst>::look(a.dst, a.c, k.ql, r.pg_dst, r.off, r.n_r, r.t);
+                if (!SideAddr<Dst>::done(a.dst, k.ql, ld, d)) r.code = kSkip;
+            }
             nskip += __popcll(__ballot(r.code == kSkip));
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -906,8 +929,11 @@ __global__ __launch_bounds__(kWave * kPagedWaves) void k_heads_hnd(HeadArgs a) {
                 const int64_t t = tok - q.off;
                 uint64_t s0 = 0, d0 = 0;
                 // head 0 of the token: page base + row * Db
-                if (head_addr(a.src, static_cast<int32_t>(ql), q.pg_src, t, 0, true, Db, s0) &&
-                    head_addr(a.dst, static_cast<int32_t>(ql), q.pg_dst, t, 0, true, Db, d0)) {
+                const SideLook ls = pool_look(a.src, q.pg_src, t);
+                const SideLook ld = pool_look(a.dst, q.pg_dst, t);
+                const bool oks = head_done(a.src, static_cast<int32_t>(ql), ls, 0, true, Db, s0);
+                const bool okd = head_done(a.dst, static_cast<int32_t>(ql), ld, 0, true, Db, d0);
+                if (oks && okd) {
                     code = kCopy;
                     sb = s0;
                     db = d0;
