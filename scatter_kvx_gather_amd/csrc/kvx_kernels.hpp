@@ -65,7 +65,7 @@ namespace kvx {
 #ifndef KVX_LOAD_NT
 #define KVX_LOAD_NT 1              // nontemporal loads
 #endif
-// Scatter of wide rows: issue the staging rows' loads before the destination
+// Scatter (wide and row-loop copies): issue the staging rows' loads before the destination
 // page table is read.  Measured (same process, alternating; 49152 tokens at
 // 144 KiB/token, 2 KiB rows): one request 5472 -> 5517 GB/s, 16 requests
 // 5304 -> 5539, 256 requests 5126 -> 5301, 1024 and more within 1%.
@@ -656,61 +656,113 @@ __device__ __forceinline__ int resolve_perm(const PermuteArgs& a, const PermChun
 // Rows of VPL KiB, U rows per chunk; row addresses broadcast to SGPRs.  Every
 // row's source is loaded (rows that are not copied point at a safe address),
 // so the loads are straight-line code; only the stores test the status.
-template <int VPL, int U, bool NTS>
-__device__ __forceinline__ void copy_wide(uint64_t s_l, uint64_t d_l, int code_l, int lane) {
+// Loads and stores are separate steps, so a caller can resolve the
+// destination between them.
+template <int VPL, int U>
+struct WideRows {
     v4u x[U][VPL];
-    const uint32_t off = static_cast<uint32_t>(lane) * 16u;
+    WideRows() = default;
+    __device__ __forceinline__ WideRows(const Common&, int) {}
+    __device__ __forceinline__ void load(uint64_t s_l, int lane) {
+        const uint32_t off = static_cast<uint32_t>(lane) * 16u;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const uint64_t s = readlane64(s_l, u);
+        for (int u = 0; u < U; ++u) {
+            const uint64_t s = readlane64(s_l, u);
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) x[u][v] = load_nt(s, off + v * 1024);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        if (__builtin_amdgcn_readlane(code_l, u) == kCopy) {
-            const uint64_t d = readlane64(d_l, u);
-#pragma unroll
-            for (int v = 0; v < VPL; ++v) store_v<NTS>(d, off + v * 1024, x[u][v]);
+            for (int v = 0; v < VPL; ++v) x[u][v] = load_nt(s, off + v * 1024);
         }
     }
+    template <bool NTS>
+    __device__ __forceinline__ void store(uint64_t d_l, int code_l, int lane) const {
+        const uint32_t off = static_cast<uint32_t>(lane) * 16u;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (__builtin_amdgcn_readlane(code_l, u) == kCopy) {
+                const uint64_t d = readlane64(d_l, u);
+#pragma unroll
+                for (int v = 0; v < VPL; ++v) store_v<NTS>(d, off + v * 1024, x[u][v]);
+            }
+        }
+    }
+};
+
+template <int VPL, int U, bool NTS>
+__device__ __forceinline__ void copy_wide(uint64_t s_l, uint64_t d_l, int code_l, int lane) {
+    WideRows<VPL, U> w;
+    w.load(s_l, lane);
+    w.template store<NTS>(d_l, code_l, lane);
 }
 
 // Rows of R bytes with 64*(KMAX-1) < V <= 64*KMAX vectors (V = R/16, not a
 // whole number of KiB), up to UMAX rows per chunk (U at run time); row
 // addresses broadcast to SGPRs as in the wide copy, lanes stride a row in
-// 1 KiB steps and the last step is masked to the row's end.
-template <int KMAX, int UMAX, bool NTS>
-__device__ __forceinline__ void copy_rows(const Common& c, uint64_t s_l, uint64_t d_l,
-                                          int code_l, int lane) {
+// 1 KiB steps and the last step is masked to the row's end.  Loads and
+// stores are separate steps, as for WideRows.
+template <int KMAX, int UMAX>
+struct LoopRows {
     v4u x[UMAX][KMAX];
     // Vector lane + 64k of a row; lanes past the row's end load the row's
     // first vector again (in bounds, same cache line) and store nothing, so
     // only the stores are predicated per lane.
     uint32_t off[KMAX];
     bool in_row[KMAX];
+    __device__ __forceinline__ LoopRows(const Common& c, int lane) {
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        in_row[k] = static_cast<uint32_t>(lane + kWave * k) < c.V;
-        off[k] = in_row[k] ? static_cast<uint32_t>(lane + kWave * k) * 16u : 0u;
+        for (int k = 0; k < KMAX; ++k) {
+            in_row[k] = static_cast<uint32_t>(lane + kWave * k) < c.V;
+            off[k] = in_row[k] ? static_cast<uint32_t>(lane + kWave * k) * 16u : 0u;
+        }
     }
     // rows u >= U resolved to kNone (safe source address), so every row is
     // loaded unconditionally and the loop needs no run-time bound
+    __device__ __forceinline__ void load(uint64_t s_l) {
 #pragma unroll
-    for (int u = 0; u < UMAX; ++u) {
-        const uint64_t s = readlane64(s_l, u);
+        for (int u = 0; u < UMAX; ++u) {
+            const uint64_t s = readlane64(s_l, u);
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) x[u][k] = load_nt(s, off[k]);
-    }
-#pragma unroll
-    for (int u = 0; u < UMAX; ++u) {
-        if (__builtin_amdgcn_readlane(code_l, u) == kCopy) {
-            const uint64_t d = readlane64(d_l, u);
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k)
-                if (in_row[k]) store_v<NTS>(d, off[k], x[u][k]);
+            for (int k = 0; k < KMAX; ++k) x[u][k] = load_nt(s, off[k]);
         }
     }
+    template <bool NTS>
+    __device__ __forceinline__ void store(uint64_t d_l, int code_l) const {
+#pragma unroll
+        for (int u = 0; u < UMAX; ++u) {
+            if (__builtin_amdgcn_readlane(code_l, u) == kCopy) {
+                const uint64_t d = readlane64(d_l, u);
+#pragma unroll
+                for (int k = 0; k < KMAX; ++k)
+                    if (in_row[k]) store_v<NTS>(d, off[k], x[u][k]);
+            }
+        }
+    }
+};
+
+template <int KMAX, int UMAX, bool NTS>
+__device__ __forceinline__ void copy_rows(const Common& c, uint64_t s_l, uint64_t d_l,
+                                          int code_l, int lane) {
+    LoopRows<KMAX, UMAX> w(c, lane);
+    w.load(s_l);
+    w.template store<NTS>(d_l, code_l);
+}
+
+// Uniform calls on WideRows / LoopRows (the early-load scatter uses either).
+template <int KMAX, int UMAX>
+__device__ __forceinline__ void load_rows(WideRows<KMAX, UMAX>& w, uint64_t s_l, int lane) {
+    w.load(s_l, lane);
+}
+template <int KMAX, int UMAX>
+__device__ __forceinline__ void load_rows(LoopRows<KMAX, UMAX>& w, uint64_t s_l, int) {
+    w.load(s_l);
+}
+template <bool NTS, int KMAX, int UMAX>
+__device__ __forceinline__ void store_rows(const WideRows<KMAX, UMAX>& w, uint64_t d_l,
+                                           int code_l, int lane) {
+    w.template store<NTS>(d_l, code_l, lane);
+}
+template <bool NTS, int KMAX, int UMAX>
+__device__ __forceinline__ void store_rows(const LoopRows<KMAX, UMAX>& w, uint64_t d_l,
+                                           int code_l, int) {
+    w.template store<NTS>(d_l, code_l);
 }
 
 // Any row size: U*V vectors dealt round-robin to lanes, kFlatNV per pass.
@@ -796,34 +848,23 @@ void k_paged(PagedArgs<Src, Dst> a) {
     unsigned long long nskip = 0;
     for (uint32_t chunk = wave_id<kPagedWaves>(a.c); chunk < a.c.nchunks; chunk += nwaves) {
         const PagedChunk k = paged_chunk(a.c, chunk);
-        if constexpr (KVX_SCATTER_EARLY != 0 && std::is_same<Src, StageRef>::value && VPL > 0) {
-            // scatter of whole 1..16 KiB rows: the staging rows' loads go out
-            // before the destination page table is read, so their latency
-            // overlaps the table reads
+        if constexpr (KVX_SCATTER_EARLY != 0 && std::is_same<Src, StageRef>::value && VPL != 0) {
+            // scatter with the wide or row-loop copy: the staging rows' loads
+            // go out before the destination page table is read, so their
+            // latency overlaps the table reads
             uint64_t s = 0, d = 0;
             StageRow r = resolve_stage_row<MANY>(a, k, static_cast<uint32_t>(lane), s);
-            v4u x[U][VPL];
-            const uint32_t off = static_cast<uint32_t>(lane) * 16u;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint64_t su = readlane64(s, u);
-#pragma unroll
-                for (int v = 0; v < VPL; ++v) x[u][v] = load_nt(su, off + v * 1024);
-            }
+            using Rows = typename std::conditional<(VPL > 0), WideRows<(VPL > 0 ? VPL : 1), U>,
+                                                   LoopRows<(VPL < 0 ? -VPL : 1), U>>::type;
+            Rows w(a.c, lane);
+            load_rows(w, s, lane);
             if (r.code == kCopy) {
                 const SideLook ld =
                     SideAddr<Dst>::look(a.dst, a.c, k.ql, r.pg_dst, r.off, r.n_r, r.t);
                 if (!SideAddr<Dst>::done(a.dst, k.ql, ld, d)) r.code = kSkip;
             }
             nskip += __popcll(__ballot(r.code == kSkip));
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (__builtin_amdgcn_readlane(r.code, u) == kCopy) {
-                    const uint64_t du = readlane64(d, u);
-#pragma unroll
-                    for (int v = 0; v < VPL; ++v) store_v<NTS>(du, off + v * 1024, x[u][v]);
-                }
-            }
+            store_rows<NTS>(w, d, r.code, lane);
             continue;
         }
         uint64_t s = 0, d = 0;
