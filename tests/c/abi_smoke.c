@@ -178,6 +178,26 @@ int main(void) {
     if (memcmp(got_dst, exp_dst, Q * dplane) != 0) { fprintf(stderr, "gather_scatter differs\n"); return 7; }
     if (memcmp(got_st, exp_st, stage_bytes) != 0) { fprintf(stderr, "gather differs\n"); return 8; }
     if ((int64_t)skipped != s1 + s2 || skipped != 0) { fprintf(stderr, "skip count %llu\n", skipped); return 9; }
+    /* the same gather with ordinary stores (KVX_OUT_CACHED), and an unknown flag refused */
+    {
+        uint8_t* st2_d;
+        uint8_t* got2 = malloc(stage_bytes);
+        if (!got2) return 4;
+        CHECK_HIP(hipMalloc((void**)&st2_d, stage_bytes));
+        CHECK_HIP(hipMemset(st2_d, 0, stage_bytes));
+        if (kvx_gather(&lay, &sp, &st, &reqs, st2_d, (int64_t)stage_bytes, NULL, 2u, stream) !=
+            KVX_E_UNSUPPORTED) {
+            fprintf(stderr, "unknown flag not rejected\n");
+            return 16;
+        }
+        CHECK_KVX(kvx_gather(&lay, &sp, &st, &reqs, st2_d, (int64_t)stage_bytes, NULL,
+                             KVX_OUT_CACHED, stream));
+        CHECK_HIP(hipStreamSynchronize(stream));
+        CHECK_HIP(hipMemcpy(got2, st2_d, stage_bytes, hipMemcpyDeviceToHost));
+        if (memcmp(got2, exp_st, stage_bytes) != 0) { fprintf(stderr, "cached gather differs\n"); return 17; }
+        CHECK_HIP(hipFree(st2_d));
+        free(got2);
+    }
 
     /* scatter the gathered staging into a third pool (destination layout) */
     {

@@ -14,7 +14,8 @@ from tests.gpu_util import (DEV, assert_bytes_equal, d, layout_of, oracle_gather
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replays_match_oracle():
+@pytest.mark.parametrize("cached", [False, True])
+def test_graph_replays_match_oracle(cached):
     g = wl.Geometry(2, 2, 8, 128, "bf16")
     case = wl.random_case(4242, geom=g, max_reqs=5, max_len=120, src_page=16, dst_page=1,
                           oor_frac=0.05)
@@ -38,12 +39,12 @@ def test_graph_replays_match_oracle():
     P_d1 = kvx.Pool(dst1, case.dst.num_pages, case.dst.page_size)
     P_d2 = kvx.Pool(dst2, case.dst.num_pages, case.dst.page_size)
 
-    def calls():
-        kvx.gather(lay, P_src, st, reqs, stage, skipped[0:1])
+    def calls():        # both store policies of the contiguous outputs
+        kvx.gather(lay, P_src, st, reqs, stage, skipped[0:1], cached_out=cached)
         kvx.scatter(lay, stage, reqs, P_d1, dt, skipped[1:2])
         kvx.gather_scatter(lay, P_src, st, reqs, P_d2, dt)
-        kvx.extract_permute(lay, hf, seq, seq, flat)
-        kvx.rebuild_permute(lay, flat, seq, hf, seq)
+        kvx.extract_permute(lay, hf, seq, seq, flat, cached_out=cached)
+        kvx.rebuild_permute(lay, flat, seq, hf, seq, cached_out=cached)
 
     # expected bytes of one pass from the prefills
     exp_st = st_h.copy()
