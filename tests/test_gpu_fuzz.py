@@ -5,7 +5,7 @@ ids out of range, random-bit payloads (NaN patterns included),
 sentinel-filled destinations and guard bytes after the staging; token-major
 pools; pools whose blocks hold several planes' pages; launches of 65-160 MiB each way with rows of 1-16 KiB; head-sliced
 copies and permutes; page-table offsets that read outside their request's
-list.  Every case is compared byte for byte over the whole
+list; more than 128 planes.  Every case is compared byte for byte over the whole
 destination, and the skip counters must agree.  KVX_FUZZ_SCALE=k multiplies
 the number of cases of each family (a longer campaign)."""
 import os
@@ -85,6 +85,28 @@ def test_fuzz_table_index_faults(seed):
                           dst_page=int(rng.choice([1, 2, 3, 16])),
                           oor_frac=float(rng.choice([0.0, 0.1])), index_faults=True)
     run_paged_case(case, 87000 + seed)
+
+
+@pytest.mark.parametrize("seed", seeds(8))
+def test_fuzz_many_planes(seed):
+    # more than 128 planes: each call runs as launches over plane ranges of
+    # 128, with short and long requests (both chunk orders of a gather)
+    rng = np.random.default_rng(86000 + seed)
+    dt = DTYPES[int(rng.integers(len(DTYPES)))]
+    elem = {"fp8": 1, "f16": 2, "bf16": 2, "f32": 4}[dt]
+    H = int(rng.choice([1, 2, 4]))
+    R = int(rng.choice([64, 256, 1024, 2048]))                # row bytes
+    g = wl.Geometry(int(rng.integers(65, 131)), 2, H, R // (H * elem), dt)
+    nreq = int(rng.choice([1, 5, 70]))
+    lens = rng.integers(0, 3 if seed % 2 else 40, size=nreq)
+    while lens.sum() * g.planes * R > (96 << 20):           # bound the host work
+        lens //= 2
+    lens[-1] = max(int(lens[-1]), 1)
+    sp, dp = (int(rng.choice([1, 2, 16])) for _ in range(2))
+    oor = float(rng.choice([0.0, 0.05]))
+    assert g.planes > 128 and g.row_bytes % 16 == 0
+    case = big_case(f"fuzzq{seed}", g, list(lens), sp, dp, 86000 + seed, oor)
+    run_paged_case(case, 86000 + seed)
 
 
 @pytest.mark.parametrize("seed", seeds(16))
