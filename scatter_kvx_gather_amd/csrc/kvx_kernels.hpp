@@ -898,6 +898,27 @@ void k_paged_sub(PagedArgs<Src, Dst> a) {
         k.ql = static_cast<int32_t>(ql);
         k.tok0 = static_cast<int64_t>(j >> a.c.sub_shift);
         const uint32_t piece = j & last;
+        if constexpr (KVX_SCATTER_EARLY != 0 && std::is_same<Src, StageRef>::value) {
+            // scatter: the staging piece's loads go out before the
+            // destination page table is read (as in k_paged)
+            uint64_t s = 0, d = 0;
+            StageRow r = resolve_stage_row<MANY>(a, k, static_cast<uint32_t>(lane), s);
+            if (r.code == kCopy) s += static_cast<uint64_t>(piece) * 2048u;
+            WideRows<2, 1> w;
+            w.load(s, lane);
+            if (r.code == kCopy) {
+                const SideLook ld =
+                    SideAddr<Dst>::look(a.dst, a.c, k.ql, r.pg_dst, r.off, r.n_r, r.t);
+                if (SideAddr<Dst>::done(a.dst, k.ql, ld, d))
+                    d += static_cast<uint64_t>(piece) * 2048u;
+                else
+                    r.code = kSkip;
+            }
+            if (r.code == kSkip && piece != 0) r.code = kNone;
+            nskip += __popcll(__ballot(r.code == kSkip));
+            w.template store<NTS>(d, r.code, lane);
+            continue;
+        }
         uint64_t s = 0, d = 0;
         int code = resolve<MANY>(a, k, static_cast<uint32_t>(lane), s, d);
         if (code == kCopy) {
