@@ -65,7 +65,7 @@ namespace kvx {
 #ifndef KVX_LOAD_NT
 #define KVX_LOAD_NT 1              // nontemporal loads
 #endif
-// Scatter (wide and row-loop copies): issue the staging rows' loads before the destination
+// Scatter (every copy shape): issue the staging rows' loads before the destination
 // page table is read.  Measured (same process, alternating; 49152 tokens at
 // 144 KiB/token, 2 KiB rows): one request 5472 -> 5517 GB/s, 16 requests
 // 5304 -> 5539, 256 requests 5126 -> 5301, 1024 and more within 1%.
@@ -801,6 +801,46 @@ __device__ __forceinline__ void copy_flat(const Common& c, uint64_t s_l, uint64_
     }
 }
 
+// The flat copy of a chunk that fits one pass of NV vectors per lane
+// (U*V <= 64 * NV; an 8 KiB paged chunk is 512 vectors), as a load step and
+// a store step, so that a scatter can resolve its destination between them.
+// A vector is loaded when its unit's status is kCopy at load time and stored
+// when it is still kCopy at store time.
+template <int NV>
+struct FlatRows {
+    v4u x[NV];
+    uint32_t act;
+    __device__ __forceinline__ void load(const Common& c, uint64_t s_l, int code_l, int lane) {
+        const uint32_t total = c.U * c.V;
+        act = 0;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const uint32_t i = j * kWave + lane;
+            const uint32_t u = c.V == 1 ? i : __umulhi(i, c.v_magic);
+            const uint32_t vec = i - u * c.V;
+            const int code = static_cast<int>(bperm32(static_cast<uint32_t>(code_l), u));
+            const uint64_t s = bperm64(s_l, u);
+            if (i < total && code == kCopy) {
+                act |= 1u << j;
+                x[j] = load_nt(s, vec * 16u);
+            }
+        }
+    }
+    template <bool NTS>
+    __device__ __forceinline__ void store(const Common& c, uint64_t d_l, int code_l,
+                                          int lane) const {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const uint32_t i = j * kWave + lane;
+            const uint32_t u = c.V == 1 ? i : __umulhi(i, c.v_magic);
+            const uint32_t vec = i - u * c.V;
+            const int code = static_cast<int>(bperm32(static_cast<uint32_t>(code_l), u));
+            const uint64_t d = bperm64(d_l, u);
+            if ((act & (1u << j)) && code == kCopy) store_v<NTS>(d, vec * 16u, x[j]);
+        }
+    }
+};
+
 // --------------------------------------------------------------- kernels --
 
 // Wave number, with XCD-aware workgroup renumbering when c.remap is set: with
@@ -866,6 +906,23 @@ void k_paged(PagedArgs<Src, Dst> a) {
             nskip += __popcll(__ballot(r.code == kSkip));
             store_rows<NTS>(w, d, r.code, lane);
             continue;
+        }
+        if constexpr (KVX_SCATTER_EARLY != 0 && std::is_same<Src, StageRef>::value && VPL == 0) {
+            // the same for the flat copy, when the chunk fits one pass
+            if (a.c.U * a.c.V <= static_cast<uint32_t>(kWave * kChunkBytes / (kWave * 16))) {
+                uint64_t s = 0, d = 0;
+                StageRow r = resolve_stage_row<MANY>(a, k, static_cast<uint32_t>(lane), s);
+                FlatRows<kChunkBytes / (kWave * 16)> f;
+                f.load(a.c, s, r.code, lane);
+                if (r.code == kCopy) {
+                    const SideLook ld =
+                        SideAddr<Dst>::look(a.dst, a.c, k.ql, r.pg_dst, r.off, r.n_r, r.t);
+                    if (!SideAddr<Dst>::done(a.dst, k.ql, ld, d)) r.code = kSkip;
+                }
+                nskip += __popcll(__ballot(r.code == kSkip));
+                f.template store<NTS>(a.c, d, r.code, lane);
+                continue;
+            }
         }
         uint64_t s = 0, d = 0;
         const int code = resolve<MANY>(a, k, static_cast<uint32_t>(lane), s, d);
