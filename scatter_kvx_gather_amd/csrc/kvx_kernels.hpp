@@ -89,6 +89,7 @@ constexpr int kTab = 128;          // plane pointers carried per side per launch
 constexpr int kChunkBytes = KVX_CHUNK_KIB * 1024;
 constexpr int kXcds = 8;           // XCDs on gfx950
 constexpr int kFlatNV = 16;        // vectors per lane per pass of the flat copy
+constexpr int kChunkNV = kChunkBytes / (kWave * 16);   // vectors per lane of a chunk
 
 enum Code : int { kNone = 0, kCopy = 1, kSkip = 2 };
 
@@ -536,6 +537,17 @@ __device__ __forceinline__ StageRow resolve_stage_row(const PagedArgs<StageRef, 
     return r;
 }
 
+// A scatter's destination half, once the row's staging loads are in flight:
+// the destination page-table read and check (kCopy becomes kSkip when an
+// index is out of range).
+template <class Dst>
+__device__ __forceinline__ void resolve_stage_dst(const PagedArgs<StageRef, Dst>& a,
+                                                  const PagedChunk& k, StageRow& r, uint64_t& d) {
+    if (r.code != kCopy) return;
+    const SideLook ld = SideAddr<Dst>::look(a.dst, a.c, k.ql, r.pg_dst, r.off, r.n_r, r.t);
+    if (!SideAddr<Dst>::done(a.dst, k.ql, ld, d)) r.code = kSkip;
+}
+
 // ------------------------------------------------- head-sliced resolver --
 
 // One side of a head-sliced copy: heads per token row, slice start, layout.
@@ -898,27 +910,19 @@ void k_paged(PagedArgs<Src, Dst> a) {
                                                    LoopRows<(VPL < 0 ? -VPL : 1), U>>::type;
             Rows w(a.c, lane);
             load_rows(w, s, lane);
-            if (r.code == kCopy) {
-                const SideLook ld =
-                    SideAddr<Dst>::look(a.dst, a.c, k.ql, r.pg_dst, r.off, r.n_r, r.t);
-                if (!SideAddr<Dst>::done(a.dst, k.ql, ld, d)) r.code = kSkip;
-            }
+            resolve_stage_dst(a, k, r, d);
             nskip += __popcll(__ballot(r.code == kSkip));
             store_rows<NTS>(w, d, r.code, lane);
             continue;
         }
         if constexpr (KVX_SCATTER_EARLY != 0 && std::is_same<Src, StageRef>::value && VPL == 0) {
             // the same for the flat copy, when the chunk fits one pass
-            if (a.c.U * a.c.V <= static_cast<uint32_t>(kWave * kChunkBytes / (kWave * 16))) {
+            if (a.c.U * a.c.V <= static_cast<uint32_t>(kWave * kChunkNV)) {
                 uint64_t s = 0, d = 0;
                 StageRow r = resolve_stage_row<MANY>(a, k, static_cast<uint32_t>(lane), s);
-                FlatRows<kChunkBytes / (kWave * 16)> f;
+                FlatRows<kChunkNV> f;
                 f.load(a.c, s, r.code, lane);
-                if (r.code == kCopy) {
-                    const SideLook ld =
-                        SideAddr<Dst>::look(a.dst, a.c, k.ql, r.pg_dst, r.off, r.n_r, r.t);
-                    if (!SideAddr<Dst>::done(a.dst, k.ql, ld, d)) r.code = kSkip;
-                }
+                resolve_stage_dst(a, k, r, d);
                 nskip += __popcll(__ballot(r.code == kSkip));
                 f.template store<NTS>(a.c, d, r.code, lane);
                 continue;
@@ -963,14 +967,8 @@ void k_paged_sub(PagedArgs<Src, Dst> a) {
             if (r.code == kCopy) s += static_cast<uint64_t>(piece) * 2048u;
             WideRows<2, 1> w;
             w.load(s, lane);
-            if (r.code == kCopy) {
-                const SideLook ld =
-                    SideAddr<Dst>::look(a.dst, a.c, k.ql, r.pg_dst, r.off, r.n_r, r.t);
-                if (SideAddr<Dst>::done(a.dst, k.ql, ld, d))
-                    d += static_cast<uint64_t>(piece) * 2048u;
-                else
-                    r.code = kSkip;
-            }
+            resolve_stage_dst(a, k, r, d);
+            if (r.code == kCopy) d += static_cast<uint64_t>(piece) * 2048u;
             if (r.code == kSkip && piece != 0) r.code = kNone;
             nskip += __popcll(__ballot(r.code == kSkip));
             w.template store<NTS>(d, r.code, lane);
