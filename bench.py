@@ -1522,6 +1522,22 @@ def summarize_counters(out_path, title, tags="kv144k", prefix="rocprof_out/pmcx_
     print(open(out_path).read())
 
 
+# What the kernels in a bench trace that are not the library's are.
+TRACE_NOTES = [
+    ("__amd_rocclr_copyBuffer",
+     "the HIP runtime's copy kernel: the host readback of the pools and staging "
+     "buffers (in pieces of about 1 MiB) for the oracle's parity check and the CPU "
+     "baseline, after the timed steps"),
+    ("k_fill_hash", "device fill of the pools with seeded SplitMix64 words "
+     "(`workloads/devfill.hip`), before any timing"),
+    ("k_copy16", "the plain contiguous copy timed beside the ops (reference rate, and "
+     "the calibration of the traffic counters)"),
+    ("FillFunctor", "torch's zero fill of output buffers at set-up"),
+    ("arange", "torch's arange, building the identity page tables of the contiguous-row "
+     "gather timed beside the ops"),
+]
+
+
 def summarize_trace(trace_dir, out_path, title, command):
     """Markdown summary of a rocprofv3 --kernel-trace --stats run."""
     files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
@@ -1546,6 +1562,12 @@ def summarize_trace(trace_dir, out_path, title, command):
             f.write(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                     f"{float(r['Percentage']):.2f} |\n")
+        notes = [(key, text) for key, text in TRACE_NOTES
+                 if any(key in r["Name"] for r in rows)]
+        if notes:
+            f.write("\nKernels that are not the library's (`kvx::`):\n\n")
+            for key, text in notes:
+                f.write(f"* `{key}`: {text}.\n")
     print(open(out_path).read())
 
 
