@@ -93,11 +93,14 @@ typedef struct {
 } pool_side;
 
 /* Page id of token t of request r, or -1 when its table index or the id it
- * holds is out of range. */
+ * holds is out of range.  The index pg_off[r] + t/B is a plain integer: its
+ * range is checked before the sum is formed, so no pg_off value makes it
+ * wrap (t/B >= 0 and num_ids >= 0, so neither bound overflows). */
 static int64_t page_of(const pool_side* s, int64_t r, int64_t t)
 {
-    int64_t idx = s->pg_off[r] + t / s->page_size;
-    if (idx < 0 || idx >= s->num_ids) return -1;
+    int64_t k = t / s->page_size;
+    if (s->pg_off[r] < -k || s->pg_off[r] >= s->num_ids - k) return -1;
+    int64_t idx = s->pg_off[r] + k;
     int64_t page = (int64_t)s->ids[idx];
     if (page < 0 || page >= s->num_pages) return -1;
     return page;
@@ -304,8 +307,9 @@ typedef struct {
  * its table index or page id is out of range (as for whole rows). */
 static int64_t head_offset(const head_side* s, int64_t Db, int64_t r, int64_t t, int64_t h)
 {
-    int64_t idx = s->pg_off[r] + t / s->page_size;
-    if (idx < 0 || idx >= s->num_ids) return -1;
+    int64_t k = t / s->page_size;              /* the index checked as in page_of */
+    if (s->pg_off[r] < -k || s->pg_off[r] >= s->num_ids - k) return -1;
+    int64_t idx = s->pg_off[r] + k;
     int64_t page = (int64_t)s->ids[idx];
     if (page < 0 || page >= s->num_pages) return -1;
     int64_t row = t % s->page_size;

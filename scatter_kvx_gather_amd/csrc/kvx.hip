@@ -818,8 +818,11 @@ kvx_status side_slots(const kvx_reqs* reqs, const kvx_pool* p, const kvx_table* 
     for (int32_t r = 0; r < reqs->num_reqs; ++r) {
         const int64_t off = reqs->tok_off[r], n = reqs->tok_off[r + 1] - off;
         for (int64_t k = 0; k < n; ++k) {
-            const int64_t idx = t->pg_off[r] + k / p->page_size;
-            if (idx < 0 || idx >= t->num_ids) continue;
+            // the index pg_off[r] + k / page_size, range-checked before the
+            // sum is formed (a plain integer: no pg_off value makes it wrap)
+            const int64_t kp = k / p->page_size, pg = t->pg_off[r];
+            if (pg < -kp || pg >= t->num_ids - kp) continue;
+            const int64_t idx = pg + kp;
             const int64_t page = t->page_ids[idx];
             if (page < 0 || page >= p->num_pages) continue;
             (*slot)[static_cast<size_t>(off + k)] = page * p->page_size + k % p->page_size;
@@ -1140,9 +1143,15 @@ kvx_status kvx_check_tables(int32_t num_reqs, int64_t total_tokens, const int64_
     std::vector<uint64_t> seen;
     if (as_destination) seen.assign(static_cast<size_t>((slots + 63) / 64), 0);
     for (int32_t r = 0; r < num_reqs; ++r) {
+        // compared before they are subtracted: tok_off[r] and pg_off[r] are
+        // >= 0 here (checked at r - 1), so neither difference can overflow
+        if (tok_off[r + 1] < tok_off[r] || pg_off[r + 1] < pg_off[r] || pg_off[r + 1] > num_ids) {
+            if (bad_token != nullptr) *bad_token = tok_off[r];
+            return KVX_E_SHAPE;
+        }
         const int64_t n = tok_off[r + 1] - tok_off[r];
         const int64_t pages = pg_off[r + 1] - pg_off[r];
-        if (n < 0 || pages < 0 || pg_off[r + 1] > num_ids || pages < (n + page_size - 1) / page_size) {
+        if (pages < n / page_size + (n % page_size != 0 ? 1 : 0)) {
             if (bad_token != nullptr) *bad_token = tok_off[r];
             return KVX_E_SHAPE;
         }

@@ -416,12 +416,16 @@ __device__ __forceinline__ SideLook pool_look(const PoolRef& p, int64_t pg_off_r
         pidx = t / p.page_size;
         row = t - pidx * p.page_size;
     }
-    const int64_t idx = pg_off_r + pidx;
+    // the index pg_off_r + pidx as a plain integer, in range exactly when
+    // its unsigned 64-bit sum is below num_ids: pidx is below 2^31, so a
+    // negative index, or one past 2^63 - 1, wraps to 2^63 or above, while
+    // one in [0, num_ids) comes out as itself (no pg_off value overflows)
+    const uint64_t idx = static_cast<uint64_t>(pg_off_r) + static_cast<uint64_t>(pidx);
     SideLook l;
     l.row = row;
     l.addr = 0;
     l.page = -1;
-    if (idx >= 0 && idx < p.num_ids) l.page = p.ids[idx];
+    if (idx < static_cast<uint64_t>(p.num_ids)) l.page = p.ids[idx];
     return l;
 }
 

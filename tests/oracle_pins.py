@@ -532,25 +532,31 @@ def check_oor_boundaries():
 
 
 def check_table_index_boundaries():
-    """A worked example of the page-table reads (pages of B = 2 tokens, five
+    """A worked example of the page-table reads (pages of B = 2 tokens, seven
     requests, three page ids held between two guard entries that name real
     pages): request 0's list starts one entry before the array (its first
     page is skipped), request 1's second page lies one past the end
     (skipped), request 2 has an empty list and reads on into the entries
-    after its start, and requests 3 and 4 start 2**62 entries before and
-    after the array (skipped).  Expected rows are written out by hand; every
-    skipped row is counted and leaves its destination untouched, and the
-    guards are never read."""
+    after its start, requests 3 and 4 start 2**62 entries before and after
+    the array (skipped), and requests 5 and 6 start at the ends of the int64
+    range, where the index pg_off[r] + t / B runs past 2**63 - 1 (request 5's
+    source, request 6's destination: three pages of tokens) or starts at
+    -2**63 (skipped: the index is a plain integer, it does not wrap).
+    Expected rows are written out by hand; every skipped row is counted and
+    leaves its destination untouched, and the guards are never read."""
     rng = np.random.default_rng(27)
     Q, H, D, B, P = 2, 1, 8, 2, 4
     big = 1 << 62
-    lens = [4, 4, 2, 2, 2]
+    i64max, i64min = (1 << 63) - 1, -(1 << 63)
+    lens = [4, 4, 2, 2, 2, 6, 6]
     tok_off = wl.csr_from_lengths(lens)
     guard = 2                                   # a real page: reading a guard copies rows
     s_buf = np.array([guard, 1, 3, 0, guard], np.int32)
     d_buf = np.array([guard, 1, 3, 0, guard], np.int32)
-    src_side = wl.Side(P, B, np.array([-1, 2, 0, -big, big, 3], np.int64), s_buf[1:4])
-    dst_side = wl.Side(P, B, np.array([-1, 2, 1, -big, big, 3], np.int64), d_buf[1:4])
+    src_side = wl.Side(P, B, np.array([-1, 2, 0, -big, big, i64max - 1, i64min, 3], np.int64),
+                       s_buf[1:4])
+    dst_side = wl.Side(P, B, np.array([-1, 2, 1, -big, big, i64min + 1, i64max, 3], np.int64),
+                       d_buf[1:4])
     assert src_side.ids.base is s_buf          # a view: the guards sit around it in memory
     case = wl.PagedCase("idx", wl.Geometry(1, 2, H, D), tok_off, src_side, dst_side, 0, 0, 0)
     # (request, token) -> slot, by hand

@@ -154,6 +154,37 @@ def test_index_faults_against_brute_force(seed):
     check(g, case, a, Side(case.dst, planes(Q, BASE), R))
 
 
+def test_offsets_at_the_ends_of_int64():
+    """Requests whose page lists start at the ends of the int64 range: the
+    index pg_off[r] + t / B runs past 2**63 - 1 or starts at -2**63, and
+    those tokens are left out (the index is a plain integer; it does not
+    wrap).  kvx_check_tables refuses such offsets as a contract violation
+    (KVX_E_SHAPE), again without forming a sum that overflows."""
+    i64max, i64min = (1 << 63) - 1, -(1 << 63)
+    lens = [3, 6, 6, 2]
+    tok = wl.csr_from_lengths(lens)
+    ids = np.array([4, 1, 6, 3, 0, 5], np.int32)
+    g = wl.Geometry(1, 2, 1, 8)
+    Q, R = g.planes, g.row_bytes
+    for B in (1, 2):
+        src = wl.Side(8, B, np.array([0, i64max - 1, i64min, 2, 6], np.int64), ids)
+        dst = wl.Side(8, B, np.array([3, i64min + 1, i64max, 0, 6], np.int64), ids[::-1].copy())
+        case = wl.PagedCase(f"ends{B}", g, tok, src, dst, 0, 0, 0)
+        a = Side(src, planes(Q, BASE), R)
+        b = Side(dst, planes(Q, BASE + (1 << 36)), R)
+        assert check(g, case, a, b) in (OK, E_DUPLICATE)
+        check(g, case, a, None, staging=BASE + (1 << 38), nbytes=case.total_tokens * Q * R)
+        check(g, case, None, b, staging=BASE + (1 << 38), nbytes=case.total_tokens * Q * R)
+        lib = kvx.load_library()
+        bad = ctypes.c_int64(-7)
+        for side in (src, dst):
+            pg = np.ascontiguousarray(side.pg_off, np.int64)
+            st = lib.kvx_check_tables(len(lens), int(tok[-1]), tok.ctypes.data, pg.ctypes.data,
+                                      side.ids.ctypes.data, side.ids.size, side.num_pages, B, 1,
+                                      ctypes.byref(bad))
+            assert st == E_SHAPE and bad.value == 0, (B, st, bad.value)   # request 0 ends out of range
+
+
 @pytest.mark.parametrize("tok_off,total", [([0, 9 + 7], 7), ([0, 5, 3, 7], 7), ([1, 7], 7),
                                            ([0, 6], 7)])
 def test_token_offsets_breaking_the_contract(tok_off, total):

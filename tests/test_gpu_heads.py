@@ -83,6 +83,24 @@ def test_heads_table_index_faults(seed):
     run_heads(case, sH, dH, nh, sh0, dh0, D, seed % 2, (seed // 2) % 2, 200 + seed)
 
 
+@pytest.mark.parametrize("li", range(len(LAYOUTS)))
+def test_heads_offsets_at_the_ends_of_int64(li):
+    """Page lists starting at the ends of the int64 range beside ordinary
+    ones, on both sides of a head-sliced copy (pages of 8 tokens of 128-byte
+    heads on both sides, so HND to HND takes the page-run kernel): the index
+    runs past 2**63 - 1 or starts at -2**63, and those tokens are skipped,
+    not wrapped."""
+    i64max, i64min = (1 << 63) - 1, -(1 << 63)
+    lens = [5, 20, 20, 3]
+    ids = np.array([3, 0, 5, 1, 4, 2, 7, 6], np.int32)
+    src = wl.Side(8, 8, np.array([0, i64max - 1, i64min, 3, 8], np.int64), ids)
+    dst = wl.Side(8, 8, np.array([4, i64min + 1, i64max, 0, 8], np.int64), ids[::-1].copy())
+    case = wl.PagedCase(f"heads_ends{li}", wl.Geometry(1, 2, 4, 64), wl.csr_from_lengths(lens),
+                        src, dst, 0, 0, 0)
+    shnd, dhnd = LAYOUTS[li]
+    run_heads(case, 8, 4, 4, 4, 0, 64, shnd, dhnd, 300 + li)
+
+
 # Batches beyond the 64-request window of the request lookup, with empty
 # requests: (requests, fraction empty, page size, src HND?, dst HND?).  HND on
 # both sides with one page size <= 64 takes the page-run kernel.

@@ -128,13 +128,15 @@ def test_paged_table_index_faults(seed):
 def test_paged_table_index_worked_example():
     """The oracle pin's worked example of the page-table reads on the GPU:
     a list starting one entry early, a page one past the end of the array, an
-    empty list that reads on into the next entries, and offsets 2**62 before
-    and after the array."""
+    empty list that reads on into the next entries, offsets 2**62 before and
+    after the array, and offsets at the ends of the int64 range, where the
+    index runs past 2**63 - 1 or starts at -2**63 (skipped, not wrapped)."""
     big = 1 << 62
-    lens = [4, 4, 2, 2, 2]
-    src = wl.Side(4, 2, np.array([-1, 2, 0, -big, big, 3], np.int64),
+    i64max, i64min = (1 << 63) - 1, -(1 << 63)
+    lens = [4, 4, 2, 2, 2, 6, 6]
+    src = wl.Side(4, 2, np.array([-1, 2, 0, -big, big, i64max - 1, i64min, 3], np.int64),
                   np.array([1, 3, 0], np.int32))
-    dst = wl.Side(4, 2, np.array([-1, 2, 1, -big, big, 3], np.int64),
+    dst = wl.Side(4, 2, np.array([-1, 2, 1, -big, big, i64min + 1, i64max, 3], np.int64),
                   np.array([1, 3, 0], np.int32))
     for g in (wl.Geometry(1, 2, 1, 8), wl.Geometry(2, 2, 8, 128)):
         case = wl.PagedCase(f"idx_example_R{g.row_bytes}", g, wl.csr_from_lengths(lens), src,

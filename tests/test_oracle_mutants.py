@@ -16,19 +16,23 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "kvx_oracle.c")
 
 # the page-table index range checks of the row and head-sliced lookups
-_ROWS_INDEX = ("    if (idx < 0 || idx >= s->num_ids) return -1;\n"
+_ROWS_INDEX = ("    if (s->pg_off[r] < -k || s->pg_off[r] >= s->num_ids - k) return -1;\n"
+               "    int64_t idx = s->pg_off[r] + k;\n"
                "    int64_t page = (int64_t)s->ids[idx];\n"
                "    if (page < 0 || page >= s->num_pages) return -1;\n"
                "    return page;")
-_HEADS_INDEX = ("    if (idx < 0 || idx >= s->num_ids) return -1;\n"
+_HEADS_INDEX = ("    if (s->pg_off[r] < -k || s->pg_off[r] >= s->num_ids - k) return -1;\n"
+                "    int64_t idx = s->pg_off[r] + k;\n"
                 "    int64_t page = (int64_t)s->ids[idx];\n"
                 "    if (page < 0 || page >= s->num_pages) return -1;\n"
                 "    int64_t row")
+_UPPER = " || s->pg_off[r] >= s->num_ids - k"
+_LOWER = "s->pg_off[r] < -k || "
 
 MUTANTS = {
     "row_in_page_uses_div": ("(t % s->page_size) * s->stride", "(t / s->page_size) * s->stride"),
-    "page_index_uses_mod": ("int64_t idx = s->pg_off[r] + t / s->page_size;\n" + _ROWS_INDEX,
-                            "int64_t idx = s->pg_off[r] + t % s->page_size;\n" + _ROWS_INDEX),
+    "page_index_uses_mod": ("int64_t k = t / s->page_size;\n" + _ROWS_INDEX,
+                            "int64_t k = t % s->page_size;\n" + _ROWS_INDEX),
     "page_stride_ignored": ("return page * s->page_stride + (t % s->page_size) * s->stride;",
                             "return page * s->page_size * s->stride + (t % s->page_size) * s->stride;"),
     "page_stride_default_wrong": ("page_stride != 0 ? page_stride : (int64_t)page_size * stride",
@@ -64,15 +68,15 @@ MUTANTS = {
                                     "                skipped += j->nh;\n                continue;\n            }\n            for (int32_t k = 0; k < j->nh; ++k)"),
     "heads_last_head_dropped": ("for (int32_t k = 0; k < j->nh; ++k)",
                                 "for (int32_t k = 0; k + 1 < j->nh; ++k)"),
-    "index_upper_unchecked": (_ROWS_INDEX, _ROWS_INDEX.replace(" || idx >= s->num_ids", "")),
-    "index_upper_off_by_one": (_ROWS_INDEX, _ROWS_INDEX.replace("idx >= s->num_ids",
-                                                                "idx > s->num_ids")),
-    "index_lower_unchecked": (_ROWS_INDEX, _ROWS_INDEX.replace("idx < 0 || ", "")),
+    "index_upper_unchecked": (_ROWS_INDEX, _ROWS_INDEX.replace(_UPPER, "")),
+    "index_upper_off_by_one": (_ROWS_INDEX, _ROWS_INDEX.replace(">= s->num_ids - k",
+                                                                "> s->num_ids - k")),
+    "index_lower_unchecked": (_ROWS_INDEX, _ROWS_INDEX.replace(_LOWER, "")),
     "list_bounded_by_next_start": (_ROWS_INDEX, _ROWS_INDEX.replace(
-        "idx >= s->num_ids)", "idx >= s->num_ids || idx >= s->pg_off[r + 1])")),
-    "heads_index_upper_unchecked": (_HEADS_INDEX, _HEADS_INDEX.replace(" || idx >= s->num_ids",
-                                                                       "")),
-    "heads_index_lower_unchecked": (_HEADS_INDEX, _HEADS_INDEX.replace("idx < 0 || ", "")),
+        "int64_t idx = s->pg_off[r] + k;\n",
+        "int64_t idx = s->pg_off[r] + k;\n    if (idx >= s->pg_off[r + 1]) return -1;\n")),
+    "heads_index_upper_unchecked": (_HEADS_INDEX, _HEADS_INDEX.replace(_UPPER, "")),
+    "heads_index_lower_unchecked": (_HEADS_INDEX, _HEADS_INDEX.replace(_LOWER, "")),
 }
 
 DRIVER = r"""
