@@ -241,6 +241,33 @@ uint32_t wide_rows_for(const Shape& sh, int64_t rows, int64_t row_bytes, int cus
     return row_bytes >= wave_bytes ? 1u : static_cast<uint32_t>(wave_bytes / row_bytes);
 }
 
+// A paged launch with fewer chunks than the GPU has compute units leaves
+// units idle: its chunks shrink -- U halves for the flat and row-loop copies,
+// the wide copy steps to its next smaller instance (1 KiB rows 8 -> 2 -> 1,
+// 2 KiB rows 4 -> 1, 4 KiB rows 2 -> 1) -- until there is at least one chunk
+// per compute unit or one row per chunk.  Measured (same process, graph-
+// timed, microseconds before -> after; gather-scatter / gather / scatter):
+// 512-byte rows of 56 planes, 16 tokens 5.03 -> 4.43 / 4.73 -> 4.14 / 4.12
+// -> 3.37, 32 tokens 5.04 -> 4.55 / 4.77 -> 4.31 / 4.26 -> 3.51, 64 tokens
+// 5.07 -> 4.80 / 4.80 -> 4.54 / 4.32 -> 3.87; 1 KiB rows, 16 tokens 3.48 ->
+// 3.15 / 3.28 -> 2.99 / 3.21 -> 2.90, 32 tokens 3.57 -> 3.63 / 3.44 -> 3.23 /
+// 3.30 -> 3.01; 2 KiB rows of 72 planes, 4 tokens 3.29 -> 2.88 / 3.13 ->
+// 2.72 / 3.08 -> 2.69; 1152-byte rows of 27 planes, 8 tokens 3.18 -> 2.78 /
+// 2.97 -> 2.57 / 2.72 -> 2.41; launches with a chunk per unit unchanged.
+// Asking for two or four chunks per unit gained less.
+uint32_t rows_for_cus(const Shape& sh, int64_t tokens, int32_t nq, int cus) {
+    uint32_t u = sh.U;
+    auto chunks = [&](uint32_t k) {
+        return (static_cast<uint64_t>(tokens) + k - 1) / k * static_cast<uint64_t>(nq);
+    };
+    while (u > 1 && chunks(u) < static_cast<uint64_t>(cus)) {
+        if (sh.vpl == 1) u = u == 8 ? 2u : 1u;
+        else if (sh.vpl > 1) u = 1u;
+        else u /= 2;
+    }
+    return u;
+}
+
 // Paged rows of 4, 8 or 16 KiB in a launch above one round move as 2 KiB
 // pieces (k_paged_sub): log2 of the pieces per row, 0 for whole rows (and when
 // the launch's piece count would not fit the chunk index).  Measured (same process,
@@ -505,6 +532,7 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
         const int32_t nq = g.Q - q0 < kTab ? g.Q - q0 : kTab;
         Shape sh = sh0;
         sh.U = wide_rows_for(sh0, reqs->total_tokens * nq, g.R, cus, kPagedWaveBytes);
+        sh.U = rows_for_cus(sh, reqs->total_tokens, nq, cus);
         const uint32_t sub = sub_shift_for(sh0, reqs->total_tokens, nq, g.R, cus);
         if (sub > 0) sh = {2, 1};                 // one 2 KiB piece per chunk
         PagedArgs<Src, Dst> a;
