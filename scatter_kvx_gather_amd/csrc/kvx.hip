@@ -268,6 +268,29 @@ uint32_t rows_for_cus(const Shape& sh, int64_t tokens, int32_t nq, int cus) {
     return u;
 }
 
+// Small permute launches take smaller chunks too: token rows one row per
+// chunk while the launch would have fewer than two 4-wave workgroups per
+// compute unit, head rows (flat copy) U halved while it has fewer chunks than
+// compute units.  Measured (same process, graph-timed, microseconds before
+// -> after; extract / rebuild; 56 planes unless stated): 1 KiB token rows,
+// seq 32 5.62 -> 2.50 / 3.53 -> 2.43, seq 128 7.82 -> 4.24 / 4.20 -> 4.09,
+// seq 256 10.20 -> 7.31 / 6.73 -> 7.07; 2 KiB rows of 72 planes, seq 64
+// 6.05 -> 4.76 / 5.16 -> 4.53; 4 KiB rows of 32 planes, seq 64 4.95 -> 4.63
+// / 4.37 -> 4.24; 256-byte head rows (two heads), seq 16 4.35 -> 3.80 / 4.35
+// -> 3.79, seq 64 4.45 -> 4.19 / 4.43 -> 4.22.  Larger launches keep their
+// chunks (4 KiB rows at seq 128, one row per chunk: 6.79 -> 7.46 / 5.99 ->
+// 6.86; head rows held to eight chunks per unit lose up to 50%).
+uint32_t permute_rows_for_cus(const Shape& sh, bool token_rows, int64_t units, int32_t nq,
+                              int cus) {
+    auto chunks = [&](uint32_t k) {
+        return (static_cast<uint64_t>(units) + k - 1) / k * static_cast<uint64_t>(nq);
+    };
+    uint32_t u = sh.U;
+    if (token_rows) return u > 1 && chunks(u) < 8ull * static_cast<uint64_t>(cus) ? 1u : u;
+    while (u > 1 && chunks(u) < static_cast<uint64_t>(cus)) u /= 2;
+    return u;
+}
+
 // Paged rows of 4, 8 or 16 KiB in a launch above one round move as 2 KiB
 // pieces (k_paged_sub): log2 of the pieces per row, 0 for whole rows (and when
 // the launch's piece count would not fit the chunk index).  Measured (same process,
@@ -609,6 +632,7 @@ kvx_status run_permute(const Geom& g, void* const* hf, int64_t s_cap, int64_t se
         const int32_t nq = g.Q - q0 < kTab ? g.Q - q0 : kTab;
         Shape sh = sh0;
         if (rows) sh.U = wide_rows_for(sh0, seq * nq, g.R, cus, 0);
+        sh.U = permute_rows_for_cus(sh, rows, units, nq, cus);
         PermuteArgs a;
         std::memset(&a, 0, sizeof(a));
         a.c.T = seq;
