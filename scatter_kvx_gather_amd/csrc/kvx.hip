@@ -726,19 +726,36 @@ kvx_status run_heads(const Geom& g, const kvx_reqs* reqs, const kvx_pool* src,
     int64_t units = kChunkBytes / g.Db;
     if (units < 1) units = 1;
     if (units > kWave) units = kWave;
-    int32_t nhc = static_cast<int32_t>(g.H < units ? g.H : units);
-    int32_t Ut = static_cast<int32_t>(units / nhc);
+    int32_t nhc0 = static_cast<int32_t>(g.H < units ? g.H : units);
+    int32_t Ut0 = static_cast<int32_t>(units / nhc0);
     if (kt > 0) {
-        Ut = src->page_size;                               // one page of tokens
-        const int64_t per_head = Ut * g.Db;
+        Ut0 = src->page_size;                              // one page of tokens
+        const int64_t per_head = Ut0 * g.Db;
         int64_t hc = kChunkBytes / per_head;
         if (hc < 1) hc = 1;
-        nhc = static_cast<int32_t>(g.H < hc ? g.H : hc);
+        nhc0 = static_cast<int32_t>(g.H < hc ? g.H : hc);
     }
-    const int32_t hblocks = (g.H + nhc - 1) / nhc;
-    const uint64_t tblocks = (static_cast<uint64_t>(reqs->total_tokens) + Ut - 1) / Ut;
     for (int32_t q0 = 0; q0 < g.Q; q0 += kTab) {
         const int32_t nq = g.Q - q0 < kTab ? g.Q - q0 : kTab;
+        // a launch with fewer chunks than compute units takes smaller ones, as
+        // the row kernels do: fewer tokens per chunk (flat copy), else fewer
+        // heads (the page-run kernel's chunk is one page of tokens).  Measured
+        // (same process, graph-timed, heads 4..7 of 8 into 0..3 of 4, 72
+        // planes, one request): 8 tokens, HND -> NHD 5.34 -> 4.80 us, HND ->
+        // HND 3.42 -> 3.31; 16 tokens at page 1, 5.40 -> 5.13; from 32 tokens
+        // unchanged
+        auto chunks_of = [&](int32_t ut, int32_t nc) {
+            return (static_cast<uint64_t>(reqs->total_tokens) + ut - 1) / ut *
+                   static_cast<uint64_t>((g.H + nc - 1) / nc) * static_cast<uint64_t>(nq);
+        };
+        int32_t Ut = Ut0, nhc = nhc0;
+        while (chunks_of(Ut, nhc) < static_cast<uint64_t>(cus)) {
+            if (kt == 0 && Ut > 1) Ut /= 2;
+            else if (nhc > 1) nhc = (nhc + 1) / 2;
+            else break;
+        }
+        const int32_t hblocks = (g.H + nhc - 1) / nhc;
+        const uint64_t tblocks = (static_cast<uint64_t>(reqs->total_tokens) + Ut - 1) / Ut;
         HeadArgs a;
         std::memset(&a, 0, sizeof(a));
         a.c.tok_off = reqs->tok_off;
