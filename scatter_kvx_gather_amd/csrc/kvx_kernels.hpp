@@ -6,7 +6,8 @@
 // unit is one row of R bytes, a token row or head row for the permutes, or a
 // (token, head) pair for head-sliced copies), each chunk sized to about
 // 8 KiB; the host lets a large launch of 1..16 KiB rows move one row per
-// chunk instead.  A wave takes one chunk at a time:
+// chunk instead, and a launch too small to give every compute unit a chunk
+// take smaller ones.  A wave takes one chunk at a time:
 //
 //   1. resolve: lane u < U computes unit u's source and destination byte
 //      addresses from the tables (token -> request from a window of 64
