@@ -3,7 +3,8 @@ KVX_LOG=1 (read once per process, so in a child) every gather, extract and
 rebuild launch reports nontemporal stores by default and cached stores with
 KVX_OUT_CACHED, scatter and gather-scatter always nontemporal; both policies
 write the same bytes.  A gather takes token-major chunk order exactly when
-its requests average at most 64 KiB of rows per plane."""
+its requests average at most 64 KiB of rows per plane, and launches too
+small to give every compute unit an 8 KiB chunk take smaller chunks."""
 import os
 import subprocess
 import sys
@@ -100,3 +101,66 @@ def test_store_policy_reaches_the_kernels():
             order[case] = line.split("order=")[1].split()[0]
     assert order == {"nreq=64 T=4096": "token-major", "nreq=63 T=4096": "plane-major",
                      "nreq=1 T=4096": "plane-major", "nreq=16 T=4096": "plane-major"}, order
+
+
+SMALL_CHILD = r"""
+import sys
+sys.path.insert(0, {root!r})
+import numpy as np
+import torch
+import scatter_kvx_gather_amd as kvx
+
+dev = torch.device("cuda:0")
+d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+print("cus", torch.cuda.get_device_properties(0).multi_processor_count, flush=True)
+# paged: 16 tokens of 512-byte rows in 56 planes (8 KiB chunks would give 56)
+lay = kvx.Layout(28, 2, 2, 128, "f16")
+A = torch.zeros((56, 64, 512), dtype=torch.uint8, device=dev)
+tok = d(np.array([0, 16], np.int64))
+st = torch.zeros(16 * 56 * 512, dtype=torch.uint8, device=dev)
+print("case paged", file=sys.stderr, flush=True)
+kvx.gather(lay, kvx.Pool(A, 64), kvx.Table(tok, d(np.arange(16, dtype=np.int32))),
+           kvx.Requests(tok, 16), st)
+# permute: 16 tokens of 1 KiB token rows in 56 planes
+lay = kvx.Layout(28, 2, 4, 128, "f16")
+hf = torch.zeros((56, 4 * 16 * 256), dtype=torch.uint8, device=dev)
+print("case permute", file=sys.stderr, flush=True)
+kvx.extract_permute(lay, hf, 16, 16, torch.zeros(56 * 16 * 1024, dtype=torch.uint8, device=dev))
+# head-sliced: 8 tokens, heads 4..7 of 8 into 0..3 of 4, HND -> NHD, page 16
+lay = kvx.Layout(36, 2, 4, 128, "bf16")
+src = torch.zeros((72, 4 * 16 * 8 * 256), dtype=torch.uint8, device=dev)
+dst = torch.zeros((72, 4 * 16 * 4 * 256), dtype=torch.uint8, device=dev)
+tok = d(np.array([0, 8], np.int64))
+pg = d(np.array([0, 1], np.int64))
+print("case heads", file=sys.stderr, flush=True)
+kvx.gather_scatter_heads(lay, kvx.Pool(src, 4, 16, slot_stride=8 * 256), kvx.Table(pg, d(np.array([2], np.int32))),
+                         kvx.Heads(8, 4, "hnd"), kvx.Requests(tok, 8),
+                         kvx.Pool(dst, 4, 16, slot_stride=4 * 256), kvx.Table(pg, d(np.array([1], np.int32))),
+                         kvx.Heads(4, 0, "nhd"))
+torch.cuda.synchronize()
+print("small ok", flush=True)
+"""
+
+
+def test_small_launches_fill_the_compute_units():
+    """A launch too small to give every compute unit an 8 KiB chunk takes
+    smaller chunks: with KVX_LOG=1 a 16-token paged gather of 512-byte rows
+    and an 8-token head-sliced copy report at least one chunk per compute
+    unit, and a 16-token extract of 1 KiB token rows one row per chunk."""
+    env = dict(os.environ, KVX_LOG="1")
+    p = subprocess.run([sys.executable, "-c", SMALL_CHILD.format(root=ROOT)], capture_output=True,
+                       text=True, timeout=180, env=env, cwd=ROOT)
+    assert p.returncode == 0, p.stdout + p.stderr
+    assert "small ok" in p.stdout
+    cus = int(p.stdout.split("cus", 1)[1].split()[0])
+    seen = {}
+    case = None
+    for line in p.stderr.splitlines():
+        if line.startswith("case "):
+            case = line.split()[1]
+        elif case and line.startswith("kvx: "):
+            f = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
+            seen[case] = f
+    assert int(seen["paged"]["chunks"]) >= cus, seen["paged"]
+    assert int(seen["heads"]["chunks"]) >= cus, seen["heads"]
+    assert seen["permute"]["unit"] == "token-row" and seen["permute"]["U"] == "1", seen["permute"]
