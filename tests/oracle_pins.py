@@ -531,6 +531,45 @@ def check_oor_boundaries():
     assert np.array_equal(out2[:, P * B:], pool[:, P * B:])
 
 
+def check_empty_page_table():
+    """A side whose page-id list is empty: every table index is outside
+    [0, 0), so every row of a gather, scatter or gather-scatter is skipped and
+    counted and every destination byte keeps its value, whatever pg_off says;
+    with the other side empty instead, the copy still moves nothing."""
+    rng = np.random.default_rng(31)
+    Q, H, D, B, P = 2, 1, 8, 4, 4
+    lens = [5, 0, 7]
+    tok_off = wl.csr_from_lengths(lens)
+    n = sum(lens)
+    pg = np.array([0, 2, 2, 4], np.int64)
+    full = wl.Side(P, B, pg, np.array([2, 0, 3, 1], np.int32))
+    empty = wl.Side(P, B, pg, np.zeros(0, np.int32))
+    pool = rand_pool(rng, Q, P * B, H, D)
+    dst = rand_pool(rng, Q, P * B, H, D)
+    case = wl.PagedCase("empty", wl.Geometry(1, 2, H, D), tok_off, empty, full, 0, 0, 0)
+    st = np.full((n * Q, H, D), 0x5A5A, np.uint16)
+    assert o_gather(pool, case, case.src, st.reshape(-1)) == Q * n
+    assert (st == 0x5A5A).all()
+    stage = rng.integers(0, 1 << 16, size=(n * Q, H, D), dtype=np.uint16)
+    got = dst.copy()
+    assert o_scatter(stage.reshape(-1), case, empty, got) == Q * n
+    assert np.array_equal(got, dst)
+    for src_side, dst_side in ((empty, full), (full, empty)):
+        c = wl.PagedCase("empty_gs", wl.Geometry(1, 2, H, D), tok_off, src_side, dst_side, 0, 0, 0)
+        got = dst.copy()
+        assert o_gather_scatter(pool, c, got) == Q * n
+        assert np.array_equal(got, dst)
+    # the full side alone moves every row (the same tables, brute force)
+    c = wl.PagedCase("full_gs", wl.Geometry(1, 2, H, D), tok_off, full, full, 0, 0, 0)
+    got = dst.copy()
+    assert o_gather_scatter(pool, c, got) == 0
+    exp = dst.copy()
+    for r in range(len(lens)):
+        for t in range(lens[r]):
+            exp[:, slot_of(full, r, t)] = pool[:, slot_of(full, r, t)]
+    assert np.array_equal(got, exp)
+
+
 def check_table_index_boundaries():
     """A worked example of the page-table reads (pages of B = 2 tokens, seven
     requests, three page ids held between two guard entries that name real
@@ -841,6 +880,7 @@ ALL_CHECKS = [
     check_closed_form_sizes,
     check_oor_boundaries,
     check_table_index_boundaries,
+    check_empty_page_table,
     check_heads_bruteforce,
     check_heads_full_row_is_row_copy,
     check_heads_layout_conversion,

@@ -144,6 +144,22 @@ def test_paged_table_index_worked_example():
         run_paged_case(case, 11)
 
 
+def test_paged_empty_page_tables():
+    """A side whose page-id array is empty (num_ids 0, page_ids passed as
+    NULL): every index is out of range, so every row is skipped and counted
+    and leaves its destination untouched, while the other side's table is an
+    ordinary one."""
+    lens = [5, 0, 7]
+    pg = np.array([0, 2, 2, 4], np.int64)
+    ids = np.array([2, 0, 3, 1], np.int32)
+    empty = np.zeros(0, np.int32)
+    for g in (wl.Geometry(1, 2, 1, 8), wl.Geometry(2, 2, 8, 128)):
+        for name, sids, dids in (("src", empty, ids), ("dst", ids, empty), ("both", empty, empty)):
+            case = wl.PagedCase(f"empty_table_{name}_R{g.row_bytes}", g, wl.csr_from_lengths(lens),
+                                wl.Side(4, 4, pg, sids), wl.Side(4, 4, pg, dids), 0, 0, 0)
+            run_paged_case(case, 13)
+
+
 def test_many_requests_and_empty_ones():
     # 300 requests, a third of them empty: the token -> request search and the
     # chunks that straddle request boundaries
