@@ -94,9 +94,9 @@ kvx_status check_layout(const kvx_layout* l, Geom* g) {
         return KVX_E_SHAPE;
     int64_t Q = static_cast<int64_t>(l->num_layers) * l->num_kv;
     int64_t Db = static_cast<int64_t>(l->head_dim) * eb;
-    int64_t R = Db * l->kv_heads;
+    int64_t R = 0;
     if (Q > (1 << 20)) return KVX_E_RANGE;
-    if (R > kMaxRowBytes) return KVX_E_RANGE;
+    if (!mul_ok(Db, l->kv_heads, &R) || R > kMaxRowBytes) return KVX_E_RANGE;
     if (R % 16 != 0) return KVX_E_ALIGN;
     g->Q = static_cast<int32_t>(Q);
     g->R = R;
@@ -831,9 +831,12 @@ kvx_status check_hf(const Geom& g, const void* const* hf, int64_t s_cap, int64_t
     if (hf == nullptr) return KVX_E_NULL;
     if (s_cap < 0 || seq < 0 || seq > s_cap) return KVX_E_SHAPE;
     if (g.Db % 16 != 0) return KVX_E_ALIGN;
-    if (seq * static_cast<int64_t>(g.H) >= (int64_t(1) << 31)) return KVX_E_RANGE;
-    int64_t plane_bytes = 0;
-    if (!mul_ok(s_cap * g.H, g.Db, &plane_bytes)) return KVX_E_RANGE;
+    // every product checked before it is used: head rows of the call below
+    // 2^31, and one plane's [H, s_cap, D] bytes within int64
+    int64_t units = 0, cap_rows = 0, plane_bytes = 0;
+    if (!mul_ok(seq, g.H, &units) || units >= (int64_t(1) << 31)) return KVX_E_RANGE;
+    if (!mul_ok(s_cap, g.H, &cap_rows) || !mul_ok(cap_rows, g.Db, &plane_bytes))
+        return KVX_E_RANGE;
     for (int32_t q = 0; q < g.Q; ++q) {
         if (hf[q] == nullptr) {
             if (plane_bytes == 0) continue;      // an empty plane (s_cap = 0) may be NULL

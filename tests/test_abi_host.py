@@ -87,6 +87,8 @@ def test_gather_validation():
     assert gather(_layout(kv=3), pool, tab, reqs) == E_SHAPE
     assert gather(_layout(L=0), pool, tab, reqs) == E_SHAPE
     assert gather(_layout(H=512, D=128), pool, tab, reqs) == E_RANGE        # R = 128 KiB
+    i32max = (1 << 31) - 1                 # R = heads * dim * 4 past 2^63: refused, not formed
+    assert gather(_layout(H=i32max, D=i32max, dtype=4), pool, tab, reqs) == E_RANGE
     assert gather(lay, None, tab, reqs) == E_NULL
     assert gather(lay, pool, None, reqs) == E_NULL
     assert gather(lay, pool, tab, None) == E_NULL
@@ -166,6 +168,12 @@ def test_permute_validation():
         E_UNSUPPORTED
     assert rb(0, flags=1) == OK
     assert rb(0, flags=1 << 31) == E_UNSUPPORTED
+    # sizes whose products pass int64: refused with KVX_E_RANGE, never formed
+    big = 1 << 62
+    assert ex(big, 0) == E_RANGE                   # s_cap * H * Db > 2^63
+    assert ex(big, big) == E_RANGE                 # seq * H as well
+    assert ex(big, 1 << 29) == E_RANGE
+    assert lib.kvx_rebuild_permute(ctypes.byref(lay), A, need, 0, hf, big, 0, None) == E_RANGE
 
 
 def test_heads_validation():
