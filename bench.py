@@ -37,6 +37,7 @@ on the host on a bounded sample of the same steps.
   python bench.py --cu-split            (the two on complementary CU-masked streams)
   python bench.py --comparators         (per-block runtime copies, DMA copy of staging)
   python bench.py --patterns            (the request's row patterns moved without tables)
+  python bench.py --dram-pages          (equal-density slot placements: rows sharing DRAM pages)
   python bench.py --sizes               (one request of 16 .. 8192 tokens: latency to bandwidth)
   python bench.py --batches             (49152 tokens in 1 .. 49152 requests: request lookup)
   python bench.py --row-sizes           (rows of 256 B .. 16 KiB at ~256 MiB each way)
@@ -1282,6 +1283,137 @@ def row_patterns(torch, kvx, wl, wdev, dev, stream, rounds=3, n=32):
     print(json.dumps(out), flush=True)
 
 
+# ------------------------------------------------------- DRAM-page probe --
+#
+# HBM serves a row fastest when other rows on the same DRAM page arrive with
+# it.  The probe keeps the 2048-token request's size and density (2048 of the
+# 32768 slots of each page-1 pool, 2 KiB rows) and varies only where the
+# slots lie: in pairs at a fixed distance, the partner a fixed number of
+# tokens later, on one side or both, or as runs of B slots (pages of a
+# block-paged pool written as page-1 tables) in their natural token order or
+# with the rows 32 KiB apart made adjacent.
+
+DRAM_SEG = 32 << 10        # bytes between rows that share a DRAM page (probe result)
+
+
+def dram_page_sets(kind, arg, rng, slots=32768, tokens=2048, nsets=8, row_bytes=2048):
+    """`nsets` pairwise disjoint slot lists of `tokens` entries each (one per
+    rotated request), every slot in [0, slots):
+      ("random", None)         a seeded permutation cut into pieces;
+      ("sorted", None)         the same, each list sorted;
+      ("pairs", (dist, gap))   slot pairs (s, s + dist) with s % (2 dist) < dist,
+                               the partner `gap` tokens after its start;
+      ("pages", (B, grouped))  runs of B slots at B-aligned starts; with
+                               `grouped` the run's rows DRAM_SEG bytes apart are
+                               consecutive in token order."""
+    import numpy as np
+    if kind in ("random", "sorted"):
+        p = rng.permutation(slots)
+        sets = [p[k * tokens:(k + 1) * tokens] for k in range(nsets)]
+        return [np.sort(s) if kind == "sorted" else s for s in sets]
+    if kind == "pairs":
+        dist, gap = arg
+        s = np.arange(slots)
+        cand = s[(s % (2 * dist) < dist) & (s + dist < slots)]
+        rng.shuffle(cand)
+        half = tokens // 2
+        out = []
+        for k in range(nsets):
+            st = cand[k * half:(k + 1) * half]
+            ids = np.empty(tokens, np.int64)
+            for b in range(0, half, gap):
+                blk = st[b:b + gap]
+                ids[2 * b:2 * b + len(blk)] = blk
+                ids[2 * b + len(blk):2 * b + 2 * len(blk)] = blk + dist
+            out.append(ids)
+        return out
+    if kind == "pages":
+        B, grouped = arg
+        per = tokens // B
+        pages = rng.permutation(slots // B)
+        within = np.arange(B)
+        g = DRAM_SEG // row_bytes
+        if grouped and B >= 2 * g and B % g == 0:
+            within = within.reshape(B // g, g).T.reshape(-1)
+        return [(pages[k * per:(k + 1) * per, None] * B + within[None, :]).reshape(-1)
+                for k in range(nsets)]
+    raise ValueError(kind)
+
+
+# (label, source sets, destination sets)
+DRAM_PAGE_DESIGNS = (
+    [("random slots (the workload's tables)", ("random", None), ("random", None)),
+     ("sorted slots", ("sorted", None), ("sorted", None))]
+    + [(f"pairs {d * 2} KiB apart, adjacent tokens", ("pairs", (d, 1)), ("pairs", (d, 1)))
+       for d in (4, 8, 12, 16, 24, 32, 48, 64)]
+    + [(f"pairs 64 KiB apart, partner {j} tokens later", ("pairs", (32, j)),
+        ("pairs", (32, j))) for j in (2, 4, 8, 16, 64, 1024)]
+    + [("pairs 64 KiB apart in the source only", ("pairs", (32, 1)), ("random", None)),
+       ("pairs 64 KiB apart in the destination only", ("random", None), ("pairs", (32, 1)))]
+    + [(f"runs of {B} slots ({B * 2} KiB), {'grouped' if g else 'natural'} order",
+        ("pages", (B, g)), ("pages", (B, g))) for B in (16, 32, 64) for g in (False, True)
+       if B > 16 or not g])
+
+
+def dram_pages(torch, kvx, wl, wdev, dev, stream, rounds=3, n=24):
+    """Gather-scatter, gather and scatter of the 2048-token request over
+    slot placements of equal density (DRAM_PAGE_DESIGNS), graph-timed, the
+    designs alternating round by round in one process on the same two
+    4.5 GiB pools; 8 disjoint requests rotated per design."""
+    import numpy as np
+    g = wl.KV144K
+    Q, R, NS, T, NSETS = g.planes, g.row_bytes, 32768, 2048, 8
+    A = torch.empty((Q, NS, R), dtype=torch.uint8, device=dev)
+    B = torch.empty_like(A)
+    wdev.fill_hash(A, 1, stream=stream)
+    wdev.fill_hash(B, 2, stream=stream)
+    st = torch.empty(T * Q * R, dtype=torch.uint8, device=dev)
+    lay = kvx.Layout(g.num_layers, g.num_kv, g.kv_heads, g.head_dim, g.dtype)
+    PA, PB = kvx.Pool(A, NS), kvx.Pool(B, NS)
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    tok = d(np.array([0, T], np.int64))
+    reqs = kvx.Requests(tok, T)
+    tabs = []
+    for i, (label, sk, dk) in enumerate(DRAM_PAGE_DESIGNS):
+        ss = dram_page_sets(*sk, np.random.default_rng(5100 + i), NS, T, NSETS, R)
+        ds = dram_page_sets(*dk, np.random.default_rng(5900 + i), NS, T, NSETS, R)
+        for x in ss + ds:
+            if len(np.unique(x)) != T or x.min() < 0 or x.max() >= NS:
+                raise AssertionError(f"{label}: bad slot list")
+        tabs.append(([kvx.Table(tok, d(x.astype(np.int32))) for x in ss],
+                      [kvx.Table(tok, d(x.astype(np.int32))) for x in ds]))
+    torch.cuda.synchronize()
+    nb = 2 * T * Q * R
+    res = [{"gather_scatter": [], "gather": [], "scatter": []} for _ in DRAM_PAGE_DESIGNS]
+    for rnd in range(rounds):
+        for i, (sT, dT) in enumerate(tabs):
+            fns = {"gather_scatter": lambda k: kvx.gather_scatter(
+                       lay, PA, sT[k % NSETS], reqs, PB, dT[k % NSETS], stream=stream),
+                   "gather": lambda k: kvx.gather(lay, PA, sT[k % NSETS], reqs, st,
+                                                  stream=stream),
+                   "scatter": lambda k: kvx.scatter(lay, st, reqs, PB, dT[k % NSETS],
+                                                    stream=stream)}
+            for op, fn in fns.items():
+                res[i][op].append(nb / (graph_timed(torch, stream, fn, n) * 1e-3) / 1e9)
+        log(f"dram-pages round {rnd + 1}/{rounds} done")
+    rows = []
+    for (label, sk, dk), r in zip(DRAM_PAGE_DESIGNS, res):
+        row = {"design": label}
+        for op, v in r.items():
+            row[f"{op}_GBps"] = round(sorted(v)[len(v) // 2], 1)
+        rows.append(row)
+        log(f"  {label:55s} {row['gather_scatter_GBps']:7.1f} {row['gather_GBps']:7.1f} "
+            f"{row['scatter_GBps']:7.1f}")
+    print(json.dumps({"dram_pages": rows,
+                      "note": "one request of 2048 tokens x 72 planes of 2 KiB rows (288 MiB "
+                              "each way) in page-1 pools of 32768 slots (4.5 GiB each); every "
+                              "design uses 2048 of the 32768 slots per request, only their "
+                              "placement differs; 8 disjoint requests rotated, 24 launches per "
+                              "graph, median of 3 rounds"}), flush=True)
+
+
 def comparators(torch, kvx, wl, wdev, dev):
     """The same 2048-token request moved by per-block runtime copies."""
     import ctypes
@@ -1583,7 +1715,8 @@ COMPARATOR_ROWS = [
 
 def summarize_json(log_path, out_path, title, command):
     """Markdown tables from the JSON lines that --concurrent, --cu-split,
-    --comparators and --patterns print (any of them, in one log)."""
+    --comparators, --patterns and --dram-pages print (any of them, in one
+    log)."""
     lines = []
     with open(log_path) as f:
         for line in f:
@@ -1658,6 +1791,16 @@ def summarize_json(log_path, out_path, title, command):
                         "process (with their page-table reads):\n\n| op | GB/s |\n|---|---:|\n")
                 for op, v in d["library_ops_alone_GBps"].items():
                     f.write(f"| {op} | {v} |\n")
+                f.write("\n")
+            if "dram_pages" in d:
+                f.write("The 2048-token request (72 planes of 2 KiB rows, 288 MiB each way) "
+                        "with its slots placed differently at the same density: 2048 of the "
+                        "32768 slots of each page-1 pool per request.\n\n")
+                f.write("| slot placement (source and destination) | gather-scatter | gather | "
+                        "scatter |\n|---|---:|---:|---:|\n")
+                for r in d["dram_pages"]:
+                    f.write(f"| {r['design']} | {r['gather_scatter_GBps']} | "
+                            f"{r['gather_GBps']} | {r['scatter_GBps']} |\n")
                 f.write("\n")
             if "mla_row_patterns" in d:
                 f.write("The MLA request (27 planes of 1152-byte rows, 2048 tokens, 32768-slot "
@@ -1746,6 +1889,9 @@ def main():
     ap.add_argument("--patterns", action="store_true",
                     help="the request's row patterns moved by a table-free kernel, beside "
                          "the library's ops")
+    ap.add_argument("--dram-pages", action="store_true",
+                    help="the request's ops over slot placements of equal density: rows that "
+                         "share DRAM pages or not")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "OUT", "TITLE", "CMD"),
                     help="markdown summary of a rocprofv3 --kernel-trace --stats run")
@@ -1757,7 +1903,7 @@ def main():
                     help="what --pmc-pass runs")
     ap.add_argument("--summarize-json", nargs=4, metavar=("LOG", "OUT", "TITLE", "CMD"),
                     help="markdown tables from the JSON lines of --concurrent / --cu-split / "
-                         "--comparators / --patterns")
+                         "--comparators / --patterns / --dram-pages")
     ap.add_argument("--counter-commands", action="store_true",
                     help="print the rocprofv3 command of every counter pass")
     args = ap.parse_args()
@@ -1821,6 +1967,9 @@ def main():
         return 0
     if args.patterns:
         row_patterns(torch, kvx, wl, wdev, dev, stream)
+        return 0
+    if args.dram_pages:
+        dram_pages(torch, kvx, wl, wdev, dev, stream)
         return 0
     if args.pmc_pass:
         pmc_pass(torch, kvx, wl, wdev, dev, stream, args.pmc_workload)

@@ -88,3 +88,38 @@ def test_cpu_share_is_within_the_machine():
     assert 1 <= s["usable"] <= s["affinity"] <= s["nproc"]
     model, sockets = b.host_cpu()
     assert isinstance(model, str) and model and sockets >= 1
+
+
+def test_dram_page_placements_have_the_structure_they_name():
+    import numpy as np
+    b = _bench()
+    NS, T, N = 32768, 2048, 8
+    for i, (label, sk, dk) in enumerate(b.DRAM_PAGE_DESIGNS):
+        for kind, arg in (sk, dk):
+            sets = b.dram_page_sets(kind, arg, np.random.default_rng(i), NS, T, N, 2048)
+            assert len(sets) == N, label
+            allx = np.concatenate(sets)
+            assert len(np.unique(allx)) == N * T, label          # disjoint requests
+            assert allx.min() >= 0 and allx.max() < NS, label
+            for x in sets:
+                assert len(x) == T
+                if kind == "sorted":
+                    assert np.all(np.diff(x) > 0)
+                if kind == "pairs":
+                    dist, gap = arg
+                    blk = x.reshape(-1, 2, gap)                 # [starts..., partners...]
+                    assert np.all(blk[:, 1, :] - blk[:, 0, :] == dist), label
+                    assert np.all(blk[:, 0, :] % (2 * dist) < dist), label
+                if kind == "pages":
+                    B, grouped = arg
+                    runs = x.reshape(-1, B)
+                    base = runs.min(axis=1)
+                    assert np.all(base % B == 0), label
+                    assert np.all(np.sort(runs, axis=1) == base[:, None] + np.arange(B)), label
+                    off = runs - base[:, None]
+                    if grouped:
+                        g = b.DRAM_SEG // 2048
+                        # consecutive tokens are g rows (32 KiB) apart within a group
+                        assert np.all(off[:, :B // g] == g * np.arange(B // g)), label
+                    else:
+                        assert np.all(off == np.arange(B)), label
