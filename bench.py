@@ -1364,12 +1364,12 @@ def dram_pages(torch, kvx, wl, wdev, dev, stream, rounds=3, n=24):
     g = wl.KV144K
     Q, R, NS, T, NSETS = g.planes, g.row_bytes, 32768, 2048, 8
     A = torch.empty((Q, NS, R), dtype=torch.uint8, device=dev)
-    B = torch.empty_like(A)
+    Bt = torch.empty_like(A)
     wdev.fill_hash(A, 1, stream=stream)
-    wdev.fill_hash(B, 2, stream=stream)
+    wdev.fill_hash(Bt, 2, stream=stream)
     st = torch.empty(T * Q * R, dtype=torch.uint8, device=dev)
     lay = kvx.Layout(g.num_layers, g.num_kv, g.kv_heads, g.head_dim, g.dtype)
-    PA, PB = kvx.Pool(A, NS), kvx.Pool(B, NS)
+    PA, PB = kvx.Pool(A, NS), kvx.Pool(Bt, NS)
 
     def d(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -1406,7 +1406,40 @@ def dram_pages(torch, kvx, wl, wdev, dev, stream, rounds=3, n=24):
         rows.append(row)
         log(f"  {label:55s} {row['gather_scatter_GBps']:7.1f} {row['gather_GBps']:7.1f} "
             f"{row['scatter_GBps']:7.1f}")
-    print(json.dumps({"dram_pages": rows,
+    # the same request in block pools (page_size B, random pages), where the
+    # library pairs the rows that share DRAM pages once a page holds 64 KiB
+    blocks = {B: {"gather_scatter": [], "gather": [], "scatter": []} for B in (16, 32, 64, 128)}
+    btabs = {}
+    for B in blocks:
+        P, npg = NS // B, T // B
+        rng = np.random.default_rng(6100 + B)
+        ps, pd = rng.permutation(P), rng.permutation(P)
+        pg = d(np.array([0, npg], np.int64))
+        btabs[B] = (kvx.Pool(A, P, B), kvx.Pool(Bt, P, B),
+                    [kvx.Table(pg, d(ps[k * npg:(k + 1) * npg].astype(np.int32)))
+                     for k in range(NSETS)],
+                    [kvx.Table(pg, d(pd[k * npg:(k + 1) * npg].astype(np.int32)))
+                     for k in range(NSETS)])
+    for rnd in range(rounds):
+        for B, (pa, pb, sT, dT) in btabs.items():
+            fns = {"gather_scatter": lambda k: kvx.gather_scatter(
+                       lay, pa, sT[k % NSETS], reqs, pb, dT[k % NSETS], stream=stream),
+                   "gather": lambda k: kvx.gather(lay, pa, sT[k % NSETS], reqs, st,
+                                                  stream=stream),
+                   "scatter": lambda k: kvx.scatter(lay, st, reqs, pb, dT[k % NSETS],
+                                                    stream=stream)}
+            for op, fn in fns.items():
+                blocks[B][op].append(nb / (graph_timed(torch, stream, fn, n) * 1e-3) / 1e9)
+    brows = []
+    for B, r in blocks.items():
+        row = {"page_size": B, "page_KiB": B * R // 1024,
+               "paired": B * R >= 2 * DRAM_SEG}
+        for op, v in r.items():
+            row[f"{op}_GBps"] = round(sorted(v)[len(v) // 2], 1)
+        brows.append(row)
+        log(f"  block pool, page {B:3d}: {row['gather_scatter_GBps']:7.1f} "
+            f"{row['gather_GBps']:7.1f} {row['scatter_GBps']:7.1f}")
+    print(json.dumps({"dram_pages": rows, "block_pools": brows,
                       "note": "one request of 2048 tokens x 72 planes of 2 KiB rows (288 MiB "
                               "each way) in page-1 pools of 32768 slots (4.5 GiB each); every "
                               "design uses 2048 of the 32768 slots per request, only their "
@@ -1800,6 +1833,18 @@ def summarize_json(log_path, out_path, title, command):
                         "scatter |\n|---|---:|---:|---:|\n")
                 for r in d["dram_pages"]:
                     f.write(f"| {r['design']} | {r['gather_scatter_GBps']} | "
+                            f"{r['gather_GBps']} | {r['scatter_GBps']} |\n")
+                f.write("\n")
+            if "block_pools" in d:
+                f.write("The same request between block pools of the same 32768 slots (pages "
+                        "of B rows, the request's pages a seeded random subset, 8 disjoint "
+                        "requests rotated); from pages of 64 KiB the library pairs the rows "
+                        "32 KiB apart on the two waves of one workgroup.\n\n")
+                f.write("| page size (rows) | page (KiB) | rows paired | gather-scatter | "
+                        "gather | scatter |\n|---:|---:|---|---:|---:|---:|\n")
+                for r in d["block_pools"]:
+                    f.write(f"| {r['page_size']} | {r['page_KiB']} | "
+                            f"{'yes' if r['paired'] else 'no'} | {r['gather_scatter_GBps']} | "
                             f"{r['gather_GBps']} | {r['scatter_GBps']} |\n")
                 f.write("\n")
             if "mla_row_patterns" in d:

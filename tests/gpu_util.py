@@ -27,6 +27,18 @@ def d(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
+def d_aligned(a: np.ndarray, align: int) -> torch.Tensor:
+    """A device copy of `a` whose first byte sits at a multiple of `align`
+    bytes (a view into a slightly larger allocation)."""
+    flat = np.ascontiguousarray(a).reshape(-1).view(np.uint8)
+    buf = torch.empty(flat.size + align, dtype=torch.uint8, device=DEV)
+    off = (-buf.data_ptr()) % align
+    t = buf[off:off + flat.size]
+    t.copy_(torch.from_numpy(flat))
+    assert t.data_ptr() % align == 0
+    return t.view(a.shape)
+
+
 def table(side: wl.Side) -> kvx.Table:
     return kvx.Table(d(side.pg_off.astype(np.int64)), d(side.ids.astype(np.int32)))
 

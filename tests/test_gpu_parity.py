@@ -9,7 +9,7 @@ import torch
 import oracle
 import scatter_kvx_gather_amd as kvx
 import workloads as wl
-from tests.gpu_util import (DEV, assert_bytes_equal, d, layout_of, oracle_gather,
+from tests.gpu_util import (DEV, assert_bytes_equal, d, d_aligned, layout_of, oracle_gather,
                             oracle_gather_scatter, oracle_scatter, requests, say, table)
 
 pytestmark = pytest.mark.gpu
@@ -40,8 +40,12 @@ GEOMS = [
 ]
 
 
-def run_paged_case(case, seed, guard=256):
+def run_paged_case(case, seed, guard=256, align=0):
+    """gather (nontemporal and cached staging stores), scatter and
+    gather-scatter of a case, every destination byte and the skip counts
+    against the oracle; `align`: the pools' first bytes at that multiple."""
     g = case.geom
+    dev_pool = (lambda a: d_aligned(a, align)) if align else d
     Q, R = g.planes, g.row_bytes
     rng = np.random.default_rng(seed)
     src_h = rng.integers(0, 256, (Q, case.src.num_slots, R), dtype=np.uint8)
@@ -52,7 +56,7 @@ def run_paged_case(case, seed, guard=256):
     lay = layout_of(g)
     reqs = requests(case)
     st, dt = table(case.src), table(case.dst)
-    src_d = d(src_h)
+    src_d = dev_pool(src_h)
     src = kvx.Pool(src_d, case.src.num_pages, case.src.page_size)
     skipped = torch.zeros(3, dtype=torch.int64, device=DEV)
 
@@ -65,11 +69,11 @@ def run_paged_case(case, seed, guard=256):
     staging_c = d(stage_prefill)
     kvx.gather(lay, src, st, reqs, staging_c, cached_out=True)
     say(case.name, "scatter")
-    dst_d1 = d(dst_h)
+    dst_d1 = dev_pool(dst_h)
     kvx.scatter(lay, d(stage_in), reqs, kvx.Pool(dst_d1, case.dst.num_pages, case.dst.page_size),
                 dt, skipped=skipped[1:2])
     say(case.name, "gather_scatter")
-    dst_d2 = d(dst_h)
+    dst_d2 = dev_pool(dst_h)
     kvx.gather_scatter(lay, src, st, reqs,
                        kvx.Pool(dst_d2, case.dst.num_pages, case.dst.page_size), dt,
                        skipped=skipped[2:3])
@@ -221,6 +225,37 @@ def test_one_row_per_wave_launches(bi):
     g, lens, sp, dp, oor = BIG[bi]
     assert sum(lens) * g.planes * g.row_bytes > 64 << 20
     run_paged_case(big_case(f"big{bi}", g, lens, sp, dp, 700 + bi, oor), 700 + bi)
+
+
+# Pools whose pages hold runs of at least 64 KiB of a plane, planes aligned
+# to 128 KiB, in launches above 64 MiB each way: the kernels take each
+# request's tokens in DRAM-page order (rows 32 KiB apart on the two waves of
+# one workgroup, or in one wave for 1 KiB rows; a block past the request's
+# end in natural order).  One 2 KiB row or two 1 KiB rows per wave, one
+# side or both paired, ragged requests whose starts are not block aligned,
+# partial last pages, out-of-range ids, a batch above 64 requests.
+# (geometry, lengths, src page, dst page, oor)
+DRAM = [
+    (wl.Geometry(36, 2, 8, 128, "bf16"), [300, 0, 257, 64, 1], 64, 64, 0.0),   # 2 KiB
+    (wl.Geometry(36, 2, 8, 128, "bf16"), [500, 130, 33], 32, 64, 0.02),
+    (wl.Geometry(36, 2, 8, 128, "bf16"), [420, 65], 64, 1, 0.0),               # source only
+    (wl.Geometry(36, 2, 8, 128, "bf16"), [400, 97], 1, 32, 0.01),              # destination only
+    (wl.Geometry(36, 2, 8, 128, "bf16"), [600, 70, 1], 64, 32, 0.01),
+    (wl.Geometry(28, 2, 4, 128, "bf16"), [700, 129, 500], 128, 64, 0.02),      # 1 KiB
+    (wl.Geometry(36, 2, 4, 128, "bf16"), [900, 250], 64, 128, 0.0),
+    (wl.Geometry(36, 2, 8, 128, "bf16"), "many", 32, 32, 0.01),                # > 64 requests
+]
+
+
+@pytest.mark.parametrize("di", range(len(DRAM)))
+def test_dram_page_order(di):
+    g, lens, sp, dp, oor = DRAM[di]
+    if lens == "many":
+        rng = np.random.default_rng(880 + di)
+        lens = [int(x) for x in rng.integers(0, 61, 70)]
+    assert sum(lens) * g.planes * g.row_bytes > 64 << 20
+    run_paged_case(big_case(f"dram{di}", g, lens, sp, dp, 880 + di, oor), 880 + di,
+                   align=128 << 10)
 
 
 # One-row-per-wave launches of batches above 64 requests (the kernels with

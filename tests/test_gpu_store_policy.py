@@ -164,3 +164,73 @@ def test_small_launches_fill_the_compute_units():
     assert int(seen["paged"]["chunks"]) >= cus, seen["paged"]
     assert int(seen["heads"]["chunks"]) >= cus, seen["heads"]
     assert seen["permute"]["unit"] == "token-row" and seen["permute"]["U"] == "1", seen["permute"]
+
+
+DRAM_CHILD = r"""
+import sys
+sys.path.insert(0, {root!r})
+import numpy as np
+import torch
+import scatter_kvx_gather_amd as kvx
+
+dev = torch.device("cuda:0")
+d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+rng = np.random.default_rng(5)
+
+
+def pool(Q, S, R, off):
+    buf = torch.zeros(Q * S * R + (256 << 10), dtype=torch.uint8, device=dev)
+    o = (-buf.data_ptr()) % (128 << 10) + off
+    return buf[o:o + Q * S * R].view(Q, S, R)
+
+
+def paged(L, H, B, T, off, op):
+    lay = kvx.Layout(L, 2, H, 128, "bf16")                  # R = H * 256 bytes
+    Q, R, P = 2 * L, H * 256, T // B + 4
+    tok, pg = d(np.array([0, T], np.int64)), d(np.array([0, T // B], np.int64))
+    reqs = kvx.Requests(tok, T)
+    A, Bp = pool(Q, P * B, R, off), pool(Q, P * B, R, off)
+    ta = kvx.Table(pg, d(rng.permutation(P)[:T // B].astype(np.int32)))
+    tb = kvx.Table(pg, d(rng.permutation(P)[:T // B].astype(np.int32)))
+    if op == "gather":
+        st = torch.zeros(Q * T * R, dtype=torch.uint8, device=dev)
+        kvx.gather(lay, kvx.Pool(A, P, B), ta, reqs, st)
+    else:
+        kvx.gather_scatter(lay, kvx.Pool(A, P, B), ta, reqs, kvx.Pool(Bp, P, B), tb)
+    torch.cuda.synchronize()
+
+
+for name, L, H, B, T, off, op in (("large64", 36, 8, 64, 640, 0, "gather_scatter"),
+                                   ("large32", 36, 8, 32, 640, 0, "gather"),
+                                   ("large1k", 28, 4, 64, 1280, 0, "gather"),
+                                   ("large16", 36, 8, 16, 640, 0, "gather"),
+                                   ("misaligned", 36, 8, 64, 640, 2048, "gather"),
+                                   ("small64", 2, 8, 64, 640, 0, "gather")):
+    print(f"case {{name}}", file=sys.stderr, flush=True)
+    paged(L, H, B, T, off, op)
+print("dram ok", flush=True)
+"""
+
+
+def test_dram_page_order_reaches_the_kernels():
+    """With KVX_LOG=1: a plane-major launch above one round of resident
+    waves pairs the rows that share DRAM pages (2 KiB rows one per wave, 1 KiB
+    rows two per wave) when a pool's pages hold runs of at least 64 KiB of a
+    plane and its planes are aligned; not for pages of 32 KiB, planes off the
+    64 KiB grid, or a launch of 8 KiB chunks."""
+    env = dict(os.environ, KVX_LOG="1")
+    p = subprocess.run([sys.executable, "-c", DRAM_CHILD.format(root=ROOT)], capture_output=True,
+                       text=True, timeout=180, env=env, cwd=ROOT)
+    assert p.returncode == 0, p.stdout + p.stderr
+    assert "dram ok" in p.stdout
+    seen, case = {}, None
+    for line in p.stderr.splitlines():
+        if line.startswith("case "):
+            case = line.split()[1]
+        elif case and line.startswith("kvx: "):
+            seen[case] = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
+    expect = {"large64": ("1", "2"), "large32": ("1", "2"), "large1k": ("2", "2"),
+              "large16": ("1", "0"), "misaligned": ("1", "0"), "small64": ("4", "0")}
+    for case, (U, grp) in expect.items():
+        f = seen[case]
+        assert f["order"] == "plane-major" and f["U"] == U and f["dram_group"] == grp, (case, f)
