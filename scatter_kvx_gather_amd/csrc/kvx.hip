@@ -444,13 +444,37 @@ bool dram_pairs(const kvx_pool* p, int32_t q0, int32_t nq, int64_t R) {
 }
 
 // The order word's DRAM-page bits (pairs: m = 2) for a plane-major paged
-// launch of the wide copy with U rows of R bytes per chunk, 0 when the
-// launch keeps the natural order.
+// launch of the wide copy with U rows of R bytes per chunk, or of 4-16 KiB
+// rows in 2 KiB pieces (`pieces`; k_paged_sub pairs the same piece of two
+// rows); `stage`: the staging buffer of a gather or scatter, else nullptr.
+// 0 when the launch keeps the natural order.  Pieces measured (same process,
+// against KVX_DRAM_ORDER=0; 2048 tokens, 16384-slot pools, 8 disjoint
+// requests rotated; gather-scatter / gather / scatter GB/s): 4 KiB rows,
+// pages of 16 rows 5514 -> 6084 / 6092 -> 6371 / 5879 -> 6259, of 32 rows
+// 5824 -> 6074 / 6184 -> 6351 / 6057 -> 6263; 8 KiB rows, pages of 8 rows
+// 5433 -> 6037 / 6063 -> 6376 / 5841 -> 6231, of 16 rows 5699 -> 6069 /
+// 6131 -> 6320 / 6014 -> 6276; 16 KiB rows, pages of 4 rows 5330 -> 5982 /
+// 6021 -> 6351 / 5790 -> 6233; page-1 pools (staging only) within 2.5%.
+// The contiguous staging of a gather or scatter pairs the same way when its
+// base is aligned to two segments (each request's plane blocks then pair
+// too when their offsets are): measured (same process, against the order
+// without it; GB/s gather / scatter): the 2048-token, 144 KiB/token request
+// 6031 -> 6096 / 5544 -> 5584, 4096 tokens 5842 -> 5929 / 5386 -> 5488, 8
+// requests of 1024 tokens 5747 -> 5849 / 5421 -> 5548, 4 ragged requests
+// 5742 -> 5794 / 5386 -> 5438; 1 KiB rows, 4096 tokens 5777 -> 5759 / 5282
+// -> 5475.
+#ifndef KVX_DRAM_STAGE
+#define KVX_DRAM_STAGE 1
+#endif
 uint32_t dram_order_bits(const kvx_pool* src, const kvx_pool* dst, int32_t q0, int32_t nq,
-                         int64_t R, const Shape& sh, bool above_round) {
-    if (KVX_DRAM_ORDER == 0 || !above_round || sh.vpl <= 0 || sh.U * R > kPagedWaveBytes)
-        return 0;
-    if (!dram_pairs(src, q0, nq, R) && !dram_pairs(dst, q0, nq, R)) return 0;
+                         int64_t R, const Shape& sh, bool above_round, const void* stage,
+                         bool pieces) {
+    if (KVX_DRAM_ORDER == 0 || !above_round) return 0;
+    if (!pieces && (sh.vpl <= 0 || sh.U * R > kPagedWaveBytes)) return 0;
+    const bool stage_ok = KVX_DRAM_STAGE != 0 && stage != nullptr && (R & (R - 1)) == 0 &&
+                          R <= kDramSegBytes / 2 &&
+                          reinterpret_cast<uintptr_t>(stage) % (2 * kDramSegBytes) == 0;
+    if (!dram_pairs(src, q0, nq, R) && !dram_pairs(dst, q0, nq, R) && !stage_ok) return 0;
     const uint32_t gs = static_cast<uint32_t>(__builtin_ctzll(static_cast<uint64_t>(kDramSegBytes / R)));
     return (gs << 8) | (1u << 16);
 }
@@ -649,10 +673,10 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
         // scatter 5310 -> 5419 GB/s, scatter 5368 -> 5415
         if (tmajor && KVX_XCD_REMAP != 0) a.c.remap = 1;
         a.c.order = tmajor ? 1u
-                           : (sub == 0 ? dram_order_bits(src, dst, q0, nq, g.R, sh,
-                                                         above_one_round(reqs->total_tokens *
-                                                                         nq * g.R, cus))
-                                       : 0u);
+                           : dram_order_bits(src, dst, q0, nq, g.R, sh,
+                                             above_one_round(reqs->total_tokens * nq * g.R, cus),
+                                             src_stage != nullptr ? src_stage : dst_stage,
+                                             sub > 0);
         const uint32_t grid = grid_for(a.c.nchunks, cus, kPagedWaves);
         const size_t lds = std::is_same<Src, StageRef>::value &&
                                    above_one_round(reqs->total_tokens * nq * g.R, cus)

@@ -271,6 +271,28 @@ __device__ __forceinline__ int64_t dram_order(const Common& c, int64_t t, int64_
     return blk + ((i & ((int64_t(1) << ms) - 1)) << gs) + (i >> ms);
 }
 
+// The same order for rows moved as 2^sub_shift pieces of 2 KiB (k_paged_sub):
+// within a block, unit u = (token - block) * pieces + piece of the natural
+// order becomes piece (u / m) % pieces of token (u / m) / pieces + (u % m) * g,
+// so the two waves of a workgroup move the same piece of two rows one
+// segment apart.  `piece` is the natural piece on entry, the moved one on
+// return.
+__device__ __forceinline__ int64_t dram_order_piece(const Common& c, int64_t t, int64_t n_r,
+                                                    uint32_t& piece) {
+    const uint32_t ms = (c.order >> 16) & 0xffu;
+    if (ms == 0) return t;
+    const uint32_t gs = (c.order >> 8) & 0xffu;
+    const uint32_t ks = gs + ms;
+    const int64_t blk = (t >> ks) << ks;
+    if (blk + (int64_t(1) << ks) > n_r) return t;
+    const uint32_t ps = c.sub_shift;
+    const uint32_t u = (static_cast<uint32_t>(t - blk) << ps) + piece;
+    const uint32_t side = u & ((1u << ms) - 1u);
+    const uint32_t h = u >> ms;
+    piece = h & ((1u << ps) - 1u);
+    return blk + static_cast<int64_t>(h >> ps) + (static_cast<int64_t>(side) << gs);
+}
+
 // The request a lane's token belongs to, with its token range and the start
 // of its page list in each pool-side table.
 struct ReqOf {
@@ -519,7 +541,8 @@ struct SideAddr<StageRef> {
 // the copy may load it unconditionally (the call never writes its source).
 template <bool MANY, class Src, class Dst>
 __device__ __forceinline__ int resolve(const PagedArgs<Src, Dst>& a, const PagedChunk& k,
-                                       uint32_t u, uint64_t& s, uint64_t& d) {
+                                       uint32_t u, uint64_t& s, uint64_t& d,
+                                       uint32_t* piece = nullptr) {
     const Common& c = a.c;
     const int64_t tok = k.tok0 + u;
     const bool active = u < c.U && tok < c.T;
@@ -530,7 +553,8 @@ __device__ __forceinline__ int resolve(const PagedArgs<Src, Dst>& a, const Paged
     // a token range that contradicts total_tokens is never dereferenced
     if (q.off < 0 || tok < q.off || tok >= q.end || q.end > c.T) return kSkip;
     const int64_t n_r = q.end - q.off;
-    const int64_t t = dram_order(c, tok - q.off, n_r);
+    const int64_t t = piece != nullptr ? dram_order_piece(c, tok - q.off, n_r, *piece)
+                                       : dram_order(c, tok - q.off, n_r);
     // both sides' page-id reads go out before either is waited for
     const SideLook ls = SideAddr<Src>::look(a.src, c, k.ql, q.pg_src, q.off, n_r, t);
     const SideLook ld = SideAddr<Dst>::look(a.dst, c, k.ql, q.pg_dst, q.off, n_r, t);
@@ -553,7 +577,7 @@ struct StageRow {
 template <bool MANY, class Dst>
 __device__ __forceinline__ StageRow resolve_stage_row(const PagedArgs<StageRef, Dst>& a,
                                                       const PagedChunk& k, uint32_t u,
-                                                      uint64_t& s) {
+                                                      uint64_t& s, uint32_t* piece = nullptr) {
     const Common& c = a.c;
     const int64_t tok = k.tok0 + u;
     const bool active = u < c.U && tok < c.T;
@@ -566,7 +590,8 @@ __device__ __forceinline__ StageRow resolve_stage_row(const PagedArgs<StageRef, 
     if (q.off < 0 || tok < q.off || tok >= q.end || q.end > c.T) return r;
     r.off = q.off;
     r.n_r = q.end - q.off;
-    r.t = dram_order(c, tok - q.off, r.n_r);
+    r.t = piece != nullptr ? dram_order_piece(c, tok - q.off, r.n_r, *piece)
+                           : dram_order(c, tok - q.off, r.n_r);
     r.pg_dst = q.pg_dst;
     s = stage_addr(a.src, c, k.ql, r.off, r.n_r, r.t);
     r.code = kCopy;
@@ -994,12 +1019,12 @@ void k_paged_sub(PagedArgs<Src, Dst> a) {
         PagedChunk k;
         k.ql = static_cast<int32_t>(ql);
         k.tok0 = static_cast<int64_t>(j >> a.c.sub_shift);
-        const uint32_t piece = j & last;
+        uint32_t piece = j & last;          // DRAM-page order may move it (see resolve)
         if constexpr (KVX_SCATTER_EARLY != 0 && std::is_same<Src, StageRef>::value) {
             // scatter: the staging piece's loads go out before the
             // destination page table is read (as in k_paged)
             uint64_t s = 0, d = 0;
-            StageRow r = resolve_stage_row<MANY>(a, k, static_cast<uint32_t>(lane), s);
+            StageRow r = resolve_stage_row<MANY>(a, k, static_cast<uint32_t>(lane), s, &piece);
             if (r.code == kCopy) s += static_cast<uint64_t>(piece) * 2048u;
             WideRows<2, 1> w;
             w.load(s, lane);
@@ -1011,7 +1036,7 @@ void k_paged_sub(PagedArgs<Src, Dst> a) {
             continue;
         }
         uint64_t s = 0, d = 0;
-        int code = resolve<MANY>(a, k, static_cast<uint32_t>(lane), s, d);
+        int code = resolve<MANY>(a, k, static_cast<uint32_t>(lane), s, d, &piece);
         if (code == kCopy) {
             s += static_cast<uint64_t>(piece) * 2048u;
             d += static_cast<uint64_t>(piece) * 2048u;

@@ -43,7 +43,8 @@ GEOMS = [
 def run_paged_case(case, seed, guard=256, align=0):
     """gather (nontemporal and cached staging stores), scatter and
     gather-scatter of a case, every destination byte and the skip counts
-    against the oracle; `align`: the pools' first bytes at that multiple."""
+    against the oracle; `align`: the pools' and staging buffers' first bytes
+    at that multiple."""
     g = case.geom
     dev_pool = (lambda a: d_aligned(a, align)) if align else d
     Q, R = g.planes, g.row_bytes
@@ -62,15 +63,15 @@ def run_paged_case(case, seed, guard=256, align=0):
 
     say(case.name, f"Q={Q} R={R} T={case.total_tokens} pages {case.src.page_size}/"
         f"{case.dst.page_size}: gather")
-    staging = d(stage_prefill)
+    staging = dev_pool(stage_prefill)
     kvx.gather(lay, src, st, reqs, staging, skipped=skipped[0:1])
     # the same gather with ordinary stores for the staging (KVX_OUT_CACHED)
     say(case.name, "gather, cached output")
-    staging_c = d(stage_prefill)
+    staging_c = dev_pool(stage_prefill)
     kvx.gather(lay, src, st, reqs, staging_c, cached_out=True)
     say(case.name, "scatter")
     dst_d1 = dev_pool(dst_h)
-    kvx.scatter(lay, d(stage_in), reqs, kvx.Pool(dst_d1, case.dst.num_pages, case.dst.page_size),
+    kvx.scatter(lay, dev_pool(stage_in), reqs, kvx.Pool(dst_d1, case.dst.num_pages, case.dst.page_size),
                 dt, skipped=skipped[1:2])
     say(case.name, "gather_scatter")
     dst_d2 = dev_pool(dst_h)
@@ -230,10 +231,11 @@ def test_one_row_per_wave_launches(bi):
 # Pools whose pages hold runs of at least 64 KiB of a plane, planes aligned
 # to 128 KiB, in launches above 64 MiB each way: the kernels take each
 # request's tokens in DRAM-page order (rows 32 KiB apart on the two waves of
-# one workgroup, or in one wave for 1 KiB rows; a block past the request's
-# end in natural order).  One 2 KiB row or two 1 KiB rows per wave, one
-# side or both paired, ragged requests whose starts are not block aligned,
-# partial last pages, out-of-range ids, a batch above 64 requests.
+# one workgroup, or in one wave for 1 KiB rows; the same 2 KiB piece of two
+# 4-16 KiB rows on the two waves of one workgroup; a block past the
+# request's end in natural order).  One side or both paired (a staging side
+# pairs at any page size), ragged requests whose starts are not block
+# aligned, partial last pages, out-of-range ids, a batch above 64 requests.
 # (geometry, lengths, src page, dst page, oor)
 DRAM = [
     (wl.Geometry(36, 2, 8, 128, "bf16"), [300, 0, 257, 64, 1], 64, 64, 0.0),   # 2 KiB
@@ -244,6 +246,11 @@ DRAM = [
     (wl.Geometry(28, 2, 4, 128, "bf16"), [700, 129, 500], 128, 64, 0.02),      # 1 KiB
     (wl.Geometry(36, 2, 4, 128, "bf16"), [900, 250], 64, 128, 0.0),
     (wl.Geometry(36, 2, 8, 128, "bf16"), "many", 32, 32, 0.01),                # > 64 requests
+    (wl.Geometry(36, 2, 8, 128, "bf16"), [700, 3, 120], 1, 1, 0.01),           # staging only
+    (wl.Geometry(8, 2, 16, 128, "bf16"), [600, 17, 500], 16, 32, 0.02),        # 4 KiB pieces
+    (wl.Geometry(8, 2, 16, 128, "bf16"), [1200], 1, 16, 0.0),
+    (wl.Geometry(4, 2, 32, 128, "bf16"), [700, 450], 8, 16, 0.01),             # 8 KiB pieces
+    (wl.Geometry(2, 2, 64, 128, "bf16"), [1000, 3, 150], 4, 1, 0.01),          # 16 KiB pieces
 ]
 
 

@@ -193,7 +193,9 @@ def paged(L, H, B, T, off, op):
     ta = kvx.Table(pg, d(rng.permutation(P)[:T // B].astype(np.int32)))
     tb = kvx.Table(pg, d(rng.permutation(P)[:T // B].astype(np.int32)))
     if op == "gather":
-        st = torch.zeros(Q * T * R, dtype=torch.uint8, device=dev)
+        st = torch.zeros(Q * T * R + (256 << 10), dtype=torch.uint8, device=dev)
+        o = (-st.data_ptr()) % (128 << 10) + off
+        st = st[o:o + Q * T * R]
         kvx.gather(lay, kvx.Pool(A, P, B), ta, reqs, st)
     else:
         kvx.gather_scatter(lay, kvx.Pool(A, P, B), ta, reqs, kvx.Pool(Bp, P, B), tb)
@@ -201,11 +203,14 @@ def paged(L, H, B, T, off, op):
 
 
 for name, L, H, B, T, off, op in (("large64", 36, 8, 64, 640, 0, "gather_scatter"),
+                                   ("large1", 36, 8, 1, 640, 0, "gather"),
+                                   ("large1gs", 36, 8, 1, 640, 0, "gather_scatter"),
                                    ("large32", 36, 8, 32, 640, 0, "gather"),
                                    ("large1k", 28, 4, 64, 1280, 0, "gather"),
                                    ("large16", 36, 8, 16, 640, 0, "gather"),
                                    ("misaligned", 36, 8, 64, 640, 2048, "gather"),
-                                   ("small64", 2, 8, 64, 640, 0, "gather")):
+                                   ("small64", 2, 8, 64, 640, 0, "gather"),
+                                   ("pieces16", 8, 16, 16, 1280, 0, "gather_scatter")):
     print(f"case {{name}}", file=sys.stderr, flush=True)
     paged(L, H, B, T, off, op)
 print("dram ok", flush=True)
@@ -216,21 +221,25 @@ def test_dram_page_order_reaches_the_kernels():
     """With KVX_LOG=1: a plane-major launch above one round of resident
     waves pairs the rows that share DRAM pages (2 KiB rows one per wave, 1 KiB
     rows two per wave) when a pool's pages hold runs of at least 64 KiB of a
-    plane and its planes are aligned; not for pages of 32 KiB, planes off the
-    64 KiB grid, or a launch of 8 KiB chunks."""
+    plane and its planes are aligned, or when a gather's or scatter's staging
+    is aligned (then at any page size); not pool to pool with pages of
+    32 KiB or less, with planes and staging off the 64 KiB grid, or in a
+    launch of 8 KiB chunks."""
     env = dict(os.environ, KVX_LOG="1")
     p = subprocess.run([sys.executable, "-c", DRAM_CHILD.format(root=ROOT)], capture_output=True,
                        text=True, timeout=180, env=env, cwd=ROOT)
     assert p.returncode == 0, p.stdout + p.stderr
     assert "dram ok" in p.stdout
+    assert "pieces/row=2" in p.stderr
     seen, case = {}, None
     for line in p.stderr.splitlines():
         if line.startswith("case "):
             case = line.split()[1]
         elif case and line.startswith("kvx: "):
             seen[case] = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
-    expect = {"large64": ("1", "2"), "large32": ("1", "2"), "large1k": ("2", "2"),
-              "large16": ("1", "0"), "misaligned": ("1", "0"), "small64": ("4", "0")}
+    expect = {"large64": ("1", "2"), "large1": ("1", "2"), "large1gs": ("1", "0"),
+              "large32": ("1", "2"), "large1k": ("2", "2"), "large16": ("1", "2"),
+              "misaligned": ("1", "0"), "small64": ("4", "0"), "pieces16": ("1", "2")}
     for case, (U, grp) in expect.items():
         f = seen[case]
         assert f["order"] == "plane-major" and f["U"] == U and f["dram_group"] == grp, (case, f)
