@@ -1430,6 +1430,44 @@ def dram_pages(torch, kvx, wl, wdev, dev, stream, rounds=3, n=24):
                                                     stream=stream)}
             for op, fn in fns.items():
                 blocks[B][op].append(nb / (graph_timed(torch, stream, fn, n) * 1e-3) / 1e9)
+    # the same bytes as pools whose blocks hold a layer's K and V pages
+    # together ([L][blocks][2][B][R]; page stride 2 B R): from pages of
+    # 32 KiB the library pairs the two planes of a token
+    kvb = {B: {"gather_scatter": [], "gather": [], "scatter": []} for B in (8, 16, 32)}
+    kvtabs = {}
+    for B in kvb:
+        nblk, npg, run = NS // B, T // B, B * R
+
+        def kvpool(t, nblk=nblk, run=run, B=B):
+            return kvx.Pool([t.data_ptr() + (q // 2) * nblk * 2 * run + (q % 2) * run
+                             for q in range(Q)], nblk, B, slot_stride=R, page_stride=2 * run,
+                            keep=t)
+        rng = np.random.default_rng(6300 + B)
+        ps, pd = rng.permutation(nblk), rng.permutation(nblk)
+        pg = d(np.array([0, npg], np.int64))
+        kvtabs[B] = (kvpool(A), kvpool(Bt),
+                     [kvx.Table(pg, d(ps[k * npg:(k + 1) * npg].astype(np.int32)))
+                      for k in range(NSETS)],
+                     [kvx.Table(pg, d(pd[k * npg:(k + 1) * npg].astype(np.int32)))
+                      for k in range(NSETS)])
+    for rnd in range(rounds):
+        for B, (pa, pb, sT, dT) in kvtabs.items():
+            fns = {"gather_scatter": lambda k: kvx.gather_scatter(
+                       lay, pa, sT[k % NSETS], reqs, pb, dT[k % NSETS], stream=stream),
+                   "gather": lambda k: kvx.gather(lay, pa, sT[k % NSETS], reqs, st,
+                                                  stream=stream),
+                   "scatter": lambda k: kvx.scatter(lay, st, reqs, pb, dT[k % NSETS],
+                                                    stream=stream)}
+            for op, fn in fns.items():
+                kvb[B][op].append(nb / (graph_timed(torch, stream, fn, n) * 1e-3) / 1e9)
+    kvrows = []
+    for B, r in kvb.items():
+        row = {"page_size": B, "page_KiB": B * R // 1024, "planes_paired": B * R >= DRAM_SEG}
+        for op, v in r.items():
+            row[f"{op}_GBps"] = round(sorted(v)[len(v) // 2], 1)
+        kvrows.append(row)
+        log(f"  K/V block pool, page {B:3d}: {row['gather_scatter_GBps']:7.1f} "
+            f"{row['gather_GBps']:7.1f} {row['scatter_GBps']:7.1f}")
     brows = []
     for B, r in blocks.items():
         row = {"page_size": B, "page_KiB": B * R // 1024,
@@ -1439,7 +1477,7 @@ def dram_pages(torch, kvx, wl, wdev, dev, stream, rounds=3, n=24):
         brows.append(row)
         log(f"  block pool, page {B:3d}: {row['gather_scatter_GBps']:7.1f} "
             f"{row['gather_GBps']:7.1f} {row['scatter_GBps']:7.1f}")
-    print(json.dumps({"dram_pages": rows, "block_pools": brows,
+    print(json.dumps({"dram_pages": rows, "block_pools": brows, "kv_block_pools": kvrows,
                       "note": "one request of 2048 tokens x 72 planes of 2 KiB rows (288 MiB "
                               "each way) in page-1 pools of 32768 slots (4.5 GiB each); every "
                               "design uses 2048 of the 32768 slots per request, only their "
@@ -1846,6 +1884,21 @@ def summarize_json(log_path, out_path, title, command):
                     f.write(f"| {r['page_size']} | {r['page_KiB']} | "
                             f"{'yes' if r['paired'] else 'no'} | {r['gather_scatter_GBps']} | "
                             f"{r['gather_GBps']} | {r['scatter_GBps']} |\n")
+                f.write("\n")
+            if "kv_block_pools" in d:
+                f.write("The same request between pools whose blocks hold a layer's K and V "
+                        "pages together (one [36][blocks][2][B][R] tensor per pool over the "
+                        "same bytes, page stride 2 B R); from pages of 32 KiB a K row and the "
+                        "V row of the same token share a DRAM page, and a gather-scatter or "
+                        "scatter runs the two planes of a token on the two waves of one "
+                        "workgroup (a gather pairs its staging rows instead).\n\n")
+                f.write("| page size (rows) | page (KiB) | planes paired | gather-scatter | "
+                        "gather | scatter |\n|---:|---:|---|---:|---:|---:|\n")
+                for r in d["kv_block_pools"]:
+                    f.write(f"| {r['page_size']} | {r['page_KiB']} | "
+                            f"{'yes' if r['planes_paired'] else 'no'} | "
+                            f"{r['gather_scatter_GBps']} | {r['gather_GBps']} | "
+                            f"{r['scatter_GBps']} |\n")
                 f.write("\n")
             if "mla_row_patterns" in d:
                 f.write("The MLA request (27 planes of 1152-byte rows, 2048 tokens, 32768-slot "

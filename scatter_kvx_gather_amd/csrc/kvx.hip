@@ -463,6 +463,36 @@ bool dram_pairs(const kvx_pool* p, int32_t q0, int32_t nq, int64_t R) {
 // requests of 1024 tokens 5747 -> 5849 / 5421 -> 5548, 4 ragged requests
 // 5742 -> 5794 / 5386 -> 5438; 1 KiB rows, 4096 tokens 5777 -> 5759 / 5282
 // -> 5475.
+// Pools whose blocks hold the K and V pages of a layer together ([survey]
+// 7.4's block length: a [num_blocks][2][B][H][D] tensor per layer, or one
+// [num_blocks][L][2][B][H][D] tensor; planes 2l and 2l + 1 one page apart):
+// with pages of 32 or 64 KiB, K row t and V row t of a block share a DRAM
+// page, so planes pair instead of tokens (order bit 1, paged_chunk: the two
+// planes of a token on the two waves of one workgroup).  Measured (same
+// process, against KVX_DRAM_ORDER=0; one [blocks][36][2][B][8][128] bf16
+// tensor per pool, 8 disjoint requests rotated; gather-scatter / scatter
+// GB/s): pages of 16 rows (32 KiB), 2048 tokens 5048 -> 5958 / 5520 ->
+// 5802, 4096 tokens 5157 -> 6146 / 5564 -> 5964, 8192 tokens 5185 -> 6197 /
+// 5599 -> 5837; pages of 32 rows 5483 -> 5993 / 5856 -> 5847; 1 KiB rows,
+// pages of 32 rows 5006 -> 5757 / 5308 -> 5254; pages of 8 rows (16 KiB, not
+// paired) unchanged.  True when every plane pair of the launch (the launch
+// starts at an even plane) is one page apart and each block's pair is
+// aligned to its own length.
+bool dram_plane_pairs(const kvx_pool* p, int32_t q0, int32_t nq, int64_t R) {
+    if (p == nullptr || nq < 2 || (q0 & 1) != 0 || p->slot_stride != R) return false;
+    const int64_t run = static_cast<int64_t>(p->page_size) * R;
+    if (run % kDramSegBytes != 0 || 2 * run > 4 * kDramSegBytes) return false;
+    if (page_stride_of(p) % (2 * run) != 0) return false;
+    for (int32_t q = q0; q + 1 < q0 + nq; q += 2) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(p->planes[q]);
+        const uintptr_t b = reinterpret_cast<uintptr_t>(p->planes[q + 1]);
+        if (b < a || b - a != static_cast<uintptr_t>(run) ||
+            a % static_cast<uintptr_t>(2 * run) != 0)
+            return false;
+    }
+    return true;
+}
+
 #ifndef KVX_DRAM_STAGE
 #define KVX_DRAM_STAGE 1
 #endif
@@ -471,6 +501,14 @@ uint32_t dram_order_bits(const kvx_pool* src, const kvx_pool* dst, int32_t q0, i
                          bool pieces) {
     if (KVX_DRAM_ORDER == 0 || !above_round) return 0;
     if (!pieces && (sh.vpl <= 0 || sh.U * R > kPagedWaveBytes)) return 0;
+    // plane pairs for gather-scatter and scatter; a gather keeps its staging
+    // rows paired instead (its waves would otherwise write two planes'
+    // staging blocks, n_r rows apart, at once: 8192 tokens of K/V blocks
+    // gathered 5994 -> 5750 GB/s with plane pairs, while 2048 and 4096
+    // tokens gained 2-3%)
+    if (!pieces && dst != nullptr &&
+        (dram_plane_pairs(src, q0, nq, R) || dram_plane_pairs(dst, q0, nq, R)))
+        return 2u;
     const bool stage_ok = KVX_DRAM_STAGE != 0 && stage != nullptr && (R & (R - 1)) == 0 &&
                           R <= kDramSegBytes / 2 &&
                           reinterpret_cast<uintptr_t>(stage) % (2 * kDramSegBytes) == 0;
@@ -690,7 +728,8 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
                          static_cast<long long>(reqs->total_tokens), reqs->num_reqs,
                          sh.vpl > 0 ? "wide" : (sh.vpl < 0 ? "row-loop" : "flat"), sh.U,
                          1u << sub, a.c.nchunks, grid, a.c.remap,
-                         tmajor ? "token-major" : "plane-major",
+                         tmajor ? "token-major"
+                                : ((a.c.order & 2u) != 0 ? "plane-pairs" : "plane-major"),
                          (a.c.order >> 16) != 0 ? 1u << (a.c.order >> 16) : 0u,
                          static_cast<int>(lds),
                          std::is_same<Dst, StageRef>::value && out_cached != 0 ? "cached"

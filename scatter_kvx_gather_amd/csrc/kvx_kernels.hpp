@@ -118,9 +118,10 @@ struct Common {
     uint32_t v_magic;           // ceil(2^32 / V)
     uint32_t remap;             // 1: XCD-aware workgroup renumbering
     uint32_t sub_shift;         // k_paged_sub: log2 of the 2 KiB pieces of a row
-    uint32_t order;             // paged: bit 0 token-major chunk order (see paged_chunk);
-                                // bits 8-15 / 16-23: log2 of the tokens per DRAM
-                                // segment and of the segments grouped (dram_order)
+    uint32_t order;             // paged: bit 0 token-major chunk order, bit 1 plane
+                                // pairs (see paged_chunk); bits 8-15 / 16-23: log2 of
+                                // the tokens per DRAM segment and of the segments
+                                // grouped (dram_order)
     double req_rate;            // paged: num_reqs / T (requests per token)
 };
 
@@ -237,6 +238,20 @@ __device__ __forceinline__ PagedChunk paged_chunk(const Common& c, uint32_t chun
         k.ql = static_cast<int32_t>(chunk - j * nq);
         k.tok0 = static_cast<int64_t>(j) * c.U;
         return k;
+    }
+    if (c.order & 2u) {
+        // plane pairs: planes 2p and 2p + 1 of a token block on adjacent
+        // waves (the K and V pages of one pool block, one DRAM page apart;
+        // see dram_order); with an odd plane count the last plane runs alone
+        const uint32_t cpp2 = 2u * c.chunks_per_plane;
+        const uint32_t p = chunk / cpp2;
+        const uint32_t nq = c.nchunks / c.chunks_per_plane;
+        if (2u * p + 1u < nq) {
+            const uint32_t r = chunk - p * cpp2;
+            k.ql = static_cast<int32_t>(2u * p + (r & 1u));
+            k.tok0 = static_cast<int64_t>(r >> 1) * c.U;
+            return k;
+        }
     }
     uint32_t ql = chunk / c.chunks_per_plane;
     uint32_t j = chunk - ql * c.chunks_per_plane;

@@ -454,12 +454,14 @@ def test_token_major_pools(ti):
     run_paged_case_token_major(big_case(f"tm{ti}", g, lens, sp, dp, 8800 + ti, oor), 8800 + ti)
 
 
-def run_paged_case_blocks(case, seed):
+def run_paged_case_blocks(case, seed, align=0):
     """gather, scatter and gather-scatter between pools whose blocks hold
     several planes' pages: the source one [blocks][2][B][R] tensor per layer
     (K and V pages of a block together), the destination one
     [blocks][layers][2][B][R] tensor; each plane addressed through the block
-    length as its page stride.  Every byte against the oracle."""
+    length as its page stride.  Every byte against the oracle.  `align`: the
+    tensors' first bytes at that multiple."""
+    dev_t = (lambda a: d_aligned(a, align)) if align else d
     g = case.geom
     Q, R, L = g.planes, g.row_bytes, g.num_layers
     kv = g.num_kv
@@ -472,7 +474,7 @@ def run_paged_case_blocks(case, seed):
     stage_in = rng.integers(0, 256, n, dtype=np.uint8)
     lay, reqs = layout_of(g), requests(case)
     st, dt = table(case.src), table(case.dst)
-    src_d = [d(a) for a in src_h]
+    src_d = [dev_t(a) for a in src_h]
     src = kvx.Pool([src_d[q // kv].data_ptr() + (q % kv) * bs * R for q in range(Q)],
                    case.src.num_pages, bs, slot_stride=R, page_stride=kv * bs * R,
                    keep=src_d)
@@ -492,10 +494,10 @@ def run_paged_case_blocks(case, seed):
     staging = torch.zeros(n, dtype=torch.uint8, device=DEV)
     kvx.gather(lay, src, st, reqs, staging, skipped=skipped[0:1])
     say(case.name, "blocks scatter")
-    dst_d1 = d(dst_h)
+    dst_d1 = dev_t(dst_h)
     kvx.scatter(lay, d(stage_in), reqs, dst_pool(dst_d1), dt, skipped=skipped[1:2])
     say(case.name, "blocks gather_scatter")
-    dst_d2 = d(dst_h)
+    dst_d2 = dev_t(dst_h)
     kvx.gather_scatter(lay, src, st, reqs, dst_pool(dst_d2), dt, skipped=skipped[2:3])
     torch.cuda.synchronize()
 
@@ -539,6 +541,86 @@ def test_block_interleaved_pools(bi):
     rng = np.random.default_rng(8900 + bi)
     lens = _ragged(rng, nreq, maxlen, zf)
     run_paged_case_blocks(big_case(f"blocks{bi}", g, lens, sp, dp, 8900 + bi, oor), 8900 + bi)
+
+
+# The same block pools, tensors aligned to 128 KiB, in launches above 64 MiB
+# each way with one 2 KiB row or two 1 KiB rows per wave: where a block's K
+# and V pages (32 or 64 KiB each) share DRAM pages, the kernels run the two
+# planes of a token on the two waves of one workgroup (plane-pair order).
+# (geometry, requests, max length, empty fraction, src page, dst page, oor)
+BLOCKS_PAIRED = [
+    (wl.Geometry(36, 2, 8, 128, "bf16"), 3, 600, 0.0, 16, 16, 0.01),   # both sides
+    (wl.Geometry(36, 2, 8, 128, "bf16"), 3, 700, 0.0, 32, 3, 0.0),     # source, 64 KiB pages
+    (wl.Geometry(36, 2, 4, 128, "bf16"), 4, 900, 0.0, 1, 32, 0.02),    # destination, 1 KiB rows
+    (wl.Geometry(35, 2, 8, 128, "bf16"), 90, 20, 0.2, 16, 16, 0.01),   # > 64 requests
+]
+
+
+@pytest.mark.parametrize("bi", range(len(BLOCKS_PAIRED)))
+def test_block_pools_plane_pairs(bi):
+    g, nreq, maxlen, zf, sp, dp, oor = BLOCKS_PAIRED[bi]
+    rng = np.random.default_rng(8950 + bi)
+    lens = _ragged(rng, nreq, maxlen, zf)
+    assert sum(lens) * g.planes * g.row_bytes > 64 << 20
+    run_paged_case_blocks(big_case(f"pairs{bi}", g, lens, sp, dp, 8950 + bi, oor), 8950 + bi,
+                          align=128 << 10)
+
+
+def test_plane_pairs_odd_plane_count():
+    """Three planes (one per layer, num_kv = 1) whose pages lie one page apart
+    in [blocks][4][16][R] tensors (a block's fourth page unused), aligned to
+    128 KiB, in a launch above 64 MiB each way: planes 0 and 1 run as a pair,
+    plane 2 alone.  Pools, staging and skip counts against the oracle."""
+    g = wl.Geometry(3, 1, 8, 128, "bf16")               # Q = 3, R = 2 KiB
+    Q, R, B = g.planes, g.row_bytes, 16
+    case = big_case("odd_pairs", g, [6000, 5500], B, B, 8990, 0.01)
+    assert case.total_tokens * Q * R > 64 << 20
+    rng = np.random.default_rng(8990)
+    blk = 4 * B * R                                     # block length (page stride)
+    src_h = rng.integers(0, 256, case.src.num_pages * blk, dtype=np.uint8)
+    dst_h = rng.integers(0, 256, case.dst.num_pages * blk, dtype=np.uint8)
+    n = case.total_tokens * Q * R
+    stage_in = rng.integers(0, 256, n, dtype=np.uint8)
+    lay, reqs = layout_of(g), requests(case)
+    st, dt = table(case.src), table(case.dst)
+    align = 128 << 10
+
+    def pool(t, pages):
+        return kvx.Pool([t.data_ptr() + q * B * R for q in range(Q)], pages, B, slot_stride=R,
+                        page_stride=blk, keep=t)
+
+    def planes(flat):
+        return [flat[q * B * R:] for q in range(Q)]
+
+    src_d = d_aligned(src_h, align)
+    skipped = torch.zeros(3, dtype=torch.int64, device=DEV)
+    say("odd_pairs gather")
+    staging = d_aligned(np.zeros(n, np.uint8), align)
+    kvx.gather(lay, pool(src_d, case.src.num_pages), st, reqs, staging, skipped=skipped[0:1])
+    say("odd_pairs scatter")
+    dst_d1 = d_aligned(dst_h, align)
+    kvx.scatter(lay, d_aligned(stage_in, align), reqs, pool(dst_d1, case.dst.num_pages), dt,
+                skipped=skipped[1:2])
+    say("odd_pairs gather_scatter")
+    dst_d2 = d_aligned(dst_h, align)
+    kvx.gather_scatter(lay, pool(src_d, case.src.num_pages), st, reqs,
+                       pool(dst_d2, case.dst.num_pages), dt, skipped=skipped[2:3])
+    torch.cuda.synchronize()
+    exp_stage = np.zeros(n, np.uint8)
+    s0 = oracle.gather(planes(src_h), R, B, case.src.num_pages, R, case.tok_off, case.src.pg_off,
+                       case.src.ids, exp_stage, page_stride=blk)
+    exp_dst1 = dst_h.copy()
+    s1 = oracle.scatter(stage_in, R, case.tok_off, case.dst.pg_off, case.dst.ids,
+                        planes(exp_dst1), R, B, case.dst.num_pages, page_stride=blk)
+    exp_dst2 = dst_h.copy()
+    s2 = oracle.gather_scatter(planes(src_h), R, B, case.src.num_pages, case.src.pg_off,
+                               case.src.ids, R, case.tok_off, planes(exp_dst2), R, B,
+                               case.dst.num_pages, case.dst.pg_off, case.dst.ids,
+                               src_page_stride=blk, dst_page_stride=blk)
+    assert_bytes_equal(staging.cpu().numpy(), exp_stage, "odd_pairs gather")
+    assert_bytes_equal(dst_d1.cpu().numpy(), exp_dst1, "odd_pairs scatter")
+    assert_bytes_equal(dst_d2.cpu().numpy(), exp_dst2, "odd_pairs gather_scatter")
+    assert skipped.cpu().tolist() == [s0, s1, s2]
 
 
 def test_more_than_128_planes():

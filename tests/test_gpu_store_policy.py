@@ -202,6 +202,31 @@ def paged(L, H, B, T, off, op):
     torch.cuda.synchronize()
 
 
+def kvblocks(L, B, T, op):
+    lay = kvx.Layout(L, 2, 8, 128, "bf16")                  # R = 2 KiB
+    Q, R, P = 2 * L, 2048, T // B + 4
+    run = B * R
+
+    def kvpool():
+        t = pool(1, L * P * 2 * B, R, 0).reshape(-1)        # [L][P][2][B][R], aligned
+        return kvx.Pool([t.data_ptr() + (q // 2) * P * 2 * run + (q % 2) * run
+                         for q in range(Q)], P, B, slot_stride=R, page_stride=2 * run, keep=t)
+    tok, pg = d(np.array([0, T], np.int64)), d(np.array([0, T // B], np.int64))
+    reqs = kvx.Requests(tok, T)
+    ta = kvx.Table(pg, d(rng.permutation(P)[:T // B].astype(np.int32)))
+    tb = kvx.Table(pg, d(rng.permutation(P)[:T // B].astype(np.int32)))
+    if op == "gather":
+        st = torch.zeros(Q * T * R, dtype=torch.uint8, device=dev)
+        kvx.gather(lay, kvpool(), ta, reqs, st)
+    else:
+        kvx.gather_scatter(lay, kvpool(), ta, reqs, kvpool(), tb)
+    torch.cuda.synchronize()
+
+
+for name, L, B, T, op in (("kv_gs", 36, 16, 640, "gather_scatter"),
+                          ("kv_gather", 36, 16, 640, "gather")):
+    print(f"case {{name}}", file=sys.stderr, flush=True)
+    kvblocks(L, B, T, op)
 for name, L, H, B, T, off, op in (("large64", 36, 8, 64, 640, 0, "gather_scatter"),
                                    ("large1", 36, 8, 1, 640, 0, "gather"),
                                    ("large1gs", 36, 8, 1, 640, 0, "gather_scatter"),
@@ -224,7 +249,8 @@ def test_dram_page_order_reaches_the_kernels():
     plane and its planes are aligned, or when a gather's or scatter's staging
     is aligned (then at any page size); not pool to pool with pages of
     32 KiB or less, with planes and staging off the 64 KiB grid, or in a
-    launch of 8 KiB chunks."""
+    launch of 8 KiB chunks.  Pools whose blocks hold a layer's K and V pages
+    together pair the two planes in a gather-scatter."""
     env = dict(os.environ, KVX_LOG="1")
     p = subprocess.run([sys.executable, "-c", DRAM_CHILD.format(root=ROOT)], capture_output=True,
                        text=True, timeout=180, env=env, cwd=ROOT)
@@ -243,3 +269,9 @@ def test_dram_page_order_reaches_the_kernels():
     for case, (U, grp) in expect.items():
         f = seen[case]
         assert f["order"] == "plane-major" and f["U"] == U and f["dram_group"] == grp, (case, f)
+    # K and V pages of one block (32 KiB each): a gather-scatter pairs the
+    # planes, a gather pairs its staging rows instead
+    f = seen["kv_gs"]
+    assert f["order"] == "plane-pairs" and f["dram_group"] == "0", f
+    f = seen["kv_gather"]
+    assert f["order"] == "plane-major" and f["dram_group"] == "2", f
