@@ -119,9 +119,10 @@ struct Common {
     uint32_t remap;             // 1: XCD-aware workgroup renumbering
     uint32_t sub_shift;         // k_paged_sub: log2 of the 2 KiB pieces of a row
     uint32_t order;             // paged: bit 0 token-major chunk order, bit 1 plane
-                                // pairs (see paged_chunk); bits 8-15 / 16-23: log2 of
-                                // the tokens per DRAM segment and of the segments
-                                // grouped (dram_order)
+                                // pairs, bit 2 token-major with planes g apart paired
+                                // (see paged_chunk); bits 8-15 / 16-23: log2 of the
+                                // tokens (planes) per DRAM segment and of the
+                                // segments grouped (dram_order)
     double req_rate;            // paged: num_reqs / T (requests per token)
 };
 
@@ -235,7 +236,20 @@ __device__ __forceinline__ PagedChunk paged_chunk(const Common& c, uint32_t chun
     if (c.order & 1u) {
         const uint32_t nq = c.nchunks / c.chunks_per_plane;
         const uint32_t j = chunk / nq;
-        k.ql = static_cast<int32_t>(chunk - j * nq);
+        uint32_t ql = chunk - j * nq;
+        if (c.order & 4u) {
+            // a token-major pool keeps a token's rows of all planes in one run:
+            // planes g apart (g = bits 8-15, the planes per 32 KiB) share DRAM
+            // pages, so within each complete block of 2 g planes position i
+            // takes plane (i % 2) * g + i / 2 (see dram_order)
+            const uint32_t gs = (c.order >> 8) & 0xffu;
+            const uint32_t b0 = (ql >> (gs + 1)) << (gs + 1);
+            if (b0 + (2u << gs) <= nq) {
+                const uint32_t i = ql - b0;
+                ql = b0 + ((i & 1u) << gs) + (i >> 1);
+            }
+        }
+        k.ql = static_cast<int32_t>(ql);
         k.tok0 = static_cast<int64_t>(j) * c.U;
         return k;
     }

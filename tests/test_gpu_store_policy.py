@@ -227,6 +227,19 @@ for name, L, B, T, op in (("kv_gs", 36, 16, 640, "gather_scatter"),
                           ("kv_gather", 36, 16, 640, "gather")):
     print(f"case {{name}}", file=sys.stderr, flush=True)
     kvblocks(L, B, T, op)
+# token-major pools (a slot's 72 rows of 2 KiB one run): planes 16 apart pair
+lay = kvx.Layout(36, 2, 8, 128, "bf16")
+S, T = 1024, 640
+tmA = torch.zeros(S * 72 * 2048, dtype=torch.uint8, device=dev)
+tmB = torch.zeros_like(tmA)
+tmpool = lambda t: kvx.Pool([t.data_ptr() + q * 2048 for q in range(72)], S, 1,
+                            slot_stride=72 * 2048, keep=t)
+tok = d(np.array([0, T], np.int64))
+print("case tm_gs", file=sys.stderr, flush=True)
+kvx.gather_scatter(lay, tmpool(tmA), kvx.Table(tok, d(rng.permutation(S)[:T].astype(np.int32))),
+                   kvx.Requests(tok, T), tmpool(tmB),
+                   kvx.Table(tok, d(rng.permutation(S)[:T].astype(np.int32))))
+torch.cuda.synchronize()
 for name, L, H, B, T, off, op in (("large64", 36, 8, 64, 640, 0, "gather_scatter"),
                                    ("large1", 36, 8, 1, 640, 0, "gather"),
                                    ("large1gs", 36, 8, 1, 640, 0, "gather_scatter"),
@@ -250,7 +263,8 @@ def test_dram_page_order_reaches_the_kernels():
     is aligned (then at any page size); not pool to pool with pages of
     32 KiB or less, with planes and staging off the 64 KiB grid, or in a
     launch of 8 KiB chunks.  Pools whose blocks hold a layer's K and V pages
-    together pair the two planes in a gather-scatter."""
+    together pair the two planes in a gather-scatter, and token-major pools
+    pair a token's planes 32 KiB apart."""
     env = dict(os.environ, KVX_LOG="1")
     p = subprocess.run([sys.executable, "-c", DRAM_CHILD.format(root=ROOT)], capture_output=True,
                        text=True, timeout=180, env=env, cwd=ROOT)
@@ -275,3 +289,5 @@ def test_dram_page_order_reaches_the_kernels():
     assert f["order"] == "plane-pairs" and f["dram_group"] == "0", f
     f = seen["kv_gather"]
     assert f["order"] == "plane-major" and f["dram_group"] == "2", f
+    # token-major pools: a token's planes 16 apart (32 KiB) pair
+    assert seen["tm_gs"]["order"] == "token-major-pairs", seen["tm_gs"]
