@@ -769,6 +769,28 @@ kvx_status run_paged(int op, const Geom& g, const kvx_reqs* reqs,
     return KVX_OK;
 }
 
+// Permutes (perm_dram_order): with one token row per wave above one round,
+// the four waves of a workgroup take the token rows that share DRAM pages on
+// both sides: rows 32 KiB apart in the flat buffer, a head's rows 32 KiB
+// apart in the HF tensors.  Measured (same process, against the natural
+// order; three buffers rotated; extract / rebuild GB/s): 4 heads of 256 B
+// (1 KiB token rows, the Qwen2.5-7B shape), seq 8192 6084-6118 -> 6376-6392
+// / 5904-5908 -> 6303-6338, seq 4096 5951 -> 6219 / 5976 -> 6275; but 8
+// heads (2 KiB rows) seq 2048 6359 -> 6027 / 6343 -> 6381, seq 8192 6207 ->
+// 5989 / 6370 -> 6327, and 16 heads 6082 -> 5795 / 6058 -> 5968.  Pairing
+// only the flat side's rows, or only the HF side's, moved none of these by
+// more than 3% either way.  So only 4-head 1 KiB token rows take it.
+#ifndef KVX_DRAM_PERMUTE
+#define KVX_DRAM_PERMUTE 1
+#endif
+uint32_t permute_order_bits(const Geom& g, uint32_t U) {
+    if (KVX_DRAM_ORDER == 0 || KVX_DRAM_PERMUTE == 0 || U != 1) return 0;
+    if (g.H != 4 || g.R != 1024) return 0;
+    const uint32_t ds = static_cast<uint32_t>(__builtin_ctzll(static_cast<uint64_t>(kDramSegBytes / g.R)));
+    const uint32_t hs = static_cast<uint32_t>(__builtin_ctz(static_cast<uint32_t>(g.H)));
+    return 8u | (ds << 8) | (hs << 16);
+}
+
 template <bool REBUILD>
 kvx_status run_permute(const Geom& g, void* const* hf, int64_t s_cap, int64_t seq, void* flat,
                        uint32_t out_cached, hipStream_t stream) {
@@ -800,15 +822,17 @@ kvx_status run_permute(const Geom& g, void* const* hf, int64_t s_cap, int64_t se
         a.H = g.H;
         a.c.remap = remap_for(static_cast<double>(nq) * g.H * s_cap * g.Db +
                               static_cast<double>(nq) * seq * g.R);
+        if (rows) a.c.order = permute_order_bits(g, sh.U);
         const uint32_t grid = grid_for(a.c.nchunks, cus, kPermuteWaves);
         if (log_enabled())
             std::fprintf(stderr,
                          "kvx: %s Q=%d planes[%d,%d) H=%d Db=%lld seq=%lld s_cap=%lld unit=%s "
-                         "U=%u chunks=%u grid=%u stores=%s\n",
+                         "U=%u chunks=%u grid=%u order=%s stores=%s\n",
                          REBUILD ? "rebuild" : "extract", g.Q, q0, q0 + nq, g.H,
                          static_cast<long long>(g.Db), static_cast<long long>(seq),
                          static_cast<long long>(s_cap), rows ? "token-row" : "head-row", sh.U,
-                         a.c.nchunks, grid, out_cached != 0 ? "cached" : "nontemporal");
+                         a.c.nchunks, grid, (a.c.order & 8u) != 0 ? "dram-pages" : "natural",
+                         out_cached != 0 ? "cached" : "nontemporal");
         // nontemporal stores unless the caller reads the output back soon
         const void* fn =
             out_cached == 0

@@ -122,7 +122,8 @@ struct Common {
                                 // pairs, bit 2 token-major with planes g apart paired
                                 // (see paged_chunk); bits 8-15 / 16-23: log2 of the
                                 // tokens (planes) per DRAM segment and of the
-                                // segments grouped (dram_order)
+                                // segments grouped (dram_order); permute: bit 3 and
+                                // bits 8-23 (perm_dram_order)
     double req_rate;            // paged: num_reqs / T (requests per token)
 };
 
@@ -1211,6 +1212,25 @@ __global__ __launch_bounds__(kWave * kPermuteWaves) void k_permute(PermuteArgs a
 // kernel, so every address is a per-lane constant plus s * Db (HF) or
 // s * H * Db (flat): no cross-lane exchange is needed.  U tokens per chunk;
 // NTS as for k_permute.
+// DRAM-page order of a permute's token rows (order bit 3; one token row per
+// wave, four waves per workgroup).  Token rows gd apart share DRAM pages on
+// the flat side (gd = 32 KiB / row bytes, order bits 8-15 hold log2 gd), a
+// head's rows gs = H * gd apart on the HF side (bits 16-23: log2 H).  Within
+// each block of 2 gs tokens, the four waves of a workgroup take tokens
+// a, a + gd, a + gs and a + gs + gd, a running over the first halves of the
+// 2 gd-token runs in [0, gs): both sides' page-sharing rows in one
+// workgroup.  A block past seq keeps its order; a bijection on [0, seq).
+__device__ __forceinline__ uint32_t perm_dram_order(const Common& c, uint32_t s, uint32_t seq) {
+    const uint32_t ds = (c.order >> 8) & 0xffu;         // log2 gd
+    const uint32_t gs_s = ds + ((c.order >> 16) & 0xffu);  // log2 gs
+    const uint32_t base = (s >> (gs_s + 1)) << (gs_s + 1);
+    if (base + (2u << gs_s) > seq) return s;
+    const uint32_t i = s - base;
+    const uint32_t k = i >> 2, w = i & 3u;
+    const uint32_t a = ((k >> ds) << (ds + 1)) + (k & ((1u << ds) - 1u));
+    return base + a + ((w & 1u) << ds) + ((w >> 1) << gs_s);
+}
+
 template <bool REBUILD, int VPL, int U, bool NTS>
 __global__ __launch_bounds__(kWave * kPermuteWaves) void k_permute_rows(PermuteArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -1228,7 +1248,8 @@ __global__ __launch_bounds__(kWave * kPermuteWaves) void k_permute_rows(PermuteA
     const uint32_t seq = a.c.units_per_plane;
     for (uint32_t chunk = wave_id<kPermuteWaves>(a.c); chunk < a.c.nchunks; chunk += nwaves) {
         const uint32_t ql = chunk / a.c.chunks_per_plane;
-        const uint32_t s0 = (chunk - ql * a.c.chunks_per_plane) * U;
+        uint32_t s0 = (chunk - ql * a.c.chunks_per_plane) * U;
+        if (U == 1 && (a.c.order & 8u) != 0) s0 = perm_dram_order(a.c, s0, seq);
         const uint64_t hf = reinterpret_cast<uint64_t>(a.hf[ql]);
         const uint64_t fl = reinterpret_cast<uint64_t>(a.flat) +
                             (static_cast<uint64_t>(a.c.q0 + ql) * seq + s0) * row;

@@ -677,7 +677,9 @@ PERMS = [
     (2, 64, 128, "bf16", 9, 9),       # token rows of 16 KiB (one token per chunk)
     (3, 12, 128, "bf16", 40, 40),     # token rows of 3 KiB: head-row kernel
     # launches above 64 MiB each way: one token row per wave
-    (72, 4, 128, "f16", 1200, 1111),  # token rows of 1 KiB (s_cap > seq)
+    (72, 4, 128, "f16", 1200, 1111),  # token rows of 1 KiB (s_cap > seq; DRAM-page order
+                                      # in 4 blocks of 256 tokens, the last 87 in order)
+    (60, 4, 128, "bf16", 1280, 1280), # 1 KiB rows: 5 whole DRAM-page blocks
     (20, 8, 128, "bf16", 2000, 2000), # token rows of 2 KiB
     (6, 16, 128, "bf16", 3100, 2999), # token rows of 4 KiB
 ]

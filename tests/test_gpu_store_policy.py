@@ -227,6 +227,14 @@ for name, L, B, T, op in (("kv_gs", 36, 16, 640, "gather_scatter"),
                           ("kv_gather", 36, 16, 640, "gather")):
     print(f"case {{name}}", file=sys.stderr, flush=True)
     kvblocks(L, B, T, op)
+# permutes above one round: 4 heads of 256 B take the DRAM-page order, 8 do not
+for name, L, H, seq in (("perm4", 28, 4, 1280), ("perm8", 36, 8, 640)):
+    lay = kvx.Layout(L, 2, H, 128, "bf16")
+    hf = torch.zeros((2 * L, H * seq * 256), dtype=torch.uint8, device=dev)
+    print(f"case {{name}}", file=sys.stderr, flush=True)
+    kvx.extract_permute(lay, hf, seq, seq,
+                        torch.zeros(2 * L * seq * H * 256, dtype=torch.uint8, device=dev))
+torch.cuda.synchronize()
 # token-major pools (a slot's 72 rows of 2 KiB one run): planes 16 apart pair
 lay = kvx.Layout(36, 2, 8, 128, "bf16")
 S, T = 1024, 640
@@ -264,7 +272,8 @@ def test_dram_page_order_reaches_the_kernels():
     32 KiB or less, with planes and staging off the 64 KiB grid, or in a
     launch of 8 KiB chunks.  Pools whose blocks hold a layer's K and V pages
     together pair the two planes in a gather-scatter, and token-major pools
-    pair a token's planes 32 KiB apart."""
+    pair a token's planes 32 KiB apart.  Permutes of 4-head 1 KiB token rows
+    take the DRAM-page order of their token rows; of 8-head rows not."""
     env = dict(os.environ, KVX_LOG="1")
     p = subprocess.run([sys.executable, "-c", DRAM_CHILD.format(root=ROOT)], capture_output=True,
                        text=True, timeout=180, env=env, cwd=ROOT)
@@ -291,3 +300,5 @@ def test_dram_page_order_reaches_the_kernels():
     assert f["order"] == "plane-major" and f["dram_group"] == "2", f
     # token-major pools: a token's planes 16 apart (32 KiB) pair
     assert seen["tm_gs"]["order"] == "token-major-pairs", seen["tm_gs"]
+    assert seen["perm4"]["U"] == "1" and seen["perm4"]["order"] == "dram-pages", seen["perm4"]
+    assert seen["perm8"]["U"] == "1" and seen["perm8"]["order"] == "natural", seen["perm8"]
