@@ -5,7 +5,8 @@ ids out of range, random-bit payloads (NaN patterns included),
 sentinel-filled destinations and guard bytes after the staging; token-major
 pools; pools whose blocks hold several planes' pages; launches of 65-160 MiB each way with rows of 1-16 KiB; head-sliced
 copies and permutes; page-table offsets that read outside their request's
-list; more than 128 planes.  Every case is compared byte for byte over the whole
+list; more than 128 planes; large launches over aligned pools, where the
+DRAM-page orders apply.  Every case is compared byte for byte over the whole
 destination, and the skip counters must agree.  KVX_FUZZ_SCALE=k multiplies
 the number of cases of each family (a longer campaign)."""
 import os
@@ -151,6 +152,35 @@ def test_fuzz_large_launches(seed):
         run_paged_case_token_major(case, 94000 + seed)
     else:
         run_paged_case(case, 94000 + seed)
+
+
+@pytest.mark.parametrize("seed", seeds(4))
+def test_fuzz_dram_page_order(seed):
+    # 65-160 MiB each way over pools and staging aligned to 128 KiB, so that
+    # the DRAM-page orders apply: pages of 16-128 rows of 1-16 KiB (rows
+    # paired inside pages of 64 KiB or more, pieces of 4-16 KiB rows paired),
+    # or blocks holding a layer's K and V pages together (planes paired);
+    # 1-400 requests with ragged lengths, empty ones and out-of-range ids
+    rng = np.random.default_rng(95000 + seed)
+    R = int(rng.choice([1024, 2048, 4096, 8192, 16384]))
+    g = wl.Geometry(int(rng.integers(2, 9)), 2, R // 256, 128, "bf16")
+    T = (int(rng.integers(65, 161)) << 20) // (g.planes * R) + 1
+    nreq = int(rng.choice([1, 5, 64, 65, 400]))
+    cuts = np.sort(rng.integers(0, T + 1, nreq - 1))
+    lens = np.diff(np.concatenate([[0], cuts, [T]]))
+    if rng.random() < 0.3:
+        emptied = rng.random(nreq) < 0.2
+        emptied[-1] = False
+        lens[-1] += int(lens[emptied].sum())
+        lens[emptied] = 0
+    sp, dp = (int(rng.choice([1, 16, 32, 64, 128])) for _ in range(2))
+    oor = float(rng.choice([0.0, 0.0, 0.02]))
+    case = big_case(f"fuzzdram{seed}", g, list(lens), sp, dp, 95000 + seed, oor)
+    assert case.total_tokens * g.planes * R > 64 << 20
+    if rng.random() < 0.3:
+        run_paged_case_blocks(case, 95000 + seed, align=128 << 10)
+    else:
+        run_paged_case(case, 95000 + seed, align=128 << 10)
 
 
 @pytest.mark.parametrize("seed", seeds(16))
