@@ -1477,12 +1477,75 @@ def dram_pages(torch, kvx, wl, wdev, dev, stream, rounds=3, n=24):
         brows.append(row)
         log(f"  block pool, page {B:3d}: {row['gather_scatter_GBps']:7.1f} "
             f"{row['gather_GBps']:7.1f} {row['scatter_GBps']:7.1f}")
+    pa = pb = fns = None                      # the loops' last pools
+    del A, Bt, st, PA, PB, tabs, btabs, kvtabs, pa, pb, fns
+    torch.cuda.empty_cache()
+    w5 = dram_pages_w5_orders(torch, kvx, wl, wdev, dev, stream, rounds)
     print(json.dumps({"dram_pages": rows, "block_pools": brows, "kv_block_pools": kvrows,
+                      "w5_orders": w5,
                       "note": "one request of 2048 tokens x 72 planes of 2 KiB rows (288 MiB "
                               "each way) in page-1 pools of 32768 slots (4.5 GiB each); every "
                               "design uses 2048 of the 32768 slots per request, only their "
                               "placement differs; 8 disjoint requests rotated, 24 launches per "
                               "graph, median of 3 rounds"}), flush=True)
+
+
+def dram_pages_w5_orders(torch, kvx, wl, wdev, dev, stream, rounds=3, n=4):
+    """Workload 5 (64 requests, page 16, two 36 GiB pools; half of each
+    pool's pages in use) written as one page-1 request over the same source
+    and destination slots, its tokens in batch order or sorted by destination
+    slot, by destination DRAM page (the rows of one 128 KiB block's pages
+    together) or by source DRAM page.  A gather-scatter's result does not
+    depend on the order; graph-timed gather-scatter GB/s per order."""
+    import numpy as np
+    case = wl.kv144k_64req_page16()
+    g = case.geom
+    Q, R, B = g.planes, g.row_bytes, case.src.page_size
+    NS, T = case.src.num_pages * B, case.total_tokens
+    src_slot = np.empty(T, np.int64)
+    dst_slot = np.empty(T, np.int64)
+    for r in range(case.num_reqs):
+        a, b = int(case.tok_off[r]), int(case.tok_off[r + 1])
+        t = np.arange(b - a)
+        src_slot[a:b] = case.src.ids[case.src.pg_off[r] + t // B].astype(np.int64) * B + t % B
+        dst_slot[a:b] = case.dst.ids[case.dst.pg_off[r] + t // B].astype(np.int64) * B + t % B
+    seg = DRAM_SEG // R                       # rows per 32 KiB
+
+    def page_key(x):                          # 128 KiB block, row within segment, segment
+        return (x // (4 * seg)) * (4 * seg) + (x % seg) * 4 + (x % (4 * seg)) // seg
+    orders = {"batch order": np.arange(T),
+              "sorted by destination slot": np.argsort(dst_slot, kind="stable"),
+              "sorted by destination DRAM page": np.argsort(page_key(dst_slot), kind="stable"),
+              "sorted by source DRAM page": np.argsort(page_key(src_slot), kind="stable")}
+    A = torch.empty((Q, NS, R), dtype=torch.uint8, device=dev)
+    Bt = torch.empty_like(A)
+    wdev.fill_hash(A, 1, stream=stream)
+    wdev.fill_hash(Bt, 2, stream=stream)
+    lay = kvx.Layout(g.num_layers, g.num_kv, g.kv_heads, g.head_dim, g.dtype)
+    PA, PB = kvx.Pool(A, NS), kvx.Pool(Bt, NS)
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    tok = d(np.array([0, T], np.int64))
+    reqs = kvx.Requests(tok, T)
+    tabs = {k: (kvx.Table(tok, d(src_slot[o].astype(np.int32))),
+                kvx.Table(tok, d(dst_slot[o].astype(np.int32)))) for k, o in orders.items()}
+    torch.cuda.synchronize()
+    nb = 2 * T * Q * R
+    res = {k: [] for k in orders}
+    for rnd in range(rounds):
+        for k, (sT, dT) in tabs.items():
+            ms = graph_timed(torch, stream, lambda i: kvx.gather_scatter(
+                lay, PA, sT, reqs, PB, dT, stream=stream), n)
+            res[k].append(nb / (ms * 1e-3) / 1e9)
+        log(f"dram-pages workload-5 orders round {rnd + 1}/{rounds} done")
+    out = [{"order": k, "gather_scatter_GBps": round(sorted(v)[len(v) // 2], 1)}
+           for k, v in res.items()]
+    for r in out:
+        log(f"  workload 5, {r['order']:35s} {r['gather_scatter_GBps']:7.1f}")
+    del A, Bt, PA, PB
+    torch.cuda.empty_cache()
+    return out
 
 
 def comparators(torch, kvx, wl, wdev, dev):
@@ -1899,6 +1962,15 @@ def summarize_json(log_path, out_path, title, command):
                             f"{'yes' if r['planes_paired'] else 'no'} | "
                             f"{r['gather_scatter_GBps']} | {r['gather_GBps']} | "
                             f"{r['scatter_GBps']} |\n")
+                f.write("\n")
+            if "w5_orders" in d:
+                f.write("Workload 5 (64 requests of 128 pages of 16 tokens, two 36 GiB pools, "
+                        "half of each pool's pages in use) written as one page-1 request over "
+                        "the same slots, its tokens in other orders (a gather-scatter's "
+                        "result does not depend on the order).\n\n")
+                f.write("| token order | gather-scatter |\n|---|---:|\n")
+                for r in d["w5_orders"]:
+                    f.write(f"| {r['order']} | {r['gather_scatter_GBps']} |\n")
                 f.write("\n")
             if "mla_row_patterns" in d:
                 f.write("The MLA request (27 planes of 1152-byte rows, 2048 tokens, 32768-slot "
