@@ -502,13 +502,14 @@ bool dram_plane_pairs(const kvx_pool* p, int32_t q0, int32_t nq, int64_t R) {
 // 2048 tokens 5607 -> 5779, 8192 tokens 5777 -> 5961, page 16 6002 -> 6087;
 // token-major into layer-major 5213 -> 5322, the reverse 5311 -> 5378;
 // scatter into a token-major pool 5653 -> 5683.  Bits for a token-major
-// launch; 0 to keep the plane order.
+// launch that writes a pool (a gather of short requests, the other
+// token-major launch, was not measured with it); 0 to keep the plane order.
 #ifndef KVX_DRAM_TMAJOR
 #define KVX_DRAM_TMAJOR 1
 #endif
 uint32_t tmajor_pair_bits(const kvx_pool* src, const kvx_pool* dst, int32_t q0, int32_t nq,
                           int64_t R, uint32_t U) {
-    if (KVX_DRAM_ORDER == 0 || KVX_DRAM_TMAJOR == 0 || U != 1) return 0;
+    if (KVX_DRAM_ORDER == 0 || KVX_DRAM_TMAJOR == 0 || U != 1 || dst == nullptr) return 0;
     if (R <= 0 || (R & (R - 1)) != 0 || R > kDramSegBytes / 2) return 0;
     const int64_t g = kDramSegBytes / R;
     if (2 * g > nq) return 0;
@@ -603,8 +604,16 @@ kvx_status launch(const void* fn, uint32_t grid, int wpb, Args& a, hipStream_t s
 // 4.5 GiB pools), scatter 5378 GB/s at full occupancy, 5439 / 5612 / 5570 at
 // 13 / 10 / 8 workgroups per CU, and the five-op step 5585 -> 5644.  The
 // other paged ops lose with the same cap (gather-scatter 5061 -> 4699 at 10,
-// gather 5739 -> 5556).
-constexpr size_t kScatterLdsPad = 16384;
+// gather 5739 -> 5556).  Re-measured with the DRAM-page orders (scatter GB/s
+// at pads 0 / 12 / 16 / 20 KiB, same process): 2 KiB rows page 1, 2048
+// tokens 5390 / 5432 / 5669 / 5736, 8192 tokens 5480 / 5503 / 5584 / 5619;
+// pages of 32 rows 6074 / 6210 / 6251 / 6055, of 16 rows 5096 / 5290 / 5825
+// / 5795; 1 KiB rows 5523 / 5599 / 5506 / 5291; 4 KiB rows in 16-row pages
+// 6152 / 6266 / 6289 / 6104: 16 KiB stays.
+#ifndef KVX_SCATTER_LDS_PAD
+#define KVX_SCATTER_LDS_PAD 16384
+#endif
+constexpr size_t kScatterLdsPad = KVX_SCATTER_LDS_PAD;
 
 template <class Src, class Dst, bool MANY, bool NTS>
 const void* paged_kernel_of(int vpl, uint32_t U) {
