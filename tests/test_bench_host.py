@@ -123,3 +123,48 @@ def test_dram_page_placements_have_the_structure_they_name():
                         assert np.all(off[:, :B // g] == g * np.arange(B // g)), label
                     else:
                         assert np.all(off == np.arange(B)), label
+
+
+def test_settle_phase_stops_when_two_blocks_agree_or_at_its_cap():
+    """settle_steps on fake CUDA objects: blocks of 8 steps until two blocks
+    in a row agree within 3% (and the host outruns the GPU), else until the
+    time cap; the step indices it used are the ones it reports."""
+    b = _bench()
+    seq = {"gpu": []}
+
+    class Ev:
+        def __init__(self, enable_timing=True):
+            pass
+
+        def record(self, stream=None):
+            pass
+
+        def elapsed_time(self, other):
+            return seq["gpu"].pop(0) * 8
+
+    class Cuda:
+        Event = Ev
+
+        @staticmethod
+        def synchronize():
+            pass
+
+    class Torch:
+        cuda = Cuda
+
+    class Wk:
+        def __init__(self):
+            self.steps = []
+
+        def step(self, i, stream):
+            self.steps.append(i)
+
+    seq["gpu"] = [1.4, 0.53, 0.52, 0.52]
+    wk = Wk()
+    out = b.settle_steps(Torch, wk, None)
+    assert out["steps"] == 24 and wk.steps == list(range(24))
+    assert [g for g, _ in out["blocks_gpu_host_ms_per_step"]] == [1.4, 0.53, 0.52]
+    seq["gpu"] = [1.0 + (k % 2) for k in range(1000000)]      # never agrees
+    wk = Wk()
+    out = b.settle_steps(Torch, wk, None, max_s=0.05)
+    assert out["steps"] == len(wk.steps) and out["steps"] % 8 == 0 and out["seconds"] >= 0.05
