@@ -1517,9 +1517,9 @@ def dram_pages(torch, kvx, wl, wdev, dev, stream, rounds=3, n=24):
     pa = pb = fns = None                      # the loops' last pools
     del A, Bt, st, PA, PB, tabs, btabs, kvtabs, pa, pb, fns
     torch.cuda.empty_cache()
-    w5 = dram_pages_w5_orders(torch, kvx, wl, wdev, dev, stream, rounds)
+    orders_64req = dram_pages_batch_orders(torch, kvx, wl, wdev, dev, stream, rounds)
     print(json.dumps({"dram_pages": rows, "block_pools": brows, "kv_block_pools": kvrows,
-                      "w5_orders": w5,
+                      "kv144k_64req_page16_orders": orders_64req,
                       "note": "one request of 2048 tokens x 72 planes of 2 KiB rows (288 MiB "
                               "each way) in page-1 pools of 32768 slots (4.5 GiB each); every "
                               "design uses 2048 of the 32768 slots per request, only their "
@@ -1527,8 +1527,8 @@ def dram_pages(torch, kvx, wl, wdev, dev, stream, rounds=3, n=24):
                               "graph, median of 3 rounds"}), flush=True)
 
 
-def dram_pages_w5_orders(torch, kvx, wl, wdev, dev, stream, rounds=3, n=4):
-    """Workload 5 (64 requests, page 16, two 36 GiB pools; half of each
+def dram_pages_batch_orders(torch, kvx, wl, wdev, dev, stream, rounds=3, n=4):
+    """The kv144k_64req_page16 batch (64 requests, page 16, two 36 GiB pools; half of each
     pool's pages in use) written as one page-1 request over the same source
     and destination slots, its tokens in batch order or sorted by destination
     slot, by destination DRAM page (the rows of one 128 KiB block's pages
@@ -1575,11 +1575,11 @@ def dram_pages_w5_orders(torch, kvx, wl, wdev, dev, stream, rounds=3, n=4):
             ms = graph_timed(torch, stream, lambda i: kvx.gather_scatter(
                 lay, PA, sT, reqs, PB, dT, stream=stream), n)
             res[k].append(nb / (ms * 1e-3) / 1e9)
-        log(f"dram-pages workload-5 orders round {rnd + 1}/{rounds} done")
+        log(f"dram-pages kv144k_64req_page16 orders round {rnd + 1}/{rounds} done")
     out = [{"order": k, "gather_scatter_GBps": round(sorted(v)[len(v) // 2], 1)}
            for k, v in res.items()]
     for r in out:
-        log(f"  workload 5, {r['order']:35s} {r['gather_scatter_GBps']:7.1f}")
+        log(f"  kv144k_64req_page16, {r['order']:35s} {r['gather_scatter_GBps']:7.1f}")
     del A, Bt, PA, PB
     torch.cuda.empty_cache()
     return out
@@ -2000,13 +2000,14 @@ def summarize_json(log_path, out_path, title, command):
                             f"{r['gather_scatter_GBps']} | {r['gather_GBps']} | "
                             f"{r['scatter_GBps']} |\n")
                 f.write("\n")
-            if "w5_orders" in d:
-                f.write("Workload 5 (64 requests of 128 pages of 16 tokens, two 36 GiB pools, "
+            if "kv144k_64req_page16_orders" in d:
+                f.write("The kv144k_64req_page16 batch (64 requests of 128 pages of 16 tokens, "
+                        "two 36 GiB pools, "
                         "half of each pool's pages in use) written as one page-1 request over "
                         "the same slots, its tokens in other orders (a gather-scatter's "
                         "result does not depend on the order).\n\n")
                 f.write("| token order | gather-scatter |\n|---|---:|\n")
-                for r in d["w5_orders"]:
+                for r in d["kv144k_64req_page16_orders"]:
                     f.write(f"| {r['order']} | {r['gather_scatter_GBps']} |\n")
                 f.write("\n")
             if "mla_row_patterns" in d:
